@@ -1,0 +1,14 @@
+"""The CPU oracle (test infrastructure).
+
+Plain fp64 C (``vq_oracle.c``) loaded through ctypes, plus the bits-per-weight
+closed form in Python.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import this package.  It shares no code with
+the HIP library and never imports it.
+"""
+from .oracle import (build, load, nnz, select, binorm, init, assign, objective, update,
+                     residual, reconstruct, fit)
+from .bits import bits_per_weight, compression_ratio_single
+
+__all__ = ["build", "load", "nnz", "select", "binorm", "init", "assign", "objective",
+           "update", "residual", "reconstruct", "fit", "bits_per_weight",
+           "compression_ratio_single"]

@@ -1,0 +1,390 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each pin takes a loaded oracle library and raises AssertionError when the
+oracle disagrees with what the pages or the mathematics fix:
+
+  * special cases that reduce to a library routine (scipy's Euclidean vector
+    quantizer and k-means, numpy's weighted average and sorts),
+  * closed forms and optimality conditions (the weighted mean is the exact
+    minimizer of the weighted objective for fixed assignments),
+  * invariants (positive rescaling of the Hessian diagonal, RMS of the
+    bi-normalized matrix, the objective identity on the reconstruction),
+  * degenerate cases (one centroid per sub-vector, every weight salient),
+  * brute force on tiny inputs.
+
+The same pins run against deliberately broken copies of the oracle
+(test_oracle_mutants.py), which shows that a plausible mistake anywhere in
+it fails at least one of them.
+"""
+import warnings
+
+import numpy as np
+import scipy.cluster.vq as scvq
+from scipy.spatial.distance import cdist
+
+import oracle as O
+
+
+def _case(seed, M, N, scale=0.02, nu=4.0, n_ch=2, gain=20.0, T=64):
+    g = np.random.default_rng([7, seed])
+    W = (scale * g.standard_t(nu, size=(M, N))).astype(np.float32)
+    X = g.standard_normal((T, N))
+    ch = g.choice(N, min(n_ch, N), replace=False)
+    X[:, ch] *= gain
+    h = (X * X).sum(0).astype(np.float32)
+    return W, h, g
+
+
+def _scores(W, h):
+    # the salience score of the HAS-VQ abstract's decoupling: second-order
+    # sensitivity of one weight, h_j * w_ij^2 (fp32: square, then scale)
+    return np.float32(h)[None, :] * (W * W)
+
+
+# --------------------------------------------------------------------------
+def pin_select_characterization(lib):
+    """Top-nnz by (score desc, linear index asc) is the unique set with:
+    exactly nnz members, every member scoring >= every non-member, and at the
+    threshold score the members holding the smallest linear indices.  Checked
+    on a random case and on all-equal scores (pure index order)."""
+    for (M, N, p, seed) in [(40, 24, 0.05, 1), (17, 32, 0.3, 2)]:
+        W, h, _ = _case(seed, M, N)
+        nz = O.nnz(M, N, p, lib)
+        assert nz == int(np.floor(p * M * N))
+        rp, col, val, keep = O.select(W, h, nz, lib)
+        s = _scores(W, h)
+        sel = keep == 0
+        assert sel.sum() == nz
+        if 0 < nz < M * N:
+            tau_in = s[sel].min()
+            tau_out = s[~sel].max()
+            assert tau_in >= tau_out
+            if tau_in == tau_out:
+                lin = np.arange(M * N).reshape(M, N)
+                assert lin[sel & (s == tau_in)].max() < lin[~sel & (s == tau_in)].min()
+        # CSR structure: row pointers, ascending columns, exact values
+        assert rp[0] == 0 and rp[-1] == nz and np.all(np.diff(rp) >= 0)
+        for i in range(M):
+            cs = col[rp[i]:rp[i + 1]]
+            assert np.all(np.diff(cs) > 0)
+            assert np.all(sel[i, cs])
+            assert np.array_equal(val[rp[i]:rp[i + 1]].view(np.uint32), W[i, cs].view(np.uint32))
+        assert np.array_equal(np.diff(rp), sel.sum(1))
+    # all scores equal: the first nnz linear positions
+    M, N = 6, 16
+    W = np.full((M, N), 0.5, np.float32)
+    h = np.ones(N, np.float32)
+    rp, col, val, keep = O.select(W, h, 20, lib)
+    assert np.array_equal(np.flatnonzero(keep.ravel() == 0), np.arange(20))
+
+
+def pin_select_brute_force(lib):
+    """Brute force on a tiny case through numpy's lexicographic sort."""
+    W, h, _ = _case(11, 12, 16, n_ch=3)
+    s = _scores(W, h).ravel()
+    order = np.lexsort((np.arange(s.size), -s.astype(np.float64)))
+    for nz in [0, 1, 7, 50, 191, 192]:
+        _, _, _, keep = O.select(W, h, nz, lib)
+        assert set(np.flatnonzero(keep.ravel() == 0)) == set(order[:nz].tolist())
+
+
+# --------------------------------------------------------------------------
+def pin_binorm_invariants(lib):
+    """Rows of W / r and columns of W' have unit RMS (fp32 rounding); r c W'
+    gives back W; the folded weights keep the original-space objective:
+    sum h_j (W - r c V)^2 == sum hcol_j rho_i (W' - V)^2 for any V."""
+    W, h, g = _case(3, 24, 40)
+    W[5, :] = 0.0  # a zero row takes scale 1
+    Wp, r, c, hcol, rho = O.binorm(W, h, lib)
+    assert r[5] == 1.0
+    Wt = W.astype(np.float64) / r[:, None]
+    rows = np.sqrt((Wt ** 2).mean(1))
+    assert np.allclose(np.delete(rows, 5), 1.0, rtol=1e-6)
+    cols = np.sqrt((Wp.astype(np.float64) ** 2).mean(0))
+    assert np.allclose(cols, 1.0, rtol=1e-6)
+    back = Wp.astype(np.float64) * c[None, :] * r[:, None]
+    assert np.allclose(back, W, rtol=1e-6, atol=0)
+    assert np.allclose(hcol, h.astype(np.float64) * c.astype(np.float64) ** 2, rtol=1e-7)
+    assert np.allclose(rho, r.astype(np.float64) ** 2, rtol=1e-7)
+    V = Wp + 0.1 * g.standard_normal(Wp.shape).astype(np.float32)
+    lhs = (h[None, :].astype(np.float64) * (W - r[:, None].astype(np.float64) * c[None, :] * V) ** 2).sum()
+    rhs = (hcol[None, :].astype(np.float64) * rho[:, None] * (Wp.astype(np.float64) - V) ** 2).sum()
+    assert abs(lhs - rhs) <= 1e-5 * rhs
+
+
+# --------------------------------------------------------------------------
+def pin_init_walk(lib):
+    """Seeding takes the first K bitwise-distinct sub-vectors in permutation
+    order, as exact copies; repeats are skipped; too few distinct -> short."""
+    g = np.random.default_rng(5)
+    d = 4
+    base = g.standard_normal((6, d)).astype(np.float32)
+    X = base[[0, 1, 0, 2, 1, 3, 3, 4, 5, 0]]          # repeats at 2, 4, 6, 9
+    perm = np.arange(10, dtype=np.int32)
+    C, taken = O.init(X, d, perm, 6, lib)
+    assert taken == 6
+    assert np.array_equal(C.view(np.uint32), base[[0, 1, 2, 3, 4, 5]].view(np.uint32))
+    perm = np.array([9, 8, 7, 6, 5, 4, 3, 2, 1, 0], np.int32)
+    C, taken = O.init(X, d, perm, 4, lib)
+    assert taken == 4
+    assert np.array_equal(C.view(np.uint32), X[[9, 8, 7, 6]].view(np.uint32))
+    C, taken = O.init(np.ones((50, d), np.float32), d, np.arange(50, dtype=np.int32), 3, lib)
+    assert taken == 1
+    # -0.0 and +0.0 are distinct bit patterns
+    Z = np.array([[0.0, 0, 0, 0], [-0.0, 0, 0, 0]], np.float32)
+    C, taken = O.init(Z, d, np.arange(2, dtype=np.int32), 2, lib)
+    assert taken == 2
+
+
+# --------------------------------------------------------------------------
+def pin_assign_euclidean_special_case(lib):
+    """h = 1, no mask, no row weight: the weighted search is Q_V of the VPTQ
+    page's core algorithm, Euclidean nearest centroid -> scipy's vq."""
+    g = np.random.default_rng(21)
+    M, N, d, K = 16, 32, 8, 37
+    X = g.standard_normal((M, N)).astype(np.float32)
+    C = g.standard_normal((K, d)).astype(np.float32)
+    idx, dist = O.assign(X, np.ones(N, np.float32), None, None, d, C, lib=lib)
+    ref, rd = scvq.vq(X.reshape(-1, d).astype(np.float64), C.astype(np.float64))
+    assert np.array_equal(idx, ref)
+    assert np.allclose(dist, rd ** 2, rtol=1e-12)
+
+
+def pin_assign_weighted_reduction(lib):
+    """With per-element weights, D(s,k) is the squared Euclidean distance
+    after scaling both sides by sqrt(omega_s); masked elements drop out.
+    Checked per sub-vector against scipy's cdist, with several column blocks,
+    a row weight and a mask; plus invariances (h -> 3h, centroid order)."""
+    W, h, g = _case(9, 12, 40, n_ch=4)
+    M, N = W.shape
+    d, K = 8, 29
+    C = (0.02 * g.standard_t(4, size=(K, d))).astype(np.float32)
+    rho = g.uniform(0.5, 2.0, M).astype(np.float32)
+    keep = (g.random((M, N)) > 0.15).astype(np.uint8)
+    keep[3, 8:16] = 0                    # one fully masked sub-vector
+    idx, dist = O.assign(W, h, rho, keep, d, C, lib=lib)
+    nb = N // d
+    for s in range(M * nb):
+        i, b = divmod(s, nb)
+        om = h[b * d:(b + 1) * d].astype(np.float64) * float(rho[i]) * keep[i, b * d:(b + 1) * d]
+        sq = np.sqrt(om)
+        dd = cdist((sq * W[i, b * d:(b + 1) * d])[None, :], sq[None, :] * C.astype(np.float64),
+                   "sqeuclidean")[0]
+        if s == 3 * nb + 1:
+            assert np.all(dd == 0) and idx[s] == 0 and dist[s] == 0
+            continue
+        assert idx[s] == int(np.argmin(dd)), s
+        assert abs(dist[s] - dd.min()) <= 1e-12 * max(dd.min(), 1e-300)
+    idx3, _ = O.assign(W, 3.0 * h, rho, keep, d, C, lib=lib)
+    assert np.array_equal(idx3, idx)
+    perm = g.permutation(K)
+    idxp, _ = O.assign(W, h, rho, keep, d, C[perm], lib=lib)
+    live = np.ones(idx.size, bool)
+    live[3 * nb + 1] = False             # all-zero distances: tie, lowest new index
+    assert np.array_equal(perm[idxp][live], idx[live])
+
+
+def pin_assign_tie_lowest(lib):
+    """Equal distances go to the lowest centroid index."""
+    g = np.random.default_rng(4)
+    d = 8
+    C = g.standard_normal((10, d)).astype(np.float32)
+    C[7] = C[2]
+    X = C[[2, 7, 2, 5]].reshape(1, -1)
+    idx, _ = O.assign(X, np.ones(4 * d, np.float32), None, None, d, C, lib=lib)
+    assert list(idx) == [2, 2, 2, 5]
+
+
+def pin_assign_subset(lib):
+    """Assigning a listed subset gives the same answers as the full pass."""
+    W, h, g = _case(13, 10, 24)
+    C = (0.02 * g.standard_t(4, size=(9, 8))).astype(np.float32)
+    full, fd = O.assign(W, h, None, None, 8, C, lib=lib)
+    sub = np.array([29, 0, 5, 17, 5], np.int64)
+    part, pd = O.assign(W, h, None, None, 8, C, subset=sub, lib=lib)
+    assert np.array_equal(part, full[sub]) and np.array_equal(pd, fd[sub])
+
+
+# --------------------------------------------------------------------------
+def pin_update_weighted_mean(lib):
+    """The update is numpy's weighted average per (centroid, dimension) with
+    weight omega; an empty centroid or a zero weight sum keeps its old value;
+    counts are numpy's bincount; J is the objective of the input codebook
+    (equal to the sum of the assigned distances)."""
+    W, h, g = _case(17, 16, 48, n_ch=3)
+    M, N = W.shape
+    d, K = 8, 23
+    C = (0.02 * g.standard_t(4, size=(K, d))).astype(np.float32)
+    rho = g.uniform(0.5, 2.0, M).astype(np.float32)
+    keep = (g.random((M, N)) > 0.2).astype(np.uint8)
+    idx, dist = O.assign(W, h, rho, keep, d, C, lib=lib)
+    idx = idx.copy()
+    idx[idx == 4] = 3                       # centroid 4 left empty
+    idx[idx == 11] = 12                     # centroid 11: one member, fully masked
+    idx[7] = 11
+    keep2 = keep.copy()
+    i7, b7 = divmod(7, N // d)
+    keep2[i7, b7 * d:(b7 + 1) * d] = 0
+    Cn, counts, J = O.update(W, h, rho, keep2, d, idx, C, lib=lib)
+    assert np.array_equal(counts, np.bincount(idx, minlength=K))
+    X = W.reshape(-1, d).astype(np.float64)
+    nb = N // d
+    om = (h.reshape(nb, d)[None, :, :].astype(np.float64) * rho[:, None, None]
+          * keep2.reshape(M, nb, d)).reshape(-1, d)
+    for k in range(K):
+        mem = idx == k
+        for t in range(d):
+            wsum = om[mem, t].sum()
+            if wsum > 0:
+                want = np.float32(np.average(X[mem, t], weights=om[mem, t]))
+                assert abs(float(Cn[k, t]) - float(want)) <= 2e-7 * abs(float(want)) + 1e-30, (k, t)
+            else:
+                assert Cn[k, t] == C[k, t]
+    assert np.array_equal(Cn[4], C[4]) and np.array_equal(Cn[11], C[11])
+    Jref = (om * (X - C[idx].astype(np.float64)) ** 2).sum()
+    assert abs(J - Jref) <= 1e-12 * Jref
+
+
+def pin_update_optimality(lib):
+    """Closed form: for fixed assignments the update is the exact minimizer of
+    J, so moving any centroid component by +-delta never lowers J."""
+    W, h, g = _case(19, 8, 32)
+    d, K = 8, 6
+    C = (0.02 * g.standard_t(4, size=(K, d))).astype(np.float32)
+    idx, _ = O.assign(W, h, None, None, d, C, lib=lib)
+    Cn, _, _ = O.update(W, h, None, None, d, idx, C, lib=lib)
+    J0 = O.objective(W, h, None, None, d, Cn, idx, lib=lib)
+    for k in range(K):
+        for t in range(d):
+            for delta in (1e-3, -1e-3):
+                Cp = Cn.copy()
+                Cp[k, t] += np.float32(delta * max(abs(float(Cn[k, t])), 1e-3))
+                assert O.objective(W, h, None, None, d, Cp, idx, lib=lib) >= J0 * (1 - 1e-12)
+
+
+# --------------------------------------------------------------------------
+def pin_lloyd_matches_scipy_kmeans(lib):
+    """h = 1, no mask, p = 0, one stage: T Lloyd iterations from a given
+    codebook are scipy's kmeans2(minit='matrix', iter=T); the returned indices
+    are scipy's vq of the final codebook (textbook Lloyd, as cited for K-means
+    on the SCVQ page)."""
+    g = np.random.default_rng(31)
+    M, N, d, K, T = 64, 32, 8, 12, 6
+    W = g.standard_normal((M, N)).astype(np.float32)
+    perm = g.permutation(M * N // d).astype(np.int32)
+    out = O.fit(W, np.ones(N, np.float32), d, K, T, 0, 0, 0.0, perm1=perm, lib=lib)
+    X = W.reshape(-1, d).astype(np.float64)
+    C0 = X[perm[:K]]
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        cb, _ = scvq.kmeans2(X, C0.copy(), iter=T, minit="matrix")
+    assert np.allclose(out["C1"], cb, rtol=1e-5, atol=1e-6)
+    lab, _ = scvq.vq(X, out["C1"].astype(np.float64))
+    assert np.array_equal(out["idx1"], lab)
+
+
+def pin_weighted_lloyd_reduces_to_scaled_kmeans(lib):
+    """One column block (N = d), no row weight, no mask: weighted K-means on x
+    with per-dimension weights h equals plain K-means on sqrt(h) * x, with
+    centroids mapped back by 1/sqrt(h)."""
+    g = np.random.default_rng(37)
+    M, d, K, T = 300, 8, 10, 5
+    W = g.standard_normal((M, d)).astype(np.float32)
+    h = g.uniform(0.2, 5.0, d).astype(np.float32)
+    perm = g.permutation(M).astype(np.int32)
+    out = O.fit(W, h, d, K, T, 0, 0, 0.0, perm1=perm, lib=lib)
+    sq = np.sqrt(h.astype(np.float64))
+    Y = W.astype(np.float64) * sq
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        cb, _ = scvq.kmeans2(Y, Y[perm[:K]].copy(), iter=T, minit="matrix")
+    assert np.allclose(out["C1"], cb / sq, rtol=1e-5, atol=1e-6)
+
+
+def pin_fit_monotone_and_identity(lib):
+    """Lloyd never raises J (both stages), and the last stage's final J equals
+    the weighted error of the reconstructed matrix over the kept positions:
+    sum_ij h_j keep_ij (W - What)_ij^2 (a real-arithmetic identity), while
+    What == W bitwise at every salient position."""
+    for binorm in (False, True):
+        W, h, g = _case(41 + binorm, 32, 64, n_ch=3)
+        M, N = W.shape
+        d, K1, T1, K2, T2 = 8, 24, 6, 8, 4
+        perm1 = g.permutation(M * N // d).astype(np.int32)
+        perm2 = g.permutation(M * N // d).astype(np.int32)
+        out = O.fit(W, h, d, K1, T1, K2, T2, 0.02, binorm=binorm, perm1=perm1, perm2=perm2, lib=lib)
+        J = out["J"]
+        for a, b in [(0, T1 + 1), (T1 + 1, T1 + T2 + 2)]:
+            seg = J[a:b]
+            assert np.all(seg[1:] <= seg[:-1] * (1 + 1e-12)), seg
+        keep = out["keep"]
+        err = (h[None, :].astype(np.float64) * keep * (W.astype(np.float64) - out["What"]) ** 2).sum()
+        assert abs(err - J[-1]) <= 2e-5 * J[-1], (err, J[-1])
+        sel = keep == 0
+        assert np.array_equal(out["What"][sel].view(np.uint32), W[sel].view(np.uint32))
+        assert sel.sum() == out["nnz"]
+
+
+def pin_degenerate_cases(lib):
+    """K = n_sub with every sub-vector distinct: J = 0 and What == W bitwise.
+    p = 1: every weight is held exactly, What == W and J = 0.  Residual
+    decode: without scales, What = C1[i1] + C2[i2] at every kept position."""
+    g = np.random.default_rng(43)
+    M, N, d = 8, 16, 8
+    W = (0.02 * g.standard_t(4, size=(M, N))).astype(np.float32)
+    h = g.uniform(1, 5, N).astype(np.float32)
+    n_sub = M * N // d
+    perm = g.permutation(n_sub).astype(np.int32)
+    out = O.fit(W, h, d, n_sub, 3, 0, 0, 0.0, perm1=perm, lib=lib)
+    assert np.all(out["J"] == 0)
+    assert np.array_equal(out["What"].view(np.uint32), W.view(np.uint32))
+    out = O.fit(W, h, d, 4, 3, 2, 2, 1.0, perm1=perm, perm2=perm, lib=lib)
+    assert np.all(out["J"] == 0)
+    assert np.array_equal(out["What"].view(np.uint32), W.view(np.uint32))
+    W2, h2, g2 = _case(47, 16, 32)
+    p1 = g2.permutation(64).astype(np.int32)
+    out = O.fit(W2, h2, 8, 10, 3, 6, 3, 0.0, perm1=p1, perm2=p1, lib=lib)
+    dec = out["C1"][out["idx1"]] + out["C2"][out["idx2"]]
+    assert np.array_equal(out["What"].reshape(-1, 8).view(np.uint32), dec.view(np.uint32))
+
+
+def pin_fit_residual_seed(lib):
+    """The residual stage seeds its codebook from the residual of the first
+    stage (VPTQ page, "Residual Vector Quantization": the second codebook
+    quantizes v - Q(v)): with no residual iterations, C2 holds the first K2
+    distinct residual sub-vectors in perm2 order, bitwise."""
+    W, h, g = _case(53, 16, 32)
+    n_sub = 16 * 32 // 8
+    p1 = g.permutation(n_sub).astype(np.int32)
+    p2 = g.permutation(n_sub).astype(np.int32)
+    out = O.fit(W, h, 8, 12, 2, 5, 0, 0.0, perm1=p1, perm2=p2, lib=lib)
+    R = W.reshape(-1, 8) - out["C1"][out["idx1"]]
+    seen, rows = set(), []
+    for s in p2:
+        key = R[s].tobytes()
+        if key not in seen:
+            seen.add(key)
+            rows.append(R[s])
+        if len(rows) == 5:
+            break
+    assert np.array_equal(out["C2"].view(np.uint32), np.array(rows).view(np.uint32))
+
+
+def pin_bits_worked_example(lib):
+    """The VPTQ page's compression-ratio example (golden fixture)."""
+    import json
+    import os
+    here = os.path.dirname(os.path.abspath(__file__))
+    with open(os.path.join(here, "golden", "vptq_compression_example.json")) as f:
+        ex = json.load(f)
+    n = ex["matrix"][0] * ex["matrix"][1]
+    cr = O.compression_ratio_single(n, ex["vector_length"], ex["centroids"],
+                                    ex["original_bits"], ex["codebook_bits"])
+    assert round(cr, ex["printed_ratio_decimals"]) == ex["printed_compression_ratio"]
+    bpw = O.bits_per_weight(ex["matrix"][0], ex["matrix"][1], ex["vector_length"],
+                            ex["centroids"], 0, 0, cb_bits=ex["codebook_bits"])
+    assert round(bpw, ex["printed_bpw_decimals"]) == ex["printed_bits_per_weight"]
+    assert abs(bpw - ex["original_bits"] / cr) < 1e-12
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
