@@ -1,0 +1,283 @@
+// Bandwidth-bound passes: bi-normalization, residual, reconstruction and the
+// objective.  Every float64 reduction here runs in a fixed order (per-thread
+// strided sums, then a fixed tree), so results are bitwise reproducible.
+#include "vq_internal.h"
+
+namespace vq {
+namespace {
+
+constexpr int kBlock = 256;
+
+// Fixed-order tree reduction of one double per thread (blockDim == 256).
+__device__ inline double block_sum_f64(double v, double* sh)
+{
+    sh[threadIdx.x] = v;
+    __syncthreads();
+    for (int w = kBlock / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) sh[threadIdx.x] = sh[threadIdx.x] + sh[threadIdx.x + w];
+        __syncthreads();
+    }
+    double r = sh[0];
+    __syncthreads();
+    return r;
+}
+
+// ---- bi-normalization (SCVQ summary: rows and columns bi-normalized) ----
+// r_i = sqrt(sum_j W_ij^2 / N) in float64, 1 when zero; rho_i = r_i^2.
+__global__ __launch_bounds__(kBlock) void k_row_rms(const float* __restrict__ W, int64_t N,
+                                                    float* __restrict__ r, float* __restrict__ rho)
+{
+    __shared__ double sh[kBlock];
+    const int64_t i = blockIdx.x;
+    const float* row = W + i * N;
+    double acc = 0.0;
+    for (int64_t j = threadIdx.x; j < N; j += kBlock) {
+        const double w = (double)row[j];
+        acc = acc + w * w;
+    }
+    const double tot = block_sum_f64(acc, sh);
+    if (threadIdx.x == 0) {
+        float ri = (float)sqrt(tot / (double)N);
+        if (ri == 0.0f) ri = 1.0f;
+        r[i] = ri;
+        const double rd = (double)ri;
+        rho[i] = (float)(rd * rd);
+    }
+}
+
+// Partial column sums of (W_ij / r_i)^2 over one group of rows.
+// Block = 64 columns x 4 row lanes; grid = (column chunks, row groups).
+__global__ __launch_bounds__(kBlock) void k_col_partial(const float* __restrict__ W,
+                                                        const float* __restrict__ r, int64_t M,
+                                                        int64_t N, int64_t rows_per_group,
+                                                        double* __restrict__ part)
+{
+    __shared__ double sh[4][64];
+    const int cl = threadIdx.x & 63;
+    const int rl = threadIdx.x >> 6;
+    const int64_t j = (int64_t)blockIdx.x * 64 + cl;
+    const int64_t i0 = (int64_t)blockIdx.y * rows_per_group;
+    const int64_t i1 = i0 + rows_per_group < M ? i0 + rows_per_group : M;
+    double acc = 0.0;
+    if (j < N) {
+        for (int64_t i = i0 + rl; i < i1; i += 4) {
+            const float wt = W[i * N + j] / r[i];
+            const double w = (double)wt;
+            acc = acc + w * w;
+        }
+    }
+    sh[rl][cl] = acc;
+    __syncthreads();
+    if (rl == 0 && j < N) {
+        const double tot = ((sh[0][cl] + sh[1][cl]) + sh[2][cl]) + sh[3][cl];
+        part[(int64_t)blockIdx.y * N + j] = tot;
+    }
+}
+
+// c_j = sqrt(sum over row groups / M) (groups added in order), 1 when zero;
+// hcol_j = h_j c_j^2 in float64.
+__global__ void k_col_finish(const double* __restrict__ part, int groups, int64_t M, int64_t N,
+                             const float* __restrict__ h, float* __restrict__ c,
+                             float* __restrict__ hcol)
+{
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= N) return;
+    double tot = 0.0;
+    for (int g = 0; g < groups; ++g) tot = tot + part[(int64_t)g * N + j];
+    float cj = (float)sqrt(tot / (double)M);
+    if (cj == 0.0f) cj = 1.0f;
+    c[j] = cj;
+    const double cd = (double)cj;
+    hcol[j] = (float)((double)h[j] * cd * cd);
+}
+
+// W'_ij = (W_ij / r_i) / c_j in float32.
+__global__ void k_binorm_apply(const float* __restrict__ W, const float* __restrict__ r,
+                               const float* __restrict__ c, int64_t M, int64_t N,
+                               float* __restrict__ Wp)
+{
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= M * N) return;
+    const int64_t i = e / N;
+    const int64_t j = e - i * N;
+    const float wt = W[e] / r[i];
+    Wp[e] = wt / c[j];
+}
+
+// ---- residual (VPTQ page, "Residual Vector Quantization") ---------------
+// An index >= K (a caller error) yields NaN instead of an out-of-range read.
+__global__ void k_residual(const float* __restrict__ X, int64_t total, int d,
+                           const float* __restrict__ C, int K, const uint16_t* __restrict__ idx,
+                           float* __restrict__ R)
+{
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= total) return;
+    const int64_t s = e / d;
+    const int t = (int)(e - s * d);
+    const int k = idx[s];
+    R[e] = k < K ? X[e] - C[(size_t)k * d + t] : __builtin_nanf("");
+}
+
+// ---- reconstruction ------------------------------------------------------
+// One thread per sub-vector: ((C1[i1] + C2[i2]) * c_j) * r_i, float32.
+// An index >= K (a caller error) decodes to NaN instead of an out-of-range read.
+__global__ void k_decode(int64_t n_sub, int64_t nb, int d, const float* __restrict__ C1, int K1,
+                         const uint16_t* __restrict__ idx1, const float* __restrict__ C2, int K2,
+                         const uint16_t* __restrict__ idx2, const float* __restrict__ rs,
+                         const float* __restrict__ cs, float* __restrict__ Wh)
+{
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= n_sub) return;
+    const int64_t i = s / nb;
+    const int64_t b = s - i * nb;
+    float* out = Wh + s * d;
+    const int k1 = idx1[s];
+    const int k2 = C2 ? idx2[s] : 0;
+    if (k1 >= K1 || (C2 && k2 >= K2)) {
+        for (int t = 0; t < d; ++t) out[t] = __builtin_nanf("");
+        return;
+    }
+    const float* c1 = C1 + (size_t)k1 * d;
+    const float* c2 = C2 ? C2 + (size_t)k2 * d : nullptr;
+    const float ri = rs ? rs[i] : 1.0f;
+    for (int t = 0; t < d; ++t) {
+        float v = c1[t];
+        if (c2) v = v + c2[t];
+        if (cs) v = v * cs[b * d + t];
+        if (rs) v = v * ri;
+        out[t] = v;
+    }
+}
+
+// The exact salient values overwrite their positions (HAS-VQ abstract:
+// exact reconstruction of the decoupled weights).  One thread per row.
+__global__ void k_sparse_overwrite(int64_t M, int64_t N, const int32_t* __restrict__ row_ptr,
+                                   const int32_t* __restrict__ col, const float* __restrict__ val,
+                                   float* __restrict__ Wh)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= M) return;
+    for (int32_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+        const int32_t j = col[e];
+        if (j >= 0 && j < N) Wh[i * N + j] = val[e];   // an out-of-range column is skipped
+    }
+}
+
+// ---- objective: per-block float64 partial sums of D(s, idx[s]) ----------
+__global__ __launch_bounds__(kBlock) void k_objective_partial(
+    const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
+    const uint8_t* __restrict__ mask, int64_t n_sub, int64_t nb, int d,
+    const float* __restrict__ C, int K, const uint16_t* __restrict__ idx, double* __restrict__ part)
+{
+    __shared__ double sh[kBlock];
+    const int64_t s = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    double D = 0.0;
+    if (s < n_sub && idx[s] >= K) D = __builtin_nan("");
+    else if (s < n_sub) {
+        const int64_t i = s / nb;
+        const int64_t b = s - i * nb;
+        const unsigned mb = mask ? mask[s] : 0u;
+        const float* c = C + (size_t)idx[s] * d;
+        for (int t = 0; t < d; ++t) {
+            double w = (double)hcol[b * d + t];
+            if (rho) w = w * (double)rho[i];
+            if ((mb >> t) & 1u) w = 0.0;
+            const double diff = (double)X[s * d + t] - (double)c[t];
+            const double sq = diff * diff;
+            D = D + w * sq;
+        }
+    }
+    const double tot = block_sum_f64(D, sh);
+    if (threadIdx.x == 0) part[blockIdx.x] = tot;
+}
+
+// One block adds the partials: strided per-thread sums, then a fixed tree.
+__global__ __launch_bounds__(kBlock) void k_sum_partials(const double* __restrict__ part, int64_t n,
+                                                         double* __restrict__ out)
+{
+    __shared__ double sh[kBlock];
+    double acc = 0.0;
+    for (int64_t e = threadIdx.x; e < n; e += kBlock) acc = acc + part[e];
+    const double tot = block_sum_f64(acc, sh);
+    if (threadIdx.x == 0) *out = tot;
+}
+
+constexpr int64_t kColChunk = 64;
+constexpr int64_t kRowGroups = 32;
+
+}  // namespace
+
+size_t ws_binorm(int64_t M, int64_t N)
+{
+    (void)M;
+    return align_up((size_t)kRowGroups * N * sizeof(double));
+}
+
+size_t ws_objective(int64_t n_sub) { return align_up((size_t)grid_for(n_sub, kBlock) * sizeof(double)); }
+
+vq_status binorm_launch(const float* W, const float* h, int64_t M, int64_t N, float* Wp, float* r,
+                        float* c, float* hcol, float* rho, void* ws, size_t ws_bytes, hipStream_t st)
+{
+    Carver cv(ws, ws_bytes);
+    double* part = cv.take<double>((size_t)kRowGroups * N);
+    if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_binorm: workspace too small");
+    hipLaunchKernelGGL(k_row_rms, dim3((unsigned)M), dim3(kBlock), 0, st, W, N, r, rho);
+    VQ_LAUNCHED("k_row_rms");
+    const int64_t rpg = (M + kRowGroups - 1) / kRowGroups;
+    hipLaunchKernelGGL(k_col_partial, dim3(grid_for(N, kColChunk), (unsigned)kRowGroups), dim3(kBlock),
+                       0, st, W, r, M, N, rpg, part);
+    VQ_LAUNCHED("k_col_partial");
+    hipLaunchKernelGGL(k_col_finish, dim3(grid_for(N, kBlock)), dim3(kBlock), 0, st, part,
+                       (int)kRowGroups, M, N, h, c, hcol);
+    VQ_LAUNCHED("k_col_finish");
+    hipLaunchKernelGGL(k_binorm_apply, dim3(grid_for(M * N, kBlock)), dim3(kBlock), 0, st, W, r, c, M,
+                       N, Wp);
+    VQ_LAUNCHED("k_binorm_apply");
+    return VQ_OK;
+}
+
+vq_status residual_launch(const float* X, int64_t M, int64_t N, int d, const float* C, int K,
+                          const uint16_t* idx, float* R, hipStream_t st)
+{
+    const int64_t total = M * N;
+    hipLaunchKernelGGL(k_residual, dim3(grid_for(total, kBlock)), dim3(kBlock), 0, st, X, total, d, C, K,
+                       idx, R);
+    VQ_LAUNCHED("k_residual");
+    return VQ_OK;
+}
+
+vq_status reconstruct_launch(int64_t M, int64_t N, int d, const float* C1, int K1, const uint16_t* idx1,
+                             const float* C2, int K2, const uint16_t* idx2, const float* rs,
+                             const float* cs, const int32_t* row_ptr, const int32_t* col,
+                             const float* val, float* Wh, hipStream_t st)
+{
+    const int64_t n_sub = M * N / d;
+    hipLaunchKernelGGL(k_decode, dim3(grid_for(n_sub, kBlock)), dim3(kBlock), 0, st, n_sub, N / d, d,
+                       C1, K1, idx1, C2, K2, idx2, rs, cs, Wh);
+    VQ_LAUNCHED("k_decode");
+    if (row_ptr) {
+        hipLaunchKernelGGL(k_sparse_overwrite, dim3(grid_for(M, kBlock)), dim3(kBlock), 0, st, M, N,
+                           row_ptr, col, val, Wh);
+        VQ_LAUNCHED("k_sparse_overwrite");
+    }
+    return VQ_OK;
+}
+
+vq_status objective_launch(const float* X, const float* hcol, const float* rho, const uint8_t* mask,
+                           int64_t M, int64_t N, int d, const float* C, int K, const uint16_t* idx,
+                           double* J, void* ws, size_t ws_bytes, hipStream_t st)
+{
+    const int64_t n_sub = M * N / d;
+    const unsigned nblk = grid_for(n_sub, kBlock);
+    Carver cv(ws, ws_bytes);
+    double* part = cv.take<double>(nblk);
+    if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_objective: workspace too small");
+    hipLaunchKernelGGL(k_objective_partial, dim3(nblk), dim3(kBlock), 0, st, X, hcol, rho, mask, n_sub,
+                       N / d, d, C, K, idx, part);
+    VQ_LAUNCHED("k_objective_partial");
+    hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kBlock), 0, st, part, (int64_t)nblk, J);
+    VQ_LAUNCHED("k_sum_partials");
+    return VQ_OK;
+}
+
+}  // namespace vq

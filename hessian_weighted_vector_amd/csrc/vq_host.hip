@@ -1,0 +1,452 @@
+// Host side of libvq: the C ABI entry points (argument validation, workspace
+// carving, launches), the codebook seeding walk and the whole-fit driver.
+#include "vq_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+namespace vq {
+
+// ---- errors ---------------------------------------------------------------
+namespace {
+thread_local std::string g_err;
+}
+
+void set_error(const std::string& msg) { g_err = msg; }
+
+vq_status fail(vq_status st, const std::string& msg)
+{
+    g_err = msg;
+    return st;
+}
+
+vq_status hip_fail(hipError_t e, const char* what)
+{
+    g_err = std::string(what) + ": " + hipGetErrorString(e);
+    return VQ_ERR_DEVICE;
+}
+
+// ---- launchers defined in the kernel files --------------------------------
+vq_status assign_launch(const float*, const float*, const float*, const uint8_t*, int64_t, int64_t,
+                        int, const float*, int, uint16_t*, float*, void*, size_t, hipStream_t);
+vq_status assign_flag_count(void*, size_t, int64_t, int, int*, hipStream_t);
+vq_status update_launch(const float*, const float*, const float*, const uint8_t*, int64_t, int64_t,
+                        int, const uint16_t*, int, float*, int32_t*, void*, size_t, hipStream_t);
+vq_status objective_launch(const float*, const float*, const float*, const uint8_t*, int64_t,
+                           int64_t, int, const float*, int, const uint16_t*, double*, void*, size_t,
+                           hipStream_t);
+vq_status select_launch(const float*, const float*, int64_t, int64_t, int, int64_t, int32_t*,
+                        int32_t*, float*, uint8_t*, void*, size_t, hipStream_t);
+vq_status binorm_launch(const float*, const float*, int64_t, int64_t, float*, float*, float*,
+                        float*, float*, void*, size_t, hipStream_t);
+vq_status residual_launch(const float*, int64_t, int64_t, int, const float*, int, const uint16_t*,
+                          float*, hipStream_t);
+vq_status reconstruct_launch(int64_t, int64_t, int, const float*, int, const uint16_t*, const float*, int,
+                             const uint16_t*, const float*, const float*, const int32_t*,
+                             const int32_t*, const float*, float*, hipStream_t);
+
+// ---- validation -------------------------------------------------------------
+vq_status check_shape(int64_t M, int64_t N, int d)
+{
+    if (M <= 0 || N <= 0) return fail(VQ_ERR_INVALID, "M and N must be positive");
+    if (d < 1 || d > 8) return fail(VQ_ERR_INVALID, "d must be in [1, 8]");
+    if (N % d != 0) return fail(VQ_ERR_INVALID, "N must be a multiple of d");
+    if (M > INT32_MAX || N > INT32_MAX || M * N / d > (int64_t)INT32_MAX || M * N > ((int64_t)1 << 40))
+        return fail(VQ_ERR_INVALID, "matrix too large (sub-vector count must fit int32)");
+    return VQ_OK;
+}
+
+vq_status check_K(int K, int64_t n_sub)
+{
+    if (K < 1 || K > 65536) return fail(VQ_ERR_INVALID, "K must be in [1, 65536]");
+    if ((int64_t)K > n_sub) return fail(VQ_ERR_INVALID, "K exceeds the number of sub-vectors");
+    return VQ_OK;
+}
+
+namespace {
+
+#define VQ_WS(cond, msg)                                            \
+    do {                                                          \
+        if (!(cond)) return ::vq::fail(VQ_ERR_WORKSPACE, (msg));  \
+    } while (0)
+
+#define VQ_TRY(expr)                          \
+    do {                                      \
+        vq_status vq_s_ = (expr);             \
+        if (vq_s_ != VQ_OK) return vq_s_;     \
+    } while (0)
+
+// The current device must be a gfx950; checked once per device.
+vq_status check_device()
+{
+    int dev = -1;
+    VQ_HIP(hipGetDevice(&dev));
+    static thread_local int ok_dev = -1;
+    if (ok_dev == dev) return VQ_OK;
+    hipDeviceProp_t prop;
+    VQ_HIP(hipGetDeviceProperties(&prop, dev));
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(VQ_ERR_UNSUPPORTED, std::string("libvq needs a gfx950 device, found ") + prop.gcnArchName);
+    ok_dev = dev;
+    return VQ_OK;
+}
+
+int64_t nnz_of(int64_t M, int64_t N, double p) { return (int64_t)std::floor(p * (double)(M * N)); }
+
+constexpr int64_t kInitChunkMin = 65536;
+
+int64_t init_chunk(int64_t n_sub, int K) { return std::min<int64_t>(n_sub, std::max<int64_t>(2 * (int64_t)K, kInitChunkMin)); }
+
+// Gathers the chunk's candidate sub-vectors in walk order.
+__global__ void k_gather(const float* __restrict__ X, const int32_t* __restrict__ perm, int64_t n, int d,
+                         float* __restrict__ out)
+{
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= n * d) return;
+    const int64_t q = e / d;
+    const int t = (int)(e - q * d);
+    out[e] = X[(int64_t)perm[q] * d + t];
+}
+
+uint64_t mix64(const uint32_t* w, int d)
+{
+    uint64_t hsh = 0x9E3779B97F4A7C15ull ^ (uint64_t)d;
+    for (int t = 0; t < d; ++t) {
+        hsh += w[t];
+        hsh ^= hsh >> 30;
+        hsh *= 0xBF58476D1CE4E5B9ull;
+        hsh ^= hsh >> 27;
+        hsh *= 0x94D049BB133111EBull;
+        hsh ^= hsh >> 31;
+    }
+    return hsh;
+}
+
+// The seeding walk: first K bitwise-distinct sub-vectors in perm order.
+vq_status init_walk(const float* X, int64_t n_sub, int d, const int32_t* perm, int K, float* C,
+                    void* ws, size_t ws_bytes, hipStream_t st)
+{
+    const int64_t chunk = init_chunk(n_sub, K);
+    Carver cv(ws, ws_bytes);
+    int32_t* dperm = cv.take<int32_t>(chunk);
+    float* dbuf = cv.take<float>((size_t)chunk * d);
+    if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_init: workspace too small");
+
+    std::vector<float> host((size_t)chunk * d);
+    std::vector<float> taken_rows((size_t)K * d);
+    size_t cap = 16;
+    while (cap < (size_t)K * 2 + 2) cap <<= 1;
+    std::vector<int32_t> table(cap, -1);
+    int taken = 0;
+    for (int64_t e0 = 0; e0 < n_sub && taken < K; e0 += chunk) {
+        const int64_t n = std::min<int64_t>(chunk, n_sub - e0);
+        for (int64_t q = 0; q < n; ++q)
+            if (perm[e0 + q] < 0 || perm[e0 + q] >= n_sub)
+                return fail(VQ_ERR_INVALID, "perm holds an id outside [0, n_sub)");
+        VQ_HIP(hipMemcpyAsync(dperm, perm + e0, (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice, st));
+        hipLaunchKernelGGL(k_gather, dim3(grid_for(n * d, 256)), dim3(256), 0, st, X, dperm, n, d, dbuf);
+        VQ_LAUNCHED("k_gather");
+        VQ_HIP(hipMemcpyAsync(host.data(), dbuf, (size_t)n * d * sizeof(float), hipMemcpyDeviceToHost, st));
+        VQ_HIP(hipStreamSynchronize(st));
+        for (int64_t q = 0; q < n && taken < K; ++q) {
+            const float* v = host.data() + (size_t)q * d;
+            uint32_t w[8];
+            std::memcpy(w, v, sizeof(float) * d);
+            size_t pos = (size_t)(mix64(w, d) & (cap - 1));
+            bool dup = false;
+            while (table[pos] >= 0) {
+                if (std::memcmp(taken_rows.data() + (size_t)table[pos] * d, v, sizeof(float) * d) == 0) {
+                    dup = true;
+                    break;
+                }
+                pos = (pos + 1) & (cap - 1);
+            }
+            if (dup) continue;
+            std::memcpy(taken_rows.data() + (size_t)taken * d, v, sizeof(float) * d);
+            table[pos] = taken++;
+        }
+    }
+    if (taken < K)
+        return fail(VQ_ERR_INIT, "only " + std::to_string(taken) + " distinct sub-vectors, K = " + std::to_string(K));
+    VQ_HIP(hipMemcpyAsync(C, taken_rows.data(), (size_t)K * d * sizeof(float), hipMemcpyHostToDevice, st));
+    VQ_HIP(hipStreamSynchronize(st));
+    return VQ_OK;
+}
+
+size_t ws_update_total(int64_t n_sub, int K) { return ws_objective(n_sub) + ws_update(n_sub, K); }
+
+// Objective then update, each with its own slice of the workspace.
+vq_status update_with_J(const float* X, const float* hcol, const float* rho, const uint8_t* mask, int64_t M,
+                        int64_t N, int d, const uint16_t* idx, int K, float* C, int32_t* counts,
+                        double* J, void* ws, size_t ws_bytes, hipStream_t st)
+{
+    const int64_t n_sub = M * N / d;
+    const size_t wo = ws_objective(n_sub);
+    if (ws_bytes < wo) return fail(VQ_ERR_WORKSPACE, "vq_update: workspace too small");
+    if (J) VQ_TRY(objective_launch(X, hcol, rho, mask, M, N, d, C, K, idx, J, ws, wo, st));
+    return update_launch(X, hcol, rho, mask, M, N, d, idx, K, C, counts, static_cast<char*>(ws) + wo,
+                         ws_bytes - wo, st);
+}
+
+// One Lloyd stage: T x (assign, objective, update), final assign, objective.
+vq_status lloyd_stage(const float* X, const float* hcol, const float* rho, const uint8_t* mask, int64_t M,
+                      int64_t N, int d, float* C, int K, int T, uint16_t* idx, double* Jd, void* ws,
+                      size_t ws_bytes, hipStream_t st)
+{
+    for (int t = 0; t < T; ++t) {
+        VQ_TRY(assign_launch(X, hcol, rho, mask, M, N, d, C, K, idx, nullptr, ws, ws_bytes, st));
+        VQ_TRY(update_with_J(X, hcol, rho, mask, M, N, d, idx, K, C, nullptr, Jd + t, ws, ws_bytes, st));
+    }
+    VQ_TRY(assign_launch(X, hcol, rho, mask, M, N, d, C, K, idx, nullptr, ws, ws_bytes, st));
+    return objective_launch(X, hcol, rho, mask, M, N, d, C, K, idx, Jd + T, ws, ws_bytes, st);
+}
+
+size_t ws_steps(int64_t M, int64_t N, int d, int K1, int K2)
+{
+    const int64_t n_sub = M * N / d;
+    const int Kmax = std::max(K1, K2);
+    size_t w = ws_assign(n_sub, Kmax);
+    w = std::max(w, ws_update_total(n_sub, Kmax));
+    w = std::max(w, ws_select(M, N));
+    w = std::max(w, ws_binorm(M, N));
+    w = std::max(w, ws_init(n_sub, Kmax, d));
+    return w;
+}
+
+}  // namespace
+
+size_t ws_init(int64_t n_sub, int K, int d)
+{
+    const int64_t chunk = init_chunk(n_sub, K);
+    return align_up((size_t)chunk * sizeof(int32_t)) + align_up((size_t)chunk * d * sizeof(float));
+}
+
+}  // namespace vq
+
+using namespace vq;
+
+// ============================================================================
+extern "C" {
+
+const char* vq_version(void) { return "libvq 0.1.0 (gfx950)"; }
+
+const char* vq_last_error(void) { return g_err.c_str(); }
+
+size_t vq_workspace_bytes(int64_t M, int64_t N, int d, int K1, int K2, int64_t nnz)
+{
+    (void)nnz;
+    if (M <= 0 || N <= 0 || d < 1 || d > 8 || N % d) return 0;
+    const int64_t n_sub = M * N / d;
+    const int iters_guess = 256;   // J history slots reserved in the workspace
+    size_t w = ws_steps(M, N, d, std::max(K1, 1), std::max(K2, 1));
+    if (K2 > 0) w += align_up((size_t)M * N * sizeof(float));
+    w += align_up(sizeof(double) * iters_guess);
+    (void)n_sub;
+    return w;
+}
+
+vq_status vq_sparse_select(const float* W, const float* h, int64_t M, int64_t N, int d, int64_t nnz,
+                           int32_t* row_ptr, int32_t* col, float* val, uint8_t* mask, void* ws,
+                           size_t ws_bytes, void* stream)
+{
+    VQ_TRY(check_shape(M, N, d));
+    VQ_CHECK(W && h && row_ptr && mask, "vq_sparse_select: null pointer");
+    VQ_CHECK(nnz >= 0 && nnz <= M * N && nnz <= INT32_MAX, "vq_sparse_select: nnz out of range");
+    VQ_CHECK(nnz == 0 || (col && val), "vq_sparse_select: col/val are null");
+    VQ_WS(ws_bytes >= ws_select(M, N) && ws, "vq_sparse_select: workspace too small");
+    VQ_TRY(check_device());
+    return select_launch(W, h, M, N, d, nnz, row_ptr, col, val, mask, ws, ws_bytes, as_stream(stream));
+}
+
+vq_status vq_binorm(const float* W, const float* h, int64_t M, int64_t N, float* Wp, float* r, float* c,
+                    float* hcol, float* rho, void* ws, size_t ws_bytes, void* stream)
+{
+    VQ_TRY(check_shape(M, N, 1));
+    VQ_CHECK(W && h && Wp && r && c && hcol && rho, "vq_binorm: null pointer");
+    VQ_CHECK(Wp != W, "vq_binorm: Wp may not alias W");
+    VQ_WS(ws && ws_bytes >= ws_binorm(M, N), "vq_binorm: workspace too small");
+    VQ_TRY(check_device());
+    return binorm_launch(W, h, M, N, Wp, r, c, hcol, rho, ws, ws_bytes, as_stream(stream));
+}
+
+vq_status vq_init(const float* X, int64_t M, int64_t N, int d, const int32_t* perm, int K, float* C,
+                  void* ws, size_t ws_bytes, void* stream)
+{
+    VQ_TRY(check_shape(M, N, d));
+    const int64_t n_sub = M * N / d;
+    VQ_TRY(check_K(K, n_sub));
+    VQ_CHECK(X && perm && C, "vq_init: null pointer");
+    VQ_WS(ws && ws_bytes >= ws_init(n_sub, K, d), "vq_init: workspace too small");
+    VQ_TRY(check_device());
+    return init_walk(X, n_sub, d, perm, K, C, ws, ws_bytes, as_stream(stream));
+}
+
+vq_status vq_assign(const float* X, const float* hcol, const float* rho, const uint8_t* mask, int64_t M,
+                    int64_t N, int d, const float* C, int K, uint16_t* idx, float* dist, void* ws,
+                    size_t ws_bytes, void* stream)
+{
+    VQ_TRY(check_shape(M, N, d));
+    const int64_t n_sub = M * N / d;
+    VQ_TRY(check_K(K, n_sub));
+    VQ_CHECK(X && hcol && C && idx, "vq_assign: null pointer");
+    VQ_WS(ws && ws_bytes >= ws_assign(n_sub, K), "vq_assign: workspace too small");
+    VQ_TRY(check_device());
+    return assign_launch(X, hcol, rho, mask, M, N, d, C, K, idx, dist, ws, ws_bytes, as_stream(stream));
+}
+
+vq_status vq_update(const float* X, const float* hcol, const float* rho, const uint8_t* mask, int64_t M,
+                    int64_t N, int d, const uint16_t* idx, int K, float* C, int32_t* counts, double* J,
+                    void* ws, size_t ws_bytes, void* stream)
+{
+    VQ_TRY(check_shape(M, N, d));
+    const int64_t n_sub = M * N / d;
+    VQ_TRY(check_K(K, n_sub));
+    VQ_CHECK(X && hcol && idx && C, "vq_update: null pointer");
+    VQ_WS(ws && ws_bytes >= ws_update_total(n_sub, K), "vq_update: workspace too small");
+    VQ_TRY(check_device());
+    return update_with_J(X, hcol, rho, mask, M, N, d, idx, K, C, counts, J, ws, ws_bytes, as_stream(stream));
+}
+
+vq_status vq_objective(const float* X, const float* hcol, const float* rho, const uint8_t* mask, int64_t M,
+                       int64_t N, int d, const float* C, int K, const uint16_t* idx, double* J, void* ws,
+                       size_t ws_bytes, void* stream)
+{
+    VQ_TRY(check_shape(M, N, d));
+    const int64_t n_sub = M * N / d;
+    VQ_TRY(check_K(K, n_sub));
+    VQ_CHECK(X && hcol && C && idx && J, "vq_objective: null pointer");
+    VQ_WS(ws && ws_bytes >= ws_objective(n_sub), "vq_objective: workspace too small");
+    VQ_TRY(check_device());
+    return objective_launch(X, hcol, rho, mask, M, N, d, C, K, idx, J, ws, ws_bytes, as_stream(stream));
+}
+
+vq_status vq_residual(const float* X, int64_t M, int64_t N, int d, const float* C, int K, const uint16_t* idx,
+                      float* R, void* stream)
+{
+    VQ_TRY(check_shape(M, N, d));
+    VQ_TRY(check_K(K, M * N / d));
+    VQ_CHECK(X && C && idx && R, "vq_residual: null pointer");
+    VQ_CHECK(R != X, "vq_residual: R may not alias X");
+    VQ_TRY(check_device());
+    return residual_launch(X, M, N, d, C, K, idx, R, as_stream(stream));
+}
+
+vq_status vq_reconstruct(int64_t M, int64_t N, int d, const float* C1, int K1, const uint16_t* idx1,
+                         const float* C2, int K2, const uint16_t* idx2, const float* rscale, const float* cscale,
+                         const int32_t* row_ptr, const int32_t* col, const float* val, float* W_hat, void* stream)
+{
+    VQ_TRY(check_shape(M, N, d));
+    const int64_t n_sub = M * N / d;
+    VQ_TRY(check_K(K1, n_sub));
+    VQ_CHECK(C1 && idx1 && W_hat, "vq_reconstruct: null pointer");
+    if (C2) {
+        VQ_TRY(check_K(K2, n_sub));
+        VQ_CHECK(idx2 != nullptr, "vq_reconstruct: idx2 is null");
+    }
+    VQ_CHECK(!row_ptr || (col && val), "vq_reconstruct: col/val are null");
+    VQ_TRY(check_device());
+    return reconstruct_launch(M, N, d, C1, K1, idx1, C2, K2, idx2, rscale, cscale, row_ptr, col, val, W_hat,
+                              as_stream(stream));
+}
+
+double vq_bits_per_weight(int64_t M, int64_t N, int d, int K1, int K2, int64_t nnz, int cb_bits, int binorm)
+{
+    if (M <= 0 || N <= 0 || d < 1 || N % d) return -1.0;
+    auto ibits = [](int K) -> int64_t {
+        int64_t b = 0;
+        while (((int64_t)1 << b) < K) ++b;
+        return b;
+    };
+    const int64_t n_sub = M * N / d;
+    double bits = (double)n_sub * (double)(ibits(K1) + (K2 > 0 ? ibits(K2) : 0));
+    bits += (double)d * (double)(K1 + (K2 > 0 ? K2 : 0)) * cb_bits;
+    bits += 64.0 * (double)nnz;
+    if (nnz > 0) bits += 32.0 * (double)(M + 1);
+    if (binorm) bits += 32.0 * (double)(M + N);
+    return bits / ((double)M * (double)N);
+}
+
+vq_status vq_fit(const vq_fit_params* p, const vq_fit_inputs* in, vq_fit_outputs* out, void* ws,
+                 size_t ws_bytes, void* stream)
+{
+    VQ_CHECK(p && in && out, "vq_fit: null params/inputs/outputs");
+    const int64_t M = p->M, N = p->N;
+    const int d = p->d;
+    VQ_TRY(check_shape(M, N, d));
+    const int64_t n_sub = M * N / d;
+    VQ_TRY(check_K(p->K1, n_sub));
+    if (p->K2 > 0) VQ_TRY(check_K(p->K2, n_sub));
+    VQ_CHECK(p->K2 >= 0, "vq_fit: K2 must be >= 0");
+    VQ_CHECK(p->iters1 >= 0 && p->iters2 >= 0 && p->iters1 + p->iters2 + 2 <= 256, "vq_fit: iteration counts out of range");
+    VQ_CHECK(p->outlier_frac >= 0.0 && p->outlier_frac <= 1.0, "vq_fit: outlier_frac must be in [0, 1]");
+    const int64_t nnz = nnz_of(M, N, p->outlier_frac);
+    VQ_CHECK(nnz <= INT32_MAX, "vq_fit: too many salient weights");
+    VQ_CHECK(in->W && in->h, "vq_fit: W/h are null");
+    VQ_CHECK(in->perm1 || in->C1_init, "vq_fit: need perm1 or C1_init");
+    VQ_CHECK(p->K2 == 0 || in->perm2 || in->C2_init, "vq_fit: need perm2 or C2_init");
+    VQ_CHECK(out->idx1 && out->C1 && out->row_ptr && out->mask && out->W_hat && out->J_hist,
+             "vq_fit: null output");
+    VQ_CHECK(nnz == 0 || (out->col && out->val), "vq_fit: col/val are null");
+    VQ_CHECK(p->K2 == 0 || (out->idx2 && out->C2), "vq_fit: idx2/C2 are null");
+    VQ_CHECK(!p->binorm || (out->Wp && out->rscale && out->cscale && out->hcol && out->rho),
+             "vq_fit: bi-normalization outputs are null");
+    const size_t need = vq_workspace_bytes(M, N, d, p->K1, p->K2, nnz);
+    VQ_WS(ws && ws_bytes >= need, "vq_fit: workspace too small");
+    VQ_TRY(check_device());
+    hipStream_t st = as_stream(stream);
+
+    Carver cv(ws, ws_bytes);
+    float* R = p->K2 > 0 ? cv.take<float>((size_t)M * N) : nullptr;
+    double* Jd = cv.take<double>(256);
+    if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_fit: workspace too small");
+    void* sws = cv.base + cv.used;
+    const size_t sws_bytes = cv.cap - cv.used;
+
+    const float* X = in->W;
+    const float* hc = in->h;
+    const float* rh = nullptr;
+    if (p->binorm) {
+        VQ_TRY(binorm_launch(in->W, in->h, M, N, out->Wp, out->rscale, out->cscale, out->hcol, out->rho, sws,
+                             sws_bytes, st));
+        X = out->Wp;
+        hc = out->hcol;
+        rh = out->rho;
+    }
+    VQ_TRY(select_launch(in->W, in->h, M, N, d, nnz, out->row_ptr, out->col, out->val, out->mask, sws,
+                         sws_bytes, st));
+    const uint8_t* mk = p->mask_outliers ? out->mask : nullptr;
+
+    if (in->C1_init)
+        VQ_HIP(hipMemcpyAsync(out->C1, in->C1_init, (size_t)p->K1 * d * sizeof(float), hipMemcpyDeviceToDevice, st));
+    else
+        VQ_TRY(init_walk(X, n_sub, d, in->perm1, p->K1, out->C1, sws, sws_bytes, st));
+    VQ_TRY(lloyd_stage(X, hc, rh, mk, M, N, d, out->C1, p->K1, p->iters1, out->idx1, Jd, sws, sws_bytes, st));
+    const int nJ = p->iters1 + 1 + (p->K2 > 0 ? p->iters2 + 1 : 0);
+    if (p->K2 > 0) {
+        VQ_TRY(residual_launch(X, M, N, d, out->C1, p->K1, out->idx1, R, st));
+        if (in->C2_init)
+            VQ_HIP(hipMemcpyAsync(out->C2, in->C2_init, (size_t)p->K2 * d * sizeof(float), hipMemcpyDeviceToDevice, st));
+        else
+            VQ_TRY(init_walk(R, n_sub, d, in->perm2, p->K2, out->C2, sws, sws_bytes, st));
+        VQ_TRY(lloyd_stage(R, hc, rh, mk, M, N, d, out->C2, p->K2, p->iters2, out->idx2, Jd + p->iters1 + 1, sws,
+                           sws_bytes, st));
+    }
+    VQ_TRY(reconstruct_launch(M, N, d, out->C1, p->K1, out->idx1, p->K2 > 0 ? out->C2 : nullptr, p->K2, out->idx2,
+                              p->binorm ? out->rscale : nullptr, p->binorm ? out->cscale : nullptr,
+                              nnz > 0 ? out->row_ptr : nullptr, out->col, out->val, out->W_hat, st));
+    VQ_HIP(hipMemcpyAsync(out->J_hist, Jd, sizeof(double) * nJ, hipMemcpyDeviceToHost, st));
+    VQ_HIP(hipStreamSynchronize(st));
+    if (out->bpw) *out->bpw = vq_bits_per_weight(M, N, d, p->K1, p->K2, nnz, 32, p->binorm);
+    return VQ_OK;
+}
+
+int vq_assign_exact_count(void* ws, size_t ws_bytes, int64_t n_sub, int K, void* stream)
+{
+    int n = -1;
+    if (assign_flag_count(ws, ws_bytes, n_sub, K, &n, as_stream(stream)) != VQ_OK) return -1;
+    return n;
+}
+
+}  // extern "C"

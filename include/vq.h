@@ -1,0 +1,209 @@
+/*
+ * vq.h -- C ABI of libvq: Hessian/salience-weighted vector quantization of
+ * one LLM weight matrix on an AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources are the pages' titles and sections):
+ *   - HAS-VQ abstract: salient weights, scored by second-order sensitivity,
+ *     are decoupled from the bulk ("Hessian-Masked Decoupling") and held
+ *     exactly ("residual sparse feedback ... exact reconstruction of
+ *     outliers"); the dense remainder is vector quantized.
+ *   - VPTQ page, "Hessian-Weighted Centroid Initialization": with a diagonal
+ *     Hessian the objective is a weighted K-means problem; centroids are
+ *     weighted means.
+ *   - VPTQ page, "Residual Vector Quantization": a second codebook quantizes
+ *     the first stage's error; decode adds the two centroids.
+ *   - SCVQ summary: weights bi-normalized across rows and columns, salience-
+ *     weighted K-means, one sparse correction matrix.
+ *
+ * Conventions (all entry points):
+ *   - W is [M x N] row-major float32, M outputs by N inputs.  h (the diagonal
+ *     Hessian proxy) has one float32 entry per input column j.
+ *   - A sub-vector s = (row i, block b) holds W[i, b*d .. b*d+d-1]; its id is
+ *     s = i*(N/d) + b, so a matrix read as [n_sub x d] is contiguous.
+ *     n_sub = M*N/d.  1 <= d <= 8 and N % d == 0.
+ *   - Element weight omega(i,j) = m_ij * hcol[j] * rho[i]; m_ij = 0 on the
+ *     salient positions (when masking is on), 1 elsewhere; rho = 1 when NULL.
+ *   - Distance D(s,k) = sum_t omega(s,t) (x(s,t) - C(k,t))^2; objective
+ *     J = sum_s D(s, a_s).
+ *   - Indices are uint16 (1 <= K <= 65536); codebooks are [K x d] float32.
+ *   - mask is one byte per sub-vector: bit t set <=> element t is salient
+ *     (weight 0 in clustering).  A NULL mask means no salient positions.
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns and
+ *     allocates every buffer, including the workspace; the library never
+ *     allocates device memory in these calls and never frees caller memory.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Step
+ *     calls enqueue work and return without synchronizing; vq_init and vq_fit
+ *     synchronize the stream (they read device data on the host).
+ *   - Every call validates its arguments on the host before any launch and
+ *     returns a vq_status; vq_last_error() (thread-local) describes the last
+ *     failure.  Non-finite W or h is a precondition violation and is not
+ *     checked.
+ */
+#ifndef VQ_H
+#define VQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    VQ_OK = 0,
+    VQ_ERR_INVALID = 1,     /* bad argument: null pointer, size or range */
+    VQ_ERR_WORKSPACE = 2,   /* ws_bytes below what the call needs */
+    VQ_ERR_INIT = 3,        /* fewer than K bitwise-distinct sub-vectors */
+    VQ_ERR_DEVICE = 4,      /* a HIP runtime call failed (message attached) */
+    VQ_ERR_UNSUPPORTED = 5  /* no gfx950 device current */
+} vq_status;
+
+/* Library version string (static storage). */
+const char* vq_version(void);
+
+/* Description of the last failure on this thread ("" if none). */
+const char* vq_last_error(void);
+
+/* Workspace bytes sufficient for every call below with these sizes
+ * (K2 = 0: no residual stage; nnz = number of salient weights). */
+size_t vq_workspace_bytes(int64_t M, int64_t N, int d, int K1, int K2, int64_t nnz);
+
+/* Salience selection into the exact sparse correction.
+ * HAS-VQ abstract (Hessian-Masked Decoupling; exact reconstruction of the
+ * salient weights); SCVQ summary (one sparse correction matrix).
+ * Score s_ij = h_j * (w_ij * w_ij) in float32 (no fused multiply-add).  The
+ * nnz largest scores are selected, ties broken by the smaller linear index
+ * i*N+j.  Outputs: row_ptr int32[M+1], col int32[nnz] (ascending within each
+ * row), val float32[nnz] (the exact W values), mask uint8[n_sub] (bit t of
+ * byte s set <=> element t of sub-vector s is selected).  Bitwise
+ * deterministic.  0 <= nnz <= min(M*N, 2^31-1); scores must be >= +0. */
+vq_status vq_sparse_select(const float* W, const float* h, int64_t M, int64_t N, int d,
+                           int64_t nnz, int32_t* row_ptr, int32_t* col, float* val,
+                           uint8_t* mask, void* ws, size_t ws_bytes, void* stream);
+
+/* Bi-normalization (SCVQ summary: rows and columns bi-normalized before
+ * clustering), one pass of RMS scaling, rows first:
+ *   r_i = sqrt(sum_j W_ij^2 / N) (fp64 sum; 1 if zero), Wt = W / r_i (fp32),
+ *   c_j = sqrt(sum_i Wt_ij^2 / M) (fp64 sum; 1 if zero), Wp = Wt / c_j (fp32),
+ *   hcol_j = h_j c_j^2 and rho_i = r_i^2 (fp64 products, stored fp32),
+ * so that the weighted objective on Wp equals the original-space objective.
+ * Outputs Wp [M x N], r [M], c [N], hcol [N], rho [M]. */
+vq_status vq_binorm(const float* W, const float* h, int64_t M, int64_t N,
+                    float* Wp, float* r, float* c, float* hcol, float* rho,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Codebook seeding: walk perm (host int32[n_sub], a permutation of the
+ * sub-vector ids) and copy the first K sub-vectors of X whose d floats are
+ * not bitwise equal to one already taken into C [K x d].  Returns
+ * VQ_ERR_INIT if fewer than K distinct sub-vectors exist.  Synchronizes. */
+vq_status vq_init(const float* X, int64_t M, int64_t N, int d, const int32_t* perm,
+                  int K, float* C, void* ws, size_t ws_bytes, void* stream);
+
+/* Assignment (VPTQ page, "The Core Algorithm": nearest centroid; here under
+ * the weighted distance D).  idx[s] = argmin_k D(s,k), ties to the lowest k.
+ * The result equals the exact (float64, direct form) argmin: a float32
+ * expanded-form search runs on the matrix cores, each winner is certified
+ * against a rigorous rounding bound, and uncertified sub-vectors are
+ * re-searched exactly.  X = the matrix being quantized ([M x N] f32),
+ * hcol [N], rho [M] (nullable), mask (nullable), C [K x d].  Outputs
+ * idx uint16[n_sub] and, if dist != NULL, dist float32[n_sub] = D(s, idx[s])
+ * computed in float64 and rounded. */
+vq_status vq_assign(const float* X, const float* hcol, const float* rho, const uint8_t* mask,
+                    int64_t M, int64_t N, int d, const float* C, int K,
+                    uint16_t* idx, float* dist, void* ws, size_t ws_bytes, void* stream);
+
+/* Diagnostics: number of sub-vectors that the last vq_assign call on this
+ * workspace (same n_sub and K) sent to the exact float64 re-search because
+ * their winner could not be certified.  Synchronizes the stream; -1 on error. */
+int vq_assign_exact_count(void* ws, size_t ws_bytes, int64_t n_sub, int K, void* stream);
+
+/* Centroid update (VPTQ page, "Hessian-Weighted Centroid Initialization":
+ * weighted-mean centroids; with one weight per element this is the
+ * per-dimension weighted mean, the exact minimizer of J for fixed indices):
+ *   C(k,t) = sum_{idx_s=k} omega x / sum_{idx_s=k} omega   (fp64 sums, one
+ *   rounding to fp32); a zero weight sum keeps the old value.
+ * C is read and overwritten in place.  counts (nullable) receives int32[K]
+ * member counts; J (nullable, device double[1]) receives the objective of
+ * the INPUT codebook with these indices.  Sorting by index and a segmented
+ * reduction without floating-point atomics make the result bitwise
+ * deterministic. */
+vq_status vq_update(const float* X, const float* hcol, const float* rho, const uint8_t* mask,
+                    int64_t M, int64_t N, int d, const uint16_t* idx, int K,
+                    float* C, int32_t* counts, double* J, void* ws, size_t ws_bytes, void* stream);
+
+/* Objective J = sum_s D(s, idx[s]) (fp64, fixed reduction order) into the
+ * device double J[0]. */
+vq_status vq_objective(const float* X, const float* hcol, const float* rho, const uint8_t* mask,
+                       int64_t M, int64_t N, int d, const float* C, int K, const uint16_t* idx,
+                       double* J, void* ws, size_t ws_bytes, void* stream);
+
+/* Residual (VPTQ page, "Residual Vector Quantization": v_res = v - Q(v)):
+ * R = X - C[idx] elementwise in float32.  R may not alias X. */
+vq_status vq_residual(const float* X, int64_t M, int64_t N, int d, const float* C, int K,
+                      const uint16_t* idx, float* R, void* stream);
+
+/* Reconstruction (VPTQ page, "Residual Vector Quantization": decode
+ * C[i1] + Cres[i2]; HAS-VQ abstract: salient weights reconstructed exactly):
+ *   W_hat_ij = ((C1[idx1]_t + C2[idx2]_t) * cscale_j) * rscale_i   (fp32)
+ * with the stage-2 term skipped when C2 == NULL and each scale skipped when
+ * NULL; then W_hat_ij = val at every CSR position (row_ptr/col/val may be
+ * NULL for no sparse part).  Bitwise deterministic. */
+vq_status vq_reconstruct(int64_t M, int64_t N, int d, const float* C1, int K1, const uint16_t* idx1,
+                         const float* C2, int K2, const uint16_t* idx2,
+                         const float* rscale, const float* cscale,
+                         const int32_t* row_ptr, const int32_t* col, const float* val,
+                         float* W_hat, void* stream);
+
+/* The whole per-matrix pipeline (HAS-VQ abstract; VPTQ page, "End-to-End
+ * Quantization Pipeline": main codebook, then a residual codebook on
+ * W - W_hat):
+ *   [bi-normalize] -> select -> seed C1 -> iters1 x (assign, update) -> assign
+ *   -> residual -> seed C2 -> iters2 x (assign, update) -> assign -> reconstruct.
+ * Salient scores are taken on the original W and h. */
+typedef struct {
+    int64_t M, N;
+    int d;
+    int K1, iters1;
+    int K2, iters2;        /* K2 = 0: no residual stage */
+    double outlier_frac;   /* p; nnz = floor(p * M * N) */
+    int binorm;            /* 1: bi-normalize before clustering */
+    int mask_outliers;     /* 1: salient weights get weight 0 in clustering */
+} vq_fit_params;
+
+typedef struct {
+    const float* W;        /* [M x N] */
+    const float* h;        /* [N] */
+    const int32_t* perm1;  /* host int32[n_sub]: seeding order, stage 1 */
+    const int32_t* perm2;  /* host int32[n_sub]: seeding order, stage 2 */
+    const float* C1_init;  /* nullable [K1 x d]: replaces stage-1 seeding (resume) */
+    const float* C2_init;  /* nullable [K2 x d]: replaces stage-2 seeding */
+} vq_fit_inputs;
+
+typedef struct {
+    uint16_t* idx1; float* C1;     /* [n_sub], [K1 x d] */
+    uint16_t* idx2; float* C2;     /* [n_sub], [K2 x d] (unused when K2 = 0) */
+    int32_t* row_ptr; int32_t* col; float* val;   /* CSR: [M+1], [nnz], [nnz] */
+    uint8_t* mask;                 /* [n_sub] */
+    float* Wp;                     /* [M x N] bi-normalized matrix (binorm only) */
+    float* rscale; float* cscale;  /* [M], [N] (binorm only) */
+    float* hcol; float* rho;       /* [N], [M] (binorm only) */
+    float* W_hat;                  /* [M x N] */
+    double* J_hist;                /* host double[iters1+1 (+ iters2+1)] */
+    double* bpw;                   /* host double[1], b_cb = 32 (nullable) */
+} vq_fit_outputs;
+
+vq_status vq_fit(const vq_fit_params* p, const vq_fit_inputs* in, vq_fit_outputs* out,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* Bits per weight of the stored result (host arithmetic; VPTQ page,
+ * "End-to-End Quantization Pipeline", compression ratio: index bits plus
+ * codebook bits, extended by the sparse part and the scales):
+ *   n_sub*(ceil(log2 K1) + ceil(log2 K2)) + d*(K1+K2)*cb_bits + 64*nnz
+ *   + 32*(M+1) [nnz > 0] + 32*(M+N) [binorm], divided by M*N. */
+double vq_bits_per_weight(int64_t M, int64_t N, int d, int K1, int K2, int64_t nnz,
+                          int cb_bits, int binorm);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VQ_H */

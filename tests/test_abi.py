@@ -1,0 +1,82 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/vq.h declares, and rejects bad arguments on the host before any
+device call.  (No compute call runs here.)"""
+import os
+import re
+
+import pytest
+
+from hessian_weighted_vector_amd import vq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000            # never dereferenced: every case below fails validation
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "vq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = set(re.findall(r"\b(vq_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = vq.load()
+    names = header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in vq.SIGNATURES, n
+    assert set(vq.SIGNATURES) == set(names)
+    assert lib.vq_version().startswith(b"libvq")
+
+
+@pytest.mark.parametrize("M,N,d,K,msg", [
+    (0, 16, 8, 4, "positive"), (8, 16, 9, 4, "d must"), (8, 16, 0, 4, "d must"),
+    (8, 12, 8, 4, "multiple"), (8, 16, 8, 0, "K must"), (8, 16, 8, 70000, "K must"),
+    (2, 16, 8, 5, "exceeds"),
+])
+def test_assign_rejects_bad_sizes(M, N, d, K, msg):
+    lib = vq.load()
+    st = lib.vq_assign(FAKE, FAKE, None, None, M, N, d, FAKE, K, FAKE, None, FAKE, 1 << 30, None)
+    assert st == vq.VQ_ERR_INVALID
+    assert msg in lib.vq_last_error().decode()
+
+
+def test_null_pointers_and_workspace():
+    lib = vq.load()
+    assert lib.vq_assign(None, FAKE, None, None, 8, 16, 8, FAKE, 4, FAKE, None, FAKE, 1 << 30, None) == vq.VQ_ERR_INVALID
+    assert lib.vq_assign(FAKE, FAKE, None, None, 8, 16, 8, FAKE, 4, FAKE, None, FAKE, 16, None) == vq.VQ_ERR_WORKSPACE
+    assert lib.vq_update(FAKE, FAKE, None, None, 8, 16, 8, FAKE, 4, FAKE, None, None, FAKE, 16, None) == vq.VQ_ERR_WORKSPACE
+    assert lib.vq_sparse_select(FAKE, FAKE, 8, 16, 8, 200, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == vq.VQ_ERR_INVALID
+    assert "nnz" in lib.vq_last_error().decode()
+    assert lib.vq_sparse_select(FAKE, FAKE, 8, 16, 8, 4, FAKE, None, None, FAKE, FAKE, 1 << 30, None) == vq.VQ_ERR_INVALID
+    assert lib.vq_residual(FAKE, 8, 16, 8, FAKE, 4, FAKE, FAKE, None) == vq.VQ_ERR_INVALID   # R aliases X
+    assert lib.vq_binorm(FAKE, FAKE, 8, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == vq.VQ_ERR_INVALID
+    assert lib.vq_reconstruct(8, 16, 8, FAKE, 4, FAKE, FAKE, 4, None, None, None, None, None, None, FAKE, None) == vq.VQ_ERR_INVALID
+    assert lib.vq_workspace_bytes(8, 12, 8, 4, 0, 0) == 0
+
+
+def test_fit_rejects_bad_params():
+    lib = vq.load()
+    import ctypes
+    p = vq.FitParams(8, 16, 8, 4, 2, 0, 0, 1.5, 0, 1)
+    i = vq.FitInputs(FAKE, FAKE, FAKE, None, None, None)
+    o = vq.FitOutputs(*([FAKE] * 16))
+    st = lib.vq_fit(ctypes.byref(p), ctypes.byref(i), ctypes.byref(o), FAKE, 1 << 40, None)
+    assert st == vq.VQ_ERR_INVALID and "outlier_frac" in lib.vq_last_error().decode()
+    p = vq.FitParams(8, 16, 8, 4, 2, 3, 2, 0.1, 0, 1)
+    i = vq.FitInputs(FAKE, FAKE, FAKE, None, None, None)          # residual stage without perm2
+    st = lib.vq_fit(ctypes.byref(p), ctypes.byref(i), ctypes.byref(o), FAKE, 1 << 40, None)
+    assert st == vq.VQ_ERR_INVALID and "perm2" in lib.vq_last_error().decode()
+
+
+def test_bits_per_weight_host_formula_matches_oracle():
+    import oracle
+    from hessian_weighted_vector_amd import configs
+    for c in configs.CONFIGS:
+        nz = oracle.nnz(c.M, c.N, c.p)
+        for cb in (16, 32):
+            a = vq.bits_per_weight(c.M, c.N, c.d, c.K1, c.K2, nz, cb, c.binorm)
+            b = oracle.bits_per_weight(c.M, c.N, c.d, c.K1, c.K2, nz, cb, c.binorm)
+            assert a == pytest.approx(b, rel=1e-15)
+    assert vq.bits_per_weight(4096, 4096, 8, 256, 0, 0, 16) == pytest.approx(16 / 15.96880, rel=1e-6)
