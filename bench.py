@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of the weighted-VQ hot path on one MI355X.
+
+One step = the whole per-matrix fit through the C ABI (vq_fit): salience
+selection into the exact sparse correction, bi-normalization, codebook
+seeding, T1 Lloyd iterations (weighted assignment + weighted-mean update) at
+K1, residual, seeding, T2 iterations at K2, and reconstruction, on the
+LLaMA-2-7B MLP workload (W 4096 x 11008, bf16 values held as fp32, d = 8,
+K1 = 65536, T1 = 10, K2 = 256, T2 = 10, 1% salient, bi-normalized).  Inputs
+are seeded synthetic arrays already resident in HBM.
+
+value = sub-vector assignments per second over Lloyd iterations, whole step:
+n_sub * (T1 + T2) / (wall time per step), in G/s.
+
+The roofline entry is for the dominant kernel, the matrix-core search of the
+stage-1 assignment (K = 65536): algorithmic flops = 32 per (sub-vector,
+centroid) pair (the 2d = 16-term inner product, one multiply and one add
+each) times n_sub * K pairs per launch, divided by that kernel's average
+duration measured with HIP events on the stream it runs on, during the timed
+steps.  The CPU baseline is the C oracle's exhaustive float64 assignment
+against the same 65536-entry codebook on a bounded sample of sub-vectors.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
+PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
+
+
+def algorithmic_bytes_update(n_sub, M, N, d, K):
+    # x (d fp32) + index (u16) + mask byte per sub-vector; hcol and rho; codebook in and out
+    return n_sub * (4 * d + 2 + 1) + 4 * N + 4 * M + 2 * K * d * 4
+
+
+def algorithmic_bytes_reconstruct(n_sub, M, N, d, K1, K2, nnz, binorm):
+    b = n_sub * (4 * d + 2 + (2 if K2 else 0)) + 8 * nnz + 4 * (M + 1) + 4 * (K1 + K2) * d
+    if binorm:
+        b += 4 * (M + N)
+    return b
+
+
+def traffic_from_profile(kernel_src):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "assign_search_c4_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        prof = json.load(f)
+    with open(kernel_src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if prof.get("kernel_src_sha256") != sha:
+        return None
+    return prof.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, seconds):
+    """The oracle's assignment on a bounded sample (float64 exhaustive search)."""
+    import numpy as np
+
+    import oracle
+    nthreads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    Wp, r, c, hcol, rho = oracle.binorm(inp["W"], inp["h"]) if cfg.binorm else (inp["W"], None, None, inp["h"], None)
+    C, taken = oracle.init(Wp, cfg.d, inp["perm1"], cfg.K1)
+    assert taken == cfg.K1
+    chunk = 8192
+    done, t_total, e0 = 0, 0.0, 0
+    while t_total < seconds and e0 < cfg.n_sub:
+        sub = np.sort(inp["perm1"][e0:e0 + chunk]).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.assign(Wp, hcol, rho, None, cfg.d, C, subset=sub, nthreads=nthreads)
+        t_total += time.perf_counter() - t0
+        done += sub.size
+        e0 += chunk
+    return {
+        "value": done / t_total / 1e9,
+        "unit": "G sub-vectors/s (one assignment pass, K=%d)" % cfg.K1,
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": "%d seeded sub-vectors of the 4096x11008 bi-normalized matrix assigned against the "
+                  "65536-centroid seed codebook (float64 direct form, exhaustive), %.1f s" % (done, t_total),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", type=int, default=4, help="workload number 1..5 (default 4)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="print per-step timings to stderr")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(each weight matrix is fitted on one device); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from hessian_weighted_vector_amd import configs, synth, vq
+
+    cfg = configs.get(args.config)
+    inp = synth.make_inputs(cfg)
+    torch.cuda.set_device(0)
+    W = torch.from_numpy(inp["W"]).cuda()
+    h = torch.from_numpy(inp["h"]).cuda()
+    nnz = vq.nnz_of(cfg.M, cfg.N, cfg.p)
+    ws = vq.workspace(cfg.M, cfg.N, cfg.d, cfg.K1, cfg.K2, nnz)
+
+    def step():
+        return vq.fit(W, h, cfg.d, cfg.K1, cfg.T1, cfg.K2, cfg.T2, cfg.p, cfg.binorm, True,
+                      inp["perm1"], inp["perm2"], ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    vq.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        out = step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    recs = vq.timing_records()
+    vq.timing_enable(False)
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    n_sub = cfg.n_sub
+    value = n_sub * (cfg.T1 + cfg.T2) / (ms_per_step * 1e-3) / 1e9
+
+    rec = {(r[0], r[1]): r for r in recs}
+    s1 = rec[("assign_search", cfg.K1)]
+    avg_s1 = s1[3] / s1[2]
+    flops = 32.0 * n_sub * cfg.K1
+    achieved = flops / (avg_s1 * 1e-3) / 1e12
+    src = os.path.join(ROOT, "hessian_weighted_vector_amd", "csrc", "vq_assign.hip")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
+                "traffic": traffic_from_profile(src)}
+
+    extra = {"assign_stage1_ms": round(avg_s1, 3),
+             "assign_stage1_Gsub_per_s": round(n_sub / (avg_s1 * 1e-3) / 1e9, 5)}
+    if ("assign", cfg.K1) in rec:
+        a = rec[("assign", cfg.K1)]
+        extra["assign_stage1_with_exact_ms"] = round(a[3] / a[2], 3)
+    if cfg.K2 and ("assign_search", cfg.K2) in rec:
+        a = rec[("assign_search", cfg.K2)]
+        extra["assign_stage2_ms"] = round(a[3] / a[2], 4)
+        extra["assign_stage2_Gsub_per_s"] = round(n_sub / (a[3] / a[2] * 1e-3) / 1e9, 4)
+    if ("update", cfg.K1) in rec:
+        u = rec[("update", cfg.K1)]
+        ub = algorithmic_bytes_update(n_sub, cfg.M, cfg.N, cfg.d, cfg.K1)
+        extra["update_stage1_us"] = round(u[3] / u[2] * 1e3, 2)
+        extra["update_stage1_GBs"] = round(ub / (u[3] / u[2] * 1e-3) / 1e9, 1)
+        extra["update_stage1_frac_hbm"] = round(extra["update_stage1_GBs"] / PEAK_HBM_GBS, 4)
+    if ("reconstruct", cfg.K1) in rec:
+        r_ = rec[("reconstruct", cfg.K1)]
+        rb = algorithmic_bytes_reconstruct(n_sub, cfg.M, cfg.N, cfg.d, cfg.K1, cfg.K2, nnz, cfg.binorm)
+        extra["reconstruct_us"] = round(r_[3] / r_[2] * 1e3, 2)
+        extra["reconstruct_GBs"] = round(rb / (r_[3] / r_[2] * 1e-3) / 1e9, 1)
+        extra["reconstruct_frac_hbm"] = round(extra["reconstruct_GBs"] / PEAK_HBM_GBS, 4)
+    extra["J_final"] = float(out["J"][-1])
+    extra["bpw"] = out["bpw"]
+
+    if args.breakdown:
+        for r in sorted(recs, key=lambda r: -r[3]):
+            print("%-14s K=%-6d launches=%-4d total=%9.3f ms avg=%9.4f ms min=%9.4f max=%9.4f"
+                  % (r[0], r[1], r[2], r[3], r[3] / r[2], r[4], r[5]), file=sys.stderr)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, inp, args.cpu_seconds)
+
+    line = {
+        "metric": "sub-vectors assigned/s per Lloyd iter (G/s) + % FP32 peak; update/recon HBM GB/s",
+        "value": round(value, 6),
+        "unit": "G sub-vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded StudentT weights, Gaussian activations with high-energy channels)",
+        "config": {"workload": cfg.name, "M": cfg.M, "N": cfg.N, "d": cfg.d, "K1": cfg.K1, "T1": cfg.T1,
+                   "K2": cfg.K2, "T2": cfg.T2, "outlier_frac": cfg.p, "nnz": nnz, "binorm": cfg.binorm,
+                   "bf16_input": cfg.bf16, "n_sub": n_sub,
+                   "value_def": "n_sub*(T1+T2)/step_time; step = full vq_fit incl. reconstruct"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

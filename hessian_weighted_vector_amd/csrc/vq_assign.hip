@@ -291,13 +291,17 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_assign: workspace too small");
 
     const int Kpad = Kt * kTile;
+    TimedRegion tr_all("assign", K, st);
     hipLaunchKernelGGL(k_cb_prep, dim3(grid_for(Kpad, 256)), dim3(256), 0, st, C, K, d, Kpad, P,
                        flag_count);
     VQ_LAUNCHED("k_cb_prep");
-    hipLaunchKernelGGL(k_assign_mfma, dim3(grid_for(n_sub, kSubPerBlock)), dim3(256), 0, st, X, hcol,
-                       rho, mask, n_sub, nb, d, reinterpret_cast<const float4*>(P), C, K, Kt, idx, dist,
-                       flag_count, flag_list);
-    VQ_LAUNCHED("k_assign_mfma");
+    {
+        TimedRegion tr("assign_search", K, st);
+        hipLaunchKernelGGL(k_assign_mfma, dim3(grid_for(n_sub, kSubPerBlock)), dim3(256), 0, st, X, hcol,
+                           rho, mask, n_sub, nb, d, reinterpret_cast<const float4*>(P), C, K, Kt, idx, dist,
+                           flag_count, flag_list);
+        VQ_LAUNCHED("k_assign_mfma");
+    }
     const unsigned gx = (unsigned)std::min<int64_t>(n_sub, kExactBlocks);
     hipLaunchKernelGGL(k_assign_exact, dim3(gx), dim3(256), 0, st, X, hcol, rho, mask, nb, d, C, K,
                        flag_count, flag_list, idx, dist);

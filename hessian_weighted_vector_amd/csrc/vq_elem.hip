@@ -221,6 +221,7 @@ vq_status binorm_launch(const float* W, const float* h, int64_t M, int64_t N, fl
     Carver cv(ws, ws_bytes);
     double* part = cv.take<double>((size_t)kRowGroups * N);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_binorm: workspace too small");
+    TimedRegion tr("binorm", 0, st);
     hipLaunchKernelGGL(k_row_rms, dim3((unsigned)M), dim3(kBlock), 0, st, W, N, r, rho);
     VQ_LAUNCHED("k_row_rms");
     const int64_t rpg = (M + kRowGroups - 1) / kRowGroups;
@@ -240,6 +241,7 @@ vq_status residual_launch(const float* X, int64_t M, int64_t N, int d, const flo
                           const uint16_t* idx, float* R, hipStream_t st)
 {
     const int64_t total = M * N;
+    TimedRegion tr("residual", K, st);
     hipLaunchKernelGGL(k_residual, dim3(grid_for(total, kBlock)), dim3(kBlock), 0, st, X, total, d, C, K,
                        idx, R);
     VQ_LAUNCHED("k_residual");
@@ -252,6 +254,7 @@ vq_status reconstruct_launch(int64_t M, int64_t N, int d, const float* C1, int K
                              const float* val, float* Wh, hipStream_t st)
 {
     const int64_t n_sub = M * N / d;
+    TimedRegion tr("reconstruct", K1, st);
     hipLaunchKernelGGL(k_decode, dim3(grid_for(n_sub, kBlock)), dim3(kBlock), 0, st, n_sub, N / d, d,
                        C1, K1, idx1, C2, K2, idx2, rs, cs, Wh);
     VQ_LAUNCHED("k_decode");
@@ -272,6 +275,7 @@ vq_status objective_launch(const float* X, const float* hcol, const float* rho, 
     Carver cv(ws, ws_bytes);
     double* part = cv.take<double>(nblk);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_objective: workspace too small");
+    TimedRegion tr("objective", K, st);
     hipLaunchKernelGGL(k_objective_partial, dim3(nblk), dim3(kBlock), 0, st, X, hcol, rho, mask, n_sub,
                        N / d, d, C, K, idx, part);
     VQ_LAUNCHED("k_objective_partial");

@@ -134,6 +134,7 @@ vq_status init_walk(const float* X, int64_t n_sub, int d, const int32_t* perm, i
     float* dbuf = cv.take<float>((size_t)chunk * d);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_init: workspace too small");
 
+    TimedRegion tr("init", K, st);
     std::vector<float> host((size_t)chunk * d);
     std::vector<float> taken_rows((size_t)K * d);
     size_t cap = 16;

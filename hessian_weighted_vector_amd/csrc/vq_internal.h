@@ -69,6 +69,22 @@ vq_status check_K(int K, int64_t n_sub);
 
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Brackets the launches in its scope with events on `st` when timing is on
+// (vq_timing_enable); a no-op otherwise.
+class TimedRegion {
+  public:
+    TimedRegion(const char* name, int K, hipStream_t st);
+    ~TimedRegion();
+    TimedRegion(const TimedRegion&) = delete;
+    TimedRegion& operator=(const TimedRegion&) = delete;
+
+  private:
+    const char* name_;
+    int K_;
+    hipStream_t st_;
+    void* a_ = nullptr;
+};
+
 inline unsigned grid_for(int64_t work, int per_block) {
     int64_t g = (work + per_block - 1) / per_block;
     return static_cast<unsigned>(g < 1 ? 1 : g);

@@ -257,6 +257,7 @@ vq_status select_launch(const float* W, const float* h, int64_t M, int64_t N, in
     int* take = cv.take<int>((size_t)M);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_sparse_select: workspace too small");
     const int64_t total = M * N;
+    TimedRegion tr("select", 0, st);
 
     // nnz == 0 skips the threshold search: the initial threshold pattern
     // 0xFFFFFFFF lies above every non-negative score, so nothing is taken.

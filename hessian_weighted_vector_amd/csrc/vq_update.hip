@@ -291,6 +291,7 @@ vq_status update_launch(const float* X, const float* hcol, const float* rho, con
     UpdateWs w = carve_update(cv, n_sub, K);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_update: workspace too small");
 
+    TimedRegion tr("update", K, st);
     const int passes = K > 256 ? 2 : 1;
     const uint16_t* kin = idx;
     const int32_t* vin = nullptr;

@@ -65,6 +65,10 @@ SIGNATURES = {
     "vq_fit": (_I, [ctypes.POINTER(FitParams), ctypes.POINTER(FitInputs), ctypes.POINTER(FitOutputs),
                     _P, _SZ, _P]),
     "vq_bits_per_weight": (_D, [_I64, _I64, _I, _I, _I, _I64, _I, _I]),
+    "vq_timing_enable": (None, [_I]),
+    "vq_timing_count": (_I, []),
+    "vq_timing_get": (_I, [_I, ctypes.c_char_p, _I, ctypes.POINTER(_I), ctypes.POINTER(_I64),
+                           ctypes.POINTER(_D), ctypes.POINTER(_D), ctypes.POINTER(_D)]),
 }
 
 _lib = None
@@ -214,6 +218,24 @@ def reconstruct(M, N, d, C1, idx1, C2=None, idx2=None, rscale=None, cscale=None,
                                  0 if C2 is None else C2.shape[0], _ptr(idx2), _ptr(rscale), _ptr(cscale),
                                  _ptr(row_ptr), _ptr(col), _ptr(val), _ptr(W_hat), _stream()))
     return W_hat
+
+
+def timing_enable(on=True):
+    load().vq_timing_enable(int(bool(on)))
+
+
+def timing_records():
+    """[(name, K, launches, total_ms, min_ms, max_ms)] of the recorded step timings."""
+    lib = load()
+    out = []
+    for i in range(lib.vq_timing_count()):
+        buf = ctypes.create_string_buffer(64)
+        K, n = _I(0), _I64(0)
+        tot, mn, mx = _D(0), _D(0), _D(0)
+        if lib.vq_timing_get(i, buf, 64, ctypes.byref(K), ctypes.byref(n), ctypes.byref(tot),
+                             ctypes.byref(mn), ctypes.byref(mx)) == 0:
+            out.append((buf.value.decode(), K.value, n.value, tot.value, mn.value, mx.value))
+    return out
 
 
 def bits_per_weight(M, N, d, K1, K2, nnz, cb_bits=32, binorm=False):

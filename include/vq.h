@@ -203,6 +203,21 @@ vq_status vq_fit(const vq_fit_params* p, const vq_fit_inputs* in, vq_fit_outputs
 double vq_bits_per_weight(int64_t M, int64_t N, int d, int K1, int K2, int64_t nnz,
                           int cb_bits, int binorm);
 
+/* Diagnostics: GPU time per step.  vq_timing_enable(1) clears the records
+ * and makes every later step call bracket its kernels with HIP events
+ * recorded on that call's stream; vq_timing_enable(0) stops recording.
+ * Records are keyed by (step name, K); names: "assign_search" (the matrix-core
+ * search kernel alone), "assign" (the whole vq_assign), "update", "objective",
+ * "select", "binorm", "residual", "reconstruct", "init".  vq_timing_count()
+ * waits for the recorded events and returns the number of records;
+ * vq_timing_get(i, ...) fills record i (name into a caller buffer of
+ * name_len bytes): launches, total, min and max milliseconds.  Returns 0 on
+ * success, 1 if i is out of range. */
+void vq_timing_enable(int on);
+int vq_timing_count(void);
+int vq_timing_get(int i, char* name, int name_len, int* K, int64_t* launches, double* total_ms,
+                  double* min_ms, double* max_ms);
+
 #ifdef __cplusplus
 }
 #endif
