@@ -4,9 +4,9 @@
  *
  * The method (sources are the pages' titles and sections):
  *   - HAS-VQ abstract: salient weights, scored by second-order sensitivity,
- *     are decoupled from the bulk ("Hessian-Masked Decoupling") and held
- *     exactly ("residual sparse feedback ... exact reconstruction of
- *     outliers"); the dense remainder is vector quantized.
+ *     are decoupled from the bulk (its Hessian-Masked Decoupling) and
+ *     reconstructed exactly through a sparse correction; the dense remainder
+ *     is vector quantized.
  *   - VPTQ page, "Hessian-Weighted Centroid Initialization": with a diagonal
  *     Hessian the objective is a weighted K-means problem; centroids are
  *     weighted means.
