@@ -17,6 +17,7 @@ SOURCES = ["vq_assign.hip", "vq_update.hip", "vq_select.hip", "vq_elem.hip", "vq
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function", "-Wno-unused-result"]
 
 

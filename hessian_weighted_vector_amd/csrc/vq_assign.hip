@@ -34,7 +34,7 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kWaves = 8;                 // waves per workgroup
 constexpr int kSubPerWave = 32;           // sub-vectors per wave (MFMA B columns)
 constexpr int kSubPerBlock = kWaves * kSubPerWave;
 constexpr int kTile = 32;                 // centroids per MFMA tile (A rows)
@@ -42,14 +42,18 @@ constexpr int kChunkTiles = 8;            // tiles staged in LDS at once
 constexpr float kPadSq = 1.0e30f;         // c*c of padding centroids
 constexpr int kExactBlocks = 2048;
 
-// P[k] = 16 floats: [-2 c_k0..-2 c_k7, c_k0^2..c_k7^2]; dims >= d are 0;
-// padding centroids (k >= K) have -2c = 0 and c^2 = kPadSq.  Also clears
-// the flag counter for the following search.
+// P[k] = 16 floats in two halves, one per half-wavefront of the MFMA A
+// operand: [-2c_0, -2c_2, -2c_4, -2c_6, c_0^2, c_2^2, c_4^2, c_6^2] then the
+// same for the odd dimensions.  Dimensions >= d are 0; padding centroids
+// (k >= K) have -2c = 0 and c^2 = kPadSq.  Also clears the flag counter.
 __global__ void k_cb_prep(const float* __restrict__ C, int K, int d, int Kpad,
-                          float* __restrict__ P, int* __restrict__ flag_count)
+                          float* __restrict__ P, int* __restrict__ flag_count, int* __restrict__ dirty_count)
 {
     int k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k == 0) *flag_count = 0;
+    if (k == 0) {
+        *flag_count = 0;
+        *dirty_count = 0;
+    }
     if (k >= Kpad) return;
     float* p = P + (size_t)k * 16;
     for (int t = 0; t < 8; ++t) {
@@ -63,8 +67,9 @@ __global__ void k_cb_prep(const float* __restrict__ C, int K, int d, int Kpad,
         } else {
             sq = kPadSq;
         }
-        p[t] = m2c;
-        p[8 + t] = sq;
+        const int h = t & 1, q = t >> 1;
+        p[h * 8 + q] = m2c;
+        p[h * 8 + 4 + q] = sq;
     }
 }
 
@@ -95,40 +100,222 @@ __device__ inline void exact_weights(const float* hcol, const float* rho, const 
     }
 }
 
-__global__ __launch_bounds__(256) void k_assign_mfma(
+// Running best / second best / best tile of accumulator slots j, j+1
+// (4 VALU ops per slot: median-of-three, compare, two selects).
+__device__ __forceinline__ void slot_pair(const f32x16& acc, int j, int kt, float* m1, float* m2, int* i1)
+{
+#pragma unroll
+    for (int q = j; q < j + 2; ++q) {
+        const float v = acc[q];
+        m2[q] = __builtin_amdgcn_fmed3f(m1[q], m2[q], v);
+        const bool lt = v < m1[q];
+        m1[q] = lt ? v : m1[q];
+        i1[q] = lt ? kt : i1[q];
+    }
+}
+
+// One 32x32 tile in the general form: eight chained MFMAs over the 16 terms
+// (4 pairs of -2c_t * omega_t x_t, then 4 pairs of c_t^2 * omega_t), with
+// the argmin updates of the previous tile's accumulator interleaved, one
+// MFMA per slot pair, so the wave's VALU work sits between its MFMAs.
+// a0 = this lane's 4 values of -2c, a1 = its 4 values of c^2; bw = omega*x,
+// bo = omega for this lane's 4 dimensions.
+__device__ __forceinline__ f32x16 tile_general(const float4 a0, const float4 a1, const float* bw, const float* bo,
+                                               const f32x16& prev, int ktp, float* m1, float* m2, int* i1)
+{
+    f32x16 acc = {};
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, bw[0], acc, 0, 0, 0);
+    slot_pair(prev, 0, ktp, m1, m2, i1);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, bw[1], acc, 0, 0, 0);
+    slot_pair(prev, 2, ktp, m1, m2, i1);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, bw[2], acc, 0, 0, 0);
+    slot_pair(prev, 4, ktp, m1, m2, i1);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, bw[3], acc, 0, 0, 0);
+    slot_pair(prev, 6, ktp, m1, m2, i1);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, bo[0], acc, 0, 0, 0);
+    slot_pair(prev, 8, ktp, m1, m2, i1);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, bo[1], acc, 0, 0, 0);
+    slot_pair(prev, 10, ktp, m1, m2, i1);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, bo[2], acc, 0, 0, 0);
+    slot_pair(prev, 12, ktp, m1, m2, i1);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, bo[3], acc, 0, 0, 0);
+    slot_pair(prev, 14, ktp, m1, m2, i1);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // eight VALU
+    }
+    return acc;
+}
+
+// The same tile when every sub-vector of the wavefront has the same weights
+// omega (same column block, same mask byte): the centroid term
+// sum_t omega_t c_t^2 is a per-centroid bias, formed here with 4 FMAs per
+// lane (each half-wave sums its 4 dimensions) and added by a fifth MFMA
+// against a B row of ones, so the tile needs 5 MFMAs instead of 8.
+__device__ __forceinline__ f32x16 tile_shared(const float4 a0, const float4 a1, const float* bw, const float* wo,
+                                              const f32x16& prev, int ktp, float* m1, float* m2, int* i1)
+{
+    float bias = a1.x * wo[0];
+    bias = fmaf(a1.y, wo[1], bias);
+    bias = fmaf(a1.z, wo[2], bias);
+    bias = fmaf(a1.w, wo[3], bias);
+    f32x16 acc = {};
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, bw[0], acc, 0, 0, 0);
+    slot_pair(prev, 0, ktp, m1, m2, i1);
+    slot_pair(prev, 2, ktp, m1, m2, i1);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, bw[1], acc, 0, 0, 0);
+    slot_pair(prev, 4, ktp, m1, m2, i1);
+    slot_pair(prev, 6, ktp, m1, m2, i1);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, bw[2], acc, 0, 0, 0);
+    slot_pair(prev, 8, ktp, m1, m2, i1);
+    slot_pair(prev, 10, ktp, m1, m2, i1);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, bw[3], acc, 0, 0, 0);
+    slot_pair(prev, 12, ktp, m1, m2, i1);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bias, 1.0f, acc, 0, 0, 0);
+    slot_pair(prev, 14, ktp, m1, m2, i1);
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // sixteen VALU
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    return acc;
+}
+
+// The majority mask byte of each column block (lowest byte on ties): the
+// weight pattern shared by most of its sub-vectors.
+__global__ __launch_bounds__(256) void k_block_pattern(const uint8_t* __restrict__ mask, int64_t M, int64_t nb,
+                                                       uint8_t* __restrict__ pattern)
+{
+    __shared__ int cnt[256];
+    __shared__ int best_c[256], best_p[256];
+    cnt[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t b = blockIdx.x;
+    for (int64_t i = threadIdx.x; i < M; i += 256) atomicAdd(&cnt[mask[i * nb + b]], 1);
+    __syncthreads();
+    best_c[threadIdx.x] = cnt[threadIdx.x];
+    best_p[threadIdx.x] = threadIdx.x;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) {
+            const int oc = best_c[threadIdx.x + w], op = best_p[threadIdx.x + w];
+            if (oc > best_c[threadIdx.x] || (oc == best_c[threadIdx.x] && op < best_p[threadIdx.x])) {
+                best_c[threadIdx.x] = oc;
+                best_p[threadIdx.x] = op;
+            }
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) pattern[b] = (uint8_t)best_p[0];
+}
+
+// Sub-vectors whose mask byte differs from their block's pattern are listed
+// for the general kernel (integer-atomic appends, one per wavefront; the
+// order of the list does not affect any result).
+__global__ void k_dirty(const uint8_t* __restrict__ mask, const uint8_t* __restrict__ pattern, int64_t n_sub,
+                        int64_t nb, int* __restrict__ count, int* __restrict__ list)
+{
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool take = s < n_sub && mask[s] != pattern[s % nb];
+    const unsigned long long ball = __ballot(take);
+    if (!ball) return;
+    const int lane = threadIdx.x & 63;
+    const int leader = __ffsll((long long)ball) - 1;
+    int base = 0;
+    if (lane == leader) base = atomicAdd(count, __popcll(ball));
+    base = __shfl(base, leader);
+    if (take) list[base + __popcll(ball & ((1ull << lane) - 1ull))] = (int)s;
+}
+
+// Workgroup = kWaves wavefronts x 32 sub-vectors, searched against the
+// whole codebook.
+//   SHARED: wavefront w takes wave group g = blockIdx.x * kWaves + w, i.e.
+//     32 consecutive rows of column block b; all lanes use the block's
+//     majority weight pattern (5-MFMA tile).  A lane whose own mask byte
+//     differs is computed but not written: it is in the list of the
+//     general kernel.
+//   general: lane l of wavefront w takes sub-vector list[(blockIdx.x *
+//     kWaves + w) * 32 + (l & 31)] with its own weights (8-MFMA tile).
+// The expanded codebook (padded to whole chunks) streams through LDS in
+// chunks of kChunkTiles*32 centroids, double buffered: the next chunk is
+// fetched into registers while the current one is searched, so there is one
+// barrier per chunk.  Within a wave the tiles are software pipelined: tile
+// t's MFMAs are issued with tile t-1's argmin updates between them (two
+// accumulators alternate).
+template <bool SHARED>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_assign_mfma(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
-    const uint8_t* __restrict__ mask, int64_t n_sub, int64_t nb, int d,
-    const float4* __restrict__ P, const float* __restrict__ C, int K, int Kt,
+    const uint8_t* __restrict__ mask, const uint8_t* __restrict__ pattern, int64_t M, int64_t nb, int d,
+    const float4* __restrict__ P, const float* __restrict__ C, int K, int nchunks,
+    const int* __restrict__ list, const int* __restrict__ list_count, int64_t groups,
     uint16_t* __restrict__ idx, float* __restrict__ dist,
     int* __restrict__ flag_count, int* __restrict__ flag_list)
 {
-    __shared__ float4 lds[kChunkTiles * kTile * 4];
+    constexpr int kChunkVec = kChunkTiles * kTile * 4;          // float4 per chunk
+    constexpr int kVecPerThread = kChunkVec / (kWaves * 64);
+    static_assert(kChunkTiles % 2 == 0, "tiles are processed in pairs");
+    static_assert(kVecPerThread == 2, "two float4 per thread per chunk");
+    __shared__ float4 lds[2][kChunkVec];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int half = lane >> 5;
-    const int64_t s = (int64_t)blockIdx.x * kSubPerBlock + wave * kSubPerWave + (lane & 31);
-    const bool valid = s < n_sub;
+    const int64_t e = (int64_t)blockIdx.x * kWaves + wave;
+    int64_t s = 0, b = 0;
+    bool active, valid;
+    unsigned mb = 0u, pat = 0u;
+    if (SHARED) {
+        if ((int64_t)blockIdx.x * kWaves >= groups) return;      // whole workgroup idle
+        active = e < groups;                                       // wave-uniform
+        const int64_t g = active ? e : 0;
+        const int64_t rg = g / nb;
+        b = g - rg * nb;
+        const int64_t i = rg * kSubPerWave + (lane & 31);
+        valid = active && i < M;
+        s = i * nb + b;
+        pat = (active && pattern) ? pattern[b] : 0u;
+        mb = (valid && mask) ? mask[s] : 0u;
+    } else {
+        const int64_t count = *list_count;
+        if ((int64_t)blockIdx.x * kWaves * kSubPerWave >= count) return;
+        const int64_t q = e * kSubPerWave + (lane & 31);
+        active = e * kSubPerWave < count;                          // wave-uniform
+        valid = q < count;
+        s = valid ? (int64_t)list[q] : 0;
+        b = s % nb;
+        mb = (valid && mask) ? mask[s] : 0u;
+    }
+    // lanes that write their result (in SHARED, only those of the pattern)
+    const bool owner = valid && (!SHARED || mb == pat);
 
-    // ---- the sub-vector's B operand and its weighted energy S ----------
+    // ---- the sub-vector's weights, B operand and weighted energy S -----
+    const unsigned wmask = SHARED ? pat : mb;
     float x[8], om[8];
     float S = 0.f;
-    {
-        unsigned mb = (valid && mask) ? mask[s] : 0u;
-        int64_t b = valid ? (s % nb) : 0;
-        for (int t = 0; t < 8; ++t) {
-            float xv = 0.f, w = 0.f;
-            if (valid && t < d) {
-                xv = X[s * d + t];
-                w = ((mb >> t) & 1u) ? 0.f : hcol[b * d + t];
-            }
-            x[t] = xv;
-            om[t] = w;
-            S += w * xv * xv;
+    for (int t = 0; t < 8; ++t) {
+        float xv = 0.f, w = 0.f;
+        if (valid && t < d) {
+            xv = X[s * d + t];
+            w = ((wmask >> t) & 1u) ? 0.f : hcol[b * d + t];
         }
+        x[t] = xv;
+        om[t] = w;
+        S += w * xv * xv;
     }
-    float bv[8];
-    for (int t = 0; t < 8; ++t) bv[t] = half ? om[t] : om[t] * x[t];
+    // this lane's half of the inner dimension: dimensions t = 2q + half;
+    // wo = the group's common weights (same for every lane in SHARED)
+    float bw[4], bo[4], wo[4];
+    for (int q = 0; q < 4; ++q) {
+        const int t = 2 * q + half;
+        bw[q] = om[t] * x[t];
+        bo[q] = om[t];
+        wo[q] = (SHARED && active && t < d && !((pat >> t) & 1u)) ? hcol[b * d + t] : 0.f;
+    }
 
     float m1[16], m2[16];
     int i1[16];
@@ -138,35 +325,50 @@ __global__ __launch_bounds__(256) void k_assign_mfma(
         i1[j] = 0;
     }
 
-    for (int c0 = 0; c0 < Kt; c0 += kChunkTiles) {
-        const int nt = min(kChunkTiles, Kt - c0);
-        __syncthreads();
-        const float4* src = P + (size_t)c0 * kTile * 4;
-        for (int q = threadIdx.x; q < nt * kTile * 4; q += blockDim.x) lds[q] = src[q];
-        __syncthreads();
-        for (int tt = 0; tt < nt; ++tt) {
-            const float4* a4 = &lds[(tt * kTile + (lane & 31)) * 4 + half * 2];
-            const float4 a0 = a4[0];
-            const float4 a1 = a4[1];
-            f32x16 acc = {};
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, bv[0], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, bv[1], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, bv[2], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, bv[3], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, bv[4], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, bv[5], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, bv[6], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, bv[7], acc, 0, 0, 0);
-            const int kt = c0 + tt;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float v = acc[j];
-                m2[j] = __builtin_amdgcn_fmed3f(m1[j], m2[j], v);
-                const bool lt = v < m1[j];
-                m1[j] = lt ? v : m1[j];
-                i1[j] = lt ? kt : i1[j];
+    float4 pre0 = P[threadIdx.x];
+    float4 pre1 = P[threadIdx.x + kWaves * 64];
+    lds[0][threadIdx.x] = pre0;
+    lds[0][threadIdx.x + kWaves * 64] = pre1;
+    __syncthreads();
+
+    // accB holds the pending tile; +inf values leave the slots unchanged
+    f32x16 accA, accB;
+    for (int j = 0; j < 16; ++j) accB[j] = __builtin_inff();
+    int ktB = 0;
+    const int a_off = (lane & 31) * 4 + half * 2;
+    for (int c = 0; c < nchunks; ++c) {
+        if (c + 1 < nchunks) {
+            const float4* src = P + (size_t)(c + 1) * kChunkVec;
+            pre0 = src[threadIdx.x];
+            pre1 = src[threadIdx.x + kWaves * 64];
+        }
+        if (active) {
+            const float4* L = lds[c & 1] + a_off;
+            const int kt0 = c * kChunkTiles;
+#pragma unroll 1
+            for (int tt = 0; tt < kChunkTiles; tt += 2) {
+                const float4* A0 = L + tt * kTile * 4;
+                const float4* A1 = A0 + kTile * 4;
+                if (SHARED) {
+                    accA = tile_shared(A0[0], A0[1], bw, wo, accB, ktB, m1, m2, i1);
+                    accB = tile_shared(A1[0], A1[1], bw, wo, accA, kt0 + tt, m1, m2, i1);
+                } else {
+                    accA = tile_general(A0[0], A0[1], bw, bo, accB, ktB, m1, m2, i1);
+                    accB = tile_general(A1[0], A1[1], bw, bo, accA, kt0 + tt, m1, m2, i1);
+                }
+                ktB = kt0 + tt + 1;
             }
         }
+        if (c + 1 < nchunks) {
+            lds[(c + 1) & 1][threadIdx.x] = pre0;
+            lds[(c + 1) & 1][threadIdx.x + kWaves * 64] = pre1;
+        }
+        __syncthreads();
+    }
+    if (!active) return;
+    {
+        const f32x16 accp = accB;
+        for (int j = 0; j < 16; j += 2) slot_pair(accp, j, ktB, m1, m2, i1);
     }
 
     // ---- epilogue: best and second best of this sub-vector -------------
@@ -196,7 +398,7 @@ __global__ __launch_bounds__(256) void k_assign_mfma(
     const float es = 32.f * u * (9.f * S + 4.f * fmaxf(gs, -S));
     const bool certified = (gs - gb) > (eb + es + 1.0e-35f) && gk < K;
 
-    const bool writer = valid && half == 0;
+    const bool writer = owner && half == 0;
     if (writer && certified) {
         idx[s] = (uint16_t)gk;
         if (dist) {
@@ -222,46 +424,99 @@ __global__ __launch_bounds__(256) void k_assign_mfma(
     }
 }
 
-// Exact float64 re-search of the flagged sub-vectors: one workgroup per
-// flagged sub-vector (grid-stride), lexicographic (D, k) minimum.
+// Exact re-search of the flagged sub-vectors.  A workgroup takes kExactBatch
+// flagged sub-vectors at a time (grid-stride) and streams the codebook once
+// for all of them.  For each centroid it forms the float32 expanded form e~
+// (a fused multiply-add chain over the 16 terms: the search's rounding
+// bound applies) and keeps a running approximate minimum b~ per thread and
+// sub-vector; a centroid whose interval e~ - err(e~) reaches b~ + err(b~) is
+// evaluated in float64 in the direct form, exactly as a plain float64
+// evaluation rounds.  Every exact minimizer lies in the final window, which
+// is contained in the evaluated set, so the lexicographic (D, k) minimum of
+// the evaluated centroids is the exact argmin (ties to the lowest index).
+constexpr int kExactBatch = 4;
+
 __global__ __launch_bounds__(256) void k_assign_exact(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
     const uint8_t* __restrict__ mask, int64_t nb, int d, const float* __restrict__ C, int K,
     const int* __restrict__ flag_count, const int* __restrict__ flag_list,
     uint16_t* __restrict__ idx, float* __restrict__ dist)
 {
-    __shared__ double sd[256];
-    __shared__ int sk[256];
+    __shared__ double sd[kExactBatch][256];
+    __shared__ int sk[kExactBatch][256];
     const int n = *flag_count;
-    for (int f = blockIdx.x; f < n; f += gridDim.x) {
-        const int64_t s = flag_list[f];
-        double om[8];
-        float x[8];
-        exact_weights(hcol, rho, mask, s, nb, d, om);
-        for (int t = 0; t < d; ++t) x[t] = X[s * d + t];
-        double best = __builtin_inf();
-        int arg = K;
-        for (int k = threadIdx.x; k < K; k += blockDim.x) {
-            const double v = exact_dist(om, x, C + (size_t)k * d, d);
-            if (v < best) { best = v; arg = k; }
+    const float u = 5.9604644775390625e-8f;
+    for (int f0 = blockIdx.x * kExactBatch; f0 < n; f0 += gridDim.x * kExactBatch) {
+        float x[kExactBatch][8], om[kExactBatch][8], bw[kExactBatch][8], S[kExactBatch], thr[kExactBatch];
+        double rr[kExactBatch], dbest[kExactBatch];
+        int arg[kExactBatch];
+#pragma unroll
+        for (int q = 0; q < kExactBatch; ++q) {
+            const bool live = f0 + q < n;
+            const int64_t s = live ? flag_list[f0 + q] : flag_list[f0];
+            const int64_t i = s / nb, b = s - (s / nb) * nb;
+            const unsigned mb = mask ? mask[s] : 0u;
+            rr[q] = rho ? (double)rho[i] : 1.0;
+            S[q] = 0.f;
+            for (int t = 0; t < 8; ++t) {
+                const float xv = t < d ? X[s * d + t] : 0.f;
+                const float w = (t < d && !((mb >> t) & 1u)) ? hcol[b * d + t] : 0.f;
+                x[q][t] = xv;
+                om[q][t] = w;
+                bw[q][t] = w * xv;
+                S[q] += w * xv * xv;
+            }
+            thr[q] = __builtin_inff();
+            dbest[q] = __builtin_inf();
+            arg[q] = K;
         }
-        sd[threadIdx.x] = best;
-        sk[threadIdx.x] = arg;
+        for (int k = threadIdx.x; k < K; k += blockDim.x) {
+            float c[8];
+            for (int t = 0; t < 8; ++t) c[t] = t < d ? C[(size_t)k * d + t] : 0.f;
+#pragma unroll
+            for (int q = 0; q < kExactBatch; ++q) {
+                float e = 0.f;
+                for (int t = 0; t < 8; ++t) e = fmaf(bw[q][t], -2.f * c[t], e);
+                for (int t = 0; t < 8; ++t) e = fmaf(om[q][t], c[t] * c[t], e);
+                const float err = 32.f * u * (9.f * S[q] + 4.f * fmaxf(e, -S[q])) + 1.0e-35f;
+                if (e - err <= thr[q]) {
+                    thr[q] = fminf(thr[q], e + err);
+                    double acc = 0.0;
+                    for (int t = 0; t < d; ++t) {
+                        double w = (double)om[q][t];
+                        if (rho) w = w * rr[q];
+                        const double diff = (double)x[q][t] - (double)c[t];
+                        const double sq = diff * diff;
+                        acc = acc + w * sq;
+                    }
+                    if (acc < dbest[q]) { dbest[q] = acc; arg[q] = k; }
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kExactBatch; ++q) {
+            sd[q][threadIdx.x] = dbest[q];
+            sk[q][threadIdx.x] = arg[q];
+        }
         __syncthreads();
         for (int w = blockDim.x / 2; w > 0; w >>= 1) {
             if ((int)threadIdx.x < w) {
-                const double ov = sd[threadIdx.x + w];
-                const int ok = sk[threadIdx.x + w];
-                if (ov < sd[threadIdx.x] || (ov == sd[threadIdx.x] && ok < sk[threadIdx.x])) {
-                    sd[threadIdx.x] = ov;
-                    sk[threadIdx.x] = ok;
+#pragma unroll
+                for (int q = 0; q < kExactBatch; ++q) {
+                    const double ov = sd[q][threadIdx.x + w];
+                    const int ok = sk[q][threadIdx.x + w];
+                    if (ov < sd[q][threadIdx.x] || (ov == sd[q][threadIdx.x] && ok < sk[q][threadIdx.x])) {
+                        sd[q][threadIdx.x] = ov;
+                        sk[q][threadIdx.x] = ok;
+                    }
                 }
             }
             __syncthreads();
         }
-        if (threadIdx.x == 0) {
-            idx[s] = (uint16_t)sk[0];
-            if (dist) dist[s] = (float)sd[0];
+        if ((int)threadIdx.x < kExactBatch && f0 + (int)threadIdx.x < n) {
+            const int64_t s = flag_list[f0 + threadIdx.x];
+            idx[s] = (uint16_t)sk[threadIdx.x][0];
+            if (dist) dist[s] = (float)sd[threadIdx.x][0];
         }
         __syncthreads();
     }
@@ -269,11 +524,18 @@ __global__ __launch_bounds__(256) void k_assign_exact(
 
 }  // namespace
 
+// Centroids per LDS chunk; the expanded codebook is padded to whole chunks.
+constexpr int kChunkK = kChunkTiles * kTile;
+
+inline int padded_K(int K) { return (K + kChunkK - 1) / kChunkK * kChunkK; }
+
 size_t ws_assign(int64_t n_sub, int K)
 {
-    const int64_t Kt = (K + kTile - 1) / kTile;
-    return align_up((size_t)Kt * kTile * 16 * sizeof(float)) + align_up(sizeof(int)) +
-           align_up((size_t)n_sub * sizeof(int));
+    // expanded codebook, flag counter, flag list, dirty counter, dirty list,
+    // block patterns (at most n_sub column blocks)
+    return align_up((size_t)padded_K(K) * 16 * sizeof(float)) + align_up(sizeof(int)) +
+           align_up((size_t)n_sub * sizeof(int)) + align_up(sizeof(int)) + align_up((size_t)n_sub * sizeof(int)) +
+           align_up((size_t)n_sub);
 }
 
 // Enqueues the assignment; arguments already validated by the caller.
@@ -283,26 +545,44 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
 {
     const int64_t n_sub = M * N / d;
     const int64_t nb = N / d;
-    const int Kt = (K + kTile - 1) / kTile;
+    const int Kpad = padded_K(K);
     Carver cv(ws, ws_bytes);
-    float* P = cv.take<float>((size_t)Kt * kTile * 16);
+    float* P = cv.take<float>((size_t)Kpad * 16);
     int* flag_count = cv.take<int>(1);
     int* flag_list = cv.take<int>((size_t)n_sub);
+    int* dirty_count = cv.take<int>(1);
+    int* dirty_list = cv.take<int>((size_t)n_sub);
+    uint8_t* pattern = cv.take<uint8_t>((size_t)nb);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_assign: workspace too small");
 
-    const int Kpad = Kt * kTile;
     TimedRegion tr_all("assign", K, st);
     hipLaunchKernelGGL(k_cb_prep, dim3(grid_for(Kpad, 256)), dim3(256), 0, st, C, K, d, Kpad, P,
-                       flag_count);
+                       flag_count, dirty_count);
     VQ_LAUNCHED("k_cb_prep");
     {
         TimedRegion tr("assign_search", K, st);
-        hipLaunchKernelGGL(k_assign_mfma, dim3(grid_for(n_sub, kSubPerBlock)), dim3(256), 0, st, X, hcol,
-                           rho, mask, n_sub, nb, d, reinterpret_cast<const float4*>(P), C, K, Kt, idx, dist,
-                           flag_count, flag_list);
-        VQ_LAUNCHED("k_assign_mfma");
+        const int64_t groups = (M + kSubPerWave - 1) / kSubPerWave * nb;
+        const float4* P4 = reinterpret_cast<const float4*>(P);
+        const int nch = Kpad / kChunkK;
+        if (mask) {
+            hipLaunchKernelGGL(k_block_pattern, dim3((unsigned)nb), dim3(256), 0, st, mask, M, nb, pattern);
+            VQ_LAUNCHED("k_block_pattern");
+            hipLaunchKernelGGL(k_dirty, dim3(grid_for(n_sub, 256)), dim3(256), 0, st, mask, pattern, n_sub, nb,
+                               dirty_count, dirty_list);
+            VQ_LAUNCHED("k_dirty");
+        }
+        hipLaunchKernelGGL(k_assign_mfma<true>, dim3(grid_for(groups, kWaves)), dim3(kWaves * 64), 0, st, X, hcol,
+                           rho, mask, mask ? pattern : nullptr, M, nb, d, P4, C, K, nch, nullptr, nullptr, groups,
+                           idx, dist, flag_count, flag_list);
+        VQ_LAUNCHED("k_assign_mfma<shared>");
+        if (mask) {
+            hipLaunchKernelGGL(k_assign_mfma<false>, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st,
+                               X, hcol, rho, mask, nullptr, M, nb, d, P4, C, K, nch, dirty_list, dirty_count, groups,
+                               idx, dist, flag_count, flag_list);
+            VQ_LAUNCHED("k_assign_mfma<general>");
+        }
     }
-    const unsigned gx = (unsigned)std::min<int64_t>(n_sub, kExactBlocks);
+    const unsigned gx = (unsigned)std::min<int64_t>((n_sub + kExactBatch - 1) / kExactBatch, kExactBlocks);
     hipLaunchKernelGGL(k_assign_exact, dim3(gx), dim3(256), 0, st, X, hcol, rho, mask, nb, d, C, K,
                        flag_count, flag_list, idx, dist);
     VQ_LAUNCHED("k_assign_exact");
@@ -312,9 +592,8 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
 // Number of sub-vectors the last search sent to the exact path (diagnostics).
 vq_status assign_flag_count(void* ws, size_t ws_bytes, int64_t n_sub, int K, int* out, hipStream_t st)
 {
-    const int Kt = (K + kTile - 1) / kTile;
     Carver cv(ws, ws_bytes);
-    cv.take<float>((size_t)Kt * kTile * 16);
+    cv.take<float>((size_t)padded_K(K) * 16);
     int* flag_count = cv.take<int>(1);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "workspace too small");
     VQ_HIP(hipMemcpyAsync(out, flag_count, sizeof(int), hipMemcpyDeviceToHost, st));

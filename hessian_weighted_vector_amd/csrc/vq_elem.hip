@@ -118,6 +118,24 @@ __global__ void k_residual(const float* __restrict__ X, int64_t total, int d,
     R[e] = k < K ? X[e] - C[(size_t)k * d + t] : __builtin_nanf("");
 }
 
+// d == 8 with 16-byte aligned buffers: one thread per half sub-vector.
+__global__ void k_residual8(const float4* __restrict__ X, int64_t n_half, const float4* __restrict__ C, int K,
+                            const uint16_t* __restrict__ idx, float4* __restrict__ R)
+{
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= n_half) return;
+    const int k = idx[q >> 1];
+    const float4 x = X[q];
+    float4 r;
+    if (k < K) {
+        const float4 c = C[(size_t)k * 2 + (q & 1)];
+        r.x = x.x - c.x; r.y = x.y - c.y; r.z = x.z - c.z; r.w = x.w - c.w;
+    } else {
+        r.x = r.y = r.z = r.w = __builtin_nanf("");
+    }
+    R[q] = r;
+}
+
 // ---- reconstruction ------------------------------------------------------
 // One thread per sub-vector: ((C1[i1] + C2[i2]) * c_j) * r_i, float32.
 // An index >= K (a caller error) decodes to NaN instead of an out-of-range read.
@@ -149,17 +167,61 @@ __global__ void k_decode(int64_t n_sub, int64_t nb, int d, const float* __restri
     }
 }
 
+// d == 8 with 16-byte aligned buffers: one thread per half sub-vector,
+// 16-byte loads and stores, same operation order as k_decode.
+__global__ void k_decode8(int64_t n_half, int64_t nb, const float4* __restrict__ C1, int K1,
+                          const uint16_t* __restrict__ idx1, const float4* __restrict__ C2, int K2,
+                          const uint16_t* __restrict__ idx2, const float* __restrict__ rs,
+                          const float4* __restrict__ cs, float4* __restrict__ Wh)
+{
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= n_half) return;
+    const int64_t s = q >> 1;
+    const int half = (int)(q & 1);
+    const int k1 = idx1[s];
+    const int k2 = C2 ? idx2[s] : 0;
+    float4 v;
+    if (k1 >= K1 || (C2 && k2 >= K2)) {
+        v.x = v.y = v.z = v.w = __builtin_nanf("");
+        Wh[q] = v;
+        return;
+    }
+    v = C1[(size_t)k1 * 2 + half];
+    if (C2) {
+        const float4 c = C2[(size_t)k2 * 2 + half];
+        v.x = v.x + c.x; v.y = v.y + c.y; v.z = v.z + c.z; v.w = v.w + c.w;
+    }
+    if (cs) {
+        const int64_t i = s / nb;
+        const int64_t b = s - i * nb;
+        const float4 c = cs[b * 2 + half];
+        v.x = v.x * c.x; v.y = v.y * c.y; v.z = v.z * c.z; v.w = v.w * c.w;
+    }
+    if (rs) {
+        const float ri = rs[s / nb];
+        v.x = v.x * ri; v.y = v.y * ri; v.z = v.z * ri; v.w = v.w * ri;
+    }
+    Wh[q] = v;
+}
+
 // The exact salient values overwrite their positions (HAS-VQ abstract:
-// exact reconstruction of the decoupled weights).  One thread per row.
+// exact reconstruction of the decoupled weights).  One thread per CSR entry
+// (grid-stride; nnz = row_ptr[M] is read on the device), row found by a
+// binary search of the row pointers.
 __global__ void k_sparse_overwrite(int64_t M, int64_t N, const int32_t* __restrict__ row_ptr,
                                    const int32_t* __restrict__ col, const float* __restrict__ val,
                                    float* __restrict__ Wh)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= M) return;
-    for (int32_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+    const int64_t nnz = row_ptr[M];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nnz; e += stride) {
+        int64_t lo = 0, hi = M;   // row_ptr[lo] <= e < row_ptr[hi]
+        while (hi - lo > 1) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (row_ptr[mid] <= e) lo = mid; else hi = mid;
+        }
         const int32_t j = col[e];
-        if (j >= 0 && j < N) Wh[i * N + j] = val[e];   // an out-of-range column is skipped
+        if (j >= 0 && j < N) Wh[lo * N + j] = val[e];   // an out-of-range column is skipped
     }
 }
 
@@ -203,6 +265,9 @@ __global__ __launch_bounds__(kBlock) void k_sum_partials(const double* __restric
 }
 
 constexpr int64_t kColChunk = 64;
+constexpr unsigned kOverwriteBlocks = 1024;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 constexpr int64_t kRowGroups = 32;
 
 }  // namespace
@@ -242,6 +307,14 @@ vq_status residual_launch(const float* X, int64_t M, int64_t N, int d, const flo
 {
     const int64_t total = M * N;
     TimedRegion tr("residual", K, st);
+    if (d == 8 && aligned16(X) && aligned16(C) && aligned16(R)) {
+        const int64_t n_half = total / 4;
+        hipLaunchKernelGGL(k_residual8, dim3(grid_for(n_half, kBlock)), dim3(kBlock), 0, st,
+                           reinterpret_cast<const float4*>(X), n_half, reinterpret_cast<const float4*>(C), K,
+                           idx, reinterpret_cast<float4*>(R));
+        VQ_LAUNCHED("k_residual8");
+        return VQ_OK;
+    }
     hipLaunchKernelGGL(k_residual, dim3(grid_for(total, kBlock)), dim3(kBlock), 0, st, X, total, d, C, K,
                        idx, R);
     VQ_LAUNCHED("k_residual");
@@ -255,12 +328,20 @@ vq_status reconstruct_launch(int64_t M, int64_t N, int d, const float* C1, int K
 {
     const int64_t n_sub = M * N / d;
     TimedRegion tr("reconstruct", K1, st);
-    hipLaunchKernelGGL(k_decode, dim3(grid_for(n_sub, kBlock)), dim3(kBlock), 0, st, n_sub, N / d, d,
-                       C1, K1, idx1, C2, K2, idx2, rs, cs, Wh);
-    VQ_LAUNCHED("k_decode");
+    if (d == 8 && aligned16(C1) && aligned16(C2) && aligned16(cs) && aligned16(Wh)) {
+        const int64_t n_half = n_sub * 2;
+        hipLaunchKernelGGL(k_decode8, dim3(grid_for(n_half, kBlock)), dim3(kBlock), 0, st, n_half, N / d,
+                           reinterpret_cast<const float4*>(C1), K1, idx1, reinterpret_cast<const float4*>(C2),
+                           K2, idx2, rs, reinterpret_cast<const float4*>(cs), reinterpret_cast<float4*>(Wh));
+        VQ_LAUNCHED("k_decode8");
+    } else {
+        hipLaunchKernelGGL(k_decode, dim3(grid_for(n_sub, kBlock)), dim3(kBlock), 0, st, n_sub, N / d, d,
+                           C1, K1, idx1, C2, K2, idx2, rs, cs, Wh);
+        VQ_LAUNCHED("k_decode");
+    }
     if (row_ptr) {
-        hipLaunchKernelGGL(k_sparse_overwrite, dim3(grid_for(M, kBlock)), dim3(kBlock), 0, st, M, N,
-                           row_ptr, col, val, Wh);
+        hipLaunchKernelGGL(k_sparse_overwrite, dim3(kOverwriteBlocks), dim3(kBlock), 0, st, M, N, row_ptr,
+                           col, val, Wh);
         VQ_LAUNCHED("k_sparse_overwrite");
     }
     return VQ_OK;

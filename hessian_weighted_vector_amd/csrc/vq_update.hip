@@ -10,10 +10,12 @@
 //      ranks inside a block come from wavefront ballots, so equal indices
 //      keep ascending sub-vector order;
 //   2. segment starts by binary search of the sorted indices;
-//   3. each segment is cut into pieces of at most kPiece members; one
-//      wavefront reduces a piece (float64 sums of omega*x and omega per
-//      dimension, lane-strided then a fixed xor butterfly);
-//   4. one thread per centroid adds its pieces in order and divides once.
+//   3. the sorted array is cut into fixed chunks; 8 lanes (one per
+//      dimension) walk a chunk in order with float64 sums of omega*x and
+//      omega, finishing the segments that lie inside it and leaving partial
+//      sums for the two that cross its ends;
+//   4. 8 lanes per crossing centroid add those partials in chunk order and
+//      divide once.
 #include "vq_internal.h"
 
 namespace vq {
@@ -22,8 +24,7 @@ namespace {
 constexpr int kSortThreads = 256;
 constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortThreads * kSortItems;   // elements per sort block
-constexpr int kPiece = 256;                             // members per wavefront piece
-constexpr int kScanThreads = 1024;
+constexpr int kChunk = 64;                              // sorted members per 8-lane group
 
 // Inclusive scan of one int per thread over a 256-thread block.
 __device__ inline int block_incl_scan_256(int v, int* sh)
@@ -80,6 +81,9 @@ __global__ __launch_bounds__(256) void k_scan_digit(int* __restrict__ hist, int 
 
 // Stable scatter of one block by the digit at `shift`.
 // vals_in == nullptr means the values are the element positions.
+// Each wavefront ranks its own contiguous sub-tile of kSortItems*64 elements
+// (ballot match of equal digits, wave-private LDS counters), then one
+// cross-wave prefix per digit gives every element its position.
 __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
     const uint16_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in, int64_t n, int shift,
     const int* __restrict__ hist, const int* __restrict__ digit_total, int nblk,
@@ -87,7 +91,6 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
 {
     __shared__ int sh[256];
     __shared__ int base[256];
-    __shared__ int running[256];
     __shared__ int wcnt[4][256];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -97,43 +100,51 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
     const int tot = digit_total[tid];
     const int incl = block_incl_scan_256(tot, sh);
     base[tid] = (incl - tot) + hist[(int64_t)tid * nblk + blockIdx.x];
-    running[tid] = 0;
+    for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
     __syncthreads();
 
-    const int64_t blk0 = (int64_t)blockIdx.x * kSortTile;
+    const int64_t wave0 = (int64_t)blockIdx.x * kSortTile + (int64_t)wave * (kSortItems * 64);
     const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint16_t key[kSortItems];
+    int32_t val[kSortItems];
+    int rank[kSortItems];
+#pragma unroll
     for (int r = 0; r < kSortItems; ++r) {
-        const int64_t e = blk0 + (int64_t)r * kSortThreads + tid;
+        const int64_t e = wave0 + (int64_t)r * 64 + lane;
         const bool valid = e < n;
-        uint16_t key = 0;
-        int32_t val = 0;
-        int dg = 0;
-        if (valid) {
-            key = keys_in[e];
-            val = vals_in ? vals_in[e] : (int32_t)e;
-            dg = (key >> shift) & 255;
-        }
-        for (int q = tid; q < 4 * 256; q += kSortThreads) (&wcnt[0][0])[q] = 0;
-        __syncthreads();
-        // lanes of this wavefront holding the same digit
+        key[r] = valid ? keys_in[e] : (uint16_t)0;
+        val[r] = valid ? (vals_in ? vals_in[e] : (int32_t)e) : 0;
+        const int dg = (key[r] >> shift) & 255;
         unsigned long long peers = __ballot(valid);
         for (int bit = 0; bit < 8; ++bit) {
             const unsigned long long bal = __ballot(valid && ((dg >> bit) & 1));
             peers &= ((dg >> bit) & 1) ? bal : ~bal;
         }
         const int wrank = __popcll(peers & lt_mask);
-        if (valid && wrank == 0) wcnt[wave][dg] = __popcll(peers);
-        __syncthreads();
-        if (valid) {
-            int off = running[dg] + wrank;
-            for (int w = 0; w < wave; ++w) off += wcnt[w][dg];
-            const int64_t pos = (int64_t)base[dg] + off;
-            keys_out[pos] = key;
-            vals_out[pos] = val;
+        int run = 0;
+        if (valid) run = wcnt[wave][dg];
+        rank[r] = valid ? run + wrank : -1;
+        if (valid && wrank == 0) wcnt[wave][dg] = run + __popcll(peers);
+    }
+    __syncthreads();
+    // offsets of each wavefront's part of each digit: prefix over the waves
+    {
+        int acc = 0;
+        for (int w = 0; w < 4; ++w) {
+            const int c = wcnt[w][tid];
+            wcnt[w][tid] = acc;
+            acc += c;
         }
-        __syncthreads();
-        running[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
-        __syncthreads();
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSortItems; ++r) {
+        if (rank[r] >= 0) {
+            const int dg = (key[r] >> shift) & 255;
+            const int64_t pos = (int64_t)base[dg] + wcnt[wave][dg] + rank[r];
+            keys_out[pos] = key[r];
+            vals_out[pos] = val[r];
+        }
     }
 }
 
@@ -151,108 +162,115 @@ __global__ void k_seg_start(const uint16_t* __restrict__ skeys, int64_t n, int K
     start[k] = (int)lo;
 }
 
-// Single-block exclusive scan of the per-centroid piece counts:
-// poff[k] = pieces before centroid k, poff[K] = total.
-__global__ __launch_bounds__(kScanThreads) void k_piece_scan(const int* __restrict__ start, int K,
-                                                             int* __restrict__ poff)
+// Weight and value of element t of sub-vector s, float64 (weight = hcol,
+// times rho if present; 0 when masked).
+__device__ inline void member_term(const float* __restrict__ X, const float* __restrict__ hcol,
+                                   const float* __restrict__ rho, const uint8_t* __restrict__ mask,
+                                   uint32_t s, uint32_t nb, int d, int t, double& w, double& x)
 {
-    __shared__ int sh[kScanThreads];
-    const int per = (K + kScanThreads - 1) / kScanThreads;
-    const int k0 = threadIdx.x * per;
-    int local = 0;
-    for (int k = k0; k < k0 + per && k < K; ++k) local += (start[k + 1] - start[k] + kPiece - 1) / kPiece;
-    sh[threadIdx.x] = local;
-    __syncthreads();
-    for (int off = 1; off < kScanThreads; off <<= 1) {
-        int add = (int)threadIdx.x >= off ? sh[threadIdx.x - off] : 0;
-        __syncthreads();
-        sh[threadIdx.x] += add;
-        __syncthreads();
-    }
-    int run = sh[threadIdx.x] - local;
-    for (int k = k0; k < k0 + per && k < K; ++k) {
-        poff[k] = run;
-        run += (start[k + 1] - start[k] + kPiece - 1) / kPiece;
-    }
-    if (threadIdx.x == kScanThreads - 1) poff[K] = sh[kScanThreads - 1];
+    const uint32_t i = s / nb;
+    const uint32_t b = s - i * nb;
+    double wt = (double)hcol[(size_t)b * d + t];
+    if (rho) wt = wt * (double)rho[i];
+    if (mask && ((mask[s] >> t) & 1u)) wt = 0.0;
+    w = wt;
+    x = (double)X[(size_t)s * d + t];
 }
 
-// One wavefront per piece: float64 sums of omega*x and omega per dimension.
-__global__ __launch_bounds__(256) void k_seg_reduce(
+// Chunked segmented reduction over the sorted (index, sub-vector) pairs.
+// The sorted array is cut into fixed chunks of kChunk members; a group of 8
+// lanes owns one chunk (lane t = dimension t) and walks it in order with
+// float64 sums of omega*x and omega.  A segment (all members of one
+// centroid) that lies inside the chunk is finished here; the segment that
+// enters the chunk from the left leaves a "head" partial and the one that
+// leaves to the right a "tail" partial, added in chunk order later.
+__global__ __launch_bounds__(256) void k_seg_chunks(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
-    const uint8_t* __restrict__ mask, int64_t nb, int d, const int32_t* __restrict__ svals,
-    const int* __restrict__ start, const int* __restrict__ poff, int K,
-    double* __restrict__ part)
+    const uint8_t* __restrict__ mask, uint32_t nb, int d, const uint16_t* __restrict__ skeys,
+    const int32_t* __restrict__ svals, const int* __restrict__ start, int64_t n, int64_t nchunks,
+    float* __restrict__ C, int32_t* __restrict__ counts, double* __restrict__ head,
+    double* __restrict__ tail)
 {
-    const int lane = threadIdx.x & 63;
-    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int total = poff[K];
-    if (w >= total) return;
-    // centroid owning piece w: last k with poff[k] <= w
-    int lo = 0, hi = K;   // poff[lo] <= w < poff[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (poff[mid] <= w) lo = mid; else hi = mid;
-    }
-    const int k = lo;
-    const int64_t j = w - poff[k];
-    const int64_t e0 = start[k] + j * kPiece;
-    const int64_t e1 = min((int64_t)start[k + 1], e0 + kPiece);
-    double num[8], den[8];
-    for (int t = 0; t < 8; ++t) { num[t] = 0.0; den[t] = 0.0; }
-    for (int64_t e = e0 + lane; e < e1; e += 64) {
-        const int64_t s = svals[e];
-        const int64_t i = s / nb;
-        const int64_t b = s - i * nb;
-        const unsigned mb = mask ? mask[s] : 0u;
-        const double rr = rho ? (double)rho[i] : 1.0;
-        for (int t = 0; t < d; ++t) {
-            double wt = (double)hcol[b * d + t];
-            if (rho) wt = wt * rr;
-            if ((mb >> t) & 1u) wt = 0.0;
-            num[t] = num[t] + wt * (double)X[s * d + t];
-            den[t] = den[t] + wt;
+    const int t = threadIdx.x & 7;
+    const int64_t ch = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+    if (ch >= nchunks) return;
+    const int64_t c0 = ch * kChunk;
+    const int64_t c1 = c0 + kChunk < n ? c0 + kChunk : n;
+    int k = skeys[c0];
+    double num = 0.0, den = 0.0;
+    for (int64_t e = c0; e < c1; ++e) {
+        const int ke = skeys[e];
+        if (ke != k) {
+            // segment k ends at e (inside this chunk)
+            const bool from_left = start[k] < c0;
+            if (from_left) {
+                if (t < d) { head[ch * 16 + t] = num; head[ch * 16 + 8 + t] = den; }
+            } else {
+                if (t < d && den > 0.0) C[(size_t)k * d + t] = (float)(num / den);
+                if (t == 0 && counts) counts[k] = start[k + 1] - start[k];
+            }
+            k = ke;
+            num = 0.0;
+            den = 0.0;
+        }
+        if (t < d) {
+            double w, x;
+            member_term(X, hcol, rho, mask, (uint32_t)svals[e], nb, d, t, w, x);
+            num = num + w * x;
+            den = den + w;
         }
     }
-    for (int off = 32; off > 0; off >>= 1) {
-        for (int t = 0; t < 8; ++t) {
-            num[t] = num[t] + __shfl_xor(num[t], off);
-            den[t] = den[t] + __shfl_xor(den[t], off);
-        }
-    }
-    if (lane == 0) {
-        double* p = part + w * 16;
-        for (int t = 0; t < 8; ++t) { p[t] = num[t]; p[8 + t] = den[t]; }
+    // the last segment of the chunk
+    const bool from_left = start[k] < c0;
+    const bool to_right = start[k + 1] > c1;
+    if (to_right) {
+        // continues in the next chunk: a tail, or a head when it also came from the left
+        double* dst = from_left ? head : tail;
+        if (t < d) { dst[ch * 16 + t] = num; dst[ch * 16 + 8 + t] = den; }
+    } else if (from_left) {
+        if (t < d) { head[ch * 16 + t] = num; head[ch * 16 + 8 + t] = den; }
+    } else {
+        if (t < d && den > 0.0) C[(size_t)k * d + t] = (float)(num / den);
+        if (t == 0 && counts) counts[k] = start[k + 1] - start[k];
     }
 }
 
-// One thread per centroid: add its pieces in order; C = num/den rounded once,
-// kept where the weight sum is 0.
-__global__ void k_seg_finish(const double* __restrict__ part, const int* __restrict__ start,
-                             const int* __restrict__ poff, int K, int d, float* __restrict__ C,
-                             int32_t* __restrict__ counts)
+// Segments that cross chunk boundaries: tail of the first chunk plus heads of
+// the following ones, in order; 8 lanes per centroid.  Empty centroids get a
+// zero count and keep their value.
+__global__ __launch_bounds__(256) void k_seg_cross(const int* __restrict__ start, int K, int d,
+                                                   const double* __restrict__ head,
+                                                   const double* __restrict__ tail,
+                                                   float* __restrict__ C, int32_t* __restrict__ counts)
 {
-    const int k = blockIdx.x * blockDim.x + threadIdx.x;
+    const int t = threadIdx.x & 7;
+    const int k = blockIdx.x * 32 + (threadIdx.x >> 3);
     if (k >= K) return;
-    if (counts) counts[k] = start[k + 1] - start[k];
-    double num[8], den[8];
-    for (int t = 0; t < 8; ++t) { num[t] = 0.0; den[t] = 0.0; }
-    for (int p = poff[k]; p < poff[k + 1]; ++p) {
-        const double* q = part + (int64_t)p * 16;
-        for (int t = 0; t < 8; ++t) { num[t] = num[t] + q[t]; den[t] = den[t] + q[8 + t]; }
+    const int s0 = start[k], s1 = start[k + 1];
+    if (s1 == s0) {
+        if (t == 0 && counts) counts[k] = 0;
+        return;
     }
-    for (int t = 0; t < d; ++t)
-        if (den[t] > 0.0) C[(size_t)k * d + t] = (float)(num[t] / den[t]);
+    const int64_t j0 = s0 / kChunk, j1 = (int64_t)(s1 - 1) / kChunk;
+    if (j0 == j1) return;   // finished inside its chunk
+    if (t == 0 && counts) counts[k] = s1 - s0;
+    if (t >= d) return;
+    double num = tail[j0 * 16 + t], den = tail[j0 * 16 + 8 + t];
+    for (int64_t j = j0 + 1; j <= j1; ++j) {
+        num = num + head[j * 16 + t];
+        den = den + head[j * 16 + 8 + t];
+    }
+    if (den > 0.0) C[(size_t)k * d + t] = (float)(num / den);
 }
 
 struct UpdateWs {
     uint16_t *k1, *k2;
     int32_t *v1, *v2;
-    int *hist, *dtot, *start, *poff;
-    double* part;
+    int *hist, *dtot, *start;
+    double *head, *tail;
 };
 
-int64_t piece_bound(int64_t n_sub, int K) { return (n_sub + kPiece - 1) / kPiece + K; }
+int64_t n_chunks(int64_t n_sub) { return (n_sub + kChunk - 1) / kChunk; }
 
 UpdateWs carve_update(Carver& cv, int64_t n_sub, int K)
 {
@@ -265,8 +283,8 @@ UpdateWs carve_update(Carver& cv, int64_t n_sub, int K)
     w.hist = cv.take<int>((size_t)256 * nblk);
     w.dtot = cv.take<int>(256);
     w.start = cv.take<int>((size_t)K + 1);
-    w.poff = cv.take<int>((size_t)K + 1);
-    w.part = cv.take<double>((size_t)piece_bound(n_sub, K) * 16);
+    w.head = cv.take<double>((size_t)n_chunks(n_sub) * 16);
+    w.tail = cv.take<double>((size_t)n_chunks(n_sub) * 16);
     return w;
 }
 
@@ -317,15 +335,13 @@ vq_status update_launch(const float* X, const float* hcol, const float* rho, con
     hipLaunchKernelGGL(k_seg_start, dim3(grid_for((int64_t)K + 1, 256)), dim3(256), 0, st, skeys, n_sub, K,
                        w.start);
     VQ_LAUNCHED("k_seg_start");
-    hipLaunchKernelGGL(k_piece_scan, dim3(1), dim3(kScanThreads), 0, st, w.start, K, w.poff);
-    VQ_LAUNCHED("k_piece_scan");
-    const int64_t bound = piece_bound(n_sub, K);
-    hipLaunchKernelGGL(k_seg_reduce, dim3(grid_for(bound, 4)), dim3(256), 0, st, X, hcol, rho, mask,
-                       N / d, d, svals, w.start, w.poff, K, w.part);
-    VQ_LAUNCHED("k_seg_reduce");
-    hipLaunchKernelGGL(k_seg_finish, dim3(grid_for(K, 256)), dim3(256), 0, st, w.part, w.start, w.poff, K,
-                       d, C, counts);
-    VQ_LAUNCHED("k_seg_finish");
+    const int64_t nch = n_chunks(n_sub);
+    hipLaunchKernelGGL(k_seg_chunks, dim3(grid_for(nch, 32)), dim3(256), 0, st, X, hcol, rho, mask,
+                       (uint32_t)(N / d), d, skeys, svals, w.start, n_sub, nch, C, counts, w.head, w.tail);
+    VQ_LAUNCHED("k_seg_chunks");
+    hipLaunchKernelGGL(k_seg_cross, dim3(grid_for(K, 32)), dim3(256), 0, st, w.start, K, d, w.head, w.tail, C,
+                       counts);
+    VQ_LAUNCHED("k_seg_cross");
     return VQ_OK;
 }
 
