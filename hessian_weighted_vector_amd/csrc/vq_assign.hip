@@ -100,51 +100,60 @@ __device__ inline void exact_weights(const float* hcol, const float* rho, const 
     }
 }
 
-// Running best / second best / best tile of accumulator slots j, j+1
-// (4 VALU ops per slot: median-of-three, compare, two selects).
-__device__ __forceinline__ void slot_pair(const f32x16& acc, int j, int kt, float* m1, float* m2, int* i1)
+// Minimum of a tile's 16 accumulator values (min3 chains).
+__device__ __forceinline__ float tile_min(const f32x16& a)
+{
+    float m0 = fminf(fminf(a[0], a[1]), a[2]);
+    float m1 = fminf(fminf(a[3], a[4]), a[5]);
+    float m2 = fminf(fminf(a[6], a[7]), a[8]);
+    float m3 = fminf(fminf(a[9], a[10]), a[11]);
+    float m4 = fminf(fminf(a[12], a[13]), a[14]);
+    m0 = fminf(fminf(m0, m1), m2);
+    m3 = fminf(fminf(m3, m4), a[15]);
+    return fminf(m0, m3);
+}
+
+// Exact update of this lane's (best, second best, best position) with the
+// 16 values of tile kt, in slot order (slot order is centroid order within
+// the lane, so equal values keep the lower index).  Position = kt*16 + slot.
+__device__ __forceinline__ void lane_update(const f32x16& a, int kt, float& b1, float& b2, int& kbp)
 {
 #pragma unroll
-    for (int q = j; q < j + 2; ++q) {
-        const float v = acc[q];
-        m2[q] = __builtin_amdgcn_fmed3f(m1[q], m2[q], v);
-        const bool lt = v < m1[q];
-        m1[q] = lt ? v : m1[q];
-        i1[q] = lt ? kt : i1[q];
+    for (int j = 0; j < 16; ++j) {
+        const float v = a[j];
+        const bool lt = v < b1;
+        b2 = __builtin_amdgcn_fmed3f(b1, b2, v);
+        b1 = lt ? v : b1;
+        kbp = lt ? kt * 16 + j : kbp;
     }
 }
 
 // One 32x32 tile in the general form: eight chained MFMAs over the 16 terms
-// (4 pairs of -2c_t * omega_t x_t, then 4 pairs of c_t^2 * omega_t), with
-// the argmin updates of the previous tile's accumulator interleaved, one
-// MFMA per slot pair, so the wave's VALU work sits between its MFMAs.
+// (4 pairs of -2c_t * omega_t x_t, then 4 pairs of c_t^2 * omega_t).  The
+// previous tile's minimum is formed between the MFMAs; only if it beats the
+// lane's second best (rare once the search has seen a few tiles) does the
+// wave walk that tile's values.
 // a0 = this lane's 4 values of -2c, a1 = its 4 values of c^2; bw = omega*x,
 // bo = omega for this lane's 4 dimensions.
 __device__ __forceinline__ f32x16 tile_general(const float4 a0, const float4 a1, const float* bw, const float* bo,
-                                               const f32x16& prev, int ktp, float* m1, float* m2, int* i1)
+                                               const f32x16& prev, int ktp, float& b1, float& b2, int& kbp)
 {
     f32x16 acc = {};
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, bw[0], acc, 0, 0, 0);
-    slot_pair(prev, 0, ktp, m1, m2, i1);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, bw[1], acc, 0, 0, 0);
-    slot_pair(prev, 2, ktp, m1, m2, i1);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, bw[2], acc, 0, 0, 0);
-    slot_pair(prev, 4, ktp, m1, m2, i1);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, bw[3], acc, 0, 0, 0);
-    slot_pair(prev, 6, ktp, m1, m2, i1);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, bo[0], acc, 0, 0, 0);
-    slot_pair(prev, 8, ktp, m1, m2, i1);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, bo[1], acc, 0, 0, 0);
-    slot_pair(prev, 10, ktp, m1, m2, i1);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, bo[2], acc, 0, 0, 0);
-    slot_pair(prev, 12, ktp, m1, m2, i1);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, bo[3], acc, 0, 0, 0);
-    slot_pair(prev, 14, ktp, m1, m2, i1);
+    const float tm = tile_min(prev);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // eight VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // one VALU
     }
+    if (tm < b2) lane_update(prev, ktp, b1, b2, kbp);
     return acc;
 }
 
@@ -154,7 +163,7 @@ __device__ __forceinline__ f32x16 tile_general(const float4 a0, const float4 a1,
 // lane (each half-wave sums its 4 dimensions) and added by a fifth MFMA
 // against a B row of ones, so the tile needs 5 MFMAs instead of 8.
 __device__ __forceinline__ f32x16 tile_shared(const float4 a0, const float4 a1, const float* bw, const float* wo,
-                                              const f32x16& prev, int ktp, float* m1, float* m2, int* i1)
+                                              const f32x16& prev, int ktp, float& b1, float& b2, int& kbp)
 {
     float bias = a1.x * wo[0];
     bias = fmaf(a1.y, wo[1], bias);
@@ -162,27 +171,18 @@ __device__ __forceinline__ f32x16 tile_shared(const float4 a0, const float4 a1, 
     bias = fmaf(a1.w, wo[3], bias);
     f32x16 acc = {};
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, bw[0], acc, 0, 0, 0);
-    slot_pair(prev, 0, ktp, m1, m2, i1);
-    slot_pair(prev, 2, ktp, m1, m2, i1);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, bw[1], acc, 0, 0, 0);
-    slot_pair(prev, 4, ktp, m1, m2, i1);
-    slot_pair(prev, 6, ktp, m1, m2, i1);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, bw[2], acc, 0, 0, 0);
-    slot_pair(prev, 8, ktp, m1, m2, i1);
-    slot_pair(prev, 10, ktp, m1, m2, i1);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, bw[3], acc, 0, 0, 0);
-    slot_pair(prev, 12, ktp, m1, m2, i1);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bias, 1.0f, acc, 0, 0, 0);
-    slot_pair(prev, 14, ktp, m1, m2, i1);
+    const float tm = tile_min(prev);
 #pragma unroll
-    for (int g = 0; g < 3; ++g) {
+    for (int g = 0; g < 4; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // sixteen VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    if (tm < b2) lane_update(prev, ktp, b1, b2, kbp);
     return acc;
 }
 
@@ -215,21 +215,46 @@ __global__ __launch_bounds__(256) void k_block_pattern(const uint8_t* __restrict
 }
 
 // Sub-vectors whose mask byte differs from their block's pattern are listed
-// for the general kernel (integer-atomic appends, one per wavefront; the
-// order of the list does not affect any result).
-__global__ void k_dirty(const uint8_t* __restrict__ mask, const uint8_t* __restrict__ pattern, int64_t n_sub,
-                        int64_t nb, int* __restrict__ count, int* __restrict__ list)
+// for the general kernel: wavefront ballots, a workgroup prefix in LDS and
+// one integer atomic per workgroup (the order of the list does not affect
+// any result).
+__global__ __launch_bounds__(1024) void k_dirty(const uint8_t* __restrict__ mask, const uint8_t* __restrict__ pattern,
+                                                int64_t n_sub, uint32_t nb, int* __restrict__ count,
+                                                int* __restrict__ list)
 {
-    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const bool take = s < n_sub && mask[s] != pattern[s % nb];
-    const unsigned long long ball = __ballot(take);
-    if (!ball) return;
-    const int lane = threadIdx.x & 63;
-    const int leader = __ffsll((long long)ball) - 1;
-    int base = 0;
-    if (lane == leader) base = atomicAdd(count, __popcll(ball));
-    base = __shfl(base, leader);
-    if (take) list[base + __popcll(ball & ((1ull << lane) - 1ull))] = (int)s;
+    constexpr int kItems = 4;
+    __shared__ int wsum[kItems][16];
+    __shared__ int base;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    bool take[kItems];
+    unsigned long long ball[kItems];
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+        const int64_t s = ((int64_t)blockIdx.x * kItems + r) * 1024 + threadIdx.x;
+        take[r] = false;
+        if (s < n_sub) take[r] = mask[s] != pattern[(uint32_t)(s % nb)];
+        ball[r] = __ballot(take[r]);
+        if (lane == 0) wsum[r][wave] = __popcll(ball[r]);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int tot = 0;
+        for (int r = 0; r < kItems; ++r)
+            for (int w = 0; w < 16; ++w) tot += wsum[r][w];
+        base = tot ? atomicAdd(count, tot) : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+        if (take[r]) {
+            int off = base + __popcll(ball[r] & ((1ull << lane) - 1ull));
+            for (int q = 0; q < r; ++q)
+                for (int w = 0; w < 16; ++w) off += wsum[q][w];
+            for (int w = 0; w < wave; ++w) off += wsum[r][w];
+            const int64_t s = ((int64_t)blockIdx.x * kItems + r) * 1024 + threadIdx.x;
+            list[off] = (int)s;
+        }
+    }
 }
 
 // Workgroup = kWaves wavefronts x 32 sub-vectors, searched against the
@@ -248,7 +273,7 @@ __global__ void k_dirty(const uint8_t* __restrict__ mask, const uint8_t* __restr
 // t's MFMAs are issued with tile t-1's argmin updates between them (two
 // accumulators alternate).
 template <bool SHARED>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_assign_mfma(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_assign_mfma(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
     const uint8_t* __restrict__ mask, const uint8_t* __restrict__ pattern, int64_t M, int64_t nb, int d,
     const float4* __restrict__ P, const float* __restrict__ C, int K, int nchunks,
@@ -317,13 +342,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
         wo[q] = (SHARED && active && t < d && !((pat >> t) & 1u)) ? hcol[b * d + t] : 0.f;
     }
 
-    float m1[16], m2[16];
-    int i1[16];
-    for (int j = 0; j < 16; ++j) {
-        m1[j] = __builtin_inff();
-        m2[j] = __builtin_inff();
-        i1[j] = 0;
-    }
+    float b1 = __builtin_inff(), b2 = __builtin_inff();
+    int kbp = 0;
 
     float4 pre0 = P[threadIdx.x];
     float4 pre1 = P[threadIdx.x + kWaves * 64];
@@ -350,11 +370,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
                 const float4* A0 = L + tt * kTile * 4;
                 const float4* A1 = A0 + kTile * 4;
                 if (SHARED) {
-                    accA = tile_shared(A0[0], A0[1], bw, wo, accB, ktB, m1, m2, i1);
-                    accB = tile_shared(A1[0], A1[1], bw, wo, accA, kt0 + tt, m1, m2, i1);
+                    accA = tile_shared(A0[0], A0[1], bw, wo, accB, ktB, b1, b2, kbp);
+                    accB = tile_shared(A1[0], A1[1], bw, wo, accA, kt0 + tt, b1, b2, kbp);
                 } else {
-                    accA = tile_general(A0[0], A0[1], bw, bo, accB, ktB, m1, m2, i1);
-                    accB = tile_general(A1[0], A1[1], bw, bo, accA, kt0 + tt, m1, m2, i1);
+                    accA = tile_general(A0[0], A0[1], bw, bo, accB, ktB, b1, b2, kbp);
+                    accB = tile_general(A1[0], A1[1], bw, bo, accA, kt0 + tt, b1, b2, kbp);
                 }
                 ktB = kt0 + tt + 1;
             }
@@ -366,22 +386,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
         __syncthreads();
     }
     if (!active) return;
-    {
-        const f32x16 accp = accB;
-        for (int j = 0; j < 16; j += 2) slot_pair(accp, j, ktB, m1, m2, i1);
-    }
+    if (tile_min(accB) < b2) lane_update(accB, ktB, b1, b2, kbp);
 
     // ---- epilogue: best and second best of this sub-vector -------------
-    // accumulator slot j of this lane holds centroid row (j/4)*8 + half*4 + j%4
-    float b1 = m1[0];
-    int bj = 0;
-    for (int j = 1; j < 16; ++j)
-        if (m1[j] < b1) { b1 = m1[j]; bj = j; }
-    float sec = __builtin_inff();
-    for (int j = 0; j < 16; ++j) sec = fminf(sec, j == bj ? m2[j] : m1[j]);
-    int kb = 0;
-    for (int j = 0; j < 16; ++j)
-        if (j == bj) kb = i1[j] * kTile + (j >> 2) * 8 + half * 4 + (j & 3);
+    // position kbp = tile * 16 + slot; slot j of this lane holds centroid row
+    // (j/4)*8 + half*4 + j%4 of the tile
+    const float sec = b2;
+    const int jb = kbp & 15;
+    const int kb = (kbp >> 4) * kTile + (jb >> 2) * 8 + half * 4 + (jb & 3);
 
     const float ob1 = __shfl_xor(b1, 32);
     const float osec = __shfl_xor(sec, 32);
@@ -424,101 +436,86 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
     }
 }
 
-// Exact re-search of the flagged sub-vectors.  A workgroup takes kExactBatch
-// flagged sub-vectors at a time (grid-stride) and streams the codebook once
-// for all of them.  For each centroid it forms the float32 expanded form e~
-// (a fused multiply-add chain over the 16 terms: the search's rounding
-// bound applies) and keeps a running approximate minimum b~ per thread and
-// sub-vector; a centroid whose interval e~ - err(e~) reaches b~ + err(b~) is
-// evaluated in float64 in the direct form, exactly as a plain float64
-// evaluation rounds.  Every exact minimizer lies in the final window, which
-// is contained in the evaluated set, so the lexicographic (D, k) minimum of
-// the evaluated centroids is the exact argmin (ties to the lowest index).
-constexpr int kExactBatch = 4;
-
+// Exact re-search of the flagged sub-vectors: one wavefront per flagged
+// sub-vector (grid-stride), its lanes striding over the codebook.  For each
+// centroid the float32 expanded form e~ (a fused multiply-add chain over the
+// 16 terms: the search's rounding bound applies) is formed; a lane keeps a
+// running approximate minimum b~, and a centroid whose interval e~ - err(e~)
+// reaches b~ + err(b~) is evaluated in float64 in the direct form, exactly
+// as a plain float64 evaluation rounds.  Every exact minimizer lies in the
+// final window, which is contained in the evaluated set, so the
+// lexicographic (D, k) minimum over the wavefront is the exact argmin (ties
+// to the lowest index).  Dimensions >= d carry weight 0 and add exact zeros.
 __global__ __launch_bounds__(256) void k_assign_exact(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
     const uint8_t* __restrict__ mask, int64_t nb, int d, const float* __restrict__ C, int K,
     const int* __restrict__ flag_count, const int* __restrict__ flag_list,
-    uint16_t* __restrict__ idx, float* __restrict__ dist)
+    uint16_t* __restrict__ idx, float* __restrict__ dist, int vecC)
 {
-    __shared__ double sd[kExactBatch][256];
-    __shared__ int sk[kExactBatch][256];
     const int n = *flag_count;
+    const int lane = threadIdx.x & 63;
     const float u = 5.9604644775390625e-8f;
-    for (int f0 = blockIdx.x * kExactBatch; f0 < n; f0 += gridDim.x * kExactBatch) {
-        float x[kExactBatch][8], om[kExactBatch][8], bw[kExactBatch][8], S[kExactBatch], thr[kExactBatch];
-        double rr[kExactBatch], dbest[kExactBatch];
-        int arg[kExactBatch];
+    const int waves = gridDim.x * (blockDim.x >> 6);
+    for (int f = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); f < n; f += waves) {
+        const int64_t s = flag_list[f];
+        const int64_t i = s / nb, b = s - i * nb;
+        const unsigned mb = mask ? mask[s] : 0u;
+        const double rr = rho ? (double)rho[i] : 1.0;
+        float x[8], om[8], bw[8];
+        double w64[8];
+        float S = 0.f;
 #pragma unroll
-        for (int q = 0; q < kExactBatch; ++q) {
-            const bool live = f0 + q < n;
-            const int64_t s = live ? flag_list[f0 + q] : flag_list[f0];
-            const int64_t i = s / nb, b = s - (s / nb) * nb;
-            const unsigned mb = mask ? mask[s] : 0u;
-            rr[q] = rho ? (double)rho[i] : 1.0;
-            S[q] = 0.f;
-            for (int t = 0; t < 8; ++t) {
-                const float xv = t < d ? X[s * d + t] : 0.f;
-                const float w = (t < d && !((mb >> t) & 1u)) ? hcol[b * d + t] : 0.f;
-                x[q][t] = xv;
-                om[q][t] = w;
-                bw[q][t] = w * xv;
-                S[q] += w * xv * xv;
-            }
-            thr[q] = __builtin_inff();
-            dbest[q] = __builtin_inf();
-            arg[q] = K;
+        for (int t = 0; t < 8; ++t) {
+            const bool on = t < d;
+            x[t] = on ? X[s * d + t] : 0.f;
+            om[t] = (on && !((mb >> t) & 1u)) ? hcol[b * d + t] : 0.f;
+            bw[t] = om[t] * x[t];
+            S += om[t] * x[t] * x[t];
+            double w = (double)om[t];
+            if (rho) w = w * rr;
+            w64[t] = w;
         }
-        for (int k = threadIdx.x; k < K; k += blockDim.x) {
+        float thr = __builtin_inff();
+        double dbest = __builtin_inf();
+        int arg = K;
+        for (int k = lane; k < K; k += 64) {
             float c[8];
-            for (int t = 0; t < 8; ++t) c[t] = t < d ? C[(size_t)k * d + t] : 0.f;
+            if (vecC) {   // d == 8 and a 16-byte aligned codebook
+                const float4 ca = reinterpret_cast<const float4*>(C)[(size_t)k * 2];
+                const float4 cb = reinterpret_cast<const float4*>(C)[(size_t)k * 2 + 1];
+                c[0] = ca.x; c[1] = ca.y; c[2] = ca.z; c[3] = ca.w;
+                c[4] = cb.x; c[5] = cb.y; c[6] = cb.z; c[7] = cb.w;
+            } else {
 #pragma unroll
-            for (int q = 0; q < kExactBatch; ++q) {
-                float e = 0.f;
-                for (int t = 0; t < 8; ++t) e = fmaf(bw[q][t], -2.f * c[t], e);
-                for (int t = 0; t < 8; ++t) e = fmaf(om[q][t], c[t] * c[t], e);
-                const float err = 32.f * u * (9.f * S[q] + 4.f * fmaxf(e, -S[q])) + 1.0e-35f;
-                if (e - err <= thr[q]) {
-                    thr[q] = fminf(thr[q], e + err);
-                    double acc = 0.0;
-                    for (int t = 0; t < d; ++t) {
-                        double w = (double)om[q][t];
-                        if (rho) w = w * rr[q];
-                        const double diff = (double)x[q][t] - (double)c[t];
-                        const double sq = diff * diff;
-                        acc = acc + w * sq;
-                    }
-                    if (acc < dbest[q]) { dbest[q] = acc; arg[q] = k; }
+                for (int t = 0; t < 8; ++t) c[t] = t < d ? C[(size_t)k * d + t] : 0.f;
+            }
+            float e = 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) e = fmaf(bw[t], -2.f * c[t], e);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) e = fmaf(om[t], c[t] * c[t], e);
+            const float err = 32.f * u * (9.f * S + 4.f * fmaxf(e, -S)) + 1.0e-35f;
+            if (e - err <= thr) {
+                thr = fminf(thr, e + err);
+                double acc = 0.0;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const double diff = (double)x[t] - (double)c[t];
+                    const double sq = diff * diff;
+                    acc = acc + w64[t] * sq;
                 }
+                if (acc < dbest) { dbest = acc; arg = k; }
             }
         }
-#pragma unroll
-        for (int q = 0; q < kExactBatch; ++q) {
-            sd[q][threadIdx.x] = dbest[q];
-            sk[q][threadIdx.x] = arg[q];
+        for (int off = 32; off > 0; off >>= 1) {
+            const double od = __shfl_xor(dbest, off);
+            const int ok = __shfl_xor(arg, off);
+            if (od < dbest || (od == dbest && ok < arg)) { dbest = od; arg = ok; }
         }
-        __syncthreads();
-        for (int w = blockDim.x / 2; w > 0; w >>= 1) {
-            if ((int)threadIdx.x < w) {
-#pragma unroll
-                for (int q = 0; q < kExactBatch; ++q) {
-                    const double ov = sd[q][threadIdx.x + w];
-                    const int ok = sk[q][threadIdx.x + w];
-                    if (ov < sd[q][threadIdx.x] || (ov == sd[q][threadIdx.x] && ok < sk[q][threadIdx.x])) {
-                        sd[q][threadIdx.x] = ov;
-                        sk[q][threadIdx.x] = ok;
-                    }
-                }
-            }
-            __syncthreads();
+        if (lane == 0) {
+            idx[s] = (uint16_t)arg;
+            if (dist) dist[s] = (float)dbest;
         }
-        if ((int)threadIdx.x < kExactBatch && f0 + (int)threadIdx.x < n) {
-            const int64_t s = flag_list[f0 + threadIdx.x];
-            idx[s] = (uint16_t)sk[threadIdx.x][0];
-            if (dist) dist[s] = (float)sd[threadIdx.x][0];
-        }
-        __syncthreads();
     }
 }
 
@@ -567,8 +564,8 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
         if (mask) {
             hipLaunchKernelGGL(k_block_pattern, dim3((unsigned)nb), dim3(256), 0, st, mask, M, nb, pattern);
             VQ_LAUNCHED("k_block_pattern");
-            hipLaunchKernelGGL(k_dirty, dim3(grid_for(n_sub, 256)), dim3(256), 0, st, mask, pattern, n_sub, nb,
-                               dirty_count, dirty_list);
+            hipLaunchKernelGGL(k_dirty, dim3(grid_for(n_sub, 4096)), dim3(1024), 0, st, mask, pattern, n_sub,
+                               (uint32_t)nb, dirty_count, dirty_list);
             VQ_LAUNCHED("k_dirty");
         }
         hipLaunchKernelGGL(k_assign_mfma<true>, dim3(grid_for(groups, kWaves)), dim3(kWaves * 64), 0, st, X, hcol,
@@ -582,9 +579,10 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
             VQ_LAUNCHED("k_assign_mfma<general>");
         }
     }
-    const unsigned gx = (unsigned)std::min<int64_t>((n_sub + kExactBatch - 1) / kExactBatch, kExactBlocks);
+    const unsigned gx = (unsigned)std::min<int64_t>((n_sub + 3) / 4, kExactBlocks);
+    const int vecC = (d == 8 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0) ? 1 : 0;
     hipLaunchKernelGGL(k_assign_exact, dim3(gx), dim3(256), 0, st, X, hcol, rho, mask, nb, d, C, K,
-                       flag_count, flag_list, idx, dist);
+                       flag_count, flag_list, idx, dist, vecC);
     VQ_LAUNCHED("k_assign_exact");
     return VQ_OK;
 }

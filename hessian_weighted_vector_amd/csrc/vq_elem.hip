@@ -226,27 +226,49 @@ __global__ void k_sparse_overwrite(int64_t M, int64_t N, const int32_t* __restri
 }
 
 // ---- objective: per-block float64 partial sums of D(s, idx[s]) ----------
+// D in the direct form, float64, terms in t order.  An index >= K (a caller
+// error) makes J NaN instead of reading out of range.
 __global__ __launch_bounds__(kBlock) void k_objective_partial(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
-    const uint8_t* __restrict__ mask, int64_t n_sub, int64_t nb, int d,
-    const float* __restrict__ C, int K, const uint16_t* __restrict__ idx, double* __restrict__ part)
+    const uint8_t* __restrict__ mask, int64_t n_sub, uint32_t nb, int d,
+    const float* __restrict__ C, int K, const uint16_t* __restrict__ idx, int vec, double* __restrict__ part)
 {
     __shared__ double sh[kBlock];
     const int64_t s = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     double D = 0.0;
-    if (s < n_sub && idx[s] >= K) D = __builtin_nan("");
-    else if (s < n_sub) {
-        const int64_t i = s / nb;
-        const int64_t b = s - i * nb;
-        const unsigned mb = mask ? mask[s] : 0u;
-        const float* c = C + (size_t)idx[s] * d;
-        for (int t = 0; t < d; ++t) {
-            double w = (double)hcol[b * d + t];
-            if (rho) w = w * (double)rho[i];
-            if ((mb >> t) & 1u) w = 0.0;
-            const double diff = (double)X[s * d + t] - (double)c[t];
-            const double sq = diff * diff;
-            D = D + w * sq;
+    if (s < n_sub) {
+        const int k = idx[s];
+        if (k >= K) {
+            D = __builtin_nan("");
+        } else {
+            const uint32_t i = (uint32_t)(s / nb);
+            const uint32_t b = (uint32_t)s - i * nb;
+            const unsigned mb = mask ? mask[s] : 0u;
+            float x[8], c[8], h[8];
+            if (vec) {   // d == 8, 16-byte aligned buffers
+                const float4* x4 = reinterpret_cast<const float4*>(X + s * 8);
+                const float4* c4 = reinterpret_cast<const float4*>(C + (size_t)k * 8);
+                const float4* h4 = reinterpret_cast<const float4*>(hcol + (size_t)b * 8);
+                const float4 xa = x4[0], xb = x4[1], ca = c4[0], cb = c4[1], ha = h4[0], hb = h4[1];
+                x[0] = xa.x; x[1] = xa.y; x[2] = xa.z; x[3] = xa.w; x[4] = xb.x; x[5] = xb.y; x[6] = xb.z; x[7] = xb.w;
+                c[0] = ca.x; c[1] = ca.y; c[2] = ca.z; c[3] = ca.w; c[4] = cb.x; c[5] = cb.y; c[6] = cb.z; c[7] = cb.w;
+                h[0] = ha.x; h[1] = ha.y; h[2] = ha.z; h[3] = ha.w; h[4] = hb.x; h[5] = hb.y; h[6] = hb.z; h[7] = hb.w;
+            } else {
+                for (int t = 0; t < 8; ++t) {
+                    x[t] = t < d ? X[s * d + t] : 0.f;
+                    c[t] = t < d ? C[(size_t)k * d + t] : 0.f;
+                    h[t] = t < d ? hcol[(size_t)b * d + t] : 0.f;
+                }
+            }
+            const double rr = rho ? (double)rho[i] : 1.0;
+            for (int t = 0; t < d; ++t) {
+                double w = (double)h[t];
+                if (rho) w = w * rr;
+                if ((mb >> t) & 1u) w = 0.0;
+                const double diff = (double)x[t] - (double)c[t];
+                const double sq = diff * diff;
+                D = D + w * sq;
+            }
         }
     }
     const double tot = block_sum_f64(D, sh);
@@ -357,8 +379,9 @@ vq_status objective_launch(const float* X, const float* hcol, const float* rho, 
     double* part = cv.take<double>(nblk);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_objective: workspace too small");
     TimedRegion tr("objective", K, st);
+    const int vec = (d == 8 && aligned16(X) && aligned16(C) && aligned16(hcol)) ? 1 : 0;
     hipLaunchKernelGGL(k_objective_partial, dim3(nblk), dim3(kBlock), 0, st, X, hcol, rho, mask, n_sub,
-                       N / d, d, C, K, idx, part);
+                       (uint32_t)(N / d), d, C, K, idx, vec, part);
     VQ_LAUNCHED("k_objective_partial");
     hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kBlock), 0, st, part, (int64_t)nblk, J);
     VQ_LAUNCHED("k_sum_partials");

@@ -80,14 +80,15 @@ __global__ __launch_bounds__(256) void k_scan_digit(int* __restrict__ hist, int 
 }
 
 // Stable scatter of one block by the digit at `shift`.
-// vals_in == nullptr means the values are the element positions.
+// vals_in == nullptr means the values are the element positions; the tag
+// bytes (the sub-vector's mask, nullable) travel with the values.
 // Each wavefront ranks its own contiguous sub-tile of kSortItems*64 elements
 // (ballot match of equal digits, wave-private LDS counters), then one
 // cross-wave prefix per digit gives every element its position.
 __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
-    const uint16_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in, int64_t n, int shift,
-    const int* __restrict__ hist, const int* __restrict__ digit_total, int nblk,
-    uint16_t* __restrict__ keys_out, int32_t* __restrict__ vals_out)
+    const uint16_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in, const uint8_t* __restrict__ tag_in,
+    int64_t n, int shift, const int* __restrict__ hist, const int* __restrict__ digit_total, int nblk,
+    uint16_t* __restrict__ keys_out, int32_t* __restrict__ vals_out, uint8_t* __restrict__ tag_out)
 {
     __shared__ int sh[256];
     __shared__ int base[256];
@@ -107,6 +108,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
     const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint16_t key[kSortItems];
     int32_t val[kSortItems];
+    uint8_t tag[kSortItems];
     int rank[kSortItems];
 #pragma unroll
     for (int r = 0; r < kSortItems; ++r) {
@@ -114,6 +116,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
         const bool valid = e < n;
         key[r] = valid ? keys_in[e] : (uint16_t)0;
         val[r] = valid ? (vals_in ? vals_in[e] : (int32_t)e) : 0;
+        tag[r] = (valid && tag_in) ? tag_in[e] : (uint8_t)0;
         const int dg = (key[r] >> shift) & 255;
         unsigned long long peers = __ballot(valid);
         for (int bit = 0; bit < 8; ++bit) {
@@ -144,6 +147,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
             const int64_t pos = (int64_t)base[dg] + wcnt[wave][dg] + rank[r];
             keys_out[pos] = key[r];
             vals_out[pos] = val[r];
+            if (tag_out) tag_out[pos] = tag[r];
         }
     }
 }
@@ -165,14 +169,14 @@ __global__ void k_seg_start(const uint16_t* __restrict__ skeys, int64_t n, int K
 // Weight and value of element t of sub-vector s, float64 (weight = hcol,
 // times rho if present; 0 when masked).
 __device__ inline void member_term(const float* __restrict__ X, const float* __restrict__ hcol,
-                                   const float* __restrict__ rho, const uint8_t* __restrict__ mask,
+                                   const float* __restrict__ rho, unsigned mb,
                                    uint32_t s, uint32_t nb, int d, int t, double& w, double& x)
 {
     const uint32_t i = s / nb;
     const uint32_t b = s - i * nb;
     double wt = (double)hcol[(size_t)b * d + t];
     if (rho) wt = wt * (double)rho[i];
-    if (mask && ((mask[s] >> t) & 1u)) wt = 0.0;
+    if ((mb >> t) & 1u) wt = 0.0;
     w = wt;
     x = (double)X[(size_t)s * d + t];
 }
@@ -186,11 +190,12 @@ __device__ inline void member_term(const float* __restrict__ X, const float* __r
 // leaves to the right a "tail" partial, added in chunk order later.
 __global__ __launch_bounds__(256) void k_seg_chunks(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
-    const uint8_t* __restrict__ mask, uint32_t nb, int d, const uint16_t* __restrict__ skeys,
+    const uint8_t* __restrict__ smask, uint32_t nb, int d, const uint16_t* __restrict__ skeys,
     const int32_t* __restrict__ svals, const int* __restrict__ start, int64_t n, int64_t nchunks,
     float* __restrict__ C, int32_t* __restrict__ counts, double* __restrict__ head,
     double* __restrict__ tail)
 {
+    constexpr int kBatch = 8;   // members whose loads are issued together
     const int t = threadIdx.x & 7;
     const int64_t ch = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
     if (ch >= nchunks) return;
@@ -198,26 +203,38 @@ __global__ __launch_bounds__(256) void k_seg_chunks(
     const int64_t c1 = c0 + kChunk < n ? c0 + kChunk : n;
     int k = skeys[c0];
     double num = 0.0, den = 0.0;
-    for (int64_t e = c0; e < c1; ++e) {
-        const int ke = skeys[e];
-        if (ke != k) {
-            // segment k ends at e (inside this chunk)
-            const bool from_left = start[k] < c0;
-            if (from_left) {
-                if (t < d) { head[ch * 16 + t] = num; head[ch * 16 + 8 + t] = den; }
-            } else {
-                if (t < d && den > 0.0) C[(size_t)k * d + t] = (float)(num / den);
-                if (t == 0 && counts) counts[k] = start[k + 1] - start[k];
+    for (int64_t e0 = c0; e0 < c1; e0 += kBatch) {
+        int kk[kBatch];
+        double wv[kBatch], xv[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int64_t e = e0 + q;
+            kk[q] = -1;
+            wv[q] = 0.0;
+            xv[q] = 0.0;
+            if (e < c1) {
+                kk[q] = skeys[e];
+                if (t < d)
+                    member_term(X, hcol, rho, smask ? smask[e] : 0u, (uint32_t)svals[e], nb, d, t, wv[q], xv[q]);
             }
-            k = ke;
-            num = 0.0;
-            den = 0.0;
         }
-        if (t < d) {
-            double w, x;
-            member_term(X, hcol, rho, mask, (uint32_t)svals[e], nb, d, t, w, x);
-            num = num + w * x;
-            den = den + w;
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            if (kk[q] < 0) break;
+            if (kk[q] != k) {
+                // segment k ends inside this chunk
+                if (start[k] < c0) {
+                    if (t < d) { head[ch * 16 + t] = num; head[ch * 16 + 8 + t] = den; }
+                } else {
+                    if (t < d && den > 0.0) C[(size_t)k * d + t] = (float)(num / den);
+                    if (t == 0 && counts) counts[k] = start[k + 1] - start[k];
+                }
+                k = kk[q];
+                num = 0.0;
+                den = 0.0;
+            }
+            num = num + wv[q] * xv[q];
+            den = den + wv[q];
         }
     }
     // the last segment of the chunk
@@ -235,37 +252,45 @@ __global__ __launch_bounds__(256) void k_seg_chunks(
     }
 }
 
-// Segments that cross chunk boundaries: tail of the first chunk plus heads of
-// the following ones, in order; 8 lanes per centroid.  Empty centroids get a
-// zero count and keep their value.
-__global__ __launch_bounds__(256) void k_seg_cross(const int* __restrict__ start, int K, int d,
-                                                   const double* __restrict__ head,
-                                                   const double* __restrict__ tail,
-                                                   float* __restrict__ C, int32_t* __restrict__ counts)
+// Segments that cross chunk boundaries: the tail of the first chunk plus the
+// heads of the following ones.  One wavefront per centroid: lane q adds
+// chunks j0+1+q, j0+1+q+64, ... in order, then a fixed xor butterfly over
+// the lanes; 16 values per chunk (8 sums of omega*x, 8 of omega).  Empty
+// centroids get a zero count and keep their value.
+__global__ __launch_bounds__(64) void k_seg_cross(const int* __restrict__ start, int K, int d,
+                                                  const double* __restrict__ head,
+                                                  const double* __restrict__ tail,
+                                                  float* __restrict__ C, int32_t* __restrict__ counts)
 {
-    const int t = threadIdx.x & 7;
-    const int k = blockIdx.x * 32 + (threadIdx.x >> 3);
-    if (k >= K) return;
+    const int k = blockIdx.x;
+    const int lane = threadIdx.x;
     const int s0 = start[k], s1 = start[k + 1];
     if (s1 == s0) {
-        if (t == 0 && counts) counts[k] = 0;
+        if (lane == 0 && counts) counts[k] = 0;
         return;
     }
     const int64_t j0 = s0 / kChunk, j1 = (int64_t)(s1 - 1) / kChunk;
     if (j0 == j1) return;   // finished inside its chunk
-    if (t == 0 && counts) counts[k] = s1 - s0;
-    if (t >= d) return;
-    double num = tail[j0 * 16 + t], den = tail[j0 * 16 + 8 + t];
-    for (int64_t j = j0 + 1; j <= j1; ++j) {
-        num = num + head[j * 16 + t];
-        den = den + head[j * 16 + 8 + t];
+    if (lane == 0 && counts) counts[k] = s1 - s0;
+    double acc[16];
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0;
+    for (int64_t j = j0 + 1 + lane; j <= j1; j += 64)
+        for (int v = 0; v < 16; ++v) acc[v] = acc[v] + head[j * 16 + v];
+    for (int off = 32; off > 0; off >>= 1)
+        for (int v = 0; v < 16; ++v) acc[v] = acc[v] + __shfl_xor(acc[v], off);
+    if (lane < d) {
+        double num = tail[j0 * 16 + lane], den = tail[j0 * 16 + 8 + lane];
+        for (int v = 0; v < 8; ++v) {   // select this lane's dimension without dynamic indexing
+            if (v == lane) { num = num + acc[v]; den = den + acc[8 + v]; }
+        }
+        if (den > 0.0) C[(size_t)k * d + lane] = (float)(num / den);
     }
-    if (den > 0.0) C[(size_t)k * d + t] = (float)(num / den);
 }
 
 struct UpdateWs {
     uint16_t *k1, *k2;
     int32_t *v1, *v2;
+    uint8_t *g1, *g2;
     int *hist, *dtot, *start;
     double *head, *tail;
 };
@@ -280,6 +305,8 @@ UpdateWs carve_update(Carver& cv, int64_t n_sub, int K)
     w.k2 = cv.take<uint16_t>(n_sub);
     w.v1 = cv.take<int32_t>(n_sub);
     w.v2 = cv.take<int32_t>(n_sub);
+    w.g1 = cv.take<uint8_t>(n_sub);
+    w.g2 = cv.take<uint8_t>(n_sub);
     w.hist = cv.take<int>((size_t)256 * nblk);
     w.dtot = cv.take<int>(256);
     w.start = cv.take<int>((size_t)K + 1);
@@ -313,8 +340,10 @@ vq_status update_launch(const float* X, const float* hcol, const float* rho, con
     const int passes = K > 256 ? 2 : 1;
     const uint16_t* kin = idx;
     const int32_t* vin = nullptr;
+    const uint8_t* gin = mask;
     uint16_t* kout = w.k1;
     int32_t* vout = w.v1;
+    uint8_t* gout = mask ? w.g1 : nullptr;
     for (int p = 0; p < passes; ++p) {
         const int shift = 8 * p;
         hipLaunchKernelGGL(k_sort_hist, dim3(nblk), dim3(kSortThreads), 0, st, kin, n_sub, shift, w.hist,
@@ -322,25 +351,27 @@ vq_status update_launch(const float* X, const float* hcol, const float* rho, con
         VQ_LAUNCHED("k_sort_hist");
         hipLaunchKernelGGL(k_scan_digit, dim3(256), dim3(256), 0, st, w.hist, nblk, w.dtot);
         VQ_LAUNCHED("k_scan_digit");
-        hipLaunchKernelGGL(k_sort_scatter, dim3(nblk), dim3(kSortThreads), 0, st, kin, vin, n_sub, shift,
-                           w.hist, w.dtot, nblk, kout, vout);
+        hipLaunchKernelGGL(k_sort_scatter, dim3(nblk), dim3(kSortThreads), 0, st, kin, vin, gin, n_sub, shift,
+                           w.hist, w.dtot, nblk, kout, vout, gout);
         VQ_LAUNCHED("k_sort_scatter");
         kin = kout;
         vin = vout;
+        gin = gout;
         kout = (kout == w.k1) ? w.k2 : w.k1;
         vout = (vout == w.v1) ? w.v2 : w.v1;
+        gout = mask ? ((gout == w.g1) ? w.g2 : w.g1) : nullptr;
     }
     const uint16_t* skeys = kin;
     const int32_t* svals = vin;
+    const uint8_t* smask = gin;
     hipLaunchKernelGGL(k_seg_start, dim3(grid_for((int64_t)K + 1, 256)), dim3(256), 0, st, skeys, n_sub, K,
                        w.start);
     VQ_LAUNCHED("k_seg_start");
     const int64_t nch = n_chunks(n_sub);
-    hipLaunchKernelGGL(k_seg_chunks, dim3(grid_for(nch, 32)), dim3(256), 0, st, X, hcol, rho, mask,
+    hipLaunchKernelGGL(k_seg_chunks, dim3(grid_for(nch, 32)), dim3(256), 0, st, X, hcol, rho, smask,
                        (uint32_t)(N / d), d, skeys, svals, w.start, n_sub, nch, C, counts, w.head, w.tail);
     VQ_LAUNCHED("k_seg_chunks");
-    hipLaunchKernelGGL(k_seg_cross, dim3(grid_for(K, 32)), dim3(256), 0, st, w.start, K, d, w.head, w.tail, C,
-                       counts);
+    hipLaunchKernelGGL(k_seg_cross, dim3((unsigned)K), dim3(64), 0, st, w.start, K, d, w.head, w.tail, C, counts);
     VQ_LAUNCHED("k_seg_cross");
     return VQ_OK;
 }
