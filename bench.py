@@ -99,6 +99,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="print per-step timings to stderr")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, copy a buffer of this many MiB three times (a plain "
+                         "copy of known size, to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -134,6 +137,14 @@ def main():
     t1 = time.perf_counter()
     recs = vq.timing_records()
     vq.timing_enable(False)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     n_sub = cfg.n_sub
