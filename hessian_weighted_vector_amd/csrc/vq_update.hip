@@ -4,27 +4,58 @@
 // exact minimizer of the objective is the per-dimension weighted mean).
 //
 // Design (no floating-point atomics; bitwise deterministic):
-//   1. binning: stable LSD radix sort of (index, sub-vector id) pairs, 8-bit
-//      digits (one pass when K <= 256, else two).  Per-block digit counts use
-//      LDS integer atomics (exact), block offsets come from a scan, and
-//      ranks inside a block come from wavefront ballots, so equal indices
-//      keep ascending sub-vector order;
-//   2. segment starts by binary search of the sorted indices;
-//   3. the sorted array is cut into fixed chunks; 8 lanes (one per
-//      dimension) walk a chunk in order with float64 sums of omega*x and
-//      omega, finishing the segments that lie inside it and leaving partial
-//      sums for the two that cross its ends;
-//   4. 8 lanes per crossing centroid add those partials in chunk order and
-//      divide once.
+//   1. buckets (K > 256 only): one stable scatter by idx >> 7 moves whole
+//      records (the sub-vector's d values and a word holding its id, mask
+//      byte and idx & 127) into 128-centroid buckets, so no sub-vector is
+//      gathered at random later.  Each 2048-record tile is ordered by bucket
+//      in LDS first (ranks from wavefront ballots: stable), then written out
+//      as contiguous runs.  Tile digit counts use LDS integer atomics
+//      (exact) and tile offsets come from a scan.  With K <= 256 the whole
+//      matrix is one bucket of up to 256 centroids, read in place;
+//   2. each bucket is cut into fixed pieces; a workgroup streams its piece
+//      through LDS in sub-chunks of 1024 records, stages each record's x,
+//      its column weights (zero where masked) and its row weight, counting-
+//      sorts the sub-chunk by centroid (stable), and 8-lane groups that own
+//      fixed centroids add their members in order into float64 sums of
+//      omega*x and omega kept in registers.  A bucket that fits one piece
+//      is finished there (members in ascending sub-vector order, the order
+//      of a plain sequential sum);
+//   3. buckets with several pieces: one pass adds the pieces' partial sums
+//      in a fixed order and divides once.
 #include "vq_internal.h"
+
+#include <algorithm>
 
 namespace vq {
 namespace {
 
-constexpr int kSortThreads = 256;
-constexpr int kSortItems = 16;
-constexpr int kSortTile = kSortThreads * kSortItems;   // elements per sort block
-constexpr int kChunk = 64;                              // sorted members per 8-lane group
+constexpr int kTile = 2048;          // records per scatter tile
+constexpr int kTileThreads = 1024;   // two records per thread
+constexpr int kMaxBuckets = 512;     // K <= 65536, 128 centroids per bucket
+constexpr int kBucketShift = 7;
+constexpr int kSub = 1024;           // records per LDS sub-chunk (one per thread)
+constexpr int kRedThreads = 1024;
+constexpr int kPieceMax = 32768;     // records per piece in bucket mode
+constexpr int kDirectPieces = 512;   // target piece count with one bucket
+
+// Per-tile bucket histogram: hist[bucket * ntile + tile].
+__global__ __launch_bounds__(256) void k_bucket_hist(const uint16_t* __restrict__ idx, int64_t n, int nbk,
+                                                     int* __restrict__ hist, int ntile)
+{
+    __shared__ int cnt[kMaxBuckets];
+    for (int q = threadIdx.x; q < kMaxBuckets; q += 256) cnt[q] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kTile;
+    for (int q = threadIdx.x; q < kTile; q += 256) {
+        const int64_t e = base + q;
+        if (e < n) {
+            const int bk = idx[e] >> kBucketShift;
+            if (bk < nbk) atomicAdd(&cnt[bk], 1);
+        }
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < nbk; q += 256) hist[(int64_t)q * ntile + blockIdx.x] = cnt[q];
+}
 
 // Inclusive scan of one int per thread over a 256-thread block.
 __device__ inline int block_incl_scan_256(int v, int* sh)
@@ -42,276 +73,431 @@ __device__ inline int block_incl_scan_256(int v, int* sh)
     return r;
 }
 
-// Per-block digit histogram: hist[digit * nblk + block].
-__global__ __launch_bounds__(kSortThreads) void k_sort_hist(const uint16_t* __restrict__ keys,
-                                                            int64_t n, int shift,
-                                                            int* __restrict__ hist, int nblk)
-{
-    __shared__ int cnt[256];
-    cnt[threadIdx.x] = 0;
-    __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kSortTile;
-    for (int q = threadIdx.x; q < kSortTile; q += kSortThreads) {
-        const int64_t e = base + q;
-        if (e < n) atomicAdd(&cnt[(keys[e] >> shift) & 255], 1);
-    }
-    __syncthreads();
-    hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = cnt[threadIdx.x];
-}
-
-// One block per digit: exclusive scan of its per-block counts, in place;
-// digit_total[digit] = the digit's count.
-__global__ __launch_bounds__(256) void k_scan_digit(int* __restrict__ hist, int nblk,
-                                                    int* __restrict__ digit_total)
+// One block per bucket: exclusive scan of its per-tile counts, in place;
+// total[bucket] = the bucket's size.
+__global__ __launch_bounds__(256) void k_bucket_scan(int* __restrict__ hist, int ntile, int* __restrict__ total)
 {
     __shared__ int sh[256];
-    int* row = hist + (int64_t)blockIdx.x * nblk;
+    int* row = hist + (int64_t)blockIdx.x * ntile;
     int carry = 0;
-    for (int c0 = 0; c0 < nblk; c0 += 256) {
+    for (int c0 = 0; c0 < ntile; c0 += 256) {
         const int q = c0 + threadIdx.x;
-        const int v = q < nblk ? row[q] : 0;
-        const int inc = block_incl_scan_256(v, sh);   // leaves the inclusive sums in sh
+        const int v = q < ntile ? row[q] : 0;
+        const int inc = block_incl_scan_256(v, sh);
         const int chunk_total = sh[255];
-        if (q < nblk) row[q] = carry + inc - v;
+        if (q < ntile) row[q] = carry + inc - v;
         carry += chunk_total;
         __syncthreads();
     }
-    if (threadIdx.x == 0) digit_total[blockIdx.x] = carry;
+    if (threadIdx.x == 0) total[blockIdx.x] = carry;
 }
 
-// Stable scatter of one block by the digit at `shift`.
-// vals_in == nullptr means the values are the element positions; the tag
-// bytes (the sub-vector's mask, nullable) travel with the values.
-// Each wavefront ranks its own contiguous sub-tile of kSortItems*64 elements
-// (ballot match of equal digits, wave-private LDS counters), then one
-// cross-wave prefix per digit gives every element its position.
-__global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
-    const uint16_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in, const uint8_t* __restrict__ tag_in,
-    int64_t n, int shift, const int* __restrict__ hist, const int* __restrict__ digit_total, int nblk,
-    uint16_t* __restrict__ keys_out, int32_t* __restrict__ vals_out, uint8_t* __restrict__ tag_out)
+// Bucket starts and piece numbering (one thread): bucket b holds records
+// [bstart[b], bstart[b+1]) and is cut into ceil(size / piece) pieces,
+// numbered from poff[b].  total == nullptr: one bucket of n records.
+__global__ void k_piece_setup(const int* __restrict__ total, int nbk, int64_t n, int piece,
+                              int64_t* __restrict__ bstart, int* __restrict__ poff)
 {
-    __shared__ int sh[256];
-    __shared__ int base[256];
-    __shared__ int wcnt[4][256];
+    if (threadIdx.x != 0) return;
+    int64_t run = 0;
+    int pr = 0;
+    for (int b = 0; b < nbk; ++b) {
+        const int64_t sz = total ? (int64_t)total[b] : n;
+        bstart[b] = run;
+        poff[b] = pr;
+        run += sz;
+        pr += (int)((sz + piece - 1) / piece);
+    }
+    bstart[nbk] = run;
+    poff[nbk] = pr;
+}
+
+// Stable ranks of up to 64 keys (< 2^bits) across one wavefront: peers =
+// lanes holding the same key; returns the lane's rank among its peers.
+__device__ inline int wave_peer_rank(int key, bool valid, int bits, unsigned long long lt_mask,
+                                     unsigned long long& peers)
+{
+    peers = __ballot(valid);
+    for (int bit = 0; bit < bits; ++bit) {
+        const unsigned long long bal = __ballot(valid && ((key >> bit) & 1));
+        peers &= ((key >> bit) & 1) ? bal : ~bal;
+    }
+    return __popcll(peers & lt_mask);
+}
+
+// Exclusive scan of cnt[0..n) (n <= 512) by the first wavefront, into out;
+// out[n] = total.  Callers synchronize around it.
+template <class T>
+__device__ inline void wave_excl_scan(const int* cnt, int n, T* out)
+{
+    const int lane = threadIdx.x;
+    if (lane >= 64) return;
+    const int per = (n + 63) / 64;
+    int s = 0;
+    for (int u = 0; u < per; ++u) {
+        const int q = lane * per + u;
+        s += q < n ? cnt[q] : 0;
+    }
+    int inc = s;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(inc, off);
+        if (lane >= off) inc += o;
+    }
+    int run = inc - s;
+    for (int u = 0; u < per; ++u) {
+        const int q = lane * per + u;
+        if (q < n) { out[q] = (T)run; run += cnt[q]; }
+    }
+    if (lane == 63) out[n] = (T)run;
+}
+
+// Stable scatter of whole records into buckets.  A tile of kTile records is
+// ranked by bucket (wavefront ballots + a prefix over the wavefronts), laid
+// out in bucket order in LDS, and written to its place in each bucket as
+// contiguous runs: rx gets the d values, rw the word
+//   id | (idx & 127) << 32 | mask << 40.
+__global__ __launch_bounds__(kTileThreads) void k_bucket_scatter(
+    const uint16_t* __restrict__ idx, const uint8_t* __restrict__ mask, const float* __restrict__ X, int d,
+    int64_t n, int nbk, const int* __restrict__ hist, int ntile, const int64_t* __restrict__ bstart,
+    float* __restrict__ rx, uint64_t* __restrict__ rw)
+{
+    __shared__ __align__(16) float sxr[kTile * 8];
+    __shared__ uint64_t sw[kTile];
+    __shared__ uint16_t sdg[kTile];
+    __shared__ uint16_t wcnt[kTileThreads / 64][kMaxBuckets];
+    __shared__ int tcnt[kMaxBuckets];
+    __shared__ int tstart[kMaxBuckets + 1];
+    __shared__ int64_t gbase[kMaxBuckets];
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-
-    // global start of each digit for this block
-    const int tot = digit_total[tid];
-    const int incl = block_incl_scan_256(tot, sh);
-    base[tid] = (incl - tot) + hist[(int64_t)tid * nblk + blockIdx.x];
-    for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
+    const int64_t e0 = (int64_t)blockIdx.x * kTile;
+    const int m = (int)min((int64_t)kTile, n - e0);
+    for (int q = tid; q < (kTileThreads / 64) * kMaxBuckets; q += kTileThreads) (&wcnt[0][0])[q] = 0;
+    for (int q = tid; q < nbk; q += kTileThreads)
+        gbase[q] = bstart[q] + hist[(int64_t)q * ntile + blockIdx.x];
     __syncthreads();
-
-    const int64_t wave0 = (int64_t)blockIdx.x * kSortTile + (int64_t)wave * (kSortItems * 64);
     const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    uint16_t key[kSortItems];
-    int32_t val[kSortItems];
-    uint8_t tag[kSortItems];
-    int rank[kSortItems];
+    int bits = 0;
+    while ((1 << bits) < nbk) ++bits;
+    int dg[2], rank[2], r_of[2];
+    uint16_t iv[2];
 #pragma unroll
-    for (int r = 0; r < kSortItems; ++r) {
-        const int64_t e = wave0 + (int64_t)r * 64 + lane;
-        const bool valid = e < n;
-        key[r] = valid ? keys_in[e] : (uint16_t)0;
-        val[r] = valid ? (vals_in ? vals_in[e] : (int32_t)e) : 0;
-        tag[r] = (valid && tag_in) ? tag_in[e] : (uint8_t)0;
-        const int dg = (key[r] >> shift) & 255;
-        unsigned long long peers = __ballot(valid);
-        for (int bit = 0; bit < 8; ++bit) {
-            const unsigned long long bal = __ballot(valid && ((dg >> bit) & 1));
-            peers &= ((dg >> bit) & 1) ? bal : ~bal;
-        }
-        const int wrank = __popcll(peers & lt_mask);
+    for (int h = 0; h < 2; ++h) {
+        const int r = wave * 128 + h * 64 + lane;
+        r_of[h] = r;
+        iv[h] = r < m ? idx[e0 + r] : (uint16_t)0;
+        const bool valid = r < m && (iv[h] >> kBucketShift) < nbk;
+        dg[h] = valid ? (iv[h] >> kBucketShift) : 0;
+        unsigned long long peers;
+        const int wr = wave_peer_rank(dg[h], valid, bits, lt_mask, peers);
         int run = 0;
-        if (valid) run = wcnt[wave][dg];
-        rank[r] = valid ? run + wrank : -1;
-        if (valid && wrank == 0) wcnt[wave][dg] = run + __popcll(peers);
+        if (valid) run = wcnt[wave][dg[h]];
+        rank[h] = valid ? run + wr : -1;
+        if (valid && wr == 0) wcnt[wave][dg[h]] = (uint16_t)(run + __popcll(peers));
     }
     __syncthreads();
-    // offsets of each wavefront's part of each digit: prefix over the waves
-    {
+    for (int q = tid; q < nbk; q += kTileThreads) {
         int acc = 0;
-        for (int w = 0; w < 4; ++w) {
-            const int c = wcnt[w][tid];
-            wcnt[w][tid] = acc;
+        for (int w = 0; w < kTileThreads / 64; ++w) {
+            const int c = wcnt[w][q];
+            wcnt[w][q] = (uint16_t)acc;
             acc += c;
         }
+        tcnt[q] = acc;
     }
     __syncthreads();
+    wave_excl_scan(tcnt, nbk, tstart);
+    __syncthreads();
+    const bool vec = (d == 8) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
 #pragma unroll
-    for (int r = 0; r < kSortItems; ++r) {
-        if (rank[r] >= 0) {
-            const int dg = (key[r] >> shift) & 255;
-            const int64_t pos = (int64_t)base[dg] + wcnt[wave][dg] + rank[r];
-            keys_out[pos] = key[r];
-            vals_out[pos] = val[r];
-            if (tag_out) tag_out[pos] = tag[r];
+    for (int h = 0; h < 2; ++h) {
+        if (rank[h] < 0) continue;
+        const int lp = tstart[dg[h]] + wcnt[wave][dg[h]] + rank[h];
+        const int64_t e = e0 + r_of[h];
+        if (vec) {
+            const float4* src = reinterpret_cast<const float4*>(X + e * 8);
+            float4* dst = reinterpret_cast<float4*>(sxr + lp * 8);
+            dst[0] = src[0];
+            dst[1] = src[1];
+        } else {
+            for (int t = 0; t < d; ++t) sxr[lp * 8 + t] = X[e * d + t];
         }
+        const uint64_t mk = mask ? (uint64_t)mask[e] : 0ull;
+        sw[lp] = (uint64_t)(uint32_t)e | ((uint64_t)(iv[h] & 127) << 32) | (mk << 40);
+        sdg[lp] = (uint16_t)dg[h];
+    }
+    __syncthreads();
+    const int mv = tstart[nbk];   // records with a valid bucket
+    for (int lp = tid; lp < mv; lp += kTileThreads) {
+        const int b = sdg[lp];
+        const int64_t pos = gbase[b] + (lp - tstart[b]);
+        if (d == 8) {
+            const float4* src = reinterpret_cast<const float4*>(sxr + lp * 8);
+            float4* dst = reinterpret_cast<float4*>(rx + pos * 8);
+            dst[0] = src[0];
+            dst[1] = src[1];
+        } else {
+            for (int t = 0; t < d; ++t) rx[pos * d + t] = sxr[lp * 8 + t];
+        }
+        rw[pos] = sw[lp];
     }
 }
 
-// start[k] = first position of key k in the sorted keys (k = 0..K).
-__global__ void k_seg_start(const uint16_t* __restrict__ skeys, int64_t n, int K,
-                            int* __restrict__ start)
+// One workgroup per piece.  The piece goes through LDS in sub-chunks of
+// kSub records, one per thread: the thread stages the record's x, its
+// column weights hcol (zero where the mask bit is set) and its row weight
+// rho, and ranks it by centroid within the sub-chunk (stable counting
+// sort).  Then 8-lane group g (lane t = dimension t) walks the members of
+// its centroids (g, and g + 128 when a bucket spans 256 centroids) in record
+// order, adding omega_t x_t and omega_t (omega = hcol * rho in float64, the
+// product of two floats, exact) into float64 sums kept in registers.
+// rx == nullptr: one bucket of up to 256 centroids read in place from X,
+// idx and mask.
+__global__ __launch_bounds__(kRedThreads) void k_piece_reduce(
+    const float* __restrict__ rx, const uint64_t* __restrict__ rw, const float* __restrict__ X,
+    const uint16_t* __restrict__ idx, const uint8_t* __restrict__ mask, const float* __restrict__ hcol,
+    const float* __restrict__ rho, uint32_t nb, int d, int K, int nbk, int piece,
+    const int64_t* __restrict__ bstart, const int* __restrict__ poff, float* __restrict__ C,
+    int32_t* __restrict__ counts, double* __restrict__ partial)
 {
-    const int k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k > K) return;
-    int64_t lo = 0, hi = n;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        if ((int)skeys[mid] < k) lo = mid + 1; else hi = mid;
+    __shared__ __align__(16) float sx[kSub * 8];
+    __shared__ __align__(16) float shv[kSub * 8];
+    __shared__ float srho[kSub];
+    __shared__ uint16_t perm[kSub];
+    __shared__ uint16_t wcnt[kRedThreads / 64][256];
+    __shared__ uint16_t cstart[257];
+    __shared__ int ccount[256];
+
+    const int j = blockIdx.x;
+    if (j >= poff[nbk]) return;
+    int bk = 0;
+    {
+        int lo = 0, hi = nbk;   // poff[lo] <= j < poff[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (poff[mid] <= j) lo = mid; else hi = mid;
+        }
+        bk = lo;
     }
-    start[k] = (int)lo;
-}
+    const bool direct = (rx == nullptr);
+    const int width = direct ? 256 : 128;     // centroids per bucket
+    const int kbits = direct ? 8 : 7;
+    const int q = j - poff[bk];
+    const int npieces = poff[bk + 1] - poff[bk];
+    const int64_t p0 = bstart[bk] + (int64_t)q * piece;
+    const int64_t p1 = min(bstart[bk + 1], p0 + (int64_t)piece);
 
-// Weight and value of element t of sub-vector s, float64 (weight = hcol,
-// times rho if present; 0 when masked).
-__device__ inline void member_term(const float* __restrict__ X, const float* __restrict__ hcol,
-                                   const float* __restrict__ rho, unsigned mb,
-                                   uint32_t s, uint32_t nb, int d, int t, double& w, double& x)
-{
-    const uint32_t i = s / nb;
-    const uint32_t b = s - i * nb;
-    double wt = (double)hcol[(size_t)b * d + t];
-    if (rho) wt = wt * (double)rho[i];
-    if ((mb >> t) & 1u) wt = 0.0;
-    w = wt;
-    x = (double)X[(size_t)s * d + t];
-}
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int t = tid & 7;
+    const int g = tid >> 3;            // 128 groups
+    const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const bool vx = (d == 8) && ((reinterpret_cast<uintptr_t>(direct ? X : rx) & 15) == 0);
+    const bool vh = (d == 8) && ((reinterpret_cast<uintptr_t>(hcol) & 15) == 0);
+    double num[2] = {0.0, 0.0}, den[2] = {0.0, 0.0};
+    int count[2] = {0, 0};
 
-// Chunked segmented reduction over the sorted (index, sub-vector) pairs.
-// The sorted array is cut into fixed chunks of kChunk members; a group of 8
-// lanes owns one chunk (lane t = dimension t) and walks it in order with
-// float64 sums of omega*x and omega.  A segment (all members of one
-// centroid) that lies inside the chunk is finished here; the segment that
-// enters the chunk from the left leaves a "head" partial and the one that
-// leaves to the right a "tail" partial, added in chunk order later.
-__global__ __launch_bounds__(256) void k_seg_chunks(
-    const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
-    const uint8_t* __restrict__ smask, uint32_t nb, int d, const uint16_t* __restrict__ skeys,
-    const int32_t* __restrict__ svals, const int* __restrict__ start, int64_t n, int64_t nchunks,
-    float* __restrict__ C, int32_t* __restrict__ counts, double* __restrict__ head,
-    double* __restrict__ tail)
-{
-    constexpr int kBatch = 8;   // members whose loads are issued together
-    const int t = threadIdx.x & 7;
-    const int64_t ch = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
-    if (ch >= nchunks) return;
-    const int64_t c0 = ch * kChunk;
-    const int64_t c1 = c0 + kChunk < n ? c0 + kChunk : n;
-    int k = skeys[c0];
-    double num = 0.0, den = 0.0;
-    for (int64_t e0 = c0; e0 < c1; e0 += kBatch) {
-        int kk[kBatch];
-        double wv[kBatch], xv[kBatch];
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-            const int64_t e = e0 + q;
-            kk[q] = -1;
-            wv[q] = 0.0;
-            xv[q] = 0.0;
-            if (e < c1) {
-                kk[q] = skeys[e];
-                if (t < d)
-                    member_term(X, hcol, rho, smask ? smask[e] : 0u, (uint32_t)svals[e], nb, d, t, wv[q], xv[q]);
+    for (int64_t c0 = p0; c0 < p1; c0 += kSub) {
+        const int m = (int)min((int64_t)kSub, p1 - c0);
+        // ---- stage record tid ----
+        const int r = tid;
+        const bool valid = r < m;
+        int key = 0;
+        if (valid) {
+            const int64_t e = c0 + r;
+            uint32_t sv, mk;
+            if (direct) {
+                sv = (uint32_t)e;
+                mk = mask ? mask[e] : 0u;
+                key = idx[e] & 255;
+            } else {
+                const uint64_t wd = rw[e];
+                sv = (uint32_t)wd;
+                key = (int)((wd >> 32) & 127);
+                mk = (uint32_t)((wd >> 40) & 255);
             }
-        }
+            const uint32_t i = sv / nb;
+            const uint32_t b = sv - i * nb;
+            srho[r] = rho ? rho[i] : 1.0f;
+            const float* xs = direct ? X + e * d : rx + e * d;
+            if (vx) {
+                const float4 a0 = reinterpret_cast<const float4*>(xs)[0];
+                const float4 a1 = reinterpret_cast<const float4*>(xs)[1];
+                reinterpret_cast<float4*>(sx + r * 8)[0] = a0;
+                reinterpret_cast<float4*>(sx + r * 8)[1] = a1;
+            } else {
+                for (int u = 0; u < d; ++u) sx[r * 8 + u] = xs[u];
+            }
+            const float* hs = hcol + (size_t)b * d;
+            float hv[8];
+            if (vh) {
+                const float4 a0 = reinterpret_cast<const float4*>(hs)[0];
+                const float4 a1 = reinterpret_cast<const float4*>(hs)[1];
+                hv[0] = a0.x; hv[1] = a0.y; hv[2] = a0.z; hv[3] = a0.w;
+                hv[4] = a1.x; hv[5] = a1.y; hv[6] = a1.z; hv[7] = a1.w;
+            } else {
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-            if (kk[q] < 0) break;
-            if (kk[q] != k) {
-                // segment k ends inside this chunk
-                if (start[k] < c0) {
-                    if (t < d) { head[ch * 16 + t] = num; head[ch * 16 + 8 + t] = den; }
-                } else {
-                    if (t < d && den > 0.0) C[(size_t)k * d + t] = (float)(num / den);
-                    if (t == 0 && counts) counts[k] = start[k + 1] - start[k];
+                for (int u = 0; u < 8; ++u) hv[u] = u < d ? hs[u] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) shv[r * 8 + u] = ((mk >> u) & 1u) ? 0.0f : hv[u];
+        }
+        for (int v = tid; v < (kRedThreads / 64) * 256; v += kRedThreads) (&wcnt[0][0])[v] = 0;
+        __syncthreads();
+        // ---- stable rank of record tid by centroid ----
+        unsigned long long peers;
+        const int wr = wave_peer_rank(key, valid, kbits, lt_mask, peers);
+        int rnk = -1;
+        {
+            int run = 0;
+            if (valid) run = wcnt[wave][key];
+            if (valid) rnk = run + wr;
+            if (valid && wr == 0) wcnt[wave][key] = (uint16_t)(run + __popcll(peers));
+        }
+        __syncthreads();
+        if (tid < width) {
+            int acc = 0;
+            for (int w = 0; w < kRedThreads / 64; ++w) {
+                const int c = wcnt[w][tid];
+                wcnt[w][tid] = (uint16_t)acc;
+                acc += c;
+            }
+            ccount[tid] = acc;
+        }
+        __syncthreads();
+        wave_excl_scan(ccount, width, cstart);
+        __syncthreads();
+        if (valid) perm[cstart[key] + wcnt[wave][key] + rnk] = (uint16_t)r;
+        __syncthreads();
+        // ---- per owned centroid, members in record order ----
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+            const int c = g + o * 128;
+            if (c >= width) break;
+            const int b0 = cstart[c], b1 = cstart[c + 1];
+            count[o] += b1 - b0;
+            int e = b0;
+            for (; e + 4 <= b1; e += 4) {
+                double w[4], x[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int rr = perm[e + u];
+                    w[u] = (double)shv[rr * 8 + t] * (double)srho[rr];
+                    x[u] = (double)sx[rr * 8 + t];
                 }
-                k = kk[q];
-                num = 0.0;
-                den = 0.0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    num[o] = num[o] + w[u] * x[u];
+                    den[o] = den[o] + w[u];
+                }
             }
-            num = num + wv[q] * xv[q];
-            den = den + wv[q];
+            for (; e < b1; ++e) {
+                const int rr = perm[e];
+                const double w = (double)shv[rr * 8 + t] * (double)srho[rr];
+                num[o] = num[o] + w * (double)sx[rr * 8 + t];
+                den[o] = den[o] + w;
+            }
         }
+        __syncthreads();
     }
-    // the last segment of the chunk
-    const bool from_left = start[k] < c0;
-    const bool to_right = start[k + 1] > c1;
-    if (to_right) {
-        // continues in the next chunk: a tail, or a head when it also came from the left
-        double* dst = from_left ? head : tail;
-        if (t < d) { dst[ch * 16 + t] = num; dst[ch * 16 + 8 + t] = den; }
-    } else if (from_left) {
-        if (t < d) { head[ch * 16 + t] = num; head[ch * 16 + 8 + t] = den; }
-    } else {
-        if (t < d && den > 0.0) C[(size_t)k * d + t] = (float)(num / den);
-        if (t == 0 && counts) counts[k] = start[k + 1] - start[k];
+    // ---- results ----
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+        const int c = g + o * 128;
+        if (c >= width) break;
+        const int k = bk * width + c;
+        if (k >= K) continue;
+        if (npieces == 1) {
+            if (t < d && den[o] > 0.0) C[(size_t)k * d + t] = (float)(num[o] / den[o]);
+            if (t == 0 && counts) counts[k] = count[o];
+        } else {
+            double* pp = partial + ((int64_t)j * 256 + c) * 17;
+            pp[t] = t < d ? num[o] : 0.0;
+            pp[8 + t] = t < d ? den[o] : 0.0;
+            if (t == 0) pp[16] = (double)count[o];
+        }
     }
 }
 
-// Segments that cross chunk boundaries: the tail of the first chunk plus the
-// heads of the following ones.  One wavefront per centroid: lane q adds
-// chunks j0+1+q, j0+1+q+64, ... in order, then a fixed xor butterfly over
-// the lanes; 16 values per chunk (8 sums of omega*x, 8 of omega).  Empty
-// centroids get a zero count and keep their value.
-__global__ __launch_bounds__(64) void k_seg_cross(const int* __restrict__ start, int K, int d,
-                                                  const double* __restrict__ head,
-                                                  const double* __restrict__ tail,
-                                                  float* __restrict__ C, int32_t* __restrict__ counts)
+// Buckets with several pieces (and empty buckets, whose counts are zeroed):
+// one wavefront per centroid (grid-stride);
+// lane = (group q, dimension t); group q adds pieces q, q + 8, ... in order,
+// then the 8 group sums are combined by a fixed butterfly and divided once.
+__global__ __launch_bounds__(64) void k_piece_finish(const int* __restrict__ poff, int nbk, int width, int K,
+                                                     int d, const double* __restrict__ partial,
+                                                     float* __restrict__ C, int32_t* __restrict__ counts)
 {
-    const int k = blockIdx.x;
     const int lane = threadIdx.x;
-    const int s0 = start[k], s1 = start[k + 1];
-    if (s1 == s0) {
-        if (lane == 0 && counts) counts[k] = 0;
-        return;
-    }
-    const int64_t j0 = s0 / kChunk, j1 = (int64_t)(s1 - 1) / kChunk;
-    if (j0 == j1) return;   // finished inside its chunk
-    if (lane == 0 && counts) counts[k] = s1 - s0;
-    double acc[16];
-    for (int v = 0; v < 16; ++v) acc[v] = 0.0;
-    for (int64_t j = j0 + 1 + lane; j <= j1; j += 64)
-        for (int v = 0; v < 16; ++v) acc[v] = acc[v] + head[j * 16 + v];
-    for (int off = 32; off > 0; off >>= 1)
-        for (int v = 0; v < 16; ++v) acc[v] = acc[v] + __shfl_xor(acc[v], off);
-    if (lane < d) {
-        double num = tail[j0 * 16 + lane], den = tail[j0 * 16 + 8 + lane];
-        for (int v = 0; v < 8; ++v) {   // select this lane's dimension without dynamic indexing
-            if (v == lane) { num = num + acc[v]; den = den + acc[8 + v]; }
+    const int t = lane & 7, qg = lane >> 3;
+    for (int k = blockIdx.x; k < K; k += gridDim.x) {
+        const int bk = k / width, c = k - bk * width;
+        if (bk >= nbk) break;
+        const int j0 = poff[bk], j1 = poff[bk + 1];
+        if (j1 - j0 == 1) continue;   // finished inside its piece
+        if (j1 == j0) {                // empty bucket: no members, C kept
+            if (lane == 0 && counts) counts[k] = 0;
+            continue;
         }
-        if (den > 0.0) C[(size_t)k * d + lane] = (float)(num / den);
+        double num = 0.0, den = 0.0, cntd = 0.0;
+        for (int jj = j0 + qg; jj < j1; jj += 8) {
+            const double* pp = partial + ((int64_t)jj * 256 + c) * 17;
+            num = num + pp[t];
+            den = den + pp[8 + t];
+            cntd = cntd + pp[16];
+        }
+#pragma unroll
+        for (int off = 8; off < 64; off <<= 1) {
+            num = num + __shfl_xor(num, off);
+            den = den + __shfl_xor(den, off);
+            cntd = cntd + __shfl_xor(cntd, off);
+        }
+        if (qg == 0) {
+            if (t < d && den > 0.0) C[(size_t)k * d + t] = (float)(num / den);
+            if (t == 0 && counts) counts[k] = (int32_t)cntd;
+        }
     }
 }
 
 struct UpdateWs {
-    uint16_t *k1, *k2;
-    int32_t *v1, *v2;
-    uint8_t *g1, *g2;
-    int *hist, *dtot, *start;
-    double *head, *tail;
+    int *hist, *total, *poff;
+    int64_t* bstart;
+    float* rx;
+    uint64_t* rw;
+    double* partial;
 };
 
-int64_t n_chunks(int64_t n_sub) { return (n_sub + kChunk - 1) / kChunk; }
-
-UpdateWs carve_update(Carver& cv, int64_t n_sub, int K)
+// Records per piece: bucket mode kPieceMax; one bucket: about kDirectPieces
+// pieces, a multiple of kSub.
+int piece_size(int64_t n_sub, int K)
 {
-    UpdateWs w;
-    const int64_t nblk = (n_sub + kSortTile - 1) / kSortTile;
-    w.k1 = cv.take<uint16_t>(n_sub);
-    w.k2 = cv.take<uint16_t>(n_sub);
-    w.v1 = cv.take<int32_t>(n_sub);
-    w.v2 = cv.take<int32_t>(n_sub);
-    w.g1 = cv.take<uint8_t>(n_sub);
-    w.g2 = cv.take<uint8_t>(n_sub);
-    w.hist = cv.take<int>((size_t)256 * nblk);
-    w.dtot = cv.take<int>(256);
-    w.start = cv.take<int>((size_t)K + 1);
-    w.head = cv.take<double>((size_t)n_chunks(n_sub) * 16);
-    w.tail = cv.take<double>((size_t)n_chunks(n_sub) * 16);
+    if (K > 256) return kPieceMax;
+    int64_t p = (n_sub + kDirectPieces - 1) / kDirectPieces;
+    p = (p + kSub - 1) / kSub * kSub;
+    return (int)std::max<int64_t>(kSub, std::min<int64_t>(kPieceMax, p));
+}
+
+int64_t max_pieces(int64_t n_sub, int K)
+{
+    const int nbk = K > 256 ? (K + 127) / 128 : 1;
+    return (n_sub + piece_size(n_sub, K) - 1) / piece_size(n_sub, K) + nbk;
+}
+
+UpdateWs carve_update(Carver& cv, int64_t n_sub, int K, int d)
+{
+    UpdateWs w = {};
+    const int64_t ntile = (n_sub + kTile - 1) / kTile;
+    w.hist = cv.take<int>((size_t)kMaxBuckets * ntile);
+    w.total = cv.take<int>(kMaxBuckets);
+    w.poff = cv.take<int>(kMaxBuckets + 1);
+    w.bstart = cv.take<int64_t>(kMaxBuckets + 1);
+    if (K > 256) {
+        w.rx = cv.take<float>((size_t)n_sub * d);
+        w.rw = cv.take<uint64_t>(n_sub);
+    }
+    w.partial = cv.take<double>((size_t)max_pieces(n_sub, K) * 256 * 17);
     return w;
 }
 
@@ -322,7 +508,7 @@ size_t ws_update(int64_t n_sub, int K)
     Carver cv(nullptr, 0);
     cv.base = reinterpret_cast<char*>(kAlign);   // size-only pass
     cv.cap = SIZE_MAX / 2;
-    carve_update(cv, n_sub, K);
+    carve_update(cv, n_sub, K, 8);
     return cv.used;
 }
 
@@ -331,48 +517,37 @@ vq_status update_launch(const float* X, const float* hcol, const float* rho, con
                         int32_t* counts, void* ws, size_t ws_bytes, hipStream_t st)
 {
     const int64_t n_sub = M * N / d;
-    const int nblk = (int)((n_sub + kSortTile - 1) / kSortTile);
     Carver cv(ws, ws_bytes);
-    UpdateWs w = carve_update(cv, n_sub, K);
+    UpdateWs w = carve_update(cv, n_sub, K, d);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_update: workspace too small");
-
+    if (n_sub > (int64_t)UINT32_MAX) return fail(VQ_ERR_UNSUPPORTED, "vq_update: more than 2^32 sub-vectors");
     TimedRegion tr("update", K, st);
-    const int passes = K > 256 ? 2 : 1;
-    const uint16_t* kin = idx;
-    const int32_t* vin = nullptr;
-    const uint8_t* gin = mask;
-    uint16_t* kout = w.k1;
-    int32_t* vout = w.v1;
-    uint8_t* gout = mask ? w.g1 : nullptr;
-    for (int p = 0; p < passes; ++p) {
-        const int shift = 8 * p;
-        hipLaunchKernelGGL(k_sort_hist, dim3(nblk), dim3(kSortThreads), 0, st, kin, n_sub, shift, w.hist,
-                           nblk);
-        VQ_LAUNCHED("k_sort_hist");
-        hipLaunchKernelGGL(k_scan_digit, dim3(256), dim3(256), 0, st, w.hist, nblk, w.dtot);
-        VQ_LAUNCHED("k_scan_digit");
-        hipLaunchKernelGGL(k_sort_scatter, dim3(nblk), dim3(kSortThreads), 0, st, kin, vin, gin, n_sub, shift,
-                           w.hist, w.dtot, nblk, kout, vout, gout);
-        VQ_LAUNCHED("k_sort_scatter");
-        kin = kout;
-        vin = vout;
-        gin = gout;
-        kout = (kout == w.k1) ? w.k2 : w.k1;
-        vout = (vout == w.v1) ? w.v2 : w.v1;
-        gout = mask ? ((gout == w.g1) ? w.g2 : w.g1) : nullptr;
+    const bool bucketed = K > 256;
+    const int nbk = bucketed ? (K + 127) / 128 : 1;
+    const int width = bucketed ? 128 : 256;
+    const int piece = piece_size(n_sub, K);
+    if (bucketed) {
+        const int ntile = (int)((n_sub + kTile - 1) / kTile);
+        hipLaunchKernelGGL(k_bucket_hist, dim3(ntile), dim3(256), 0, st, idx, n_sub, nbk, w.hist, ntile);
+        VQ_LAUNCHED("k_bucket_hist");
+        hipLaunchKernelGGL(k_bucket_scan, dim3(nbk), dim3(256), 0, st, w.hist, ntile, w.total);
+        VQ_LAUNCHED("k_bucket_scan");
+        hipLaunchKernelGGL(k_piece_setup, dim3(1), dim3(64), 0, st, w.total, nbk, n_sub, piece, w.bstart, w.poff);
+        VQ_LAUNCHED("k_piece_setup");
+        hipLaunchKernelGGL(k_bucket_scatter, dim3(ntile), dim3(kTileThreads), 0, st, idx, mask, X, d, n_sub, nbk,
+                           w.hist, ntile, w.bstart, w.rx, w.rw);
+        VQ_LAUNCHED("k_bucket_scatter");
+    } else {
+        hipLaunchKernelGGL(k_piece_setup, dim3(1), dim3(64), 0, st, nullptr, 1, n_sub, piece, w.bstart, w.poff);
+        VQ_LAUNCHED("k_piece_setup");
     }
-    const uint16_t* skeys = kin;
-    const int32_t* svals = vin;
-    const uint8_t* smask = gin;
-    hipLaunchKernelGGL(k_seg_start, dim3(grid_for((int64_t)K + 1, 256)), dim3(256), 0, st, skeys, n_sub, K,
-                       w.start);
-    VQ_LAUNCHED("k_seg_start");
-    const int64_t nch = n_chunks(n_sub);
-    hipLaunchKernelGGL(k_seg_chunks, dim3(grid_for(nch, 32)), dim3(256), 0, st, X, hcol, rho, smask,
-                       (uint32_t)(N / d), d, skeys, svals, w.start, n_sub, nch, C, counts, w.head, w.tail);
-    VQ_LAUNCHED("k_seg_chunks");
-    hipLaunchKernelGGL(k_seg_cross, dim3((unsigned)K), dim3(64), 0, st, w.start, K, d, w.head, w.tail, C, counts);
-    VQ_LAUNCHED("k_seg_cross");
+    hipLaunchKernelGGL(k_piece_reduce, dim3((unsigned)max_pieces(n_sub, K)), dim3(kRedThreads), 0, st,
+                       bucketed ? w.rx : nullptr, w.rw, X, idx, mask, hcol, rho, (uint32_t)(N / d), d, K, nbk, piece,
+                       w.bstart, w.poff, C, counts, w.partial);
+    VQ_LAUNCHED("k_piece_reduce");
+    hipLaunchKernelGGL(k_piece_finish, dim3((unsigned)std::min(K, 4096)), dim3(64), 0, st, w.poff, nbk, width, K, d,
+                       w.partial, C, counts);
+    VQ_LAUNCHED("k_piece_finish");
     return VQ_OK;
 }
 

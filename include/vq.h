@@ -124,9 +124,11 @@ int vq_assign_exact_count(void* ws, size_t ws_bytes, int64_t n_sub, int K, void*
  *   rounding to fp32); a zero weight sum keeps the old value.
  * C is read and overwritten in place.  counts (nullable) receives int32[K]
  * member counts; J (nullable, device double[1]) receives the objective of
- * the INPUT codebook with these indices.  Sorting by index and a segmented
- * reduction without floating-point atomics make the result bitwise
- * deterministic. */
+ * the INPUT codebook with these indices.  Members are grouped by a stable
+ * bucket scatter and per-bucket counting sorts, and every sum is taken in a
+ * fixed order without floating-point atomics, so the result is bitwise
+ * deterministic.  Every idx[s] must be < K: an index >= K never causes an
+ * out-of-bounds access, but the centroids it lands on are then unspecified. */
 vq_status vq_update(const float* X, const float* hcol, const float* rho, const uint8_t* mask,
                     int64_t M, int64_t N, int d, const uint16_t* idx, int K,
                     float* C, int32_t* counts, double* J, void* ws, size_t ws_bytes, void* stream);

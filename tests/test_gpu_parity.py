@@ -128,6 +128,57 @@ def test_update_matches_oracle(case):
     # empty centroids keep their value bit for bit
     empty = cref == 0
     assert bits_equal(host(Cg)[empty], C[empty])
+    # with at most 32768 members per 256-centroid group every sum is taken in
+    # ascending sub-vector order, as in the oracle: the centroids agree bit for bit
+    if np.bincount(idx.astype(np.int64) >> 8).max() <= 32768:
+        assert bits_equal(host(Cg), Cref)
+
+
+@pytest.mark.parametrize("case", [(8, 1024, 1024, 8, 200, 0.0), (9, 1024, 768, 8, 700, 0.6),
+                                  (10, 700, 1024, 8, 5000, 0.45)],
+                         ids=["one-group-4-pieces", "skewed-700", "skewed-5000"])
+def test_update_many_members_per_group(case):
+    # groups of 256 centroids with more members than one LDS piece holds: the
+    # pieces' partial sums are combined in a second pass
+    seed, M, N, d, K, skew = case
+    say("update multi-piece", case)
+    W, h, C, keep, rho = _case(seed, M, N, d, K)
+    g = np.random.default_rng([99, seed, 1])
+    idx, _ = oracle.assign(W, h, rho, keep, d, C)
+    hot = g.random(idx.size) < skew
+    idx[hot] = g.integers(0, min(K, 256), size=int(hot.sum()))   # crowd the first group
+    idx[: min(5, idx.size)] = K - 1
+    Cref, cref, Jref = oracle.update(W, h, rho, keep, d, idx, C)
+    ws = vq.workspace(M, N, d, K)
+    Cg = dev(C)
+    counts, J = vq.update(dev(W), dev(h), dev(rho), dev(mask_from_keep(keep, d)), d, dev(idx), Cg, ws)
+    ok, bad = centroid_close(host(Cg), Cref)
+    assert ok, bad[:10]
+    assert np.array_equal(host(counts), cref)
+    assert abs(float(host(J)[0]) - Jref) <= 1e-12 * abs(Jref)
+
+
+@pytest.mark.parametrize("case", [(11, 256, 512, 8, 1000), (12, 200, 96, 3, 1500), (13, 90, 70, 7, 400)],
+                         ids=["empty-group-d8", "empty-group-d3", "empty-group-d7"])
+def test_update_empty_centroid_group(case):
+    # K > 256 with no member in centroids [128, 256): their counts are zero and
+    # their rows of C stay as they were, bit for bit; d < 8 takes the scalar paths
+    seed, M, N, d, K = case
+    say("update empty group", case)
+    W, h, C, keep, rho = _case(seed, M, N, d, K)
+    g = np.random.default_rng([99, seed, 2])
+    idx, _ = oracle.assign(W, h, rho, keep, d, C)
+    hole = (idx >= 128) & (idx < 256)
+    idx[hole] = g.integers(0, 128, size=int(hole.sum()))
+    idx[: min(5, idx.size)] = K - 1
+    Cref, cref, Jref = oracle.update(W, h, rho, keep, d, idx, C)
+    assert (cref[128:256] == 0).all()
+    ws = vq.workspace(M, N, d, K)
+    Cg = dev(C)
+    counts, J = vq.update(dev(W), dev(h), dev(rho), dev(mask_from_keep(keep, d)), d, dev(idx), Cg, ws)
+    assert np.array_equal(host(counts), cref)
+    assert bits_equal(host(Cg), Cref)
+    assert abs(float(host(J)[0]) - Jref) <= 1e-12 * abs(Jref)
 
 
 def test_update_deterministic():
