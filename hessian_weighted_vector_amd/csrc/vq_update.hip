@@ -92,24 +92,47 @@ __global__ __launch_bounds__(256) void k_bucket_scan(int* __restrict__ hist, int
     if (threadIdx.x == 0) total[blockIdx.x] = carry;
 }
 
-// Bucket starts and piece numbering (one thread): bucket b holds records
-// [bstart[b], bstart[b+1]) and is cut into ceil(size / piece) pieces,
-// numbered from poff[b].  total == nullptr: one bucket of n records.
-__global__ void k_piece_setup(const int* __restrict__ total, int nbk, int64_t n, int piece,
-                              int64_t* __restrict__ bstart, int* __restrict__ poff)
+// Bucket starts and piece numbering (one wavefront, nbk <= 512): bucket b
+// holds records [bstart[b], bstart[b+1]) and is cut into ceil(size / piece)
+// pieces, numbered from poff[b].  total == nullptr: one bucket of n records.
+__global__ __launch_bounds__(64) void k_piece_setup(const int* __restrict__ total, int nbk, int64_t n, int piece,
+                                                    int64_t* __restrict__ bstart, int* __restrict__ poff)
 {
-    if (threadIdx.x != 0) return;
-    int64_t run = 0;
-    int pr = 0;
-    for (int b = 0; b < nbk; ++b) {
-        const int64_t sz = total ? (int64_t)total[b] : n;
-        bstart[b] = run;
-        poff[b] = pr;
-        run += sz;
-        pr += (int)((sz + piece - 1) / piece);
+    const int lane = threadIdx.x;
+    const int per = (nbk + 63) / 64;
+    int64_t sz[8];
+    int64_t s_sum = 0;
+    int p_sum = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int q = lane * per + u;
+        sz[u] = (u < per && q < nbk) ? (total ? (int64_t)total[q] : n) : 0;
+        s_sum += sz[u];
+        p_sum += (int)((sz[u] + piece - 1) / piece);
     }
-    bstart[nbk] = run;
-    poff[nbk] = pr;
+    int64_t s_inc = s_sum;
+    int p_inc = p_sum;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t so = __shfl_up(s_inc, off);
+        const int po = __shfl_up(p_inc, off);
+        if (lane >= off) { s_inc += so; p_inc += po; }
+    }
+    int64_t srun = s_inc - s_sum;
+    int prun = p_inc - p_sum;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int q = lane * per + u;
+        if (u < per && q < nbk) {
+            bstart[q] = srun;
+            poff[q] = prun;
+        }
+        srun += sz[u];
+        prun += (int)((sz[u] + piece - 1) / piece);
+    }
+    if (lane == 63) {
+        bstart[nbk] = srun;
+        poff[nbk] = prun;
+    }
 }
 
 // Stable ranks of up to 64 keys (< 2^bits) across one wavefront: peers =
@@ -169,14 +192,20 @@ __global__ __launch_bounds__(kTileThreads) void k_bucket_scatter(
     __shared__ int tstart[kMaxBuckets + 1];
     __shared__ int64_t gbase[kMaxBuckets];
 
+    // Workgroups are dealt to the 8 XCDs in turn; numbering tiles so that
+    // each XCD takes a contiguous range lets one L2 merge the partial lines
+    // that neighbouring tiles write into the same bucket run.
+    const int tiles_per_xcd = (ntile + 7) / 8;
+    const int tile = (int)(blockIdx.x % 8) * tiles_per_xcd + (int)(blockIdx.x / 8);
+    if (tile >= ntile) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t e0 = (int64_t)blockIdx.x * kTile;
+    const int64_t e0 = (int64_t)tile * kTile;
     const int m = (int)min((int64_t)kTile, n - e0);
     for (int q = tid; q < (kTileThreads / 64) * kMaxBuckets; q += kTileThreads) (&wcnt[0][0])[q] = 0;
     for (int q = tid; q < nbk; q += kTileThreads)
-        gbase[q] = bstart[q] + hist[(int64_t)q * ntile + blockIdx.x];
+        gbase[q] = bstart[q] + hist[(int64_t)q * ntile + tile];
     __syncthreads();
     const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int bits = 0;
@@ -255,7 +284,7 @@ __global__ __launch_bounds__(kTileThreads) void k_bucket_scatter(
 // product of two floats, exact) into float64 sums kept in registers.
 // rx == nullptr: one bucket of up to 256 centroids read in place from X,
 // idx and mask.
-__global__ __launch_bounds__(kRedThreads) void k_piece_reduce(
+__global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_piece_reduce(
     const float* __restrict__ rx, const uint64_t* __restrict__ rw, const float* __restrict__ X,
     const uint16_t* __restrict__ idx, const uint8_t* __restrict__ mask, const float* __restrict__ hcol,
     const float* __restrict__ rho, uint32_t nb, int d, int K, int nbk, int piece,
@@ -300,50 +329,66 @@ __global__ __launch_bounds__(kRedThreads) void k_piece_reduce(
     double num[2] = {0.0, 0.0}, den[2] = {0.0, 0.0};
     int count[2] = {0, 0};
 
-    for (int64_t c0 = p0; c0 < p1; c0 += kSub) {
+    // Raw fields of record tid of a sub-chunk (the next one is loaded while
+    // the current one is reduced).
+    auto load_raw = [&](int64_t c0, bool& valid, int& key, uint32_t& sv, uint32_t& mk, float4& xa, float4& xb) {
         const int m = (int)min((int64_t)kSub, p1 - c0);
-        // ---- stage record tid ----
+        valid = c0 < p1 && tid < m;
+        key = 0; sv = 0; mk = 0;
+        xa = make_float4(0.f, 0.f, 0.f, 0.f);
+        xb = xa;
+        if (!valid) return;
+        const int64_t e = c0 + tid;
+        if (direct) {
+            sv = (uint32_t)e;
+            mk = mask ? mask[e] : 0u;
+            key = idx[e] & 255;
+        } else {
+            const uint64_t wd = rw[e];
+            sv = (uint32_t)wd;
+            key = (int)((wd >> 32) & 127);
+            mk = (uint32_t)((wd >> 40) & 255);
+        }
+        const float* xs = direct ? X + e * d : rx + e * d;
+        if (vx) {
+            xa = reinterpret_cast<const float4*>(xs)[0];
+            xb = reinterpret_cast<const float4*>(xs)[1];
+        } else {
+            float tmp[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) tmp[u] = u < d ? xs[u] : 0.0f;
+            xa = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
+            xb = make_float4(tmp[4], tmp[5], tmp[6], tmp[7]);
+        }
+    };
+    bool valid;
+    int key;
+    uint32_t sv, mk;
+    float4 xa, xb;
+    load_raw(p0, valid, key, sv, mk, xa, xb);
+
+    for (int64_t c0 = p0; c0 < p1; c0 += kSub) {
+        // ---- stage record tid: x now, weights requested (used after the ranking) ----
         const int r = tid;
-        const bool valid = r < m;
-        int key = 0;
+        float4 ha = make_float4(0.f, 0.f, 0.f, 0.f), hb = ha;
+        float rhov = 1.0f;
         if (valid) {
-            const int64_t e = c0 + r;
-            uint32_t sv, mk;
-            if (direct) {
-                sv = (uint32_t)e;
-                mk = mask ? mask[e] : 0u;
-                key = idx[e] & 255;
-            } else {
-                const uint64_t wd = rw[e];
-                sv = (uint32_t)wd;
-                key = (int)((wd >> 32) & 127);
-                mk = (uint32_t)((wd >> 40) & 255);
-            }
             const uint32_t i = sv / nb;
             const uint32_t b = sv - i * nb;
-            srho[r] = rho ? rho[i] : 1.0f;
-            const float* xs = direct ? X + e * d : rx + e * d;
-            if (vx) {
-                const float4 a0 = reinterpret_cast<const float4*>(xs)[0];
-                const float4 a1 = reinterpret_cast<const float4*>(xs)[1];
-                reinterpret_cast<float4*>(sx + r * 8)[0] = a0;
-                reinterpret_cast<float4*>(sx + r * 8)[1] = a1;
-            } else {
-                for (int u = 0; u < d; ++u) sx[r * 8 + u] = xs[u];
-            }
+            if (rho) rhov = rho[i];
             const float* hs = hcol + (size_t)b * d;
-            float hv[8];
             if (vh) {
-                const float4 a0 = reinterpret_cast<const float4*>(hs)[0];
-                const float4 a1 = reinterpret_cast<const float4*>(hs)[1];
-                hv[0] = a0.x; hv[1] = a0.y; hv[2] = a0.z; hv[3] = a0.w;
-                hv[4] = a1.x; hv[5] = a1.y; hv[6] = a1.z; hv[7] = a1.w;
+                ha = reinterpret_cast<const float4*>(hs)[0];
+                hb = reinterpret_cast<const float4*>(hs)[1];
             } else {
+                float tmp[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) hv[u] = u < d ? hs[u] : 0.0f;
+                for (int u = 0; u < 8; ++u) tmp[u] = u < d ? hs[u] : 0.0f;
+                ha = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
+                hb = make_float4(tmp[4], tmp[5], tmp[6], tmp[7]);
             }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) shv[r * 8 + u] = ((mk >> u) & 1u) ? 0.0f : hv[u];
+            reinterpret_cast<float4*>(sx + r * 8)[0] = xa;
+            reinterpret_cast<float4*>(sx + r * 8)[1] = xb;
         }
         for (int v = tid; v < (kRedThreads / 64) * 256; v += kRedThreads) (&wcnt[0][0])[v] = 0;
         __syncthreads();
@@ -370,7 +415,20 @@ __global__ __launch_bounds__(kRedThreads) void k_piece_reduce(
         __syncthreads();
         wave_excl_scan(ccount, width, cstart);
         __syncthreads();
-        if (valid) perm[cstart[key] + wcnt[wave][key] + rnk] = (uint16_t)r;
+        if (valid) {
+            perm[cstart[key] + wcnt[wave][key] + rnk] = (uint16_t)r;
+            srho[r] = rhov;
+            shv[r * 8 + 0] = (mk & 1u) ? 0.0f : ha.x;
+            shv[r * 8 + 1] = (mk & 2u) ? 0.0f : ha.y;
+            shv[r * 8 + 2] = (mk & 4u) ? 0.0f : ha.z;
+            shv[r * 8 + 3] = (mk & 8u) ? 0.0f : ha.w;
+            shv[r * 8 + 4] = (mk & 16u) ? 0.0f : hb.x;
+            shv[r * 8 + 5] = (mk & 32u) ? 0.0f : hb.y;
+            shv[r * 8 + 6] = (mk & 64u) ? 0.0f : hb.z;
+            shv[r * 8 + 7] = (mk & 128u) ? 0.0f : hb.w;
+        }
+        // next sub-chunk's raw fields, in flight during the sums below
+        load_raw(c0 + kSub, valid, key, sv, mk, xa, xb);
         __syncthreads();
         // ---- per owned centroid, members in record order ----
 #pragma unroll
@@ -380,16 +438,16 @@ __global__ __launch_bounds__(kRedThreads) void k_piece_reduce(
             const int b0 = cstart[c], b1 = cstart[c + 1];
             count[o] += b1 - b0;
             int e = b0;
-            for (; e + 4 <= b1; e += 4) {
-                double w[4], x[4];
+            for (; e + 2 <= b1; e += 2) {
+                double w[2], x[2];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < 2; ++u) {
                     const int rr = perm[e + u];
                     w[u] = (double)shv[rr * 8 + t] * (double)srho[rr];
                     x[u] = (double)sx[rr * 8 + t];
                 }
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < 2; ++u) {
                     num[o] = num[o] + w[u] * x[u];
                     den[o] = den[o] + w[u];
                 }
@@ -534,7 +592,7 @@ vq_status update_launch(const float* X, const float* hcol, const float* rho, con
         VQ_LAUNCHED("k_bucket_scan");
         hipLaunchKernelGGL(k_piece_setup, dim3(1), dim3(64), 0, st, w.total, nbk, n_sub, piece, w.bstart, w.poff);
         VQ_LAUNCHED("k_piece_setup");
-        hipLaunchKernelGGL(k_bucket_scatter, dim3(ntile), dim3(kTileThreads), 0, st, idx, mask, X, d, n_sub, nbk,
+        hipLaunchKernelGGL(k_bucket_scatter, dim3((ntile + 7) / 8 * 8), dim3(kTileThreads), 0, st, idx, mask, X, d, n_sub, nbk,
                            w.hist, ntile, w.bstart, w.rx, w.rw);
         VQ_LAUNCHED("k_bucket_scatter");
     } else {
