@@ -8,23 +8,35 @@
 // same positive factor, so the search ranks e(s,k) = D(s,k)/rho_i - S_s with
 // S_s = sum_t omega_t x_t^2 (omega without rho), written as one inner product
 // of length 2d = 16:
-//     e(s,k) = < [omega (.) x, omega], [-2 c_k, c_k (.) c_k] >
-// That is a skinny GEMM (sub-vectors x 16) . (16 x centroids), run on the
-// fp32 matrix cores: v_mfma_f32_32x32x2f32, A = 32 centroids, B = 32
-// sub-vectors, 8 instructions per 32x32 tile of pairs.  Each lane of the
-// 32x32 accumulator holds 16 centroid rows of one sub-vector, so the running
-// argmin needs no cross-lane traffic: per accumulator slot it keeps the best
-// value, the second-best value and the tile of the best (4 VALU ops per
-// pair: compare, min, select, median-of-three).
+//     e(s,k) = < [omega (.) x, omega], [-2 c_k, c_k (.) c_k] >.
+// That is a skinny GEMM (centroids x 16) . (16 x sub-vectors).  It runs on
+// the fp16 matrix cores (v_mfma_f32_32x32x16_f16, fp32 accumulation) with
+// every fp32 operand split into two fp16 parts after an exact power-of-two
+// scaling: the codebook side by one factor per term kind for the whole
+// codebook, the sub-vector side by one factor per sub-vector, so each side's
+// largest value lies in [2^14, 2^15) (no overflow; small parts may be fp16
+// subnormals, which the conversion forms and the matrix cores multiply
+// exactly).  A tile of 32 centroids x 32 sub-vectors takes three MFMAs,
+// lo*hi and hi*lo first and hi*hi last:
+//     e~ = sum_t (al bh + ah bl + ah bh)   (the lo*lo product is dropped).
+// The per-sub-vector factor does not change the ranking.  Each lane of the
+// accumulator holds 16 centroid rows of one sub-vector, so the running
+// argmin needs no cross-lane traffic: per lane it keeps the best value,
+// the second-best value and the position of the best.
 //
-// Exactness.  Eight chained 32x32x2 fp32 MFMAs round like a sequential
-// fused-multiply-add chain over the 16 terms, so |e~ - e| <= 17u sum|terms|
-// (u = 2^-24, one more u for rounding omega*x and c*c).  Using
-// sum|terms| <= 9 S + 4 e, a winner is certified when the gap to the second
-// best exceeds the sum of both bounds (taken with a factor ~2 margin).
-// Certified winners are the exact argmin; the rest are re-searched in
-// float64 with the direct form in t order (k_assign_exact), which rounds
-// exactly like a plain float64 implementation, ties to the lowest index.
+// Exactness.  With u = 2^-24: splitting leaves |a - ah - al| <= 2^-22 |a|
+// (two 11-bit parts), so the three products miss at most 12.1u|ab| of each
+// term; the fp32 terms omega*x and c*c carry one rounding (u); the first two
+// MFMAs sum products that are 2^-11 smaller, and the last one adds 16
+// products with fp32 roundings, at most 16u (round to nearest) or 32u
+// (truncation) of sum|terms| whatever the order of its additions: 45.2u in
+// all.  Rounding in fp16's subnormal range adds at most 2^-25 per part,
+// under 2^-5 per pair in scaled units.  Using sum|terms| <= 9 S + 4 e, a
+// winner is certified when the gap to the second best exceeds
+// 48u (9 S + 4 e) + 1 for both of them.  Certified winners are the exact
+// argmin; the rest are re-searched in float64 with the direct form in t
+// order (k_assign_exact), which rounds exactly like a plain float64
+// implementation, ties to the lowest index.
 #include "vq_internal.h"
 
 #include <algorithm>
@@ -33,44 +45,95 @@ namespace vq {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 8;                 // waves per workgroup
 constexpr int kSubPerWave = 32;           // sub-vectors per wave (MFMA B columns)
 constexpr int kSubPerBlock = kWaves * kSubPerWave;
 constexpr int kTile = 32;                 // centroids per MFMA tile (A rows)
 constexpr int kChunkTiles = 8;            // tiles staged in LDS at once
-constexpr float kPadSq = 1.0e30f;         // c*c of padding centroids
 constexpr int kExactBlocks = 2048;
+constexpr float kPadSq = 16384.0f;           // scaled c*c term of padding centroids
 
-// P[k] = 16 floats in two halves, one per half-wavefront of the MFMA A
-// operand: [-2c_0, -2c_2, -2c_4, -2c_6, c_0^2, c_2^2, c_4^2, c_6^2] then the
-// same for the odd dimensions.  Dimensions >= d are 0; padding centroids
-// (k >= K) have -2c = 0 and c^2 = kPadSq.  Also clears the flag counter.
-__global__ void k_cb_prep(const float* __restrict__ C, int K, int d, int Kpad,
-                          float* __restrict__ P, int* __restrict__ flag_count, int* __restrict__ dirty_count)
+// Largest |C| over the codebook (one block) into *cmax; clears the flag
+// counter.
+__global__ __launch_bounds__(1024) void k_cb_absmax(const float* __restrict__ C, int64_t n, float* __restrict__ cmax,
+                                                    int* __restrict__ flag_count)
 {
-    int k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k == 0) {
-        *flag_count = 0;
-        *dirty_count = 0;
+    __shared__ float red[1024];
+    float m = 0.f;
+    for (int64_t q = threadIdx.x; q < n; q += 1024) m = fmaxf(m, fabsf(C[q]));
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int w = 512; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+        __syncthreads();
     }
+    if (threadIdx.x == 0) {
+        *cmax = red[0];
+        *flag_count = 0;
+    }
+}
+
+// Binary exponents of the codebook scale factors from the largest |c|:
+// beta = 2^(15 - e1) puts max|2c| in [2^14, 2^15), beta2 = 2^(15 - e2) does
+// the same for max c*c.
+__device__ inline void cb_exponents(float cmax, int& e1, int& e2)
+{
+    frexpf(2.f * cmax, &e1);
+    frexpf(cmax * cmax, &e2);
+}
+
+// Splits a scaled fp32 value into fp16 parts hi + lo, both rounded to
+// nearest (fp16 subnormals included: the conversion produces them and the
+// matrix cores multiply them exactly).
+__device__ inline void split_h16(float v, _Float16& hi, _Float16& lo)
+{
+    const _Float16 h = (_Float16)v;
+    hi = h;
+    lo = (_Float16)(v - (float)h);
+}
+
+// Expanded, scaled and split codebook.  Per tile of 32 centroids, 4 rows of
+// 32 x 16 bytes: (hi, terms 0-7), (hi, terms 8-15), (lo, terms 0-7),
+// (lo, terms 8-15), where term t < 8 is -2 beta c_t and term 8 + t is
+// beta2 c_t^2.  Centroid m of the tile sits at position m of each row, so
+// the 64 lanes of a wavefront read one row pair as 1 KB of consecutive
+// bytes.  Dimensions >= d are 0; padding centroids (k >= K) have 0 cross
+// terms and kPadSq square terms.
+__global__ void k_cb_prep16(const float* __restrict__ C, int K, int d, int Kpad, const float* __restrict__ cmax,
+                            uint4* __restrict__ P)
+{
+    const int k = blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= Kpad) return;
-    float* p = P + (size_t)k * 16;
+    int e1, e2;
+    cb_exponents(*cmax, e1, e2);
+    _Float16 hv[2][16];
+#pragma unroll
     for (int t = 0; t < 8; ++t) {
         float m2c = 0.f, sq = 0.f;
         if (k < K) {
             if (t < d) {
-                float c = C[(size_t)k * d + t];
-                m2c = -2.f * c;
-                sq = c * c;
+                const float c = C[(size_t)k * d + t];
+                m2c = ldexpf(-2.f * c, 15 - e1);
+                sq = ldexpf(c * c, 15 - e2);
             }
         } else {
             sq = kPadSq;
         }
-        const int h = t & 1, q = t >> 1;
-        p[h * 8 + q] = m2c;
-        p[h * 8 + 4 + q] = sq;
+        split_h16(m2c, hv[0][t], hv[1][t]);
+        split_h16(sq, hv[0][8 + t], hv[1][8 + t]);
     }
+    const int tile = k / kTile, m = k % kTile;
+#pragma unroll
+    for (int part = 0; part < 2; ++part)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            h16x8 v;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = hv[part][half * 8 + i];
+            P[(size_t)tile * 128 + (part * 2 + half) * 32 + m] = __builtin_bit_cast(uint4, v);
+        }
 }
 
 // The float64 direct form, in t order: acc += omega_t * ((x_t - c_t)^2).
@@ -128,225 +191,105 @@ __device__ __forceinline__ void lane_update(const f32x16& a, int kt, float& b1, 
     }
 }
 
-// One 32x32 tile in the general form: eight chained MFMAs over the 16 terms
-// (4 pairs of -2c_t * omega_t x_t, then 4 pairs of c_t^2 * omega_t).  The
-// previous tile's minimum is formed between the MFMAs; only if it beats the
+// One 32x32 tile: three chained MFMAs (lo*hi, hi*lo, then hi*hi).  The
+// previous tile's minimum is formed between them; only if it beats the
 // lane's second best (rare once the search has seen a few tiles) does the
 // wave walk that tile's values.
-// a0 = this lane's 4 values of -2c, a1 = its 4 values of c^2; bw = omega*x,
-// bo = omega for this lane's 4 dimensions.
-__device__ __forceinline__ f32x16 tile_general(const float4 a0, const float4 a1, const float* bw, const float* bo,
-                                               const f32x16& prev, int ktp, float& b1, float& b2, int& kbp)
+__device__ __forceinline__ f32x16 tile_h16(const h16x8 ah, const h16x8 al, const h16x8 bh, const h16x8 bl,
+                                           const f32x16& prev, int ktp, float& b1, float& b2, int& kbp)
 {
     f32x16 acc = {};
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, bw[0], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, bw[1], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, bw[2], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, bw[3], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, bo[0], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, bo[1], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, bo[2], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, bo[3], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc, 0, 0, 0);
     const float tm = tile_min(prev);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
+    for (int g = 0; g < 3; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // one VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
     }
     if (tm < b2) lane_update(prev, ktp, b1, b2, kbp);
     return acc;
 }
 
-// The same tile when every sub-vector of the wavefront has the same weights
-// omega (same column block, same mask byte): the centroid term
-// sum_t omega_t c_t^2 is a per-centroid bias, formed here with 4 FMAs per
-// lane (each half-wave sums its 4 dimensions) and added by a fifth MFMA
-// against a B row of ones, so the tile needs 5 MFMAs instead of 8.
-__device__ __forceinline__ f32x16 tile_shared(const float4 a0, const float4 a1, const float* bw, const float* wo,
-                                              const f32x16& prev, int ktp, float& b1, float& b2, int& kbp)
-{
-    float bias = a1.x * wo[0];
-    bias = fmaf(a1.y, wo[1], bias);
-    bias = fmaf(a1.z, wo[2], bias);
-    bias = fmaf(a1.w, wo[3], bias);
-    f32x16 acc = {};
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, bw[0], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, bw[1], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, bw[2], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, bw[3], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bias, 1.0f, acc, 0, 0, 0);
-    const float tm = tile_min(prev);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (tm < b2) lane_update(prev, ktp, b1, b2, kbp);
-    return acc;
-}
-
-// The majority mask byte of each column block (lowest byte on ties): the
-// weight pattern shared by most of its sub-vectors.
-__global__ __launch_bounds__(256) void k_block_pattern(const uint8_t* __restrict__ mask, int64_t M, int64_t nb,
-                                                       uint8_t* __restrict__ pattern)
-{
-    __shared__ int cnt[256];
-    __shared__ int best_c[256], best_p[256];
-    cnt[threadIdx.x] = 0;
-    __syncthreads();
-    const int64_t b = blockIdx.x;
-    for (int64_t i = threadIdx.x; i < M; i += 256) atomicAdd(&cnt[mask[i * nb + b]], 1);
-    __syncthreads();
-    best_c[threadIdx.x] = cnt[threadIdx.x];
-    best_p[threadIdx.x] = threadIdx.x;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) {
-            const int oc = best_c[threadIdx.x + w], op = best_p[threadIdx.x + w];
-            if (oc > best_c[threadIdx.x] || (oc == best_c[threadIdx.x] && op < best_p[threadIdx.x])) {
-                best_c[threadIdx.x] = oc;
-                best_p[threadIdx.x] = op;
-            }
-        }
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) pattern[b] = (uint8_t)best_p[0];
-}
-
-// Sub-vectors whose mask byte differs from their block's pattern are listed
-// for the general kernel: wavefront ballots, a workgroup prefix in LDS and
-// one integer atomic per workgroup (the order of the list does not affect
-// any result).
-__global__ __launch_bounds__(1024) void k_dirty(const uint8_t* __restrict__ mask, const uint8_t* __restrict__ pattern,
-                                                int64_t n_sub, uint32_t nb, int* __restrict__ count,
-                                                int* __restrict__ list)
-{
-    constexpr int kItems = 4;
-    __shared__ int wsum[kItems][16];
-    __shared__ int base;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    bool take[kItems];
-    unsigned long long ball[kItems];
-#pragma unroll
-    for (int r = 0; r < kItems; ++r) {
-        const int64_t s = ((int64_t)blockIdx.x * kItems + r) * 1024 + threadIdx.x;
-        take[r] = false;
-        if (s < n_sub) take[r] = mask[s] != pattern[(uint32_t)(s % nb)];
-        ball[r] = __ballot(take[r]);
-        if (lane == 0) wsum[r][wave] = __popcll(ball[r]);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int tot = 0;
-        for (int r = 0; r < kItems; ++r)
-            for (int w = 0; w < 16; ++w) tot += wsum[r][w];
-        base = tot ? atomicAdd(count, tot) : 0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kItems; ++r) {
-        if (take[r]) {
-            int off = base + __popcll(ball[r] & ((1ull << lane) - 1ull));
-            for (int q = 0; q < r; ++q)
-                for (int w = 0; w < 16; ++w) off += wsum[q][w];
-            for (int w = 0; w < wave; ++w) off += wsum[r][w];
-            const int64_t s = ((int64_t)blockIdx.x * kItems + r) * 1024 + threadIdx.x;
-            list[off] = (int)s;
-        }
-    }
-}
-
-// Workgroup = kWaves wavefronts x 32 sub-vectors, searched against the
-// whole codebook.
-//   SHARED: wavefront w takes wave group g = blockIdx.x * kWaves + w, i.e.
-//     32 consecutive rows of column block b; all lanes use the block's
-//     majority weight pattern (5-MFMA tile).  A lane whose own mask byte
-//     differs is computed but not written: it is in the list of the
-//     general kernel.
-//   general: lane l of wavefront w takes sub-vector list[(blockIdx.x *
-//     kWaves + w) * 32 + (l & 31)] with its own weights (8-MFMA tile).
-// The expanded codebook (padded to whole chunks) streams through LDS in
-// chunks of kChunkTiles*32 centroids, double buffered: the next chunk is
-// fetched into registers while the current one is searched, so there is one
-// barrier per chunk.  Within a wave the tiles are software pipelined: tile
-// t's MFMAs are issued with tile t-1's argmin updates between them (two
-// accumulators alternate).
-template <bool SHARED>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_assign_mfma(
+// Workgroup = kWaves wavefronts x 32 consecutive sub-vectors; lane l of a
+// wavefront works on sub-vector (l & 31) of its 32: the lanes of the lower
+// half supply the scaled omega*x parts (MFMA k-slots 0-7), those of the
+// upper half the scaled omega parts (k-slots 8-15).  The split codebook
+// (padded to whole chunks) streams through LDS in chunks of kChunkTiles*32
+// centroids, double buffered: the next chunk is fetched into registers
+// while the current one is searched, so there is one barrier per chunk.
+// Within a wave the tiles are software pipelined: tile t's MFMAs are issued
+// with tile t-1's argmin updates between them (two accumulators alternate).
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_assign_h16(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
-    const uint8_t* __restrict__ mask, const uint8_t* __restrict__ pattern, int64_t M, int64_t nb, int d,
-    const float4* __restrict__ P, const float* __restrict__ C, int K, int nchunks,
-    const int* __restrict__ list, const int* __restrict__ list_count, int64_t groups,
-    uint16_t* __restrict__ idx, float* __restrict__ dist,
-    int* __restrict__ flag_count, int* __restrict__ flag_list)
+    const uint8_t* __restrict__ mask, int64_t n_sub, int64_t nb, int d, const uint4* __restrict__ P,
+    const float* __restrict__ cmax, const float* __restrict__ C, int K, int nchunks,
+    uint16_t* __restrict__ idx, float* __restrict__ dist, int* __restrict__ flag_count, int* __restrict__ flag_list)
 {
-    constexpr int kChunkVec = kChunkTiles * kTile * 4;          // float4 per chunk
-    constexpr int kVecPerThread = kChunkVec / (kWaves * 64);
+    constexpr int kChunkVec = kChunkTiles * 128;                 // uint4 per chunk
     static_assert(kChunkTiles % 2 == 0, "tiles are processed in pairs");
-    static_assert(kVecPerThread == 2, "two float4 per thread per chunk");
-    __shared__ float4 lds[2][kChunkVec];
+    static_assert(kChunkVec == 2 * kWaves * 64, "two uint4 per thread per chunk");
+    __shared__ uint4 lds[2][kChunkVec];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int half = lane >> 5;
-    const int64_t e = (int64_t)blockIdx.x * kWaves + wave;
-    int64_t s = 0, b = 0;
-    bool active, valid;
-    unsigned mb = 0u, pat = 0u;
-    if (SHARED) {
-        if ((int64_t)blockIdx.x * kWaves >= groups) return;      // whole workgroup idle
-        active = e < groups;                                       // wave-uniform
-        const int64_t g = active ? e : 0;
-        const int64_t rg = g / nb;
-        b = g - rg * nb;
-        const int64_t i = rg * kSubPerWave + (lane & 31);
-        valid = active && i < M;
-        s = i * nb + b;
-        pat = (active && pattern) ? pattern[b] : 0u;
-        mb = (valid && mask) ? mask[s] : 0u;
-    } else {
-        const int64_t count = *list_count;
-        if ((int64_t)blockIdx.x * kWaves * kSubPerWave >= count) return;
-        const int64_t q = e * kSubPerWave + (lane & 31);
-        active = e * kSubPerWave < count;                          // wave-uniform
-        valid = q < count;
-        s = valid ? (int64_t)list[q] : 0;
-        b = s % nb;
-        mb = (valid && mask) ? mask[s] : 0u;
-    }
-    // lanes that write their result (in SHARED, only those of the pattern)
-    const bool owner = valid && (!SHARED || mb == pat);
+    const int64_t w0 = ((int64_t)blockIdx.x * kWaves + wave) * kSubPerWave;
+    const bool active = w0 < n_sub;                               // wave-uniform
+    const int64_t s = w0 + (lane & 31);
+    const bool valid = s < n_sub;
 
-    // ---- the sub-vector's weights, B operand and weighted energy S -----
-    const unsigned wmask = SHARED ? pat : mb;
-    float x[8], om[8];
-    float S = 0.f;
-    for (int t = 0; t < 8; ++t) {
-        float xv = 0.f, w = 0.f;
-        if (valid && t < d) {
-            xv = X[s * d + t];
-            w = ((wmask >> t) & 1u) ? 0.f : hcol[b * d + t];
+    // ---- the sub-vector's weights, scaled split B operand, S -----------
+    h16x8 bh, bl;
+    float S_sc;
+    {
+        float raw[8];
+        float S = 0.f;
+        const int64_t b = valid ? s % nb : 0;
+        const unsigned mb = (valid && mask) ? mask[s] : 0u;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            float xv = 0.f, w = 0.f;
+            if (valid && t < d) {
+                xv = X[s * d + t];
+                w = ((mb >> t) & 1u) ? 0.f : hcol[b * d + t];
+            }
+            S += w * xv * xv;
+            // lower half: omega*x (scale alpha*beta); upper half: omega
+            // (scale alpha*beta2*(beta/beta2))
+            raw[t] = half ? w : w * xv;
         }
-        x[t] = xv;
-        om[t] = w;
-        S += w * xv * xv;
-    }
-    // this lane's half of the inner dimension: dimensions t = 2q + half;
-    // wo = the group's common weights (same for every lane in SHARED)
-    float bw[4], bo[4], wo[4];
-    for (int q = 0; q < 4; ++q) {
-        const int t = 2 * q + half;
-        bw[q] = om[t] * x[t];
-        bo[q] = om[t];
-        wo[q] = (SHARED && active && t < d && !((pat >> t) & 1u)) ? hcol[b * d + t] : 0.f;
+        int e1, e2;
+        cb_exponents(*cmax, e1, e2);
+        float mx = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) mx = fmaxf(mx, fabsf(raw[t]));
+        // alpha from the larger of the two halves
+        const int rel = half ? (e2 - e1) : 0;
+        int ex = -100000;
+        if (mx > 0.f) {
+            frexpf(mx, &ex);
+            ex += rel;
+        }
+        int en = max(ex, __shfl_xor(ex, 32));
+        if (en < -50000) en = 0;                                  // all weights zero
+        const int shift = (15 - en) + rel;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            _Float16 h, l;
+            split_h16(ldexpf(raw[t], shift), h, l);
+            bh[t] = h;
+            bl[t] = l;
+        }
+        S_sc = ldexpf(S, (15 - en) + (15 - e1));
     }
 
     float b1 = __builtin_inff(), b2 = __builtin_inff();
     int kbp = 0;
 
-    float4 pre0 = P[threadIdx.x];
-    float4 pre1 = P[threadIdx.x + kWaves * 64];
+    uint4 pre0 = P[threadIdx.x];
+    uint4 pre1 = P[threadIdx.x + kWaves * 64];
     lds[0][threadIdx.x] = pre0;
     lds[0][threadIdx.x + kWaves * 64] = pre1;
     __syncthreads();
@@ -355,27 +298,26 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
     f32x16 accA, accB;
     for (int j = 0; j < 16; ++j) accB[j] = __builtin_inff();
     int ktB = 0;
-    const int a_off = (lane & 31) * 4 + half * 2;
+    const int a_off = half * 32 + (lane & 31);
     for (int c = 0; c < nchunks; ++c) {
         if (c + 1 < nchunks) {
-            const float4* src = P + (size_t)(c + 1) * kChunkVec;
+            const uint4* src = P + (size_t)(c + 1) * kChunkVec;
             pre0 = src[threadIdx.x];
             pre1 = src[threadIdx.x + kWaves * 64];
         }
         if (active) {
-            const float4* L = lds[c & 1] + a_off;
+            const uint4* L = lds[c & 1] + a_off;
             const int kt0 = c * kChunkTiles;
 #pragma unroll 1
             for (int tt = 0; tt < kChunkTiles; tt += 2) {
-                const float4* A0 = L + tt * kTile * 4;
-                const float4* A1 = A0 + kTile * 4;
-                if (SHARED) {
-                    accA = tile_shared(A0[0], A0[1], bw, wo, accB, ktB, b1, b2, kbp);
-                    accB = tile_shared(A1[0], A1[1], bw, wo, accA, kt0 + tt, b1, b2, kbp);
-                } else {
-                    accA = tile_general(A0[0], A0[1], bw, bo, accB, ktB, b1, b2, kbp);
-                    accB = tile_general(A1[0], A1[1], bw, bo, accA, kt0 + tt, b1, b2, kbp);
-                }
+                const uint4* A0 = L + tt * 128;
+                const uint4* A1 = A0 + 128;
+                const h16x8 ah0 = __builtin_bit_cast(h16x8, A0[0]);
+                const h16x8 al0 = __builtin_bit_cast(h16x8, A0[64]);
+                accA = tile_h16(ah0, al0, bh, bl, accB, ktB, b1, b2, kbp);
+                const h16x8 ah1 = __builtin_bit_cast(h16x8, A1[0]);
+                const h16x8 al1 = __builtin_bit_cast(h16x8, A1[64]);
+                accB = tile_h16(ah1, al1, bh, bl, accA, kt0 + tt, b1, b2, kbp);
                 ktB = kt0 + tt + 1;
             }
         }
@@ -406,18 +348,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
         gb = ob1; gk = okb; gs = fminf(osec, b1);
     }
     const float u = 5.9604644775390625e-8f;   // 2^-24
-    const float eb = 32.f * u * (9.f * S + 4.f * fmaxf(gb, -S));
-    const float es = 32.f * u * (9.f * S + 4.f * fmaxf(gs, -S));
-    const bool certified = (gs - gb) > (eb + es + 1.0e-35f) && gk < K;
+    const float eb = 48.f * u * (9.f * S_sc + 4.f * fmaxf(gb, -S_sc)) + 1.f;
+    const float es = 48.f * u * (9.f * S_sc + 4.f * fmaxf(gs, -S_sc)) + 1.f;
+    const bool certified = (gs - gb) > (eb + es) && gk < K;
 
-    const bool writer = owner && half == 0;
+    const bool writer = valid && half == 0;
     if (writer && certified) {
         idx[s] = (uint16_t)gk;
         if (dist) {
             double omd[8];
             float xs[8];
             exact_weights(hcol, rho, mask, s, nb, d, omd);
-            for (int t = 0; t < d; ++t) xs[t] = x[t];
+            for (int t = 0; t < d; ++t) xs[t] = X[s * d + t];
             dist[s] = (float)exact_dist(omd, xs, C + (size_t)gk * d, d);
         }
     }
@@ -521,18 +463,16 @@ __global__ __launch_bounds__(256) void k_assign_exact(
 
 }  // namespace
 
-// Centroids per LDS chunk; the expanded codebook is padded to whole chunks.
+// Centroids per LDS chunk; the split codebook is padded to whole chunks.
 constexpr int kChunkK = kChunkTiles * kTile;
 
 inline int padded_K(int K) { return (K + kChunkK - 1) / kChunkK * kChunkK; }
 
 size_t ws_assign(int64_t n_sub, int K)
 {
-    // expanded codebook, flag counter, flag list, dirty counter, dirty list,
-    // block patterns (at most n_sub column blocks)
-    return align_up((size_t)padded_K(K) * 16 * sizeof(float)) + align_up(sizeof(int)) +
-           align_up((size_t)n_sub * sizeof(int)) + align_up(sizeof(int)) + align_up((size_t)n_sub * sizeof(int)) +
-           align_up((size_t)n_sub);
+    // split codebook (64 bytes per centroid), flag counter, flag list, max |c|
+    return align_up((size_t)padded_K(K) * 64) + align_up(sizeof(int)) + align_up((size_t)n_sub * sizeof(int)) +
+           align_up(sizeof(float));
 }
 
 // Enqueues the assignment; arguments already validated by the caller.
@@ -544,40 +484,23 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
     const int64_t nb = N / d;
     const int Kpad = padded_K(K);
     Carver cv(ws, ws_bytes);
-    float* P = cv.take<float>((size_t)Kpad * 16);
+    uint4* P = cv.take<uint4>((size_t)Kpad * 4);
     int* flag_count = cv.take<int>(1);
     int* flag_list = cv.take<int>((size_t)n_sub);
-    int* dirty_count = cv.take<int>(1);
-    int* dirty_list = cv.take<int>((size_t)n_sub);
-    uint8_t* pattern = cv.take<uint8_t>((size_t)nb);
+    float* cmax = cv.take<float>(1);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_assign: workspace too small");
+    if (n_sub > (int64_t)INT32_MAX) return fail(VQ_ERR_UNSUPPORTED, "vq_assign: more than 2^31 sub-vectors");
 
     TimedRegion tr_all("assign", K, st);
-    hipLaunchKernelGGL(k_cb_prep, dim3(grid_for(Kpad, 256)), dim3(256), 0, st, C, K, d, Kpad, P,
-                       flag_count, dirty_count);
-    VQ_LAUNCHED("k_cb_prep");
+    hipLaunchKernelGGL(k_cb_absmax, dim3(1), dim3(1024), 0, st, C, (int64_t)K * d, cmax, flag_count);
+    VQ_LAUNCHED("k_cb_absmax");
+    hipLaunchKernelGGL(k_cb_prep16, dim3(grid_for(Kpad, 256)), dim3(256), 0, st, C, K, d, Kpad, cmax, P);
+    VQ_LAUNCHED("k_cb_prep16");
     {
         TimedRegion tr("assign_search", K, st);
-        const int64_t groups = (M + kSubPerWave - 1) / kSubPerWave * nb;
-        const float4* P4 = reinterpret_cast<const float4*>(P);
-        const int nch = Kpad / kChunkK;
-        if (mask) {
-            hipLaunchKernelGGL(k_block_pattern, dim3((unsigned)nb), dim3(256), 0, st, mask, M, nb, pattern);
-            VQ_LAUNCHED("k_block_pattern");
-            hipLaunchKernelGGL(k_dirty, dim3(grid_for(n_sub, 4096)), dim3(1024), 0, st, mask, pattern, n_sub,
-                               (uint32_t)nb, dirty_count, dirty_list);
-            VQ_LAUNCHED("k_dirty");
-        }
-        hipLaunchKernelGGL(k_assign_mfma<true>, dim3(grid_for(groups, kWaves)), dim3(kWaves * 64), 0, st, X, hcol,
-                           rho, mask, mask ? pattern : nullptr, M, nb, d, P4, C, K, nch, nullptr, nullptr, groups,
-                           idx, dist, flag_count, flag_list);
-        VQ_LAUNCHED("k_assign_mfma<shared>");
-        if (mask) {
-            hipLaunchKernelGGL(k_assign_mfma<false>, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st,
-                               X, hcol, rho, mask, nullptr, M, nb, d, P4, C, K, nch, dirty_list, dirty_count, groups,
-                               idx, dist, flag_count, flag_list);
-            VQ_LAUNCHED("k_assign_mfma<general>");
-        }
+        hipLaunchKernelGGL(k_assign_h16, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st, X, hcol,
+                           rho, mask, n_sub, nb, d, P, cmax, C, K, Kpad / kChunkK, idx, dist, flag_count, flag_list);
+        VQ_LAUNCHED("k_assign_h16");
     }
     const unsigned gx = (unsigned)std::min<int64_t>((n_sub + 3) / 4, kExactBlocks);
     const int vecC = (d == 8 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0) ? 1 : 0;
@@ -591,7 +514,7 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
 vq_status assign_flag_count(void* ws, size_t ws_bytes, int64_t n_sub, int K, int* out, hipStream_t st)
 {
     Carver cv(ws, ws_bytes);
-    cv.take<float>((size_t)padded_K(K) * 16);
+    cv.take<uint4>((size_t)padded_K(K) * 4);
     int* flag_count = cv.take<int>(1);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "workspace too small");
     VQ_HIP(hipMemcpyAsync(out, flag_count, sizeof(int), hipMemcpyDeviceToHost, st));
