@@ -53,19 +53,36 @@ constexpr int kSubPerBlock = kWaves * kSubPerWave;
 constexpr int kTile = 32;                 // centroids per MFMA tile (A rows)
 constexpr int kChunkTiles = 8;            // tiles staged in LDS at once
 constexpr int kExactBlocks = 2048;
+constexpr int kSlotChunks = 8;            // codebooks of <= 8 chunks use per-slot tracking
 constexpr float kPadSq = 16384.0f;           // scaled c*c term of padding centroids
 
-// Largest |C| over the codebook (one block) into *cmax; clears the flag
-// counter.
-__global__ __launch_bounds__(1024) void k_cb_absmax(const float* __restrict__ C, int64_t n, float* __restrict__ cmax,
-                                                    int* __restrict__ flag_count)
+constexpr int kMaxBlocks = 256;   // blocks of the codebook max reduction
+
+// Largest |C| over the codebook, two passes: block maxima into part[], then
+// one block reduces them into *cmax and clears the flag counter.
+__global__ __launch_bounds__(256) void k_cb_absmax_part(const float* __restrict__ C, int64_t n,
+                                                        float* __restrict__ part)
 {
-    __shared__ float red[1024];
+    __shared__ float red[256];
     float m = 0.f;
-    for (int64_t q = threadIdx.x; q < n; q += 1024) m = fmaxf(m, fabsf(C[q]));
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n; q += (int64_t)gridDim.x * 256)
+        m = fmaxf(m, fabsf(C[q]));
     red[threadIdx.x] = m;
     __syncthreads();
-    for (int w = 512; w > 0; w >>= 1) {
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void k_cb_absmax_final(const float* __restrict__ part, int nparts,
+                                                         float* __restrict__ cmax, int* __restrict__ flag_count)
+{
+    __shared__ float red[256];
+    red[threadIdx.x] = (int)threadIdx.x < nparts ? part[threadIdx.x] : 0.f;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
         if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
         __syncthreads();
     }
@@ -176,39 +193,62 @@ __device__ __forceinline__ float tile_min(const f32x16& a)
     return fminf(m0, m3);
 }
 
-// Exact update of this lane's (best, second best, best position) with the
-// 16 values of tile kt, in slot order (slot order is centroid order within
-// the lane, so equal values keep the lower index).  Position = kt*16 + slot.
-__device__ __forceinline__ void lane_update(const f32x16& a, int kt, float& b1, float& b2, int& kbp)
+// Per-lane tracking over tiles, branch-free: b1 = smallest tile minimum so
+// far and kt1 its tile (the earlier tile on equal minima), b2 = smallest
+// minimum of every other tile.  b1 <= b2 always, so b2' = med3(b1, tm, b2).
+__device__ __forceinline__ void tile_track(const f32x16& a, int kt, float& b1, float& b2, int& kt1)
 {
+    const float tm = tile_min(a);
+    b2 = __builtin_amdgcn_fmed3f(b1, tm, b2);
+    const bool lt = tm < b1;
+    b1 = lt ? tm : b1;
+    kt1 = lt ? kt : kt1;
+}
+
+// Per-slot tracking (short codebooks, where a few branchy updates cost less
+// than forming a tile again at the end): exact (best, second best, position
+// = kt*16 + slot) over the 16 values of tile kt, in slot order (slot order is
+// centroid order within the lane, so equal values keep the lower index).
+// Only tiles whose minimum beats the second best are walked.
+__device__ __forceinline__ void slot_track(const f32x16& a, int kt, float& b1, float& b2, int& kbp)
+{
+    if (tile_min(a) < b2) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const float v = a[j];
-        const bool lt = v < b1;
-        b2 = __builtin_amdgcn_fmed3f(b1, b2, v);
-        b1 = lt ? v : b1;
-        kbp = lt ? kt * 16 + j : kbp;
+        for (int j = 0; j < 16; ++j) {
+            const float v = a[j];
+            const bool lt = v < b1;
+            b2 = __builtin_amdgcn_fmed3f(b1, b2, v);
+            b1 = lt ? v : b1;
+            kbp = lt ? kt * 16 + j : kbp;
+        }
     }
 }
 
-// One 32x32 tile: three chained MFMAs (lo*hi, hi*lo, then hi*hi).  The
-// previous tile's minimum is formed between them; only if it beats the
-// lane's second best (rare once the search has seen a few tiles) does the
-// wave walk that tile's values.
+template <bool SLOT>
+__device__ __forceinline__ void track(const f32x16& a, int kt, float& b1, float& b2, int& pos)
+{
+    if (SLOT)
+        slot_track(a, kt, b1, b2, pos);
+    else
+        tile_track(a, kt, b1, b2, pos);
+}
+
+// One 32x32 tile: three chained MFMAs (lo*hi, hi*lo, then hi*hi), with the
+// previous tile's tracking update between them.
+template <bool SLOT>
 __device__ __forceinline__ f32x16 tile_h16(const h16x8 ah, const h16x8 al, const h16x8 bh, const h16x8 bl,
-                                           const f32x16& prev, int ktp, float& b1, float& b2, int& kbp)
+                                           const f32x16& prev, int ktp, float& b1, float& b2, int& pos)
 {
     f32x16 acc = {};
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc, 0, 0, 0);
-    const float tm = tile_min(prev);
+    track<SLOT>(prev, ktp, b1, b2, pos);
 #pragma unroll
     for (int g = 0; g < 3; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
     }
-    if (tm < b2) lane_update(prev, ktp, b1, b2, kbp);
     return acc;
 }
 
@@ -221,6 +261,9 @@ __device__ __forceinline__ f32x16 tile_h16(const h16x8 ah, const h16x8 al, const
 // while the current one is searched, so there is one barrier per chunk.
 // Within a wave the tiles are software pipelined: tile t's MFMAs are issued
 // with tile t-1's argmin updates between them (two accumulators alternate).
+// SLOT selects per-slot tracking (short codebooks) over per-tile tracking
+// with the best tile formed again at the end (long codebooks).
+template <bool SLOT>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_assign_h16(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
     const uint8_t* __restrict__ mask, int64_t n_sub, int64_t nb, int d, const uint4* __restrict__ P,
@@ -243,6 +286,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
     // ---- the sub-vector's weights, scaled split B operand, S -----------
     h16x8 bh, bl;
     float S_sc;
+    int shift_s;   // S_sc = S * 2^shift_s: the sub-vector's scale alpha*beta
     {
         float raw[8];
         float S = 0.f;
@@ -282,11 +326,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
             bh[t] = h;
             bl[t] = l;
         }
-        S_sc = ldexpf(S, (15 - en) + (15 - e1));
+        shift_s = (15 - en) + (15 - e1);
+        S_sc = ldexpf(S, shift_s);
     }
 
     float b1 = __builtin_inff(), b2 = __builtin_inff();
-    int kbp = 0;
+    int kt1 = 0;
 
     uint4 pre0 = P[threadIdx.x];
     uint4 pre1 = P[threadIdx.x + kWaves * 64];
@@ -314,10 +359,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
                 const uint4* A1 = A0 + 128;
                 const h16x8 ah0 = __builtin_bit_cast(h16x8, A0[0]);
                 const h16x8 al0 = __builtin_bit_cast(h16x8, A0[64]);
-                accA = tile_h16(ah0, al0, bh, bl, accB, ktB, b1, b2, kbp);
+                accA = tile_h16<SLOT>(ah0, al0, bh, bl, accB, ktB, b1, b2, kt1);
                 const h16x8 ah1 = __builtin_bit_cast(h16x8, A1[0]);
                 const h16x8 al1 = __builtin_bit_cast(h16x8, A1[64]);
-                accB = tile_h16(ah1, al1, bh, bl, accA, kt0 + tt, b1, b2, kbp);
+                accB = tile_h16<SLOT>(ah1, al1, bh, bl, accA, kt0 + tt, b1, b2, kt1);
                 ktB = kt0 + tt + 1;
             }
         }
@@ -328,14 +373,68 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
         __syncthreads();
     }
     if (!active) return;
-    if (tile_min(accB) < b2) lane_update(accB, ktB, b1, b2, kbp);
+    track<SLOT>(accB, ktB, b1, b2, kt1);
 
     // ---- epilogue: best and second best of this sub-vector -------------
-    // position kbp = tile * 16 + slot; slot j of this lane holds centroid row
-    // (j/4)*8 + half*4 + j%4 of the tile
-    const float sec = b2;
-    const int jb = kbp & 15;
-    const int kb = (kbp >> 4) * kTile + (jb >> 2) * 8 + half * 4 + (jb & 3);
+    // Slot j of this lane holds centroid row (j/4)*8 + half*4 + j%4 of a tile,
+    // rows ascending with j.  Per-slot tracking knows the best position
+    // (kt1 = tile*16 + slot).  Per-tile tracking knows the best tile: its 16
+    // values of this lane are formed again in fp32 (a fused multiply-add chain
+    // over the 16 terms: within 17u of exact, inside the search's bound) to
+    // find the best slot (the first minimum: lowest index) and the tile's
+    // second best.
+    float v1 = __builtin_inff(), v2 = __builtin_inff();
+    int kb = K;
+    if (SLOT) {
+        const int jb = kt1 & 15;
+        kb = (kt1 >> 4) * kTile + (jb >> 2) * 8 + half * 4 + (jb & 3);
+        v1 = b1;
+    } else {
+        float bw[8], om[8];
+        const int64_t b = valid ? s % nb : 0;
+        const unsigned mb = (valid && mask) ? mask[s] : 0u;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            float xv = 0.f, w = 0.f;
+            if (valid && t < d) {
+                xv = X[s * d + t];
+                w = ((mb >> t) & 1u) ? 0.f : hcol[b * d + t];
+            }
+            om[t] = w;
+            bw[t] = w * xv;
+        }
+        const bool vecC = d == 8 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
+#pragma unroll 2
+        for (int j = 0; j < 16; ++j) {
+            const int k = kt1 * kTile + (j >> 2) * 8 + half * 4 + (j & 3);
+            if (k >= K) continue;
+            float c[8];
+            if (vecC) {
+                const float4 ca = reinterpret_cast<const float4*>(C)[(size_t)k * 2];
+                const float4 cb = reinterpret_cast<const float4*>(C)[(size_t)k * 2 + 1];
+                c[0] = ca.x; c[1] = ca.y; c[2] = ca.z; c[3] = ca.w;
+                c[4] = cb.x; c[5] = cb.y; c[6] = cb.z; c[7] = cb.w;
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) c[t] = t < d ? C[(size_t)k * d + t] : 0.f;
+            }
+            float e = 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) e = fmaf(bw[t], -2.f * c[t], e);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) e = fmaf(om[t], c[t] * c[t], e);
+            const float v = ldexpf(e, shift_s);
+            if (v < v1) {
+                v2 = v1;
+                v1 = v;
+                kb = k;
+            } else {
+                v2 = fminf(v2, v);
+            }
+        }
+    }
+    b1 = v1;
+    const float sec = fminf(b2, v2);
 
     const float ob1 = __shfl_xor(b1, 32);
     const float osec = __shfl_xor(sec, 32);
@@ -470,9 +569,10 @@ inline int padded_K(int K) { return (K + kChunkK - 1) / kChunkK * kChunkK; }
 
 size_t ws_assign(int64_t n_sub, int K)
 {
-    // split codebook (64 bytes per centroid), flag counter, flag list, max |c|
+    // split codebook (64 bytes per centroid), flag counter, flag list, max |c|,
+    // partial maxima
     return align_up((size_t)padded_K(K) * 64) + align_up(sizeof(int)) + align_up((size_t)n_sub * sizeof(int)) +
-           align_up(sizeof(float));
+           align_up(sizeof(float)) + align_up(sizeof(float) * kMaxBlocks);
 }
 
 // Enqueues the assignment; arguments already validated by the caller.
@@ -488,18 +588,27 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
     int* flag_count = cv.take<int>(1);
     int* flag_list = cv.take<int>((size_t)n_sub);
     float* cmax = cv.take<float>(1);
+    float* part = cv.take<float>(kMaxBlocks);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_assign: workspace too small");
     if (n_sub > (int64_t)INT32_MAX) return fail(VQ_ERR_UNSUPPORTED, "vq_assign: more than 2^31 sub-vectors");
 
     TimedRegion tr_all("assign", K, st);
-    hipLaunchKernelGGL(k_cb_absmax, dim3(1), dim3(1024), 0, st, C, (int64_t)K * d, cmax, flag_count);
-    VQ_LAUNCHED("k_cb_absmax");
+    const int nparts = (int)std::min<int64_t>(kMaxBlocks, ((int64_t)K * d + 255) / 256);
+    hipLaunchKernelGGL(k_cb_absmax_part, dim3(nparts), dim3(256), 0, st, C, (int64_t)K * d, part);
+    VQ_LAUNCHED("k_cb_absmax_part");
+    hipLaunchKernelGGL(k_cb_absmax_final, dim3(1), dim3(256), 0, st, part, nparts, cmax, flag_count);
+    VQ_LAUNCHED("k_cb_absmax_final");
     hipLaunchKernelGGL(k_cb_prep16, dim3(grid_for(Kpad, 256)), dim3(256), 0, st, C, K, d, Kpad, cmax, P);
     VQ_LAUNCHED("k_cb_prep16");
     {
         TimedRegion tr("assign_search", K, st);
-        hipLaunchKernelGGL(k_assign_h16, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st, X, hcol,
-                           rho, mask, n_sub, nb, d, P, cmax, C, K, Kpad / kChunkK, idx, dist, flag_count, flag_list);
+            const int nch = Kpad / kChunkK;
+        if (nch <= kSlotChunks)
+            hipLaunchKernelGGL(k_assign_h16<true>, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st,
+                               X, hcol, rho, mask, n_sub, nb, d, P, cmax, C, K, nch, idx, dist, flag_count, flag_list);
+        else
+            hipLaunchKernelGGL(k_assign_h16<false>, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st,
+                               X, hcol, rho, mask, n_sub, nb, d, P, cmax, C, K, nch, idx, dist, flag_count, flag_list);
         VQ_LAUNCHED("k_assign_h16");
     }
     const unsigned gx = (unsigned)std::min<int64_t>((n_sub + 3) / 4, kExactBlocks);

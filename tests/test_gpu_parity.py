@@ -58,6 +58,8 @@ ASSIGN_CASES = [
     (8, 1, 8, 8, 1, False, False),         # one sub-vector, K = 1
     (9, 50, 80, 8, 500, False, True),      # K = n_sub
     (10, 96, 96, 6, 200, True, True),
+    (11, 256, 512, 8, 3000, True, True),   # long codebook: per-tile tracking, last tile re-formed
+    (12, 300, 96, 3, 2500, True, False),   # long codebook, d = 3, ragged last chunk
 ]
 
 
