@@ -59,7 +59,7 @@ constexpr float kPadSq = 16384.0f;           // scaled c*c term of padding centr
 constexpr int kMaxBlocks = 256;   // blocks of the codebook max reduction
 
 // Largest |C| over the codebook, two passes: block maxima into part[], then
-// one block reduces them into *cmax and clears the flag counter.
+// one block reduces them into *cmax and clears the flag and dirty counters.
 __global__ __launch_bounds__(256) void k_cb_absmax_part(const float* __restrict__ C, int64_t n,
                                                         float* __restrict__ part)
 {
@@ -77,7 +77,8 @@ __global__ __launch_bounds__(256) void k_cb_absmax_part(const float* __restrict_
 }
 
 __global__ __launch_bounds__(256) void k_cb_absmax_final(const float* __restrict__ part, int nparts,
-                                                         float* __restrict__ cmax, int* __restrict__ flag_count)
+                                                         float* __restrict__ cmax, int* __restrict__ flag_count,
+                                                         int* __restrict__ dirty_count)
 {
     __shared__ float red[256];
     red[threadIdx.x] = (int)threadIdx.x < nparts ? part[threadIdx.x] : 0.f;
@@ -89,6 +90,7 @@ __global__ __launch_bounds__(256) void k_cb_absmax_final(const float* __restrict
     if (threadIdx.x == 0) {
         *cmax = red[0];
         *flag_count = 0;
+        *dirty_count = 0;
     }
 }
 
@@ -252,7 +254,212 @@ __device__ __forceinline__ f32x16 tile_h16(const h16x8 ah, const h16x8 al, const
     return acc;
 }
 
-// Workgroup = kWaves wavefronts x 32 consecutive sub-vectors; lane l of a
+// The majority mask byte of each column block (lowest byte on ties): the
+// weight pattern shared by most of its sub-vectors.
+__global__ __launch_bounds__(256) void k_block_pattern(const uint8_t* __restrict__ mask, int64_t M, int64_t nb,
+                                                       uint8_t* __restrict__ pattern)
+{
+    __shared__ int cnt[256];
+    __shared__ int best_c[256], best_p[256];
+    cnt[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t b = blockIdx.x;
+    for (int64_t i = threadIdx.x; i < M; i += 256) atomicAdd(&cnt[mask[i * nb + b]], 1);
+    __syncthreads();
+    best_c[threadIdx.x] = cnt[threadIdx.x];
+    best_p[threadIdx.x] = threadIdx.x;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) {
+            const int oc = best_c[threadIdx.x + w], op = best_p[threadIdx.x + w];
+            if (oc > best_c[threadIdx.x] || (oc == best_c[threadIdx.x] && op < best_p[threadIdx.x])) {
+                best_c[threadIdx.x] = oc;
+                best_p[threadIdx.x] = op;
+            }
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) pattern[b] = (uint8_t)best_p[0];
+}
+
+// Sub-vectors whose mask byte differs from their block's pattern are listed
+// for the general kernel: wavefront ballots, a workgroup prefix in LDS and
+// one integer atomic per workgroup (the order of the list does not affect
+// any result).
+__global__ __launch_bounds__(1024) void k_dirty(const uint8_t* __restrict__ mask, const uint8_t* __restrict__ pattern,
+                                                int64_t n_sub, uint32_t nb, int* __restrict__ count,
+                                                int* __restrict__ list)
+{
+    constexpr int kItems = 4;
+    __shared__ int wsum[kItems][16];
+    __shared__ int base;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    bool take[kItems];
+    unsigned long long ball[kItems];
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+        const int64_t s = ((int64_t)blockIdx.x * kItems + r) * 1024 + threadIdx.x;
+        take[r] = false;
+        if (s < n_sub) take[r] = mask[s] != pattern[(uint32_t)(s % nb)];
+        ball[r] = __ballot(take[r]);
+        if (lane == 0) wsum[r][wave] = __popcll(ball[r]);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int tot = 0;
+        for (int r = 0; r < kItems; ++r)
+            for (int w = 0; w < 16; ++w) tot += wsum[r][w];
+        base = tot ? atomicAdd(count, tot) : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+        if (take[r]) {
+            int off = base + __popcll(ball[r] & ((1ull << lane) - 1ull));
+            for (int q = 0; q < r; ++q)
+                for (int w = 0; w < 16; ++w) off += wsum[q][w];
+            for (int w = 0; w < wave; ++w) off += wsum[r][w];
+            const int64_t s = ((int64_t)blockIdx.x * kItems + r) * 1024 + threadIdx.x;
+            list[off] = (int)s;
+        }
+    }
+}
+
+// One 32x32 tile of the shared-weight form: two chained MFMAs (the small
+// cross products, then hi*hi with the bias), with the previous tile's
+// tracking update between them.
+template <bool SLOT>
+__device__ __forceinline__ f32x16 tile2_h16(const h16x8 a0, const h16x8 a1, const h16x8 b0, const h16x8 b1v,
+                                            const f32x16& prev, int ktp, float& b1, float& b2, int& pos)
+{
+    f32x16 acc = {};
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1v, acc, 0, 0, 0);
+    track<SLOT>(prev, ktp, b1, b2, pos);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
+    }
+    return acc;
+}
+
+// Final merge and certification of one lane pair (the two halves of a
+// wavefront column), shared by both search kernels.  b1, b2 and pos come from
+// the tracking; S_sc and shift_s are the sub-vector's scaled energy and
+// scale; a writer lane that is not certified (or is marked bad) is appended
+// to the exact re-search list.
+template <bool SLOT>
+__device__ __forceinline__ void search_epilogue(
+    const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
+    const uint8_t* __restrict__ mask, int64_t nb, int d, const float* __restrict__ C, int K, int64_t s,
+    bool valid, bool writer_ok, bool bad, int lane, int half, float b1, float b2, int kt1, float S_sc, int shift_s,
+    uint16_t* __restrict__ idx, float* __restrict__ dist, int* __restrict__ flag_count, int* __restrict__ flag_list)
+{
+    // ---- epilogue: best and second best of this sub-vector -------------
+    // Slot j of this lane holds centroid row (j/4)*8 + half*4 + j%4 of a tile,
+    // rows ascending with j.  Per-slot tracking knows the best position
+    // (kt1 = tile*16 + slot).  Per-tile tracking knows the best tile: its 16
+    // values of this lane are formed again in fp32 (a fused multiply-add chain
+    // over the 16 terms: within 17u of exact, inside the search's bound) to
+    // find the best slot (the first minimum: lowest index) and the tile's
+    // second best.
+    float v1 = __builtin_inff(), v2 = __builtin_inff();
+    int kb = K;
+    if (SLOT) {
+        const int jb = kt1 & 15;
+        kb = (kt1 >> 4) * kTile + (jb >> 2) * 8 + half * 4 + (jb & 3);
+        v1 = b1;
+    } else {
+        float bw[8], om[8];
+        const int64_t b = valid ? s % nb : 0;
+        const unsigned mb = (valid && mask) ? mask[s] : 0u;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            float xv = 0.f, w = 0.f;
+            if (valid && t < d) {
+                xv = X[s * d + t];
+                w = ((mb >> t) & 1u) ? 0.f : hcol[b * d + t];
+            }
+            om[t] = w;
+            bw[t] = w * xv;
+        }
+        const bool vecC = d == 8 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
+#pragma unroll 2
+        for (int j = 0; j < 16; ++j) {
+            const int k = kt1 * kTile + (j >> 2) * 8 + half * 4 + (j & 3);
+            if (k >= K) continue;
+            float c[8];
+            if (vecC) {
+                const float4 ca = reinterpret_cast<const float4*>(C)[(size_t)k * 2];
+                const float4 cb = reinterpret_cast<const float4*>(C)[(size_t)k * 2 + 1];
+                c[0] = ca.x; c[1] = ca.y; c[2] = ca.z; c[3] = ca.w;
+                c[4] = cb.x; c[5] = cb.y; c[6] = cb.z; c[7] = cb.w;
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) c[t] = t < d ? C[(size_t)k * d + t] : 0.f;
+            }
+            float e = 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) e = fmaf(bw[t], -2.f * c[t], e);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) e = fmaf(om[t], c[t] * c[t], e);
+            const float v = ldexpf(e, shift_s);
+            if (v < v1) {
+                v2 = v1;
+                v1 = v;
+                kb = k;
+            } else {
+                v2 = fminf(v2, v);
+            }
+        }
+    }
+    b1 = v1;
+    const float sec = fminf(b2, v2);
+
+    const float ob1 = __shfl_xor(b1, 32);
+    const float osec = __shfl_xor(sec, 32);
+    const int okb = __shfl_xor(kb, 32);
+    float gb, gs;
+    int gk;
+    if (b1 < ob1 || (b1 == ob1 && kb < okb)) {
+        gb = b1; gk = kb; gs = fminf(sec, ob1);
+    } else {
+        gb = ob1; gk = okb; gs = fminf(osec, b1);
+    }
+    const float u = 5.9604644775390625e-8f;   // 2^-24
+    const float eb = 48.f * u * (9.f * S_sc + 4.f * fmaxf(gb, -S_sc)) + 1.f;
+    const float es = 48.f * u * (9.f * S_sc + 4.f * fmaxf(gs, -S_sc)) + 1.f;
+    const bool certified = (gs - gb) > (eb + es) && gk < K && !bad;
+
+    const bool writer = writer_ok && half == 0;
+    if (writer && certified) {
+        idx[s] = (uint16_t)gk;
+        if (dist) {
+            double omd[8];
+            float xs[8];
+            exact_weights(hcol, rho, mask, s, nb, d, omd);
+            for (int t = 0; t < d; ++t) xs[t] = X[s * d + t];
+            dist[s] = (float)exact_dist(omd, xs, C + (size_t)gk * d, d);
+        }
+    }
+    // uncertified winners go to the exact search (one atomic per wave)
+    const bool flag = writer && !certified;
+    const unsigned long long ball = __ballot(flag);
+    if (ball) {
+        int base = 0;
+        const int leader = __ffsll((long long)ball) - 1;
+        if (lane == leader) base = atomicAdd(flag_count, __popcll(ball));
+        base = __shfl(base, leader);
+        if (flag) {
+            const int rank = __popcll(ball & ((1ull << lane) - 1ull));
+            flag_list[base + rank] = (int)s;
+        }
+    }
+}
+
+// Workgroup = kWaves wavefronts x 32 sub-vectors (consecutive ones, or the
+// next 256 entries of a list); lane l of a
 // wavefront works on sub-vector (l & 31) of its 32: the lanes of the lower
 // half supply the scaled omega*x parts (MFMA k-slots 0-7), those of the
 // upper half the scaled omega parts (k-slots 8-15).  The split codebook
@@ -268,6 +475,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
     const uint8_t* __restrict__ mask, int64_t n_sub, int64_t nb, int d, const uint4* __restrict__ P,
     const float* __restrict__ cmax, const float* __restrict__ C, int K, int nchunks,
+    const int* __restrict__ list, const int* __restrict__ list_count,
     uint16_t* __restrict__ idx, float* __restrict__ dist, int* __restrict__ flag_count, int* __restrict__ flag_list)
 {
     constexpr int kChunkVec = kChunkTiles * 128;                 // uint4 per chunk
@@ -275,13 +483,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
     static_assert(kChunkVec == 2 * kWaves * 64, "two uint4 per thread per chunk");
     __shared__ uint4 lds[2][kChunkVec];
 
+    // without a list: sub-vectors 0 .. n_sub-1; with one: list[0 .. *list_count-1]
+    const int64_t count = list ? (int64_t)*list_count : n_sub;
+    if ((int64_t)blockIdx.x * kSubPerBlock >= count) return;     // whole workgroup idle
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int half = lane >> 5;
     const int64_t w0 = ((int64_t)blockIdx.x * kWaves + wave) * kSubPerWave;
-    const bool active = w0 < n_sub;                               // wave-uniform
-    const int64_t s = w0 + (lane & 31);
-    const bool valid = s < n_sub;
+    const bool active = w0 < count;                               // wave-uniform
+    const int64_t q = w0 + (lane & 31);
+    const bool valid = q < count;
+    const int64_t s = valid ? (list ? (int64_t)list[q] : q) : 0;
 
     // ---- the sub-vector's weights, scaled split B operand, S -----------
     h16x8 bh, bl;
@@ -375,106 +587,195 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
     if (!active) return;
     track<SLOT>(accB, ktB, b1, b2, kt1);
 
-    // ---- epilogue: best and second best of this sub-vector -------------
-    // Slot j of this lane holds centroid row (j/4)*8 + half*4 + j%4 of a tile,
-    // rows ascending with j.  Per-slot tracking knows the best position
-    // (kt1 = tile*16 + slot).  Per-tile tracking knows the best tile: its 16
-    // values of this lane are formed again in fp32 (a fused multiply-add chain
-    // over the 16 terms: within 17u of exact, inside the search's bound) to
-    // find the best slot (the first minimum: lowest index) and the tile's
-    // second best.
-    float v1 = __builtin_inff(), v2 = __builtin_inff();
-    int kb = K;
-    if (SLOT) {
-        const int jb = kt1 & 15;
-        kb = (kt1 >> 4) * kTile + (jb >> 2) * 8 + half * 4 + (jb & 3);
-        v1 = b1;
-    } else {
-        float bw[8], om[8];
-        const int64_t b = valid ? s % nb : 0;
-        const unsigned mb = (valid && mask) ? mask[s] : 0u;
+    search_epilogue<SLOT>(X, hcol, rho, mask, nb, d, C, K, s, valid, valid, false, lane, half, b1, b2, kt1, S_sc,
+                          shift_s, idx, dist, flag_count, flag_list);
+}
+
+// Sub-vectors that share one weight vector: workgroup = column block b x 256
+// consecutive rows (wavefront w: rows rb*256 + w*32 + (l & 31)), taken with
+// the block's majority mask byte.  Their common weights make
+// sum_t omega_t c_t^2 a per-centroid bias.  The workgroup forms it once per
+// chunk in float64 (rounded once to fp32), scales it by 2^sb and splits it
+// into two fp16 parts that enter the second MFMA through two k-slots against
+// a power-of-two gamma on the B side.  A tile then takes two MFMAs:
+//   1: lower half al(-2 beta c) . bh(alpha omega x), upper half ah(-2 beta c) . bl(alpha omega x)
+//   2: lower half ah(-2 beta c) . bh(alpha omega x), upper half [bias_hi, bias_lo] . [gamma, gamma]
+// with gamma = alpha * beta * 2^-sb.  alpha is capped so that gamma <= 2^15.
+// A lane whose gamma would fall below 2^-24 is sent to the exact re-search.
+// The general form's error bound holds: the bias is within 1.25u of
+// sum omega c*c, and the last MFMA adds 10 products to a small accumulator.
+// Lanes whose own mask byte differs from the block's are computed but not
+// written: they are in the list of the general kernel.
+template <bool SLOT>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_assign_h16s(
+    const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
+    const uint8_t* __restrict__ mask, const uint8_t* __restrict__ pattern, int64_t M, int64_t nb, int d,
+    const uint4* __restrict__ P, const float* __restrict__ cmax, const float* __restrict__ C, int K, int nchunks,
+    uint16_t* __restrict__ idx, float* __restrict__ dist, int* __restrict__ flag_count, int* __restrict__ flag_list)
+{
+    constexpr int kRowVec = kChunkTiles * 96;    // uint4 per chunk: rows (lo, hi, bias) of 32 per tile
+    static_assert(kChunkTiles * 64 == kWaves * 64, "one cross-term uint4 per thread per chunk");
+    static_assert(kChunkTiles % 2 == 0, "tiles are processed in pairs");
+    __shared__ uint4 lds[2][kRowVec];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int half = lane >> 5;
+    const int64_t rb = (int64_t)blockIdx.x / nb;
+    const int64_t b = (int64_t)blockIdx.x - rb * nb;
+    const int64_t i = rb * kSubPerBlock + wave * kSubPerWave + (lane & 31);
+    const bool active = rb * kSubPerBlock + wave * kSubPerWave < M;    // wave-uniform
+    const bool valid = i < M;
+    const int64_t s = valid ? i * nb + b : 0;
+    const unsigned pat = pattern ? pattern[b] : 0u;
+    const unsigned mb = (valid && mask) ? mask[s] : 0u;
+    const bool owner = valid && mb == pat;
+
+    // the block's weights (its majority pattern), the same in every lane:
+    // kept in scalar registers
+    float om[8];
+    float wsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const float w = (t < d && !((pat >> t) & 1u)) ? hcol[b * d + t] : 0.f;
+        om[t] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, w)));
+        wsum += om[t];
+    }
+    int e1, e2;
+    cb_exponents(*cmax, e1, e2);
+    // bias scale: every bias_k <= sum_t omega_t * max c^2 (margin for roundings)
+    const float cm = *cmax;
+    const float bmax = wsum * (cm * cm) * 1.0001f;
+    int eb = 0;
+    if (bmax > 0.f) frexpf(bmax, &eb);
+    const int sb = 15 - eb;                   // bias * 2^sb < 2^15
+
+    h16x8 bA, bB;    // B operands of the two MFMAs (per half)
+    float S_sc;
+    int shift_s;
+    bool bad;
+    {
+        float raw[8];
+        float S = 0.f, mx = 0.f;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            float xv = 0.f, w = 0.f;
-            if (valid && t < d) {
-                xv = X[s * d + t];
-                w = ((mb >> t) & 1u) ? 0.f : hcol[b * d + t];
-            }
-            om[t] = w;
-            bw[t] = w * xv;
+            const float xv = (valid && t < d) ? X[s * d + t] : 0.f;
+            S += om[t] * xv * xv;
+            raw[t] = om[t] * xv;
+            mx = fmaxf(mx, fabsf(raw[t]));
         }
-        const bool vecC = d == 8 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
-#pragma unroll 2
-        for (int j = 0; j < 16; ++j) {
-            const int k = kt1 * kTile + (j >> 2) * 8 + half * 4 + (j & 3);
-            if (k >= K) continue;
-            float c[8];
-            if (vecC) {
-                const float4 ca = reinterpret_cast<const float4*>(C)[(size_t)k * 2];
-                const float4 cb = reinterpret_cast<const float4*>(C)[(size_t)k * 2 + 1];
-                c[0] = ca.x; c[1] = ca.y; c[2] = ca.z; c[3] = ca.w;
-                c[4] = cb.x; c[5] = cb.y; c[6] = cb.z; c[7] = cb.w;
-            } else {
+        int ex = 0;
+        if (mx > 0.f) frexpf(mx, &ex);
+        const int cap = sb + e1;                                  // keeps gamma <= 2^15
+        const int sh = mx > 0.f ? min(15 - ex, cap) : cap;
+        const int gexp = sh + (15 - e1) - sb;
+        bad = gexp < -24;
+        h16x8 bh, bl;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) c[t] = t < d ? C[(size_t)k * d + t] : 0.f;
-            }
-            float e = 0.f;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) e = fmaf(bw[t], -2.f * c[t], e);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) e = fmaf(om[t], c[t] * c[t], e);
-            const float v = ldexpf(e, shift_s);
-            if (v < v1) {
-                v2 = v1;
-                v1 = v;
-                kb = k;
-            } else {
-                v2 = fminf(v2, v);
-            }
+        for (int t = 0; t < 8; ++t) {
+            _Float16 h, l;
+            split_h16(ldexpf(raw[t], sh), h, l);
+            bh[t] = h;
+            bl[t] = l;
         }
+        h16x8 gv = {};
+        const _Float16 g = (_Float16)ldexpf(1.f, max(gexp, -24));
+        gv[0] = g;
+        gv[1] = g;
+        bA = half ? bl : bh;
+        bB = half ? gv : bh;
+        shift_s = sh + (15 - e1);
+        S_sc = ldexpf(S, shift_s);
     }
-    b1 = v1;
-    const float sec = fminf(b2, v2);
 
-    const float ob1 = __shfl_xor(b1, 32);
-    const float osec = __shfl_xor(sec, 32);
-    const int okb = __shfl_xor(kb, 32);
-    float gb, gs;
-    int gk;
-    if (b1 < ob1 || (b1 == ob1 && kb < okb)) {
-        gb = b1; gk = kb; gs = fminf(sec, ob1);
-    } else {
-        gb = ob1; gk = okb; gs = fminf(osec, b1);
-    }
-    const float u = 5.9604644775390625e-8f;   // 2^-24
-    const float eb = 48.f * u * (9.f * S_sc + 4.f * fmaxf(gb, -S_sc)) + 1.f;
-    const float es = 48.f * u * (9.f * S_sc + 4.f * fmaxf(gs, -S_sc)) + 1.f;
-    const bool certified = (gs - gb) > (eb + es) && gk < K;
+    // chunk staging: thread q copies one cross-term uint4 (tile q/64, row
+    // (q/32)&1: 0 = lo, 1 = hi, position q&31); threads q < 256 form the bias
+    // part of centroid q of the chunk
+    const int ct = threadIdx.x >> 6, crow = (threadIdx.x >> 5) & 1, cpos = threadIdx.x & 31;
+    const bool vecC = d == 8 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
+    auto load_cross = [&](int c) -> uint4 {
+        return P[(size_t)(c * kChunkTiles + ct) * 128 + (crow == 0 ? 64 : 0) + cpos];
+    };
+    auto load_row = [&](int c, float4& r0, float4& r1) {
+        r0 = make_float4(0.f, 0.f, 0.f, 0.f);
+        r1 = r0;
+        const int k = c * kChunkTiles * kTile + (int)threadIdx.x;
+        if (threadIdx.x >= kChunkTiles * kTile || k >= K) return;
+        if (vecC) {
+            r0 = reinterpret_cast<const float4*>(C)[(size_t)k * 2];
+            r1 = reinterpret_cast<const float4*>(C)[(size_t)k * 2 + 1];
+        } else {
+            float v[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[t] = t < d ? C[(size_t)k * d + t] : 0.f;
+            r0 = make_float4(v[0], v[1], v[2], v[3]);
+            r1 = make_float4(v[4], v[5], v[6], v[7]);
+        }
+    };
+    auto store_chunk = [&](int buf, int c, const uint4& cross, const float4& r0, const float4& r1) {
+        lds[buf][ct * 96 + crow * 32 + cpos] = cross;
+        if (threadIdx.x < kChunkTiles * kTile) {
+            const int k = c * kChunkTiles * kTile + (int)threadIdx.x;
+            float a;
+            if (k < K) {
+                const double cv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+                double acc = 0.0;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) acc = acc + (double)om[t] * (cv[t] * cv[t]);
+                a = ldexpf((float)acc, sb);
+            } else {
+                a = kPadSq;
+            }
+            _Float16 h, l;
+            split_h16(a, h, l);
+            h16x8 v = {};
+            v[0] = h;
+            v[1] = l;
+            const int tt = threadIdx.x >> 5, m = threadIdx.x & 31;
+            lds[buf][tt * 96 + 64 + m] = __builtin_bit_cast(uint4, v);
+        }
+    };
 
-    const bool writer = valid && half == 0;
-    if (writer && certified) {
-        idx[s] = (uint16_t)gk;
-        if (dist) {
-            double omd[8];
-            float xs[8];
-            exact_weights(hcol, rho, mask, s, nb, d, omd);
-            for (int t = 0; t < d; ++t) xs[t] = X[s * d + t];
-            dist[s] = (float)exact_dist(omd, xs, C + (size_t)gk * d, d);
+    float b1 = __builtin_inff(), b2 = __builtin_inff();
+    int kt1 = 0;
+    uint4 pre = load_cross(0);
+    float4 r0, r1;
+    load_row(0, r0, r1);
+    store_chunk(0, 0, pre, r0, r1);
+    __syncthreads();
+
+    f32x16 accA, accB;
+    for (int j = 0; j < 16; ++j) accB[j] = __builtin_inff();
+    int ktB = 0;
+    const int a_off = half * 32 + (lane & 31);
+    for (int c = 0; c < nchunks; ++c) {
+        if (c + 1 < nchunks) {
+            pre = load_cross(c + 1);
+            load_row(c + 1, r0, r1);
         }
-    }
-    // uncertified winners go to the exact search (one atomic per wave)
-    const bool flag = writer && !certified;
-    const unsigned long long ball = __ballot(flag);
-    if (ball) {
-        int base = 0;
-        const int leader = __ffsll((long long)ball) - 1;
-        if (lane == leader) base = atomicAdd(flag_count, __popcll(ball));
-        base = __shfl(base, leader);
-        if (flag) {
-            const int rank = __popcll(ball & ((1ull << lane) - 1ull));
-            flag_list[base + rank] = (int)s;
+        if (active) {
+            const uint4* L = lds[c & 1] + a_off;
+            const int kt0 = c * kChunkTiles;
+#pragma unroll 1
+            for (int tt = 0; tt < kChunkTiles; tt += 2) {
+                const uint4* A0 = L + tt * 96;
+                const uint4* A1 = A0 + 96;
+                const h16x8 p0 = __builtin_bit_cast(h16x8, A0[0]);
+                const h16x8 q0 = __builtin_bit_cast(h16x8, A0[32]);
+                accA = tile2_h16<SLOT>(p0, q0, bA, bB, accB, ktB, b1, b2, kt1);
+                const h16x8 p1 = __builtin_bit_cast(h16x8, A1[0]);
+                const h16x8 q1 = __builtin_bit_cast(h16x8, A1[32]);
+                accB = tile2_h16<SLOT>(p1, q1, bA, bB, accA, kt0 + tt, b1, b2, kt1);
+                ktB = kt0 + tt + 1;
+            }
         }
+        if (c + 1 < nchunks) store_chunk((c + 1) & 1, c + 1, pre, r0, r1);
+        __syncthreads();
     }
+    if (!active) return;
+    track<SLOT>(accB, ktB, b1, b2, kt1);
+    search_epilogue<SLOT>(X, hcol, rho, mask, nb, d, C, K, s, valid, owner, bad, lane, half, b1, b2, kt1, S_sc,
+                          shift_s, idx, dist, flag_count, flag_list);
 }
 
 // Exact re-search of the flagged sub-vectors: one wavefront per flagged
@@ -570,9 +871,11 @@ inline int padded_K(int K) { return (K + kChunkK - 1) / kChunkK * kChunkK; }
 size_t ws_assign(int64_t n_sub, int K)
 {
     // split codebook (64 bytes per centroid), flag counter, flag list, max |c|,
-    // partial maxima
+    // partial maxima, dirty counter, dirty list, block patterns (at most n_sub
+    // column blocks)
     return align_up((size_t)padded_K(K) * 64) + align_up(sizeof(int)) + align_up((size_t)n_sub * sizeof(int)) +
-           align_up(sizeof(float)) + align_up(sizeof(float) * kMaxBlocks);
+           align_up(sizeof(float)) + align_up(sizeof(float) * kMaxBlocks) + align_up(sizeof(int)) +
+           align_up((size_t)n_sub * sizeof(int)) + align_up((size_t)n_sub);
 }
 
 // Enqueues the assignment; arguments already validated by the caller.
@@ -589,27 +892,54 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
     int* flag_list = cv.take<int>((size_t)n_sub);
     float* cmax = cv.take<float>(1);
     float* part = cv.take<float>(kMaxBlocks);
+    int* dirty_count = cv.take<int>(1);
+    int* dirty_list = cv.take<int>((size_t)n_sub);
+    uint8_t* pattern = cv.take<uint8_t>((size_t)nb);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_assign: workspace too small");
     if (n_sub > (int64_t)INT32_MAX) return fail(VQ_ERR_UNSUPPORTED, "vq_assign: more than 2^31 sub-vectors");
+    const int64_t shared_groups = (M + kSubPerBlock - 1) / kSubPerBlock * nb;
+    if (shared_groups > (int64_t)UINT32_MAX) return fail(VQ_ERR_UNSUPPORTED, "vq_assign: grid too large");
 
     TimedRegion tr_all("assign", K, st);
     const int nparts = (int)std::min<int64_t>(kMaxBlocks, ((int64_t)K * d + 255) / 256);
     hipLaunchKernelGGL(k_cb_absmax_part, dim3(nparts), dim3(256), 0, st, C, (int64_t)K * d, part);
     VQ_LAUNCHED("k_cb_absmax_part");
-    hipLaunchKernelGGL(k_cb_absmax_final, dim3(1), dim3(256), 0, st, part, nparts, cmax, flag_count);
+    hipLaunchKernelGGL(k_cb_absmax_final, dim3(1), dim3(256), 0, st, part, nparts, cmax, flag_count, dirty_count);
     VQ_LAUNCHED("k_cb_absmax_final");
     hipLaunchKernelGGL(k_cb_prep16, dim3(grid_for(Kpad, 256)), dim3(256), 0, st, C, K, d, Kpad, cmax, P);
     VQ_LAUNCHED("k_cb_prep16");
     {
         TimedRegion tr("assign_search", K, st);
-            const int nch = Kpad / kChunkK;
-        if (nch <= kSlotChunks)
-            hipLaunchKernelGGL(k_assign_h16<true>, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st,
-                               X, hcol, rho, mask, n_sub, nb, d, P, cmax, C, K, nch, idx, dist, flag_count, flag_list);
-        else
-            hipLaunchKernelGGL(k_assign_h16<false>, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st,
-                               X, hcol, rho, mask, n_sub, nb, d, P, cmax, C, K, nch, idx, dist, flag_count, flag_list);
-        VQ_LAUNCHED("k_assign_h16");
+        const int nch = Kpad / kChunkK;
+        const bool slot = nch <= kSlotChunks;
+        if (slot) {
+            // short codebooks: one pass of the general form (the block
+            // classification would cost more than the shared form saves)
+            hipLaunchKernelGGL(k_assign_h16<true>, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st, X,
+                               hcol, rho, mask, n_sub, nb, d, P, cmax, C, K, nch, nullptr, nullptr, idx, dist,
+                               flag_count, flag_list);
+            VQ_LAUNCHED("k_assign_h16");
+        } else {
+        if (mask) {
+            hipLaunchKernelGGL(k_block_pattern, dim3((unsigned)nb), dim3(256), 0, st, mask, M, nb, pattern);
+            VQ_LAUNCHED("k_block_pattern");
+            hipLaunchKernelGGL(k_dirty, dim3(grid_for(n_sub, 4096)), dim3(1024), 0, st, mask, pattern, n_sub,
+                               (uint32_t)nb, dirty_count, dirty_list);
+            VQ_LAUNCHED("k_dirty");
+        }
+        // sub-vectors with their block's weights: two MFMAs per tile
+        hipLaunchKernelGGL(k_assign_h16s<false>, dim3((unsigned)shared_groups), dim3(kWaves * 64), 0, st, X, hcol,
+                           rho, mask, mask ? pattern : nullptr, M, nb, d, P, cmax, C, K, nch, idx, dist, flag_count,
+                           flag_list);
+        VQ_LAUNCHED("k_assign_h16s");
+        // the rest, each with its own weights: three MFMAs per tile
+        if (mask) {
+            hipLaunchKernelGGL(k_assign_h16<false>, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st, X,
+                               hcol, rho, mask, n_sub, nb, d, P, cmax, C, K, nch, dirty_list, dirty_count, idx, dist,
+                               flag_count, flag_list);
+            VQ_LAUNCHED("k_assign_h16");
+        }
+        }
     }
     const unsigned gx = (unsigned)std::min<int64_t>((n_sub + 3) / 4, kExactBlocks);
     const int vecC = (d == 8 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0) ? 1 : 0;
