@@ -182,17 +182,19 @@ __device__ inline void exact_weights(const float* hcol, const float* rho, const 
     }
 }
 
-// Minimum of a tile's 16 accumulator values (min3 chains).
+// Minimum of a tile's 16 accumulator values: five three-way minima of the
+// raw values, then two of their results, then one pair (seven v_min3 and one
+// v_min; no operand of a two-way minimum is a raw accumulator value).
 __device__ __forceinline__ float tile_min(const f32x16& a)
 {
-    float m0 = fminf(fminf(a[0], a[1]), a[2]);
-    float m1 = fminf(fminf(a[3], a[4]), a[5]);
-    float m2 = fminf(fminf(a[6], a[7]), a[8]);
-    float m3 = fminf(fminf(a[9], a[10]), a[11]);
-    float m4 = fminf(fminf(a[12], a[13]), a[14]);
-    m0 = fminf(fminf(m0, m1), m2);
-    m3 = fminf(fminf(m3, m4), a[15]);
-    return fminf(m0, m3);
+    const float m0 = fminf(fminf(a[0], a[1]), a[2]);
+    const float m1 = fminf(fminf(a[3], a[4]), a[5]);
+    const float m2 = fminf(fminf(a[6], a[7]), a[8]);
+    const float m3 = fminf(fminf(a[9], a[10]), a[11]);
+    const float m4 = fminf(fminf(a[12], a[13]), a[14]);
+    const float n0 = fminf(fminf(m0, m1), m2);
+    const float n1 = fminf(fminf(m3, m4), a[15]);
+    return fminf(n0, n1);
 }
 
 // Per-lane tracking over tiles, branch-free: b1 = smallest tile minimum so
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
 // Lanes whose own mask byte differs from the block's are computed but not
 // written: they are in the list of the general kernel.
 template <bool SLOT>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_assign_h16s(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_assign_h16s(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
     const uint8_t* __restrict__ mask, const uint8_t* __restrict__ pattern, int64_t M, int64_t nb, int d,
     const uint4* __restrict__ P, const float* __restrict__ cmax, const float* __restrict__ C, int K, int nchunks,
