@@ -168,16 +168,22 @@ __global__ void k_decode(int64_t n_sub, int64_t nb, int d, const float* __restri
 }
 
 // d == 8 with 16-byte aligned buffers: one thread per half sub-vector,
-// 16-byte loads and stores, same operation order as k_decode.
-__global__ void k_decode8(int64_t n_half, int64_t nb, const float4* __restrict__ C1, int K1,
-                          const uint16_t* __restrict__ idx1, const float4* __restrict__ C2, int K2,
-                          const uint16_t* __restrict__ idx2, const float* __restrict__ rs,
-                          const float4* __restrict__ cs, float4* __restrict__ Wh)
+// 16-byte loads and stores, same operation order as k_decode.  Workgroups are
+// laid out by row (bpr workgroups per row), so the row and its scale come
+// from the workgroup number.
+__global__ __launch_bounds__(kBlock) void k_decode8(int64_t nb, unsigned bpr, const float4* __restrict__ C1, int K1,
+                                                    const uint16_t* __restrict__ idx1, const float4* __restrict__ C2,
+                                                    int K2, const uint16_t* __restrict__ idx2,
+                                                    const float* __restrict__ rs, const float4* __restrict__ cs,
+                                                    float4* __restrict__ Wh)
 {
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= n_half) return;
-    const int64_t s = q >> 1;
-    const int half = (int)(q & 1);
+    const int64_t i = blockIdx.x / bpr;
+    const int64_t hq = (int64_t)(blockIdx.x - (unsigned)i * bpr) * kBlock + threadIdx.x;
+    if (hq >= 2 * nb) return;
+    const int64_t b = hq >> 1;
+    const int half = (int)(hq & 1);
+    const int64_t s = i * nb + b;
+    const int64_t q = i * 2 * nb + hq;
     const int k1 = idx1[s];
     const int k2 = C2 ? idx2[s] : 0;
     float4 v;
@@ -192,36 +198,28 @@ __global__ void k_decode8(int64_t n_half, int64_t nb, const float4* __restrict__
         v.x = v.x + c.x; v.y = v.y + c.y; v.z = v.z + c.z; v.w = v.w + c.w;
     }
     if (cs) {
-        const int64_t i = s / nb;
-        const int64_t b = s - i * nb;
         const float4 c = cs[b * 2 + half];
         v.x = v.x * c.x; v.y = v.y * c.y; v.z = v.z * c.z; v.w = v.w * c.w;
     }
     if (rs) {
-        const float ri = rs[s / nb];
+        const float ri = rs[i];
         v.x = v.x * ri; v.y = v.y * ri; v.z = v.z * ri; v.w = v.w * ri;
     }
     Wh[q] = v;
 }
 
 // The exact salient values overwrite their positions (HAS-VQ abstract:
-// exact reconstruction of the decoupled weights).  One thread per CSR entry
-// (grid-stride; nnz = row_ptr[M] is read on the device), row found by a
-// binary search of the row pointers.
-__global__ void k_sparse_overwrite(int64_t M, int64_t N, const int32_t* __restrict__ row_ptr,
-                                   const int32_t* __restrict__ col, const float* __restrict__ val,
-                                   float* __restrict__ Wh)
+// exact reconstruction of the decoupled weights).  One workgroup per row;
+// its threads stride over the row's CSR entries.
+__global__ __launch_bounds__(kBlock) void k_sparse_overwrite(int64_t N, const int32_t* __restrict__ row_ptr,
+                                                             const int32_t* __restrict__ col,
+                                                             const float* __restrict__ val, float* __restrict__ Wh)
 {
-    const int64_t nnz = row_ptr[M];
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nnz; e += stride) {
-        int64_t lo = 0, hi = M;   // row_ptr[lo] <= e < row_ptr[hi]
-        while (hi - lo > 1) {
-            const int64_t mid = (lo + hi) >> 1;
-            if (row_ptr[mid] <= e) lo = mid; else hi = mid;
-        }
+    const int64_t i = blockIdx.x;
+    const int64_t e1 = row_ptr[i + 1];
+    for (int64_t e = row_ptr[i] + threadIdx.x; e < e1; e += kBlock) {
         const int32_t j = col[e];
-        if (j >= 0 && j < N) Wh[lo * N + j] = val[e];   // an out-of-range column is skipped
+        if (j >= 0 && j < N) Wh[i * N + j] = val[e];   // an out-of-range column is skipped
     }
 }
 
@@ -275,19 +273,29 @@ __global__ __launch_bounds__(kBlock) void k_objective_partial(
     if (threadIdx.x == 0) part[blockIdx.x] = tot;
 }
 
-// One block adds the partials: strided per-thread sums, then a fixed tree.
-__global__ __launch_bounds__(kBlock) void k_sum_partials(const double* __restrict__ part, int64_t n,
-                                                         double* __restrict__ out)
+// One block of 1024 adds the partials: strided per-thread sums (four
+// independent chains, added in a fixed order), then a fixed tree.
+__global__ __launch_bounds__(1024) void k_sum_partials(const double* __restrict__ part, int64_t n,
+                                                       double* __restrict__ out)
 {
-    __shared__ double sh[kBlock];
-    double acc = 0.0;
-    for (int64_t e = threadIdx.x; e < n; e += kBlock) acc = acc + part[e];
-    const double tot = block_sum_f64(acc, sh);
-    if (threadIdx.x == 0) *out = tot;
+    __shared__ double sh[1024];
+    double a[4] = {0.0, 0.0, 0.0, 0.0};
+    int64_t e = threadIdx.x;
+    for (; e + 3 * 1024 < n; e += 4 * 1024) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a[u] = a[u] + part[e + u * 1024];
+    }
+    for (; e < n; e += 1024) a[0] = a[0] + part[e];
+    sh[threadIdx.x] = (a[0] + a[1]) + (a[2] + a[3]);
+    __syncthreads();
+    for (int w = 512; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) sh[threadIdx.x] = sh[threadIdx.x] + sh[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *out = sh[0];
 }
 
 constexpr int64_t kColChunk = 64;
-constexpr unsigned kOverwriteBlocks = 1024;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 constexpr int64_t kRowGroups = 32;
@@ -350,9 +358,9 @@ vq_status reconstruct_launch(int64_t M, int64_t N, int d, const float* C1, int K
 {
     const int64_t n_sub = M * N / d;
     TimedRegion tr("reconstruct", K1, st);
-    if (d == 8 && aligned16(C1) && aligned16(C2) && aligned16(cs) && aligned16(Wh)) {
-        const int64_t n_half = n_sub * 2;
-        hipLaunchKernelGGL(k_decode8, dim3(grid_for(n_half, kBlock)), dim3(kBlock), 0, st, n_half, N / d,
+    const int64_t bpr = (2 * (N / d) + kBlock - 1) / kBlock;   // workgroups per row in k_decode8
+    if (d == 8 && aligned16(C1) && aligned16(C2) && aligned16(cs) && aligned16(Wh) && M * bpr <= (int64_t)UINT32_MAX) {
+        hipLaunchKernelGGL(k_decode8, dim3((unsigned)(M * bpr)), dim3(kBlock), 0, st, N / d, (unsigned)bpr,
                            reinterpret_cast<const float4*>(C1), K1, idx1, reinterpret_cast<const float4*>(C2),
                            K2, idx2, rs, reinterpret_cast<const float4*>(cs), reinterpret_cast<float4*>(Wh));
         VQ_LAUNCHED("k_decode8");
@@ -362,8 +370,8 @@ vq_status reconstruct_launch(int64_t M, int64_t N, int d, const float* C1, int K
         VQ_LAUNCHED("k_decode");
     }
     if (row_ptr) {
-        hipLaunchKernelGGL(k_sparse_overwrite, dim3(kOverwriteBlocks), dim3(kBlock), 0, st, M, N, row_ptr,
-                           col, val, Wh);
+        if (M > (int64_t)UINT32_MAX) return fail(VQ_ERR_UNSUPPORTED, "vq_reconstruct: too many rows");
+        hipLaunchKernelGGL(k_sparse_overwrite, dim3((unsigned)M), dim3(kBlock), 0, st, N, row_ptr, col, val, Wh);
         VQ_LAUNCHED("k_sparse_overwrite");
     }
     return VQ_OK;
@@ -383,7 +391,7 @@ vq_status objective_launch(const float* X, const float* hcol, const float* rho, 
     hipLaunchKernelGGL(k_objective_partial, dim3(nblk), dim3(kBlock), 0, st, X, hcol, rho, mask, n_sub,
                        (uint32_t)(N / d), d, C, K, idx, vec, part);
     VQ_LAUNCHED("k_objective_partial");
-    hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kBlock), 0, st, part, (int64_t)nblk, J);
+    hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(1024), 0, st, part, (int64_t)nblk, J);
     VQ_LAUNCHED("k_sum_partials");
     return VQ_OK;
 }
