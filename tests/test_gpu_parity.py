@@ -78,6 +78,40 @@ def test_assign_matches_oracle_bitwise(case):
     assert bits_equal(host(dist), ref_dist.astype(np.float32))
 
 
+@pytest.mark.parametrize("mode", ["no-mask", "zero-mask", "salient"])
+def test_assign_long_codebook_block_shared_weights(mode):
+    # K > 2048: sub-vectors of a column block that share its weights take the
+    # two-MFMA form, the others (their own mask byte) the three-MFMA form
+    say("assign long codebook", mode)
+    M, N, d, K = 640, 256, 8, 2600          # 2.5 row groups of 256, ragged codebook chunk
+    W, h, C, keep, rho = _case(41, M, N, d, K, masked=(mode != "no-mask"), with_rho=True)
+    if mode == "zero-mask":
+        keep = np.ones_like(keep)
+    ref_idx, ref_dist = oracle.assign(W, h, rho, keep, d, C)
+    ws = vq.workspace(M, N, d, K)
+    mask = None if keep is None else dev(mask_from_keep(keep, d))
+    idx, dist = vq.assign(dev(W), dev(h), dev(rho), mask, d, dev(C), ws, want_dist=True)
+    assert bits_equal(host(idx), ref_idx), np.flatnonzero(host(idx) != ref_idx)[:10]
+    assert bits_equal(host(dist), ref_dist.astype(np.float32))
+
+
+def test_assign_far_outlier_goes_to_exact_search():
+    # a sub-vector ~1e15 times larger than every centroid: its scaled weights
+    # cannot share the codebook's scale, so the search leaves it to the exact path
+    say("assign far outlier")
+    M, N, d, K = 256, 128, 8, 2100
+    W, h, C, keep, rho = _case(43, M, N, d, K, masked=False, with_rho=False)
+    W = W.copy()
+    W[5, 8:16] = np.float32(3e13) * np.arange(1, 9, dtype=np.float32)
+    W[77, 0:8] = -np.float32(1e14)
+    ref_idx, ref_dist = oracle.assign(W, h, None, None, d, C)
+    ws = vq.workspace(M, N, d, K)
+    idx, dist = vq.assign(dev(W), dev(h), None, None, d, dev(C), ws, want_dist=True)
+    assert bits_equal(host(idx), ref_idx), np.flatnonzero(host(idx) != ref_idx)[:10]
+    assert bits_equal(host(dist), ref_dist.astype(np.float32))
+    assert vq.assign_exact_count(ws, M * N // d, K) >= 2
+
+
 def test_assign_exact_ties_go_to_lowest_index():
     say("assign ties")
     g = np.random.default_rng(5)
