@@ -66,6 +66,91 @@ def traffic_from_profile(kernel_src):
     return prof.get("hbm_bytes_per_launch")
 
 
+def row_table(cfg, recs, nnz, oracle_ms):
+    """Per-row GPU time per call (HIP events during the timed steps) against the row's
+    roofline, with the oracle's CPU time for the same operation at the same size."""
+    M, N, d, n_sub = cfg.M, cfg.N, cfg.d, cfg.n_sub
+    rec = {(r[0], r[1]): r for r in recs}
+
+    def ms(name, K):
+        r = rec.get((name, K))
+        return r[3] / r[2] if r else None
+
+    def hbm(name, K, nbytes, key):
+        t = ms(name, K)
+        if t is None:
+            return None
+        out = {"gpu_ms": round(t, 4), "algorithmic_MB": round(nbytes / 1e6, 1),
+               "GBs": round(nbytes / (t * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        if key in oracle_ms:
+            out["oracle_ms"] = round(oracle_ms[key], 1)
+        return out
+
+    rows = {
+        "A1_select": hbm("select", 0, 4 * M * N + 4 * N + 8 * nnz + 4 * (M + 1) + n_sub, "select"),
+        "A2_binorm": hbm("binorm", 0, 8 * M * N + 8 * (M + N), "binorm") if cfg.binorm else None,
+        "A5_update_stage1": hbm("update", cfg.K1, algorithmic_bytes_update(n_sub, M, N, d, cfg.K1), "update"),
+        "A5_objective": hbm("objective", cfg.K1, n_sub * (4 * d + 3) + 4 * (M + N), "objective"),
+        "A6_residual": hbm("residual", cfg.K1, n_sub * (8 * d + 2) + 4 * cfg.K1 * d, "residual"),
+        "A7_reconstruct": hbm("reconstruct", cfg.K1, algorithmic_bytes_reconstruct(n_sub, M, N, d, cfg.K1, cfg.K2, nnz,
+                                                                              cfg.binorm), "reconstruct"),
+    }
+    t = ms("init", cfg.K1)
+    if t is not None:
+        rows["A3_init"] = {"gpu_ms": round(t, 4), "note": "device gather + host walk over a hash set"}
+        if "init" in oracle_ms:
+            rows["A3_init"]["oracle_ms"] = round(oracle_ms["init"], 1)
+    t = ms("assign_search", cfg.K1)
+    if t is not None:
+        fl = 32.0 * n_sub * cfg.K1
+        rows["A4_assign_stage1"] = {"gpu_ms": round(t, 4), "algorithmic_TFLOP": round(fl / 1e12, 2),
+                                    "TFLOPs": round(fl / (t * 1e-3) / 1e12, 1),
+                                    "frac_fp16_mfma": round(fl / (t * 1e-3) / 1e12 / PEAK_FP16_MFMA_TFLOPS, 4)}
+        if "assign" in oracle_ms:
+            rows["A4_assign_stage1"]["oracle_ms"] = round(oracle_ms["assign"], 1)
+    return {k: v for k, v in rows.items() if v is not None}
+
+
+def cpu_rows(cfg, inp, nnz):
+    """The oracle on each row at the workload's full size (one call each), on inputs the
+    oracle makes itself or seeded synthetic indices; returns milliseconds per row."""
+    import numpy as np
+
+    import oracle
+    out = {}
+
+    def timed(key, f):
+        t0 = time.perf_counter()
+        r = f()
+        out[key] = (time.perf_counter() - t0) * 1e3
+        return r
+
+    W, h = inp["W"], inp["h"]
+    _, _, _, keep = timed("select", lambda: oracle.select(W, h, nnz))
+    if cfg.binorm:
+        Wp, r, c, hcol, rho = timed("binorm", lambda: oracle.binorm(W, h))
+    else:
+        Wp, r, c, hcol, rho = W, None, None, h, None
+    C1, _ = timed("init", lambda: oracle.init(Wp, cfg.d, inp["perm1"], cfg.K1))
+    g = np.random.default_rng([cfg.cid, 91])
+    i1 = g.integers(0, cfg.K1, size=cfg.n_sub).astype(np.uint16)
+    timed("update", lambda: oracle.update(Wp, hcol, rho, keep, cfg.d, i1, C1))
+    timed("objective", lambda: oracle.objective(Wp, hcol, rho, keep, cfg.d, C1, i1))
+    R = timed("residual", lambda: oracle.residual(Wp, cfg.d, C1, i1))
+    if cfg.K2:
+        C2, _ = oracle.init(R, cfg.d, inp["perm2"], cfg.K2)
+        i2 = g.integers(0, cfg.K2, size=cfg.n_sub).astype(np.uint16)
+    else:
+        C2, i2 = None, None
+    M, N = W.shape
+    per = g.integers(0, 2 * max(1, nnz // M), size=M)
+    rp = np.concatenate([[0], np.cumsum(per)]).astype(np.int32)
+    col = np.concatenate([np.sort(g.choice(N, min(k, N), replace=False)) for k in per]).astype(np.int32)
+    val = np.ones(col.size, np.float32)
+    timed("reconstruct", lambda: oracle.reconstruct(M, N, cfg.d, C1, i1, C2, i2, r, c, rp, col, val))
+    return out
+
+
 def cpu_baseline(cfg, inp, seconds):
     """The oracle's assignment on a bounded sample (float64 exhaustive search)."""
     import numpy as np
@@ -195,8 +280,12 @@ def main():
                   % (r[0], r[1], r[2], r[3], r[3] / r[2], r[4], r[5]), file=sys.stderr)
 
     cpu = None
+    oracle_ms = {}
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, inp, args.cpu_seconds)
+        oracle_ms = cpu_rows(cfg, inp, nnz)
+        oracle_ms["assign"] = n_sub / (cpu["value"] * 1e9) * 1e3   # full pass at the sampled rate
+    extra["rows"] = row_table(cfg, recs, nnz, oracle_ms)
 
     line = {
         "metric": "sub-vectors assigned/s per Lloyd iter (G/s) + % FP32 peak; update/recon HBM GB/s",
