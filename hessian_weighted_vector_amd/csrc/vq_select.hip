@@ -70,23 +70,47 @@ __global__ __launch_bounds__(256) void k_sel_hist(const float* __restrict__ W,
 }
 
 // Picks the digit holding the remaining-th largest element; clears hist.
-__global__ void k_sel_pick(SelState* st, int* hist, int shift, int nbins)
+// 256 threads, kBins / 256 consecutive bins each: a suffix sum of the
+// per-thread totals (from the highest digit down) locates the one thread
+// whose bins hold the crossing, which walks them from the top.
+__global__ __launch_bounds__(256) void k_sel_pick(SelState* st, int* hist, int shift, int nbins)
 {
-    if (threadIdx.x == 0) {
-        int64_t cum = 0;
-        const int64_t rem = st->remaining;
-        for (int b = nbins - 1; b >= 0; --b) {
-            const int64_t c = hist[b];
-            if (cum + c >= rem) {
-                st->prefix |= ((uint32_t)b) << shift;
+    constexpr int kPer = kBins / 256;
+    __shared__ int64_t suf[257];
+    const int t = threadIdx.x;
+    const int64_t rem = st->remaining;   // read before any thread can update it (barriers follow)
+    int64_t c[kPer];
+    int64_t tot = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int b = t * kPer + u;
+        c[u] = b < nbins ? (int64_t)hist[b] : 0;
+        tot += c[u];
+    }
+    suf[t] = tot;
+    if (t == 0) suf[256] = 0;
+    __syncthreads();
+    // inclusive suffix sums over threads: suf[t] = sum of totals of threads >= t
+    for (int off = 1; off < 256; off <<= 1) {
+        const int64_t add = (t + off < 256) ? suf[t + off] : 0;
+        __syncthreads();
+        suf[t] += add;
+        __syncthreads();
+    }
+    const int64_t above = suf[t + 1];    // suf[256] = 0
+    if (above < rem && rem <= suf[t]) {
+        int64_t cum = above;
+        for (int u = kPer - 1; u >= 0; --u) {
+            if (cum + c[u] >= rem) {
+                st->prefix |= ((uint32_t)(t * kPer + u)) << shift;
                 st->remaining = rem - cum;
                 break;
             }
-            cum += c;
+            cum += c[u];
         }
     }
     __syncthreads();
-    for (int q = threadIdx.x; q < kBins; q += blockDim.x) hist[q] = 0;
+    for (int q = t; q < kBins; q += 256) hist[q] = 0;
 }
 
 // Per row: number of scores > tau and == tau.
@@ -166,17 +190,22 @@ __global__ __launch_bounds__(kScanThreads) void k_sel_rows(const SelState* __res
 // Inclusive scan of one int per thread over a 256-thread block.
 __device__ inline int scan256(int v, int* sh)
 {
-    sh[threadIdx.x] = v;
-    __syncthreads();
-    for (int off = 1; off < kRowThreads; off <<= 1) {
-        const int add = (int)threadIdx.x >= off ? sh[threadIdx.x - off] : 0;
-        __syncthreads();
-        sh[threadIdx.x] += add;
-        __syncthreads();
+    // inclusive scan within each wavefront by shuffles, then the totals of
+    // the earlier wavefronts (4 per block) from LDS
+    static_assert(kRowThreads == 256, "four wavefronts");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
     }
-    const int r = sh[threadIdx.x];
+    if (lane == 63) sh[wave] = x;
     __syncthreads();
-    return r;
+    int add = 0;
+    for (int w = 0; w < wave; ++w) add += sh[w];
+    __syncthreads();   // sh is reused by the next call
+    return x + add;
 }
 
 // Per row: walk sub-vectors in column order, write CSR entries and masks.
