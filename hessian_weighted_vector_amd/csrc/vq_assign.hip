@@ -209,6 +209,42 @@ __device__ __forceinline__ void tile_track(const f32x16& a, int kt, float& b1, f
     kt1 = lt ? kt : kt1;
 }
 
+// x and its weights omega (hcol, zero where masked) of sub-vector s; zeros
+// for an invalid lane and for dimensions >= d.  16-byte loads when d == 8
+// and the buffers allow; n_sub < 2^31, so 32-bit index arithmetic.
+__device__ __forceinline__ void load_sub(const float* __restrict__ X, const float* __restrict__ hcol,
+                                         const uint8_t* __restrict__ mask, int64_t s, int64_t nb, int d, bool valid,
+                                         bool vec, float (&x)[8], float (&w)[8])
+{
+#pragma unroll
+    for (int t = 0; t < 8; ++t) { x[t] = 0.f; w[t] = 0.f; }
+    if (!valid) return;
+    const uint32_t su = (uint32_t)s;
+    const uint32_t b = su % (uint32_t)nb;
+    const unsigned mb = mask ? mask[s] : 0u;
+    if (vec) {
+        const float4 x0 = reinterpret_cast<const float4*>(X)[(size_t)su * 2];
+        const float4 x1 = reinterpret_cast<const float4*>(X)[(size_t)su * 2 + 1];
+        const float4 h0 = reinterpret_cast<const float4*>(hcol)[(size_t)b * 2];
+        const float4 h1 = reinterpret_cast<const float4*>(hcol)[(size_t)b * 2 + 1];
+        x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+        x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+        w[0] = h0.x; w[1] = h0.y; w[2] = h0.z; w[3] = h0.w;
+        w[4] = h1.x; w[5] = h1.y; w[6] = h1.z; w[7] = h1.w;
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if (t < d) {
+                x[t] = X[(size_t)su * d + t];
+                w[t] = hcol[(size_t)b * d + t];
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        if ((mb >> t) & 1u) w[t] = 0.f;
+}
+
 // Per-slot tracking (short codebooks, where a few branchy updates cost less
 // than forming a tile again at the end): exact (best, second best, position
 // = kt*16 + slot) over the 16 values of tile kt, in slot order (slot order is
@@ -368,24 +404,16 @@ __device__ __forceinline__ void search_epilogue(
     // second best.
     float v1 = __builtin_inff(), v2 = __builtin_inff();
     int kb = K;
+    const bool vecX = d == 8 && ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(hcol)) & 15u) == 0;
     if (SLOT) {
         const int jb = kt1 & 15;
         kb = (kt1 >> 4) * kTile + (jb >> 2) * 8 + half * 4 + (jb & 3);
         v1 = b1;
     } else {
-        float bw[8], om[8];
-        const int64_t b = valid ? s % nb : 0;
-        const unsigned mb = (valid && mask) ? mask[s] : 0u;
+        float bw[8], om[8], xs[8];
+        load_sub(X, hcol, mask, s, nb, d, valid, vecX, xs, om);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            float xv = 0.f, w = 0.f;
-            if (valid && t < d) {
-                xv = X[s * d + t];
-                w = ((mb >> t) & 1u) ? 0.f : hcol[b * d + t];
-            }
-            om[t] = w;
-            bw[t] = w * xv;
-        }
+        for (int t = 0; t < 8; ++t) bw[t] = om[t] * xs[t];
         const bool vecC = d == 8 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
 #pragma unroll 2
         for (int j = 0; j < 16; ++j) {
@@ -498,21 +526,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
     const int64_t s = valid ? (list ? (int64_t)list[q] : q) : 0;
 
     // ---- the sub-vector's weights, scaled split B operand, S -----------
+    const bool vecX = d == 8 && ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(hcol)) & 15u) == 0;
     h16x8 bh, bl;
     float S_sc;
     int shift_s;   // S_sc = S * 2^shift_s: the sub-vector's scale alpha*beta
     {
         float raw[8];
         float S = 0.f;
-        const int64_t b = valid ? s % nb : 0;
-        const unsigned mb = (valid && mask) ? mask[s] : 0u;
+        float xs[8], ws_[8];
+        load_sub(X, hcol, mask, s, nb, d, valid, vecX, xs, ws_);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            float xv = 0.f, w = 0.f;
-            if (valid && t < d) {
-                xv = X[s * d + t];
-                w = ((mb >> t) & 1u) ? 0.f : hcol[b * d + t];
-            }
+            const float xv = xs[t], w = ws_[t];
             S += w * xv * xv;
             // lower half: omega*x (scale alpha*beta); upper half: omega
             // (scale alpha*beta2*(beta/beta2))
@@ -659,9 +684,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
     {
         float raw[8];
         float S = 0.f, mx = 0.f;
+        float xs[8];
+        if (valid && d == 8 && (reinterpret_cast<uintptr_t>(X) & 15u) == 0) {
+            const float4 x0 = reinterpret_cast<const float4*>(X)[(size_t)s * 2];
+            const float4 x1 = reinterpret_cast<const float4*>(X)[(size_t)s * 2 + 1];
+            xs[0] = x0.x; xs[1] = x0.y; xs[2] = x0.z; xs[3] = x0.w;
+            xs[4] = x1.x; xs[5] = x1.y; xs[6] = x1.z; xs[7] = x1.w;
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) xs[t] = (valid && t < d) ? X[s * d + t] : 0.f;
+        }
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const float xv = (valid && t < d) ? X[s * d + t] : 0.f;
+            const float xv = xs[t];
             S += om[t] * xv * xv;
             raw[t] = om[t] * xv;
             mx = fmaxf(mx, fabsf(raw[t]));
