@@ -386,13 +386,15 @@ __device__ __forceinline__ f32x16 tile2_h16(const h16x8 a0, const h16x8 a1, cons
 // wavefront column), shared by both search kernels.  b1, b2 and pos come from
 // the tracking; S_sc and shift_s are the sub-vector's scaled energy and
 // scale; a writer lane that is not certified (or is marked bad) is appended
-// to the exact re-search list.
+// to the exact re-search list.  A sub-vector whose weights are all zero has
+// D = 0 for every centroid: index 0 (allzero, or found from its weights).
 template <bool SLOT>
 __device__ __forceinline__ void search_epilogue(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
     const uint8_t* __restrict__ mask, int64_t nb, int d, const float* __restrict__ C, int K, int64_t s,
-    bool valid, bool writer_ok, bool bad, int lane, int half, float b1, float b2, int kt1, float S_sc, int shift_s,
-    uint16_t* __restrict__ idx, float* __restrict__ dist, int* __restrict__ flag_count, int* __restrict__ flag_list)
+    bool valid, bool writer_ok, bool bad, bool allzero, int lane, int half, float b1, float b2, int kt1, float S_sc,
+    int shift_s, uint16_t* __restrict__ idx, float* __restrict__ dist, int* __restrict__ flag_count,
+    int* __restrict__ flag_list)
 {
     // ---- epilogue: best and second best of this sub-vector -------------
     // Slot j of this lane holds centroid row (j/4)*8 + half*4 + j%4 of a tile,
@@ -405,6 +407,14 @@ __device__ __forceinline__ void search_epilogue(
     float v1 = __builtin_inff(), v2 = __builtin_inff();
     int kb = K;
     const bool vecX = d == 8 && ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(hcol)) & 15u) == 0;
+    {
+        float xz[8], wz[8];
+        load_sub(X, hcol, mask, s, nb, d, valid, vecX, xz, wz);
+        bool z = true;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) z = z && wz[t] == 0.f;
+        allzero = allzero || z;
+    }
     if (SLOT) {
         const int jb = kt1 & 15;
         kb = (kt1 >> 4) * kTile + (jb >> 2) * 8 + half * 4 + (jb & 3);
@@ -460,7 +470,9 @@ __device__ __forceinline__ void search_epilogue(
     const float u = 5.9604644775390625e-8f;   // 2^-24
     const float eb = 48.f * u * (9.f * S_sc + 4.f * fmaxf(gb, -S_sc)) + 1.f;
     const float es = 48.f * u * (9.f * S_sc + 4.f * fmaxf(gs, -S_sc)) + 1.f;
-    const bool certified = (gs - gb) > (eb + es) && gk < K && !bad;
+    // all weights zero: every D is exactly 0 and the lowest index wins
+    if (allzero) gk = 0;
+    const bool certified = allzero || ((gs - gb) > (eb + es) && gk < K && !bad);
 
     const bool writer = writer_ok && half == 0;
     if (writer && certified) {
@@ -614,8 +626,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
     if (!active) return;
     track<SLOT>(accB, ktB, b1, b2, kt1);
 
-    search_epilogue<SLOT>(X, hcol, rho, mask, nb, d, C, K, s, valid, valid, false, lane, half, b1, b2, kt1, S_sc,
-                          shift_s, idx, dist, flag_count, flag_list);
+    search_epilogue<SLOT>(X, hcol, rho, mask, nb, d, C, K, s, valid, valid, false, false, lane, half, b1, b2,
+                          kt1, S_sc, shift_s, idx, dist, flag_count, flag_list);
 }
 
 // Sub-vectors that share one weight vector: workgroup = column block b x 256
@@ -811,8 +823,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
     }
     if (!active) return;
     track<SLOT>(accB, ktB, b1, b2, kt1);
-    search_epilogue<SLOT>(X, hcol, rho, mask, nb, d, C, K, s, valid, owner, bad, lane, half, b1, b2, kt1, S_sc,
-                          shift_s, idx, dist, flag_count, flag_list);
+    search_epilogue<SLOT>(X, hcol, rho, mask, nb, d, C, K, s, valid, owner, bad, wsum == 0.f, lane, half, b1, b2,
+                          kt1, S_sc, shift_s, idx, dist, flag_count, flag_list);
 }
 
 // Exact re-search of the flagged sub-vectors: one wavefront per flagged
@@ -840,7 +852,7 @@ __global__ __launch_bounds__(256) void k_assign_exact(
         const int64_t i = s / nb, b = s - i * nb;
         const unsigned mb = mask ? mask[s] : 0u;
         const double rr = rho ? (double)rho[i] : 1.0;
-        float x[8], om[8], bw[8];
+        float x[8], om[8], bw2[8];
         double w64[8];
         float S = 0.f;
 #pragma unroll
@@ -848,12 +860,15 @@ __global__ __launch_bounds__(256) void k_assign_exact(
             const bool on = t < d;
             x[t] = on ? X[s * d + t] : 0.f;
             om[t] = (on && !((mb >> t) & 1u)) ? hcol[b * d + t] : 0.f;
-            bw[t] = om[t] * x[t];
+            bw2[t] = -2.f * (om[t] * x[t]);   // exact: fma(-2 bw, c, e) == fma(bw, -2 c, e)
             S += om[t] * x[t] * x[t];
             double w = (double)om[t];
             if (rho) w = w * rr;
             w64[t] = w;
         }
+        // filter bound err(e) = 32u (9 S + 4 max(e, -S)) + 1e-35 = A + B max(e, -S)
+        const float A = 32.f * u * 9.f * S + 1.0e-35f;
+        const float B = 128.f * u;
         float thr = __builtin_inff();
         double dbest = __builtin_inf();
         int arg = K;
@@ -870,12 +885,12 @@ __global__ __launch_bounds__(256) void k_assign_exact(
             }
             float e = 0.f;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) e = fmaf(bw[t], -2.f * c[t], e);
+            for (int t = 0; t < 8; ++t) e = fmaf(bw2[t], c[t], e);
 #pragma unroll
             for (int t = 0; t < 8; ++t) e = fmaf(om[t], c[t] * c[t], e);
-            const float err = 32.f * u * (9.f * S + 4.f * fmaxf(e, -S)) + 1.0e-35f;
-            if (e - err <= thr) {
-                thr = fminf(thr, e + err);
+            const float mm = fmaxf(e, -S);
+            if (fmaf(-B, mm, e) - A <= thr) {
+                thr = fminf(thr, e + fmaf(B, mm, A));
                 double acc = 0.0;
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {

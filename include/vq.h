@@ -101,10 +101,11 @@ vq_status vq_init(const float* X, int64_t M, int64_t N, int d, const int32_t* pe
 
 /* Assignment (VPTQ page, "The Core Algorithm": nearest centroid; here under
  * the weighted distance D).  idx[s] = argmin_k D(s,k), ties to the lowest k.
- * The result equals the exact (float64, direct form) argmin: a float32
- * expanded-form search runs on the matrix cores, each winner is certified
- * against a rigorous rounding bound, and uncertified sub-vectors are
- * re-searched exactly.  X = the matrix being quantized ([M x N] f32),
+ * The result equals the exact (float64, direct form) argmin: the expanded
+ * form runs on the fp16 matrix cores with every fp32 operand split into two
+ * fp16 parts (fp32 accumulation), each winner is certified against a
+ * rigorous rounding bound, and uncertified sub-vectors are re-searched
+ * exactly in float64.  X = the matrix being quantized ([M x N] f32),
  * hcol [N], rho [M] (nullable), mask (nullable), C [K x d].  Outputs
  * idx uint16[n_sub] and, if dist != NULL, dist float32[n_sub] = D(s, idx[s])
  * computed in float64 and rounded. */
