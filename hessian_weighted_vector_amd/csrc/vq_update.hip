@@ -57,39 +57,40 @@ __global__ __launch_bounds__(256) void k_bucket_hist(const uint16_t* __restrict_
     for (int q = threadIdx.x; q < nbk; q += 256) hist[(int64_t)q * ntile + blockIdx.x] = cnt[q];
 }
 
-// Inclusive scan of one int per thread over a 256-thread block.
-__device__ inline int block_incl_scan_256(int v, int* sh)
-{
-    sh[threadIdx.x] = v;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        int add = (int)threadIdx.x >= off ? sh[threadIdx.x - off] : 0;
-        __syncthreads();
-        sh[threadIdx.x] += add;
-        __syncthreads();
-    }
-    int r = sh[threadIdx.x];
-    __syncthreads();
-    return r;
-}
-
 // One block per bucket: exclusive scan of its per-tile counts, in place;
-// total[bucket] = the bucket's size.
-__global__ __launch_bounds__(256) void k_bucket_scan(int* __restrict__ hist, int ntile, int* __restrict__ total)
+// total[bucket] = the bucket's size.  1024 threads: a wavefront-shuffle
+// scan, the 16 wavefront totals from LDS, a running carry per 1024 tiles.
+__global__ __launch_bounds__(1024) void k_bucket_scan(int* __restrict__ hist, int ntile, int* __restrict__ total)
 {
-    __shared__ int sh[256];
+    __shared__ int wsum[16];
+    __shared__ int carry_sh;
     int* row = hist + (int64_t)blockIdx.x * ntile;
-    int carry = 0;
-    for (int c0 = 0; c0 < ntile; c0 += 256) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (threadIdx.x == 0) carry_sh = 0;
+    __syncthreads();
+    for (int c0 = 0; c0 < ntile; c0 += 1024) {
         const int q = c0 + threadIdx.x;
         const int v = q < ntile ? row[q] : 0;
-        const int inc = block_incl_scan_256(v, sh);
-        const int chunk_total = sh[255];
-        if (q < ntile) row[q] = carry + inc - v;
-        carry += chunk_total;
+        int x = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        int before = carry_sh;
+        for (int w = 0; w < wave; ++w) before += wsum[w];
+        if (q < ntile) row[q] = before + x - v;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int t = 0;
+            for (int w = 0; w < 16; ++w) t += wsum[w];
+            carry_sh += t;
+        }
         __syncthreads();
     }
-    if (threadIdx.x == 0) total[blockIdx.x] = carry;
+    if (threadIdx.x == 0) total[blockIdx.x] = carry_sh;
 }
 
 // Bucket starts and piece numbering (one wavefront, nbk <= 512): bucket b
@@ -588,7 +589,7 @@ vq_status update_launch(const float* X, const float* hcol, const float* rho, con
         const int ntile = (int)((n_sub + kTile - 1) / kTile);
         hipLaunchKernelGGL(k_bucket_hist, dim3(ntile), dim3(256), 0, st, idx, n_sub, nbk, w.hist, ntile);
         VQ_LAUNCHED("k_bucket_hist");
-        hipLaunchKernelGGL(k_bucket_scan, dim3(nbk), dim3(256), 0, st, w.hist, ntile, w.total);
+        hipLaunchKernelGGL(k_bucket_scan, dim3(nbk), dim3(1024), 0, st, w.hist, ntile, w.total);
         VQ_LAUNCHED("k_bucket_scan");
         hipLaunchKernelGGL(k_piece_setup, dim3(1), dim3(64), 0, st, w.total, nbk, n_sub, piece, w.bstart, w.poff);
         VQ_LAUNCHED("k_piece_setup");
