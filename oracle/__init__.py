@@ -6,9 +6,9 @@ benchmark's CPU-baseline leg may import this package.  It shares no code with
 the HIP library and never imports it.
 """
 from .oracle import (build, load, nnz, select, binorm, init, assign, objective, update,
-                     residual, reconstruct, fit)
+                     residual, reconstruct, qgemv, fit)
 from .bits import bits_per_weight, compression_ratio_single
 
 __all__ = ["build", "load", "nnz", "select", "binorm", "init", "assign", "objective",
-           "update", "residual", "reconstruct", "fit", "bits_per_weight",
+           "update", "residual", "reconstruct", "qgemv", "fit", "bits_per_weight",
            "compression_ratio_single"]

@@ -46,6 +46,7 @@ _SIGS = {
     "orc_update": (_D, [_P, _P, _P, _P, _LL, _LL, _I, _P, _I, _P, _P]),
     "orc_residual": (None, [_P, _LL, _I, _P, _P, _P]),
     "orc_reconstruct": (None, [_LL, _LL, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "orc_qgemv": (_I, [_LL, _LL, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _LL, _P]),
     "orc_fit": (_I, [_P, _P, _LL, _LL, _I, _I, _I, _I, _I, _D, _I, _I, _P, _P, _I,
                      _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
 }
@@ -185,6 +186,23 @@ def reconstruct(M, N, d, C1, idx1, C2=None, idx2=None, r=None, c=None,
                         _ptr(_c(row_ptr, np.int32)), _ptr(_c(col, np.int32)),
                         _ptr(_c(val, np.float32)), _ptr(What))
     return What
+
+
+def qgemv(M, N, d, C1, idx1, X, C2=None, idx2=None, r=None, c=None,
+          row_ptr=None, col=None, val=None, lib=None):
+    """Y = X What^T in float64 (What as reconstruct writes it); X is [B x N]."""
+    lib = lib or load()
+    X = _c(np.atleast_2d(X), np.float32)
+    B = X.shape[0]
+    Y = np.empty((B, M), np.float64)
+    rc = lib.orc_qgemv(M, N, d, _ptr(_c(C1, np.float32)), _ptr(_c(idx1, np.uint16)),
+                       _ptr(_c(C2, np.float32)), _ptr(_c(idx2, np.uint16)),
+                       _ptr(_c(r, np.float32)), _ptr(_c(c, np.float32)),
+                       _ptr(_c(row_ptr, np.int32)), _ptr(_c(col, np.int32)),
+                       _ptr(_c(val, np.float32)), _ptr(X), B, _ptr(Y))
+    if rc:
+        raise MemoryError("orc_qgemv: allocation failed")
+    return Y
 
 
 def fit(W, h, d, K1, T1, K2, T2, p, binorm=False, mask_outliers=True, perm1=None, perm2=None,

@@ -344,6 +344,36 @@ void orc_reconstruct(long long M, long long N, int d,
 }
 
 /* ------------------------------------------------------------------ */
+/* The product of the compressed matrix with B activation vectors (VPTQ page,
+ * "End-to-End Quantization Pipeline": at inference the weights are decoded by
+ * codebook lookup inside the matrix-vector product; SCVQ summary: the sparse
+ * correction takes part in that product).  By definition
+ *   Y[b, i] = sum_j What[i, j] * X[b, j]
+ * with What exactly as orc_reconstruct writes it (float32), the products and
+ * the sum taken in float64, j ascending.  X is [B x N], Y is [B x M]. */
+int orc_qgemv(long long M, long long N, int d,
+              const float* C1, const unsigned short* idx1,
+              const float* C2, const unsigned short* idx2,
+              const float* r, const float* c,
+              const int* row_ptr, const int* col, const float* val,
+              const float* X, long long B, double* Y)
+{
+    float* What = (float*)malloc((size_t)M * (size_t)N * sizeof(float));
+    if (!What) return 1;
+    orc_reconstruct(M, N, d, C1, idx1, C2, idx2, r, c, row_ptr, col, val, What);
+    for (long long b = 0; b < B; ++b) {
+        const float* x = X + b * N;
+        for (long long i = 0; i < M; ++i) {
+            double acc = 0.0;
+            for (long long j = 0; j < N; ++j) acc += (double)What[i * N + j] * (double)x[j];
+            Y[b * M + i] = acc;
+        }
+    }
+    free(What);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* One stage of weighted K-means (Lloyd): T times (assign, update), then a
  * final assign, so the returned indices are the argmin for the returned
  * codebook.  J[0..T] receives the objective of each (codebook, assignment)

@@ -387,4 +387,94 @@ def pin_bits_worked_example(lib):
     assert abs(bpw - ex["original_bits"] / cr) < 1e-12
 
 
+def _qg_case(seed, M=6, N=24, d=4, K1=7, K2=3, B=3, pow2_scales=False):
+    g = np.random.default_rng([11, seed])
+    nb = N // d
+    C1 = g.standard_normal((K1, d)).astype(np.float32)
+    C2 = (0.1 * g.standard_normal((K2, d))).astype(np.float32)
+    idx1 = g.integers(0, K1, M * nb).astype(np.uint16)
+    idx2 = g.integers(0, K2, M * nb).astype(np.uint16)
+    if pow2_scales:
+        r = np.ldexp(1.0, g.integers(-3, 4, M)).astype(np.float32)
+        c = np.ldexp(1.0, g.integers(-3, 4, N)).astype(np.float32)
+    else:
+        r = g.uniform(0.5, 2.0, M).astype(np.float32)
+        c = g.uniform(0.5, 2.0, N).astype(np.float32)
+    # two salient positions in row 1, none in row 0, one in the last row
+    rows = {1: [3, N - 1], M - 1: [0]}
+    row_ptr = np.zeros(M + 1, np.int32)
+    col, val = [], []
+    for i in range(M):
+        for j in rows.get(i, []):
+            col.append(j)
+            val.append(g.standard_normal() * 5.0)
+        row_ptr[i + 1] = len(col)
+    X = g.standard_normal((B, N)).astype(np.float32)
+    return dict(M=M, N=N, d=d, C1=C1, idx1=idx1, C2=C2, idx2=idx2, r=r, c=c, row_ptr=row_ptr,
+                col=np.array(col, np.int32), val=np.array(val, np.float32)), X
+
+
+def pin_qgemv_unit_tokens(lib):
+    """Multiplying by the unit vectors e_j reads back column j of the
+    reconstruction, for every token row: pins rows, columns and the token
+    stride of the product to the (separately pinned) reconstruction."""
+    cs, _ = _qg_case(1)
+    N = cs["N"]
+    What = O.reconstruct(lib=lib, **cs)
+    Y = O.qgemv(X=np.eye(N, dtype=np.float32), lib=lib, **cs)
+    assert Y.shape == (N, cs["M"])
+    assert np.array_equal(Y, What.T.astype(np.float64))
+
+
+def pin_qgemv_matches_numpy_matmul(lib):
+    """Special case of a library routine: numpy's float64 matrix product of the
+    reconstruction with the activations."""
+    cs, X = _qg_case(2, M=9, N=40, d=8, B=4)
+    What = O.reconstruct(lib=lib, **cs).astype(np.float64)
+    ref = X.astype(np.float64) @ What.T
+    Y = O.qgemv(X=X, lib=lib, **cs)
+    assert np.allclose(Y, ref, rtol=1e-13, atol=1e-13)
+
+
+def pin_qgemv_power_of_two_scales(lib):
+    """With power-of-two row and column scales, What(r, c) = r_i * What(1, 1) * c_j
+    exactly, so Y(r, c; X) = r * Y(1, 1; X * c) bit for bit (rows scale outputs,
+    columns scale inputs)."""
+    cs, X = _qg_case(3, pow2_scales=True)
+    cs["row_ptr"] = cs["col"] = cs["val"] = None
+    r, c = cs.pop("r"), cs.pop("c")
+    Y = O.qgemv(X=X, r=r, c=c, lib=lib, **cs)
+    Y1 = O.qgemv(X=X * c[None, :], lib=lib, **cs)
+    assert np.array_equal(Y, Y1 * r[None, :].astype(np.float64))
+
+
+def pin_qgemv_float64_accumulation(lib):
+    """A row [2^30, 1, -2^30, 0, ...] against ones gives exactly 1; a float32
+    running sum would return 0."""
+    d, N = 4, 8
+    C1 = np.array([[2.0 ** 30, 1.0, -(2.0 ** 30), 0.0], [0.0, 0.0, 0.0, 0.0]], np.float32)
+    idx1 = np.array([0, 1], np.uint16)
+    Y = O.qgemv(1, N, d, C1, idx1, np.ones((1, N), np.float32), lib=lib)
+    assert Y[0, 0] == 1.0
+
+
+def pin_qgemv_sparse_term(lib):
+    """The salient positions replace the decoded weight: adding the CSR changes
+    y_i by sum_k (val_k - What_dense[i, col_k]) * x[col_k], and rows without
+    salient positions do not change at all."""
+    cs, X = _qg_case(4)
+    Y = O.qgemv(X=X, lib=lib, **cs)
+    dense = dict(cs, row_ptr=None, col=None, val=None)
+    Y0 = O.qgemv(X=X, lib=lib, **dense)
+    Wd = O.reconstruct(lib=lib, **dense).astype(np.float64)
+    rp, col, val = cs["row_ptr"], cs["col"], cs["val"]
+    for i in range(cs["M"]):
+        e = list(range(rp[i], rp[i + 1]))
+        if not e:
+            assert np.array_equal(Y[:, i], Y0[:, i])
+            continue
+        delta = sum((float(val[k]) - Wd[i, col[k]]) * X[:, col[k]].astype(np.float64) for k in e)
+        assert np.allclose(Y[:, i] - Y0[:, i], delta, rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -54,6 +54,11 @@ MUTANTS = {
     "reconstruct_wrong_col_scale": [("if (c) v = v * c[j];", "if (c) v = v * c[(j + 1) % N];")],
     "reconstruct_drops_row_scale": [("if (r) v = v * r[i];", "if (0) v = v * r[i];")],
     "reconstruct_no_overwrite": [("if (row_ptr)\n            for", "if (0)\n            for")],
+    "qgemv_wrong_row": [("acc += (double)What[i * N + j] * (double)x[j];",
+                         "acc += (double)What[((i + 1) % M) * N + j] * (double)x[j];")],
+    "qgemv_float_accumulation": [("            double acc = 0.0;\n            for (long long j = 0; j < N; ++j) acc +=",
+                                  "            float acc = 0.0f;\n            for (long long j = 0; j < N; ++j) acc +=")],
+    "qgemv_token_stride": [("const float* x = X + b * N;", "const float* x = X;")],
     "lloyd_no_final_assign": [
         ("    orc_assign(X, hcol, rho, keep, M, N, d, C, K, NULL, 0, idx, NULL, nthreads);\n    J[T] =",
          "    J[T] =")],
