@@ -151,6 +151,99 @@ def cpu_rows(cfg, inp, nnz):
     return out
 
 
+def qgemv_inputs(cfg, inp):
+    """Seeded compressed form of the workload's matrix for the fused product: the
+    full codebook sizes, uniform indices, codebook rows drawn from the matrix,
+    row/column scales when the workload bi-normalizes, and a CSR with about the
+    workload's salient fraction per row holding the matrix's exact values."""
+    import numpy as np
+    g = np.random.default_rng([cfg.cid, 93])
+    M, N, d, n_sub = cfg.M, cfg.N, cfg.d, cfg.n_sub
+    flat = inp["W"].reshape(-1, d)
+    C1 = flat[np.sort(g.choice(n_sub, cfg.K1, replace=False))].copy()
+    K2 = cfg.K2
+    C2 = (0.1 * flat[np.sort(g.choice(n_sub, K2, replace=False))]).astype(np.float32) if K2 else None
+    i1 = g.integers(0, cfg.K1, n_sub).astype(np.uint16)
+    i2 = g.integers(0, K2, n_sub).astype(np.uint16) if K2 else None
+    r = g.uniform(0.5, 2.0, M).astype(np.float32) if cfg.binorm else None
+    c = g.uniform(0.5, 2.0, N).astype(np.float32) if cfg.binorm else None
+    per = g.integers(0, int(2 * cfg.p * N) + 1, size=M)
+    rp = np.concatenate([[0], np.cumsum(per)]).astype(np.int32)
+    col = np.concatenate([np.sort(g.choice(N, k, replace=False)) for k in per]).astype(np.int32)
+    val = inp["W"][np.repeat(np.arange(M), per), col].copy()
+    return dict(C1=C1, idx1=i1, C2=C2, idx2=i2, r=r, c=c, row_ptr=rp, col=col, val=val)
+
+
+def qgemv_bytes(cfg, q, B):
+    """Compressed bytes one fused-product call must move: indices, codebooks,
+    scales, the CSR, the activations in and the outputs out."""
+    M, N, d, n_sub = cfg.M, cfg.N, cfg.d, cfg.n_sub
+    b = n_sub * 2 * (2 if q["C2"] is not None else 1) + q["C1"].nbytes
+    b += q["C2"].nbytes if q["C2"] is not None else 0
+    b += 4 * (M + N) if q["r"] is not None else 0
+    b += q["row_ptr"].nbytes + q["col"].nbytes + q["val"].nbytes
+    return b + 4 * B * (N + M)
+
+
+def qgemv_bench(cfg, inp, run_oracle, reps=50):
+    """The fused dequantize-and-multiply at one token (decode) and eight tokens,
+    timed with HIP events on its stream, against HBM peak on the compressed bytes;
+    beside it the materialized path (reconstruct, then a dense float32 product)
+    and the oracle (float64, one token)."""
+    import numpy as np
+    import torch
+
+    from hessian_weighted_vector_amd import vq
+    q = qgemv_inputs(cfg, inp)
+    M, N, d = cfg.M, cfg.N, cfg.d
+    gq = {k: (None if v is None else torch.from_numpy(v).cuda()) for k, v in q.items()}
+    args = (gq["C2"], gq["idx2"], gq["r"], gq["c"], gq["row_ptr"], gq["col"], gq["val"])
+    out = {}
+    for B in (1, 8):
+        X = torch.from_numpy(np.random.default_rng([cfg.cid, 94, B]).standard_normal((B, N)).astype(np.float32)).cuda()
+        Y = torch.empty((B, M), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(vq.qgemv_workspace_bytes(M, N, d, B), 256), dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            vq.qgemv(M, N, d, gq["C1"], gq["idx1"], X, *args, out=Y, ws=ws)
+        torch.cuda.synchronize()
+        vq.timing_enable(True)
+        for _ in range(reps):
+            vq.qgemv(M, N, d, gq["C1"], gq["idx1"], X, *args, out=Y, ws=ws)
+        torch.cuda.synchronize()
+        rec = {(r[0], r[1]): r for r in vq.timing_records()}[("qgemv", cfg.K1)]
+        vq.timing_enable(False)
+        t = rec[3] / rec[2]
+        nbytes = qgemv_bytes(cfg, q, B)
+        e = {"gpu_us": round(t * 1e3, 2), "tokens_per_s": round(B / (t * 1e-3), 1),
+             "compressed_MB": round(nbytes / 1e6, 2), "GBs": round(nbytes / (t * 1e-3) / 1e9, 1),
+             "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+             "dense_fp32_equivalent_GBs": round(4.0 * M * N / (t * 1e-3) / 1e9, 1)}
+        # the materialized path: write What, then a dense float32 product
+        What = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for _ in range(2):
+            vq.reconstruct(M, N, d, gq["C1"], gq["idx1"], *args, out=What)
+            torch.matmul(X, What.t())
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(10):
+            vq.reconstruct(M, N, d, gq["C1"], gq["idx1"], *args, out=What)
+            torch.matmul(X, What.t())
+        ev[1].record()
+        torch.cuda.synchronize()
+        e["materialized_us"] = round(ev[0].elapsed_time(ev[1]) / 10 * 1e3, 1)
+        del What
+        if run_oracle and B == 1:
+            import oracle
+            Xh = X.cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.qgemv(M, N, d, q["C1"], q["idx1"], Xh, q["C2"], q["idx2"], q["r"], q["c"], q["row_ptr"],
+                         q["col"], q["val"])
+            e["oracle_ms"] = round((time.perf_counter() - t0) * 1e3, 1)
+        out["B%d" % B] = e
+    return out
+
+
 def cpu_baseline(cfg, inp, seconds):
     """The oracle's assignment on a bounded sample (float64 exhaustive search)."""
     import numpy as np
@@ -187,6 +280,7 @@ def main():
     ap.add_argument("--config", type=int, default=4, help="workload number 1..5 (default 4)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-qgemv", action="store_true", help="skip the fused dequantize-and-multiply rows")
     ap.add_argument("--breakdown", action="store_true", help="print per-step timings to stderr")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB three times (a plain "
@@ -286,6 +380,8 @@ def main():
         oracle_ms = cpu_rows(cfg, inp, nnz)
         oracle_ms["assign"] = n_sub / (cpu["value"] * 1e9) * 1e3   # full pass at the sampled rate
     extra["rows"] = row_table(cfg, recs, nnz, oracle_ms)
+    if not args.no_qgemv:
+        extra["rows"]["NEXT1_qgemv"] = qgemv_bench(cfg, inp, not args.no_cpu_baseline)
 
     line = {
         "metric": "sub-vectors assigned/s per Lloyd iter (G/s) + % FP32 peak; update/recon HBM GB/s",

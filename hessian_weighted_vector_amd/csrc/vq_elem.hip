@@ -297,7 +297,6 @@ __global__ __launch_bounds__(1024) void k_sum_partials(const double* __restrict_
 
 constexpr int64_t kColChunk = 64;
 
-inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 constexpr int64_t kRowGroups = 32;
 
 }  // namespace

@@ -46,6 +46,9 @@ vq_status residual_launch(const float*, int64_t, int64_t, int, const float*, int
 vq_status reconstruct_launch(int64_t, int64_t, int, const float*, int, const uint16_t*, const float*, int,
                              const uint16_t*, const float*, const float*, const int32_t*,
                              const int32_t*, const float*, float*, hipStream_t);
+vq_status qgemv_launch(int64_t, int64_t, int, const float*, int, const uint16_t*, const float*, int,
+                       const uint16_t*, const float*, const float*, const int32_t*, const int32_t*,
+                       const float*, const float*, int64_t, float*, void*, size_t, hipStream_t);
 
 // ---- validation -------------------------------------------------------------
 vq_status check_shape(int64_t M, int64_t N, int d)
@@ -350,6 +353,37 @@ vq_status vq_reconstruct(int64_t M, int64_t N, int d, const float* C1, int K1, c
     VQ_TRY(check_device());
     return reconstruct_launch(M, N, d, C1, K1, idx1, C2, K2, idx2, rscale, cscale, row_ptr, col, val, W_hat,
                               as_stream(stream));
+}
+
+size_t vq_qgemv_workspace_bytes(int64_t M, int64_t N, int d, int64_t B)
+{
+    if (M <= 0 || N <= 0 || d < 1 || d > 8 || N % d || B < 0) return 0;
+    return ws_qgemv(M, N, d, B);
+}
+
+vq_status vq_qgemv(int64_t M, int64_t N, int d, const float* C1, int K1, const uint16_t* idx1,
+                   const float* C2, int K2, const uint16_t* idx2, const float* rscale, const float* cscale,
+                   const int32_t* row_ptr, const int32_t* col, const float* val, const float* X, int64_t B,
+                   float* Y, void* ws, size_t ws_bytes, void* stream)
+{
+    VQ_TRY(check_shape(M, N, d));
+    const int64_t n_sub = M * N / d;
+    VQ_TRY(check_K(K1, n_sub));
+    VQ_CHECK(C1 && idx1, "vq_qgemv: null pointer");
+    if (C2) {
+        VQ_TRY(check_K(K2, n_sub));
+        VQ_CHECK(idx2 != nullptr, "vq_qgemv: idx2 is null");
+    }
+    VQ_CHECK(!row_ptr || (col && val), "vq_qgemv: col/val are null");
+    VQ_CHECK(B >= 0, "vq_qgemv: B must be >= 0");
+    if (B == 0) return VQ_OK;
+    VQ_CHECK(X && Y, "vq_qgemv: null pointer");
+    VQ_CHECK((const void*)Y != (const void*)X, "vq_qgemv: Y may not alias X");
+    const size_t need = ws_qgemv(M, N, d, B);
+    VQ_WS(need == 0 || (ws && ws_bytes >= need), "vq_qgemv: workspace too small");
+    VQ_TRY(check_device());
+    return qgemv_launch(M, N, d, C1, K1, idx1, C2, K2, idx2, rscale, cscale, row_ptr, col, val, X, B, Y, ws,
+                        ws_bytes, as_stream(stream));
 }
 
 double vq_bits_per_weight(int64_t M, int64_t N, int d, int K1, int K2, int64_t nnz, int cb_bits, int binorm)

@@ -62,10 +62,13 @@ size_t ws_objective(int64_t n_sub);
 size_t ws_select(int64_t M, int64_t N);
 size_t ws_binorm(int64_t M, int64_t N);
 size_t ws_init(int64_t n_sub, int K, int d);
+size_t ws_qgemv(int64_t M, int64_t N, int d, int64_t B);
 
 // Argument checks shared by the entry points.
 vq_status check_shape(int64_t M, int64_t N, int d);
 vq_status check_K(int K, int64_t n_sub);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 

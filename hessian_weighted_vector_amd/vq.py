@@ -62,6 +62,9 @@ SIGNATURES = {
     "vq_objective": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P]),
     "vq_residual": (_I, [_P, _I64, _I64, _I, _P, _I, _P, _P, _P]),
     "vq_reconstruct": (_I, [_I64, _I64, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "vq_qgemv_workspace_bytes": (_SZ, [_I64, _I64, _I, _I64]),
+    "vq_qgemv": (_I, [_I64, _I64, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _SZ,
+                      _P]),
     "vq_fit": (_I, [ctypes.POINTER(FitParams), ctypes.POINTER(FitInputs), ctypes.POINTER(FitOutputs),
                     _P, _SZ, _P]),
     "vq_bits_per_weight": (_D, [_I64, _I64, _I, _I, _I, _I64, _I, _I]),
@@ -218,6 +221,25 @@ def reconstruct(M, N, d, C1, idx1, C2=None, idx2=None, rscale=None, cscale=None,
                                  0 if C2 is None else C2.shape[0], _ptr(idx2), _ptr(rscale), _ptr(cscale),
                                  _ptr(row_ptr), _ptr(col), _ptr(val), _ptr(W_hat), _stream()))
     return W_hat
+
+
+def qgemv_workspace_bytes(M, N, d, B):
+    return int(load().vq_qgemv_workspace_bytes(M, N, d, B))
+
+
+def qgemv(M, N, d, C1, idx1, X, C2=None, idx2=None, rscale=None, cscale=None, row_ptr=None, col=None,
+          val=None, out=None, ws=None):
+    """Y = X W_hat^T from the compressed form (X [B x N] -> Y [B x M], float32)."""
+    B = X.shape[0]
+    Y = out if out is not None else torch.empty((B, M), dtype=torch.float32, device=X.device)
+    need = qgemv_workspace_bytes(M, N, d, B)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=X.device)
+    _check(load().vq_qgemv(M, N, d, _ptr(C1), C1.shape[0], _ptr(idx1), _ptr(C2),
+                           0 if C2 is None else C2.shape[0], _ptr(idx2), _ptr(rscale), _ptr(cscale),
+                           _ptr(row_ptr), _ptr(col), _ptr(val), _ptr(X), B, _ptr(Y), _ptr(ws),
+                           0 if ws is None else ws.numel(), _stream()))
+    return Y
 
 
 def timing_enable(on=True):

@@ -157,6 +157,32 @@ vq_status vq_reconstruct(int64_t M, int64_t N, int d, const float* C1, int K1, c
                          const int32_t* row_ptr, const int32_t* col, const float* val,
                          float* W_hat, void* stream);
 
+/* Fused dequantize-and-multiply (VPTQ page, "End-to-End Quantization
+ * Pipeline": at inference the centroids are looked up inside the
+ * matrix-vector product so the full weight matrix is never written; SCVQ
+ * summary: the sparse correction takes part in the product):
+ *   Y[b, i] = sum_j W_hat[i, j] * X[b, j],   b < B, i < M,
+ * where W_hat is what vq_reconstruct writes for the same arguments; W_hat is
+ * never materialized.  X is [B x N] and Y is [B x M], float32 row-major, Y
+ * may not alias X.  Arithmetic: float32.  The kernel multiplies the decoded
+ * C1 (+ C2) value by x_j * cscale_j, sums with fused multiply-adds, scales the
+ * row sum by rscale_i, and for a salient entry takes the decoded term back out
+ * and adds val * x_j.  Error bound against the exact product: with
+ * u = 2^-24 and
+ *   T[b,i] = sum_j |Wd[i,j] x[b,j]| + sum_{salient (i,j)} (|Wd[i,j]| + |val|) |x[b,j]|
+ * (Wd = W_hat without the sparse overwrite),
+ *   |Y[b,i] - exact| <= (N/32 + nnz_i + 40) * u * T[b,i],
+ * nnz_i the salient count of row i.  Salient columns must be distinct within
+ * a row.  Results are bitwise reproducible for fixed arguments.  B = 0 is a
+ * no-op.  ws: at least vq_qgemv_workspace_bytes(M, N, d, B) bytes (may be 0,
+ * then ws may be NULL). */
+size_t vq_qgemv_workspace_bytes(int64_t M, int64_t N, int d, int64_t B);
+vq_status vq_qgemv(int64_t M, int64_t N, int d, const float* C1, int K1, const uint16_t* idx1,
+                   const float* C2, int K2, const uint16_t* idx2,
+                   const float* rscale, const float* cscale,
+                   const int32_t* row_ptr, const int32_t* col, const float* val,
+                   const float* X, int64_t B, float* Y, void* ws, size_t ws_bytes, void* stream);
+
 /* The whole per-matrix pipeline (HAS-VQ abstract; VPTQ page, "End-to-End
  * Quantization Pipeline": main codebook, then a residual codebook on
  * W - W_hat):

@@ -54,6 +54,20 @@ def test_null_pointers_and_workspace():
     assert lib.vq_binorm(FAKE, FAKE, 8, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == vq.VQ_ERR_INVALID
     assert lib.vq_reconstruct(8, 16, 8, FAKE, 4, FAKE, FAKE, 4, None, None, None, None, None, None, FAKE, None) == vq.VQ_ERR_INVALID
     assert lib.vq_workspace_bytes(8, 12, 8, 4, 0, 0) == 0
+    # qgemv: Y aliasing X, negative B, missing idx2, too little workspace
+    assert lib.vq_qgemv(8, 16, 8, FAKE, 4, FAKE, None, 0, None, None, None, None, None, None,
+                        FAKE, 1, FAKE, None, 0, None) == vq.VQ_ERR_INVALID
+    assert "alias" in lib.vq_last_error().decode()
+    assert lib.vq_qgemv(8, 16, 8, FAKE, 4, FAKE, None, 0, None, None, None, None, None, None,
+                        FAKE, -1, FAKE + 64, None, 0, None) == vq.VQ_ERR_INVALID
+    assert lib.vq_qgemv(8, 16, 8, FAKE, 4, FAKE, FAKE, 4, None, None, None, None, None, None,
+                        FAKE, 1, FAKE + 64, None, 0, None) == vq.VQ_ERR_INVALID
+    assert lib.vq_qgemv_workspace_bytes(8, 12, 8, 1) == 0
+    big_N = 8 * 14336 * 3          # three column slabs at one token
+    need = lib.vq_qgemv_workspace_bytes(64, big_N, 8, 1)
+    assert need >= 3 * 64 * 4
+    assert lib.vq_qgemv(64, big_N, 8, FAKE, 4, FAKE, None, 0, None, None, None, None, None, None,
+                        FAKE, 1, FAKE + 64, FAKE, need - 1, None) == vq.VQ_ERR_WORKSPACE
 
 
 def test_fit_rejects_bad_params():

@@ -169,6 +169,45 @@ def test_residual_reconstruct_fullsize(world):
     assert bits_equal(host(got), ref)
 
 
+@pytest.mark.parametrize("B", [1, 8])
+def test_qgemv_fullsize(world, B):
+    """The fused product at the full shape with the full codebook sizes and a
+    seeded ~1% CSR, every output against the oracle within the header's bound
+    (one token: the decode shape the benchmark times; eight: a batched decode)."""
+    cfg, Wp = world["cfg"], world["Wp"]
+    M, N, d = cfg.M, cfg.N, cfg.d
+    say("qgemv", cfg.name, "B =", B)
+    g = np.random.default_rng([cfg.cid, 91, B])
+    n_sub = M * N // d
+    flat = Wp.reshape(-1, d)
+    C1 = flat[np.sort(g.choice(n_sub, cfg.K1, replace=False))].copy()
+    K2 = cfg.K2 or 1
+    C2 = (0.1 * flat[np.sort(g.choice(n_sub, K2, replace=False))]).astype(np.float32)
+    i1 = g.integers(0, cfg.K1, n_sub).astype(np.uint16)
+    i2 = g.integers(0, K2, n_sub).astype(np.uint16)
+    per = g.integers(0, int(2 * cfg.p * N) + 1, size=M)
+    rp = np.concatenate([[0], np.cumsum(per)]).astype(np.int32)
+    col = np.concatenate([np.sort(g.choice(N, k, replace=False)) for k in per]).astype(np.int32)
+    rows = np.repeat(np.arange(M), per)
+    val = world["W"][rows, col].copy()
+    X = g.standard_normal((B, N)).astype(np.float32)
+    r, c = world["r"], world["c"]
+    ref = oracle.qgemv(M, N, d, C1, i1, X, C2, i2, r, c, rp, col, val)
+    Wd = np.abs(oracle.reconstruct(M, N, d, C1, i1, C2, i2, r, c).astype(np.float64))
+    Xa = np.abs(X.astype(np.float64))
+    T = Xa @ Wd.T
+    extra = np.zeros((B, M))
+    np.add.at(extra.T, rows, ((Wd[rows, col] + np.abs(val.astype(np.float64)))[:, None] * Xa[:, col].T))
+    T += extra
+    del Wd
+    tol = (N / 32.0 + per[None, :].astype(np.float64) + 40.0) * 2.0 ** -24 * T
+    got = vq.qgemv(M, N, d, dev(C1), dev(i1), dev(X), dev(C2), dev(i2),
+                   None if r is None else dev(r), None if c is None else dev(c), dev(rp), dev(col), dev(val))
+    err = np.abs(host(got).astype(np.float64) - ref)
+    say("  max err / bound = %.3g" % float((err / tol).max()))
+    assert np.all(err <= tol)
+
+
 def test_fit_fullsize_properties(world):
     cfg, W, h = world["cfg"], world["W"], world["h"]
     say("fit", cfg.name)
