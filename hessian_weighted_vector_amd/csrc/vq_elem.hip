@@ -8,6 +8,23 @@ namespace {
 
 constexpr int kBlock = 256;
 
+// Streaming accesses of the residual pass: the nontemporal hint lets the
+// matrix stream pass through L2 without evicting the codebook that every
+// sub-vector gathers from.
+typedef float vf4_t __attribute__((ext_vector_type(4)));
+__device__ inline float4 ld_stream(const float4* p)
+{
+    const vf4_t v = __builtin_nontemporal_load(reinterpret_cast<const vf4_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ inline void st_stream(float4* p, float4 v)
+{
+    vf4_t w;
+    w.x = v.x; w.y = v.y; w.z = v.z; w.w = v.w;
+    __builtin_nontemporal_store(w, reinterpret_cast<vf4_t*>(p));
+}
+__device__ inline int ld_stream(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+
 // Fixed-order tree reduction of one double per thread (blockDim == 256).
 __device__ inline double block_sum_f64(double v, double* sh)
 {
@@ -124,8 +141,8 @@ __global__ void k_residual8(const float4* __restrict__ X, int64_t n_half, const 
 {
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= n_half) return;
-    const int k = idx[q >> 1];
-    const float4 x = X[q];
+    const int k = ld_stream(idx + (q >> 1));
+    const float4 x = ld_stream(X + q);
     float4 r;
     if (k < K) {
         const float4 c = C[(size_t)k * 2 + (q & 1)];
@@ -133,7 +150,7 @@ __global__ void k_residual8(const float4* __restrict__ X, int64_t n_half, const 
     } else {
         r.x = r.y = r.z = r.w = __builtin_nanf("");
     }
-    R[q] = r;
+    st_stream(R + q, r);
 }
 
 // ---- reconstruction ------------------------------------------------------

@@ -8,10 +8,11 @@
 // that the slab of scaled activations x'_bj = x_bj * cscale_j of every token
 // in the launch fits in LDS (each workgroup stages it once and every row
 // reuses it).  A workgroup owns one slab and a group of rows; each wave walks
-// one row at a time with one sub-vector per lane per step: two coalesced
-// index loads, one gather of the d-float centroid row from C1 (L2-resident),
-// the residual row from LDS when the residual codebook is small, and d fused
-// multiply-adds per token.  The row's salient entries that fall in the slab
+// one row at a time.  For d = 8 a lane pair owns a sub-vector per step (each
+// lane half of it): coalesced index loads, one gather instruction that
+// fetches 32 whole centroid rows from C1 (L2-resident), the residual rows from
+// LDS when the residual codebook is small, and 4 fused multiply-adds per lane
+// and token.  The row's salient entries that fall in the slab
 // are applied by the same wave afterwards: the decoded weight's term is taken
 // back out and val * x added.  A fixed shuffle tree sums the wave; with more
 // than one slab the partial sums go to the workspace and a second kernel adds
@@ -97,27 +98,26 @@ __global__ __launch_bounds__(kQThreads) void k_qgemv(
         for (int b = 0; b < TB; ++b) acc[b] = 0.0f;
 
         if (D == 8) {
-#pragma unroll 4
-            for (int s = lane; s < nsv; s += 64) {
-                const float4* c1 = reinterpret_cast<const float4*>(C1) + 2 * (int)ir1[s];
-                float4 lo = c1[0], hi = c1[1];
+            // lane pairs share a sub-vector: the even lane takes elements 0-3,
+            // the odd lane 4-7, so one load instruction fetches whole centroid
+            // rows (one cache-line request per sub-vector) and every lane keeps
+            // a partial sum over its half
+            const int h = lane & 1;
+#pragma unroll 8
+            for (int s = lane >> 1; s < nsv; s += 32) {
+                float4 w = reinterpret_cast<const float4*>(C1)[2 * (int)ir1[s] + h];
                 if (C2M != 0) {
                     const int k2 = ir2[s];
-                    const float4* c2 = C2M == 1 ? reinterpret_cast<const float4*>(c2s) + 2 * k2
-                                                : reinterpret_cast<const float4*>(C2) + 2 * k2;
-                    const float4 l2 = c2[0], h2 = c2[1];
-                    lo.x = lo.x + l2.x; lo.y = lo.y + l2.y; lo.z = lo.z + l2.z; lo.w = lo.w + l2.w;
-                    hi.x = hi.x + h2.x; hi.y = hi.y + h2.y; hi.z = hi.z + h2.z; hi.w = hi.w + h2.w;
+                    const float4 w2 = C2M == 1 ? reinterpret_cast<const float4*>(c2s)[2 * k2 + h]
+                                               : reinterpret_cast<const float4*>(C2)[2 * k2 + h];
+                    w.x = w.x + w2.x; w.y = w.y + w2.y; w.z = w.z + w2.z; w.w = w.w + w2.w;
                 }
 #pragma unroll
                 for (int b = 0; b < TB; ++b) {
-                    const float4* xq = reinterpret_cast<const float4*>(xs + b * sbd) + 2 * s;
-                    const float4 xl = xq[0], xh = xq[1];
+                    const float4 xv = reinterpret_cast<const float4*>(xs + b * sbd)[2 * s + h];
                     float a = acc[b];
-                    a = fmaf(lo.x, xl.x, a); a = fmaf(lo.y, xl.y, a);
-                    a = fmaf(lo.z, xl.z, a); a = fmaf(lo.w, xl.w, a);
-                    a = fmaf(hi.x, xh.x, a); a = fmaf(hi.y, xh.y, a);
-                    a = fmaf(hi.z, xh.z, a); a = fmaf(hi.w, xh.w, a);
+                    a = fmaf(w.x, xv.x, a); a = fmaf(w.y, xv.y, a);
+                    a = fmaf(w.z, xv.z, a); a = fmaf(w.w, xv.w, a);
                     acc[b] = a;
                 }
             }
