@@ -5,10 +5,10 @@ closed form in Python.  Only the test suite, the package smoke check and the
 benchmark's CPU-baseline leg may import this package.  It shares no code with
 the HIP library and never imports it.
 """
-from .oracle import (build, load, nnz, select, binorm, init, assign, objective, update,
+from .oracle import (build, load, nnz, select, select_subvectors, select_residual, keep_to_csr, binorm, init, assign, objective, update,
                      residual, reconstruct, qgemv, fit)
 from .bits import bits_per_weight, compression_ratio_single
 
-__all__ = ["build", "load", "nnz", "select", "binorm", "init", "assign", "objective",
+__all__ = ["build", "load", "nnz", "select", "select_subvectors", "select_residual", "keep_to_csr", "binorm", "init", "assign", "objective",
            "update", "residual", "reconstruct", "qgemv", "fit", "bits_per_weight",
            "compression_ratio_single"]

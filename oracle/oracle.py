@@ -46,6 +46,9 @@ _SIGS = {
     "orc_update": (_D, [_P, _P, _P, _P, _LL, _LL, _I, _P, _I, _P, _P]),
     "orc_residual": (None, [_P, _LL, _I, _P, _P, _P]),
     "orc_reconstruct": (None, [_LL, _LL, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "orc_select_subvectors": (_I, [_P, _P, _LL, _LL, _I, _LL, _P]),
+    "orc_select_residual": (_I, [_P, _P, _P, _LL, _LL, _LL, _P]),
+    "orc_keep_to_csr": (_LL, [_P, _P, _LL, _LL, _P, _P, _P]),
     "orc_qgemv": (_I, [_LL, _LL, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _LL, _P]),
     "orc_fit": (_I, [_P, _P, _LL, _LL, _I, _I, _I, _I, _I, _D, _I, _I, _P, _P, _I,
                      _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -95,6 +98,46 @@ def select(W, h, nnz_, lib=None):
     if rc:
         raise RuntimeError("orc_select failed: %d" % rc)
     return row_ptr, col[:nnz_], val[:nnz_], keep.reshape(M, N)
+
+
+def select_subvectors(W, h, d, n_sel, keep=None, lib=None):
+    """keep (1 = kept) with every position of the n_sel most salient sub-vectors set to 0."""
+    lib = lib or load()
+    W = _c(W, np.float32)
+    M, N = W.shape
+    keep = np.ones((M, N), np.uint8) if keep is None else np.array(keep, dtype=np.uint8, copy=True, order="C")
+    rc = lib.orc_select_subvectors(_ptr(W), _ptr(_c(h, np.float32)), M, N, d, int(n_sel), _ptr(keep))
+    if rc:
+        raise ValueError("orc_select_subvectors failed: %d" % rc)
+    return keep
+
+
+def select_residual(W, What, h, n_sel, keep=None, lib=None):
+    """keep with the n_sel largest weighted residuals among kept positions set to 0."""
+    lib = lib or load()
+    W = _c(W, np.float32)
+    M, N = W.shape
+    keep = np.ones((M, N), np.uint8) if keep is None else np.array(keep, dtype=np.uint8, copy=True, order="C")
+    rc = lib.orc_select_residual(_ptr(W), _ptr(_c(What, np.float32)), _ptr(_c(h, np.float32)), M, N,
+                                 int(n_sel), _ptr(keep))
+    if rc:
+        raise ValueError("orc_select_residual failed: %d" % rc)
+    return keep
+
+
+def keep_to_csr(W, keep, lib=None):
+    """CSR (row_ptr, col, val) of the positions with keep == 0."""
+    lib = lib or load()
+    W = _c(W, np.float32)
+    M, N = W.shape
+    keep = _c(keep, np.uint8)
+    n = int((keep == 0).sum())
+    row_ptr = np.zeros(M + 1, np.int32)
+    col = np.zeros(max(n, 1), np.int32)
+    val = np.zeros(max(n, 1), np.float32)
+    got = lib.orc_keep_to_csr(_ptr(W), _ptr(keep), M, N, _ptr(row_ptr), _ptr(col), _ptr(val))
+    assert got == n
+    return row_ptr, col[:n], val[:n]
 
 
 def binorm(W, h, lib=None):

@@ -103,6 +103,89 @@ int orc_select(const float* W, const float* h, long long M, long long N, long lo
 }
 
 /* ------------------------------------------------------------------ */
+/* The unified sparse correction (SCVQ summary: outliers, highly salient
+ * sub-vectors and the largest quantization residuals share one sparse
+ * correction matrix).  keep[M*N] marks the correction: 0 = held exactly.
+ *
+ * Salient sub-vectors: score of sub-vector s = (row i, block b) is
+ *   S_s = sum over t = 0..d-1, in that order, of h_j * (w_j * w_j), j = b*d+t,
+ * each product and the running sum rounded to fp32.  The n_sel largest
+ * (ties: smaller s) have all d positions set to 0 in keep. */
+int orc_select_subvectors(const float* W, const float* h, long long M, long long N, int d,
+                          long long n_sel, unsigned char* keep)
+{
+    long long nb = N / d, n_sub = M * nb;
+    if (n_sel < 0 || n_sel > n_sub) return 2;
+    orc_scored* all = (orc_scored*)malloc(sizeof(orc_scored) * (size_t)(n_sub > 0 ? n_sub : 1));
+    if (!all) return 3;
+    for (long long s = 0; s < n_sub; ++s) {
+        long long i = s / nb, b = s % nb;
+        float acc = 0.0f;
+        for (int t = 0; t < d; ++t) {
+            long long j = b * d + t;
+            float w = W[i * N + j];
+            float sq = w * w;
+            float term = h[j] * sq;
+            acc = acc + term;
+        }
+        all[s].score = acc;
+        all[s].lin = s;
+    }
+    qsort(all, (size_t)n_sub, sizeof(orc_scored), orc_scored_cmp);
+    for (long long e = 0; e < n_sel; ++e) {
+        long long s = all[e].lin;
+        for (int t = 0; t < d; ++t) keep[s * d + t] = 0;
+    }
+    free(all);
+    return 0;
+}
+
+/* Largest quantization residuals: among the positions still kept
+ * (keep == 1), score r_ij = h_j * ((w_ij - what_ij) * (w_ij - what_ij)) in
+ * fp32 (difference, square, scale).  The min(n_sel, #kept) largest (ties:
+ * smaller linear index) are set to 0 in keep. */
+int orc_select_residual(const float* W, const float* What, const float* h, long long M, long long N,
+                        long long n_sel, unsigned char* keep)
+{
+    long long total = M * N, n = 0;
+    if (n_sel < 0) return 2;
+    orc_scored* all = (orc_scored*)malloc(sizeof(orc_scored) * (size_t)(total > 0 ? total : 1));
+    if (!all) return 3;
+    for (long long e = 0; e < total; ++e) {
+        if (keep[e] == 0) continue;
+        float r = W[e] - What[e];
+        float sq = r * r;
+        all[n].score = h[e % N] * sq;
+        all[n].lin = e;
+        ++n;
+    }
+    qsort(all, (size_t)n, sizeof(orc_scored), orc_scored_cmp);
+    for (long long e = 0; e < n_sel && e < n; ++e) keep[all[e].lin] = 0;
+    free(all);
+    return 0;
+}
+
+/* The CSR of every position with keep == 0, row by row, columns ascending,
+ * values the exact W entries; returns the count. */
+long long orc_keep_to_csr(const float* W, const unsigned char* keep, long long M, long long N,
+                          int* row_ptr, int* col, float* val)
+{
+    long long pos = 0;
+    row_ptr[0] = 0;
+    for (long long i = 0; i < M; ++i) {
+        for (long long j = 0; j < N; ++j) {
+            if (keep[i * N + j] == 0) {
+                col[pos] = (int)j;
+                val[pos] = W[i * N + j];
+                ++pos;
+            }
+        }
+        row_ptr[i + 1] = (int)pos;
+    }
+    return pos;
+}
+
+/* ------------------------------------------------------------------ */
 /* Bi-normalization (SCVQ summary: weights bi-normalized across rows and
  * columns before clustering).  One pass of RMS scaling, rows first:
  *   r_i = sqrt(sum_j W_ij^2 / N)            (sum in fp64; r = 1 if 0)

@@ -387,6 +387,73 @@ def pin_bits_worked_example(lib):
     assert abs(bpw - ex["original_bits"] / cr) < 1e-12
 
 
+def _tie_case(seed, M, N):
+    """Tiny matrix with many exact score ties: weights and h from small sets."""
+    g = np.random.default_rng([13, seed])
+    W = (g.integers(-3, 4, size=(M, N)) * 0.25).astype(np.float32)
+    h = g.choice(np.array([0.5, 1.0, 2.0], np.float32), N)
+    return W, h, g
+
+
+def _subvector_scores_np(W, h, d):
+    """fp32 score per sub-vector: sum over t in order of h_j * (w * w), numpy float32 ops."""
+    M, N = W.shape
+    Wr = W.reshape(M, N // d, d)
+    hr = h.reshape(N // d, d)
+    acc = np.zeros((M, N // d), np.float32)
+    for t in range(d):
+        term = (hr[None, :, t] * (Wr[:, :, t] * Wr[:, :, t])).astype(np.float32)
+        acc = (acc + term).astype(np.float32)
+    return acc.ravel()
+
+
+def pin_select_subvectors_brute_force(lib):
+    """Brute force with numpy: fp32 sub-vector scores, lexsort (score desc, id asc), and the
+    selection ORed into an existing correction."""
+    for seed, (M, N, d, n_sel) in enumerate([(6, 16, 4, 5), (5, 24, 8, 7), (4, 9, 3, 12), (3, 8, 8, 0)]):
+        W, h, g = _tie_case(seed, M, N)
+        n_sub = M * N // d
+        sc = _subvector_scores_np(W, h, d)
+        order = np.lexsort((np.arange(n_sub), -sc))
+        keep0 = (g.random((M, N)) > 0.1).astype(np.uint8)
+        exp = keep0.copy().reshape(n_sub, d)
+        exp[order[:n_sel]] = 0
+        got = O.select_subvectors(W, h, d, n_sel, keep=keep0, lib=lib)
+        assert np.array_equal(got.reshape(n_sub, d), exp)
+        # taking all sub-vectors clears everything
+        assert not O.select_subvectors(W, h, d, n_sub, lib=lib).any()
+
+
+def pin_select_residual_brute_force(lib):
+    """Brute force with numpy over the kept positions only: fp32 h * (w - what)^2, lexsort
+    (score desc, linear index asc); asking for more than remain takes every kept position."""
+    for seed, (M, N, n_sel) in enumerate([(6, 16, 9), (5, 24, 30), (4, 10, 1000)]):
+        W, h, g = _tie_case(seed + 10, M, N)
+        What = (g.integers(-2, 3, size=(M, N)) * 0.25).astype(np.float32)
+        keep0 = (g.random((M, N)) > 0.2).astype(np.uint8)
+        r = (W - What).astype(np.float32)
+        sc = (h[None, :] * (r * r).astype(np.float32)).astype(np.float32).ravel()
+        lin = np.arange(M * N)
+        cand = lin[keep0.ravel() == 1]
+        order = cand[np.lexsort((cand, -sc[cand]))]
+        exp = keep0.ravel().copy()
+        exp[order[:n_sel]] = 0
+        got = O.select_residual(W, What, h, n_sel, keep=keep0, lib=lib)
+        assert np.array_equal(got.ravel(), exp)
+
+
+def pin_keep_to_csr_matches_nonzero(lib):
+    """The CSR of a mask is numpy's row-major nonzero list of the held positions."""
+    W, h, g = _tie_case(20, 7, 13)
+    keep = (g.random((7, 13)) > 0.3).astype(np.uint8)
+    keep[2] = 1                                   # an empty row
+    rp, col, val = O.keep_to_csr(W, keep, lib=lib)
+    ii, jj = np.nonzero(keep == 0)
+    assert np.array_equal(col, jj.astype(np.int32))
+    assert np.array_equal(val, W[ii, jj])
+    assert np.array_equal(rp, np.concatenate([[0], np.cumsum((keep == 0).sum(1))]).astype(np.int32))
+
+
 def _qg_case(seed, M=6, N=24, d=4, K1=7, K2=3, B=3, pow2_scales=False):
     g = np.random.default_rng([11, seed])
     nb = N // d

@@ -54,6 +54,17 @@ MUTANTS = {
     "reconstruct_wrong_col_scale": [("if (c) v = v * c[j];", "if (c) v = v * c[(j + 1) % N];")],
     "reconstruct_drops_row_scale": [("if (r) v = v * r[i];", "if (0) v = v * r[i];")],
     "reconstruct_no_overwrite": [("if (row_ptr)\n            for", "if (0)\n            for")],
+    "subvec_score_ignores_h": [("float term = h[j] * sq;", "float term = sq;")],
+    "subvec_wrong_block": [("long long j = b * d + t;\n            float w = W[i * N + j];",
+                            "long long j = t;\n            float w = W[i * N + j];")],
+    "residual_ignores_keep": [("        if (keep[e] == 0) continue;\n        float r", "        float r")],
+    "residual_not_squared": [("float sq = r * r;", "float sq = r;")],
+    "residual_takes_one_more": [("for (long long e = 0; e < n_sel && e < n; ++e)",
+                                 "for (long long e = 0; e <= n_sel && e < n; ++e)")],
+    "keep_to_csr_skips_row0": [("int* row_ptr, int* col, float* val)\n{\n    long long pos = 0;\n    row_ptr[0] = 0;\n"
+                                "    for (long long i = 0;",
+                                "int* row_ptr, int* col, float* val)\n{\n    long long pos = 0;\n    row_ptr[0] = 0;\n"
+                                "    for (long long i = 1;")],
     "qgemv_wrong_row": [("acc += (double)What[i * N + j] * (double)x[j];",
                          "acc += (double)What[((i + 1) % M) * N + j] * (double)x[j];")],
     "qgemv_float_accumulation": [("            double acc = 0.0;\n            for (long long j = 0; j < N; ++j) acc +=",
