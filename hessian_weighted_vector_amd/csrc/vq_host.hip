@@ -46,6 +46,12 @@ vq_status residual_launch(const float*, int64_t, int64_t, int, const float*, int
 vq_status reconstruct_launch(int64_t, int64_t, int, const float*, int, const uint16_t*, const float*, int,
                              const uint16_t*, const float*, const float*, const int32_t*,
                              const int32_t*, const float*, float*, hipStream_t);
+vq_status subvector_select_launch(const float*, const float*, int64_t, int64_t, int, int64_t, uint8_t*, void*,
+                                  size_t, hipStream_t);
+vq_status residual_select_launch(const float*, const float*, const float*, int64_t, int64_t, int, int64_t,
+                                 uint8_t*, void*, size_t, hipStream_t);
+vq_status mask_to_csr_launch(const float*, const uint8_t*, int64_t, int64_t, int, int64_t, int32_t*, int32_t*,
+                             float*, void*, size_t, hipStream_t);
 vq_status qgemv_launch(int64_t, int64_t, int, const float*, int, const uint16_t*, const float*, int,
                        const uint16_t*, const float*, const float*, const int32_t*, const int32_t*,
                        const float*, const float*, int64_t, float*, void*, size_t, hipStream_t);
@@ -353,6 +359,44 @@ vq_status vq_reconstruct(int64_t M, int64_t N, int d, const float* C1, int K1, c
     VQ_TRY(check_device());
     return reconstruct_launch(M, N, d, C1, K1, idx1, C2, K2, idx2, rscale, cscale, row_ptr, col, val, W_hat,
                               as_stream(stream));
+}
+
+vq_status vq_select_subvectors(const float* W, const float* h, int64_t M, int64_t N, int d, int64_t n_sel,
+                               uint8_t* mask, void* ws, size_t ws_bytes, void* stream)
+{
+    VQ_TRY(check_shape(M, N, d));
+    const int64_t n_sub = M * N / d;
+    VQ_CHECK(W && h && mask, "vq_select_subvectors: null pointer");
+    VQ_CHECK(n_sel >= 0 && n_sel <= n_sub, "vq_select_subvectors: n_sel must be in [0, n_sub]");
+    VQ_CHECK(M <= (int64_t)UINT32_MAX, "vq_select_subvectors: too many rows");
+    VQ_WS(ws && ws_bytes >= ws_select(M, N), "vq_select_subvectors: workspace too small");
+    VQ_TRY(check_device());
+    return subvector_select_launch(W, h, M, N, d, n_sel, mask, ws, ws_bytes, as_stream(stream));
+}
+
+vq_status vq_select_residual(const float* W, const float* W_hat, const float* h, int64_t M, int64_t N, int d,
+                             int64_t n_sel, uint8_t* mask, void* ws, size_t ws_bytes, void* stream)
+{
+    VQ_TRY(check_shape(M, N, d));
+    VQ_CHECK(W && W_hat && h && mask, "vq_select_residual: null pointer");
+    VQ_CHECK(n_sel >= 0, "vq_select_residual: n_sel must be >= 0");
+    VQ_CHECK(M <= (int64_t)UINT32_MAX, "vq_select_residual: too many rows");
+    VQ_WS(ws && ws_bytes >= ws_select(M, N), "vq_select_residual: workspace too small");
+    VQ_TRY(check_device());
+    return residual_select_launch(W, W_hat, h, M, N, d, n_sel, mask, ws, ws_bytes, as_stream(stream));
+}
+
+vq_status vq_mask_to_csr(const float* W, const uint8_t* mask, int64_t M, int64_t N, int d, int64_t nnz_cap,
+                         int32_t* row_ptr, int32_t* col, float* val, void* ws, size_t ws_bytes, void* stream)
+{
+    VQ_TRY(check_shape(M, N, d));
+    VQ_CHECK(W && mask && row_ptr, "vq_mask_to_csr: null pointer");
+    VQ_CHECK(nnz_cap >= 0, "vq_mask_to_csr: nnz_cap must be >= 0");
+    VQ_CHECK(nnz_cap == 0 || (col && val), "vq_mask_to_csr: col/val are null");
+    VQ_CHECK(M * N <= (int64_t)INT32_MAX, "vq_mask_to_csr: M*N exceeds the int32 row pointer");
+    VQ_WS(ws && ws_bytes >= ws_select(M, N), "vq_mask_to_csr: workspace too small");
+    VQ_TRY(check_device());
+    return mask_to_csr_launch(W, mask, M, N, d, nnz_cap, row_ptr, col, val, ws, ws_bytes, as_stream(stream));
 }
 
 size_t vq_qgemv_workspace_bytes(int64_t M, int64_t N, int d, int64_t B)

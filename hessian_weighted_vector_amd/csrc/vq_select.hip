@@ -53,7 +53,8 @@ __global__ void k_sel_init(SelState* st, int64_t nnz, int* hist)
 __global__ __launch_bounds__(256) void k_sel_hist(const float* __restrict__ W,
                                                   const float* __restrict__ h, int64_t total,
                                                   int64_t N, const SelState* __restrict__ st,
-                                                  uint32_t pmask, int shift, int* __restrict__ hist)
+                                                  uint32_t pmask, int shift, uint32_t dmask,
+                                                  int* __restrict__ hist)
 {
     __shared__ int cnt[kBins];
     for (int q = threadIdx.x; q < kBins; q += blockDim.x) cnt[q] = 0;
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(256) void k_sel_hist(const float* __restrict__ W,
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
         const uint32_t b = score_bits(W, h, e, N);
-        if ((b & pmask) == prefix) atomicAdd(&cnt[(b >> shift) & (kBins - 1)], 1);
+        if ((b & pmask) == prefix) atomicAdd(&cnt[(b >> shift) & dmask], 1);
     }
     __syncthreads();
     for (int q = threadIdx.x; q < kBins; q += blockDim.x)
@@ -179,6 +180,7 @@ __global__ __launch_bounds__(kScanThreads) void k_sel_rows(const SelState* __res
         eq_before += ceq[i];
         sel_local += cgt[i] + t;
     }
+    if (row_ptr == nullptr) return;   // uniform: the selection only needs take[]
     int64_t run = scan1024(sel_local, sh) - sel_local;
     for (int64_t i = r0; i < r1; ++i) {
         row_ptr[i] = (int32_t)run;
@@ -266,6 +268,272 @@ __global__ __launch_bounds__(kRowThreads) void k_sel_compact(
     }
 }
 
+// ---- the unified sparse correction ---------------------------------------
+// SCVQ summary: outliers, highly salient sub-vectors and the largest
+// quantization residuals share one sparse correction matrix.  The two extra
+// selections mark the mask (bit t of byte s = element t of sub-vector s is
+// held exactly); vq_mask_to_csr turns the mask into the CSR.
+//
+// Keys are uint32: 0 = not eligible, otherwise the score's float bits + 1
+// (non-negative floats order like their bits), so the same radix select
+// (k_sel_init / k_sel_pick / k_sel_rows) finds the n-th largest key; a
+// threshold of 0 means fewer eligible keys than asked, and then every
+// eligible key is taken and no tie is.  The unit of work is one sub-vector
+// (contiguous d floats of W); a functor yields its keys in linear order.
+
+// One key per sub-vector: S_s = sum over t of h_j * (w_j * w_j), fp32, t in
+// order, no fused multiply-add.
+struct KeySubvector {
+    const float* W;
+    const float* h;
+    int64_t nb;
+    int d;
+    static constexpr int kKeys = 1;
+    __device__ int count() const { return 1; }
+    __device__ void keys(int64_t s, uint32_t* k) const
+    {
+        const float* w = W + s * d;
+        const float* hh = h + (s % nb) * d;
+        float acc = 0.0f;
+        for (int t = 0; t < d; ++t) {
+            const float x = w[t];
+            const float sq = x * x;
+            const float term = hh[t] * sq;
+            acc = acc + term;
+        }
+        k[0] = __float_as_uint(acc) + 1u;
+    }
+};
+
+// One key per element: r = h_j * ((w - what) * (w - what)), fp32, not
+// eligible where the mask bit is already set.
+struct KeyResidual {
+    const float* W;
+    const float* Wh;
+    const float* h;
+    const uint8_t* mask;
+    int64_t nb;
+    int d;
+    static constexpr int kKeys = 8;
+    __device__ int count() const { return d; }
+    __device__ void keys(int64_t s, uint32_t* k) const
+    {
+        const float* w = W + s * d;
+        const float* wh = Wh + s * d;
+        const float* hh = h + (s % nb) * d;
+        const unsigned mb = mask[s];
+        for (int t = 0; t < d; ++t) {
+            const float r = w[t] - wh[t];
+            const float sq = r * r;
+            const float sc = hh[t] * sq;
+            k[t] = ((mb >> t) & 1u) ? 0u : __float_as_uint(sc) + 1u;
+        }
+    }
+};
+
+template <class F>
+__global__ __launch_bounds__(256) void k_key_hist(F f, int64_t n_units, const SelState* __restrict__ st,
+                                                  uint32_t pmask, int shift, uint32_t dmask,
+                                                  int* __restrict__ hist)
+{
+    __shared__ int cnt[kBins];
+    for (int q = threadIdx.x; q < kBins; q += blockDim.x) cnt[q] = 0;
+    __syncthreads();
+    const uint32_t prefix = st->prefix;
+    const int g = f.count();
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < n_units; s += stride) {
+        uint32_t k[F::kKeys];
+        f.keys(s, k);
+        for (int t = 0; t < g; ++t)
+            if ((k[t] & pmask) == prefix) atomicAdd(&cnt[(k[t] >> shift) & dmask], 1);
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < kBins; q += blockDim.x)
+        if (cnt[q]) atomicAdd(&hist[q], cnt[q]);
+}
+
+// Per row (units [i*upr, (i+1)*upr)): keys above the threshold, and ties
+// (none when the threshold is 0).
+template <class F>
+__global__ __launch_bounds__(kRowThreads) void k_key_row_count(F f, int64_t upr, const SelState* __restrict__ st,
+                                                               int* __restrict__ cgt, int* __restrict__ ceq)
+{
+    __shared__ int sg[kRowThreads], se[kRowThreads];
+    const int64_t i = blockIdx.x;
+    const uint32_t tau = st->prefix;
+    const int g_n = f.count();
+    int g = 0, q = 0;
+    for (int64_t u = threadIdx.x; u < upr; u += kRowThreads) {
+        uint32_t k[F::kKeys];
+        f.keys(i * upr + u, k);
+        for (int t = 0; t < g_n; ++t) {
+            g += k[t] > tau;
+            q += (k[t] == tau) && tau != 0u;
+        }
+    }
+    sg[threadIdx.x] = g;
+    se[threadIdx.x] = q;
+    __syncthreads();
+    for (int w = kRowThreads / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) {
+            sg[threadIdx.x] += sg[threadIdx.x + w];
+            se[threadIdx.x] += se[threadIdx.x + w];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) { cgt[i] = sg[0]; ceq[i] = se[0]; }
+}
+
+// Per row: walk the units in order, decide each key (above the threshold, or
+// one of the row's first take[i] ties), and OR the decisions into the mask:
+// bit t per element key, or every bit of the sub-vector for a sub-vector key.
+template <class F>
+__global__ __launch_bounds__(kRowThreads) void k_key_mark(F f, int64_t upr, int d, const SelState* __restrict__ st,
+                                                          const int* __restrict__ take, uint8_t* __restrict__ mask)
+{
+    __shared__ int sh[kRowThreads];
+    __shared__ int tot_eq;
+    const int64_t i = blockIdx.x;
+    const uint32_t tau = st->prefix;
+    const int row_take = take[i];
+    const int g_n = f.count();
+    const unsigned all_bits = (1u << d) - 1u;
+    int eq_run = 0;
+    for (int64_t u0 = 0; u0 < upr; u0 += kRowThreads) {
+        const int64_t u = u0 + threadIdx.x;
+        uint32_t k[F::kKeys];
+        int n_eq = 0;
+        if (u < upr) {
+            f.keys(i * upr + u, k);
+            for (int t = 0; t < g_n; ++t) n_eq += (k[t] == tau) && tau != 0u;
+        }
+        const int eq_incl = scan256(n_eq, sh);
+        if (threadIdx.x == kRowThreads - 1) tot_eq = eq_incl;
+        if (u < upr) {
+            int eq_rank = eq_run + eq_incl - n_eq;
+            unsigned mb = 0;
+            for (int t = 0; t < g_n; ++t) {
+                bool sel = k[t] > tau;
+                if (k[t] == tau && tau != 0u) { sel = eq_rank < row_take; ++eq_rank; }
+                if (sel) mb |= (F::kKeys == 1) ? all_bits : (1u << t);
+            }
+            if (mb) {
+                const int64_t s = i * upr + u;
+                mask[s] = (uint8_t)(mask[s] | mb);
+            }
+        }
+        __syncthreads();
+        eq_run += tot_eq;
+        __syncthreads();
+    }
+}
+
+// mask -> CSR: per-row counts, one block scans the rows, then per row a
+// block writes the held positions in column order (at most cap entries).
+__global__ __launch_bounds__(kRowThreads) void k_mask_row_count(const uint8_t* __restrict__ mask, int64_t nb, int d,
+                                                                int* __restrict__ cnt)
+{
+    __shared__ int sh[kRowThreads];
+    const int64_t i = blockIdx.x;
+    const unsigned all_bits = (1u << d) - 1u;
+    int c = 0;
+    for (int64_t b = threadIdx.x; b < nb; b += kRowThreads) c += __popc(mask[i * nb + b] & all_bits);
+    sh[threadIdx.x] = c;
+    __syncthreads();
+    for (int w = kRowThreads / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) cnt[i] = sh[0];
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_mask_rows(int64_t M, const int* __restrict__ cnt,
+                                                            int32_t* __restrict__ row_ptr)
+{
+    __shared__ int64_t sh[kScanThreads];
+    const int64_t per = (M + kScanThreads - 1) / kScanThreads;
+    const int64_t r0 = threadIdx.x * per;
+    const int64_t r1 = r0 + per < M ? r0 + per : M;
+    int64_t local = 0;
+    for (int64_t i = r0; i < r1; ++i) local += cnt[i];
+    int64_t run = scan1024(local, sh) - local;
+    for (int64_t i = r0; i < r1; ++i) {
+        row_ptr[i] = (int32_t)run;
+        run += cnt[i];
+    }
+    if (threadIdx.x == kScanThreads - 1) row_ptr[M] = (int32_t)run;
+}
+
+__global__ __launch_bounds__(kRowThreads) void k_mask_compact(const float* __restrict__ W,
+                                                              const uint8_t* __restrict__ mask, int64_t N, int d,
+                                                              const int32_t* __restrict__ row_ptr, int64_t cap,
+                                                              int32_t* __restrict__ col, float* __restrict__ val)
+{
+    __shared__ int sh[kRowThreads];
+    __shared__ int tot;
+    const int64_t i = blockIdx.x;
+    const int64_t nb = N / d;
+    const unsigned all_bits = (1u << d) - 1u;
+    int64_t pos_run = row_ptr[i];
+    for (int64_t b0 = 0; b0 < nb; b0 += kRowThreads) {
+        const int64_t b = b0 + threadIdx.x;
+        const unsigned mb = b < nb ? (mask[i * nb + b] & all_bits) : 0u;
+        const int n = __popc(mb);
+        const int incl = scan256(n, sh);
+        if (threadIdx.x == kRowThreads - 1) tot = incl;
+        int64_t p = pos_run + incl - n;
+        for (int t = 0; t < d; ++t) {
+            if (((mb >> t) & 1u) && p < cap) {
+                col[p] = (int32_t)(b * d + t);
+                val[p] = W[i * N + b * d + t];
+                ++p;
+            }
+        }
+        __syncthreads();
+        pos_run += tot;
+        __syncthreads();
+    }
+}
+
+// Radix select of the n-th largest key, then per-row counts, ties and marks.
+template <class F>
+vq_status key_select_launch(const F& f, int64_t M, int64_t upr, int d, int64_t n, uint8_t* mask, void* ws,
+                            size_t ws_bytes, const char* what, hipStream_t st)
+{
+    Carver cv(ws, ws_bytes);
+    SelState* state = cv.take<SelState>(1);
+    int* hist = cv.take<int>(kBins);
+    int* cgt = cv.take<int>((size_t)M);
+    int* ceq = cv.take<int>((size_t)M);
+    int* take = cv.take<int>((size_t)M);
+    if (!cv.ok) return fail(VQ_ERR_WORKSPACE, std::string(what) + ": workspace too small");
+    const int64_t n_units = M * upr;
+    hipLaunchKernelGGL(k_sel_init, dim3(grid_for(kBins, 256)), dim3(256), 0, st, state, n, hist);
+    VQ_LAUNCHED("k_sel_init");
+    if (n > 0) {
+        const int shifts[3] = {21, 10, 0};
+        const int nbins[3] = {2048, 2048, 1024};
+        const uint32_t pmasks[3] = {0u, 0xFFE00000u, 0xFFFFFC00u};
+        const unsigned hb = (unsigned)std::min<int64_t>(kHistBlocks, grid_for(n_units, 256 * 4));
+        for (int p = 0; p < 3; ++p) {
+            hipLaunchKernelGGL((k_key_hist<F>), dim3(hb), dim3(256), 0, st, f, n_units, state, pmasks[p], shifts[p],
+                               (uint32_t)(nbins[p] - 1), hist);
+            VQ_LAUNCHED("k_key_hist");
+            hipLaunchKernelGGL(k_sel_pick, dim3(1), dim3(256), 0, st, state, hist, shifts[p], nbins[p]);
+            VQ_LAUNCHED("k_sel_pick");
+        }
+    }
+    hipLaunchKernelGGL((k_key_row_count<F>), dim3((unsigned)M), dim3(kRowThreads), 0, st, f, upr, state, cgt, ceq);
+    VQ_LAUNCHED("k_key_row_count");
+    hipLaunchKernelGGL(k_sel_rows, dim3(1), dim3(kScanThreads), 0, st, state, M, cgt, ceq, take,
+                       static_cast<int32_t*>(nullptr));
+    VQ_LAUNCHED("k_sel_rows");
+    hipLaunchKernelGGL((k_key_mark<F>), dim3((unsigned)M), dim3(kRowThreads), 0, st, f, upr, d, state, take, mask);
+    VQ_LAUNCHED("k_key_mark");
+    return VQ_OK;
+}
+
 }  // namespace
 
 size_t ws_select(int64_t M, int64_t N)
@@ -299,7 +567,7 @@ vq_status select_launch(const float* W, const float* h, int64_t M, int64_t N, in
         const unsigned hb = (unsigned)std::min<int64_t>(kHistBlocks, grid_for(total, 256 * 16));
         for (int p = 0; p < 3; ++p) {
             hipLaunchKernelGGL(k_sel_hist, dim3(hb), dim3(256), 0, st, W, h, total, N, state, pmasks[p],
-                               shifts[p], hist);
+                               shifts[p], (uint32_t)(nbins[p] - 1), hist);
             VQ_LAUNCHED("k_sel_hist");
             hipLaunchKernelGGL(k_sel_pick, dim3(1), dim3(256), 0, st, state, hist, shifts[p], nbins[p]);
             VQ_LAUNCHED("k_sel_pick");
@@ -313,6 +581,39 @@ vq_status select_launch(const float* W, const float* h, int64_t M, int64_t N, in
     hipLaunchKernelGGL(k_sel_compact, dim3((unsigned)M), dim3(kRowThreads), 0, st, W, h, N, d, state,
                        take, row_ptr, nnz, col, val, mask);
     VQ_LAUNCHED("k_sel_compact");
+    return VQ_OK;
+}
+
+vq_status subvector_select_launch(const float* W, const float* h, int64_t M, int64_t N, int d, int64_t n_sel,
+                                  uint8_t* mask, void* ws, size_t ws_bytes, hipStream_t st)
+{
+    TimedRegion tr("select_subvectors", 0, st);
+    const KeySubvector f{W, h, N / d, d};
+    return key_select_launch(f, M, N / d, d, n_sel, mask, ws, ws_bytes, "vq_select_subvectors", st);
+}
+
+vq_status residual_select_launch(const float* W, const float* Wh, const float* h, int64_t M, int64_t N, int d,
+                                 int64_t n_sel, uint8_t* mask, void* ws, size_t ws_bytes, hipStream_t st)
+{
+    TimedRegion tr("select_residual", 0, st);
+    const KeyResidual f{W, Wh, h, mask, N / d, d};
+    return key_select_launch(f, M, N / d, d, n_sel, mask, ws, ws_bytes, "vq_select_residual", st);
+}
+
+vq_status mask_to_csr_launch(const float* W, const uint8_t* mask, int64_t M, int64_t N, int d, int64_t cap,
+                             int32_t* row_ptr, int32_t* col, float* val, void* ws, size_t ws_bytes, hipStream_t st)
+{
+    Carver cv(ws, ws_bytes);
+    int* cnt = cv.take<int>((size_t)M);
+    if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_mask_to_csr: workspace too small");
+    TimedRegion tr("mask_to_csr", 0, st);
+    hipLaunchKernelGGL(k_mask_row_count, dim3((unsigned)M), dim3(kRowThreads), 0, st, mask, N / d, d, cnt);
+    VQ_LAUNCHED("k_mask_row_count");
+    hipLaunchKernelGGL(k_mask_rows, dim3(1), dim3(kScanThreads), 0, st, M, cnt, row_ptr);
+    VQ_LAUNCHED("k_mask_rows");
+    hipLaunchKernelGGL(k_mask_compact, dim3((unsigned)M), dim3(kRowThreads), 0, st, W, mask, N, d, row_ptr, cap, col,
+                       val);
+    VQ_LAUNCHED("k_mask_compact");
     return VQ_OK;
 }
 

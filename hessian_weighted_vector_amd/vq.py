@@ -62,6 +62,9 @@ SIGNATURES = {
     "vq_objective": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P]),
     "vq_residual": (_I, [_P, _I64, _I64, _I, _P, _I, _P, _P, _P]),
     "vq_reconstruct": (_I, [_I64, _I64, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "vq_select_subvectors": (_I, [_P, _P, _I64, _I64, _I, _I64, _P, _P, _SZ, _P]),
+    "vq_select_residual": (_I, [_P, _P, _P, _I64, _I64, _I, _I64, _P, _P, _SZ, _P]),
+    "vq_mask_to_csr": (_I, [_P, _P, _I64, _I64, _I, _I64, _P, _P, _P, _P, _SZ, _P]),
     "vq_qgemv_workspace_bytes": (_SZ, [_I64, _I64, _I, _I64]),
     "vq_qgemv": (_I, [_I64, _I64, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _SZ,
                       _P]),
@@ -221,6 +224,33 @@ def reconstruct(M, N, d, C1, idx1, C2=None, idx2=None, rscale=None, cscale=None,
                                  0 if C2 is None else C2.shape[0], _ptr(idx2), _ptr(rscale), _ptr(cscale),
                                  _ptr(row_ptr), _ptr(col), _ptr(val), _ptr(W_hat), _stream()))
     return W_hat
+
+
+def select_subvectors(W, h, d, n_sel, mask, ws):
+    """OR every bit of the n_sel most salient sub-vectors into mask (in place)."""
+    M, N = W.shape
+    _check(load().vq_select_subvectors(_ptr(W), _ptr(h), M, N, d, int(n_sel), _ptr(mask), _ptr(ws), ws.numel(),
+                                       _stream()))
+    return mask
+
+
+def select_residual(W, W_hat, h, d, n_sel, mask, ws):
+    """OR the n_sel largest weighted residuals among clear positions into mask (in place)."""
+    M, N = W.shape
+    _check(load().vq_select_residual(_ptr(W), _ptr(W_hat), _ptr(h), M, N, d, int(n_sel), _ptr(mask), _ptr(ws),
+                                     ws.numel(), _stream()))
+    return mask
+
+
+def mask_to_csr(W, mask, d, nnz_cap, ws):
+    """(row_ptr, col, val) of the held positions; row_ptr[M] is the full count."""
+    M, N = W.shape
+    row_ptr = torch.empty(M + 1, dtype=torch.int32, device=W.device)
+    col = torch.empty(max(int(nnz_cap), 1), dtype=torch.int32, device=W.device)
+    val = torch.empty(max(int(nnz_cap), 1), dtype=torch.float32, device=W.device)
+    _check(load().vq_mask_to_csr(_ptr(W), _ptr(mask), M, N, d, int(nnz_cap), _ptr(row_ptr), _ptr(col), _ptr(val),
+                                 _ptr(ws), ws.numel(), _stream()))
+    return row_ptr, col, val
 
 
 def qgemv_workspace_bytes(M, N, d, B):

@@ -81,6 +81,35 @@ vq_status vq_sparse_select(const float* W, const float* h, int64_t M, int64_t N,
                            int64_t nnz, int32_t* row_ptr, int32_t* col, float* val,
                            uint8_t* mask, void* ws, size_t ws_bytes, void* stream);
 
+/* The unified sparse correction (SCVQ summary: outliers, highly salient
+ * sub-vectors and the largest quantization residuals are held together in
+ * one sparse correction matrix).  The mask (one byte per sub-vector, bit t =
+ * element t held exactly) is the correction set; these calls OR new positions
+ * into it and vq_mask_to_csr writes its CSR.  Keys below are float32 scores,
+ * which must be >= +0 (h >= 0); ties go to the smaller id.  Bitwise
+ * deterministic.  Workspace: vq_workspace_bytes for these sizes.
+ *
+ * Salient sub-vectors: S_s = sum over t in order of h_j * (w_j * w_j), each
+ * product and partial sum rounded to float32 (no fused multiply-add); the
+ * n_sel largest get every mask bit set.  0 <= n_sel <= n_sub. */
+vq_status vq_select_subvectors(const float* W, const float* h, int64_t M, int64_t N, int d,
+                               int64_t n_sel, uint8_t* mask, void* ws, size_t ws_bytes, void* stream);
+
+/* Largest quantization residuals: among positions whose mask bit is clear,
+ * r_ij = h_j * ((w_ij - what_ij) * (w_ij - what_ij)) in float32 (difference,
+ * square, scale); the min(n_sel, #clear) largest get their bit set.  W_hat is
+ * the quantized matrix [M x N] (vq_reconstruct without a sparse part). */
+vq_status vq_select_residual(const float* W, const float* W_hat, const float* h, int64_t M, int64_t N,
+                             int d, int64_t n_sel, uint8_t* mask, void* ws, size_t ws_bytes, void* stream);
+
+/* CSR of every position whose mask bit is set: row_ptr int32[M+1], col
+ * ascending within each row, val = the exact W value.  At most nnz_cap entries
+ * are written; row_ptr[M] is the full count (> nnz_cap: the CSR was cut).
+ * M*N <= 2^31-1. */
+vq_status vq_mask_to_csr(const float* W, const uint8_t* mask, int64_t M, int64_t N, int d,
+                         int64_t nnz_cap, int32_t* row_ptr, int32_t* col, float* val,
+                         void* ws, size_t ws_bytes, void* stream);
+
 /* Bi-normalization (SCVQ summary: rows and columns bi-normalized before
  * clustering), one pass of RMS scaling, rows first:
  *   r_i = sqrt(sum_j W_ij^2 / N) (fp64 sum; 1 if zero), Wt = W / r_i (fp32),

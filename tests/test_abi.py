@@ -63,6 +63,15 @@ def test_null_pointers_and_workspace():
     assert lib.vq_qgemv(8, 16, 8, FAKE, 4, FAKE, FAKE, 4, None, None, None, None, None, None,
                         FAKE, 1, FAKE + 64, None, 0, None) == vq.VQ_ERR_INVALID
     assert lib.vq_qgemv_workspace_bytes(8, 12, 8, 1) == 0
+    # unified correction: sizes and pointers
+    assert lib.vq_select_subvectors(FAKE, FAKE, 8, 16, 8, 17, FAKE, FAKE, 1 << 30, None) == vq.VQ_ERR_INVALID
+    assert "n_sel" in lib.vq_last_error().decode()
+    assert lib.vq_select_subvectors(FAKE, FAKE, 8, 16, 8, 4, FAKE, FAKE, 16, None) == vq.VQ_ERR_WORKSPACE
+    assert lib.vq_select_residual(FAKE, None, FAKE, 8, 16, 8, 4, FAKE, FAKE, 1 << 30, None) == vq.VQ_ERR_INVALID
+    assert lib.vq_select_residual(FAKE, FAKE, FAKE, 8, 16, 8, -1, FAKE, FAKE, 1 << 30, None) == vq.VQ_ERR_INVALID
+    assert lib.vq_mask_to_csr(FAKE, FAKE, 8, 16, 8, 5, FAKE, None, None, FAKE, 1 << 30, None) == vq.VQ_ERR_INVALID
+    assert lib.vq_mask_to_csr(FAKE, FAKE, 1 << 16, 1 << 16, 8, 5, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                              None) == vq.VQ_ERR_INVALID
     big_N = 8 * 14336 * 3          # three column slabs at one token
     need = lib.vq_qgemv_workspace_bytes(64, big_N, 8, 1)
     assert need >= 3 * 64 * 4
