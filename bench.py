@@ -247,6 +247,61 @@ def qgemv_bench(cfg, inp, run_oracle, reps=50):
     return out
 
 
+def correction_bench(cfg, inp, out, W, h, ws, run_oracle, reps=5):
+    """The unified sparse correction on the fit's output: 0.25% salient sub-vectors
+    and 0.5% largest weighted residuals ORed into the fit's mask, then the CSR.
+    HIP-event time per call against the algorithmic bytes (one read of each input,
+    the mask read and written, the CSR written); the oracle beside it on seeded
+    inputs of the same size."""
+    import numpy as np
+    import torch
+
+    from hessian_weighted_vector_amd import vq
+    M, N, d, n_sub = cfg.M, cfg.N, cfg.d, cfg.n_sub
+    n_sv, n_res = n_sub // 400, (M * N) // 200
+    cap = out["nnz"] + n_sv * d + n_res
+    What = vq.reconstruct(M, N, d, out["C1"], out["idx1"], out["C2"], out["idx2"], out.get("rscale"),
+                          out.get("cscale"))
+    torch.cuda.synchronize()
+    vq.timing_enable(True)
+    torch.cuda._sleep(int(2e7))
+    for _ in range(reps):
+        mask = out["mask"].clone()
+        vq.select_subvectors(W, h, d, n_sv, mask, ws)
+        vq.select_residual(W, What, h, d, n_res, mask, ws)
+        rp, _, _ = vq.mask_to_csr(W, mask, d, cap, ws)
+    torch.cuda.synchronize()
+    rec = {r[0]: r for r in vq.timing_records()}
+    vq.timing_enable(False)
+    held = int(rp[-1].item())
+    nb = {"select_subvectors": 4 * M * N + 4 * N + 2 * n_sub,
+          "select_residual": 8 * M * N + 4 * N + 2 * n_sub,
+          "mask_to_csr": n_sub + 12 * held + 4 * (M + 1)}
+    res = {"held_positions": held, "n_subvectors": n_sv, "n_residuals": n_res}
+    for k, b in nb.items():
+        t = rec[k][3] / rec[k][2]
+        res[k] = {"gpu_ms": round(t, 4), "algorithmic_MB": round(b / 1e6, 1),
+                  "GBs": round(b / (t * 1e-3) / 1e9, 1), "frac_hbm": round(b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if run_oracle:
+        import oracle
+        Wn, hn = inp["W"], inp["h"]
+        g = np.random.default_rng([cfg.cid, 96])
+        C1 = Wn.reshape(-1, d)[np.sort(g.choice(n_sub, 4096, replace=False))].copy()
+        Wq = oracle.reconstruct(M, N, d, C1, g.integers(0, 4096, n_sub).astype(np.uint16))
+        keep = np.ones((M, N), np.uint8)
+        t0 = time.perf_counter()
+        keep = oracle.select_subvectors(Wn, hn, d, n_sv, keep=keep)
+        t1 = time.perf_counter()
+        keep = oracle.select_residual(Wn, Wq, hn, n_res, keep=keep)
+        t2 = time.perf_counter()
+        oracle.keep_to_csr(Wn, keep)
+        t3 = time.perf_counter()
+        res["select_subvectors"]["oracle_ms"] = round((t1 - t0) * 1e3, 1)
+        res["select_residual"]["oracle_ms"] = round((t2 - t1) * 1e3, 1)
+        res["mask_to_csr"]["oracle_ms"] = round((t3 - t2) * 1e3, 1)
+    return res
+
+
 def cpu_baseline(cfg, inp, seconds):
     """The oracle's assignment on a bounded sample (float64 exhaustive search)."""
     import numpy as np
@@ -284,6 +339,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-qgemv", action="store_true", help="skip the fused dequantize-and-multiply rows")
+    ap.add_argument("--no-correction", action="store_true", help="skip the unified sparse correction rows")
     ap.add_argument("--breakdown", action="store_true", help="print per-step timings to stderr")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB three times (a plain "
@@ -385,6 +441,9 @@ def main():
     extra["rows"] = row_table(cfg, recs, nnz, oracle_ms)
     if not args.no_qgemv:
         extra["rows"]["NEXT1_qgemv"] = qgemv_bench(cfg, inp, not args.no_cpu_baseline)
+    if not args.no_correction:
+        extra["rows"]["NEXT3_unified_correction"] = correction_bench(cfg, inp, out, W, h, ws,
+                                                                     not args.no_cpu_baseline)
 
     line = {
         "metric": "sub-vectors assigned/s per Lloyd iter (G/s) + % FP32 peak; update/recon HBM GB/s",

@@ -368,7 +368,7 @@ vq_status vq_select_subvectors(const float* W, const float* h, int64_t M, int64_
     const int64_t n_sub = M * N / d;
     VQ_CHECK(W && h && mask, "vq_select_subvectors: null pointer");
     VQ_CHECK(n_sel >= 0 && n_sel <= n_sub, "vq_select_subvectors: n_sel must be in [0, n_sub]");
-    VQ_CHECK(M <= (int64_t)UINT32_MAX, "vq_select_subvectors: too many rows");
+    VQ_CHECK(n_sub <= (int64_t)UINT32_MAX, "vq_select_subvectors: too many sub-vectors");
     VQ_WS(ws && ws_bytes >= ws_select(M, N), "vq_select_subvectors: workspace too small");
     VQ_TRY(check_device());
     return subvector_select_launch(W, h, M, N, d, n_sel, mask, ws, ws_bytes, as_stream(stream));
@@ -380,7 +380,7 @@ vq_status vq_select_residual(const float* W, const float* W_hat, const float* h,
     VQ_TRY(check_shape(M, N, d));
     VQ_CHECK(W && W_hat && h && mask, "vq_select_residual: null pointer");
     VQ_CHECK(n_sel >= 0, "vq_select_residual: n_sel must be >= 0");
-    VQ_CHECK(M <= (int64_t)UINT32_MAX, "vq_select_residual: too many rows");
+    VQ_CHECK(M * N / d <= (int64_t)UINT32_MAX, "vq_select_residual: too many sub-vectors");
     VQ_WS(ws && ws_bytes >= ws_select(M, N), "vq_select_residual: workspace too small");
     VQ_TRY(check_device());
     return residual_select_launch(W, W_hat, h, M, N, d, n_sel, mask, ws, ws_bytes, as_stream(stream));

@@ -286,20 +286,36 @@ __global__ __launch_bounds__(kRowThreads) void k_sel_compact(
 struct KeySubvector {
     const float* W;
     const float* h;
-    int64_t nb;
+    uint32_t nb;
     int d;
+    bool vec;   // d == 8 with 16-byte aligned W and h
     static constexpr int kKeys = 1;
     __device__ int count() const { return 1; }
     __device__ void keys(int64_t s, uint32_t* k) const
     {
-        const float* w = W + s * d;
-        const float* hh = h + (s % nb) * d;
+        const uint32_t b = (uint32_t)s % nb;
         float acc = 0.0f;
-        for (int t = 0; t < d; ++t) {
-            const float x = w[t];
-            const float sq = x * x;
-            const float term = hh[t] * sq;
-            acc = acc + term;
+        if (vec) {
+            const float4* w4 = reinterpret_cast<const float4*>(W + s * 8);
+            const float4* h4 = reinterpret_cast<const float4*>(h + (size_t)b * 8);
+            const float4 wa = w4[0], wb = w4[1], ha = h4[0], hb = h4[1];
+            const float w[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+            const float hh[8] = {ha.x, ha.y, ha.z, ha.w, hb.x, hb.y, hb.z, hb.w};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float sq = w[t] * w[t];
+                const float term = hh[t] * sq;
+                acc = acc + term;
+            }
+        } else {
+            const float* w = W + s * d;
+            const float* hh = h + (size_t)b * d;
+            for (int t = 0; t < d; ++t) {
+                const float x = w[t];
+                const float sq = x * x;
+                const float term = hh[t] * sq;
+                acc = acc + term;
+            }
         }
         k[0] = __float_as_uint(acc) + 1u;
     }
@@ -312,16 +328,35 @@ struct KeyResidual {
     const float* Wh;
     const float* h;
     const uint8_t* mask;
-    int64_t nb;
+    uint32_t nb;
     int d;
+    bool vec;   // d == 8 with 16-byte aligned W, W_hat and h
     static constexpr int kKeys = 8;
     __device__ int count() const { return d; }
     __device__ void keys(int64_t s, uint32_t* k) const
     {
+        const uint32_t b = (uint32_t)s % nb;
+        const unsigned mb = mask[s];
+        if (vec) {
+            const float4* w4 = reinterpret_cast<const float4*>(W + s * 8);
+            const float4* q4 = reinterpret_cast<const float4*>(Wh + s * 8);
+            const float4* h4 = reinterpret_cast<const float4*>(h + (size_t)b * 8);
+            const float4 wa = w4[0], wb = w4[1], qa = q4[0], qb = q4[1], ha = h4[0], hb = h4[1];
+            const float w[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+            const float q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+            const float hh[8] = {ha.x, ha.y, ha.z, ha.w, hb.x, hb.y, hb.z, hb.w};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float r = w[t] - q[t];
+                const float sq = r * r;
+                const float sc = hh[t] * sq;
+                k[t] = ((mb >> t) & 1u) ? 0u : __float_as_uint(sc) + 1u;
+            }
+            return;
+        }
         const float* w = W + s * d;
         const float* wh = Wh + s * d;
-        const float* hh = h + (s % nb) * d;
-        const unsigned mb = mask[s];
+        const float* hh = h + (size_t)b * d;
         for (int t = 0; t < d; ++t) {
             const float r = w[t] - wh[t];
             const float sq = r * r;
@@ -588,7 +623,8 @@ vq_status subvector_select_launch(const float* W, const float* h, int64_t M, int
                                   uint8_t* mask, void* ws, size_t ws_bytes, hipStream_t st)
 {
     TimedRegion tr("select_subvectors", 0, st);
-    const KeySubvector f{W, h, N / d, d};
+    const bool vec = d == 8 && aligned16(W) && aligned16(h);
+    const KeySubvector f{W, h, (uint32_t)(N / d), d, vec};
     return key_select_launch(f, M, N / d, d, n_sel, mask, ws, ws_bytes, "vq_select_subvectors", st);
 }
 
@@ -596,7 +632,8 @@ vq_status residual_select_launch(const float* W, const float* Wh, const float* h
                                  int64_t n_sel, uint8_t* mask, void* ws, size_t ws_bytes, hipStream_t st)
 {
     TimedRegion tr("select_residual", 0, st);
-    const KeyResidual f{W, Wh, h, mask, N / d, d};
+    const bool vec = d == 8 && aligned16(W) && aligned16(Wh) && aligned16(h);
+    const KeyResidual f{W, Wh, h, mask, (uint32_t)(N / d), d, vec};
     return key_select_launch(f, M, N / d, d, n_sel, mask, ws, ws_bytes, "vq_select_residual", st);
 }
 
