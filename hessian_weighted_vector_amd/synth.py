@@ -13,7 +13,8 @@ Recipe (stand-in for real LLM weights and calibration activations):
     giving the few high-energy input channels that the VPTQ page ("Outlier
     Elimination") says show up as large Hessian diagonal entries.
   * h_j = sum_t X[t, j]^2 (accumulated in float64, stored fp32): the diagonal of
-    X^T X, i.e. the diagonal Hessian proxy of a linear layer's input.
+    X^T X, i.e. the diagonal Hessian proxy of a linear layer's input; the full
+    H = X^T X (make_hessian) for the second-order error propagation.
   * perm1, perm2: seeded permutations of the sub-vector ids (codebook seeding).
 Streams: rng([cid, s]) with s = 0 W, 1 X, 2 channel choice, 3 perm1, 4 perm2.
 """
@@ -38,12 +39,26 @@ def make_weight(cid, M, N, scale, nu, bf16):
     return round_bf16(w) if bf16 else w
 
 
-def make_hdiag(cid, N, T, n_ch, gain):
-    g = rng(cid, 1)
-    X = g.standard_normal((T, N))
+def make_activations(cid, N, T, n_ch, gain):
+    """The synthetic calibration activations X [T x N] (float64) and the
+    high-energy channels."""
+    X = rng(cid, 1).standard_normal((T, N))
     ch = rng(cid, 2).choice(N, n_ch, replace=False)
     X[:, ch] *= gain
-    return np.einsum("tj,tj->j", X, X).astype(np.float32), np.sort(ch)
+    return X, np.sort(ch)
+
+
+def make_hdiag(cid, N, T, n_ch, gain):
+    X, ch = make_activations(cid, N, T, n_ch, gain)
+    return np.einsum("tj,tj->j", X, X).astype(np.float32), ch
+
+
+def make_hessian(cid, N, T, n_ch, gain):
+    """The full Hessian proxy H = X^T X [N x N] of a linear layer's input
+    (float64 products and sums, stored fp32); its diagonal is make_hdiag's h
+    up to the order of the float64 sums."""
+    X, _ = make_activations(cid, N, T, n_ch, gain)
+    return (X.T @ X).astype(np.float32)
 
 
 def make_perm(cid, stream, n_sub):

@@ -49,6 +49,7 @@ _SIGS = {
     "orc_select_subvectors": (_I, [_P, _P, _LL, _LL, _I, _LL, _P]),
     "orc_select_residual": (_I, [_P, _P, _P, _LL, _LL, _LL, _P]),
     "orc_keep_to_csr": (_LL, [_P, _P, _LL, _LL, _P, _P, _P]),
+    "orc_vptq": (_I, [_P, _P, _LL, _LL, _I, _P, _I, _I, _P, _P, _P, _P]),
     "orc_qgemv": (_I, [_LL, _LL, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _LL, _P]),
     "orc_fit": (_I, [_P, _P, _LL, _LL, _I, _I, _I, _I, _I, _D, _I, _I, _P, _P, _I,
                      _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -74,7 +75,9 @@ def load(path=None):
 
 
 def _ptr(a):
-    return None if a is None else a.ctypes.data
+    # a ctypes pointer that holds a reference to the array, so that a
+    # temporary converted copy stays alive until the C call returns
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
 def _c(a, dtype):
@@ -229,6 +232,38 @@ def reconstruct(M, N, d, C1, idx1, C2=None, idx2=None, r=None, c=None,
                         _ptr(_c(row_ptr, np.int32)), _ptr(_c(col, np.int32)),
                         _ptr(_c(val, np.float32)), _ptr(What))
     return What
+
+
+def inverse_hessian_factor(H, damp=0.01):
+    """GPTQ's reading of the H^-1 that the error propagation reads: the upper
+    Cholesky factor U (U^T U = Hd^-1) of the inverse of the damped Hessian
+    Hd = H + damp * mean(diag H) * I, in float64 (numpy)."""
+    H = np.asarray(H, dtype=np.float64)
+    Hd = H + damp * float(np.mean(np.diag(H))) * np.eye(H.shape[0])
+    Hinv = np.linalg.inv(Hd)
+    Hinv = 0.5 * (Hinv + Hinv.T)
+    return np.linalg.cholesky(Hinv).T
+
+
+def vptq(W, U, V, C, B, lib=None):
+    """Algorithm 1 on W [M x N] with column sub-vectors of length V, codebook C
+    [K x V], block size B and the matrix U [N x N] (cast to float32, as the
+    library receives it).  Returns idx [N, M/V], What [M, N] (fp32), E [M, N]
+    (fp64) and gap [N, M/V]."""
+    lib = lib or load()
+    W = _c(W, np.float32)
+    M, N = W.shape
+    C = _c(C, np.float32)
+    nv = M // V
+    idx = np.zeros((N, nv), np.uint16)
+    What = np.zeros((M, N), np.float32)
+    E = np.zeros((M, N), np.float64)
+    gap = np.zeros((N, nv), np.float64)
+    rc = lib.orc_vptq(_ptr(W), _ptr(_c(U, np.float32)), M, N, V, _ptr(C), C.shape[0], int(B), _ptr(idx),
+                      _ptr(What), _ptr(E), _ptr(gap))
+    if rc:
+        raise MemoryError("orc_vptq: allocation failed")
+    return idx, What, E, gap
 
 
 def qgemv(M, N, d, C1, idx1, X, C2=None, idx2=None, r=None, c=None,

@@ -457,6 +457,68 @@ int orc_qgemv(long long M, long long N, int d,
 }
 
 /* ------------------------------------------------------------------ */
+/* Second-order error propagation with column sub-vectors (VPTQ page, "The
+ * Core Algorithm", Algorithm 1).  W [M x N] is quantized one column at a
+ * time, left to right, in blocks of B columns.  Column n is cut into M/V
+ * sub-vectors W[m:m+V, n]; each is replaced by its nearest codebook row under
+ * the plain Euclidean distance (fp64, lowest index on ties).  The column's
+ * error E[:,n] = (W[:,n] - What[:,n]) / U[n,n] is subtracted, scaled by
+ * U[n,j], from the block's later columns j; at the end of a block the
+ * block's errors are subtracted from every later column through
+ * U[s:s+B, s+B:].  U [N x N] is the matrix the algorithm reads where the page
+ * writes H^-1 (GPTQ's upper Cholesky factor of the inverse Hessian, or the
+ * inverse itself; the algorithm is the same).  The working copy of W is
+ * fp64.  Outputs: idx[n*(M/V) + v] (column n, sub-vector v), What [M x N],
+ * E [M x N] (fp64) and gap[n*(M/V) + v] = (second - best) / second, the
+ * relative margin of each decision (0 when second == 0). */
+int orc_vptq(const float* W, const float* U, long long M, long long N, int V, const float* C, int K,
+             int B, unsigned short* idx, float* What, double* E, double* gap)
+{
+    long long nv = M / V;
+    double* Wk = (double*)malloc(sizeof(double) * (size_t)(M * N));
+    if (!Wk) return 3;
+    for (long long e = 0; e < M * N; ++e) Wk[e] = (double)W[e];
+    for (long long s = 0; s < N; s += B) {
+        long long s_end = s + B < N ? s + B : N;
+        for (long long n = s; n < s_end; ++n) {
+#pragma omp parallel for schedule(static)
+            for (long long v = 0; v < nv; ++v) {
+                double best = INFINITY, second = INFINITY;
+                int arg = 0;
+                for (int k = 0; k < K; ++k) {
+                    double dist = 0.0;
+                    for (int t = 0; t < V; ++t) {
+                        double diff = Wk[(v * V + t) * N + n] - (double)C[(size_t)k * (size_t)V + (size_t)t];
+                        dist += diff * diff;
+                    }
+                    if (dist < best) { second = best; best = dist; arg = k; }
+                    else if (dist < second) second = dist;
+                }
+                idx[n * nv + v] = (unsigned short)arg;
+                gap[n * nv + v] = second > 0.0 ? (second - best) / second : 0.0;
+                for (int t = 0; t < V; ++t)
+                    What[(v * V + t) * N + n] = C[(size_t)arg * (size_t)V + (size_t)t];
+            }
+            double unn = (double)U[n * N + n];
+            for (long long m = 0; m < M; ++m) E[m * N + n] = (Wk[m * N + n] - (double)What[m * N + n]) / unn;
+            for (long long j = n + 1; j < s_end; ++j) {
+                double unj = (double)U[n * N + j];
+                for (long long m = 0; m < M; ++m) Wk[m * N + j] -= E[m * N + n] * unj;
+            }
+        }
+        for (long long m = 0; m < M; ++m) {
+            for (long long j = s_end; j < N; ++j) {
+                double acc = 0.0;
+                for (long long n = s; n < s_end; ++n) acc += E[m * N + n] * (double)U[n * N + j];
+                Wk[m * N + j] -= acc;
+            }
+        }
+    }
+    free(Wk);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* One stage of weighted K-means (Lloyd): T times (assign, update), then a
  * final assign, so the returned indices are the argmin for the returned
  * codebook.  J[0..T] receives the objective of each (codebook, assignment)

@@ -454,6 +454,70 @@ def pin_keep_to_csr_matches_nonzero(lib):
     assert np.array_equal(rp, np.concatenate([[0], np.cumsum((keep == 0).sum(1))]).astype(np.int32))
 
 
+def _vptq_case(seed, M=16, N=24, V=4, K=10, T=40):
+    g = np.random.default_rng([17, seed])
+    W = (0.05 * g.standard_t(4.0, size=(M, N))).astype(np.float32)
+    X = g.standard_normal((T, N))
+    X[:, g.choice(N, 2, replace=False)] *= 8.0
+    H = X.T @ X
+    C = (0.05 * g.standard_normal((K, V))).astype(np.float32)
+    U = O.inverse_hessian_factor(H).astype(np.float32)
+    return W, H, U, C
+
+
+def pin_vptq_error_factorization(lib):
+    """Algorithm 1's updates leave W - What = E U exactly (each column's final
+    error is its own scaled error plus everything pushed into it from the left),
+    for any upper-triangular U; and with GPTQ's U the OBS objective
+    tr(dW H dW^T) is ||E||^2 up to the damping (here within 5%)."""
+    W, H, U, C = _vptq_case(1)
+    for B in (5, 24):
+        idx, What, E, gap = O.vptq(W, U, 4, C, B, lib=lib)
+        dW = W.astype(np.float64) - What.astype(np.float64)
+        assert np.allclose(dW, E @ U.astype(np.float64), rtol=1e-10, atol=1e-12)
+        obj = float(np.trace(dW @ H @ dW.T))
+        assert abs(obj - float((E * E).sum())) <= 0.05 * obj
+
+
+def pin_vptq_quantizes_updated_columns(lib):
+    """Each column's indices are scipy's Euclidean nearest codebook rows of that
+    column as updated by every error to its left: W[:,n] - sum_{n'<n} E[:,n'] U[n',n]."""
+    W, H, U, C = _vptq_case(2)
+    V = 4
+    idx, What, E, gap = O.vptq(W, U, V, C, 7, lib=lib)
+    M, N = W.shape
+    Ud = U.astype(np.float64)
+    for n in range(N):
+        wn = W[:, n].astype(np.float64) - E[:, :n] @ Ud[:n, n]
+        ref, _ = scvq.vq(wn.reshape(M // V, V), C.astype(np.float64))
+        ok = gap[n] > 1e-9
+        assert np.array_equal(idx[n][ok], ref[ok].astype(np.uint16))
+        assert np.array_equal(What[:, n], C[idx[n]].ravel())
+
+
+def pin_vptq_block_size_invariance(lib):
+    """Deferring the pushes to columns past the block (the block-boundary update)
+    changes nothing in exact arithmetic: B = 1, 3 and N agree."""
+    W, H, U, C = _vptq_case(3)
+    runs = [O.vptq(W, U, 4, C, B, lib=lib) for B in (1, 3, W.shape[1])]
+    for idx, What, E, gap in runs[1:]:
+        ok = (gap > 1e-9) & (runs[0][3] > 1e-9)
+        assert np.array_equal(idx[ok], runs[0][0][ok])
+        assert np.allclose(E, runs[0][2], rtol=1e-9, atol=1e-12)
+
+
+def pin_vptq_identity_is_plain_vq(lib):
+    """With U = I there is no coupling: every column is plain Euclidean VQ of the
+    original weights and E = W - What."""
+    W, H, U, C = _vptq_case(4)
+    M, N = W.shape
+    idx, What, E, gap = O.vptq(W, np.eye(N, dtype=np.float32), 4, C, 5, lib=lib)
+    for n in range(N):
+        ref, _ = scvq.vq(W[:, n].astype(np.float64).reshape(M // 4, 4), C.astype(np.float64))
+        assert np.array_equal(idx[n], ref.astype(np.uint16))
+    assert np.array_equal(E, W.astype(np.float64) - What.astype(np.float64))
+
+
 def _qg_case(seed, M=6, N=24, d=4, K1=7, K2=3, B=3, pow2_scales=False):
     g = np.random.default_rng([11, seed])
     nb = N // d

@@ -65,6 +65,14 @@ MUTANTS = {
                                 "    for (long long i = 0;",
                                 "int* row_ptr, int* col, float* val)\n{\n    long long pos = 0;\n    row_ptr[0] = 0;\n"
                                 "    for (long long i = 1;")],
+    "vptq_error_not_scaled": [("E[m * N + n] = (Wk[m * N + n] - (double)What[m * N + n]) / unn;",
+                               "E[m * N + n] = (Wk[m * N + n] - (double)What[m * N + n]);")],
+    "vptq_boundary_skips_column": [("for (long long j = s_end; j < N; ++j) {\n                double acc",
+                                    "for (long long j = s_end + 1; j < N; ++j) {\n                double acc")],
+    "vptq_inblock_sign": [("Wk[m * N + j] -= E[m * N + n] * unj;", "Wk[m * N + j] += E[m * N + n] * unj;")],
+    "vptq_quantizes_original": [("double diff = Wk[(v * V + t) * N + n] -", "double diff = (double)W[(v * V + t) * N + n] -")],
+    "vptq_inblock_reaches_past_block": [("for (long long j = n + 1; j < s_end; ++j) {\n                double unj",
+                                         "for (long long j = n + 1; j < N; ++j) {\n                double unj")],
     "qgemv_wrong_row": [("acc += (double)What[i * N + j] * (double)x[j];",
                          "acc += (double)What[((i + 1) % M) * N + j] * (double)x[j];")],
     "qgemv_float_accumulation": [("            double acc = 0.0;\n            for (long long j = 0; j < N; ++j) acc +=",
