@@ -470,7 +470,7 @@ int orc_qgemv(long long M, long long N, int d,
  * inverse itself; the algorithm is the same).  The working copy of W is
  * fp64.  Outputs: idx[n*(M/V) + v] (column n, sub-vector v), What [M x N],
  * E [M x N] (fp64) and gap[n*(M/V) + v] = (second - best) / second, the
- * relative margin of each decision (0 when second == 0). */
+ * relative margin of each decision (0 when second == 0, 1 when K == 1). */
 int orc_vptq(const float* W, const float* U, long long M, long long N, int V, const float* C, int K,
              int B, unsigned short* idx, float* What, double* E, double* gap)
 {
@@ -495,7 +495,7 @@ int orc_vptq(const float* W, const float* U, long long M, long long N, int V, co
                     else if (dist < second) second = dist;
                 }
                 idx[n * nv + v] = (unsigned short)arg;
-                gap[n * nv + v] = second > 0.0 ? (second - best) / second : 0.0;
+                gap[n * nv + v] = isinf(second) ? 1.0 : (second > 0.0 ? (second - best) / second : 0.0);
                 for (int t = 0; t < V; ++t)
                     What[(v * V + t) * N + n] = C[(size_t)arg * (size_t)V + (size_t)t];
             }
