@@ -52,6 +52,8 @@ vq_status residual_select_launch(const float*, const float*, const float*, int64
                                  uint8_t*, void*, size_t, hipStream_t);
 vq_status mask_to_csr_launch(const float*, const uint8_t*, int64_t, int64_t, int, int64_t, int32_t*, int32_t*,
                              float*, void*, size_t, hipStream_t);
+vq_status vptq_launch(const float*, const float*, int64_t, int64_t, int, const float*, int, int, uint16_t*, float*,
+                      float*, void*, size_t, hipStream_t);
 vq_status qgemv_launch(int64_t, int64_t, int, const float*, int, const uint16_t*, const float*, int,
                        const uint16_t*, const float*, const float*, const int32_t*, const int32_t*,
                        const float*, const float*, int64_t, float*, void*, size_t, hipStream_t);
@@ -397,6 +399,28 @@ vq_status vq_mask_to_csr(const float* W, const uint8_t* mask, int64_t M, int64_t
     VQ_WS(ws && ws_bytes >= ws_select(M, N), "vq_mask_to_csr: workspace too small");
     VQ_TRY(check_device());
     return mask_to_csr_launch(W, mask, M, N, d, nnz_cap, row_ptr, col, val, ws, ws_bytes, as_stream(stream));
+}
+
+size_t vq_vptq_workspace_bytes(int64_t M, int64_t N, int V)
+{
+    if (M <= 0 || N <= 0 || V < 1 || V > 8 || M % V) return 0;
+    return ws_vptq(M, N, V);
+}
+
+vq_status vq_vptq(const float* W, const float* U, int64_t M, int64_t N, int V, const float* C, int K, int B,
+                  uint16_t* idx, float* W_hat, float* E, void* ws, size_t ws_bytes, void* stream)
+{
+    VQ_CHECK(M > 0 && N > 0, "vq_vptq: M and N must be positive");
+    VQ_CHECK(V >= 1 && V <= 8 && M % V == 0, "vq_vptq: V must be in [1, 8] and divide M");
+    VQ_CHECK(K >= 1 && K <= 65536, "vq_vptq: K must be in [1, 65536]");
+    VQ_CHECK(B >= 1 && B <= 128, "vq_vptq: B must be in [1, 128]");
+    VQ_CHECK(M <= (int64_t)32 * 65535 && N <= (int64_t)32 * 65535 && M / V <= (int64_t)INT32_MAX,
+             "vq_vptq: matrix too large");
+    VQ_CHECK(W && U && C && idx && W_hat, "vq_vptq: null pointer");
+    VQ_CHECK(W_hat != W && (E == nullptr || (E != W && E != W_hat)), "vq_vptq: outputs may not alias");
+    VQ_WS(ws && ws_bytes >= ws_vptq(M, N, V), "vq_vptq: workspace too small");
+    VQ_TRY(check_device());
+    return vptq_launch(W, U, M, N, V, C, K, B, idx, W_hat, E, ws, ws_bytes, as_stream(stream));
 }
 
 size_t vq_qgemv_workspace_bytes(int64_t M, int64_t N, int d, int64_t B)

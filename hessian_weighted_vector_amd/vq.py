@@ -65,6 +65,8 @@ SIGNATURES = {
     "vq_select_subvectors": (_I, [_P, _P, _I64, _I64, _I, _I64, _P, _P, _SZ, _P]),
     "vq_select_residual": (_I, [_P, _P, _P, _I64, _I64, _I, _I64, _P, _P, _SZ, _P]),
     "vq_mask_to_csr": (_I, [_P, _P, _I64, _I64, _I, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "vq_vptq_workspace_bytes": (_SZ, [_I64, _I64, _I]),
+    "vq_vptq": (_I, [_P, _P, _I64, _I64, _I, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "vq_qgemv_workspace_bytes": (_SZ, [_I64, _I64, _I, _I64]),
     "vq_qgemv": (_I, [_I64, _I64, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _SZ,
                       _P]),
@@ -251,6 +253,21 @@ def mask_to_csr(W, mask, d, nnz_cap, ws):
     _check(load().vq_mask_to_csr(_ptr(W), _ptr(mask), M, N, d, int(nnz_cap), _ptr(row_ptr), _ptr(col), _ptr(val),
                                  _ptr(ws), ws.numel(), _stream()))
     return row_ptr, col, val
+
+
+def vptq(W, U, V, C, B=128, want_E=False, ws=None):
+    """Algorithm 1 (column sub-vectors of length V): returns idx [N, M/V], W_hat [M, N]
+    and, with want_E, E [M, N]."""
+    M, N = W.shape
+    dev = W.device
+    idx = torch.empty((N, M // V), dtype=torch.uint16, device=dev)
+    W_hat = torch.empty_like(W)
+    E = torch.empty_like(W) if want_E else None
+    if ws is None:
+        ws = torch.empty(max(int(load().vq_vptq_workspace_bytes(M, N, V)), 256), dtype=torch.uint8, device=dev)
+    _check(load().vq_vptq(_ptr(W), _ptr(U), M, N, V, _ptr(C), C.shape[0], int(B), _ptr(idx), _ptr(W_hat),
+                          _ptr(E), _ptr(ws), ws.numel(), _stream()))
+    return idx, W_hat, E
 
 
 def qgemv_workspace_bytes(M, N, d, B):

@@ -212,6 +212,26 @@ vq_status vq_qgemv(int64_t M, int64_t N, int d, const float* C1, int K1, const u
                    const int32_t* row_ptr, const int32_t* col, const float* val,
                    const float* X, int64_t B, float* Y, void* ws, size_t ws_bytes, void* stream);
 
+/* Second-order error propagation with column sub-vectors (VPTQ page, "The
+ * Core Algorithm", Algorithm 1).  Columns of W [M x N] are quantized left to
+ * right in blocks of B: each of a column's M/V sub-vectors W[m:m+V, n] takes
+ * its nearest row of C [K x V] under the plain Euclidean distance (float32,
+ * direct form; the lowest index among equal distances); the column's error
+ * E[:,n] = (W[:,n] - What[:,n]) / U[n,n] is subtracted, times U[n,j], from the
+ * block's later columns j, and at the block's end E[:, s:s+B] U[s:s+B, s+B:]
+ * is subtracted from every later column.  U [N x N] row-major is the matrix
+ * the algorithm reads where the page writes H^-1; only its upper triangle is
+ * read (GPTQ's upper Cholesky factor of the damped inverse Hessian, or the
+ * inverse itself).  W is not modified.  Outputs: idx uint16 [N x M/V]
+ * (idx[n*(M/V) + v] for sub-vector v of column n), W_hat [M x N] (codebook
+ * rows), E [M x N] (nullable).  Arithmetic: float32 state; the block update
+ * runs on the float32 matrix cores.  1 <= V <= 8 with M % V == 0;
+ * 1 <= K <= 65536; 1 <= B <= 128.  Bitwise reproducible.  Workspace:
+ * vq_vptq_workspace_bytes(M, N, V) (three transposed M x N copies). */
+size_t vq_vptq_workspace_bytes(int64_t M, int64_t N, int V);
+vq_status vq_vptq(const float* W, const float* U, int64_t M, int64_t N, int V, const float* C, int K, int B,
+                  uint16_t* idx, float* W_hat, float* E, void* ws, size_t ws_bytes, void* stream);
+
 /* The whole per-matrix pipeline (HAS-VQ abstract; VPTQ page, "End-to-End
  * Quantization Pipeline": main codebook, then a residual codebook on
  * W - W_hat):

@@ -63,6 +63,14 @@ def test_null_pointers_and_workspace():
     assert lib.vq_qgemv(8, 16, 8, FAKE, 4, FAKE, FAKE, 4, None, None, None, None, None, None,
                         FAKE, 1, FAKE + 64, None, 0, None) == vq.VQ_ERR_INVALID
     assert lib.vq_qgemv_workspace_bytes(8, 12, 8, 1) == 0
+    # Algorithm 1: sizes
+    assert lib.vq_vptq(FAKE, FAKE, 10, 16, 4, FAKE, 8, 16, FAKE, FAKE + 64, None, FAKE, 1 << 30,
+                       None) == vq.VQ_ERR_INVALID          # V does not divide M
+    assert lib.vq_vptq(FAKE, FAKE, 16, 16, 4, FAKE, 8, 129, FAKE, FAKE + 64, None, FAKE, 1 << 30,
+                       None) == vq.VQ_ERR_INVALID          # B > 128
+    assert lib.vq_vptq(FAKE, FAKE, 16, 16, 4, FAKE, 8, 16, FAKE, FAKE + 64, None, FAKE, 16,
+                       None) == vq.VQ_ERR_WORKSPACE
+    assert lib.vq_vptq_workspace_bytes(16, 16, 4) >= 3 * 16 * 16 * 4
     # unified correction: sizes and pointers
     assert lib.vq_select_subvectors(FAKE, FAKE, 8, 16, 8, 17, FAKE, FAKE, 1 << 30, None) == vq.VQ_ERR_INVALID
     assert "n_sel" in lib.vq_last_error().decode()

@@ -1,0 +1,145 @@
+"""Parity of Algorithm 1 (second-order error propagation, column sub-vectors)
+with the oracle (GPU).
+
+The oracle keeps the working matrix in float64, the library in float32, so the
+two trajectories agree until a decision whose best and second-best distances
+are within the float32 state's error of each other; after such a decision the
+two legitimately part for that row group (V rows share every later decision).
+The bar, per group of V rows and column by column:
+  * indices equal, until the first disagreement, which must sit on an oracle
+    decision with relative margin (second - best) / second < 1e-3 (float32
+    state error is about 1e-5 relative); the group is not compared after it;
+  * on every column compared: What equal bit for bit (codebook rows) and
+    |E - E_ref| <= 1e-4 * max |E_ref[:, n]| + 1e-30.
+At most 1% of groups may part.  Cases cover V = 8 (vector path) and V = 4, 6
+(scalar path), K below, at and across 256-centroid chunks, K = 1, blocks that
+do not divide N, B > N, B = 1, U = I, and the 4096 x 11008 workload on eight
+sampled row groups.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import dev, host
+from hessian_weighted_vector_amd import configs, synth, vq
+
+pytestmark = pytest.mark.gpu
+
+GAP_TOL = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def make_case(seed, M, N, V, K, T=64, eye=False):
+    g = np.random.default_rng([61, seed])
+    W = (0.02 * g.standard_t(4.0, size=(M, N))).astype(np.float32)
+    X = g.standard_normal((T, N))
+    X[:, g.choice(N, max(1, N // 20), replace=False)] *= 10.0
+    U = np.eye(N, dtype=np.float32) if eye else oracle.inverse_hessian_factor(X.T @ X).astype(np.float32)
+    cols = W.T.reshape(-1, V)
+    if K <= cols.shape[0]:
+        C = cols[np.sort(g.choice(cols.shape[0], K, replace=False))].copy()
+    else:
+        C = (0.02 * g.standard_normal((K, V))).astype(np.float32)
+    return W, U, C
+
+
+def compare(W, U, C, V, B, idx_g, What_g, E_g, rows=None):
+    """Walks each row group against the oracle run on the same rows; returns
+    (groups compared, groups parted)."""
+    Wr = W if rows is None else W[rows]
+    idx_o, What_o, E_o, gap_o = oracle.vptq(Wr, U, V, C, B)
+    M, N = Wr.shape
+    nv = M // V
+    parted = 0
+    for v in range(nv):
+        rs = slice(v * V, v * V + V)
+        diff = np.nonzero(idx_g[:, v] != idx_o[:, v])[0]
+        upto = N
+        if diff.size:
+            n0 = int(diff[0])
+            assert gap_o[n0, v] < GAP_TOL, ("group %d parts at column %d with margin %.3g"
+                                            % (v, n0, gap_o[n0, v]))
+            parted += 1
+            upto = n0
+        if upto == 0:
+            continue
+        assert np.array_equal(What_g[rs, :upto].view(np.uint32), What_o[rs, :upto].view(np.uint32))
+        if E_g is not None:
+            scale = np.abs(E_o[:, :upto]).max(axis=0)
+            err = np.abs(E_g[rs, :upto].astype(np.float64) - E_o[rs, :upto])
+            assert np.all(err <= 1e-4 * scale[None, :] + 1e-30), float((err / (scale + 1e-30)).max())
+    return nv, parted
+
+
+CASES = [
+    # (seed, M, N, V, K, B)
+    (1, 64, 96, 8, 32, 16),
+    (2, 60, 50, 4, 100, 7),      # scalar path, blocks that do not divide N
+    (3, 32, 40, 8, 700, 128),    # three centroid chunks, one block (B > N)
+    (4, 16, 24, 8, 1, 5),        # K = 1
+    (5, 96, 300, 6, 64, 128),    # V = 6, three blocks, the last ragged
+    (6, 40, 20, 8, 256, 1),      # B = 1, exactly one centroid chunk
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["v%d" % c[0] for c in CASES])
+def test_vptq_matches_oracle(case):
+    seed, M, N, V, K, B = case
+    say("vptq", case)
+    W, U, C = make_case(seed, M, N, V, K)
+    idx, What, E = vq.vptq(dev(W), dev(U), V, dev(C), B, want_E=True)
+    nv, parted = compare(W, U, C, V, B, host(idx).reshape(N, M // V), host(What), host(E))
+    say("  groups parted: %d of %d" % (parted, nv))
+    assert parted <= max(1, nv // 100)
+
+
+def test_vptq_identity_is_plain_column_vq():
+    """U = I: no coupling, each column's sub-vectors take their Euclidean nearest
+    codebook rows and E = W - What exactly."""
+    say("vptq U = I")
+    W, U, C = make_case(7, 48, 33, 8, 50, eye=True)
+    idx, What, E = vq.vptq(dev(W), dev(U), 8, dev(C), 10, want_E=True)
+    nv, parted = compare(W, U, C, 8, 10, host(idx).reshape(33, 6), host(What), host(E))
+    assert parted == 0
+    assert np.array_equal(host(E), W - host(What))
+
+
+def test_vptq_reproducible():
+    say("vptq reproducibility")
+    W, U, C = make_case(8, 64, 200, 8, 300)
+    a = [vq.vptq(dev(W), dev(U), 8, dev(C), 32, want_E=True) for _ in range(2)]
+    for x, y in zip(a[0], a[1]):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.uint16 else x.view(torch.int32),
+                           y.view(torch.int16) if y.dtype == torch.uint16 else y.view(torch.int32))
+
+
+def test_vptq_fullsize_sampled_rows():
+    """4096 x 11008 with K = 65536, V = 8, B = 128, H = X^T X of the workload's
+    activations, GPTQ's U; eight row groups (64 rows) against the oracle run on
+    those rows (groups of V rows evolve independently given U and C)."""
+    cfg = configs.get(4)
+    M, N, V, K, B = cfg.M, cfg.N, 8, cfg.K1, 128
+    say("vptq full size: hessian")
+    W = synth.make_weight(cfg.cid, M, N, cfg.scale, cfg.nu, cfg.bf16)
+    H = synth.make_hessian(cfg.cid, N, cfg.T, cfg.n_ch, cfg.ch_gain)
+    U = oracle.inverse_hessian_factor(H).astype(np.float32)
+    del H
+    g = np.random.default_rng([cfg.cid, 97])
+    cols = W.T.reshape(-1, V)
+    C = cols[np.sort(g.choice(cols.shape[0], K, replace=False))].copy()
+    say("vptq full size: GPU")
+    idx, What, E = vq.vptq(dev(W), dev(U), V, dev(C), B, want_E=True)
+    idx, What, E = host(idx).reshape(N, M // V), host(What), host(E)
+    groups = np.sort(g.choice(M // V, 8, replace=False))
+    rows = np.concatenate([np.arange(q * V, q * V + V) for q in groups])
+    say("vptq full size: oracle on groups", groups)
+    nv, parted = compare(W, U, C, V, B, idx[:, groups], What[rows], E[rows], rows=rows)
+    say("  groups parted: %d of %d" % (parted, nv))
+    assert parted <= 1
