@@ -54,6 +54,7 @@ vq_status mask_to_csr_launch(const float*, const uint8_t*, int64_t, int64_t, int
                              float*, void*, size_t, hipStream_t);
 vq_status vptq_launch(const float*, const float*, int64_t, int64_t, int, const float*, int, int, uint16_t*, float*,
                       float*, void*, size_t, hipStream_t);
+vq_status hfactor_launch(const float*, int64_t, double, float*, void*, size_t, hipStream_t);
 vq_status qgemv_launch(int64_t, int64_t, int, const float*, int, const uint16_t*, const float*, int,
                        const uint16_t*, const float*, const float*, const int32_t*, const int32_t*,
                        const float*, const float*, int64_t, float*, void*, size_t, hipStream_t);
@@ -399,6 +400,23 @@ vq_status vq_mask_to_csr(const float* W, const uint8_t* mask, int64_t M, int64_t
     VQ_WS(ws && ws_bytes >= ws_select(M, N), "vq_mask_to_csr: workspace too small");
     VQ_TRY(check_device());
     return mask_to_csr_launch(W, mask, M, N, d, nnz_cap, row_ptr, col, val, ws, ws_bytes, as_stream(stream));
+}
+
+size_t vq_hessian_factor_workspace_bytes(int64_t N)
+{
+    if (N <= 0) return 0;
+    return ws_hfactor(N);
+}
+
+vq_status vq_hessian_factor(const float* H, int64_t N, double damp, float* U, void* ws, size_t ws_bytes,
+                            void* stream)
+{
+    VQ_CHECK(N > 0 && N <= 65536, "vq_hessian_factor: N must be in [1, 65536]");
+    VQ_CHECK(damp >= 0.0 && damp < 1e300, "vq_hessian_factor: damp must be finite and >= 0");
+    VQ_CHECK(H && U && (const void*)H != (const void*)U, "vq_hessian_factor: null or aliased pointer");
+    VQ_WS(ws && ws_bytes >= ws_hfactor(N), "vq_hessian_factor: workspace too small");
+    VQ_TRY(check_device());
+    return hfactor_launch(H, N, damp, U, ws, ws_bytes, as_stream(stream));
 }
 
 size_t vq_vptq_workspace_bytes(int64_t M, int64_t N, int V)

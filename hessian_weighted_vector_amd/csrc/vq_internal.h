@@ -64,6 +64,7 @@ size_t ws_binorm(int64_t M, int64_t N);
 size_t ws_init(int64_t n_sub, int K, int d);
 size_t ws_qgemv(int64_t M, int64_t N, int d, int64_t B);
 size_t ws_vptq(int64_t M, int64_t N, int V);
+size_t ws_hfactor(int64_t N);
 
 // Argument checks shared by the entry points.
 vq_status check_shape(int64_t M, int64_t N, int d);

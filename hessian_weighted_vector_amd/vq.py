@@ -65,6 +65,8 @@ SIGNATURES = {
     "vq_select_subvectors": (_I, [_P, _P, _I64, _I64, _I, _I64, _P, _P, _SZ, _P]),
     "vq_select_residual": (_I, [_P, _P, _P, _I64, _I64, _I, _I64, _P, _P, _SZ, _P]),
     "vq_mask_to_csr": (_I, [_P, _P, _I64, _I64, _I, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "vq_hessian_factor_workspace_bytes": (_SZ, [_I64]),
+    "vq_hessian_factor": (_I, [_P, _I64, _D, _P, _P, _SZ, _P]),
     "vq_vptq_workspace_bytes": (_SZ, [_I64, _I64, _I]),
     "vq_vptq": (_I, [_P, _P, _I64, _I64, _I, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "vq_qgemv_workspace_bytes": (_SZ, [_I64, _I64, _I, _I64]),
@@ -253,6 +255,17 @@ def mask_to_csr(W, mask, d, nnz_cap, ws):
     _check(load().vq_mask_to_csr(_ptr(W), _ptr(mask), M, N, d, int(nnz_cap), _ptr(row_ptr), _ptr(col), _ptr(val),
                                  _ptr(ws), ws.numel(), _stream()))
     return row_ptr, col, val
+
+
+def hessian_factor(H, damp=0.01, ws=None):
+    """U [N, N] (float32, upper): U^T U = (H + damp mean(diag H) I)^-1."""
+    N = H.shape[0]
+    U = torch.empty_like(H)
+    if ws is None:
+        ws = torch.empty(max(int(load().vq_hessian_factor_workspace_bytes(N)), 256), dtype=torch.uint8,
+                         device=H.device)
+    _check(load().vq_hessian_factor(_ptr(H), N, float(damp), _ptr(U), _ptr(ws), ws.numel(), _stream()))
+    return U
 
 
 def vptq(W, U, V, C, B=128, want_E=False, ws=None):

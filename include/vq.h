@@ -212,6 +212,19 @@ vq_status vq_qgemv(int64_t M, int64_t N, int d, const float* C1, int K1, const u
                    const int32_t* row_ptr, const int32_t* col, const float* val,
                    const float* X, int64_t B, float* Y, void* ws, size_t ws_bytes, void* stream);
 
+/* The matrix the second-order error propagation below reads where the VPTQ
+ * page ("The Core Algorithm") writes H^-1, in GPTQ's form (the page says the
+ * technique is inherited from it): U [N x N], upper triangular with positive
+ * diagonal, U^T U = (H + damp * mean(diag H) * I)^-1.  Computed in float64 as
+ * U = P L^-1 P, where P reverses the order and L is the Cholesky factor of
+ * P (H + damp * mean(diag H) * I) P; stored float32 with the strict lower
+ * triangle zero.  H [N x N] float32 symmetric (read in full); the damped
+ * matrix must be positive definite (else U holds NaN).  Workspace:
+ * vq_hessian_factor_workspace_bytes(N) (two N x N float64 matrices). */
+size_t vq_hessian_factor_workspace_bytes(int64_t N);
+vq_status vq_hessian_factor(const float* H, int64_t N, double damp, float* U, void* ws, size_t ws_bytes,
+                            void* stream);
+
 /* Second-order error propagation with column sub-vectors (VPTQ page, "The
  * Core Algorithm", Algorithm 1).  Columns of W [M x N] are quantized left to
  * right in blocks of B: each of a column's M/V sub-vectors W[m:m+V, n] takes

@@ -465,6 +465,21 @@ def _vptq_case(seed, M=16, N=24, V=4, K=10, T=40):
     return W, H, U, C
 
 
+def pin_inverse_hessian_factor_properties(lib):
+    """U is upper triangular with a positive diagonal and U^T U (H + damp mean(diag H) I) = I;
+    for a diagonal H it is diag(1 / sqrt(h + damp mean h))."""
+    g = np.random.default_rng(23)
+    X = g.standard_normal((30, 12))
+    H = X.T @ X
+    U = O.inverse_hessian_factor(H, damp=0.01)
+    Hd = H + 0.01 * np.mean(np.diag(H)) * np.eye(12)
+    assert np.allclose(np.tril(U, -1), 0.0) and np.all(np.diag(U) > 0)
+    assert np.allclose(U.T @ U @ Hd, np.eye(12), atol=1e-10)
+    h = g.uniform(1.0, 3.0, 7)
+    U2 = O.inverse_hessian_factor(np.diag(h), damp=0.1)
+    assert np.allclose(U2, np.diag(1.0 / np.sqrt(h + 0.1 * h.mean())), rtol=1e-14)
+
+
 def pin_vptq_error_factorization(lib):
     """Algorithm 1's updates leave W - What = E U exactly (each column's final
     error is its own scaled error plus everything pushed into it from the left),

@@ -63,6 +63,11 @@ def test_null_pointers_and_workspace():
     assert lib.vq_qgemv(8, 16, 8, FAKE, 4, FAKE, FAKE, 4, None, None, None, None, None, None,
                         FAKE, 1, FAKE + 64, None, 0, None) == vq.VQ_ERR_INVALID
     assert lib.vq_qgemv_workspace_bytes(8, 12, 8, 1) == 0
+    # inverse-Hessian factor
+    assert lib.vq_hessian_factor(FAKE, 0, 0.01, FAKE + 64, FAKE, 1 << 30, None) == vq.VQ_ERR_INVALID
+    assert lib.vq_hessian_factor(FAKE, 8, -1.0, FAKE + 64, FAKE, 1 << 30, None) == vq.VQ_ERR_INVALID
+    assert lib.vq_hessian_factor(FAKE, 8, 0.01, FAKE, FAKE, 1 << 30, None) == vq.VQ_ERR_INVALID
+    assert lib.vq_hessian_factor(FAKE, 8, 0.01, FAKE + 64, FAKE, 16, None) == vq.VQ_ERR_WORKSPACE
     # Algorithm 1: sizes
     assert lib.vq_vptq(FAKE, FAKE, 10, 16, 4, FAKE, 8, 16, FAKE, FAKE + 64, None, FAKE, 1 << 30,
                        None) == vq.VQ_ERR_INVALID          # V does not divide M

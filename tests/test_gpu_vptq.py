@@ -143,3 +143,34 @@ def test_vptq_fullsize_sampled_rows():
     nv, parted = compare(W, U, C, V, B, idx[:, groups], What[rows], E[rows], rows=rows)
     say("  groups parted: %d of %d" % (parted, nv))
     assert parted <= 1
+
+
+@pytest.mark.parametrize("N,T,damp", [(1, 4, 0.01), (5, 3, 0.01), (33, 40, 0.01), (64, 20, 0.1), (100, 300, 0.01),
+                                      (300, 64, 0.01)])
+def test_hessian_factor_matches_oracle(N, T, damp):
+    """U from the float64 Cholesky route against numpy's inverse-then-Cholesky
+    (float64), both stored float32: |dU| <= 1e-5 max|U|; strict lower triangle 0.
+    T < N cases make X^T X singular, so the damping carries them."""
+    say("hessian factor N =", N)
+    g = np.random.default_rng([71, N])
+    X = g.standard_normal((T, N))
+    X[:, g.choice(N, max(1, N // 10), replace=False)] *= 10.0
+    H = (X.T @ X).astype(np.float32)
+    ref = oracle.inverse_hessian_factor(H.astype(np.float64), damp)
+    got = host(vq.hessian_factor(dev(H), damp))
+    assert np.all(np.tril(got, -1) == 0.0)
+    err = np.abs(got.astype(np.float64) - ref)
+    assert err.max() <= 1e-5 * np.abs(ref).max(), float(err.max() / np.abs(ref).max())
+
+
+def test_hessian_factor_fullsize():
+    """N = 11008 with the 4096 x 11008 workload's activations (T = 1024 < N)."""
+    cfg = configs.get(4)
+    say("hessian factor full size")
+    H = synth.make_hessian(cfg.cid, cfg.N, cfg.T, cfg.n_ch, cfg.ch_gain)
+    got = host(vq.hessian_factor(dev(H), 0.01))
+    ref = oracle.inverse_hessian_factor(H.astype(np.float64), 0.01)
+    err = np.abs(got.astype(np.float64) - ref)
+    say("  max |dU| / max |U| = %.3g" % float(err.max() / np.abs(ref).max()))
+    assert np.all(np.tril(got, -1) == 0.0)
+    assert err.max() <= 1e-5 * np.abs(ref).max()
