@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 PEAK_FP16_MFMA_TFLOPS = 2500.0    # MI355X dense fp16 matrix peak
 PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 matrix peak (what an fp32 search is bounded by)
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
+PEAK_FP64_TFLOPS = 78.6           # MI355X float64 (vector and matrix)
 
 
 def algorithmic_bytes_update(n_sub, M, N, d, K):
@@ -302,6 +303,69 @@ def correction_bench(cfg, inp, out, W, h, ws, run_oracle, reps=5):
     return res
 
 
+def vptq_bench(cfg, inp, run_oracle, V=8, B=128):
+    """VPTQ Algorithm 1 on the workload's matrix: the inverse-Hessian factor from
+    H = X^T X of the workload's activations (float64 Cholesky and triangular
+    inverse), then the column-by-column quantization with the workload's codebook
+    size (codebook rows drawn from the matrix's column sub-vectors).  HIP-event
+    times: the factor against the float64 peak (2N^3/3 flops), the block updates
+    against the float32 matrix-core peak, the columns as distance pairs/s; the
+    oracle on one group of V rows at the full width."""
+    import numpy as np
+    import torch
+
+    from hessian_weighted_vector_amd import synth, vq
+    M, N, K = cfg.M, cfg.N, cfg.K1
+    H = torch.from_numpy(synth.make_hessian(cfg.cid, cfg.N, cfg.T, cfg.n_ch, cfg.ch_gain)).cuda()
+    W = torch.from_numpy(inp["W"]).cuda()
+    g = np.random.default_rng([cfg.cid, 98])
+    cols = inp["W"].T.reshape(-1, V)
+    Cn = cols[np.sort(g.choice(cols.shape[0], K, replace=False))].copy()
+    C = torch.from_numpy(Cn).cuda()
+    ws_f = torch.empty(vq.load().vq_hessian_factor_workspace_bytes(N), dtype=torch.uint8, device="cuda")
+    ws_v = torch.empty(vq.load().vq_vptq_workspace_bytes(M, N, V), dtype=torch.uint8, device="cuda")
+    U = vq.hessian_factor(H, 0.01, ws=ws_f)
+    vq.vptq(W, U, V, C, B, ws=ws_v)
+    torch.cuda.synchronize()
+    vq.timing_enable(True)
+    t0 = time.perf_counter()
+    U = vq.hessian_factor(H, 0.01, ws=ws_f)
+    idx, What, _ = vq.vptq(W, U, V, C, B, ws=ws_v)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    rec = {(r[0], r[1]): r for r in vq.timing_records()}
+    vq.timing_enable(False)
+    t_f = rec[("hessian_factor", 0)][3]
+    t_v = rec[("vptq", K)][3]
+    gu = rec[("vptq_block_update", K)]
+    gemm_flops = 0.0
+    for s in range(0, N, B):
+        s_end = min(s + B, N)
+        gemm_flops += 2.0 * (N - s_end) * M * (s_end - s)
+    f_flops = 2.0 * N ** 3 / 3.0
+    pairs = float(N) * (M // V) * K
+    res = {"V": V, "K": K, "B": B, "wall_ms": round(wall, 1),
+           "hessian_factor": {"gpu_ms": round(t_f, 2), "flop": f_flops,
+                              "TFLOPs": round(f_flops / (t_f * 1e-3) / 1e12, 2),
+                              "frac_fp64": round(f_flops / (t_f * 1e-3) / 1e12 / PEAK_FP64_TFLOPS, 4)},
+           "vptq_total_ms": round(t_v, 2),
+           "block_update": {"gpu_ms": round(gu[3], 2), "launches": gu[2], "flop": gemm_flops,
+                            "TFLOPs": round(gemm_flops / (gu[3] * 1e-3) / 1e12, 2),
+                            "frac_fp32_mfma": round(gemm_flops / (gu[3] * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)},
+           "columns": {"gpu_ms": round(t_v - gu[3], 2),
+                       "G_pairs_per_s": round(pairs / ((t_v - gu[3]) * 1e-3) / 1e9, 1),
+                       "us_per_column": round((t_v - gu[3]) * 1e3 / N, 2)}}
+    if run_oracle:
+        import oracle
+        Un = U.cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.vptq(inp["W"][:V], Un, V, Cn, B)
+        t_o = time.perf_counter() - t0
+        res["oracle_ms_one_row_group"] = round(t_o * 1e3, 1)
+        res["oracle_ms_full_extrapolated"] = round(t_o * 1e3 * (M // V), 0)
+    return res
+
+
 def cpu_baseline(cfg, inp, seconds):
     """The oracle's assignment on a bounded sample (float64 exhaustive search)."""
     import numpy as np
@@ -340,6 +404,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-qgemv", action="store_true", help="skip the fused dequantize-and-multiply rows")
     ap.add_argument("--no-correction", action="store_true", help="skip the unified sparse correction rows")
+    ap.add_argument("--no-vptq", action="store_true", help="skip the VPTQ Algorithm 1 rows")
     ap.add_argument("--breakdown", action="store_true", help="print per-step timings to stderr")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB three times (a plain "
@@ -441,6 +506,8 @@ def main():
     extra["rows"] = row_table(cfg, recs, nnz, oracle_ms)
     if not args.no_qgemv:
         extra["rows"]["NEXT1_qgemv"] = qgemv_bench(cfg, inp, not args.no_cpu_baseline)
+    if not args.no_vptq:
+        extra["rows"]["NEXT2_vptq_algorithm1"] = vptq_bench(cfg, inp, not args.no_cpu_baseline)
     if not args.no_correction:
         extra["rows"]["NEXT3_unified_correction"] = correction_bench(cfg, inp, out, W, h, ws,
                                                                      not args.no_cpu_baseline)

@@ -11,11 +11,13 @@
 // kept transposed too; they are transposed back at the end.
 //
 // Per column, two launches:
-//   k_col_assign   the M/V x K distances of the column, direct form in
-//                  float32; workgroups split K, each stages its centroids in
-//                  LDS, and the per-sub-vector minima meet in a packed 64-bit
-//                  atomicMin of (distance bits, index): the order of arrival
-//                  does not matter, and equal distances keep the lowest index;
+//   k_col_assign   the M/V x K distances of the column; V = 8 on the float32
+//                  matrix cores (k_col_assign_mfma, expanded form), other V
+//                  in the direct form on the vector units; workgroups split K,
+//                  each stages its centroids in LDS, and the per-sub-vector
+//                  minima meet in a packed 64-bit atomicMin of (score bits,
+//                  index): the order of arrival does not matter, and equal
+//                  scores keep the lowest index;
 //   k_col_finalize reads the winners, writes indices, What and E, clears the
 //                  other key buffer for the next column, and applies the
 //                  in-block update to the rows j of the block (a 2D grid over
@@ -60,14 +62,20 @@ __global__ void k_fill_u64(unsigned long long* __restrict__ p, int64_t n, unsign
 }
 
 // Nearest codebook row of each sub-vector of x (one column, nv sub-vectors of
-// V floats) among the workgroup's chunk of centroids; the chunk's winner is
-// merged into keys[v].
-template <bool V8>
+// V floats, any V) among the workgroup's chunk of centroids, direct form in
+// float32 on the vector units; the chunk's winner is merged into keys[v] as
+// (order-preserving bits of the distance, index).
+__device__ inline unsigned sortable(float f)
+{
+    const unsigned u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 __global__ __launch_bounds__(kAsgThreads) void k_col_assign(const float* __restrict__ x, int nv, int V,
                                                             const float* __restrict__ C, int K,
                                                             unsigned long long* __restrict__ keys)
 {
-    __shared__ __align__(16) float cs[kAsgChunk * 8];
+    __shared__ float cs[kAsgChunk * 8];
     const int k0 = blockIdx.y * kAsgChunk;
     const int kn = K - k0 < kAsgChunk ? K - k0 : kAsgChunk;
     for (int q = threadIdx.x; q < kn * V; q += kAsgThreads) cs[q] = C[(size_t)k0 * V + q];
@@ -75,43 +83,118 @@ __global__ __launch_bounds__(kAsgThreads) void k_col_assign(const float* __restr
     const int v = blockIdx.x * kAsgThreads + threadIdx.x;
     if (v >= nv) return;
     float xv[8];
-    if (V8) {
-        const float4 a = reinterpret_cast<const float4*>(x)[2 * v];
-        const float4 b = reinterpret_cast<const float4*>(x)[2 * v + 1];
-        xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
-        xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
-    } else {
-        for (int t = 0; t < 8; ++t) xv[t] = t < V ? x[(size_t)v * V + t] : 0.0f;
-    }
+    for (int t = 0; t < 8; ++t) xv[t] = t < V ? x[(size_t)v * V + t] : 0.0f;
     float best = __builtin_inff();
     int arg = 0;
-    if (V8) {
-        const float4* c4 = reinterpret_cast<const float4*>(cs);
-        for (int k = 0; k < kn; ++k) {
-            const float4 a = c4[2 * k], b = c4[2 * k + 1];
-            float dist = 0.0f, df;
-            df = xv[0] - a.x; dist = fmaf(df, df, dist);
-            df = xv[1] - a.y; dist = fmaf(df, df, dist);
-            df = xv[2] - a.z; dist = fmaf(df, df, dist);
-            df = xv[3] - a.w; dist = fmaf(df, df, dist);
-            df = xv[4] - b.x; dist = fmaf(df, df, dist);
-            df = xv[5] - b.y; dist = fmaf(df, df, dist);
-            df = xv[6] - b.z; dist = fmaf(df, df, dist);
-            df = xv[7] - b.w; dist = fmaf(df, df, dist);
-            if (dist < best) { best = dist; arg = k; }
+    for (int k = 0; k < kn; ++k) {
+        float dist = 0.0f;
+        for (int t = 0; t < V; ++t) {
+            const float df = xv[t] - cs[k * V + t];
+            dist = fmaf(df, df, dist);
         }
-    } else {
-        for (int k = 0; k < kn; ++k) {
-            float dist = 0.0f;
-            for (int t = 0; t < V; ++t) {
-                const float df = xv[t] - cs[k * V + t];
-                dist = fmaf(df, df, dist);
-            }
-            if (dist < best) { best = dist; arg = k; }
-        }
+        if (dist < best) { best = dist; arg = k; }
     }
-    const unsigned long long key = ((unsigned long long)__float_as_uint(best) << 32) | (unsigned)(k0 + arg);
+    const unsigned long long key = ((unsigned long long)sortable(best) << 32) | (unsigned)(k0 + arg);
     atomicMin(&keys[v], key);
+}
+
+// V = 8 on the float32 matrix cores.  ||x - c||^2 = ||x||^2 + 2 (||c||^2 / 2
+// - <c, x>): the workgroup stages kMChunk centroids transposed in LDS (k
+// slow, so the 32 lanes that feed one MFMA row read consecutive words) with
+// their half norms; each wavefront takes 32 sub-vectors and, per tile of 32
+// centroids, forms the 32 x 32 inner products with four
+// v_mfma_f32_32x32x2f32 (lane l feeds A = c_{l%32}[2s + l/32] and
+// B = x_{l%32}[2s + l/32]) and scans its 16 accumulator rows (centroid
+// (r/4)*8 + (l/32)*4 + r%4 of the tile) in increasing index order.  The two
+// lanes holding one sub-vector merge, then the chunk's winner enters keys[v]
+// as (order-preserving bits of the score, index) through atomicMin.
+constexpr int kMChunk = 256;
+
+__global__ __launch_bounds__(256) void k_col_assign_mfma(const float* __restrict__ x, int nv,
+                                                         const float* __restrict__ C, int K,
+                                                         unsigned long long* __restrict__ keys)
+{
+    __shared__ float csT[8][kMChunk];
+    __shared__ float hn[kMChunk];
+    const int k0 = blockIdx.y * kMChunk;
+    const int kn = K - k0 < kMChunk ? K - k0 : kMChunk;
+    for (int q = threadIdx.x; q < kMChunk; q += 256) {
+        float c[8];
+        if (q < kn) {
+            const float4 a = reinterpret_cast<const float4*>(C)[2 * (size_t)(k0 + q)];
+            const float4 b = reinterpret_cast<const float4*>(C)[2 * (size_t)(k0 + q) + 1];
+            c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w; c[4] = b.x; c[5] = b.y; c[6] = b.z; c[7] = b.w;
+            float nrm = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) nrm = fmaf(c[t], c[t], nrm);
+            hn[q] = 0.5f * nrm;
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) c[t] = 0.0f;
+            hn[q] = __builtin_inff();   // padding never wins
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) csT[t][q] = c[t];
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j0 = (blockIdx.x * 4 + wave) * 32;
+    if (j0 >= nv) return;
+    const int jl = lane & 31, half = lane >> 5;
+    const int j = j0 + jl;
+    float xb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xb[s] = j < nv ? x[(size_t)j * 8 + 2 * s + half] : 0.0f;
+    typedef float f16x_t __attribute__((ext_vector_type(16)));
+    float best = __builtin_inff();
+    int bi = 0;
+    const int ntiles = (kn + 31) / 32;
+    // The tile's minimum first; the row is located only when it beats the
+    // running best (rare after the first tiles), scanning rows in increasing
+    // index order so equal scores keep the lowest index.  Two tiles per step
+    // keep two independent MFMA chains in flight.
+    auto scan = [&](const f16x_t& acc, int tb) {
+        float sc[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = hn[tb + (r >> 2) * 8 + half * 4 + (r & 3)] - acc[r];
+        float m = sc[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) m = fminf(m, sc[r]);
+        if (m < best) {
+            int rr = 0;
+#pragma unroll
+            for (int r = 15; r >= 0; --r)
+                if (sc[r] == m) rr = r;
+            best = m;
+            bi = tb + (rr >> 2) * 8 + half * 4 + (rr & 3);
+        }
+    };
+    int tb = 0;
+    for (; tb + 32 < ntiles * 32; tb += 64) {
+        f16x_t a0, a1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { a0[r] = 0.0f; a1[r] = 0.0f; }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            a0 = __builtin_amdgcn_mfma_f32_32x32x2f32(csT[2 * s + half][tb + jl], xb[s], a0, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_f32_32x32x2f32(csT[2 * s + half][tb + 32 + jl], xb[s], a1, 0, 0, 0);
+        }
+        scan(a0, tb);
+        scan(a1, tb + 32);
+    }
+    if (tb < ntiles * 32) {
+        f16x_t a0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a0[r] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            a0 = __builtin_amdgcn_mfma_f32_32x32x2f32(csT[2 * s + half][tb + jl], xb[s], a0, 0, 0, 0);
+        scan(a0, tb);
+    }
+    unsigned long long key = ((unsigned long long)sortable(best) << 32) | (unsigned)(k0 + bi);
+    const unsigned long long other = __shfl_xor(key, 32);
+    key = other < key ? other : key;
+    if (half == 0 && j < nv) atomicMin(&keys[j], key);
 }
 
 // Column n: winners -> indices, What, E; the other key buffer is cleared for
@@ -216,17 +299,16 @@ vq_status vptq_launch(const float* W, const float* U, int64_t M, int64_t N, int 
     VQ_LAUNCHED("k_fill_u64");
     const bool v8 = V == 8 && aligned16(C) && (M % 4 == 0);
     const dim3 ga(grid_for(nv, kAsgThreads), grid_for(K, kAsgChunk));
+    const dim3 gm(grid_for(nv, 128), grid_for(K, kMChunk));
     for (int64_t s = 0; s < N; s += B) {
         const int64_t s_end = s + B < N ? s + B : N;
         for (int64_t n = s; n < s_end; ++n) {
             unsigned long long* kc = (n & 1) ? keys1 : keys0;
             unsigned long long* kn = (n & 1) ? keys0 : keys1;
             if (v8)
-                hipLaunchKernelGGL((k_col_assign<true>), ga, dim3(kAsgThreads), 0, st, Wt + n * M, (int)nv, V, C,
-                                   K, kc);
+                hipLaunchKernelGGL(k_col_assign_mfma, gm, dim3(256), 0, st, Wt + n * M, (int)nv, C, K, kc);
             else
-                hipLaunchKernelGGL((k_col_assign<false>), ga, dim3(kAsgThreads), 0, st, Wt + n * M, (int)nv, V, C,
-                                   K, kc);
+                hipLaunchKernelGGL(k_col_assign, ga, dim3(kAsgThreads), 0, st, Wt + n * M, (int)nv, V, C, K, kc);
             VQ_LAUNCHED("k_col_assign");
             const int64_t rows = s_end - n - 1;
             const dim3 gf(grid_for(M, kFinThreads), (unsigned)(rows > 0 ? (rows + kFinRows - 1) / kFinRows : 1));
@@ -235,6 +317,7 @@ vq_status vptq_launch(const float* W, const float* U, int64_t M, int64_t N, int 
             VQ_LAUNCHED("k_col_finalize");
         }
         if (s_end < N) {
+            TimedRegion tg("vptq_block_update", K, st);
             const dim3 gg(grid_for(M, kGemmTile), grid_for(N - s_end, kGemmTile));
             hipLaunchKernelGGL(k_block_gemm, gg, dim3(256), 0, st, Wt, U, Et, N, M, s, (int)(s_end - s), s_end);
             VQ_LAUNCHED("k_block_gemm");
