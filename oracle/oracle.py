@@ -49,6 +49,9 @@ _SIGS = {
     "orc_select_subvectors": (_I, [_P, _P, _LL, _LL, _I, _LL, _P]),
     "orc_select_residual": (_I, [_P, _P, _P, _LL, _LL, _LL, _P]),
     "orc_keep_to_csr": (_LL, [_P, _P, _LL, _LL, _P, _P, _P]),
+    "orc_column_order": (_I, [_P, _LL, _LL, _P]),
+    "orc_fit_grouped": (_I, [_P, _P, _LL, _LL, _I, _I, _I, _I, _I, _D, _I, _I, _LL, _I, _I, _I, _I, _P, _P, _I,
+                             _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "orc_vptq": (_I, [_P, _P, _LL, _LL, _I, _P, _I, _I, _P, _P, _P, _P]),
     "orc_qgemv": (_I, [_LL, _LL, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _LL, _P]),
     "orc_fit": (_I, [_P, _P, _LL, _LL, _I, _I, _I, _I, _I, _D, _I, _I, _P, _P, _I,
@@ -232,6 +235,60 @@ def reconstruct(M, N, d, C1, idx1, C2=None, idx2=None, r=None, c=None,
                         _ptr(_c(row_ptr, np.int32)), _ptr(_c(col, np.int32)),
                         _ptr(_c(val, np.float32)), _ptr(What))
     return What
+
+
+def column_order(h, n_out, lib=None):
+    """Column order of the grouped fit: the n_out columns with the largest h (ties:
+    smaller index) ascending, then the rest ascending."""
+    lib = lib or load()
+    h = _c(h, np.float32)
+    cols = np.zeros(h.size, np.int32)
+    rc = lib.orc_column_order(_ptr(h), h.size, int(n_out), _ptr(cols))
+    if rc:
+        raise ValueError("orc_column_order failed: %d" % rc)
+    return cols
+
+
+def grouped_layout(N, d, n_out, d0, K0, T0, n_groups, K1, T1, K2, T2):
+    """[(first column of the order, columns, d, K, T, K2, T2)] per group, in order."""
+    groups = []
+    if n_out > 0:
+        groups.append((0, n_out, d0, K0, T0, 0, 0))
+    nb = (N - n_out) // d
+    w = -(-nb // n_groups) * d
+    for g in range(n_groups):
+        c0 = n_out + g * w
+        groups.append((c0, min(w, N - c0), d, K1, T1, K2, T2))
+    return groups
+
+
+def fit_grouped(W, h, d, K1, T1, K2, T2, p, n_out, d0, K0, T0, n_groups, perm1_all, perm2_all,
+                binorm=False, mask_outliers=True, nthreads=0, lib=None):
+    """The grouped fit; returns cols, idx_all, cb_all, CSR, keep, What, J_all."""
+    lib = lib or load()
+    W = _c(W, np.float32)
+    h = _c(h, np.float32)
+    M, N = W.shape
+    lay = grouped_layout(N, d, n_out, d0, K0, T0, n_groups, K1, T1, K2, T2)
+    n_idx = sum(M * Ng // dg * (2 if K2g else 1) for _, Ng, dg, _, _, K2g, _ in lay)
+    n_cb = sum(Kg * dg + K2g * dg for _, _, dg, Kg, _, K2g, _ in lay)
+    n_J = sum(Tg + 1 + ((T2g + 1) if K2g else 0) for _, _, _, _, Tg, K2g, T2g in lay)
+    nz = nnz(M, N, p, lib)
+    out = {"cols": np.zeros(N, np.int32), "idx": np.zeros(n_idx, np.uint16), "cb": np.zeros(n_cb, np.float32),
+           "row_ptr": np.zeros(M + 1, np.int32), "col": np.zeros(max(nz, 1), np.int32),
+           "val": np.zeros(max(nz, 1), np.float32), "keep": np.zeros((M, N), np.uint8),
+           "What": np.zeros((M, N), np.float32), "J": np.zeros(n_J), "layout": lay}
+    rc = lib.orc_fit_grouped(_ptr(W), _ptr(h), M, N, d, K1, T1, K2, T2, float(p), int(bool(binorm)),
+                             int(bool(mask_outliers)), int(n_out), d0, K0, T0, n_groups,
+                             _ptr(_c(perm1_all, np.int32)), _ptr(_c(perm2_all, np.int32)), int(nthreads),
+                             _ptr(out["cols"]), _ptr(out["idx"]), _ptr(out["cb"]), _ptr(out["row_ptr"]),
+                             _ptr(out["col"]), _ptr(out["val"]), _ptr(out["keep"]), _ptr(out["What"]),
+                             _ptr(out["J"]))
+    if rc:
+        raise RuntimeError("orc_fit_grouped failed: %d" % rc)
+    out["col"] = out["col"][:nz]
+    out["val"] = out["val"][:nz]
+    return out
 
 
 def inverse_hessian_factor(H, damp=0.01):

@@ -457,6 +457,148 @@ int orc_qgemv(long long M, long long N, int d,
 }
 
 /* ------------------------------------------------------------------ */
+/* Column groups (VPTQ page, "Outlier Elimination": the columns with the
+ * largest Hessian diagonal are held apart with their own codebook, shorter
+ * vectors and more centroids; "Interaction with group partitioning": the
+ * remaining columns may be split into groups with independent codebooks).
+ *
+ * Column order: the n_out columns with the largest h (ties: smaller j), in
+ * ascending j, then every other column in ascending j.  Groups: group 0 =
+ * the first n_out columns of that order (vector length d0, K0 centroids, T0
+ * Lloyd iterations, no residual stage) when n_out > 0; then the other
+ * N - n_out columns in n_groups contiguous runs of w = ceil(nb/n_groups)*d
+ * columns (nb = (N - n_out)/d; the last run may be shorter), each a full
+ * two-stage fit (d, K1, T1, K2, T2).  Selection of the salient weights and
+ * bi-normalization are done once on the whole matrix, as in orc_fit; each
+ * group quantizes the gathered columns of the (bi-normalized) matrix with the
+ * gathered column weights, masks and column scales; its reconstruction is
+ * written back to its columns and the salient values overwrite at the end.
+ * Per-group arrays are concatenated in group order: idx_all holds a group's
+ * stage-1 indices then its stage-2 indices; cb_all its C1 then C2; J_all its
+ * T+1 (then T2+1) objectives; perm1_all / perm2_all its seeding orders. */
+static void orc_lloyd(const float* X, const float* hcol, const float* rho, const unsigned char* keep,
+                      long long M, long long N, int d, float* C, int K, int T,
+                      unsigned short* idx, double* J, int nthreads);
+
+static int orc_h_desc_cmp(const void* a, const void* b)
+{
+    const orc_scored* x = (const orc_scored*)a;
+    const orc_scored* y = (const orc_scored*)b;
+    if (x->score > y->score) return -1;
+    if (x->score < y->score) return 1;
+    return (x->lin > y->lin) - (x->lin < y->lin);
+}
+
+static int orc_int_cmp(const void* a, const void* b)
+{
+    int x = *(const int*)a, y = *(const int*)b;
+    return (x > y) - (x < y);
+}
+
+int orc_column_order(const float* h, long long N, long long n_out, int* cols)
+{
+    if (n_out < 0 || n_out > N) return 2;
+    orc_scored* all = (orc_scored*)malloc(sizeof(orc_scored) * (size_t)N);
+    unsigned char* out = (unsigned char*)calloc((size_t)N, 1);
+    if (!all || !out) { free(all); free(out); return 3; }
+    for (long long j = 0; j < N; ++j) { all[j].score = h[j]; all[j].lin = j; }
+    qsort(all, (size_t)N, sizeof(orc_scored), orc_h_desc_cmp);
+    for (long long e = 0; e < n_out; ++e) { cols[e] = (int)all[e].lin; out[all[e].lin] = 1; }
+    qsort(cols, (size_t)n_out, sizeof(int), orc_int_cmp);
+    long long pos = n_out;
+    for (long long j = 0; j < N; ++j)
+        if (!out[j]) cols[pos++] = (int)j;
+    free(all);
+    free(out);
+    return 0;
+}
+
+int orc_fit_grouped(const float* W, const float* h, long long M, long long N, int d,
+                    int K1, int T1, int K2, int T2, double p, int binorm, int mask_outliers,
+                    long long n_out, int d0, int K0, int T0, int n_groups,
+                    const int* perm1_all, const int* perm2_all, int nthreads,
+                    int* cols, unsigned short* idx_all, float* cb_all,
+                    int* row_ptr, int* col, float* val, unsigned char* keep,
+                    float* What, double* J_all)
+{
+    if (M <= 0 || N <= 0 || d <= 0 || N % d || n_out < 0 || n_out % d || n_groups < 1) return 2;
+    if (n_out > 0 && (d0 <= 0 || n_out % d0 || K0 < 1)) return 2;
+    long long nb_main = (N - n_out) / d;
+    long long w = (nb_main + n_groups - 1) / n_groups * d;
+    if (nb_main < 1 || (long long)(n_groups - 1) * w >= N - n_out) return 2;
+    long long nnz = orc_nnz(M, N, p);
+    int rc = orc_select(W, h, M, N, nnz, row_ptr, col, val, keep);
+    if (rc) return rc;
+    float* Wp = (float*)malloc(sizeof(float) * (size_t)(M * N));
+    float* r = (float*)malloc(sizeof(float) * (size_t)M);
+    float* c = (float*)malloc(sizeof(float) * (size_t)N);
+    float* hcol = (float*)malloc(sizeof(float) * (size_t)N);
+    float* rho = (float*)malloc(sizeof(float) * (size_t)M);
+    if (!Wp || !r || !c || !hcol || !rho) return 3;
+    if (binorm) orc_binorm(W, h, M, N, Wp, r, c, hcol, rho);
+    else memcpy(Wp, W, sizeof(float) * (size_t)(M * N));
+    const float* hc = binorm ? hcol : h;
+    rc = orc_column_order(h, N, n_out, cols);
+    if (rc) return rc;
+    long long oi = 0, oc = 0, oj = 0, op1 = 0, op2 = 0;
+    int n_all = n_groups + (n_out > 0 ? 1 : 0);
+    for (int g = 0; g < n_all && rc == 0; ++g) {
+        int outlier = (n_out > 0 && g == 0);
+        long long c0 = outlier ? 0 : n_out + (long long)(g - (n_out > 0 ? 1 : 0)) * w;
+        long long c1 = outlier ? n_out : (c0 + w < N ? c0 + w : N);
+        long long Ng = c1 - c0;
+        int dg = outlier ? d0 : d, Kg = outlier ? K0 : K1, Tg = outlier ? T0 : T1;
+        int K2g = outlier ? 0 : K2;
+        long long nsg = M * Ng / dg;
+        float* Xg = (float*)malloc(sizeof(float) * (size_t)(M * Ng));
+        float* hg = (float*)malloc(sizeof(float) * (size_t)Ng);
+        float* cg = (float*)malloc(sizeof(float) * (size_t)Ng);
+        unsigned char* kg = (unsigned char*)malloc((size_t)(M * Ng));
+        float* Wg = (float*)malloc(sizeof(float) * (size_t)(M * Ng));
+        float* Rg = (float*)malloc(sizeof(float) * (size_t)(M * Ng));
+        if (!Xg || !hg || !cg || !kg || !Wg || !Rg) return 3;
+        for (long long q = 0; q < Ng; ++q) {
+            long long j = cols[c0 + q];
+            hg[q] = hc[j];
+            cg[q] = c[j];
+            for (long long i = 0; i < M; ++i) {
+                Xg[i * Ng + q] = Wp[i * N + j];
+                kg[i * Ng + q] = keep[i * N + j];
+            }
+        }
+        if (Kg > nsg || K2g > nsg) rc = 2;
+        unsigned short* i1 = idx_all + oi;
+        float* C1 = cb_all + oc;
+        if (!rc && orc_init(Xg, nsg, dg, perm1_all + op1, Kg, C1) != Kg) rc = 1;
+        if (!rc) orc_lloyd(Xg, hg, binorm ? rho : NULL, mask_outliers ? kg : NULL, M, Ng, dg, C1, Kg, Tg, i1,
+                           J_all + oj, nthreads);
+        oi += nsg; oc += (long long)Kg * dg; oj += Tg + 1; op1 += nsg;
+        unsigned short* i2 = NULL;
+        float* C2 = NULL;
+        if (!rc && K2g > 0) {
+            i2 = idx_all + oi;
+            C2 = cb_all + oc;
+            orc_residual(Xg, nsg, dg, C1, i1, Rg);
+            if (orc_init(Rg, nsg, dg, perm2_all + op2, K2g, C2) != K2g) rc = 1;
+            if (!rc) orc_lloyd(Rg, hg, binorm ? rho : NULL, mask_outliers ? kg : NULL, M, Ng, dg, C2, K2g, T2, i2,
+                               J_all + oj, nthreads);
+            oi += nsg; oc += (long long)K2g * dg; oj += T2 + 1; op2 += nsg;
+        }
+        if (!rc) {
+            orc_reconstruct(M, Ng, dg, C1, i1, C2, i2, binorm ? r : NULL, binorm ? cg : NULL, NULL, NULL, NULL, Wg);
+            for (long long q = 0; q < Ng; ++q)
+                for (long long i = 0; i < M; ++i) What[i * N + cols[c0 + q]] = Wg[i * Ng + q];
+        }
+        free(Xg); free(hg); free(cg); free(kg); free(Wg); free(Rg);
+    }
+    if (!rc)
+        for (long long i = 0; i < M; ++i)
+            for (int e = row_ptr[i]; e < row_ptr[i + 1]; ++e) What[i * N + col[e]] = val[e];
+    free(Wp); free(r); free(c); free(hcol); free(rho);
+    return rc;
+}
+
+/* ------------------------------------------------------------------ */
 /* Second-order error propagation with column sub-vectors (VPTQ page, "The
  * Core Algorithm", Algorithm 1).  W [M x N] is quantized one column at a
  * time, left to right, in blocks of B columns.  Column n is cut into M/V

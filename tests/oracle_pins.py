@@ -325,6 +325,64 @@ def pin_fit_monotone_and_identity(lib):
         assert sel.sum() == out["nnz"]
 
 
+def _grouped_perms(g, M, layout):
+    p1 = np.concatenate([g.permutation(M * Ng // dg) for _, Ng, dg, _, _, _, _ in layout]).astype(np.int32)
+    p2 = [g.permutation(M * Ng // dg) for _, Ng, dg, _, _, K2g, _ in layout if K2g]
+    return p1, (np.concatenate(p2).astype(np.int32) if p2 else np.zeros(1, np.int32))
+
+
+def pin_grouped_reduces_to_fit(lib):
+    """No outlier columns and one group: the grouped fit is the plain fit, bit for bit."""
+    for binorm in (False, True):
+        W, h, g = _case(51 + binorm, 24, 64, n_ch=3)
+        M, N = W.shape
+        d, K1, T1, K2, T2 = 8, 20, 4, 6, 3
+        lay = O.grouped_layout(N, d, 0, 4, 0, 0, 1, K1, T1, K2, T2)
+        p1, p2 = _grouped_perms(g, M, lay)
+        gout = O.fit_grouped(W, h, d, K1, T1, K2, T2, 0.02, 0, 4, 0, 0, 1, p1, p2, binorm=binorm, lib=lib)
+        out = O.fit(W, h, d, K1, T1, K2, T2, 0.02, binorm=binorm, perm1=p1, perm2=p2, lib=lib)
+        n_sub = M * N // d
+        assert np.array_equal(gout["cols"], np.arange(N, dtype=np.int32))
+        assert np.array_equal(gout["idx"][:n_sub], out["idx1"]) and np.array_equal(gout["idx"][n_sub:], out["idx2"])
+        assert np.array_equal(gout["cb"][:K1 * d], out["C1"].ravel())
+        assert np.array_equal(gout["What"].view(np.uint32), out["What"].view(np.uint32))
+        assert np.array_equal(gout["J"], out["J"])
+
+
+def pin_grouped_columns_and_identity(lib):
+    """The outlier group is the n_out columns with the largest h (ties: smaller index),
+    listed ascending, then the rest ascending; every group's Lloyd stages never raise J;
+    and the groups' final objectives add up to sum_ij h_j keep_ij (W - What)_ij^2 over
+    the whole matrix (so every group's reconstruction landed in its own columns), with
+    What == W at every salient position."""
+    for binorm, n_groups in ((False, 2), (True, 3)):
+        W, h, g = _case(53 + binorm, 24, 96, n_ch=4)
+        h[5] = h[17] = h.max()                      # a tie at the top
+        M, N = W.shape
+        d, K1, T1, K2, T2, n_out, d0, K0, T0 = 8, 16, 4, 4, 3, 16, 4, 24, 5
+        lay = O.grouped_layout(N, d, n_out, d0, K0, T0, n_groups, K1, T1, K2, T2)
+        p1, p2 = _grouped_perms(g, M, lay)
+        out = O.fit_grouped(W, h, d, K1, T1, K2, T2, 0.02, n_out, d0, K0, T0, n_groups, p1, p2, binorm=binorm,
+                            lib=lib)
+        order = np.lexsort((np.arange(N), -h.astype(np.float64)))
+        top = np.sort(order[:n_out])
+        rest = np.setdiff1d(np.arange(N), top)
+        assert np.array_equal(out["cols"], np.concatenate([top, rest]).astype(np.int32))
+        J, o, finals = out["J"], 0, []
+        for _, Ng, dg, Kg, Tg, K2g, T2g in lay:
+            segs = [Tg + 1] + ([T2g + 1] if K2g else [])
+            for L in segs:
+                seg = J[o:o + L]
+                assert np.all(seg[1:] <= seg[:-1] * (1 + 1e-12)), seg
+                o += L
+            finals.append(J[o - 1])
+        keep = out["keep"]
+        err = (h[None, :].astype(np.float64) * keep * (W.astype(np.float64) - out["What"]) ** 2).sum()
+        assert abs(err - sum(finals)) <= 2e-5 * sum(finals), (err, sum(finals))
+        sel = keep == 0
+        assert np.array_equal(out["What"][sel].view(np.uint32), W[sel].view(np.uint32))
+
+
 def pin_degenerate_cases(lib):
     """K = n_sub with every sub-vector distinct: J = 0 and What == W bitwise.
     p = 1: every weight is held exactly, What == W and J = 0.  Residual

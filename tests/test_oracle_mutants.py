@@ -73,6 +73,12 @@ MUTANTS = {
     "vptq_quantizes_original": [("double diff = Wk[(v * V + t) * N + n] -", "double diff = (double)W[(v * V + t) * N + n] -")],
     "vptq_inblock_reaches_past_block": [("for (long long j = n + 1; j < s_end; ++j) {\n                double unj",
                                          "for (long long j = n + 1; j < N; ++j) {\n                double unj")],
+    "grouped_outliers_smallest_h": [("if (x->score > y->score) return -1;\n    if (x->score < y->score) return 1;\n    return (x->lin > y->lin)",
+                                     "if (x->score > y->score) return 1;\n    if (x->score < y->score) return -1;\n    return (x->lin > y->lin)")],
+    "grouped_scatter_shifted": [("What[i * N + cols[c0 + q]] = Wg[i * Ng + q];",
+                                 "What[i * N + cols[(c0 + q + 1) % N]] = Wg[i * Ng + q];")],
+    "grouped_h_not_gathered": [("hg[q] = hc[j];", "hg[q] = hc[q];")],
+    "grouped_outlier_group_uses_main_d": [("int dg = outlier ? d0 : d,", "int dg = outlier ? d : d,")],
     "qgemv_wrong_row": [("acc += (double)What[i * N + j] * (double)x[j];",
                          "acc += (double)What[((i + 1) % M) * N + j] * (double)x[j];")],
     "qgemv_float_accumulation": [("            double acc = 0.0;\n            for (long long j = 0; j < N; ++j) acc +=",
