@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvq.so")
-SOURCES = ["vq_assign.hip", "vq_update.hip", "vq_select.hip", "vq_elem.hip", "vq_qgemv.hip", "vq_vptq.hip", "vq_hfactor.hip", "vq_host.hip",
+SOURCES = ["vq_assign.hip", "vq_update.hip", "vq_select.hip", "vq_elem.hip", "vq_qgemv.hip", "vq_vptq.hip", "vq_hfactor.hip", "vq_groups.hip", "vq_host.hip",
            "vq_timing.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

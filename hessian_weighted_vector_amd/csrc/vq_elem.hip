@@ -393,6 +393,15 @@ vq_status reconstruct_launch(int64_t M, int64_t N, int d, const float* C1, int K
     return VQ_OK;
 }
 
+vq_status sparse_overwrite_launch(int64_t M, int64_t N, const int32_t* row_ptr, const int32_t* col,
+                                  const float* val, float* Wh, hipStream_t st)
+{
+    if (M > (int64_t)UINT32_MAX) return fail(VQ_ERR_UNSUPPORTED, "sparse overwrite: too many rows");
+    hipLaunchKernelGGL(k_sparse_overwrite, dim3((unsigned)M), dim3(kBlock), 0, st, N, row_ptr, col, val, Wh);
+    VQ_LAUNCHED("k_sparse_overwrite");
+    return VQ_OK;
+}
+
 vq_status objective_launch(const float* X, const float* hcol, const float* rho, const uint8_t* mask,
                            int64_t M, int64_t N, int d, const float* C, int K, const uint16_t* idx,
                            double* J, void* ws, size_t ws_bytes, hipStream_t st)

@@ -55,6 +55,13 @@ vq_status mask_to_csr_launch(const float*, const uint8_t*, int64_t, int64_t, int
 vq_status vptq_launch(const float*, const float*, int64_t, int64_t, int, const float*, int, int, uint16_t*, float*,
                       float*, void*, size_t, hipStream_t);
 vq_status hfactor_launch(const float*, int64_t, double, float*, void*, size_t, hipStream_t);
+vq_status sparse_overwrite_launch(int64_t, int64_t, const int32_t*, const int32_t*, const float*, float*,
+                                  hipStream_t);
+vq_status column_order_launch(const float*, int64_t, int64_t, int32_t*, uint8_t*, hipStream_t);
+vq_status gather_cols_launch(const float*, int64_t, int64_t, const int32_t*, int64_t, float*, hipStream_t);
+vq_status scatter_cols_launch(const float*, int64_t, int64_t, const int32_t*, float*, int64_t, hipStream_t);
+vq_status gather_mask_launch(const uint8_t*, int64_t, int64_t, int, const int32_t*, int64_t, int, uint8_t*,
+                             hipStream_t);
 vq_status qgemv_launch(int64_t, int64_t, int, const float*, int, const uint16_t*, const float*, int,
                        const uint16_t*, const float*, const float*, const int32_t*, const int32_t*,
                        const float*, const float*, int64_t, float*, void*, size_t, hipStream_t);
@@ -560,6 +567,214 @@ vq_status vq_fit(const vq_fit_params* p, const vq_fit_inputs* in, vq_fit_outputs
     VQ_HIP(hipMemcpyAsync(out->J_hist, Jd, sizeof(double) * nJ, hipMemcpyDeviceToHost, st));
     VQ_HIP(hipStreamSynchronize(st));
     if (out->bpw) *out->bpw = vq_bits_per_weight(M, N, d, p->K1, p->K2, nnz, 32, p->binorm);
+    return VQ_OK;
+}
+
+}  // extern "C"
+
+namespace vq {
+namespace {
+
+struct GroupSpec {
+    int64_t c0, Ng;   // first position in the column order, columns
+    int d, K, T, K2, T2;
+};
+
+// Groups in order (outlier group first); false if the sizes do not split.
+bool group_layout(const vq_grouped_params* p, std::vector<GroupSpec>& g)
+{
+    const vq_fit_params& f = p->fit;
+    g.clear();
+    if (f.N <= 0 || f.d < 1 || f.N % f.d || p->n_out < 0 || p->n_out % f.d || p->n_groups < 1) return false;
+    if (p->n_out > 0) {
+        if (p->d0 < 1 || p->d0 > 8 || p->n_out % p->d0) return false;
+        g.push_back({0, p->n_out, p->d0, p->K0, p->iters0, 0, 0});
+    }
+    const int64_t nb = (f.N - p->n_out) / f.d;
+    const int64_t w = (nb + p->n_groups - 1) / p->n_groups * f.d;
+    if (nb < 1 || (int64_t)(p->n_groups - 1) * w >= f.N - p->n_out) return false;
+    for (int q = 0; q < p->n_groups; ++q) {
+        const int64_t c0 = p->n_out + q * w;
+        g.push_back({c0, std::min(w, f.N - c0), f.d, f.K1, f.iters1, f.K2, f.iters2});
+    }
+    return true;
+}
+
+struct GroupTotals {
+    int64_t n_idx = 0, n_cb = 0, n_J = 0, n_perm1 = 0, n_perm2 = 0, max_elems = 0, max_mask = 0;
+    size_t steps = 0;
+};
+
+GroupTotals group_totals(const vq_grouped_params* p, const std::vector<GroupSpec>& g)
+{
+    GroupTotals t;
+    const int64_t M = p->fit.M;
+    for (const GroupSpec& s : g) {
+        const int64_t ns = M * s.Ng / s.d;
+        t.n_idx += ns * (s.K2 > 0 ? 2 : 1);
+        t.n_cb += (int64_t)s.K * s.d + (int64_t)s.K2 * s.d;
+        t.n_J += s.T + 1 + (s.K2 > 0 ? s.T2 + 1 : 0);
+        t.n_perm1 += ns;
+        if (s.K2 > 0) t.n_perm2 += ns;
+        t.max_elems = std::max(t.max_elems, M * s.Ng);
+        t.max_mask = std::max(t.max_mask, ns);
+        t.steps = std::max(t.steps, ws_steps(M, s.Ng, s.d, s.K, s.K2));
+    }
+    t.steps = std::max(t.steps, std::max(ws_select(M, p->fit.N), ws_binorm(M, p->fit.N)));
+    return t;
+}
+
+size_t grouped_ws(const vq_grouped_params* p, const GroupTotals& t)
+{
+    const int64_t M = p->fit.M, N = p->fit.N;
+    size_t b = 0;
+    if (p->fit.binorm)
+        b += align_up((size_t)M * N * 4) + 2 * align_up((size_t)M * 4) + 2 * align_up((size_t)N * 4);
+    b += 3 * align_up((size_t)t.max_elems * 4) + 2 * align_up((size_t)N * 4) + align_up((size_t)t.max_mask);
+    b += align_up((size_t)N) + align_up((size_t)t.n_J * 8);
+    return b + t.steps;
+}
+
+}  // namespace
+}  // namespace vq
+
+extern "C" {
+
+double vq_bits_per_weight_grouped(const vq_grouped_params* p)
+{
+    std::vector<GroupSpec> g;
+    if (!p || !group_layout(p, g) || p->fit.M <= 0) return -1.0;
+    auto ibits = [](int K) -> int64_t {
+        int64_t b = 0;
+        while (((int64_t)1 << b) < K) ++b;
+        return b;
+    };
+    const int64_t M = p->fit.M, N = p->fit.N;
+    double bits = 0.0;
+    for (const GroupSpec& s : g) {
+        const double ns = (double)(M * s.Ng / s.d);
+        bits += ns * (double)(ibits(s.K) + (s.K2 > 0 ? ibits(s.K2) : 0));
+        bits += 32.0 * (double)s.d * (double)(s.K + (s.K2 > 0 ? s.K2 : 0));
+    }
+    const int64_t nnz = (int64_t)std::floor(p->fit.outlier_frac * (double)(M * N));
+    bits += 64.0 * (double)nnz;
+    if (nnz > 0) bits += 32.0 * (double)(M + 1);
+    if (p->fit.binorm) bits += 32.0 * (double)(M + N);
+    if (p->n_out > 0) bits += 32.0 * (double)p->n_out;
+    return bits / ((double)M * (double)N);
+}
+
+size_t vq_grouped_sizes(const vq_grouped_params* p, int64_t* n_idx, int64_t* n_codebook, int64_t* n_J,
+                        int64_t* n_perm1, int64_t* n_perm2)
+{
+    std::vector<GroupSpec> g;
+    if (!p || !group_layout(p, g)) return 0;
+    const GroupTotals t = group_totals(p, g);
+    if (n_idx) *n_idx = t.n_idx;
+    if (n_codebook) *n_codebook = t.n_cb;
+    if (n_J) *n_J = t.n_J;
+    if (n_perm1) *n_perm1 = t.n_perm1;
+    if (n_perm2) *n_perm2 = t.n_perm2;
+    return grouped_ws(p, t);
+}
+
+vq_status vq_fit_grouped(const vq_grouped_params* p, const vq_grouped_inputs* in, vq_grouped_outputs* out,
+                         void* ws, size_t ws_bytes, void* stream)
+{
+    VQ_CHECK(p && in && out, "vq_fit_grouped: null params/inputs/outputs");
+    const vq_fit_params& f = p->fit;
+    const int64_t M = f.M, N = f.N;
+    VQ_TRY(check_shape(M, N, f.d));
+    std::vector<GroupSpec> groups;
+    VQ_CHECK(group_layout(p, groups), "vq_fit_grouped: n_out must be a multiple of d and d0, and n_groups must "
+                                      "split the other columns into non-empty groups");
+    for (const GroupSpec& g : groups) {
+        const int64_t ns = M * g.Ng / g.d;
+        VQ_TRY(check_K(g.K, ns));
+        if (g.K2 > 0) VQ_TRY(check_K(g.K2, ns));
+    }
+    VQ_CHECK(f.K2 >= 0 && f.iters1 >= 0 && f.iters2 >= 0 && p->iters0 >= 0, "vq_fit_grouped: negative count");
+    VQ_CHECK(f.outlier_frac >= 0.0 && f.outlier_frac <= 1.0, "vq_fit_grouped: outlier_frac must be in [0, 1]");
+    const int64_t nnz = nnz_of(M, N, f.outlier_frac);
+    VQ_CHECK(nnz <= INT32_MAX, "vq_fit_grouped: too many salient weights");
+    VQ_CHECK(in->W && in->h && in->perm1 && (f.K2 == 0 || in->perm2), "vq_fit_grouped: null input");
+    VQ_CHECK(out->cols && out->idx && out->codebooks && out->row_ptr && out->mask && out->W_hat && out->J_hist,
+             "vq_fit_grouped: null output");
+    VQ_CHECK(nnz == 0 || (out->col && out->val), "vq_fit_grouped: col/val are null");
+    const GroupTotals tot = group_totals(p, groups);
+    VQ_WS(ws && ws_bytes >= grouped_ws(p, tot), "vq_fit_grouped: workspace too small");
+    VQ_TRY(check_device());
+    hipStream_t st = as_stream(stream);
+
+    Carver cv(ws, ws_bytes);
+    float *Wp = nullptr, *r = nullptr, *c = nullptr, *hcol = nullptr, *rho = nullptr;
+    if (f.binorm) {
+        Wp = cv.take<float>((size_t)M * N);
+        r = cv.take<float>(M);
+        rho = cv.take<float>(M);
+        c = cv.take<float>(N);
+        hcol = cv.take<float>(N);
+    }
+    float* Xg = cv.take<float>(tot.max_elems);
+    float* Rg = cv.take<float>(tot.max_elems);
+    float* Wg = cv.take<float>(tot.max_elems);
+    float* hg = cv.take<float>(N);
+    float* cg = cv.take<float>(N);
+    uint8_t* mg = cv.take<uint8_t>(tot.max_mask);
+    uint8_t* flag = cv.take<uint8_t>(N);
+    double* Jd = cv.take<double>(tot.n_J);
+    if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_fit_grouped: workspace too small");
+    void* sws = cv.base + cv.used;
+    const size_t sws_bytes = cv.cap - cv.used;
+
+    VQ_TRY(select_launch(in->W, in->h, M, N, f.d, nnz, out->row_ptr, out->col, out->val, out->mask, sws, sws_bytes,
+                         st));
+    const float* X = in->W;
+    const float* hc = in->h;
+    if (f.binorm) {
+        VQ_TRY(binorm_launch(in->W, in->h, M, N, Wp, r, c, hcol, rho, sws, sws_bytes, st));
+        X = Wp;
+        hc = hcol;
+    }
+    VQ_TRY(column_order_launch(in->h, N, p->n_out, out->cols, flag, st));
+
+    int64_t oi = 0, oc = 0, oj = 0, op1 = 0, op2 = 0;
+    for (const GroupSpec& g : groups) {
+        const int32_t* gc = out->cols + g.c0;
+        const int64_t ns = M * g.Ng / g.d;
+        VQ_TRY(gather_cols_launch(X, M, N, gc, g.Ng, Xg, st));
+        VQ_TRY(gather_cols_launch(hc, 1, N, gc, g.Ng, hg, st));
+        if (f.binorm) VQ_TRY(gather_cols_launch(c, 1, N, gc, g.Ng, cg, st));
+        const uint8_t* mk = nullptr;
+        if (f.mask_outliers) {
+            VQ_TRY(gather_mask_launch(out->mask, M, N, f.d, gc, g.Ng, g.d, mg, st));
+            mk = mg;
+        }
+        uint16_t* i1 = out->idx + oi;
+        float* C1 = out->codebooks + oc;
+        VQ_TRY(init_walk(Xg, ns, g.d, in->perm1 + op1, g.K, C1, sws, sws_bytes, st));
+        VQ_TRY(lloyd_stage(Xg, hg, f.binorm ? rho : nullptr, mk, M, g.Ng, g.d, C1, g.K, g.T, i1, Jd + oj, sws,
+                           sws_bytes, st));
+        oi += ns; oc += (int64_t)g.K * g.d; oj += g.T + 1; op1 += ns;
+        uint16_t* i2 = nullptr;
+        float* C2 = nullptr;
+        if (g.K2 > 0) {
+            i2 = out->idx + oi;
+            C2 = out->codebooks + oc;
+            VQ_TRY(residual_launch(Xg, M, g.Ng, g.d, C1, g.K, i1, Rg, st));
+            VQ_TRY(init_walk(Rg, ns, g.d, in->perm2 + op2, g.K2, C2, sws, sws_bytes, st));
+            VQ_TRY(lloyd_stage(Rg, hg, f.binorm ? rho : nullptr, mk, M, g.Ng, g.d, C2, g.K2, g.T2, i2, Jd + oj, sws,
+                               sws_bytes, st));
+            oi += ns; oc += (int64_t)g.K2 * g.d; oj += g.T2 + 1; op2 += ns;
+        }
+        VQ_TRY(reconstruct_launch(M, g.Ng, g.d, C1, g.K, i1, C2, g.K2, i2, f.binorm ? r : nullptr,
+                                  f.binorm ? cg : nullptr, nullptr, nullptr, nullptr, Wg, st));
+        VQ_TRY(scatter_cols_launch(Wg, M, g.Ng, gc, out->W_hat, N, st));
+    }
+    if (nnz > 0) VQ_TRY(sparse_overwrite_launch(M, N, out->row_ptr, out->col, out->val, out->W_hat, st));
+    VQ_HIP(hipMemcpyAsync(out->J_hist, Jd, sizeof(double) * tot.n_J, hipMemcpyDeviceToHost, st));
+    VQ_HIP(hipStreamSynchronize(st));
+    if (out->bpw) *out->bpw = vq_bits_per_weight_grouped(p);
     return VQ_OK;
 }
 

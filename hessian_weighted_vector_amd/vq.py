@@ -10,6 +10,7 @@ import ctypes
 import math
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -48,6 +49,19 @@ class FitOutputs(ctypes.Structure):
                 ("rho", _P), ("W_hat", _P), ("J_hist", _P), ("bpw", _P)]
 
 
+class GroupedParams(ctypes.Structure):
+    _fields_ = [("fit", FitParams), ("n_out", _I64), ("d0", _I), ("K0", _I), ("iters0", _I), ("n_groups", _I)]
+
+
+class GroupedInputs(ctypes.Structure):
+    _fields_ = [("W", _P), ("h", _P), ("perm1", _P), ("perm2", _P)]
+
+
+class GroupedOutputs(ctypes.Structure):
+    _fields_ = [("cols", _P), ("idx", _P), ("codebooks", _P), ("row_ptr", _P), ("col", _P), ("val", _P),
+                ("mask", _P), ("W_hat", _P), ("J_hist", _P), ("bpw", _P)]
+
+
 # name -> (restype, argtypes); every symbol declared in include/vq.h
 SIGNATURES = {
     "vq_version": (ctypes.c_char_p, []),
@@ -74,6 +88,11 @@ SIGNATURES = {
                       _P]),
     "vq_fit": (_I, [ctypes.POINTER(FitParams), ctypes.POINTER(FitInputs), ctypes.POINTER(FitOutputs),
                     _P, _SZ, _P]),
+    "vq_grouped_sizes": (_SZ, [ctypes.POINTER(GroupedParams), ctypes.POINTER(_I64), ctypes.POINTER(_I64),
+                               ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "vq_fit_grouped": (_I, [ctypes.POINTER(GroupedParams), ctypes.POINTER(GroupedInputs),
+                            ctypes.POINTER(GroupedOutputs), _P, _SZ, _P]),
+    "vq_bits_per_weight_grouped": (_D, [ctypes.POINTER(GroupedParams)]),
     "vq_bits_per_weight": (_D, [_I64, _I64, _I, _I, _I, _I64, _I, _I]),
     "vq_timing_enable": (None, [_I]),
     "vq_timing_count": (_I, []),
@@ -167,7 +186,6 @@ def binorm(W, h, ws):
 
 def init(X, d, perm_host, K, ws):
     """perm_host: numpy int32 array (host)."""
-    import numpy as np
     M, N = X.shape
     perm = np.ascontiguousarray(perm_host, dtype=np.int32)
     C = torch.empty((K, d), dtype=torch.float32, device=X.device)
@@ -302,6 +320,54 @@ def qgemv(M, N, d, C1, idx1, X, C2=None, idx2=None, rscale=None, cscale=None, ro
     return Y
 
 
+def grouped_params(M, N, d, K1, iters1, K2, iters2, outlier_frac, binorm, mask_outliers, n_out, d0, K0, iters0,
+                   n_groups):
+    return GroupedParams(FitParams(M, N, d, K1, iters1, K2, iters2, float(outlier_frac), int(bool(binorm)),
+                                   int(bool(mask_outliers))), int(n_out), d0, K0, iters0, n_groups)
+
+
+def grouped_sizes(params):
+    """(workspace bytes, n_idx, n_codebook, n_J, n_perm1, n_perm2)."""
+    v = [_I64(0) for _ in range(5)]
+    ws = load().vq_grouped_sizes(ctypes.byref(params), *[ctypes.byref(x) for x in v])
+    return (int(ws),) + tuple(int(x.value) for x in v)
+
+
+def fit_grouped(W, h, params, perm1, perm2=None, ws=None):
+    """The grouped fit; returns a dict of the outputs (device tensors; J and bpw on the host)."""
+    M, N = W.shape
+    dev = W.device
+    wsb, n_idx, n_cb, n_J, n_p1, n_p2 = grouped_sizes(params)
+    if wsb == 0:
+        raise ValueError("the column groups do not split these sizes")
+    nnz = nnz_of(M, N, params.fit.outlier_frac)
+    o = {"cols": torch.empty(N, dtype=torch.int32, device=dev),
+         "idx": torch.empty(max(n_idx, 1), dtype=torch.uint16, device=dev),
+         "codebooks": torch.empty(max(n_cb, 1), dtype=torch.float32, device=dev),
+         "row_ptr": torch.empty(M + 1, dtype=torch.int32, device=dev),
+         "col": torch.empty(max(nnz, 1), dtype=torch.int32, device=dev),
+         "val": torch.empty(max(nnz, 1), dtype=torch.float32, device=dev),
+         "mask": torch.empty(M * N // params.fit.d, dtype=torch.uint8, device=dev),
+         "W_hat": torch.empty_like(W)}
+    J = np.zeros(max(n_J, 1), np.float64)
+    bpw = np.zeros(1, np.float64)
+    p1 = np.ascontiguousarray(perm1, dtype=np.int32)
+    p2 = None if perm2 is None else np.ascontiguousarray(perm2, dtype=np.int32)
+    if ws is None:
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    inputs = GroupedInputs(_ptr(W), _ptr(h), p1.ctypes.data, None if p2 is None else p2.ctypes.data)
+    outputs = GroupedOutputs(_ptr(o["cols"]), _ptr(o["idx"]), _ptr(o["codebooks"]), _ptr(o["row_ptr"]),
+                             _ptr(o["col"]), _ptr(o["val"]), _ptr(o["mask"]), _ptr(o["W_hat"]), J.ctypes.data,
+                             bpw.ctypes.data)
+    _check(load().vq_fit_grouped(ctypes.byref(params), ctypes.byref(inputs), ctypes.byref(outputs), _ptr(ws),
+                                 ws.numel(), _stream()))
+    o["col"] = o["col"][:nnz]
+    o["val"] = o["val"][:nnz]
+    o["J"] = J[:n_J]
+    o["bpw"] = float(bpw[0])
+    return o
+
+
 def timing_enable(on=True):
     load().vq_timing_enable(int(bool(on)))
 
@@ -327,7 +393,6 @@ def bits_per_weight(M, N, d, K1, K2, nnz, cb_bits=32, binorm=False):
 def fit(W, h, d, K1, iters1, K2=0, iters2=0, outlier_frac=0.0, binorm=False, mask_outliers=True,
         perm1=None, perm2=None, C1_init=None, C2_init=None, ws=None):
     """The whole pipeline on the GPU; returns a dict of device tensors + host J/bpw."""
-    import numpy as np
     M, N = W.shape
     dev = W.device
     n_sub = M * N // d

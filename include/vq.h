@@ -286,6 +286,68 @@ typedef struct {
 vq_status vq_fit(const vq_fit_params* p, const vq_fit_inputs* in, vq_fit_outputs* out,
                  void* ws, size_t ws_bytes, void* stream);
 
+/* Column groups (VPTQ page, "Outlier Elimination": the columns with the
+ * largest Hessian diagonal are held apart, quantized with a separate codebook
+ * of shorter vectors and more centroids; "Interaction with group
+ * partitioning": the other columns may be split into groups with independent
+ * codebooks).  The whole pipeline of vq_fit with its vector-quantization part
+ * run per column group:
+ *   select (on W, h) and bi-normalization, both on the whole matrix;
+ *   column order cols [N]: the n_out columns with the largest h (ties: the
+ *     smaller index) ascending, then the other columns ascending;
+ *   groups, in order: the outlier group cols[0, n_out) (d0, K0, iters0, one
+ *     stage) when n_out > 0; then the other columns in n_groups contiguous
+ *     runs of w = ceil(((N - n_out)/d) / n_groups) * d columns of the order
+ *     (the last may be shorter), each a two-stage fit with fit.d, K1, iters1,
+ *     K2, iters2;
+ *   each group gathers its columns of the (bi-normalized) matrix, column
+ *     weights, salient bits and column scales, is seeded from its own
+ *     permutation, runs its Lloyd stages, and is reconstructed (with the
+ *     scales, without the sparse part) back into its columns; the salient
+ *     values overwrite at the end.
+ * n_out must be a multiple of fit.d and of d0 (1 <= d0 <= 8).  Per-group
+ * arrays are concatenated in group order: idx = a group's stage-1 indices then
+ * its stage-2 indices (sub-vector ids of the group's own M x N_g matrix);
+ * codebooks = its C1 [K x d_g] then C2; J_hist its iters+1 (then iters2+1)
+ * objectives; perm1 (host) its stage-1 seeding order, perm2 (host) the
+ * stage-2 orders of the main groups.  vq_grouped_sizes returns the workspace
+ * bytes (0 when the sizes do not split) and the lengths of those arrays.
+ * Synchronizes. */
+typedef struct {
+    vq_fit_params fit;      /* the main groups and the salient selection */
+    int64_t n_out;          /* outlier columns; 0 = none */
+    int d0, K0, iters0;     /* the outlier group */
+    int n_groups;           /* groups of the other columns, >= 1 */
+} vq_grouped_params;
+
+typedef struct {
+    const float* W;         /* [M x N] */
+    const float* h;         /* [N] */
+    const int32_t* perm1;   /* host */
+    const int32_t* perm2;   /* host (unused when K2 = 0) */
+} vq_grouped_inputs;
+
+typedef struct {
+    int32_t* cols;          /* [N] column order */
+    uint16_t* idx;
+    float* codebooks;
+    int32_t* row_ptr; int32_t* col; float* val;   /* salient CSR, [M+1], [nnz], [nnz] */
+    uint8_t* mask;          /* [M*N/fit.d], the whole matrix's salient bits */
+    float* W_hat;           /* [M x N] */
+    double* J_hist;         /* host */
+    double* bpw;            /* host, nullable */
+} vq_grouped_outputs;
+
+size_t vq_grouped_sizes(const vq_grouped_params* p, int64_t* n_idx, int64_t* n_codebook, int64_t* n_J,
+                        int64_t* n_perm1, int64_t* n_perm2);
+vq_status vq_fit_grouped(const vq_grouped_params* p, const vq_grouped_inputs* in, vq_grouped_outputs* out,
+                         void* ws, size_t ws_bytes, void* stream);
+/* Bits per weight of a grouped fit: every group's index bits and 32-bit
+ * codebooks, 64 bits per salient weight plus the int32 row pointer, the
+ * scales (bi-normalization) and one int32 per outlier column, over M*N. */
+double vq_bits_per_weight_grouped(const vq_grouped_params* p);
+
+
 /* Bits per weight of the stored result (host arithmetic; VPTQ page,
  * "End-to-End Quantization Pipeline", compression ratio: index bits plus
  * codebook bits, extended by the sparse part and the scales):

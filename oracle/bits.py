@@ -34,6 +34,25 @@ def bits_per_weight(M, N, d, K1, K2, nnz, cb_bits=32, binorm=False):
     return bits / (M * N)
 
 
+def bits_per_weight_grouped(M, N, groups, nnz, n_out, cb_bits=32, binorm=False):
+    """Grouped form (VPTQ page, "Outlier Elimination" and its group partitioning:
+    every group stores its own indices and codebooks).  groups = [(N_g, d_g, K_g,
+    K2_g)]; one int32 per outlier column records which columns were held apart."""
+    bits = 0
+    for Ng, dg, Kg, K2g in groups:
+        ns = M * Ng // dg
+        bits += ns * (_index_bits(Kg) + (_index_bits(K2g) if K2g > 0 else 0))
+        bits += dg * (Kg + (K2g if K2g > 0 else 0)) * cb_bits
+    bits += 64 * nnz
+    if nnz > 0:
+        bits += 32 * (M + 1)
+    if binorm:
+        bits += 32 * (M + N)
+    if n_out > 0:
+        bits += 32 * n_out
+    return bits / (M * N)
+
+
 def compression_ratio_single(n_elem, V, k, orig_bits=16, cb_bits=16):
     """The page's ratio for one codebook: orig / (codebook + index bits)."""
     return (orig_bits * n_elem) / (V * k * cb_bits + n_elem * _index_bits(k) / V)

@@ -445,6 +445,24 @@ def pin_bits_worked_example(lib):
     assert abs(bpw - ex["original_bits"] / cr) < 1e-12
 
 
+def pin_bits_grouped_counts(lib):
+    """Grouped bits per weight: one group without outlier columns is the plain
+    count; a two-group case counted by hand; splitting a group in two adds
+    exactly one more set of codebooks."""
+    for d, K1, K2, nnz, bn in [(8, 256, 0, 0, False), (8, 4096, 256, 37, True), (4, 16, 4, 5, False)]:
+        a = O.bits_per_weight_grouped(32, 64, [(64, d, K1, K2)], nnz, 0, 32, bn)
+        assert a == O.bits_per_weight(32, 64, d, K1, K2, nnz, 32, bn)
+    # 16 x 24: outlier group 8 columns, v = 4, 16 centroids (32 sub-vectors x 4 bits,
+    # 4 x 16 x 16 codebook bits); main group 16 columns, v = 8, 256 + 4 centroids
+    # (32 sub-vectors x (8 + 2) bits, 8 x 260 x 16 codebook bits); 3 salient
+    # entries (64 bits each + 17 row pointers); bi-norm 16 + 24 scales; 8 column ids.
+    bits = 32 * 4 + 4 * 16 * 16 + 32 * 10 + 8 * 260 * 16 + 3 * 64 + 17 * 32 + 40 * 32 + 8 * 32
+    assert O.bits_per_weight_grouped(16, 24, [(8, 4, 16, 0), (16, 8, 256, 4)], 3, 8, 16, True) == bits / 384
+    one = O.bits_per_weight_grouped(64, 128, [(128, 8, 64, 8)], 0, 0, 32)
+    two = O.bits_per_weight_grouped(64, 128, [(64, 8, 64, 8), (64, 8, 64, 8)], 0, 0, 32)
+    assert (two - one) * 64 * 128 == 8 * (64 + 8) * 32
+
+
 def _tie_case(seed, M, N):
     """Tiny matrix with many exact score ties: weights and h from small sets."""
     g = np.random.default_rng([13, seed])

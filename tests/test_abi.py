@@ -1,6 +1,7 @@
 """The C ABI without a GPU: the library loads, exports every symbol that
 include/vq.h declares, and rejects bad arguments on the host before any
 device call.  (No compute call runs here.)"""
+import ctypes
 import os
 import re
 
@@ -116,3 +117,28 @@ def test_bits_per_weight_host_formula_matches_oracle():
             b = oracle.bits_per_weight(c.M, c.N, c.d, c.K1, c.K2, nz, cb, c.binorm)
             assert a == pytest.approx(b, rel=1e-15)
     assert vq.bits_per_weight(4096, 4096, 8, 256, 0, 0, 16) == pytest.approx(16 / 15.96880, rel=1e-6)
+
+
+def test_grouped_sizes_and_bits_match_oracle_layout():
+    """The library's group layout (array lengths) and grouped bits-per-weight
+    against the oracle's layout and closed form (host arithmetic only)."""
+    import oracle
+    for (M, N, d, K1, T1, K2, T2, p, binorm, n_out, d0, K0, T0, ng) in [
+            (24, 96, 8, 16, 4, 4, 3, 0.02, False, 16, 4, 24, 5, 2),
+            (4096, 11008, 8, 65536, 10, 256, 10, 0.01, True, 104, 4, 4096, 10, 1),
+            (64, 64, 8, 32, 2, 0, 0, 0.0, False, 0, 4, 0, 0, 3)]:
+        prm = vq.grouped_params(M, N, d, K1, T1, K2, T2, p, binorm, True, n_out, d0, K0, T0, ng)
+        ws, n_idx, n_cb, n_J, n_p1, n_p2 = vq.grouped_sizes(prm)
+        lay = oracle.grouped_layout(N, d, n_out, d0, K0, T0, ng, K1, T1, K2, T2)
+        assert ws > 0
+        assert n_idx == sum(M * Ng // dg * (2 if K2g else 1) for _, Ng, dg, _, _, K2g, _ in lay)
+        assert n_cb == sum((Kg + K2g) * dg for _, _, dg, Kg, _, K2g, _ in lay)
+        assert n_J == sum(Tg + 1 + (T2g + 1 if K2g else 0) for _, _, _, _, Tg, K2g, T2g in lay)
+        assert n_p1 == sum(M * Ng // dg for _, Ng, dg, _, _, _, _ in lay)
+        a = vq.load().vq_bits_per_weight_grouped(ctypes.byref(prm))
+        b = oracle.bits_per_weight_grouped(M, N, [(Ng, dg, Kg, K2g) for _, Ng, dg, Kg, _, K2g, _ in lay],
+                                           oracle.nnz(M, N, p), n_out, 32, binorm)
+        assert abs(a - b) <= 1e-12 * b, (a, b)
+    # sizes that do not split: n_out not a multiple of d, or an empty last group
+    assert vq.grouped_sizes(vq.grouped_params(8, 64, 8, 4, 1, 0, 0, 0.0, False, True, 12, 4, 4, 1, 1))[0] == 0
+    assert vq.grouped_sizes(vq.grouped_params(8, 72, 8, 4, 1, 0, 0, 0.0, False, True, 0, 4, 4, 1, 4))[0] == 0
