@@ -366,6 +366,64 @@ def vptq_bench(cfg, inp, run_oracle, V=8, B=128):
     return res
 
 
+def grouped_bench(cfg, inp, W, h, plain_ms, run_oracle, d0=4, K0=4096, n_groups=1, outlier_frac=0.0, reps=2):
+    """The grouped fit on the workload: the 1% of columns with the largest Hessian
+    diagonal (rounded down to a multiple of 8) held apart with a v = 4, 4096-centroid
+    codebook, the rest fitted as one group with the workload's codebooks.  The
+    outlier columns take the place of the per-weight salient set here (fraction 0 by
+    default), as in VPTQ's own configuration; with the workload's 1% salient weights
+    most of those columns' weights would be masked.  Wall time
+    per call beside the plain fit's step, the HIP-event time of the pieces the
+    grouping adds (column order, gathers, scatters), and the assignment rate over all
+    groups; the oracle's column order and one assignment pass over the outlier group,
+    both at the full size."""
+    import numpy as np
+    import torch
+
+    from hessian_weighted_vector_amd import vq
+    M, N, d = cfg.M, cfg.N, cfg.d
+    n_out = int(0.01 * N) // 8 * 8
+    prm = vq.grouped_params(M, N, d, cfg.K1, cfg.T1, cfg.K2, cfg.T2, outlier_frac, cfg.binorm, True, n_out, d0,
+                            K0, cfg.T1, n_groups)
+    wsb, n_idx, n_cb, n_J, n_p1, n_p2 = vq.grouped_sizes(prm)
+    ns0, ns1 = M * n_out // d0, M * (N - n_out) // d
+    assert n_groups == 1 and n_p1 == ns0 + ns1 and n_p2 == (ns1 if cfg.K2 else 0)
+    g = np.random.default_rng([cfg.cid, 99])
+    p1 = np.concatenate([g.permutation(ns0), g.permutation(ns1)]).astype(np.int32)
+    p2 = g.permutation(ns1).astype(np.int32) if cfg.K2 else None
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    vq.fit_grouped(W, h, prm, p1, p2, ws=ws)
+    torch.cuda.synchronize()
+    vq.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        out = vq.fit_grouped(W, h, prm, p1, p2, ws=ws)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / reps
+    recs = vq.timing_records()
+    vq.timing_enable(False)
+    added = sum(r[3] for r in recs if r[0] in ("column_order", "group_gather", "group_scatter")) / reps
+    col = [r for r in recs if r[0] == "column_order"]
+    iters = ns0 * cfg.T1 + ns1 * (cfg.T1 + cfg.T2)
+    res = {"n_out": n_out, "d0": d0, "K0": K0, "n_groups": n_groups, "outlier_frac": outlier_frac,
+           "ms": round(wall, 2),
+           "plain_fit_ms": round(plain_ms, 2), "ms_added_by_grouping": round(added, 3),
+           "column_order_ms": round(sum(r[3] for r in col) / reps, 4),
+           "G_subvector_assignments_per_s": round(iters / (wall * 1e-3) / 1e9, 4),
+           "bpw": round(out["bpw"], 4), "J_final_sum": float(out["J"][cfg.T1] + out["J"][-1])}
+    if run_oracle:
+        import oracle
+        t0 = time.perf_counter()
+        cols = oracle.column_order(inp["h"], n_out)
+        res["oracle_column_order_ms"] = round((time.perf_counter() - t0) * 1e3, 1)
+        Xo = np.ascontiguousarray(inp["W"][:, cols[:n_out]])
+        C0 = Xo.reshape(-1, d0)[np.sort(g.choice(ns0, K0, replace=False))].copy()
+        t0 = time.perf_counter()
+        oracle.assign(Xo, inp["h"][cols[:n_out]], None, None, d0, C0)
+        res["oracle_outlier_assign_pass_ms"] = round((time.perf_counter() - t0) * 1e3, 1)
+    return res
+
+
 def cpu_baseline(cfg, inp, seconds):
     """The oracle's assignment on a bounded sample (float64 exhaustive search)."""
     import numpy as np
@@ -405,6 +463,7 @@ def main():
     ap.add_argument("--no-qgemv", action="store_true", help="skip the fused dequantize-and-multiply rows")
     ap.add_argument("--no-correction", action="store_true", help="skip the unified sparse correction rows")
     ap.add_argument("--no-vptq", action="store_true", help="skip the VPTQ Algorithm 1 rows")
+    ap.add_argument("--no-grouped", action="store_true", help="skip the grouped-fit row")
     ap.add_argument("--breakdown", action="store_true", help="print per-step timings to stderr")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB three times (a plain "
@@ -511,6 +570,8 @@ def main():
     if not args.no_correction:
         extra["rows"]["NEXT3_unified_correction"] = correction_bench(cfg, inp, out, W, h, ws,
                                                                      not args.no_cpu_baseline)
+    if not args.no_grouped:
+        extra["rows"]["NEXT4_grouped_fit"] = grouped_bench(cfg, inp, W, h, ms_per_step, not args.no_cpu_baseline)
 
     line = {
         "metric": "sub-vectors assigned/s per Lloyd iter (G/s) + % FP32 peak; update/recon HBM GB/s",

@@ -4,8 +4,9 @@
 // codebooks).  The pieces the grouped fit adds to the plain fit:
 //   k_col_rank / k_col_order  the column order: the n_out columns with the
 //                             largest h (ties: smaller index) ascending, then
-//                             the rest ascending (ranks by comparison against
-//                             LDS tiles of h, then one block's scans);
+//                             the rest ascending (partial ranks by comparison
+//                             against LDS tiles of h over slices of the
+//                             columns, their sums, then one block's scans);
 //   k_gather_cols             a group's columns of a matrix (or of h, c);
 //   k_gather_mask             a group's salient bits, in its own sub-vector
 //                             layout (d_g bits per byte);
@@ -16,16 +17,23 @@ namespace vq {
 namespace {
 
 constexpr int kRankTile = 1024;
+constexpr int kRankSlicesMax = 32;
 
-__global__ __launch_bounds__(256) void k_col_rank(const float* __restrict__ h, int64_t N, int64_t n_out,
-                                                  uint8_t* __restrict__ flag)
+// Partial ranks: slice blockIdx.y of the columns k compares its h[k] with
+// every h[j] of this block; part[slice * N + j] counts the k that come before
+// j (larger h, or equal h and smaller index).  Slicing the k range gives the
+// launch enough workgroups to fill the chip for N of a few thousand.
+__global__ __launch_bounds__(256) void k_col_rank(const float* __restrict__ h, int64_t N, int64_t chunk,
+                                                  int32_t* __restrict__ part)
 {
     __shared__ float th[kRankTile];
     const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const float hj = j < N ? h[j] : 0.0f;
-    int64_t r = 0;
-    for (int64_t k0 = 0; k0 < N; k0 += kRankTile) {
-        const int kn = (int)(N - k0 < kRankTile ? N - k0 : kRankTile);
+    const int64_t ka = (int64_t)blockIdx.y * chunk;
+    const int64_t kb = ka + chunk < N ? ka + chunk : N;
+    int32_t r = 0;
+    for (int64_t k0 = ka; k0 < kb; k0 += kRankTile) {
+        const int kn = (int)(kb - k0 < kRankTile ? kb - k0 : kRankTile);
         __syncthreads();
         for (int q = threadIdx.x; q < kn; q += 256) th[q] = h[k0 + q];
         __syncthreads();
@@ -34,7 +42,19 @@ __global__ __launch_bounds__(256) void k_col_rank(const float* __restrict__ h, i
             r += (hk > hj) || (hk == hj && k0 + q < j);
         }
     }
-    if (j < N) flag[j] = r < n_out ? 1 : 0;
+    if (j < N) part[(int64_t)blockIdx.y * N + j] = r;
+}
+
+// Rank of column j = the sum of its slices' partial ranks; the n_out columns
+// of rank < n_out are flagged.
+__global__ __launch_bounds__(256) void k_col_flag(const int32_t* __restrict__ part, int nslice, int64_t N,
+                                                  int64_t n_out, uint8_t* __restrict__ flag)
+{
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= N) return;
+    int64_t r = 0;
+    for (int q = 0; q < nslice; ++q) r += part[(int64_t)q * N + j];
+    flag[j] = r < n_out ? 1 : 0;
 }
 
 // cols = [flagged columns ascending, unflagged columns ascending]; one block.
@@ -104,11 +124,21 @@ __global__ __launch_bounds__(256) void k_gather_mask(const uint8_t* __restrict__
 
 }  // namespace
 
-vq_status column_order_launch(const float* h, int64_t N, int64_t n_out, int32_t* cols, uint8_t* flag,
+int column_order_slices(int64_t N)
+{
+    const int64_t s = (N + 1023) / 1024 * 4;   // about 256 columns of k per slice
+    return (int)(s < 1 ? 1 : (s > kRankSlicesMax ? kRankSlicesMax : s));
+}
+
+vq_status column_order_launch(const float* h, int64_t N, int64_t n_out, int32_t* cols, uint8_t* flag, int32_t* part,
                               hipStream_t st)
 {
-    hipLaunchKernelGGL(k_col_rank, dim3(grid_for(N, 256)), dim3(256), 0, st, h, N, n_out, flag);
+    const int ns = column_order_slices(N);
+    const int64_t chunk = (N + ns - 1) / ns;
+    hipLaunchKernelGGL(k_col_rank, dim3(grid_for(N, 256), ns), dim3(256), 0, st, h, N, chunk, part);
     VQ_LAUNCHED("k_col_rank");
+    hipLaunchKernelGGL(k_col_flag, dim3(grid_for(N, 256)), dim3(256), 0, st, part, ns, N, n_out, flag);
+    VQ_LAUNCHED("k_col_flag");
     hipLaunchKernelGGL(k_col_order, dim3(1), dim3(1024), 0, st, flag, N, cols);
     VQ_LAUNCHED("k_col_order");
     return VQ_OK;

@@ -57,7 +57,8 @@ vq_status vptq_launch(const float*, const float*, int64_t, int64_t, int, const f
 vq_status hfactor_launch(const float*, int64_t, double, float*, void*, size_t, hipStream_t);
 vq_status sparse_overwrite_launch(int64_t, int64_t, const int32_t*, const int32_t*, const float*, float*,
                                   hipStream_t);
-vq_status column_order_launch(const float*, int64_t, int64_t, int32_t*, uint8_t*, hipStream_t);
+int column_order_slices(int64_t N);
+vq_status column_order_launch(const float*, int64_t, int64_t, int32_t*, uint8_t*, int32_t*, hipStream_t);
 vq_status gather_cols_launch(const float*, int64_t, int64_t, const int32_t*, int64_t, float*, hipStream_t);
 vq_status scatter_cols_launch(const float*, int64_t, int64_t, const int32_t*, float*, int64_t, hipStream_t);
 vq_status gather_mask_launch(const uint8_t*, int64_t, int64_t, int, const int32_t*, int64_t, int, uint8_t*,
@@ -631,7 +632,7 @@ size_t grouped_ws(const vq_grouped_params* p, const GroupTotals& t)
     if (p->fit.binorm)
         b += align_up((size_t)M * N * 4) + 2 * align_up((size_t)M * 4) + 2 * align_up((size_t)N * 4);
     b += 3 * align_up((size_t)t.max_elems * 4) + 2 * align_up((size_t)N * 4) + align_up((size_t)t.max_mask);
-    b += align_up((size_t)N) + align_up((size_t)t.n_J * 8);
+    b += align_up((size_t)N) + align_up((size_t)column_order_slices(N) * N * 4) + align_up((size_t)t.n_J * 8);
     return b + t.steps;
 }
 
@@ -722,6 +723,7 @@ vq_status vq_fit_grouped(const vq_grouped_params* p, const vq_grouped_inputs* in
     float* cg = cv.take<float>(N);
     uint8_t* mg = cv.take<uint8_t>(tot.max_mask);
     uint8_t* flag = cv.take<uint8_t>(N);
+    int32_t* part = cv.take<int32_t>((size_t)column_order_slices(N) * N);
     double* Jd = cv.take<double>(tot.n_J);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_fit_grouped: workspace too small");
     void* sws = cv.base + cv.used;
@@ -736,19 +738,25 @@ vq_status vq_fit_grouped(const vq_grouped_params* p, const vq_grouped_inputs* in
         X = Wp;
         hc = hcol;
     }
-    VQ_TRY(column_order_launch(in->h, N, p->n_out, out->cols, flag, st));
+    {
+        TimedRegion tr("column_order", 0, st);
+        VQ_TRY(column_order_launch(in->h, N, p->n_out, out->cols, flag, part, st));
+    }
 
     int64_t oi = 0, oc = 0, oj = 0, op1 = 0, op2 = 0;
     for (const GroupSpec& g : groups) {
         const int32_t* gc = out->cols + g.c0;
         const int64_t ns = M * g.Ng / g.d;
-        VQ_TRY(gather_cols_launch(X, M, N, gc, g.Ng, Xg, st));
-        VQ_TRY(gather_cols_launch(hc, 1, N, gc, g.Ng, hg, st));
-        if (f.binorm) VQ_TRY(gather_cols_launch(c, 1, N, gc, g.Ng, cg, st));
         const uint8_t* mk = nullptr;
-        if (f.mask_outliers) {
-            VQ_TRY(gather_mask_launch(out->mask, M, N, f.d, gc, g.Ng, g.d, mg, st));
-            mk = mg;
+        {
+            TimedRegion tr("group_gather", g.K, st);
+            VQ_TRY(gather_cols_launch(X, M, N, gc, g.Ng, Xg, st));
+            VQ_TRY(gather_cols_launch(hc, 1, N, gc, g.Ng, hg, st));
+            if (f.binorm) VQ_TRY(gather_cols_launch(c, 1, N, gc, g.Ng, cg, st));
+            if (f.mask_outliers) {
+                VQ_TRY(gather_mask_launch(out->mask, M, N, f.d, gc, g.Ng, g.d, mg, st));
+                mk = mg;
+            }
         }
         uint16_t* i1 = out->idx + oi;
         float* C1 = out->codebooks + oc;
@@ -769,6 +777,7 @@ vq_status vq_fit_grouped(const vq_grouped_params* p, const vq_grouped_inputs* in
         }
         VQ_TRY(reconstruct_launch(M, g.Ng, g.d, C1, g.K, i1, C2, g.K2, i2, f.binorm ? r : nullptr,
                                   f.binorm ? cg : nullptr, nullptr, nullptr, nullptr, Wg, st));
+        TimedRegion tr("group_scatter", g.K, st);
         VQ_TRY(scatter_cols_launch(Wg, M, g.Ng, gc, out->W_hat, N, st));
     }
     if (nnz > 0) VQ_TRY(sparse_overwrite_launch(M, N, out->row_ptr, out->col, out->val, out->W_hat, st));
