@@ -1,7 +1,10 @@
 """Builds libvq.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
 Every translation unit is compiled with -ffp-contract=off (no multiply-add is
-fused unless written as one) and with packed fp32 instructions disabled.
+fused unless written as one) and with packed fp32 instructions disabled.  The
+assignment search is compiled with -fno-honor-nans: its inputs are finite by
+contract, and without NaNs a minimum of accumulator values needs no quieting
+step (two VALU instructions fewer per tile in the search's inner loop).
 """
 import concurrent.futures
 import os
@@ -19,11 +22,12 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=o
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function", "-Wno-unused-result"]
+EXTRA = {"vq_assign.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, p.stderr))

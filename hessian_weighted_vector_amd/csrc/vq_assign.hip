@@ -630,9 +630,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
                           kt1, S_sc, shift_s, idx, dist, flag_count, flag_list);
 }
 
-// Sub-vectors that share one weight vector: workgroup = column block b x 256
-// consecutive rows (wavefront w: rows rb*256 + w*32 + (l & 31)), taken with
-// the block's majority mask byte.  Their common weights make
+// Sub-vectors that share one weight vector: workgroup = column block b x
+// 256*NS consecutive rows (wavefront w: NS sets of 32 rows, set u holding rows
+// (rb*8 + w)*32*NS + u*32 + (l & 31)), taken with the block's majority mask
+// byte.  Every A operand read from LDS feeds the MFMAs of all NS sets, so the
+// LDS traffic per MFMA falls as 1/NS.  Their common weights make
 // sum_t omega_t c_t^2 a per-centroid bias.  The workgroup forms it once per
 // chunk in float64 (rounded once to fp32), scales it by 2^sb and splits it
 // into two fp16 parts that enter the second MFMA through two k-slots against
@@ -645,8 +647,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
 // sum omega c*c, and the last MFMA adds 10 products to a small accumulator.
 // Lanes whose own mask byte differs from the block's are computed but not
 // written: they are in the list of the general kernel.
-template <bool SLOT>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_assign_h16s(
+template <bool SLOT, int NS>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS == 1 ? 4 : 3, 8))) void k_assign_h16s(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
     const uint8_t* __restrict__ mask, const uint8_t* __restrict__ pattern, int64_t M, int64_t nb, int d,
     const uint4* __restrict__ P, const float* __restrict__ cmax, const float* __restrict__ C, int K, int nchunks,
@@ -662,13 +664,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
     const int half = lane >> 5;
     const int64_t rb = (int64_t)blockIdx.x / nb;
     const int64_t b = (int64_t)blockIdx.x - rb * nb;
-    const int64_t i = rb * kSubPerBlock + wave * kSubPerWave + (lane & 31);
-    const bool active = rb * kSubPerBlock + wave * kSubPerWave < M;    // wave-uniform
-    const bool valid = i < M;
-    const int64_t s = valid ? i * nb + b : 0;
+    // NS sets of 32 rows per wave: set u holds rows w0 + u*32 + (l & 31)
+    const int64_t w0 = (rb * kWaves + wave) * (int64_t)(kSubPerWave * NS);
+    const bool active = w0 < M;                                   // wave-uniform
     const unsigned pat = pattern ? pattern[b] : 0u;
-    const unsigned mb = (valid && mask) ? mask[s] : 0u;
-    const bool owner = valid && mb == pat;
+    int64_t s[NS];
+    bool valid[NS], owner[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        const int64_t i = w0 + u * kSubPerWave + (lane & 31);
+        valid[u] = i < M;
+        s[u] = valid[u] ? i * nb + b : 0;
+        const unsigned mb = (valid[u] && mask) ? mask[s[u]] : 0u;
+        owner[u] = valid[u] && mb == pat;
+    }
 
     // the block's weights (its majority pattern), the same in every lane:
     // kept in scalar registers
@@ -689,22 +698,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
     if (bmax > 0.f) frexpf(bmax, &eb);
     const int sb = 15 - eb;                   // bias * 2^sb < 2^15
 
-    h16x8 bA, bB;    // B operands of the two MFMAs (per half)
-    float S_sc;
-    int shift_s;
-    bool bad;
-    {
+    h16x8 bA[NS], bB[NS];    // B operands of the two MFMAs (per half), per set
+    float S_sc[NS];
+    int shift_s[NS];
+    bool bad[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
         float raw[8];
         float S = 0.f, mx = 0.f;
         float xs[8];
-        if (valid && d == 8 && (reinterpret_cast<uintptr_t>(X) & 15u) == 0) {
-            const float4 x0 = reinterpret_cast<const float4*>(X)[(size_t)s * 2];
-            const float4 x1 = reinterpret_cast<const float4*>(X)[(size_t)s * 2 + 1];
+        if (valid[u] && d == 8 && (reinterpret_cast<uintptr_t>(X) & 15u) == 0) {
+            const float4 x0 = reinterpret_cast<const float4*>(X)[(size_t)s[u] * 2];
+            const float4 x1 = reinterpret_cast<const float4*>(X)[(size_t)s[u] * 2 + 1];
             xs[0] = x0.x; xs[1] = x0.y; xs[2] = x0.z; xs[3] = x0.w;
             xs[4] = x1.x; xs[5] = x1.y; xs[6] = x1.z; xs[7] = x1.w;
         } else {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) xs[t] = (valid && t < d) ? X[s * d + t] : 0.f;
+            for (int t = 0; t < 8; ++t) xs[t] = (valid[u] && t < d) ? X[s[u] * d + t] : 0.f;
         }
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -718,7 +728,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
         const int cap = sb + e1;                                  // keeps gamma <= 2^15
         const int sh = mx > 0.f ? min(15 - ex, cap) : cap;
         const int gexp = sh + (15 - e1) - sb;
-        bad = gexp < -24;
+        bad[u] = gexp < -24;
         h16x8 bh, bl;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -731,10 +741,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
         const _Float16 g = (_Float16)ldexpf(1.f, max(gexp, -24));
         gv[0] = g;
         gv[1] = g;
-        bA = half ? bl : bh;
-        bB = half ? gv : bh;
-        shift_s = sh + (15 - e1);
-        S_sc = ldexpf(S, shift_s);
+        bA[u] = half ? bl : bh;
+        bB[u] = half ? gv : bh;
+        shift_s[u] = sh + (15 - e1);
+        S_sc[u] = ldexpf(S, shift_s[u]);
     }
 
     // chunk staging: thread q copies one cross-term uint4 (tile q/64, row
@@ -785,16 +795,26 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
         }
     };
 
-    float b1 = __builtin_inff(), b2 = __builtin_inff();
-    int kt1 = 0;
+    float b1[NS], b2[NS];
+    int kt1[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        b1[u] = __builtin_inff();
+        b2[u] = __builtin_inff();
+        kt1[u] = 0;
+    }
     uint4 pre = load_cross(0);
     float4 r0, r1;
     load_row(0, r0, r1);
     store_chunk(0, 0, pre, r0, r1);
     __syncthreads();
 
-    f32x16 accA, accB;
-    for (int j = 0; j < 16; ++j) accB[j] = __builtin_inff();
+    // each set's A operands are read from LDS once per tile and used by the
+    // MFMAs of every set
+    f32x16 accA[NS], accB[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+        for (int j = 0; j < 16; ++j) accB[u][j] = __builtin_inff();
     int ktB = 0;
     const int a_off = half * 32 + (lane & 31);
     for (int c = 0; c < nchunks; ++c) {
@@ -811,10 +831,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
                 const uint4* A1 = A0 + 96;
                 const h16x8 p0 = __builtin_bit_cast(h16x8, A0[0]);
                 const h16x8 q0 = __builtin_bit_cast(h16x8, A0[32]);
-                accA = tile2_h16<SLOT>(p0, q0, bA, bB, accB, ktB, b1, b2, kt1);
+#pragma unroll
+                for (int u = 0; u < NS; ++u)
+                    accA[u] = tile2_h16<SLOT>(p0, q0, bA[u], bB[u], accB[u], ktB, b1[u], b2[u], kt1[u]);
                 const h16x8 p1 = __builtin_bit_cast(h16x8, A1[0]);
                 const h16x8 q1 = __builtin_bit_cast(h16x8, A1[32]);
-                accB = tile2_h16<SLOT>(p1, q1, bA, bB, accA, kt0 + tt, b1, b2, kt1);
+#pragma unroll
+                for (int u = 0; u < NS; ++u)
+                    accB[u] = tile2_h16<SLOT>(p1, q1, bA[u], bB[u], accA[u], kt0 + tt, b1[u], b2[u], kt1[u]);
                 ktB = kt0 + tt + 1;
             }
         }
@@ -822,9 +846,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
         __syncthreads();
     }
     if (!active) return;
-    track<SLOT>(accB, ktB, b1, b2, kt1);
-    search_epilogue<SLOT>(X, hcol, rho, mask, nb, d, C, K, s, valid, owner, bad, wsum == 0.f, lane, half, b1, b2,
-                          kt1, S_sc, shift_s, idx, dist, flag_count, flag_list);
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        track<SLOT>(accB[u], ktB, b1[u], b2[u], kt1[u]);
+        search_epilogue<SLOT>(X, hcol, rho, mask, nb, d, C, K, s[u], valid[u], owner[u], bad[u], wsum == 0.f, lane,
+                              half, b1[u], b2[u], kt1[u], S_sc[u], shift_s[u], idx, dist, flag_count, flag_list);
+    }
 }
 
 // Exact re-search of the flagged sub-vectors: one wavefront per flagged
@@ -917,6 +944,9 @@ __global__ __launch_bounds__(256) void k_assign_exact(
 
 // Centroids per LDS chunk; the split codebook is padded to whole chunks.
 constexpr int kChunkK = kChunkTiles * kTile;
+// Row sets of 32 per wave in the shared-weight search, and rows per workgroup.
+constexpr int kSharedSets = 2;
+constexpr int kSharedRows = kSubPerBlock * kSharedSets;
 
 inline int padded_K(int K) { return (K + kChunkK - 1) / kChunkK * kChunkK; }
 
@@ -949,7 +979,7 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
     uint8_t* pattern = cv.take<uint8_t>((size_t)nb);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_assign: workspace too small");
     if (n_sub > (int64_t)INT32_MAX) return fail(VQ_ERR_UNSUPPORTED, "vq_assign: more than 2^31 sub-vectors");
-    const int64_t shared_groups = (M + kSubPerBlock - 1) / kSubPerBlock * nb;
+    const int64_t shared_groups = (M + kSharedRows - 1) / kSharedRows * nb;
     if (shared_groups > (int64_t)UINT32_MAX) return fail(VQ_ERR_UNSUPPORTED, "vq_assign: grid too large");
 
     TimedRegion tr_all("assign", K, st);
@@ -980,7 +1010,7 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
             VQ_LAUNCHED("k_dirty");
         }
         // sub-vectors with their block's weights: two MFMAs per tile
-        hipLaunchKernelGGL(k_assign_h16s<false>, dim3((unsigned)shared_groups), dim3(kWaves * 64), 0, st, X, hcol,
+        hipLaunchKernelGGL((k_assign_h16s<false, kSharedSets>), dim3((unsigned)shared_groups), dim3(kWaves * 64), 0, st, X, hcol,
                            rho, mask, mask ? pattern : nullptr, M, nb, d, P, cmax, C, K, nch, idx, dist, flag_count,
                            flag_list);
         VQ_LAUNCHED("k_assign_h16s");
