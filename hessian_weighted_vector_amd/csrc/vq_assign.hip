@@ -648,7 +648,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
 // Lanes whose own mask byte differs from the block's are computed but not
 // written: they are in the list of the general kernel.
 template <bool SLOT, int NS>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS == 1 ? 4 : 3, 8))) void k_assign_h16s(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS == 1 ? 4 : (NS == 2 ? 3 : 2), 8))) void k_assign_h16s(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
     const uint8_t* __restrict__ mask, const uint8_t* __restrict__ pattern, int64_t M, int64_t nb, int d,
     const uint4* __restrict__ P, const float* __restrict__ cmax, const float* __restrict__ C, int K, int nchunks,
@@ -668,16 +668,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
     const int64_t w0 = (rb * kWaves + wave) * (int64_t)(kSubPerWave * NS);
     const bool active = w0 < M;                                   // wave-uniform
     const unsigned pat = pattern ? pattern[b] : 0u;
-    int64_t s[NS];
-    bool valid[NS], owner[NS];
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-        const int64_t i = w0 + u * kSubPerWave + (lane & 31);
-        valid[u] = i < M;
-        s[u] = valid[u] ? i * nb + b : 0;
-        const unsigned mb = (valid[u] && mask) ? mask[s[u]] : 0u;
-        owner[u] = valid[u] && mb == pat;
-    }
+    // Row i of set u, its sub-vector id s and whether its weights are the
+    // block's; formed before the main loop and again after it (r is passed
+    // through an empty asm so the second forming is not merged with the
+    // first: keeping these per-set values alive across the loop would spill).
+    auto row_of = [&](int u, int r, int64_t& s, bool& valid, bool& owner) {
+        const int64_t i = w0 + u * kSubPerWave + r;
+        valid = i < M;
+        s = valid ? i * nb + b : 0;
+        const unsigned mb = (valid && mask) ? mask[s] : 0u;
+        owner = valid && mb == pat;
+    };
 
     // the block's weights (its majority pattern), the same in every lane:
     // kept in scalar registers
@@ -698,23 +699,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
     if (bmax > 0.f) frexpf(bmax, &eb);
     const int sb = 15 - eb;                   // bias * 2^sb < 2^15
 
-    h16x8 bA[NS], bB[NS];    // B operands of the two MFMAs (per half), per set
-    float S_sc[NS];
-    int shift_s[NS];
-    bool bad[NS];
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
+    // The sub-vector's scaled split B operands, its scaled energy S_sc, its
+    // scale exponent and whether gamma underflows.
+    auto prep = [&](int64_t s, bool valid, h16x8& bA, h16x8& bB, float& S_sc, int& shift_s, bool& bad) {
         float raw[8];
         float S = 0.f, mx = 0.f;
         float xs[8];
-        if (valid[u] && d == 8 && (reinterpret_cast<uintptr_t>(X) & 15u) == 0) {
-            const float4 x0 = reinterpret_cast<const float4*>(X)[(size_t)s[u] * 2];
-            const float4 x1 = reinterpret_cast<const float4*>(X)[(size_t)s[u] * 2 + 1];
+        if (valid && d == 8 && (reinterpret_cast<uintptr_t>(X) & 15u) == 0) {
+            const float4 x0 = reinterpret_cast<const float4*>(X)[(size_t)s * 2];
+            const float4 x1 = reinterpret_cast<const float4*>(X)[(size_t)s * 2 + 1];
             xs[0] = x0.x; xs[1] = x0.y; xs[2] = x0.z; xs[3] = x0.w;
             xs[4] = x1.x; xs[5] = x1.y; xs[6] = x1.z; xs[7] = x1.w;
         } else {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) xs[t] = (valid[u] && t < d) ? X[s[u] * d + t] : 0.f;
+            for (int t = 0; t < 8; ++t) xs[t] = (valid && t < d) ? X[s * d + t] : 0.f;
         }
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -728,7 +726,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
         const int cap = sb + e1;                                  // keeps gamma <= 2^15
         const int sh = mx > 0.f ? min(15 - ex, cap) : cap;
         const int gexp = sh + (15 - e1) - sb;
-        bad[u] = gexp < -24;
+        bad = gexp < -24;
         h16x8 bh, bl;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -741,10 +739,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
         const _Float16 g = (_Float16)ldexpf(1.f, max(gexp, -24));
         gv[0] = g;
         gv[1] = g;
-        bA[u] = half ? bl : bh;
-        bB[u] = half ? gv : bh;
-        shift_s[u] = sh + (15 - e1);
-        S_sc[u] = ldexpf(S, shift_s[u]);
+        bA = half ? bl : bh;
+        bB = half ? gv : bh;
+        shift_s = sh + (15 - e1);
+        S_sc = ldexpf(S, shift_s);
+    };
+    h16x8 bA[NS], bB[NS];    // B operands of the two MFMAs (per half), per set
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        int64_t s;
+        bool valid, owner, bad;
+        float S_sc;
+        int shift_s;
+        row_of(u, lane & 31, s, valid, owner);
+        prep(s, valid, bA[u], bB[u], S_sc, shift_s, bad);
     }
 
     // chunk staging: thread q copies one cross-term uint4 (tile q/64, row
@@ -847,10 +855,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
     }
     if (!active) return;
 #pragma unroll
+    for (int u = 0; u < NS; ++u) track<SLOT>(accB[u], ktB, b1[u], b2[u], kt1[u]);
+#pragma unroll
     for (int u = 0; u < NS; ++u) {
-        track<SLOT>(accB[u], ktB, b1[u], b2[u], kt1[u]);
-        search_epilogue<SLOT>(X, hcol, rho, mask, nb, d, C, K, s[u], valid[u], owner[u], bad[u], wsum == 0.f, lane,
-                              half, b1[u], b2[u], kt1[u], S_sc[u], shift_s[u], idx, dist, flag_count, flag_list);
+        int r = lane & 31;
+        asm volatile("" : "+v"(r));
+        int64_t s;
+        bool valid, owner, bad;
+        float S_sc;
+        int shift_s;
+        h16x8 ua, ub;
+        row_of(u, r, s, valid, owner);
+        prep(s, valid, ua, ub, S_sc, shift_s, bad);
+        search_epilogue<SLOT>(X, hcol, rho, mask, nb, d, C, K, s, valid, owner, bad, wsum == 0.f, lane, half, b1[u],
+                              b2[u], kt1[u], S_sc, shift_s, idx, dist, flag_count, flag_list);
     }
 }
 
@@ -945,7 +963,7 @@ __global__ __launch_bounds__(256) void k_assign_exact(
 // Centroids per LDS chunk; the split codebook is padded to whole chunks.
 constexpr int kChunkK = kChunkTiles * kTile;
 // Row sets of 32 per wave in the shared-weight search, and rows per workgroup.
-constexpr int kSharedSets = 2;
+constexpr int kSharedSets = 4;
 constexpr int kSharedRows = kSubPerBlock * kSharedSets;
 
 inline int padded_K(int K) { return (K + kChunkK - 1) / kChunkK * kChunkK; }
