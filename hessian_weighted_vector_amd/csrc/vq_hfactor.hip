@@ -6,23 +6,24 @@
 // Route, all in float64: with P the reversal permutation, G = P Hd P has the
 // ordinary Cholesky factor L (G = L L^T), so Hd = (P L P)(P L P)^T with P L P
 // upper triangular and U = (P L P)^-1 = P L^-1 P.  Both L and L^-1 are formed
-// by right-looking blocked algorithms over panels of kNb columns:
-//   Cholesky:  factor the diagonal block in LDS (one workgroup), solve the
-//              panel below it (one thread per row), subtract the panel's
-//              outer product from the trailing lower triangle (GEMM);
-//   inverse:   X = I, then per block row i: X_i = L_ii^-1 X_i (one thread per
-//              column), and X_{i+1:} -= L_{i+1:, i} X_i over the columns X_i
-//              can be non-zero in (GEMM).
-// The GEMM is a 64 x 64-tile float64 kernel on the vector units (MI355X's
-// float64 vector and matrix rates are equal); each thread holds 4 x 4 sums.
+// by right-looking blocked algorithms over panels of kNo = 128 columns, each
+// worked as kNb = 32-column sub-panels:
+//   Cholesky:  factor the sub-panel's diagonal block in LDS (one workgroup),
+//              solve the sub-panel below it (one thread per row), subtract
+//              its outer product from the rest of the panel (GEMM); after the
+//              panel, one rank-128 update of the trailing lower triangle;
+//   inverse:   X = I, then per sub-block row: X_i = L_ii^-1 X_i (one thread
+//              per column) and X_{rows below in the block row} -= L X_i; after
+//              the block row, one rank-128 update of every row below over the
+//              columns the block row can be non-zero in.
+// The GEMMs run on the float64 matrix cores (128 x 64 workgroup tiles).
 #include "vq_internal.h"
 
 namespace vq {
 namespace {
 
-constexpr int kNb = 32;       // panel width
-constexpr int kGt = 64;       // GEMM output tile
-constexpr int kGk = 16;       // GEMM k chunk
+constexpr int kNb = 32;       // sub-panel width (factored in LDS)
+constexpr int kNo = 128;      // panel width (one trailing update per panel)
 
 // G[i][j] = H[N-1-i][N-1-j] in float64, plus damp * mean(diag H) on the
 // diagonal; mean from a fixed-order sum (one block).
@@ -153,66 +154,106 @@ __global__ __launch_bounds__(256) void k_trsm_rows(double* __restrict__ X, const
         if (r < ib) X[(i0 + r) * N + c] = x[r];
 }
 
-// C[m x n] -= A[m x k] * op(B); op(B)[kk][j] = B[j*ldb + kk] (TB) or
-// B[kk*ldb + j].  lower: only tiles whose columns start at or before the
-// tile's last row (the lower triangle of a square C).
+// C[m x n] -= A[m x k] * op(B) on the float64 matrix cores
+// (v_mfma_f64_16x16x4f64).  op(B)[kk][j] = B[j*ldb + kk] (TB) or
+// B[kk*ldb + j].  Workgroup tile 128 x 64: wavefront w owns rows
+// 32w .. 32w+31 as 2 x 4 blocks of 16 x 16; k moves through LDS in chunks of
+// 16 (double buffered, one barrier per chunk).  Operand layout of one MFMA:
+// lane l supplies A[l%16][l/16] and B[l/16][l%16]; it holds
+// D[l/16 + 4r][l%16] in element r of its accumulator (checked on the device
+// against a host product).  lower: only tiles
+// whose columns start at or before the tile's last row.
+constexpr int kDm = 128, kDn = 64, kDk = 16;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
 template <bool TB>
-__global__ __launch_bounds__(256) void k_gemm64(double* __restrict__ C, int64_t ldc, const double* __restrict__ A,
-                                                int64_t lda, const double* __restrict__ B, int64_t ldb, int64_t m,
-                                                int64_t n, int k, bool lower)
+__global__ __launch_bounds__(256) void k_dgemm(double* __restrict__ C, int64_t ldc, const double* __restrict__ A,
+                                               int64_t lda, const double* __restrict__ B, int64_t ldb, int64_t m,
+                                               int64_t n, int k, bool lower)
 {
-    __shared__ double As[kGk][kGt + 1];
-    __shared__ double Bs[kGk][kGt + 1];
-    const int64_t i0 = (int64_t)blockIdx.y * kGt, j0 = (int64_t)blockIdx.x * kGt;
-    if (lower && j0 > i0 + kGt - 1) return;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    double acc[4][4];
+    __shared__ double As[2][kDk][kDm + 2];
+    __shared__ double Bs[2][kDk][kDn + 2];
+    const int64_t i0 = (int64_t)blockIdx.y * kDm, j0 = (int64_t)blockIdx.x * kDn;
+    if (lower && j0 > i0 + kDm - 1) return;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    // staging: A row ar, k ak..ak+7; B (TB) column bc, k bk..bk+3, or (!TB) k bkk, columns bj..bj+3
+    const int ar = t >> 1, ak = (t & 1) * 8;
+    const int bc = t >> 2, bk = (t & 3) * 4;
+    const int bkk = t >> 4, bj = (t & 15) * 4;
+    double ra[8], rb[4];
+    auto load = [&](int k0) {
+        const int64_t gi = i0 + ar;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+        for (int q = 0; q < 8; ++q) {
+            const int kk = k0 + ak + q;
+            ra[q] = (gi < m && kk < k) ? A[gi * lda + kk] : 0.0;
+        }
+        if (TB) {
+            const int64_t gj = j0 + bc;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-    for (int k0 = 0; k0 < k; k0 += kGk) {
-        for (int q = threadIdx.x; q < kGk * kGt; q += 256) {
-            const int r = q / kGk, kk = q - r * kGk;           // A: row r, column kk
-            const int64_t gi = i0 + r;
-            As[kk][r] = (gi < m && k0 + kk < k) ? A[gi * lda + k0 + kk] : 0.0;
-            if (TB) {
-                const int64_t gj = j0 + r;
-                Bs[kk][r] = (gj < n && k0 + kk < k) ? B[gj * ldb + k0 + kk] : 0.0;
+            for (int q = 0; q < 4; ++q) {
+                const int kk = k0 + bk + q;
+                rb[q] = (gj < n && kk < k) ? B[gj * ldb + kk] : 0.0;
+            }
+        } else {
+            const int kk = k0 + bkk;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t gj = j0 + bj + q;
+                rb[q] = (gj < n && kk < k) ? B[(int64_t)kk * ldb + gj] : 0.0;
             }
         }
-        if (!TB) {
-            for (int q = threadIdx.x; q < kGk * kGt; q += 256) {
-                const int kk = q / kGt, c = q - kk * kGt;
-                const int64_t gj = j0 + c;
-                Bs[kk][c] = (gj < n && k0 + kk < k) ? B[(int64_t)(k0 + kk) * ldb + gj] : 0.0;
-            }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) As[buf][ak + q][ar] = ra[q];
+        if (TB) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Bs[buf][bk + q][bc] = rb[q];
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Bs[buf][bkk][bj + q] = rb[q];
         }
-        __syncthreads();
+    };
+    f64x4 acc[2][4];
 #pragma unroll
-        for (int kk = 0; kk < kGk; ++kk) {
-            double av[4], bv[4];
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) av[a] = As[kk][ty * 4 + a];
+        for (int b = 0; b < 4; ++b) acc[a][b] = (f64x4){0.0, 0.0, 0.0, 0.0};
+    const int nk = (k + kDk - 1) / kDk;
+    load(0);
+    store(0);
+    __syncthreads();
+    const int lr = lane & 15, lk = lane >> 4;
+    for (int c = 0; c < nk; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < nk) load((c + 1) * kDk);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) bv[b] = Bs[kk][tx * 4 + b];
+        for (int ks = 0; ks < kDk; ks += 4) {
+            double av[2], bv[4];
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 2; ++a) av[a] = As[buf][ks + lk][w * 32 + a * 16 + lr];
 #pragma unroll
-                for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
+            for (int b = 0; b < 4; ++b) bv[b] = Bs[buf][ks + lk][b * 16 + lr];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
         }
+        if (c + 1 < nk) store(buf ^ 1);
         __syncthreads();
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int64_t gi = i0 + ty * 4 + a;
-        if (gi >= m) continue;
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int64_t gj = j0 + tx * 4 + b;
-            if (gj < n) C[gi * ldc + gj] -= acc[a][b];
-        }
-    }
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t gi = i0 + w * 32 + a * 16 + lk + 4 * r;
+                const int64_t gj = j0 + b * 16 + lr;
+                if (gi < m && gj < n) C[gi * ldc + gj] -= acc[a][b][r];
+            }
 }
 
 }  // namespace
@@ -235,34 +276,62 @@ vq_status hfactor_launch(const float* H, int64_t N, double damp, float* U, void*
     VQ_LAUNCHED("k_diag_mean");
     hipLaunchKernelGGL(k_build_g, dim3(ge), dim3(256), 0, st, H, N, damp, mean, G);
     VQ_LAUNCHED("k_build_g");
-    // Cholesky, lower, in place
-    for (int64_t k0 = 0; k0 < N; k0 += kNb) {
-        const int kb = (int)(N - k0 < kNb ? N - k0 : kNb);
-        hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, st, G, N, k0, kb);
-        VQ_LAUNCHED("k_potrf_diag");
-        const int64_t rest = N - k0 - kb;
+    auto dgemm = [&](bool tb, double* Cp, const double* Ap, const double* Bp, int64_t m, int64_t n, int k,
+                     bool lower) {
+        const dim3 grid(grid_for(n, kDn), grid_for(m, kDm));
+        if (tb)
+            hipLaunchKernelGGL((k_dgemm<true>), grid, dim3(256), 0, st, Cp, N, Ap, N, Bp, N, m, n, k, lower);
+        else
+            hipLaunchKernelGGL((k_dgemm<false>), grid, dim3(256), 0, st, Cp, N, Ap, N, Bp, N, m, n, k, lower);
+    };
+    // Cholesky, lower, in place: panels of kNo columns, each factored as
+    // kNb-column sub-panels whose updates stay inside the panel; then one
+    // rank-kNo update of the trailing lower triangle.
+    for (int64_t K0 = 0; K0 < N; K0 += kNo) {
+        const int64_t K1 = K0 + kNo < N ? K0 + kNo : N;
+        for (int64_t k0 = K0; k0 < K1; k0 += kNb) {
+            const int kb = (int)(K1 - k0 < kNb ? K1 - k0 : kNb);
+            hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, st, G, N, k0, kb);
+            VQ_LAUNCHED("k_potrf_diag");
+            const int64_t rest = N - k0 - kb;
+            if (rest <= 0) break;
+            hipLaunchKernelGGL(k_trsm_panel, dim3(grid_for(rest, 256)), dim3(256), 0, st, G, N, k0, kb);
+            VQ_LAUNCHED("k_trsm_panel");
+            const int64_t wr = K1 - (k0 + kb);          // panel columns right of this sub-panel
+            if (wr > 0) {
+                const double* P = G + (k0 + kb) * N + k0;
+                dgemm(true, G + (k0 + kb) * N + (k0 + kb), P, P, rest, wr, kb, true);
+                VQ_LAUNCHED("k_dgemm");
+            }
+        }
+        const int64_t rest = N - K1;
         if (rest <= 0) break;
-        hipLaunchKernelGGL(k_trsm_panel, dim3(grid_for(rest, 256)), dim3(256), 0, st, G, N, k0, kb);
-        VQ_LAUNCHED("k_trsm_panel");
-        double* T = G + (k0 + kb) * N + (k0 + kb);
-        const double* P = G + (k0 + kb) * N + k0;
-        hipLaunchKernelGGL((k_gemm64<true>), dim3(grid_for(rest, kGt), grid_for(rest, kGt)), dim3(256), 0, st, T, N, P,
-                           N, P, N, rest, rest, kb, true);
-        VQ_LAUNCHED("k_gemm64");
+        const double* P = G + K1 * N + K0;
+        dgemm(true, G + K1 * N + K1, P, P, rest, rest, (int)(K1 - K0), true);
+        VQ_LAUNCHED("k_dgemm");
     }
-    // X = L^-1
+    // X = L^-1: block rows of kNo, each solved as kNb-row sub-blocks whose
+    // updates stay inside the block row; then one rank-kNo update of the rows
+    // below over the columns the block row can be non-zero in.
     hipLaunchKernelGGL(k_identity, dim3(ge), dim3(256), 0, st, X, N);
     VQ_LAUNCHED("k_identity");
-    for (int64_t i0 = 0; i0 < N; i0 += kNb) {
-        const int ib = (int)(N - i0 < kNb ? N - i0 : kNb);
-        const int64_t ncols = i0 + ib;
-        hipLaunchKernelGGL(k_trsm_rows, dim3(grid_for(ncols, 256)), dim3(256), 0, st, X, G, N, i0, ib, ncols);
-        VQ_LAUNCHED("k_trsm_rows");
-        const int64_t rest = N - i0 - ib;
+    for (int64_t I0 = 0; I0 < N; I0 += kNo) {
+        const int64_t I1 = I0 + kNo < N ? I0 + kNo : N;
+        for (int64_t i0 = I0; i0 < I1; i0 += kNb) {
+            const int ib = (int)(I1 - i0 < kNb ? I1 - i0 : kNb);
+            const int64_t ncols = i0 + ib;
+            hipLaunchKernelGGL(k_trsm_rows, dim3(grid_for(ncols, 256)), dim3(256), 0, st, X, G, N, i0, ib, ncols);
+            VQ_LAUNCHED("k_trsm_rows");
+            const int64_t rr = I1 - i0 - ib;                // block-row rows below this sub-block
+            if (rr > 0) {
+                dgemm(false, X + (i0 + ib) * N, G + (i0 + ib) * N + i0, X + i0 * N, rr, ncols, ib, false);
+                VQ_LAUNCHED("k_dgemm");
+            }
+        }
+        const int64_t rest = N - I1;
         if (rest <= 0) break;
-        hipLaunchKernelGGL((k_gemm64<false>), dim3(grid_for(ncols, kGt), grid_for(rest, kGt)), dim3(256), 0, st,
-                           X + (i0 + ib) * N, N, G + (i0 + ib) * N + i0, N, X + i0 * N, N, rest, ncols, ib, false);
-        VQ_LAUNCHED("k_gemm64");
+        dgemm(false, X + I1 * N, G + I1 * N + I0, X + I0 * N, rest, I1, (int)(I1 - I0), false);
+        VQ_LAUNCHED("k_dgemm");
     }
     hipLaunchKernelGGL(k_reverse_out, dim3(ge), dim3(256), 0, st, X, N, U);
     VQ_LAUNCHED("k_reverse_out");

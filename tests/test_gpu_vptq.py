@@ -146,11 +146,13 @@ def test_vptq_fullsize_sampled_rows():
 
 
 @pytest.mark.parametrize("N,T,damp", [(1, 4, 0.01), (5, 3, 0.01), (33, 40, 0.01), (64, 20, 0.1), (100, 300, 0.01),
-                                      (300, 64, 0.01)])
+                                      (129, 200, 0.01), (300, 64, 0.01), (517, 300, 0.01)])
 def test_hessian_factor_matches_oracle(N, T, damp):
     """U from the float64 Cholesky route against numpy's inverse-then-Cholesky
     (float64), both stored float32: |dU| <= 1e-5 max|U|; strict lower triangle 0.
-    T < N cases make X^T X singular, so the damping carries them."""
+    T < N cases make X^T X singular, so the damping carries them.  N = 129,
+    300 and 517 cross the 128-column panels (a one-column last panel, ragged
+    sub-panels)."""
     say("hessian factor N =", N)
     g = np.random.default_rng([71, N])
     X = g.standard_normal((T, N))
