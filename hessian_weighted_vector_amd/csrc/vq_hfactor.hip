@@ -6,24 +6,24 @@
 // Route, all in float64: with P the reversal permutation, G = P Hd P has the
 // ordinary Cholesky factor L (G = L L^T), so Hd = (P L P)(P L P)^T with P L P
 // upper triangular and U = (P L P)^-1 = P L^-1 P.  Both L and L^-1 are formed
-// by right-looking blocked algorithms over panels of kNo = 128 columns, each
+// by right-looking blocked algorithms over panels of kNo = 256 columns, each
 // worked as kNb = 32-column sub-panels:
 //   Cholesky:  factor the sub-panel's diagonal block in LDS (one workgroup),
 //              solve the sub-panel below it (one thread per row), subtract
 //              its outer product from the rest of the panel (GEMM); after the
-//              panel, one rank-128 update of the trailing lower triangle;
+//              panel, one rank-256 update of the trailing lower triangle;
 //   inverse:   X = I, then per sub-block row: X_i = L_ii^-1 X_i (one thread
 //              per column) and X_{rows below in the block row} -= L X_i; after
-//              the block row, one rank-128 update of every row below over the
+//              the block row, one rank-256 update of every row below over the
 //              columns the block row can be non-zero in.
-// The GEMMs run on the float64 matrix cores (128 x 64 workgroup tiles).
+// The GEMMs run on the float64 matrix cores (128 x 128 workgroup tiles).
 #include "vq_internal.h"
 
 namespace vq {
 namespace {
 
 constexpr int kNb = 32;       // sub-panel width (factored in LDS)
-constexpr int kNo = 128;      // panel width (one trailing update per panel)
+constexpr int kNo = 256;      // panel width (one trailing update per panel)
 
 // G[i][j] = H[N-1-i][N-1-j] in float64, plus damp * mean(diag H) on the
 // diagonal; mean from a fixed-order sum (one block).
@@ -156,18 +156,19 @@ __global__ __launch_bounds__(256) void k_trsm_rows(double* __restrict__ X, const
 
 // C[m x n] -= A[m x k] * op(B) on the float64 matrix cores
 // (v_mfma_f64_16x16x4f64).  op(B)[kk][j] = B[j*ldb + kk] (TB) or
-// B[kk*ldb + j].  Workgroup tile 128 x 64: wavefront w owns rows
-// 32w .. 32w+31 as 2 x 4 blocks of 16 x 16; k moves through LDS in chunks of
-// 16 (double buffered, one barrier per chunk).  Operand layout of one MFMA:
+// B[kk*ldb + j].  Workgroup tile 128 x 128, eight wavefronts: wavefront w
+// owns rows 32(w%4) .. +31 and columns 64(w/4) .. +63 as 2 x 4 blocks of
+// 16 x 16; k moves through LDS in chunks of 16 (double buffered, one barrier
+// per chunk).  Operand layout of one MFMA:
 // lane l supplies A[l%16][l/16] and B[l/16][l%16]; it holds
 // D[l/16 + 4r][l%16] in element r of its accumulator (checked on the device
 // against a host product).  lower: only tiles
 // whose columns start at or before the tile's last row.
-constexpr int kDm = 128, kDn = 64, kDk = 16;
+constexpr int kDm = 128, kDn = 128, kDk = 16;
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <bool TB>
-__global__ __launch_bounds__(256) void k_dgemm(double* __restrict__ C, int64_t ldc, const double* __restrict__ A,
+__global__ __launch_bounds__(512) void k_dgemm(double* __restrict__ C, int64_t ldc, const double* __restrict__ A,
                                                int64_t lda, const double* __restrict__ B, int64_t ldb, int64_t m,
                                                int64_t n, int k, bool lower)
 {
@@ -176,15 +177,16 @@ __global__ __launch_bounds__(256) void k_dgemm(double* __restrict__ C, int64_t l
     const int64_t i0 = (int64_t)blockIdx.y * kDm, j0 = (int64_t)blockIdx.x * kDn;
     if (lower && j0 > i0 + kDm - 1) return;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    // staging: A row ar, k ak..ak+7; B (TB) column bc, k bk..bk+3, or (!TB) k bkk, columns bj..bj+3
-    const int ar = t >> 1, ak = (t & 1) * 8;
+    const int wr = (w & 3) * 32, wc = (w >> 2) * 64;
+    // staging: A row ar, k ak..ak+3; B (TB) column bc, k bk..bk+3, or (!TB) k bkk, columns bj..bj+3
+    const int ar = t >> 2, ak = (t & 3) * 4;
     const int bc = t >> 2, bk = (t & 3) * 4;
-    const int bkk = t >> 4, bj = (t & 15) * 4;
-    double ra[8], rb[4];
+    const int bkk = t >> 5, bj = (t & 31) * 4;
+    double ra[4], rb[4];
     auto load = [&](int k0) {
         const int64_t gi = i0 + ar;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < 4; ++q) {
             const int kk = k0 + ak + q;
             ra[q] = (gi < m && kk < k) ? A[gi * lda + kk] : 0.0;
         }
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(256) void k_dgemm(double* __restrict__ C, int64_t l
     };
     auto store = [&](int buf) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) As[buf][ak + q][ar] = ra[q];
+        for (int q = 0; q < 4; ++q) As[buf][ak + q][ar] = ra[q];
         if (TB) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) Bs[buf][bk + q][bc] = rb[q];
@@ -232,9 +234,9 @@ __global__ __launch_bounds__(256) void k_dgemm(double* __restrict__ C, int64_t l
         for (int ks = 0; ks < kDk; ks += 4) {
             double av[2], bv[4];
 #pragma unroll
-            for (int a = 0; a < 2; ++a) av[a] = As[buf][ks + lk][w * 32 + a * 16 + lr];
+            for (int a = 0; a < 2; ++a) av[a] = As[buf][ks + lk][wr + a * 16 + lr];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) bv[b] = Bs[buf][ks + lk][b * 16 + lr];
+            for (int b = 0; b < 4; ++b) bv[b] = Bs[buf][ks + lk][wc + b * 16 + lr];
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -250,8 +252,8 @@ __global__ __launch_bounds__(256) void k_dgemm(double* __restrict__ C, int64_t l
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t gi = i0 + w * 32 + a * 16 + lk + 4 * r;
-                const int64_t gj = j0 + b * 16 + lr;
+                const int64_t gi = i0 + wr + a * 16 + lk + 4 * r;
+                const int64_t gj = j0 + wc + b * 16 + lr;
                 if (gi < m && gj < n) C[gi * ldc + gj] -= acc[a][b][r];
             }
 }
@@ -280,9 +282,9 @@ vq_status hfactor_launch(const float* H, int64_t N, double damp, float* U, void*
                      bool lower) {
         const dim3 grid(grid_for(n, kDn), grid_for(m, kDm));
         if (tb)
-            hipLaunchKernelGGL((k_dgemm<true>), grid, dim3(256), 0, st, Cp, N, Ap, N, Bp, N, m, n, k, lower);
+            hipLaunchKernelGGL((k_dgemm<true>), grid, dim3(512), 0, st, Cp, N, Ap, N, Bp, N, m, n, k, lower);
         else
-            hipLaunchKernelGGL((k_dgemm<false>), grid, dim3(256), 0, st, Cp, N, Ap, N, Bp, N, m, n, k, lower);
+            hipLaunchKernelGGL((k_dgemm<false>), grid, dim3(512), 0, st, Cp, N, Ap, N, Bp, N, m, n, k, lower);
     };
     // Cholesky, lower, in place: panels of kNo columns, each factored as
     // kNb-column sub-panels whose updates stay inside the panel; then one
