@@ -470,8 +470,8 @@ def main():
                          "copy of known size, to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(each weight matrix is fitted on one device); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: each weight matrix is fitted on one device and there "
+              "is no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
