@@ -53,8 +53,9 @@ def algorithmic_bytes_reconstruct(n_sub, M, N, d, K1, K2, nnz, binorm):
 
 
 def traffic_from_profile(kernel_src):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source (else None)."""
+    """HBM bytes per launch of the 4096 x 11008 workload's stage-1 search from the
+    committed counter summary, if it was taken on the current kernel source (else
+    None)."""
     path = os.path.join(ROOT, "profiles", "assign_search_c4_pmc.json")
     if not os.path.exists(path):
         return None
@@ -447,8 +448,9 @@ def cpu_baseline(cfg, inp, seconds):
         "unit": "G sub-vectors/s (one assignment pass, K=%d)" % cfg.K1,
         "cores": nthreads,
         "kind": "oracle",
-        "sample": "%d seeded sub-vectors of the 4096x11008 bi-normalized matrix assigned against the "
-                  "65536-centroid seed codebook (float64 direct form, exhaustive), %.1f s" % (done, t_total),
+        "sample": "%d seeded sub-vectors of the %dx%d%s matrix assigned against the %d-centroid seed "
+                  "codebook (float64 direct form, exhaustive), %.1f s"
+                  % (done, cfg.M, cfg.N, " bi-normalized" if cfg.binorm else "", cfg.K1, t_total),
     }
 
 
@@ -524,7 +526,7 @@ def main():
     src = os.path.join(ROOT, "hessian_weighted_vector_amd", "csrc", "vq_assign.hip")
     roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP16_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_MFMA_TFLOPS, 4),
-                "traffic": traffic_from_profile(src)}
+                "traffic": traffic_from_profile(src) if cfg.cid == 4 else None}
 
     extra = {"assign_stage1_ms": round(avg_s1, 3),
              "assign_stage1_Gsub_per_s": round(n_sub / (avg_s1 * 1e-3) / 1e9, 5),
