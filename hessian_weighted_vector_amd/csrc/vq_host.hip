@@ -119,6 +119,14 @@ constexpr int64_t kInitChunkMin = 65536;
 
 int64_t init_chunk(int64_t n_sub, int K) { return std::min<int64_t>(n_sub, std::max<int64_t>(2 * (int64_t)K, kInitChunkMin)); }
 
+// Slots of the device table for one chunk: a power of two, at least twice the chunk.
+int64_t init_table_cap(int64_t chunk)
+{
+    int64_t cap = 16;
+    while (cap < 2 * chunk) cap <<= 1;
+    return cap;
+}
+
 // Gathers the chunk's candidate sub-vectors in walk order.
 __global__ void k_gather(const float* __restrict__ X, const int32_t* __restrict__ perm, int64_t n, int d,
                          float* __restrict__ out)
@@ -128,6 +136,134 @@ __global__ void k_gather(const float* __restrict__ X, const int32_t* __restrict_
     const int64_t q = e / d;
     const int t = (int)(e - q * d);
     out[e] = X[(int64_t)perm[q] * d + t];
+}
+
+// Bitwise-distinct rows of the gathered chunk, on the device: an
+// open-addressing table keyed by the row's bits keeps, per distinct value,
+// the smallest walk position holding it (positions only ever go down, and a
+// slot's value never changes once claimed), so the outcome does not depend on
+// the order in which threads arrive.  A position is taken when it is the
+// first of its value; positions keep walk order through a block-wise scan.
+constexpr int kInitThreads = 1024;
+constexpr int32_t kInitEmpty = 0x7FFFFFFF;
+
+__device__ inline uint32_t row_hash(const uint32_t (&w)[8], int d)
+{
+    uint64_t hsh = 0x9E3779B97F4A7C15ull ^ (uint64_t)d;
+    for (int t = 0; t < d; ++t) {
+        hsh += w[t];
+        hsh ^= hsh >> 30;
+        hsh *= 0xBF58476D1CE4E5B9ull;
+        hsh ^= hsh >> 27;
+        hsh *= 0x94D049BB133111EBull;
+        hsh ^= hsh >> 31;
+    }
+    return (uint32_t)hsh;
+}
+
+__device__ inline void load_row_bits(const float* __restrict__ rows, int64_t q, int d, uint32_t (&w)[8])
+{
+#pragma unroll
+    for (int t = 0; t < 8; ++t) w[t] = t < d ? __float_as_uint(rows[q * d + t]) : 0u;
+}
+
+__device__ inline bool row_equal(const float* __restrict__ rows, int64_t r, int d, const uint32_t (&w)[8])
+{
+    for (int t = 0; t < d; ++t)
+        if (__float_as_uint(rows[r * d + t]) != w[t]) return false;
+    return true;
+}
+
+__global__ __launch_bounds__(256) void k_init_fill(int32_t* __restrict__ table, int64_t cap)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q < cap) table[q] = kInitEmpty;
+}
+
+__global__ __launch_bounds__(256) void k_init_insert(const float* __restrict__ rows, int64_t n, int d,
+                                                     int32_t* __restrict__ table, uint32_t cap_mask)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= n) return;
+    uint32_t w[8];
+    load_row_bits(rows, q, d, w);
+    uint32_t h = row_hash(w, d) & cap_mask;
+    for (;;) {
+        int32_t r = __atomic_load_n(&table[h], __ATOMIC_RELAXED);
+        if (r == kInitEmpty) {
+            r = atomicCAS(&table[h], kInitEmpty, (int32_t)q);
+            if (r == kInitEmpty) return;
+        }
+        if (row_equal(rows, r, d, w)) {
+            atomicMin(&table[h], (int32_t)q);
+            return;
+        }
+        h = (h + 1) & cap_mask;
+    }
+}
+
+// flag[q] = 1 when q is the first position of its value; per-block counts.
+__global__ __launch_bounds__(kInitThreads) void k_init_flag(const float* __restrict__ rows, int64_t n, int d,
+                                                            const int32_t* __restrict__ table, uint32_t cap_mask,
+                                                            int32_t* __restrict__ flag, int32_t* __restrict__ bcount)
+{
+    __shared__ int wsum[kInitThreads / 64];
+    const int64_t q = (int64_t)blockIdx.x * kInitThreads + threadIdx.x;
+    int f = 0;
+    if (q < n) {
+        uint32_t w[8];
+        load_row_bits(rows, q, d, w);
+        uint32_t h = row_hash(w, d) & cap_mask;
+        for (;;) {
+            const int32_t r = table[h];
+            if (r != kInitEmpty && row_equal(rows, r, d, w)) {
+                f = r == (int32_t)q;
+                break;
+            }
+            h = (h + 1) & cap_mask;
+        }
+        flag[q] = f;
+    }
+    const unsigned long long b = __ballot(f);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = __popcll(b);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int c = 0;
+        for (int k = 0; k < kInitThreads / 64; ++k) c += wsum[k];
+        bcount[blockIdx.x] = c;
+    }
+}
+
+// Exclusive scan of the block counts (one block); boff[nblk] = total.
+__global__ __launch_bounds__(256) void k_init_scan(const int32_t* __restrict__ bcount, int nblk,
+                                                   int32_t* __restrict__ boff)
+{
+    if (threadIdx.x != 0) return;
+    int run = 0;
+    for (int k = 0; k < nblk; ++k) {
+        boff[k] = run;
+        run += bcount[k];
+    }
+    boff[nblk] = run;
+}
+
+// The first K taken positions, in walk order, become the codebook rows.
+__global__ __launch_bounds__(kInitThreads) void k_init_write(const float* __restrict__ rows, int64_t n, int d,
+                                                             const int32_t* __restrict__ flag,
+                                                             const int32_t* __restrict__ boff, int K,
+                                                             float* __restrict__ C)
+{
+    __shared__ int wsum[kInitThreads / 64];
+    const int64_t q = (int64_t)blockIdx.x * kInitThreads + threadIdx.x;
+    const int f = q < n ? flag[q] : 0;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const unsigned long long b = __ballot(f);
+    if (lane == 0) wsum[wave] = __popcll(b);
+    __syncthreads();
+    int pos = boff[blockIdx.x] + __popcll(b & ((1ull << lane) - 1ull));
+    for (int k = 0; k < wave; ++k) pos += wsum[k];
+    if (f && pos < K)
+        for (int t = 0; t < d; ++t) C[(int64_t)pos * d + t] = rows[q * d + t];
 }
 
 uint64_t mix64(const uint32_t* w, int d)
@@ -155,6 +291,39 @@ vq_status init_walk(const float* X, int64_t n_sub, int d, const int32_t* perm, i
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_init: workspace too small");
 
     TimedRegion tr("init", K, st);
+    {
+        // the first chunk on the device; if it holds fewer than K distinct
+        // rows, the walk is done again below on the host, chunk by chunk
+        const int64_t n = chunk;
+        for (int64_t q = 0; q < n; ++q)
+            if (perm[q] < 0 || perm[q] >= n_sub) return fail(VQ_ERR_INVALID, "perm holds an id outside [0, n_sub)");
+        const int64_t cap = init_table_cap(chunk);
+        const int nblk = (int)((n + kInitThreads - 1) / kInitThreads);
+        int32_t* table = cv.take<int32_t>((size_t)cap);
+        int32_t* flag = cv.take<int32_t>((size_t)chunk);
+        int32_t* bcount = cv.take<int32_t>((size_t)nblk);
+        int32_t* boff = cv.take<int32_t>((size_t)nblk + 1);
+        if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_init: workspace too small");
+        VQ_HIP(hipMemcpyAsync(dperm, perm, (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice, st));
+        hipLaunchKernelGGL(k_gather, dim3(grid_for(n * d, 256)), dim3(256), 0, st, X, dperm, n, d, dbuf);
+        VQ_LAUNCHED("k_gather");
+        hipLaunchKernelGGL(k_init_fill, dim3(grid_for(cap, 256)), dim3(256), 0, st, table, cap);
+        VQ_LAUNCHED("k_init_fill");
+        hipLaunchKernelGGL(k_init_insert, dim3(grid_for(n, 256)), dim3(256), 0, st, dbuf, n, d, table,
+                           (uint32_t)(cap - 1));
+        VQ_LAUNCHED("k_init_insert");
+        hipLaunchKernelGGL(k_init_flag, dim3(nblk), dim3(kInitThreads), 0, st, dbuf, n, d, table,
+                           (uint32_t)(cap - 1), flag, bcount);
+        VQ_LAUNCHED("k_init_flag");
+        hipLaunchKernelGGL(k_init_scan, dim3(1), dim3(256), 0, st, bcount, nblk, boff);
+        VQ_LAUNCHED("k_init_scan");
+        hipLaunchKernelGGL(k_init_write, dim3(nblk), dim3(kInitThreads), 0, st, dbuf, n, d, flag, boff, K, C);
+        VQ_LAUNCHED("k_init_write");
+        int32_t total = 0;
+        VQ_HIP(hipMemcpyAsync(&total, boff + nblk, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+        VQ_HIP(hipStreamSynchronize(st));
+        if (total >= K) return VQ_OK;
+    }
     std::vector<float> host((size_t)chunk * d);
     std::vector<float> taken_rows((size_t)K * d);
     size_t cap = 16;
@@ -241,7 +410,10 @@ size_t ws_steps(int64_t M, int64_t N, int d, int K1, int K2)
 size_t ws_init(int64_t n_sub, int K, int d)
 {
     const int64_t chunk = init_chunk(n_sub, K);
-    return align_up((size_t)chunk * sizeof(int32_t)) + align_up((size_t)chunk * d * sizeof(float));
+    const int64_t nblk = (chunk + kInitThreads - 1) / kInitThreads;
+    return align_up((size_t)chunk * sizeof(int32_t)) + align_up((size_t)chunk * d * sizeof(float)) +
+           align_up((size_t)init_table_cap(chunk) * sizeof(int32_t)) + align_up((size_t)chunk * sizeof(int32_t)) +
+           align_up((size_t)nblk * sizeof(int32_t)) + align_up((size_t)(nblk + 1) * sizeof(int32_t));
 }
 
 }  // namespace vq

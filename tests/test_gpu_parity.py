@@ -284,6 +284,24 @@ def test_init_matches_oracle_bitwise():
             assert bits_equal(host(vq.init(dev(W), 8, inp["perm1"], K, ws)), Cref)
 
 
+def test_init_walk_beyond_first_chunk_matches_oracle():
+    """The device dedupes the first chunk of the walk (65536 positions here); when
+    that chunk holds fewer than K distinct rows the walk is done again on the host
+    and continues into the next chunk.  Both paths against the oracle, bitwise."""
+    say("init beyond the first chunk")
+    g = np.random.default_rng([52, 0])
+    M, N, d = 1024, 1024, 8
+    W = (0.02 * g.standard_normal((M, N))).astype(np.float32)
+    perm = g.permutation(M * N // d).astype(np.int32)
+    base = (0.02 * g.standard_normal((500, d))).astype(np.float32)
+    W.reshape(-1, d)[perm[:65536]] = base[np.arange(65536) % 500]    # 500 distinct rows in the first chunk
+    for K in (400, 1000):
+        Cref, taken = oracle.init(W, d, perm, K)
+        assert taken == K
+        ws = vq.workspace(M, N, d, K)
+        assert bits_equal(host(vq.init(dev(W), d, perm, K, ws)), Cref)
+
+
 def test_residual_and_reconstruct_bitwise():
     say("residual + reconstruct")
     W, h, C, keep, rho = _case(61, 128, 256, 8, 64)
