@@ -228,8 +228,10 @@ vq_status vq_hessian_factor(const float* H, int64_t N, double damp, float* U, vo
 /* Second-order error propagation with column sub-vectors (VPTQ page, "The
  * Core Algorithm", Algorithm 1).  Columns of W [M x N] are quantized left to
  * right in blocks of B: each of a column's M/V sub-vectors W[m:m+V, n] takes
- * its nearest row of C [K x V] under the plain Euclidean distance (float32,
- * direct form; the lowest index among equal distances); the column's error
+ * its nearest row of C [K x V] under the plain Euclidean distance (the
+ * lowest index among equal scores; V = 8 with C 16-byte aligned and M % 4 == 0:
+ * expanded form |c|^2/2 - <c, x> on the fp16 matrix cores with split fp16
+ * operands, error at float32 level; other V: direct form in float32); the column's error
  * E[:,n] = (W[:,n] - What[:,n]) / U[n,n] is subtracted, times U[n,j], from the
  * block's later columns j, and at the block's end E[:, s:s+B] U[s:s+B, s+B:]
  * is subtracted from every later column.  U [N x N] row-major is the matrix
@@ -240,7 +242,8 @@ vq_status vq_hessian_factor(const float* H, int64_t N, double damp, float* U, vo
  * rows), E [M x N] (nullable).  Arithmetic: float32 state; the block update
  * runs on the float32 matrix cores.  1 <= V <= 8 with M % V == 0;
  * 1 <= K <= 65536; 1 <= B <= 128.  Bitwise reproducible.  Workspace:
- * vq_vptq_workspace_bytes(M, N, V) (three transposed M x N copies). */
+ * vq_vptq_workspace_bytes(M, N, V) (three transposed M x N copies, the
+ * split codebook, per-column keys). */
 size_t vq_vptq_workspace_bytes(int64_t M, int64_t N, int V);
 vq_status vq_vptq(const float* W, const float* U, int64_t M, int64_t N, int V, const float* C, int K, int B,
                   uint16_t* idx, float* W_hat, float* E, void* ws, size_t ws_bytes, void* stream);
