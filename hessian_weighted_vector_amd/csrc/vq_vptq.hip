@@ -10,21 +10,26 @@
 // column n of W, contiguous), and the quantized matrix and the errors are
 // kept transposed too; they are transposed back at the end.
 //
-// Per column, two launches:
-//   k_col_assign   the M/V x K distances of the column; V = 8 on the fp16
-//                  matrix cores with split operands (k_col_assign_h16,
-//                  expanded form, the codebook prepared once per call), other
-//                  V in the direct form on the vector units; workgroups split K,
-//                  each stages its centroids in LDS, and the per-sub-vector
-//                  minima meet in a packed 64-bit atomicMin of (score bits,
-//                  index): the order of arrival does not matter, and equal
-//                  scores keep the lowest index;
+// V = 8 (C 16-byte aligned, M % 4 == 0): one launch per column,
+//   k_col_step_h16 finishes column n-1 (its winner, value and error, the
+//                  error's share of the block's later columns) and searches
+//                  column n on the fp16 matrix cores with split operands
+//                  (expanded form, the codebook prepared once per call by
+//                  k_vp_absmax and k_vp_prep); workgroups split K, and the
+//                  per-sub-vector minima meet in a packed 64-bit atomicMin of
+//                  (score bits, index): the order of arrival does not matter,
+//                  and equal scores keep the lowest index;
+//   k_col_last     finishes the block's last column.
+// Other V, two launches per column:
+//   k_col_assign   the direct form in float32 on the vector units, merged the
+//                  same way;
 //   k_col_finalize reads the winners, writes indices, What and E, clears the
 //                  other key buffer for the next column, and applies the
 //                  in-block update to the rows j of the block (a 2D grid over
 //                  elements and groups of rows).
 // Per block: k_block_gemm, Wt[s+B:, :] -= U[s:s+B, s+B:]^T Et[s:s+B, :], a
-// float32 matrix-core GEMM (v_mfma_f32_32x32x2f32) over LDS panels.
+// float32 matrix-core GEMM (v_mfma_f32_32x32x2f32) over double-buffered LDS
+// panels.
 #include "vq_internal.h"
 
 namespace vq {
@@ -35,8 +40,6 @@ constexpr int kAsgThreads = 256;
 constexpr int kAsgChunk = 256;      // centroids per assignment workgroup
 constexpr int kFinThreads = 256;
 constexpr int kFinRows = 16;        // in-block rows per finalize workgroup
-constexpr int kGemmTile = 64;       // output tile of the block update
-constexpr int kGemmMaxK = 128;      // largest block size the GEMM stages at once
 
 // dst [Cc x R] = src [R x Cc]^T through a padded LDS tile.
 __global__ __launch_bounds__(256) void k_transpose(const float* __restrict__ src, int64_t R, int64_t Cc,
@@ -363,45 +366,80 @@ __global__ __launch_bounds__(kFinThreads) void k_col_finalize(
 }
 
 // Wt[s_end + r, m] -= sum_k U[s + k, s_end + r] * Et[s + k, m], k < kb, for a
-// 64 x 64 tile of (r, m).  The U and Et panels of the tile sit in LDS with k
-// as the slow index; each of the 4 wavefronts accumulates one 32 x 32 block
-// with v_mfma_f32_32x32x2f32 (lane l feeds A[l%32][l/32] and B[l/32][l%32]).
-__global__ __launch_bounds__(256) void k_block_gemm(float* __restrict__ Wt, const float* __restrict__ U,
+// 128 x 128 tile of (r, m).  k runs in chunks of kGemmK through double-buffered
+// LDS panels (k the slow index; the next chunk is loaded into registers while
+// the current one is used, one barrier per chunk).  Each of the 8 wavefronts
+// accumulates a 32 x 64 block as two 32 x 32 blocks of v_mfma_f32_32x32x2f32
+// (lane l feeds A[l%32][l/32] and B[l/32][l%32]); k pairs are taken in
+// increasing order.
+constexpr int kGemmT = 128;          // output tile edge
+constexpr int kGemmK = 16;           // k per LDS chunk
+constexpr int kGemmLd = kGemmT + 4;  // padded LDS row
+
+__global__ __launch_bounds__(512) void k_block_gemm(float* __restrict__ Wt, const float* __restrict__ U,
                                                     const float* __restrict__ Et, int64_t N, int64_t M,
                                                     int64_t s, int kb, int64_t s_end)
 {
-    __shared__ float As[kGemmMaxK][kGemmTile];
-    __shared__ float Bs[kGemmMaxK][kGemmTile];
+    __shared__ float As[2][kGemmK][kGemmLd];
+    __shared__ float Bs[2][kGemmK][kGemmLd];
     const int64_t R = N - s_end;
-    const int64_t r0 = (int64_t)blockIdx.y * kGemmTile, m0 = (int64_t)blockIdx.x * kGemmTile;
-    const int kp = (kb + 1) & ~1;   // padded to the MFMA's k of 2
-    for (int q = threadIdx.x; q < kp * kGemmTile; q += 256) {
-        const int k = q / kGemmTile, c = q - k * kGemmTile;
-        const int64_t r = r0 + c, mm = m0 + c;
-        As[k][c] = (k < kb && r < R) ? U[(s + k) * N + s_end + r] : 0.0f;
-        Bs[k][c] = (k < kb && mm < M) ? Et[(s + k) * M + mm] : 0.0f;
-    }
-    __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;
+    const int64_t r0 = (int64_t)blockIdx.y * kGemmT, m0 = (int64_t)blockIdx.x * kGemmT;
+    const int tid = threadIdx.x;
+    // loader: thread -> (k = tid / 32, columns 4 * (tid % 32) .. + 4) of each panel
+    const int lk_ = tid >> 5, lc = (tid & 31) * 4;
+    float ra[4], rb[4];
+    auto load = [&](int kc) {
+        const int k = kc + lk_;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t r = r0 + lc + i, mm = m0 + lc + i;
+            ra[i] = (k < kb && r < R) ? U[(s + k) * N + s_end + r] : 0.0f;
+            rb[i] = (k < kb && mm < M) ? Et[(s + k) * M + mm] : 0.0f;
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            As[buf][lk_][lc + i] = ra[i];
+            Bs[buf][lk_][lc + i] = rb[i];
+        }
+    };
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wr = (wave & 3) * 32, wc = (wave >> 2) * 64;
     const int li = lane & 31, lk = lane >> 5;
     typedef float f16x_t __attribute__((ext_vector_type(16)));
-    f16x_t acc;
+    f16x_t acc0, acc1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    for (int k = 0; k < kp; k += 2) {
-        const float a = As[k + lk][wr + li];
-        const float b = Bs[k + lk][wc + li];
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    for (int r = 0; r < 16; ++r) { acc0[r] = 0.0f; acc1[r] = 0.0f; }
+    const int nk = (kb + kGemmK - 1) / kGemmK;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int c = 0; c < nk; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < nk) load((c + 1) * kGemmK);
+#pragma unroll
+        for (int kk = 0; kk < kGemmK; kk += 2) {
+            const float a = As[buf][kk + lk][wr + li];
+            const float b0 = Bs[buf][kk + lk][wc + li];
+            const float b1 = Bs[buf][kk + lk][wc + 32 + li];
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b0, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b1, acc1, 0, 0, 0);
+        }
+        if (c + 1 < nk) store(buf ^ 1);
+        __syncthreads();
     }
-    const int64_t mm = m0 + wc + li;
-    if (mm >= M) return;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int64_t row = r0 + wr + (r >> 2) * 8 + lk * 4 + (r & 3);
-        if (row < R) {
-            float* p = Wt + (s_end + row) * M + mm;
-            *p = *p - acc[r];
+    for (int h = 0; h < 2; ++h) {
+        const int64_t mm = m0 + wc + h * 32 + li;
+        if (mm >= M) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t row = r0 + wr + (r >> 2) * 8 + lk * 4 + (r & 3);
+            if (row < R) {
+                float* p = Wt + (s_end + row) * M + mm;
+                *p = *p - (h ? acc1[r] : acc0[r]);
+            }
         }
     }
 }
@@ -479,8 +517,8 @@ vq_status vptq_launch(const float* W, const float* U, int64_t M, int64_t N, int 
         }
         if (s_end < N) {
             TimedRegion tg("vptq_block_update", K, st);
-            const dim3 gg(grid_for(M, kGemmTile), grid_for(N - s_end, kGemmTile));
-            hipLaunchKernelGGL(k_block_gemm, gg, dim3(256), 0, st, Wt, U, Et, N, M, s, (int)(s_end - s), s_end);
+            const dim3 gg(grid_for(M, kGemmT), grid_for(N - s_end, kGemmT));
+            hipLaunchKernelGGL(k_block_gemm, gg, dim3(512), 0, st, Wt, U, Et, N, M, s, (int)(s_end - s), s_end);
             VQ_LAUNCHED("k_block_gemm");
         }
     }
