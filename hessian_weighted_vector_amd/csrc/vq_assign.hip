@@ -917,8 +917,7 @@ __global__ __launch_bounds__(256) void k_assign_exact(
         float thr = __builtin_inff();
         double dbest = __builtin_inf();
         int arg = K;
-        for (int k = lane; k < K; k += 64) {
-            float c[8];
+        auto load_c = [&](int k, float* c) {
             if (vecC) {   // d == 8 and a 16-byte aligned codebook
                 const float4 ca = reinterpret_cast<const float4*>(C)[(size_t)k * 2];
                 const float4 cb = reinterpret_cast<const float4*>(C)[(size_t)k * 2 + 1];
@@ -928,6 +927,8 @@ __global__ __launch_bounds__(256) void k_assign_exact(
 #pragma unroll
                 for (int t = 0; t < 8; ++t) c[t] = t < d ? C[(size_t)k * d + t] : 0.f;
             }
+        };
+        auto visit = [&](int k, const float* c) {
             float e = 0.f;
 #pragma unroll
             for (int t = 0; t < 8; ++t) e = fmaf(bw2[t], c[t], e);
@@ -945,6 +946,25 @@ __global__ __launch_bounds__(256) void k_assign_exact(
                 }
                 if (acc < dbest) { dbest = acc; arg = k; }
             }
+        };
+        // a lane's centroids k = lane, lane + 64, ... in increasing order; the
+        // rows of four steps are loaded before any of them is visited
+        int k = lane;
+        for (; k + 192 < K; k += 256) {
+            float c0[8], c1[8], c2[8], c3[8];
+            load_c(k, c0);
+            load_c(k + 64, c1);
+            load_c(k + 128, c2);
+            load_c(k + 192, c3);
+            visit(k, c0);
+            visit(k + 64, c1);
+            visit(k + 128, c2);
+            visit(k + 192, c3);
+        }
+        for (; k < K; k += 64) {
+            float c[8];
+            load_c(k, c);
+            visit(k, c);
         }
         for (int off = 32; off > 0; off >>= 1) {
             const double od = __shfl_xor(dbest, off);
