@@ -20,8 +20,9 @@ The bar, per group of V rows and column by column:
     W_n the working column the error is taken from (W_n = What_n + U_nn E_n).
 At most 1% of groups may part.  Cases cover V = 8 (vector path) and V = 4, 6
 (scalar path), K below, at and across 256-centroid chunks, K = 1, blocks that
-do not divide N, B > N, B = 1, U = I, and the 4096 x 11008 workload on eight
-sampled row groups.
+do not divide N, B > N, B = 1, U = I, an unaligned codebook (direct form for
+V = 8), working values 1e-6 and 1e4 times the codebook's scale, an all-zero
+codebook, and the 4096 x 11008 workload on eight sampled row groups.
 """
 import sys
 
@@ -142,6 +143,48 @@ def test_vptq_reproducible():
     for x, y in zip(a[0], a[1]):
         assert torch.equal(x.view(torch.int16) if x.dtype == torch.uint16 else x.view(torch.int32),
                            y.view(torch.int16) if y.dtype == torch.uint16 else y.view(torch.int32))
+
+
+def test_vptq_unaligned_codebook_takes_the_direct_form():
+    """V = 8 with a codebook that is not 16-byte aligned runs the direct-form
+    search (the split fp16 path needs aligned rows); both meet the oracle."""
+    say("vptq unaligned codebook")
+    W, U, C = make_case(9, 48, 70, 8, 300)
+    buf = torch.empty(C.size + 1, dtype=torch.float32, device="cuda")
+    Cu = buf[1:].view(C.shape)
+    Cu.copy_(torch.from_numpy(C))
+    assert Cu.data_ptr() % 16 != 0
+    idx, What, E = vq.vptq(dev(W), dev(U), 8, Cu, 16, want_E=True)
+    nv, parted = compare(W, U, C, 8, 16, host(idx).reshape(70, 6), host(What), host(E))
+    assert parted <= 1
+
+
+@pytest.mark.parametrize("wscale", [1e-6, 1e4])
+def test_vptq_scale_extremes(wscale):
+    """Working values far below or far above the codebook's scale: the
+    per-wavefront power-of-two scale is clamped (tiny columns) or the norm
+    term's factor shrinks (huge columns); the oracle is met either way."""
+    say("vptq scale", wscale)
+    W, U, C = make_case(10, 64, 40, 8, 200)
+    idx, What, E = vq.vptq(dev(W * np.float32(wscale)), dev(U), 8, dev(C), 8, want_E=True)
+    nv, parted = compare(W * np.float32(wscale), U, C, 8, 8, host(idx).reshape(40, 8), host(What), host(E))
+    say("  groups parted: %d of %d" % (parted, nv))
+    if wscale < 1:
+        assert parted <= 1
+    # at 1e4 the distances are about |x|^2 and the decisions sit at relative
+    # margins near 1e-7 (float32 ties); compare() has checked every parting
+
+
+def test_vptq_zero_codebook():
+    """Every centroid zero: all distances tie and index 0 wins everywhere."""
+    say("vptq zero codebook")
+    W, U, _ = make_case(11, 32, 24, 8, 4)
+    C = np.zeros((600, 8), np.float32)
+    idx, What, E = vq.vptq(dev(W), dev(U), 8, dev(C), 8, want_E=True)
+    assert not host(idx).any()
+    assert not host(What).any()
+    nv, parted = compare(W, U, C, 8, 8, host(idx).reshape(24, 4), host(What), host(E))
+    assert parted == 0
 
 
 def test_vptq_fullsize_sampled_rows():
