@@ -116,11 +116,34 @@ __global__ __launch_bounds__(kAsgThreads) void k_col_assign(const float* __restr
 // l % 32; accumulator r of lane l is centroid (r / 4) * 8 + (l / 32) * 4 +
 // r % 4 of the tile.  The workgroup stages kVpChunk prepared centroids in LDS
 // and its four wavefronts search them for 32 sub-vectors each; the chunk's
-// winner enters keys[v] as (order-preserving bits of -acc, index) through
-// atomicMin.  Scores of different chunks are comparable: the wave grouping of
-// sub-vectors, hence sx, is the same in every chunk.
+// winner enters one of kKeySlots copies of keys[v] as (order-preserving bits
+// of -acc, index) through atomicMin; readers take the smallest copy.  Scores
+// of different chunks are comparable: the wave grouping of sub-vectors, hence
+// sx, is the same in every chunk.
 constexpr int kVpChunk = 512;        // centroids per workgroup (prepared codebook is padded to whole chunks)
 constexpr int kHnShift = 9;          // hn 2^(2 sc) < 2^22, its pieces below 2^13
+
+constexpr int kKeySlots = 4;         // key copies per column: chunk y merges into slot y % kKeySlots
+
+// Key buffers of the V = 8 path: three columns in rotation, each with
+// kKeySlots copies of nv keys (spreading the atomicMin traffic of the
+// K-chunk workgroups over several addresses); a column's winner is the
+// smallest key over its slots.
+__device__ inline size_t key_at(int nv, int slot, int64_t n, int j)
+{
+    return ((size_t)(n % 3) * kKeySlots + (size_t)slot) * (size_t)nv + (size_t)j;
+}
+
+__device__ inline unsigned long long key_min(const unsigned long long* __restrict__ keys, int nv, int64_t n, int j)
+{
+    unsigned long long k = ~0ull;
+#pragma unroll
+    for (int q = 0; q < kKeySlots; ++q) {
+        const unsigned long long o = keys[key_at(nv, q, n, j)];
+        k = o < k ? o : k;
+    }
+    return k;
+}
 
 typedef float vp_f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 vp_h16x8 __attribute__((ext_vector_type(8)));
@@ -216,7 +239,7 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
             // forms the same values), its share of the block's later columns
             // is split over the workgroups of these rows by column
             const int64_t p = n - 1;
-            const unsigned kp = (unsigned)(keys[(size_t)(p % 3) * nv + j] & 0xFFFFFFFFull);
+            const unsigned kp = (unsigned)(key_min(keys, nv, p, j) & 0xFFFFFFFFull);
             const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)kp;
             const float4 ca = c4[0], cb = c4[1];
             const float qv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
@@ -249,7 +272,8 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
         if (blockIdx.y == 0 && half == 0) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) Xc[(size_t)(n & 1) * M + (size_t)j * 8 + t] = xv[t];
-            keys[(size_t)((n + 1) % 3) * nv + j] = ~0ull;
+#pragma unroll
+            for (int q = 0; q < kKeySlots; ++q) keys[key_at(nv, q, n + 1, j)] = ~0ull;
         }
     }
     __syncthreads();
@@ -314,7 +338,7 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
     unsigned long long key = ((unsigned long long)sortable(sco) << 32) | (unsigned)(k0 + bi);
     const unsigned long long other = __shfl_xor(key, 32);
     key = other < key ? other : key;
-    if (half == 0 && j < nv) atomicMin(&keys[(size_t)(n % 3) * nv + j], key);
+    if (half == 0 && j < nv) atomicMin(&keys[key_at(nv, blockIdx.y % kKeySlots, n, j)], key);
 }
 
 // The block's last column n (V = 8 path): winner, value and error; nothing of
@@ -328,7 +352,7 @@ __global__ __launch_bounds__(256) void k_col_last(int64_t M, int nv, int64_t n, 
     const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (m >= M) return;
     const int v = (int)(m >> 3), t = (int)(m & 7);
-    const unsigned k = (unsigned)(keys[(size_t)(n % 3) * nv + v] & 0xFFFFFFFFull);
+    const unsigned k = (unsigned)(key_min(keys, nv, n, v) & 0xFFFFFFFFull);
     const float wq = C[(size_t)k * 8 + t];
     const float e = (Xc[(size_t)(n & 1) * M + m] - wq) / U[n * N + n];
     Wht[n * M + m] = wq;
@@ -449,9 +473,9 @@ __global__ __launch_bounds__(512) void k_block_gemm(float* __restrict__ Wt, cons
 size_t ws_vptq(int64_t M, int64_t N, int V)
 {
     const int64_t nv = M / V;
-    // three transposed M x N copies, three key buffers, two working columns,
+    // three transposed M x N copies, three key buffers (kKeySlots slots each), two working columns,
     // the prepared codebook (3 x 16 bytes per centroid, at most 65536), max |C|
-    return 3 * align_up((size_t)M * (size_t)N * sizeof(float)) + align_up((size_t)(3 * nv) * sizeof(uint64_t)) +
+    return 3 * align_up((size_t)M * (size_t)N * sizeof(float)) + align_up((size_t)(3 * kKeySlots * nv) * sizeof(uint64_t)) +
            align_up((size_t)(2 * M) * sizeof(float)) + 3 * align_up((size_t)65536 * sizeof(vp_h16x8)) +
            align_up(sizeof(float));
 }
@@ -464,7 +488,7 @@ vq_status vptq_launch(const float* W, const float* U, int64_t M, int64_t N, int 
     float* Wt = cv.take<float>((size_t)(M * N));
     float* Wht = cv.take<float>((size_t)(M * N));
     float* Et = cv.take<float>((size_t)(M * N));
-    unsigned long long* keys = cv.take<unsigned long long>((size_t)(3 * nv));
+    unsigned long long* keys = cv.take<unsigned long long>((size_t)(3 * kKeySlots * nv));
     float* Xc = cv.take<float>((size_t)(2 * M));
     const int Kp = (K + kVpChunk - 1) / kVpChunk * kVpChunk;
     vp_h16x8* Phi = cv.take<vp_h16x8>(65536);
@@ -476,7 +500,8 @@ vq_status vptq_launch(const float* W, const float* U, int64_t M, int64_t N, int 
     const dim3 tw(grid_for(N, kTr), grid_for(M, kTr));
     hipLaunchKernelGGL(k_transpose, tw, dim3(256), 0, st, W, M, N, Wt);
     VQ_LAUNCHED("k_transpose");
-    hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(3 * nv, 256)), dim3(256), 0, st, keys, 3 * nv, ~0ull);
+    hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(3 * kKeySlots * nv, 256)), dim3(256), 0, st, keys,
+                       3 * kKeySlots * nv, ~0ull);
     VQ_LAUNCHED("k_fill_u64");
     const bool v8 = V == 8 && aligned16(C) && (M % 4 == 0);
     if (v8) {
