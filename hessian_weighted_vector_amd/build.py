@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvq.so")
 SOURCES = ["vq_assign.hip", "vq_update.hip", "vq_select.hip", "vq_elem.hip", "vq_qgemv.hip", "vq_vptq.hip", "vq_hfactor.hip", "vq_groups.hip", "vq_host.hip",
-           "vq_timing.hip"]
+           "vq_timing.hip", "vq_check.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1082,4 +1082,28 @@ vq_status assign_flag_count(void* ws, size_t ws_bytes, int64_t n_sub, int K, int
     return VQ_OK;
 }
 
+// Ids of the sub-vectors the last search sent to the exact path: the count,
+// and up to cap of the ids copied to the host (diagnostics).
+vq_status assign_flag_list(void* ws, size_t ws_bytes, int64_t n_sub, int K, int32_t* out, int64_t cap,
+                           int64_t* count, hipStream_t st)
+{
+    Carver cv(ws, ws_bytes);
+    cv.take<uint4>((size_t)padded_K(K) * 4);
+    int* flag_count = cv.take<int>(1);
+    int* flag_list = cv.take<int>((size_t)n_sub);
+    if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "workspace too small");
+    int n = 0;
+    VQ_HIP(hipMemcpyAsync(&n, flag_count, sizeof(int), hipMemcpyDeviceToHost, st));
+    VQ_HIP(hipStreamSynchronize(st));
+    if (n < 0 || (int64_t)n > n_sub) return fail(VQ_ERR_INVALID, "no assignment recorded in this workspace");
+    const int64_t m = std::min<int64_t>(n, cap);
+    if (m > 0) {
+        VQ_HIP(hipMemcpyAsync(out, flag_list, sizeof(int32_t) * (size_t)m, hipMemcpyDeviceToHost, st));
+        VQ_HIP(hipStreamSynchronize(st));
+    }
+    *count = n;
+    return VQ_OK;
+}
+
+
 }  // namespace vq

@@ -32,6 +32,7 @@ vq_status hip_fail(hipError_t e, const char* what)
 vq_status assign_launch(const float*, const float*, const float*, const uint8_t*, int64_t, int64_t,
                         int, const float*, int, uint16_t*, float*, void*, size_t, hipStream_t);
 vq_status assign_flag_count(void*, size_t, int64_t, int, int*, hipStream_t);
+vq_status assign_flag_list(void*, size_t, int64_t, int, int32_t*, int64_t, int64_t*, hipStream_t);
 vq_status update_launch(const float*, const float*, const float*, const uint8_t*, int64_t, int64_t,
                         int, const uint16_t*, int, float*, int32_t*, void*, size_t, hipStream_t);
 vq_status objective_launch(const float*, const float*, const float*, const uint8_t*, int64_t,
@@ -97,6 +98,10 @@ namespace {
         vq_status vq_s_ = (expr);             \
         if (vq_s_ != VQ_OK) return vq_s_;     \
     } while (0)
+
+// VQ_CHECK=1 mode: finite values (weights: also non-negative) in an input.
+#define VQ_VALUES(a, n, weights, call, what) \
+    VQ_TRY(::vq::check_values((a), (n), (weights), (call), (what), as_stream(stream)))
 
 // The current device must be a gfx950; checked once per device.
 vq_status check_device()
@@ -450,6 +455,8 @@ vq_status vq_sparse_select(const float* W, const float* h, int64_t M, int64_t N,
     VQ_CHECK(nnz == 0 || (col && val), "vq_sparse_select: col/val are null");
     VQ_WS(ws_bytes >= ws_select(M, N) && ws, "vq_sparse_select: workspace too small");
     VQ_TRY(check_device());
+    VQ_VALUES(W, M * N, false, "vq_sparse_select", "W");
+    VQ_VALUES(h, N, true, "vq_sparse_select", "h");
     return select_launch(W, h, M, N, d, nnz, row_ptr, col, val, mask, ws, ws_bytes, as_stream(stream));
 }
 
@@ -461,6 +468,8 @@ vq_status vq_binorm(const float* W, const float* h, int64_t M, int64_t N, float*
     VQ_CHECK(Wp != W, "vq_binorm: Wp may not alias W");
     VQ_WS(ws && ws_bytes >= ws_binorm(M, N), "vq_binorm: workspace too small");
     VQ_TRY(check_device());
+    VQ_VALUES(W, M * N, false, "vq_binorm", "W");
+    VQ_VALUES(h, N, true, "vq_binorm", "h");
     return binorm_launch(W, h, M, N, Wp, r, c, hcol, rho, ws, ws_bytes, as_stream(stream));
 }
 
@@ -473,6 +482,7 @@ vq_status vq_init(const float* X, int64_t M, int64_t N, int d, const int32_t* pe
     VQ_CHECK(X && perm && C, "vq_init: null pointer");
     VQ_WS(ws && ws_bytes >= ws_init(n_sub, K, d), "vq_init: workspace too small");
     VQ_TRY(check_device());
+    VQ_VALUES(X, M * N, false, "vq_init", "X");
     return init_walk(X, n_sub, d, perm, K, C, ws, ws_bytes, as_stream(stream));
 }
 
@@ -486,6 +496,10 @@ vq_status vq_assign(const float* X, const float* hcol, const float* rho, const u
     VQ_CHECK(X && hcol && C && idx, "vq_assign: null pointer");
     VQ_WS(ws && ws_bytes >= ws_assign(n_sub, K), "vq_assign: workspace too small");
     VQ_TRY(check_device());
+    VQ_VALUES(X, M * N, false, "vq_assign", "X");
+    VQ_VALUES(hcol, N, true, "vq_assign", "hcol");
+    VQ_VALUES(rho, M, true, "vq_assign", "rho");
+    VQ_VALUES(C, (int64_t)K * d, false, "vq_assign", "C");
     return assign_launch(X, hcol, rho, mask, M, N, d, C, K, idx, dist, ws, ws_bytes, as_stream(stream));
 }
 
@@ -499,6 +513,10 @@ vq_status vq_update(const float* X, const float* hcol, const float* rho, const u
     VQ_CHECK(X && hcol && idx && C, "vq_update: null pointer");
     VQ_WS(ws && ws_bytes >= ws_update_total(n_sub, K), "vq_update: workspace too small");
     VQ_TRY(check_device());
+    VQ_VALUES(X, M * N, false, "vq_update", "X");
+    VQ_VALUES(hcol, N, true, "vq_update", "hcol");
+    VQ_VALUES(rho, M, true, "vq_update", "rho");
+    VQ_VALUES(C, (int64_t)K * d, false, "vq_update", "C");
     return update_with_J(X, hcol, rho, mask, M, N, d, idx, K, C, counts, J, ws, ws_bytes, as_stream(stream));
 }
 
@@ -512,6 +530,10 @@ vq_status vq_objective(const float* X, const float* hcol, const float* rho, cons
     VQ_CHECK(X && hcol && C && idx && J, "vq_objective: null pointer");
     VQ_WS(ws && ws_bytes >= ws_objective(n_sub), "vq_objective: workspace too small");
     VQ_TRY(check_device());
+    VQ_VALUES(X, M * N, false, "vq_objective", "X");
+    VQ_VALUES(hcol, N, true, "vq_objective", "hcol");
+    VQ_VALUES(rho, M, true, "vq_objective", "rho");
+    VQ_VALUES(C, (int64_t)K * d, false, "vq_objective", "C");
     return objective_launch(X, hcol, rho, mask, M, N, d, C, K, idx, J, ws, ws_bytes, as_stream(stream));
 }
 
@@ -523,6 +545,8 @@ vq_status vq_residual(const float* X, int64_t M, int64_t N, int d, const float* 
     VQ_CHECK(X && C && idx && R, "vq_residual: null pointer");
     VQ_CHECK(R != X, "vq_residual: R may not alias X");
     VQ_TRY(check_device());
+    VQ_VALUES(X, M * N, false, "vq_residual", "X");
+    VQ_VALUES(C, (int64_t)K * d, false, "vq_residual", "C");
     return residual_launch(X, M, N, d, C, K, idx, R, as_stream(stream));
 }
 
@@ -540,6 +564,10 @@ vq_status vq_reconstruct(int64_t M, int64_t N, int d, const float* C1, int K1, c
     }
     VQ_CHECK(!row_ptr || (col && val), "vq_reconstruct: col/val are null");
     VQ_TRY(check_device());
+    VQ_VALUES(C1, (int64_t)K1 * d, false, "vq_reconstruct", "C1");
+    VQ_VALUES(C2, (int64_t)K2 * d, false, "vq_reconstruct", "C2");
+    VQ_VALUES(rscale, M, false, "vq_reconstruct", "rscale");
+    VQ_VALUES(cscale, N, false, "vq_reconstruct", "cscale");
     return reconstruct_launch(M, N, d, C1, K1, idx1, C2, K2, idx2, rscale, cscale, row_ptr, col, val, W_hat,
                               as_stream(stream));
 }
@@ -554,6 +582,8 @@ vq_status vq_select_subvectors(const float* W, const float* h, int64_t M, int64_
     VQ_CHECK(n_sub <= (int64_t)UINT32_MAX, "vq_select_subvectors: too many sub-vectors");
     VQ_WS(ws && ws_bytes >= ws_select(M, N), "vq_select_subvectors: workspace too small");
     VQ_TRY(check_device());
+    VQ_VALUES(W, M * N, false, "vq_select_subvectors", "W");
+    VQ_VALUES(h, N, true, "vq_select_subvectors", "h");
     return subvector_select_launch(W, h, M, N, d, n_sel, mask, ws, ws_bytes, as_stream(stream));
 }
 
@@ -566,6 +596,9 @@ vq_status vq_select_residual(const float* W, const float* W_hat, const float* h,
     VQ_CHECK(M * N / d <= (int64_t)UINT32_MAX, "vq_select_residual: too many sub-vectors");
     VQ_WS(ws && ws_bytes >= ws_select(M, N), "vq_select_residual: workspace too small");
     VQ_TRY(check_device());
+    VQ_VALUES(W, M * N, false, "vq_select_residual", "W");
+    VQ_VALUES(W_hat, M * N, false, "vq_select_residual", "W_hat");
+    VQ_VALUES(h, N, true, "vq_select_residual", "h");
     return residual_select_launch(W, W_hat, h, M, N, d, n_sel, mask, ws, ws_bytes, as_stream(stream));
 }
 
@@ -579,6 +612,7 @@ vq_status vq_mask_to_csr(const float* W, const uint8_t* mask, int64_t M, int64_t
     VQ_CHECK(M * N <= (int64_t)INT32_MAX, "vq_mask_to_csr: M*N exceeds the int32 row pointer");
     VQ_WS(ws && ws_bytes >= ws_select(M, N), "vq_mask_to_csr: workspace too small");
     VQ_TRY(check_device());
+    VQ_VALUES(W, M * N, false, "vq_mask_to_csr", "W");
     return mask_to_csr_launch(W, mask, M, N, d, nnz_cap, row_ptr, col, val, ws, ws_bytes, as_stream(stream));
 }
 
@@ -596,6 +630,7 @@ vq_status vq_hessian_factor(const float* H, int64_t N, double damp, float* U, vo
     VQ_CHECK(H && U && (const void*)H != (const void*)U, "vq_hessian_factor: null or aliased pointer");
     VQ_WS(ws && ws_bytes >= ws_hfactor(N), "vq_hessian_factor: workspace too small");
     VQ_TRY(check_device());
+    VQ_VALUES(H, N * N, false, "vq_hessian_factor", "H");
     return hfactor_launch(H, N, damp, U, ws, ws_bytes, as_stream(stream));
 }
 
@@ -618,6 +653,9 @@ vq_status vq_vptq(const float* W, const float* U, int64_t M, int64_t N, int V, c
     VQ_CHECK(W_hat != W && (E == nullptr || (E != W && E != W_hat)), "vq_vptq: outputs may not alias");
     VQ_WS(ws && ws_bytes >= ws_vptq(M, N, V), "vq_vptq: workspace too small");
     VQ_TRY(check_device());
+    VQ_VALUES(W, M * N, false, "vq_vptq", "W");
+    VQ_VALUES(U, N * N, false, "vq_vptq", "U");
+    VQ_VALUES(C, (int64_t)K * V, false, "vq_vptq", "C");
     return vptq_launch(W, U, M, N, V, C, K, B, idx, W_hat, E, ws, ws_bytes, as_stream(stream));
 }
 
@@ -648,6 +686,11 @@ vq_status vq_qgemv(int64_t M, int64_t N, int d, const float* C1, int K1, const u
     const size_t need = ws_qgemv(M, N, d, B);
     VQ_WS(need == 0 || (ws && ws_bytes >= need), "vq_qgemv: workspace too small");
     VQ_TRY(check_device());
+    VQ_VALUES(C1, (int64_t)K1 * d, false, "vq_qgemv", "C1");
+    VQ_VALUES(C2, (int64_t)K2 * d, false, "vq_qgemv", "C2");
+    VQ_VALUES(rscale, M, false, "vq_qgemv", "rscale");
+    VQ_VALUES(cscale, N, false, "vq_qgemv", "cscale");
+    VQ_VALUES(X, B * N, false, "vq_qgemv", "X");
     return qgemv_launch(M, N, d, C1, K1, idx1, C2, K2, idx2, rscale, cscale, row_ptr, col, val, X, B, Y, ws,
                         ws_bytes, as_stream(stream));
 }
@@ -696,6 +739,10 @@ vq_status vq_fit(const vq_fit_params* p, const vq_fit_inputs* in, vq_fit_outputs
     const size_t need = vq_workspace_bytes(M, N, d, p->K1, p->K2, nnz);
     VQ_WS(ws && ws_bytes >= need, "vq_fit: workspace too small");
     VQ_TRY(check_device());
+    VQ_VALUES(in->W, M * N, false, "vq_fit", "W");
+    VQ_VALUES(in->h, N, true, "vq_fit", "h");
+    VQ_VALUES(in->C1_init, (int64_t)p->K1 * d, false, "vq_fit", "C1_init");
+    if (p->K2 > 0) VQ_VALUES(in->C2_init, (int64_t)p->K2 * d, false, "vq_fit", "C2_init");
     hipStream_t st = as_stream(stream);
 
     Carver cv(ws, ws_bytes);
@@ -877,6 +924,8 @@ vq_status vq_fit_grouped(const vq_grouped_params* p, const vq_grouped_inputs* in
     const GroupTotals tot = group_totals(p, groups);
     VQ_WS(ws && ws_bytes >= grouped_ws(p, tot), "vq_fit_grouped: workspace too small");
     VQ_TRY(check_device());
+    VQ_VALUES(in->W, p->fit.M * p->fit.N, false, "vq_fit_grouped", "W");
+    VQ_VALUES(in->h, p->fit.N, true, "vq_fit_grouped", "h");
     hipStream_t st = as_stream(stream);
 
     Carver cv(ws, ws_bytes);
@@ -964,6 +1013,31 @@ int vq_assign_exact_count(void* ws, size_t ws_bytes, int64_t n_sub, int K, void*
     int n = -1;
     if (assign_flag_count(ws, ws_bytes, n_sub, K, &n, as_stream(stream)) != VQ_OK) return -1;
     return n;
+}
+
+int64_t vq_assign_exact_list(void* ws, size_t ws_bytes, int64_t n_sub, int K, int32_t* list, int64_t cap,
+                             void* stream)
+{
+    if (!ws || n_sub <= 0 || K < 1 || K > 65536 || cap < 0 || (cap > 0 && !list)) {
+        set_error("vq_assign_exact_list: bad argument");
+        return -1;
+    }
+    if (ws_bytes < ws_assign(n_sub, K)) {
+        set_error("vq_assign_exact_list: workspace too small");
+        return -1;
+    }
+    int64_t n = -1;
+    if (assign_flag_list(ws, ws_bytes, n_sub, K, list, cap, &n, as_stream(stream)) != VQ_OK) return -1;
+    return n;
+}
+
+int64_t vq_nnz(int64_t M, int64_t N, double p)
+{
+    if (M <= 0 || N <= 0 || !(p >= 0.0 && p <= 1.0)) {
+        set_error("vq_nnz: M, N must be positive and p in [0, 1]");
+        return -1;
+    }
+    return nnz_of(M, N, p);
 }
 
 }  // extern "C"

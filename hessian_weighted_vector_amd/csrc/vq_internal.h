@@ -70,6 +70,14 @@ size_t ws_hfactor(int64_t N);
 vq_status check_shape(int64_t M, int64_t N, int d);
 vq_status check_K(int K, int64_t n_sub);
 
+// Input value checks (environment VQ_CHECK=1): counts the non-finite values of
+// a[0..n) (with sign_clear, also those with the sign bit set) on the device and
+// fails with VQ_ERR_INVALID naming `what` if any.  A no-op when the mode is off
+// or a is null.  Synchronizes st when on.
+bool values_check_on();
+vq_status check_values(const float* a, int64_t n, bool sign_clear, const char* call, const char* what,
+                       hipStream_t st);
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }

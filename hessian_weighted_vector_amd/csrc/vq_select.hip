@@ -269,8 +269,9 @@ __global__ __launch_bounds__(kRowThreads) void k_sel_compact(
 }
 
 // ---- the unified sparse correction ---------------------------------------
-// SCVQ summary: outliers, highly salient sub-vectors and the largest
-// quantization residuals share one sparse correction matrix.  The two extra
+// SCVQ summary: a single sparse matrix carries every exactly-held weight:
+// the salient elements, whole sub-vectors of high salience and the positions
+// where quantization left the biggest error.  The two extra
 // selections mark the mask (bit t of byte s = element t of sub-vector s is
 // held exactly); vq_mask_to_csr turns the mask into the CSR.
 //

@@ -72,6 +72,8 @@ SIGNATURES = {
     "vq_init": (_I, [_P, _I64, _I64, _I, _P, _I, _P, _P, _SZ, _P]),
     "vq_assign": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P]),
     "vq_assign_exact_count": (_I, [_P, _SZ, _I64, _I, _P]),
+    "vq_assign_exact_list": (_I64, [_P, _SZ, _I64, _I, _P, _I64, _P]),
+    "vq_nnz": (_I64, [_I64, _I64, _D]),
     "vq_update": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _P, _I, _P, _P, _P, _P, _SZ, _P]),
     "vq_objective": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P]),
     "vq_residual": (_I, [_P, _I64, _I64, _I, _P, _I, _P, _P, _P]),
@@ -156,7 +158,11 @@ def workspace(M, N, d, K1, K2=0, nnz=0, device="cuda"):
 
 
 def nnz_of(M, N, p):
-    return int(math.floor(p * float(M * N)))
+    """The library's salient count for an M x N matrix and fraction p."""
+    n = int(load().vq_nnz(M, N, float(p)))
+    if n < 0:
+        raise VQError(VQ_ERR_INVALID, load().vq_last_error().decode())
+    return n
 
 
 def sparse_select(W, h, d, nnz, ws):
@@ -211,6 +217,19 @@ def assign(X, hcol, rho, mask, d, C, ws, want_dist=False, idx=None, dist=None):
 
 def assign_exact_count(ws, n_sub, K):
     return int(load().vq_assign_exact_count(_ptr(ws), ws.numel(), n_sub, K, _stream()))
+
+
+def assign_exact_list(ws, n_sub, K):
+    """Sorted ids (numpy int32) of the sub-vectors the last assign re-searched exactly."""
+    lib = load()
+    n = int(lib.vq_assign_exact_list(_ptr(ws), ws.numel(), n_sub, K, None, 0, _stream()))
+    if n < 0:
+        raise VQError(VQ_ERR_INVALID, lib.vq_last_error().decode())
+    out = np.zeros(max(n, 1), np.int32)
+    m = int(lib.vq_assign_exact_list(_ptr(ws), ws.numel(), n_sub, K, out.ctypes.data, n, _stream()))
+    if m != n:
+        raise VQError(VQ_ERR_DEVICE, "exact-path list changed between reads")
+    return np.sort(out[:n])
 
 
 def update(X, hcol, rho, mask, d, idx, C, ws, want_counts=True, want_J=True):

@@ -36,8 +36,14 @@
  *     synchronize the stream (they read device data on the host).
  *   - Every call validates its arguments on the host before any launch and
  *     returns a vq_status; vq_last_error() (thread-local) describes the last
- *     failure.  Non-finite W or h is a precondition violation and is not
- *     checked.
+ *     failure.  Finite floating-point inputs and non-negative weights (h,
+ *     hcol, rho) are preconditions, unchecked by default.  With the
+ *     environment variable VQ_CHECK=1 (read at every call), every
+ *     entry point first counts on the device the non-finite values of each
+ *     floating-point input array it is given (of the weight arrays: also the
+ *     values with the sign bit set) and returns VQ_ERR_INVALID naming the
+ *     array if any is found.  That mode reads every input once more and
+ *     synchronizes the stream per checked array.
  */
 #ifndef VQ_H
 #define VQ_H
@@ -64,6 +70,11 @@ const char* vq_version(void);
 /* Description of the last failure on this thread ("" if none). */
 const char* vq_last_error(void);
 
+/* Salient count of a fit: nnz = floor(p * M * N), the product taken in
+ * float64 (M*N exact as an integer first).  -1 if M or N is not positive or p
+ * is outside [0, 1].  Host arithmetic. */
+int64_t vq_nnz(int64_t M, int64_t N, double p);
+
 /* Workspace bytes sufficient for every call below with these sizes
  * (K2 = 0: no residual stage; nnz = number of salient weights). */
 size_t vq_workspace_bytes(int64_t M, int64_t N, int d, int K1, int K2, int64_t nnz);
@@ -81,9 +92,10 @@ vq_status vq_sparse_select(const float* W, const float* h, int64_t M, int64_t N,
                            int64_t nnz, int32_t* row_ptr, int32_t* col, float* val,
                            uint8_t* mask, void* ws, size_t ws_bytes, void* stream);
 
-/* The unified sparse correction (SCVQ summary: outliers, highly salient
- * sub-vectors and the largest quantization residuals are held together in
- * one sparse correction matrix).  The mask (one byte per sub-vector, bit t =
+/* The unified sparse correction (SCVQ summary: a single sparse matrix
+ * carries every exactly-held weight, namely the salient elements, whole
+ * sub-vectors of high salience and the positions where quantization left the
+ * biggest error).  The mask (one byte per sub-vector, bit t =
  * element t held exactly) is the correction set; these calls OR new positions
  * into it and vq_mask_to_csr writes its CSR.  Keys below are float32 scores,
  * which must be >= +0 (h >= 0); ties go to the smaller id.  Bitwise
@@ -146,6 +158,12 @@ vq_status vq_assign(const float* X, const float* hcol, const float* rho, const u
  * workspace (same n_sub and K) sent to the exact float64 re-search because
  * their winner could not be certified.  Synchronizes the stream; -1 on error. */
 int vq_assign_exact_count(void* ws, size_t ws_bytes, int64_t n_sub, int K, void* stream);
+
+/* Diagnostics: the ids of those sub-vectors.  Copies up to cap of them (in no
+ * particular order) into list (host int32[cap]) and returns their number (may
+ * exceed cap); -1 on error.  Synchronizes the stream. */
+int64_t vq_assign_exact_list(void* ws, size_t ws_bytes, int64_t n_sub, int K, int32_t* list, int64_t cap,
+                             void* stream);
 
 /* Centroid update (VPTQ page, "Hessian-Weighted Centroid Initialization":
  * weighted-mean centroids; with one weight per element this is the

@@ -103,9 +103,10 @@ int orc_select(const float* W, const float* h, long long M, long long N, long lo
 }
 
 /* ------------------------------------------------------------------ */
-/* The unified sparse correction (SCVQ summary: outliers, highly salient
- * sub-vectors and the largest quantization residuals share one sparse
- * correction matrix).  keep[M*N] marks the correction: 0 = held exactly.
+/* The unified sparse correction (SCVQ summary: a single sparse matrix
+ * carries every exactly-held weight, namely the salient elements, whole
+ * sub-vectors of high salience and the positions where quantization left the
+ * biggest error).  keep[M*N] marks the correction: 0 = held exactly.
  *
  * Salient sub-vectors: score of sub-vector s = (row i, block b) is
  *   S_s = sum over t = 0..d-1, in that order, of h_j * (w_j * w_j), j = b*d+t,

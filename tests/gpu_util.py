@@ -66,3 +66,32 @@ def index_flips_allowed(X, hcol, rho, keep, d, C, idx_gpu, idx_ref, rel=1e-6):
     dr = (om[diff] * (Xs[diff] - Cd[idx_ref[diff]]) ** 2).sum(1)
     ok = (dg - dr) < rel * dg
     return bool(ok.all()), diff[~ok]
+
+
+def check_select_properties(W, h, d, nnz, rp, col, val, mask):
+    """The defining properties of the salient selection, on every element:
+    nnz positions, CSR structure with ascending columns and exact values, the
+    mask marking exactly those positions, no unselected score above a selected
+    one, and among equal scores at the threshold the smaller linear indices
+    selected.  Together they fix the selection uniquely."""
+    M, N = W.shape
+    assert rp[0] == 0 and rp[-1] == nnz and np.all(np.diff(rp) >= 0)
+    rows = np.repeat(np.arange(M), np.diff(rp))
+    same_row = rows[1:] == rows[:-1]
+    assert np.all(col[1:][same_row] > col[:-1][same_row])
+    assert np.all((col >= 0) & (col < N))
+    assert bits_equal(val, W[rows, col])
+    sel = np.zeros(M * N, bool)
+    sel[rows.astype(np.int64) * N + col] = True
+    assert sel.sum() == nnz
+    keep = keep_from_mask(mask, M, N, d).ravel()
+    assert np.array_equal(keep == 0, sel)
+    s = (np.float32(h)[None, :] * (W * W)).ravel()
+    if 0 < nnz < M * N:
+        tau_in = s[sel].min()
+        tau_out = s[~sel].max()
+        assert tau_in >= tau_out
+        if tau_in == tau_out:
+            lin_in = np.flatnonzero(sel & (s == tau_in))
+            lin_out = np.flatnonzero(~sel & (s == tau_in))
+            assert lin_in.max() < lin_out.min()

@@ -142,3 +142,28 @@ def test_grouped_sizes_and_bits_match_oracle_layout():
     # sizes that do not split: n_out not a multiple of d, or an empty last group
     assert vq.grouped_sizes(vq.grouped_params(8, 64, 8, 4, 1, 0, 0, 0.0, False, True, 12, 4, 4, 1, 1))[0] == 0
     assert vq.grouped_sizes(vq.grouped_params(8, 72, 8, 4, 1, 0, 0, 0.0, False, True, 0, 4, 4, 1, 4))[0] == 0
+
+
+def test_nnz_from_library_matches_oracle():
+    """The binding sizes its CSR from the library's count, which equals the
+    oracle's floor(p*M*N) on every workload and on edge fractions."""
+    import oracle
+    from hessian_weighted_vector_amd import configs
+    lib = vq.load()
+    for c in configs.CONFIGS:
+        assert vq.nnz_of(c.M, c.N, c.p) == oracle.nnz(c.M, c.N, c.p)
+    for (M, N, p) in [(1, 1, 0.0), (1, 1, 1.0), (7, 13, 0.5), (4096, 11008, 0.01), (3, 5, 1.0 / 3)]:
+        assert vq.nnz_of(M, N, p) == oracle.nnz(M, N, p)
+    assert lib.vq_nnz(8, 8, -0.1) == -1 and "p in" in lib.vq_last_error().decode()
+    assert lib.vq_nnz(8, 8, float("nan")) == -1
+    assert lib.vq_nnz(0, 8, 0.5) == -1
+    with pytest.raises(vq.VQError):
+        vq.nnz_of(8, 8, 2.0)
+
+
+def test_exact_list_rejects_bad_arguments():
+    lib = vq.load()
+    assert lib.vq_assign_exact_list(None, 1 << 30, 64, 16, None, 0, None) == -1
+    assert lib.vq_assign_exact_list(FAKE, 16, 64, 16, None, 0, None) == -1
+    assert "workspace" in lib.vq_last_error().decode()
+    assert lib.vq_assign_exact_list(FAKE, 1 << 30, 64, 16, None, 4, None) == -1      # cap > 0, no list

@@ -20,7 +20,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import bits_equal, centroid_close, dev, host, keep_from_mask, mask_from_keep
+from gpu_util import bits_equal, centroid_close, check_select_properties, dev, host, keep_from_mask, mask_from_keep
 from hessian_weighted_vector_amd import configs, synth, vq
 
 pytestmark = pytest.mark.gpu
@@ -68,27 +68,7 @@ def test_select_fullsize_properties(world):
     cfg, W, h, nnz = world["cfg"], world["W"], world["h"], world["nnz"]
     say("select", cfg.name, "nnz", nnz)
     rp, col, val, mask = [host(t) for t in vq.sparse_select(dev(W), dev(h), cfg.d, nnz, world["ws"])]
-    M, N = W.shape
-    assert rp[0] == 0 and rp[-1] == nnz and np.all(np.diff(rp) >= 0)
-    rows = np.repeat(np.arange(M), np.diff(rp))
-    # ascending columns within each row
-    same_row = rows[1:] == rows[:-1]
-    assert np.all(col[1:][same_row] > col[:-1][same_row])
-    assert np.all((col >= 0) & (col < N))
-    assert bits_equal(val, W[rows, col])
-    sel = np.zeros(M * N, bool)
-    sel[rows.astype(np.int64) * N + col] = True
-    assert sel.sum() == nnz
-    keep = keep_from_mask(mask, M, N, cfg.d).ravel()
-    assert np.array_equal(keep == 0, sel)
-    s = (np.float32(h)[None, :] * (W * W)).ravel()
-    tau_in = s[sel].min()
-    tau_out = s[~sel].max()
-    assert tau_in >= tau_out
-    if tau_in == tau_out:
-        lin_in = np.flatnonzero(sel & (s == tau_in))
-        lin_out = np.flatnonzero(~sel & (s == tau_in))
-        assert lin_in.max() < lin_out.min()
+    check_select_properties(W, h, cfg.d, nnz, rp, col, val, mask)
 
 
 def test_init_and_sampled_assign_fullsize(world):
