@@ -40,6 +40,8 @@
 #include "vq_internal.h"
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 namespace vq {
 namespace {
@@ -1105,5 +1107,52 @@ vq_status assign_flag_list(void* ws, size_t ws_bytes, int64_t n_sub, int K, int3
     return VQ_OK;
 }
 
+
+// ---- allocation-free assignment ---------------------------------------------
+// For callers that cannot allocate device memory (code under stream capture,
+// tight serving loops): the workspace of an assignment lives in one
+// file-scope device array per GPU, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it only stands in for
+// the symbol); it fetches the array's device address once per device, with
+// that device current, and uses that address everywhere.  The kernels clear
+// the counters they use at the start of every call; calls that overlap on one
+// GPU share the array and race.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // per device: the array's device address
+}  // namespace
+
+size_t assign_scratch_bytes() { return kScratchBytes; }
+
+vq_status scratch_address(void** out)
+{
+    int dev = -1;
+    VQ_HIP(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (p == nullptr) return fail(VQ_ERR_DEVICE, "hipGetSymbolAddress(scratch) returned a null address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return VQ_OK;
+}
+
+// vq_assign with the file-scope array as its workspace; sizes already checked
+// against kScratchBytes by the caller.
+vq_status assign_noalloc_launch(const float* X, const float* hcol, const float* rho, const uint8_t* mask,
+                                int64_t M, int64_t N, int d, const float* C, int K, uint16_t* idx, float* dist,
+                                hipStream_t st)
+{
+    void* ws = nullptr;
+    if (vq_status s = scratch_address(&ws); s != VQ_OK) return s;
+    return assign_launch(X, hcol, rho, mask, M, N, d, C, K, idx, dist, ws, kScratchBytes, st);
+}
 
 }  // namespace vq

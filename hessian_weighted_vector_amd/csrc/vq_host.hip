@@ -33,6 +33,9 @@ vq_status assign_launch(const float*, const float*, const float*, const uint8_t*
                         int, const float*, int, uint16_t*, float*, void*, size_t, hipStream_t);
 vq_status assign_flag_count(void*, size_t, int64_t, int, int*, hipStream_t);
 vq_status assign_flag_list(void*, size_t, int64_t, int, int32_t*, int64_t, int64_t*, hipStream_t);
+size_t assign_scratch_bytes();
+vq_status assign_noalloc_launch(const float*, const float*, const float*, const uint8_t*, int64_t, int64_t, int,
+                                const float*, int, uint16_t*, float*, hipStream_t);
 vq_status update_launch(const float*, const float*, const float*, const uint8_t*, int64_t, int64_t,
                         int, const uint16_t*, int, float*, int32_t*, void*, size_t, hipStream_t);
 vq_status objective_launch(const float*, const float*, const float*, const uint8_t*, int64_t,
@@ -501,6 +504,26 @@ vq_status vq_assign(const float* X, const float* hcol, const float* rho, const u
     VQ_VALUES(rho, M, true, "vq_assign", "rho");
     VQ_VALUES(C, (int64_t)K * d, false, "vq_assign", "C");
     return assign_launch(X, hcol, rho, mask, M, N, d, C, K, idx, dist, ws, ws_bytes, as_stream(stream));
+}
+
+vq_status vq_assign_noalloc(const float* X, const float* hcol, const float* rho, const uint8_t* mask, int64_t M,
+                            int64_t N, int d, const float* C, int K, uint16_t* idx, float* dist, void* stream)
+{
+    VQ_TRY(check_shape(M, N, d));
+    const int64_t n_sub = M * N / d;
+    VQ_TRY(check_K(K, n_sub));
+    VQ_CHECK(X && hcol && C && idx, "vq_assign_noalloc: null pointer");
+    const size_t need = ws_assign(n_sub, K);
+    if (need > assign_scratch_bytes())
+        return fail(VQ_ERR_INVALID, "vq_assign_noalloc: these sizes need " + std::to_string(need) +
+                                        " bytes of scratch; the library holds " +
+                                        std::to_string(assign_scratch_bytes()) + " per device");
+    VQ_TRY(check_device());
+    VQ_VALUES(X, M * N, false, "vq_assign_noalloc", "X");
+    VQ_VALUES(hcol, N, true, "vq_assign_noalloc", "hcol");
+    VQ_VALUES(rho, M, true, "vq_assign_noalloc", "rho");
+    VQ_VALUES(C, (int64_t)K * d, false, "vq_assign_noalloc", "C");
+    return assign_noalloc_launch(X, hcol, rho, mask, M, N, d, C, K, idx, dist, as_stream(stream));
 }
 
 vq_status vq_update(const float* X, const float* hcol, const float* rho, const uint8_t* mask, int64_t M,

@@ -71,6 +71,7 @@ SIGNATURES = {
     "vq_binorm": (_I, [_P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "vq_init": (_I, [_P, _I64, _I64, _I, _P, _I, _P, _P, _SZ, _P]),
     "vq_assign": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P]),
+    "vq_assign_noalloc": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _P, _I, _P, _P, _P]),
     "vq_assign_exact_count": (_I, [_P, _SZ, _I64, _I, _P]),
     "vq_assign_exact_list": (_I64, [_P, _SZ, _I64, _I, _P, _I64, _P]),
     "vq_nnz": (_I64, [_I64, _I64, _D]),

@@ -154,6 +154,21 @@ vq_status vq_assign(const float* X, const float* hcol, const float* rho, const u
                     int64_t M, int64_t N, int d, const float* C, int K,
                     uint16_t* idx, float* dist, void* ws, size_t ws_bytes, void* stream);
 
+/* vq_assign without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, serving loops, harnesses that
+ * forbid allocation).  Same arguments and results as vq_assign; its scratch
+ * (the prepared codebook, the re-search and per-sub-vector lists) lives in one
+ * library-held device array of 64 MiB per GPU, allocated when the library is
+ * loaded and held until the process ends.  Needs 64*ceil(K/256)*256 +
+ * 9*n_sub bytes plus about 2 KiB: K = 65536 allows n_sub up to about 6.99
+ * million.  Larger sizes return VQ_ERR_INVALID before any launch.  The call
+ * allocates nothing.  Every call on one GPU shares that GPU's array (each call
+ * clears what it needs), so calls that overlap in time on one GPU race; the
+ * vq_assign_exact_* diagnostics do not see this array. */
+vq_status vq_assign_noalloc(const float* X, const float* hcol, const float* rho, const uint8_t* mask,
+                            int64_t M, int64_t N, int d, const float* C, int K,
+                            uint16_t* idx, float* dist, void* stream);
+
 /* Diagnostics: number of sub-vectors that the last vq_assign call on this
  * workspace (same n_sub and K) sent to the exact float64 re-search because
  * their winner could not be certified.  Synchronizes the stream; -1 on error. */
