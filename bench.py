@@ -425,6 +425,145 @@ def grouped_bench(cfg, inp, W, h, plain_ms, run_oracle, d0=4, K0=4096, n_groups=
     return res
 
 
+def cold_warm_rows(cfg, out, W, h, nnz, ws, reps=10, scrub_mib=1024):
+    """The HBM-bound rows timed cold and warm (HIP events on the library's stream).
+
+    Cold: before every rep a resident scrub buffer of scrub_mib MiB (more than the
+    256 MB Infinity Cache plus the L2s) is read once, so the call's inputs come
+    from HBM and the caches hold only clean lines of another buffer.  Warm: the
+    reps run back to back, as inside the Lloyd loop, where the 180 MB matrix of
+    the 4096 x 11008 workload stays in the Infinity Cache.  Inputs are the fit's
+    own state (matrix, weights, mask, indices, codebooks, CSR); the update
+    restores its codebook before every rep."""
+    import torch
+
+    from hessian_weighted_vector_amd import vq
+    M, N, d, n_sub = cfg.M, cfg.N, cfg.d, cfg.n_sub
+    X = out["Wp"] if cfg.binorm else W
+    hcol = out["hcol"] if cfg.binorm else h
+    rho = out["rho"] if cfg.binorm else None
+    mask = out["mask"]
+    scrub = torch.ones(scrub_mib * (1 << 18), dtype=torch.float32, device="cuda")
+    R = vq.residual(X, d, out["C1"], out["idx1"]) if cfg.K2 else None
+    What = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    C1w = out["C1"].clone()
+    C2w = out["C2"].clone() if cfg.K2 else None
+    recon_args = (out["C2"], out["idx2"], out.get("rscale"), out.get("cscale"),
+                  out["row_ptr"] if nnz else None, out["col"] if nnz else None, out["val"] if nnz else None)
+    ops = [
+        ("A1_select", ("select", 0), lambda: vq.sparse_select(W, h, d, nnz, ws), None,
+         4 * M * N + 4 * N + 8 * nnz + 4 * (M + 1) + n_sub),
+        ("A5_update_stage1", ("update", cfg.K1),
+         lambda: vq.update(X, hcol, rho, mask, d, out["idx1"], C1w, ws, want_counts=False, want_J=False),
+         lambda: C1w.copy_(out["C1"]), algorithmic_bytes_update(n_sub, M, N, d, cfg.K1)),
+        ("A6_residual", ("residual", cfg.K1), lambda: vq.residual(X, d, out["C1"], out["idx1"]), None,
+         n_sub * (8 * d + 2) + 4 * cfg.K1 * d),
+        ("A7_reconstruct", ("reconstruct", cfg.K1),
+         lambda: vq.reconstruct(M, N, d, out["C1"], out["idx1"], *recon_args, out=What), None,
+         algorithmic_bytes_reconstruct(n_sub, M, N, d, cfg.K1, cfg.K2, nnz, cfg.binorm)),
+    ]
+    if cfg.K2:
+        ops.insert(2, ("A5_update_stage2", ("update", cfg.K2),
+                       lambda: vq.update(R, hcol, rho, mask, d, out["idx2"], C2w, ws, want_counts=False,
+                                         want_J=False),
+                       lambda: C2w.copy_(out["C2"]), algorithmic_bytes_update(n_sub, M, N, d, cfg.K2)))
+    res = {}
+    for name, key, fn, prep, nbytes in ops:
+        e = {"algorithmic_MB": round(nbytes / 1e6, 1)}
+        for mode in ("warm", "cold"):
+            if prep:
+                prep()
+            fn()
+            torch.cuda.synchronize()
+            vq.timing_enable(True)
+            for _ in range(reps):
+                if prep:
+                    prep()
+                if mode == "cold":
+                    scrub.sum()
+                fn()
+            torch.cuda.synchronize()
+            r = {(x[0], x[1]): x for x in vq.timing_records()}[key]
+            vq.timing_enable(False)
+            t = r[3] / r[2]
+            e[mode + "_ms"] = round(t, 4)
+            e[mode + "_GBs"] = round(nbytes / (t * 1e-3) / 1e9, 1)
+            e[mode + "_frac_hbm"] = round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        res[name] = e
+    del scrub, R, What
+    torch.cuda.empty_cache()
+    return res
+
+
+def config_rows(cfg_ids, steps_for, cpu_seconds):
+    """One timed whole fit per workload (inputs resident in HBM, one untimed
+    warm-up fit): step time, value, and the per-row times of the stage-1
+    search, update and the reconstruction from HIP events inside the timed
+    fits, each against its roofline; beside it the oracle's exhaustive
+    assignment rate on a short seeded sample of the workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from hessian_weighted_vector_amd import configs, synth, vq
+    out_rows = {}
+    for cid in cfg_ids:
+        cfg = configs.get(cid)
+        inp = synth.make_inputs(cfg)
+        W = torch.from_numpy(inp["W"]).cuda()
+        h = torch.from_numpy(inp["h"]).cuda()
+        nnz = vq.nnz_of(cfg.M, cfg.N, cfg.p)
+        ws = vq.workspace(cfg.M, cfg.N, cfg.d, cfg.K1, cfg.K2, nnz)
+        fit = lambda: vq.fit(W, h, cfg.d, cfg.K1, cfg.T1, cfg.K2, cfg.T2, cfg.p, cfg.binorm, True,  # noqa: E731
+                             inp["perm1"], inp["perm2"], ws=ws)
+        fit()
+        torch.cuda.synchronize()
+        steps = steps_for(cfg)
+        vq.timing_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fit()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        rec = {(r[0], r[1]): r for r in vq.timing_records()}
+        vq.timing_enable(False)
+        n_sub = cfg.n_sub
+        row = {"M": cfg.M, "N": cfg.N, "K1": cfg.K1, "K2": cfg.K2, "steps": steps, "step_ms": round(ms, 2),
+               "value_G_subvector_assignments_per_s": round(n_sub * (cfg.T1 + cfg.T2) / (ms * 1e-3) / 1e9, 5)}
+
+        def avg(key):
+            r = rec.get(key)
+            return r[3] / r[2] if r else None
+        t = avg(("assign_search", cfg.K1))
+        if t:
+            fl = 32.0 * n_sub * cfg.K1
+            row["A4_search_stage1_ms"] = round(t, 4)
+            row["A4_frac_fp16_mfma"] = round(fl / (t * 1e-3) / 1e12 / PEAK_FP16_MFMA_TFLOPS, 4)
+        t = avg(("update", cfg.K1))
+        if t:
+            row["A5_update_stage1_ms"] = round(t, 4)
+            row["A5_frac_hbm_in_fit"] = round(algorithmic_bytes_update(n_sub, cfg.M, cfg.N, cfg.d, cfg.K1)
+                                              / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        t = avg(("reconstruct", cfg.K1))
+        if t:
+            row["A7_reconstruct_ms"] = round(t, 4)
+            row["A7_frac_hbm_in_fit"] = round(algorithmic_bytes_reconstruct(n_sub, cfg.M, cfg.N, cfg.d, cfg.K1,
+                                                                            cfg.K2, nnz, cfg.binorm)
+                                              / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        t = avg(("select", 0))
+        if t:
+            row["A1_select_ms"] = round(t, 4)
+        del W, h, ws
+        torch.cuda.empty_cache()
+        if cpu_seconds > 0:
+            c = cpu_baseline(cfg, inp, cpu_seconds)
+            row["oracle_assign_G_per_s"] = c["value"]
+            row["oracle_cores"] = c["cores"]
+        out_rows[cfg.name] = row
+        del inp
+    return out_rows
+
+
 def cpu_baseline(cfg, inp, seconds):
     """The oracle's assignment on a bounded sample (float64 exhaustive search)."""
     import numpy as np
@@ -466,6 +605,8 @@ def main():
     ap.add_argument("--no-correction", action="store_true", help="skip the unified sparse correction rows")
     ap.add_argument("--no-vptq", action="store_true", help="skip the VPTQ Algorithm 1 rows")
     ap.add_argument("--no-grouped", action="store_true", help="skip the grouped-fit row")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold/warm timing of the HBM rows")
+    ap.add_argument("--no-configs", action="store_true", help="skip the one-fit rows of the other workloads")
     ap.add_argument("--breakdown", action="store_true", help="print per-step timings to stderr")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB three times (a plain "
@@ -574,6 +715,35 @@ def main():
                                                                      not args.no_cpu_baseline)
     if not args.no_grouped:
         extra["rows"]["NEXT4_grouped_fit"] = grouped_bench(cfg, inp, W, h, ms_per_step, not args.no_cpu_baseline)
+    if not args.no_cold:
+        cw = cold_warm_rows(cfg, out, W, h, nnz, ws)
+        for k, v in cw.items():
+            extra["rows"].setdefault(k, {}).update({kk: vv for kk, vv in v.items() if kk != "algorithmic_MB"})
+        for k in ("A5_update_stage1", "A5_update_stage2", "A7_reconstruct"):
+            if k in cw:
+                extra[k + "_frac_hbm_cold"] = cw[k]["cold_frac_hbm"]
+                extra[k + "_frac_hbm_warm"] = cw[k]["warm_frac_hbm"]
+    if not args.no_configs:
+        del W, h, ws, out
+        torch.cuda.empty_cache()
+        others = [c for c in (1, 2, 3, 4, 5) if c != cfg.cid]
+        rows = config_rows(others, lambda c: 1 if c.n_sub > 10_000_000 else (2 if c.n_sub > 1_000_000 else 5),
+                           0.0 if args.no_cpu_baseline else 2.0)
+        main_row = {"M": cfg.M, "N": cfg.N, "K1": cfg.K1, "K2": cfg.K2, "steps": args.steps,
+                    "step_ms": round(ms_per_step, 2), "value_G_subvector_assignments_per_s": round(value, 5),
+                    "A4_search_stage1_ms": round(avg_s1, 4), "A4_frac_fp16_mfma": roofline["frac"]}
+        for k_src, k_dst in (("update_stage1_us", "A5_update_stage1_ms"), ("reconstruct_us", "A7_reconstruct_ms")):
+            if k_src in extra:
+                main_row[k_dst] = round(extra[k_src] / 1e3, 4)
+        if "update_stage1_frac_hbm" in extra:
+            main_row["A5_frac_hbm_in_fit"] = extra["update_stage1_frac_hbm"]
+        if "reconstruct_frac_hbm" in extra:
+            main_row["A7_frac_hbm_in_fit"] = extra["reconstruct_frac_hbm"]
+        if cpu:
+            main_row["oracle_assign_G_per_s"] = cpu["value"]
+            main_row["oracle_cores"] = cpu["cores"]
+        rows[cfg.name] = main_row
+        extra["rows"]["configs"] = {configs.get(c).name: rows[configs.get(c).name] for c in (1, 2, 3, 4, 5)}
 
     line = {
         "metric": "sub-vectors assigned/s per Lloyd iter (G/s) + % FP32 peak; update/recon HBM GB/s",
