@@ -309,9 +309,10 @@ def vptq_bench(cfg, inp, run_oracle, V=8, B=128):
     H = X^T X of the workload's activations (float64 Cholesky and triangular
     inverse), then the column-by-column quantization with the workload's codebook
     size (codebook rows drawn from the matrix's column sub-vectors).  HIP-event
-    times: the factor against the float64 peak (2N^3/3 flops), the block updates
-    against the float32 matrix-core peak, the columns as distance pairs/s; the
-    oracle on one group of V rows at the full width."""
+    times: the factor against the float64 peak (2N^3/3 flops), the float64 block
+    updates against the float64 peak, the columns as distance pairs/s, and the
+    number of decisions that took the exact float64 search; the oracle on one
+    group of V rows at the full width."""
     import numpy as np
     import torch
 
@@ -352,7 +353,9 @@ def vptq_bench(cfg, inp, run_oracle, V=8, B=128):
            "vptq_total_ms": round(t_v, 2),
            "block_update": {"gpu_ms": round(gu[3], 2), "launches": gu[2], "flop": gemm_flops,
                             "TFLOPs": round(gemm_flops / (gu[3] * 1e-3) / 1e12, 2),
-                            "frac_fp32_mfma": round(gemm_flops / (gu[3] * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)},
+                            "frac_fp64": round(gemm_flops / (gu[3] * 1e-3) / 1e12 / PEAK_FP64_TFLOPS, 4),
+                            "note": "float64 vector units, each product rounded then added (the oracle's order)"},
+           "exact_searches": rec[("vptq_exact_searches", K)][2] if ("vptq_exact_searches", K) in rec else None,
            "columns": {"gpu_ms": round(t_v - gu[3], 2),
                        "G_pairs_per_s": round(pairs / ((t_v - gu[3]) * 1e-3) / 1e9, 1),
                        "us_per_column": round((t_v - gu[3]) * 1e3 / N, 2)}}

@@ -98,6 +98,11 @@ class TimedRegion {
     void* a_ = nullptr;
 };
 
+// Diagnostics beside the timing records: whether timing is on, and a count
+// added to the launches of record (name, K) (no time) while it is.
+bool timing_on();
+void timing_count(const char* name, int K, int64_t n);
+
 inline unsigned grid_for(int64_t work, int per_block) {
     int64_t g = (work + per_block - 1) / per_block;
     return static_cast<unsigned>(g < 1 ? 1 : g);

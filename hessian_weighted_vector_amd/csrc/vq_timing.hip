@@ -82,6 +82,21 @@ TimedRegion::~TimedRegion()
     g_pending.push_back({name_, K_, static_cast<hipEvent_t>(a_), b});
 }
 
+bool timing_on()
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    return g_on;
+}
+
+void timing_count(const char* name, int K, int64_t n)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_on) return;
+    Stat& s = g_stats[{name, K}];
+    s.launches += n;
+    s.min_ms = 0.0;
+}
+
 }  // namespace vq
 
 using namespace vq;

@@ -6,6 +6,15 @@
 // column at the block's end through U[s:s+B, s+B:].  U is the matrix the
 // algorithm reads where the page writes H^-1.
 //
+// Arithmetic.  The working matrix and the errors are float64, and every
+// update is taken in the order and rounding of the algorithm as written: a
+// column's error is applied to each later column of its block, column after
+// column, as w - e*u (product rounded, then the difference; no fused
+// multiply-add), and the block's end adds e*u over the block's columns in
+// column order into a float64 sum that is then subtracted.  Every nearest-row
+// decision equals the exact float64 direct-form one (lowest index among equal
+// distances), so the whole trajectory is the float64 algorithm's, bit for bit.
+//
 // Layout.  The matrix is transposed into the workspace (row n of Wt is
 // column n of W, contiguous), and the quantized matrix and the errors are
 // kept transposed too; they are transposed back at the end.
@@ -15,21 +24,20 @@
 //                  error's share of the block's later columns) and searches
 //                  column n on the fp16 matrix cores with split operands
 //                  (expanded form, the codebook prepared once per call by
-//                  k_vp_absmax and k_vp_prep); workgroups split K, and the
-//                  per-sub-vector minima meet in a packed 64-bit atomicMin of
-//                  (score bits, index): the order of arrival does not matter,
-//                  and equal scores keep the lowest index;
+//                  k_vp_absmax and k_vp_prep); workgroups split K, and each
+//                  sub-vector's best and second-best scores meet in packed
+//                  64-bit atomicMin keys of (score bits, index);
+//   k_col_exact    certifies each best against a rounding bound and searches
+//                  the rest again exactly in float64, split over K;
 //   k_col_last     finishes the block's last column.
-// Other V, two launches per column:
-//   k_col_assign   the direct form in float32 on the vector units, merged the
-//                  same way;
-//   k_col_finalize reads the winners, writes indices, What and E, clears the
-//                  other key buffer for the next column, and applies the
-//                  in-block update to the rows j of the block (a 2D grid over
-//                  elements and groups of rows).
-// Per block: k_block_gemm, Wt[s+B:, :] -= U[s:s+B, s+B:]^T Et[s:s+B, :], a
-// float32 matrix-core GEMM (v_mfma_f32_32x32x2f32) over double-buffered LDS
-// panels.
+// Other V, or a codebook that is not 16-byte aligned, two launches per column:
+//   k_col_assign   the direct form in float64 on the vector units, one result
+//                  per 256-centroid chunk;
+//   k_col_finalize merges the chunks in order, writes indices, What and E, and
+//                  applies the in-block update to the rows j of the block (a
+//                  2D grid over elements and groups of rows).
+// Per block: k_block_gemm, Wt[s+B:, :] -= U[s:s+B, s+B:]^T Et[s:s+B, :] in
+// float64 on the vector units, each output's sum taken over k in order.
 #include "vq_internal.h"
 
 namespace vq {
@@ -41,9 +49,9 @@ constexpr int kAsgChunk = 256;      // centroids per assignment workgroup
 constexpr int kFinThreads = 256;
 constexpr int kFinRows = 16;        // in-block rows per finalize workgroup
 
-// dst [Cc x R] = src [R x Cc]^T through a padded LDS tile.
-__global__ __launch_bounds__(256) void k_transpose(const float* __restrict__ src, int64_t R, int64_t Cc,
-                                                   float* __restrict__ dst)
+// dst [Cc x R] (float64) = src [R x Cc]^T (float32) through a padded LDS tile.
+__global__ __launch_bounds__(256) void k_transpose_in(const float* __restrict__ src, int64_t R, int64_t Cc,
+                                                      double* __restrict__ dst)
 {
     __shared__ float t[kTr][kTr + 1];
     const int64_t r0 = (int64_t)blockIdx.y * kTr, c0 = (int64_t)blockIdx.x * kTr;
@@ -51,6 +59,26 @@ __global__ __launch_bounds__(256) void k_transpose(const float* __restrict__ src
     for (int k = ty; k < kTr; k += 8) {
         const int64_t r = r0 + k, c = c0 + tx;
         if (r < R && c < Cc) t[k][tx] = src[r * Cc + c];
+    }
+    __syncthreads();
+    for (int k = ty; k < kTr; k += 8) {
+        const int64_t c = c0 + k, r = r0 + tx;
+        if (r < R && c < Cc) dst[c * R + r] = (double)t[tx][k];
+    }
+}
+
+// dst [Cc x R] (float32) = src [R x Cc]^T, src float32 or float64 (rounded to
+// nearest float32).
+template <class T>
+__global__ __launch_bounds__(256) void k_transpose_out(const T* __restrict__ src, int64_t R, int64_t Cc,
+                                                       float* __restrict__ dst)
+{
+    __shared__ float t[kTr][kTr + 1];
+    const int64_t r0 = (int64_t)blockIdx.y * kTr, c0 = (int64_t)blockIdx.x * kTr;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    for (int k = ty; k < kTr; k += 8) {
+        const int64_t r = r0 + k, c = c0 + tx;
+        if (r < R && c < Cc) t[k][tx] = (float)src[r * Cc + c];
     }
     __syncthreads();
     for (int k = ty; k < kTr; k += 8) {
@@ -65,19 +93,19 @@ __global__ void k_fill_u64(unsigned long long* __restrict__ p, int64_t n, unsign
     if (q < n) p[q] = v;
 }
 
-// Nearest codebook row of each sub-vector of x (one column, nv sub-vectors of
-// V floats, any V) among the workgroup's chunk of centroids, direct form in
-// float32 on the vector units; the chunk's winner is merged into keys[v] as
-// (order-preserving bits of the distance, index).
-__device__ inline unsigned sortable(float f)
+__global__ void k_fill_i32(int* __restrict__ p, int64_t n, int v)
 {
-    const unsigned u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q < n) p[q] = v;
 }
 
-__global__ __launch_bounds__(kAsgThreads) void k_col_assign(const float* __restrict__ x, int nv, int V,
+// Nearest codebook row of each sub-vector of x (one working column, nv
+// sub-vectors of V float64 values, any V) among the workgroup's chunk of
+// centroids: the direct form in float64 with the terms added in t order, the
+// lowest index among equal distances.  Result per (chunk, sub-vector).
+__global__ __launch_bounds__(kAsgThreads) void k_col_assign(const double* __restrict__ x, int nv, int V,
                                                             const float* __restrict__ C, int K,
-                                                            unsigned long long* __restrict__ keys)
+                                                            double* __restrict__ part_d, int* __restrict__ part_i)
 {
     __shared__ float cs[kAsgChunk * 8];
     const int k0 = blockIdx.y * kAsgChunk;
@@ -86,20 +114,32 @@ __global__ __launch_bounds__(kAsgThreads) void k_col_assign(const float* __restr
     __syncthreads();
     const int v = blockIdx.x * kAsgThreads + threadIdx.x;
     if (v >= nv) return;
-    float xv[8];
-    for (int t = 0; t < 8; ++t) xv[t] = t < V ? x[(size_t)v * V + t] : 0.0f;
-    float best = __builtin_inff();
+    double xv[8];
+    for (int t = 0; t < 8; ++t) xv[t] = t < V ? x[(size_t)v * V + t] : 0.0;
+    double best = __builtin_inf();
     int arg = 0;
     for (int k = 0; k < kn; ++k) {
-        float dist = 0.0f;
+        double dist = 0.0;
         for (int t = 0; t < V; ++t) {
-            const float df = xv[t] - cs[k * V + t];
-            dist = fmaf(df, df, dist);
+            const double df = xv[t] - (double)cs[k * V + t];
+            dist += df * df;
         }
         if (dist < best) { best = dist; arg = k; }
     }
-    const unsigned long long key = ((unsigned long long)sortable(best) << 32) | (unsigned)(k0 + arg);
-    atomicMin(&keys[v], key);
+    part_d[(size_t)blockIdx.y * nv + v] = best;
+    part_i[(size_t)blockIdx.y * nv + v] = k0 + arg;
+}
+
+// order-preserving bits of a float (finite or infinite)
+__device__ inline unsigned sortable(float f)
+{
+    const unsigned u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline float unsortable(unsigned v)
+{
+    return __uint_as_float((v & 0x80000000u) ? (v & 0x7FFFFFFFu) : ~v);
 }
 
 // V = 8 on the fp16 matrix cores with split operands.  Once per call the
@@ -115,34 +155,43 @@ __global__ __launch_bounds__(kAsgThreads) void k_col_assign(const float* __restr
 // k-slots (l / 32) * 8 .. + 8 of row (A: centroid) or column (B: sub-vector)
 // l % 32; accumulator r of lane l is centroid (r / 4) * 8 + (l / 32) * 4 +
 // r % 4 of the tile.  The workgroup stages kVpChunk prepared centroids in LDS
-// and its four wavefronts search them for 32 sub-vectors each; the chunk's
-// winner enters one of kKeySlots copies of keys[v] as (order-preserving bits
-// of -acc, index) through atomicMin; readers take the smallest copy.  Scores
-// of different chunks are comparable: the wave grouping of sub-vectors, hence
-// sx, is the same in every chunk.
+// and its four wavefronts search them for 32 sub-vectors each.  Each lane
+// keeps the largest and second-largest acc it sees; per sub-vector the
+// chunk's best enters key A and the chunk's second-best (and every best that
+// a smaller key displaces from A) enters key B, both by atomicMin on
+// (order-preserving bits of -acc, index), one of kKeySlots copies per chunk:
+// afterwards the smallest key over A's copies is the best of all chunks and
+// the smallest over the rest is the second best.  Scores of different chunks
+// are comparable: the wave grouping of sub-vectors, hence sx, is the same in
+// every chunk.
+//
+// Certification.  With u = 2^-24, the computed score of centroid k differs
+// from <c_k, x> - |c_k|^2/2 (x the float64 working values) by at most
+//   2^-18 (1.25 |c_k| |x| + 0.625 |c_k|^2 / 2) + beta 2^-(sc+sx):
+// each of the two 16-product float32 sums errs by at most 32u of the
+// magnitudes it adds (the first: the sum of |c_t x_t|; the second: that again
+// plus the norm term), the split drops at most 3 * 2^-22 |c_t x_t| per term,
+// and x's rounding to float32 adds u; beta = 2^-8 covers subnormal split parts
+// in scaled units.  Without the norm term (its power-of-two factor below
+// fp16's range) |c_k|^2 / 2 is added.  Any centroid at least as near as the
+// best's has |c_k| <= R = |x| + sqrt(D_best), so when best - second exceeds
+// twice that bound at |c_k| = R the best is the exact nearest row, and
+// float64 rounding of the direct form (relative 2^-49) cannot reorder it.
+// k_col_exact makes this check and searches the sub-vectors that fail again
+// over the whole codebook in float64 (the direct form, terms in t order), each
+// workgroup over its 512-centroid chunk, and the last of them merges the
+// chunks in order (lowest index on ties).
 constexpr int kVpChunk = 512;        // centroids per workgroup (prepared codebook is padded to whole chunks)
 constexpr int kHnShift = 9;          // hn 2^(2 sc) < 2^22, its pieces below 2^13
+constexpr int kStepRows = 128;       // sub-vectors per workgroup of the column step (4 waves x 32)
 
 constexpr int kKeySlots = 4;         // key copies per column: chunk y merges into slot y % kKeySlots
 
 // Key buffers of the V = 8 path: three columns in rotation, each with
-// kKeySlots copies of nv keys (spreading the atomicMin traffic of the
-// K-chunk workgroups over several addresses); a column's winner is the
-// smallest key over its slots.
-__device__ inline size_t key_at(int nv, int slot, int64_t n, int j)
+// kKeySlots copies of an A and a B key per sub-vector.
+__device__ inline size_t key_at(int nv, int slot, int kind, int64_t n, int j)
 {
-    return ((size_t)(n % 3) * kKeySlots + (size_t)slot) * (size_t)nv + (size_t)j;
-}
-
-__device__ inline unsigned long long key_min(const unsigned long long* __restrict__ keys, int nv, int64_t n, int j)
-{
-    unsigned long long k = ~0ull;
-#pragma unroll
-    for (int q = 0; q < kKeySlots; ++q) {
-        const unsigned long long o = keys[key_at(nv, q, n, j)];
-        k = o < k ? o : k;
-    }
-    return k;
+    return (((size_t)(n % 3) * kKeySlots + (size_t)slot) * 2 + (size_t)kind) * (size_t)nv + (size_t)j;
 }
 
 typedef float vp_f32x16 __attribute__((ext_vector_type(16)));
@@ -209,10 +258,11 @@ __global__ __launch_bounds__(256) void k_vp_prep(const float* __restrict__ C, in
 }
 
 __global__ __launch_bounds__(256) void k_col_step_h16(
-    float* __restrict__ Wt, int64_t M, int nv, int64_t n, int64_t s, int64_t s_end, const float* __restrict__ C,
-    const float* __restrict__ U, int64_t N, unsigned long long* __restrict__ keys, float* __restrict__ Xc,
-    uint16_t* __restrict__ idx, float* __restrict__ Wht, float* __restrict__ Et, const vp_h16x8* __restrict__ Phi,
-    const vp_h16x8* __restrict__ Plo, const vp_h16x8* __restrict__ Phn, const float* __restrict__ cmax, int K)
+    double* __restrict__ Wt, int64_t M, int nv, int64_t n, int64_t s, int64_t s_end, const float* __restrict__ C,
+    const float* __restrict__ U, int64_t N, unsigned long long* __restrict__ keys, const int* __restrict__ win,
+    double* __restrict__ Xc, uint16_t* __restrict__ idx, float* __restrict__ Wht, double* __restrict__ Et,
+    const vp_h16x8* __restrict__ Phi, const vp_h16x8* __restrict__ Plo, const vp_h16x8* __restrict__ Phn,
+    const float* __restrict__ cmax, int K)
 {
     __shared__ vp_h16x8 L[3][kVpChunk];
     const int k0 = blockIdx.y * kVpChunk;
@@ -226,30 +276,36 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
     const int j0 = (blockIdx.x * 4 + wave) * 32;
     const int jl = lane & 31, half = lane >> 5;
     const int j = j0 + jl;
-    float xv[8];
+    const bool active = j0 < nv;                         // the wave holds sub-vectors
+    double x64[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) xv[t] = 0.0f;
+    for (int t = 0; t < 8; ++t) x64[t] = 0.0;
     if (j < nv) {
-        const float4* w4 = reinterpret_cast<const float4*>(Wt + n * M) + 2 * (size_t)j;
-        const float4 wa = w4[0], wb = w4[1];
-        const float w[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+        const double2* w2 = reinterpret_cast<const double2*>(Wt + n * M) + 4 * (size_t)j;
+        double w[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const double2 v2 = w2[q];
+            w[2 * q] = v2.x;
+            w[2 * q + 1] = v2.y;
+        }
         if (n > s) {
             // column n-1 of the block: its winner, value, error; the error's
             // share of column n is applied here (every workgroup of these rows
             // forms the same values), its share of the block's later columns
             // is split over the workgroups of these rows by column
             const int64_t p = n - 1;
-            const unsigned kp = (unsigned)(key_min(keys, nv, p, j) & 0xFFFFFFFFull);
+            const int kp = win[(size_t)(p & 1) * nv + j];
             const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)kp;
             const float4 ca = c4[0], cb = c4[1];
             const float qv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
-            const float* xp = Xc + (size_t)(p & 1) * M + (size_t)j * 8;
-            const float unn = U[p * N + p], un = U[p * N + n];
-            float e[8];
+            const double* xp = Xc + (size_t)(p & 1) * M + (size_t)j * 8;
+            const double unn = (double)U[p * N + p], un = (double)U[p * N + n];
+            double e[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                e[t] = (xp[t] - qv[t]) / unn;
-                xv[t] = fmaf(-e[t], un, w[t]);
+                e[t] = (xp[t] - (double)qv[t]) / unn;
+                x64[t] = w[t] - e[t] * un;
             }
             if (blockIdx.y == 0 && half == 0) {
 #pragma unroll
@@ -260,181 +316,371 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
                 idx[p * nv + j] = (uint16_t)kp;
             }
             for (int64_t r = n + 1 + blockIdx.y; r < s_end; r += gridDim.y) {
-                const float u = U[p * N + r];
-                float* wr = Wt + r * M + (int64_t)j * 8 + half * 4;
+                const double u = (double)U[p * N + r];
+                double* wr = Wt + r * M + (int64_t)j * 8 + half * 4;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) wr[t] = fmaf(-e[half * 4 + t], u, wr[t]);
+                for (int t = 0; t < 4; ++t) wr[t] = wr[t] - e[half * 4 + t] * u;
             }
         } else {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) xv[t] = w[t];
+            for (int t = 0; t < 8; ++t) x64[t] = w[t];
         }
         if (blockIdx.y == 0 && half == 0) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) Xc[(size_t)(n & 1) * M + (size_t)j * 8 + t] = xv[t];
+            for (int t = 0; t < 8; ++t) Xc[(size_t)(n & 1) * M + (size_t)j * 8 + t] = x64[t];
 #pragma unroll
-            for (int q = 0; q < kKeySlots; ++q) keys[key_at(nv, q, n + 1, j)] = ~0ull;
+            for (int q = 0; q < kKeySlots; ++q) {
+                keys[key_at(nv, q, 0, n + 1, j)] = ~0ull;
+                keys[key_at(nv, q, 1, n + 1, j)] = ~0ull;
+            }
         }
     }
     __syncthreads();
-    if (j0 >= nv) return;
     // the wave's scale (both halves hold the same 32 sub-vectors)
+    float xv[8];
     float mx = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) mx = fmaxf(mx, fabsf(xv[t]));
+    for (int t = 0; t < 8; ++t) {
+        xv[t] = (float)x64[t];
+        mx = fmaxf(mx, fabsf(xv[t]));
+    }
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     const int sc = vp_scale_exp(*cmax);
     const int sx = min(vp_scale_exp(mx), sc + 15 - kHnShift);
     const int eb = kHnShift + sx - sc;                  // <= 15: b is a finite fp16
     const _Float16 b = eb >= -24 ? (_Float16)(-ldexpf(1.0f, eb)) : (_Float16)0.0f;
-    vp_h16x8 bh, b2;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const float xs = ldexpf(xv[t], sx);
-        const _Float16 h = (_Float16)xs;
-        bh[t] = h;
-        b2[t] = half ? (t < 3 ? b : (_Float16)0.0f) : (_Float16)(xs - (float)h);
-    }
-    const vp_h16x8* A1 = L[half ? 1 : 0];
-    const vp_h16x8* A2 = L[half ? 2 : 0];
-    float best = -__builtin_inff();
+    float best = -__builtin_inff(), sec = -__builtin_inff();
     int bi = 0;
-    const int ntiles = (kn + 31) / 32;
-    auto scan = [&](vp_f32x16 acc, int tb) {
-        if (tb + 32 > kn) {                              // the chunk's last, partial tile
+    if (active) {
+        vp_h16x8 bh, b2;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (tb + (r >> 2) * 8 + half * 4 + (r & 3) >= kn) acc[r] = -__builtin_inff();
+        for (int t = 0; t < 8; ++t) {
+            const float xs = ldexpf(xv[t], sx);
+            const _Float16 h = (_Float16)xs;
+            bh[t] = h;
+            b2[t] = half ? (t < 3 ? b : (_Float16)0.0f) : (_Float16)(xs - (float)h);
         }
-        float m = acc[0];
+        const vp_h16x8* A1 = L[half ? 1 : 0];
+        const vp_h16x8* A2 = L[half ? 2 : 0];
+        const int ntiles = (kn + 31) / 32;
+        // running best and second best of the lane's scores; the best's index
+        auto scan = [&](vp_f32x16 acc, int tb) {
+            if (tb + 32 > kn) {                          // the chunk's last, partial tile
 #pragma unroll
-        for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[r]);
-        if (m > best) {
-            int rr = 0;
+                for (int r = 0; r < 16; ++r)
+                    if (tb + (r >> 2) * 8 + half * 4 + (r & 3) >= kn) acc[r] = -__builtin_inff();
+            }
+            float m = acc[0], m2 = -__builtin_inff();
 #pragma unroll
-            for (int r = 15; r >= 0; --r)
-                if (acc[r] == m) rr = r;
-            best = m;
-            bi = tb + (rr >> 2) * 8 + half * 4 + (rr & 3);
+            for (int r = 1; r < 16; ++r) {
+                m2 = __builtin_amdgcn_fmed3f(m, m2, acc[r]);
+                m = fmaxf(m, acc[r]);
+            }
+            sec = fmaxf(__builtin_amdgcn_fmed3f(best, sec, m), m2);
+            if (m > best) {
+                int rr = 0;
+#pragma unroll
+                for (int r = 15; r >= 0; --r)
+                    if (acc[r] == m) rr = r;
+                best = m;
+                bi = tb + (rr >> 2) * 8 + half * 4 + (rr & 3);
+            }
+        };
+        const vp_f32x16 zero = {};
+        int tb = 0;
+        for (; tb + 32 < ntiles * 32; tb += 64) {
+            vp_f32x16 a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[tb + jl], bh, zero, 0, 0, 0);
+            vp_f32x16 a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[tb + 32 + jl], bh, zero, 0, 0, 0);
+            a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A2[tb + jl], b2, a0, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A2[tb + 32 + jl], b2, a1, 0, 0, 0);
+            scan(a0, tb);
+            scan(a1, tb + 32);
         }
-    };
-    const vp_f32x16 zero = {};
-    int tb = 0;
-    for (; tb + 32 < ntiles * 32; tb += 64) {
-        vp_f32x16 a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[tb + jl], bh, zero, 0, 0, 0);
-        vp_f32x16 a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[tb + 32 + jl], bh, zero, 0, 0, 0);
-        a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A2[tb + jl], b2, a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A2[tb + 32 + jl], b2, a1, 0, 0, 0);
-        scan(a0, tb);
-        scan(a1, tb + 32);
+        if (tb < ntiles * 32) {
+            vp_f32x16 a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[tb + jl], bh, zero, 0, 0, 0);
+            a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A2[tb + jl], b2, a0, 0, 0, 0);
+            scan(a0, tb);
+        }
+        // the two halves of the sub-vector's centroid rows: best with the
+        // lower index among equal scores, second best of the four values
+        const float ob = __shfl_xor(best, 32), os = __shfl_xor(sec, 32);
+        const int oi = __shfl_xor(bi, 32);
+        const float lo = fminf(best, ob);
+        sec = fmaxf(fmaxf(sec, os), lo);
+        if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+        if (half == 0 && j < nv) {
+            const int slot = blockIdx.y % kKeySlots;
+            const unsigned long long kb_ = ((unsigned long long)sortable(-best + 0.0f) << 32) | (unsigned)(k0 + bi);
+            const unsigned long long ks_ = ((unsigned long long)sortable(-sec + 0.0f) << 32) | 0xFFFFFFFFull;
+            const unsigned long long old = atomicMin(&keys[key_at(nv, slot, 0, n, j)], kb_);
+            const unsigned long long lost = old > kb_ ? old : kb_;
+            atomicMin(&keys[key_at(nv, slot, 1, n, j)], lost < ks_ ? lost : ks_);
+        }
     }
-    if (tb < ntiles * 32) {
-        vp_f32x16 a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[tb + jl], bh, zero, 0, 0, 0);
-        a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A2[tb + jl], b2, a0, 0, 0, 0);
-        scan(a0, tb);
+}
+
+// Column n's winners (V = 8 path).  Grid: x over row blocks of kStepRows
+// sub-vectors, y over 512-centroid chunks.  Every workgroup of a row block
+// reads the best and second-best keys of its sub-vectors and makes the same
+// certification (the working values from Xc give the same per-wave scale as
+// the search); the first chunk's workgroup writes the certified winners.  The
+// others are searched again in float64 (direct form, terms in t order,
+// strictly smaller wins, so the lowest index keeps a tie), each workgroup over
+// its chunk, and the last workgroup of the row block (an arrival counter)
+// merges the chunks in chunk order.
+__global__ __launch_bounds__(256) void k_col_exact(int nv, int64_t n, int64_t M, const float* __restrict__ C, int K,
+                                                   const unsigned long long* __restrict__ keys,
+                                                   const float* __restrict__ cmax, const double* __restrict__ Xc,
+                                                   double* __restrict__ part_d, int* __restrict__ part_i,
+                                                   int* __restrict__ arrived, int* __restrict__ win,
+                                                   int* __restrict__ fl_total)
+{
+    __shared__ int s_nflag, s_last;
+    __shared__ int s_flag[kStepRows];
+    __shared__ double s_rd[256];
+    __shared__ int s_ri[256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int jl = lane & 31, half = lane >> 5;
+    const int j = (blockIdx.x * 4 + wave) * 32 + jl;
+    if (threadIdx.x == 0) s_nflag = 0;
+    double x64[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) x64[t] = 0.0;
+    float mx = 0.0f;
+    if (j < nv) {
+        const double* x = Xc + (size_t)(n & 1) * M + (size_t)j * 8;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            x64[t] = x[t];
+            mx = fmaxf(mx, fabsf((float)x64[t]));
+        }
     }
-    const float sco = -best + 0.0f;                      // -0 -> +0: one key per score
-    unsigned long long key = ((unsigned long long)sortable(sco) << 32) | (unsigned)(k0 + bi);
-    const unsigned long long other = __shfl_xor(key, 32);
-    key = other < key ? other : key;
-    if (half == 0 && j < nv) atomicMin(&keys[key_at(nv, blockIdx.y % kKeySlots, n, j)], key);
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const int sc = vp_scale_exp(*cmax);
+    const int sx = min(vp_scale_exp(mx), sc + 15 - kHnShift);
+    const bool no_norm = kHnShift + sx - sc < -24;      // the search ran without the norm term
+    __syncthreads();
+    if (half == 0 && j < nv) {
+        unsigned long long a1 = ~0ull, a2 = ~0ull, bmin = ~0ull;
+#pragma unroll
+        for (int q = 0; q < kKeySlots; ++q) {
+            const unsigned long long ka = keys[key_at(nv, q, 0, n, j)];
+            const unsigned long long kb = keys[key_at(nv, q, 1, n, j)];
+            if (ka < a1) { a2 = a1; a1 = ka; } else if (ka < a2) { a2 = ka; }
+            bmin = kb < bmin ? kb : bmin;
+        }
+        const unsigned long long k2 = a2 < bmin ? a2 : bmin;
+        const int kbest = (int)(a1 & 0xFFFFFFFFull);
+        bool ok = true;
+        if (k2 != ~0ull) {
+            const double sA = -(double)unsortable((unsigned)(a1 >> 32));
+            const double sB = -(double)unsortable((unsigned)(k2 >> 32));
+            const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)kbest;
+            const float4 ca = c4[0], cb = c4[1];
+            const float qv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+            double nx2 = 0.0, db = 0.0;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                nx2 += x64[t] * x64[t];
+                const double df = x64[t] - (double)qv[t];
+                db += df * df;
+            }
+            const double nx = sqrt(nx2) * (1.0 + 0x1p-40);
+            const double R = nx + sqrt(db) * (1.0 + 0x1p-40);
+            double bound = 0x1p-18 * (1.25 * R * nx + 0.3125 * R * R) + ldexp(0x1p-8, -(sc + sx)) +
+                           0x1p-45 * (nx2 + db);
+            if (no_norm) bound += 0.5 * R * R;
+            const double gap = ldexp(sA - sB, -(sc + sx));
+            ok = gap > 2.0 * bound;                      // false also for NaN
+        }
+        if (ok) {
+            if (blockIdx.y == 0) win[(size_t)(n & 1) * nv + j] = kbest;
+        } else {
+            s_flag[atomicAdd(&s_nflag, 1)] = wave * 32 + jl;
+        }
+    }
+    __syncthreads();
+    const int cnt = s_nflag;
+    if (cnt == 0) return;
+    const int k0 = blockIdx.y * kVpChunk;
+    const int kn = K - k0 < kVpChunk ? K - k0 : kVpChunk;
+    for (int f = 0; f < cnt; ++f) {
+        const int jj = blockIdx.x * kStepRows + s_flag[f];
+        const double* x = Xc + (size_t)(n & 1) * M + (size_t)jj * 8;
+        double xv[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) xv[t] = x[t];
+        double bd = __builtin_inf();
+        int bk = 0;
+        for (int q = threadIdx.x; q < kn; q += 256) {
+            const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)(k0 + q);
+            const float4 ca = c4[0], cb = c4[1];
+            const float cv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+            double dist = 0.0;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const double df = xv[t] - (double)cv[t];
+                dist += df * df;
+            }
+            if (dist < bd) { bd = dist; bk = k0 + q; }
+        }
+        s_rd[threadIdx.x] = bd;
+        s_ri[threadIdx.x] = bk;
+        __syncthreads();
+        for (int w = 128; w > 0; w >>= 1) {
+            if ((int)threadIdx.x < w) {
+                const double od = s_rd[threadIdx.x + w];
+                const int oi = s_ri[threadIdx.x + w];
+                if (od < s_rd[threadIdx.x] || (od == s_rd[threadIdx.x] && oi < s_ri[threadIdx.x])) {
+                    s_rd[threadIdx.x] = od;
+                    s_ri[threadIdx.x] = oi;
+                }
+            }
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) {
+            // device-scope stores: visible to the merging workgroup without a
+            // cache write-back
+            __hip_atomic_store(&part_d[(size_t)blockIdx.y * nv + jj], s_rd[0], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&part_i[(size_t)blockIdx.y * nv + jj], s_ri[0], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(&arrived[blockIdx.x], 1) == (int)gridDim.y - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // one wavefront per listed sub-vector: its lanes load the chunks' results
+    // at once, then the smallest (distance, index) wins, which is the
+    // chunk-order merge with strict comparison
+    for (int f = wave; f < cnt; f += 4) {
+        const int jj = blockIdx.x * kStepRows + s_flag[f];
+        double bd = __builtin_inf();
+        int bk = 0x7FFFFFFF;
+        for (int c = lane; c < (int)gridDim.y; c += 64) {
+            const double d = __hip_atomic_load(&part_d[(size_t)c * nv + jj], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+            const int i = __hip_atomic_load(&part_i[(size_t)c * nv + jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d < bd || (d == bd && i < bk)) { bd = d; bk = i; }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const double od = __shfl_xor(bd, o);
+            const int oi = __shfl_xor(bk, o);
+            if (od < bd || (od == bd && oi < bk)) { bd = od; bk = oi; }
+        }
+        if (lane == 0) win[(size_t)(n & 1) * nv + jj] = bk;
+    }
+    if (threadIdx.x == 0) {
+        arrived[blockIdx.x] = 0;
+        atomicAdd(fl_total, cnt);
+    }
 }
 
 // The block's last column n (V = 8 path): winner, value and error; nothing of
 // the block is left to update.
 __global__ __launch_bounds__(256) void k_col_last(int64_t M, int nv, int64_t n, const float* __restrict__ C,
-                                                  const float* __restrict__ U, int64_t N,
-                                                  const unsigned long long* __restrict__ keys,
-                                                  const float* __restrict__ Xc, uint16_t* __restrict__ idx,
-                                                  float* __restrict__ Wht, float* __restrict__ Et)
+                                                  const float* __restrict__ U, int64_t N, const int* __restrict__ win,
+                                                  const double* __restrict__ Xc, uint16_t* __restrict__ idx,
+                                                  float* __restrict__ Wht, double* __restrict__ Et)
 {
     const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (m >= M) return;
     const int v = (int)(m >> 3), t = (int)(m & 7);
-    const unsigned k = (unsigned)(key_min(keys, nv, n, v) & 0xFFFFFFFFull);
+    const int k = win[(size_t)(n & 1) * nv + v];
     const float wq = C[(size_t)k * 8 + t];
-    const float e = (Xc[(size_t)(n & 1) * M + m] - wq) / U[n * N + n];
+    const double e = (Xc[(size_t)(n & 1) * M + m] - (double)wq) / (double)U[n * N + n];
     Wht[n * M + m] = wq;
     Et[n * M + m] = e;
     if (t == 0) idx[n * nv + v] = (uint16_t)k;
 }
 
-// Column n: winners -> indices, What, E; the other key buffer is cleared for
-// the next column; the block's rows j in (n, s_end) receive -E[:,n] U[n,j].
-// Grid: x over the M elements, y over groups of kFinRows rows.
+// Column n (other V): the chunks' winners merged in chunk order (strictly
+// smaller distance wins, so the lowest index keeps a tie) -> indices, What,
+// E; the block's rows j in (n, s_end) receive w - E[:,n] U[n,j].  Grid: x over
+// the M elements, y over groups of kFinRows rows.
 __global__ __launch_bounds__(kFinThreads) void k_col_finalize(
-    float* __restrict__ Wt, int64_t M, int V, int nv, int64_t n, int64_t s_end, const float* __restrict__ C,
-    const float* __restrict__ U, int64_t N, const unsigned long long* __restrict__ keys,
-    unsigned long long* __restrict__ keys_next, uint16_t* __restrict__ idx, float* __restrict__ Wht,
-    float* __restrict__ Et)
+    double* __restrict__ Wt, int64_t M, int V, int nv, int64_t n, int64_t s_end, const float* __restrict__ C,
+    const float* __restrict__ U, int64_t N, const double* __restrict__ part_d, const int* __restrict__ part_i,
+    int nch, uint16_t* __restrict__ idx, float* __restrict__ Wht, double* __restrict__ Et)
 {
     const int64_t m = (int64_t)blockIdx.x * kFinThreads + threadIdx.x;
     if (m >= M) return;
     const int v = (int)(m / V);
     const int t = (int)(m - (int64_t)v * V);
-    const unsigned k = (unsigned)(keys[v] & 0xFFFFFFFFull);
+    double bd = part_d[v];
+    int k = part_i[v];
+    for (int c = 1; c < nch; ++c) {
+        const double d = part_d[(size_t)c * nv + v];
+        if (d < bd) { bd = d; k = part_i[(size_t)c * nv + v]; }
+    }
     const float wq = C[(size_t)k * V + t];
-    const float e = (Wt[n * M + m] - wq) / U[n * N + n];
+    const double e = (Wt[n * M + m] - (double)wq) / (double)U[n * N + n];
     const int64_t j0 = n + 1 + (int64_t)blockIdx.y * kFinRows;
     const int64_t j1 = j0 + kFinRows < s_end ? j0 + kFinRows : s_end;
-    for (int64_t j = j0; j < j1; ++j) Wt[j * M + m] = fmaf(-e, U[n * N + j], Wt[j * M + m]);
+    for (int64_t j = j0; j < j1; ++j) Wt[j * M + m] = Wt[j * M + m] - e * (double)U[n * N + j];
     if (blockIdx.y == 0) {
         Wht[n * M + m] = wq;
         Et[n * M + m] = e;
-        if (t == 0) {
-            idx[n * nv + v] = (uint16_t)k;
-            keys_next[v] = ~0ull;
-        }
+        if (t == 0) idx[n * nv + v] = (uint16_t)k;
     }
 }
 
-// Wt[s_end + r, m] -= sum_k U[s + k, s_end + r] * Et[s + k, m], k < kb, for a
-// 128 x 128 tile of (r, m).  k runs in chunks of kGemmK through double-buffered
-// LDS panels (k the slow index; the next chunk is loaded into registers while
-// the current one is used, one barrier per chunk).  Each of the 8 wavefronts
-// accumulates a 32 x 64 block as two 32 x 32 blocks of v_mfma_f32_32x32x2f32
-// (lane l feeds A[l%32][l/32] and B[l/32][l%32]); k pairs are taken in
-// increasing order.
-constexpr int kGemmT = 128;          // output tile edge
+// Wt[s_end + r, m] -= sum_{k < kb} Et[s + k, m] * U[s + k, s_end + r] in
+// float64: each output's sum starts at 0 and adds the products (each rounded,
+// then added) in k order, then is subtracted.  A 128 (r) x 64 (m) tile per
+// workgroup, 8 x 4 outputs per thread; k runs in chunks of kGemmK through
+// double-buffered LDS panels (U converted to float64 on the way in; the next
+// chunk is loaded into registers while the current one is used).
+constexpr int kGemmR = 128;          // output rows (later columns of W) per tile
+constexpr int kGemmM = 64;           // output elements per tile
 constexpr int kGemmK = 16;           // k per LDS chunk
-constexpr int kGemmLd = kGemmT + 4;  // padded LDS row
 
-__global__ __launch_bounds__(512) void k_block_gemm(float* __restrict__ Wt, const float* __restrict__ U,
-                                                    const float* __restrict__ Et, int64_t N, int64_t M,
+__global__ __launch_bounds__(256) void k_block_gemm(double* __restrict__ Wt, const float* __restrict__ U,
+                                                    const double* __restrict__ Et, int64_t N, int64_t M,
                                                     int64_t s, int kb, int64_t s_end)
 {
-    __shared__ float As[2][kGemmK][kGemmLd];
-    __shared__ float Bs[2][kGemmK][kGemmLd];
+    __shared__ double As[2][kGemmK][kGemmR];
+    __shared__ double Bs[2][kGemmK][kGemmM];
     const int64_t R = N - s_end;
-    const int64_t r0 = (int64_t)blockIdx.y * kGemmT, m0 = (int64_t)blockIdx.x * kGemmT;
+    const int64_t r0 = (int64_t)blockIdx.y * kGemmR, m0 = (int64_t)blockIdx.x * kGemmM;
     const int tid = threadIdx.x;
-    // loader: thread -> (k = tid / 32, columns 4 * (tid % 32) .. + 4) of each panel
-    const int lk_ = tid >> 5, lc = (tid & 31) * 4;
-    float ra[4], rb[4];
+    // loaders: U panel kGemmK x 128 (8 values per thread), E panel kGemmK x 64 (4 per thread)
+    const int ak = tid >> 4, ac = (tid & 15) * 8;
+    const int bk = tid >> 4, bc = (tid & 15) * 4;
+    double ra[8], rb[4];
     auto load = [&](int kc) {
-        const int k = kc + lk_;
+        const int k = kc + ak;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t r = r0 + ac + i;
+            ra[i] = (k < kb && r < R) ? (double)U[(s + k) * N + s_end + r] : 0.0;
+        }
+        const int k2 = kc + bk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t r = r0 + lc + i, mm = m0 + lc + i;
-            ra[i] = (k < kb && r < R) ? U[(s + k) * N + s_end + r] : 0.0f;
-            rb[i] = (k < kb && mm < M) ? Et[(s + k) * M + mm] : 0.0f;
+            const int64_t mm = m0 + bc + i;
+            rb[i] = (k2 < kb && mm < M) ? Et[(s + k2) * M + mm] : 0.0;
         }
     };
     auto store = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            As[buf][lk_][lc + i] = ra[i];
-            Bs[buf][lk_][lc + i] = rb[i];
-        }
-    };
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wr = (wave & 3) * 32, wc = (wave >> 2) * 64;
-    const int li = lane & 31, lk = lane >> 5;
-    typedef float f16x_t __attribute__((ext_vector_type(16)));
-    f16x_t acc0, acc1;
+        for (int i = 0; i < 8; ++i) As[buf][ak][ac + i] = ra[i];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { acc0[r] = 0.0f; acc1[r] = 0.0f; }
+        for (int i = 0; i < 4; ++i) Bs[buf][bk][bc + i] = rb[i];
+    };
+    const int tr = (tid >> 4) * 8, tm = (tid & 15) * 4;
+    double acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] = 0.0;
     const int nk = (kb + kGemmK - 1) / kGemmK;
     load(0);
     store(0);
@@ -442,29 +688,29 @@ __global__ __launch_bounds__(512) void k_block_gemm(float* __restrict__ Wt, cons
     for (int c = 0; c < nk; ++c) {
         const int buf = c & 1;
         if (c + 1 < nk) load((c + 1) * kGemmK);
+        const int kk_end = kb - c * kGemmK < kGemmK ? kb - c * kGemmK : kGemmK;
+        for (int kk = 0; kk < kk_end; ++kk) {
+            double a[8], bb[4];
 #pragma unroll
-        for (int kk = 0; kk < kGemmK; kk += 2) {
-            const float a = As[buf][kk + lk][wr + li];
-            const float b0 = Bs[buf][kk + lk][wc + li];
-            const float b1 = Bs[buf][kk + lk][wc + 32 + li];
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b1, acc1, 0, 0, 0);
+            for (int i = 0; i < 8; ++i) a[i] = As[buf][kk][tr + i];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bb[q] = Bs[buf][kk][tm + q];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[i][q] = acc[i][q] + bb[q] * a[i];
         }
         if (c + 1 < nk) store(buf ^ 1);
         __syncthreads();
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int64_t mm = m0 + wc + h * 32 + li;
-        if (mm >= M) continue;
+    for (int i = 0; i < 8; ++i) {
+        const int64_t row = r0 + tr + i;
+        if (row >= R) continue;
+        double* p = Wt + (s_end + row) * M + m0 + tm;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t row = r0 + wr + (r >> 2) * 8 + lk * 4 + (r & 3);
-            if (row < R) {
-                float* p = Wt + (s_end + row) * M + mm;
-                *p = *p - (h ? acc1[r] : acc0[r]);
-            }
-        }
+        for (int q = 0; q < 4; ++q)
+            if (m0 + tm + q < M) p[q] = p[q] - acc[i][q];
     }
 }
 
@@ -473,46 +719,67 @@ __global__ __launch_bounds__(512) void k_block_gemm(float* __restrict__ Wt, cons
 size_t ws_vptq(int64_t M, int64_t N, int V)
 {
     const int64_t nv = M / V;
-    // three transposed M x N copies, three key buffers (kKeySlots slots each), two working columns,
-    // the prepared codebook (3 x 16 bytes per centroid, at most 65536), max |C|
-    return 3 * align_up((size_t)M * (size_t)N * sizeof(float)) + align_up((size_t)(3 * kKeySlots * nv) * sizeof(uint64_t)) +
-           align_up((size_t)(2 * M) * sizeof(float)) + 3 * align_up((size_t)65536 * sizeof(vp_h16x8)) +
-           align_up(sizeof(float));
+    const int64_t nrb = (nv + kStepRows - 1) / kStepRows;
+    const int64_t nch = (65536 + kAsgChunk - 1) / kAsgChunk;
+    // the float64 working matrix and errors, the float32 quantized matrix (all
+    // transposed), three key buffers (A and B keys, kKeySlots copies), two
+    // winner columns, the row-block arrival counters, two float64 working
+    // columns, the prepared codebook (3 x 16 bytes per centroid, at most
+    // 65536), max |C|, and the per-chunk winners of the exact searches; per
+    // row block an arrival counter; the count of exact searches
+    return 2 * align_up((size_t)M * (size_t)N * sizeof(double)) + align_up((size_t)M * (size_t)N * sizeof(float)) +
+           align_up((size_t)(3 * kKeySlots * 2 * nv) * sizeof(uint64_t)) + align_up((size_t)(2 * nv) * sizeof(int)) +
+           align_up((size_t)nrb * sizeof(int)) + align_up(sizeof(int)) +
+           align_up((size_t)(2 * M) * sizeof(double)) +
+           3 * align_up((size_t)65536 * sizeof(vp_h16x8)) + align_up(sizeof(float)) +
+           align_up((size_t)(nch * nv) * sizeof(double)) + align_up((size_t)(nch * nv) * sizeof(int));
 }
 
 vq_status vptq_launch(const float* W, const float* U, int64_t M, int64_t N, int V, const float* C, int K, int B,
                       uint16_t* idx, float* W_hat, float* E, void* ws, size_t ws_bytes, hipStream_t st)
 {
     const int64_t nv = M / V;
+    const int64_t nrb = (nv + kStepRows - 1) / kStepRows;
+    const int64_t nch_all = (65536 + kAsgChunk - 1) / kAsgChunk;
     Carver cv(ws, ws_bytes);
-    float* Wt = cv.take<float>((size_t)(M * N));
+    double* Wt = cv.take<double>((size_t)(M * N));
+    double* Et = cv.take<double>((size_t)(M * N));
     float* Wht = cv.take<float>((size_t)(M * N));
-    float* Et = cv.take<float>((size_t)(M * N));
-    unsigned long long* keys = cv.take<unsigned long long>((size_t)(3 * kKeySlots * nv));
-    float* Xc = cv.take<float>((size_t)(2 * M));
+    unsigned long long* keys = cv.take<unsigned long long>((size_t)(3 * kKeySlots * 2 * nv));
+    int* win = cv.take<int>((size_t)(2 * nv));
+    int* arrived = cv.take<int>((size_t)nrb);
+    int* fl_total = cv.take<int>(1);
+    double* Xc = cv.take<double>((size_t)(2 * M));
     const int Kp = (K + kVpChunk - 1) / kVpChunk * kVpChunk;
     vp_h16x8* Phi = cv.take<vp_h16x8>(65536);
     vp_h16x8* Plo = cv.take<vp_h16x8>(65536);
     vp_h16x8* Phn = cv.take<vp_h16x8>(65536);
     float* cmax = cv.take<float>(1);
+    double* part_d = cv.take<double>((size_t)(nch_all * nv));
+    int* part_i = cv.take<int>((size_t)(nch_all * nv));
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_vptq: workspace too small");
     TimedRegion tr("vptq", K, st);
     const dim3 tw(grid_for(N, kTr), grid_for(M, kTr));
-    hipLaunchKernelGGL(k_transpose, tw, dim3(256), 0, st, W, M, N, Wt);
-    VQ_LAUNCHED("k_transpose");
-    hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(3 * kKeySlots * nv, 256)), dim3(256), 0, st, keys,
-                       3 * kKeySlots * nv, ~0ull);
-    VQ_LAUNCHED("k_fill_u64");
+    hipLaunchKernelGGL(k_transpose_in, tw, dim3(256), 0, st, W, M, N, Wt);
+    VQ_LAUNCHED("k_transpose_in");
     const bool v8 = V == 8 && aligned16(C) && (M % 4 == 0);
     if (v8) {
+        hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(3 * kKeySlots * 2 * nv, 256)), dim3(256), 0, st, keys,
+                           3 * kKeySlots * 2 * nv, ~0ull);
+        VQ_LAUNCHED("k_fill_u64");
+        hipLaunchKernelGGL(k_fill_i32, dim3(grid_for(nrb, 256)), dim3(256), 0, st, arrived, nrb, 0);
+        VQ_LAUNCHED("k_fill_i32");
+        hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, st, fl_total, (int64_t)1, 0);
+        VQ_LAUNCHED("k_fill_i32");
         hipLaunchKernelGGL(k_vp_absmax, dim3(1), dim3(1024), 0, st, reinterpret_cast<const float4*>(C),
                            (int64_t)K * 2, cmax);
         VQ_LAUNCHED("k_vp_absmax");
         hipLaunchKernelGGL(k_vp_prep, dim3(grid_for(Kp, 256)), dim3(256), 0, st, C, K, Kp, cmax, Phi, Plo, Phn);
         VQ_LAUNCHED("k_vp_prep");
     }
-    const dim3 ga(grid_for(nv, kAsgThreads), grid_for(K, kAsgChunk));
-    const dim3 gm(grid_for(nv, 128), (unsigned)(Kp / kVpChunk));
+    const int nch = (K + kAsgChunk - 1) / kAsgChunk;
+    const dim3 ga(grid_for(nv, kAsgThreads), (unsigned)nch);
+    const dim3 gm((unsigned)nrb, (unsigned)(Kp / kVpChunk));
     for (int64_t s = 0; s < N; s += B) {
         const int64_t s_end = s + B < N ? s + B : N;
         if (v8) {
@@ -520,39 +787,48 @@ vq_status vptq_launch(const float* W, const float* U, int64_t M, int64_t N, int 
             // and one for the block's last column
             for (int64_t n = s; n < s_end; ++n) {
                 hipLaunchKernelGGL(k_col_step_h16, gm, dim3(256), 0, st, Wt, M, (int)nv, n, s, s_end, C, U, N, keys,
-                                   Xc, idx, Wht, Et, Phi, Plo, Phn, cmax, K);
+                                   win, Xc, idx, Wht, Et, Phi, Plo, Phn, cmax, K);
                 VQ_LAUNCHED("k_col_step_h16");
+                hipLaunchKernelGGL(k_col_exact, gm, dim3(256), 0, st, (int)nv, n, M, C, K, keys, cmax, Xc, part_d,
+                                   part_i, arrived, win, fl_total);
+                VQ_LAUNCHED("k_col_exact");
             }
             hipLaunchKernelGGL(k_col_last, dim3(grid_for(M, 256)), dim3(256), 0, st, M, (int)nv, s_end - 1, C, U, N,
-                               keys, Xc, idx, Wht, Et);
+                               win, Xc, idx, Wht, Et);
             VQ_LAUNCHED("k_col_last");
         } else {
             for (int64_t n = s; n < s_end; ++n) {
-                unsigned long long* kc = (n & 1) ? keys + nv : keys;
-                unsigned long long* kn = (n & 1) ? keys : keys + nv;
-                hipLaunchKernelGGL(k_col_assign, ga, dim3(kAsgThreads), 0, st, Wt + n * M, (int)nv, V, C, K, kc);
+                hipLaunchKernelGGL(k_col_assign, ga, dim3(kAsgThreads), 0, st, Wt + n * M, (int)nv, V, C, K, part_d,
+                                   part_i);
                 VQ_LAUNCHED("k_col_assign");
                 const int64_t rows = s_end - n - 1;
                 const dim3 gf(grid_for(M, kFinThreads),
                               (unsigned)(rows > 0 ? (rows + kFinRows - 1) / kFinRows : 1));
                 hipLaunchKernelGGL(k_col_finalize, gf, dim3(kFinThreads), 0, st, Wt, M, V, (int)nv, n, s_end, C, U,
-                                   N, kc, kn, idx, Wht, Et);
+                                   N, part_d, part_i, nch, idx, Wht, Et);
                 VQ_LAUNCHED("k_col_finalize");
             }
         }
         if (s_end < N) {
             TimedRegion tg("vptq_block_update", K, st);
-            const dim3 gg(grid_for(M, kGemmT), grid_for(N - s_end, kGemmT));
-            hipLaunchKernelGGL(k_block_gemm, gg, dim3(512), 0, st, Wt, U, Et, N, M, s, (int)(s_end - s), s_end);
+            const dim3 gg(grid_for(M, kGemmM), grid_for(N - s_end, kGemmR));
+            hipLaunchKernelGGL(k_block_gemm, gg, dim3(256), 0, st, Wt, U, Et, N, M, s, (int)(s_end - s), s_end);
             VQ_LAUNCHED("k_block_gemm");
         }
     }
     const dim3 tb(grid_for(M, kTr), grid_for(N, kTr));
-    hipLaunchKernelGGL(k_transpose, tb, dim3(256), 0, st, Wht, N, M, W_hat);
-    VQ_LAUNCHED("k_transpose");
+    hipLaunchKernelGGL(k_transpose_out<float>, tb, dim3(256), 0, st, Wht, N, M, W_hat);
+    VQ_LAUNCHED("k_transpose_out");
     if (E) {
-        hipLaunchKernelGGL(k_transpose, tb, dim3(256), 0, st, Et, N, M, E);
-        VQ_LAUNCHED("k_transpose");
+        hipLaunchKernelGGL(k_transpose_out<double>, tb, dim3(256), 0, st, Et, N, M, E);
+        VQ_LAUNCHED("k_transpose_out");
+    }
+    if (v8 && timing_on()) {
+        // diagnostics: how many decisions the exact search took
+        int n_exact = 0;
+        VQ_HIP(hipMemcpyAsync(&n_exact, fl_total, sizeof(int), hipMemcpyDeviceToHost, st));
+        VQ_HIP(hipStreamSynchronize(st));
+        timing_count("vptq_exact_searches", K, n_exact);
     }
     return VQ_OK;
 }

@@ -262,9 +262,7 @@ vq_status vq_hessian_factor(const float* H, int64_t N, double damp, float* U, vo
  * Core Algorithm", Algorithm 1).  Columns of W [M x N] are quantized left to
  * right in blocks of B: each of a column's M/V sub-vectors W[m:m+V, n] takes
  * its nearest row of C [K x V] under the plain Euclidean distance (the
- * lowest index among equal scores; V = 8 with C 16-byte aligned and M % 4 == 0:
- * expanded form |c|^2/2 - <c, x> on the fp16 matrix cores with split fp16
- * operands, error at float32 level; other V: direct form in float32); the column's error
+ * lowest index among equal distances); the column's error
  * E[:,n] = (W[:,n] - What[:,n]) / U[n,n] is subtracted, times U[n,j], from the
  * block's later columns j, and at the block's end E[:, s:s+B] U[s:s+B, s+B:]
  * is subtracted from every later column.  U [N x N] row-major is the matrix
@@ -272,11 +270,22 @@ vq_status vq_hessian_factor(const float* H, int64_t N, double damp, float* U, vo
  * read (GPTQ's upper Cholesky factor of the damped inverse Hessian, or the
  * inverse itself).  W is not modified.  Outputs: idx uint16 [N x M/V]
  * (idx[n*(M/V) + v] for sub-vector v of column n), W_hat [M x N] (codebook
- * rows), E [M x N] (nullable).  Arithmetic: float32 state; the block update
- * runs on the float32 matrix cores.  1 <= V <= 8 with M % V == 0;
- * 1 <= K <= 65536; 1 <= B <= 128.  Bitwise reproducible.  Workspace:
- * vq_vptq_workspace_bytes(M, N, V) (three transposed M x N copies, the
- * split codebook, per-column keys). */
+ * rows), E [M x N] (nullable; the float64 errors rounded to float32).
+ * Arithmetic: the working matrix and the errors are float64, each in-block
+ * update is taken as w - e*u (product rounded, then the difference) column
+ * after column, and the block's end update forms each sum of e*u over the
+ * block's columns in column order (each product rounded, then added) before
+ * subtracting it; every decision equals the exact float64 direct-form one
+ * (V = 8 with C 16-byte aligned and M % 4 == 0: the expanded form |c|^2/2 -
+ * <c, x> on the fp16 matrix cores with split operands, each winner certified
+ * against a rounding bound and the uncertified searched again in float64;
+ * otherwise the float64 direct form throughout).  The results are therefore
+ * those of the float64 algorithm as written, bit for bit.  1 <= V <= 8 with
+ * M % V == 0; 1 <= K <= 65536; 1 <= B <= 128.  Workspace:
+ * vq_vptq_workspace_bytes(M, N, V) (two float64 and one float32 transposed
+ * M x N matrices, the split codebook, per-column keys and chunk results).
+ * With timing on, the record "vptq_exact_searches" counts (as launches) the
+ * decisions that took the exact search. */
 size_t vq_vptq_workspace_bytes(int64_t M, int64_t N, int V);
 vq_status vq_vptq(const float* W, const float* U, int64_t M, int64_t N, int V, const float* C, int K, int B,
                   uint16_t* idx, float* W_hat, float* E, void* ws, size_t ws_bytes, void* stream);

@@ -4,8 +4,7 @@ against the oracle (GPU).
 Algorithm 1: 24 seeded draws of (M, N, V, K, B), V = 1..8 (the scalar and the
 vector path), K from 1 to 1500 (one to six 256-centroid chunks), B from 1 to
 128 and past N, compared with the oracle's trajectory at the fixed cases' bar
-(indices equal until a near-tie decision, codebook rows bit for bit, E within
-1e-4 of the column's scale, at most 1% of row groups parted).
+(indices, codebook rows and E identical).
 
 Factor: 12 seeded draws of (N, T, damp), T below N (singular X^T X carried by
 the damping) and above, N crossing the 128-column panels; U within 1e-5 of
@@ -51,9 +50,7 @@ def test_random_vptq_matches_oracle(seed):
     say("random vptq", seed, dict(M=M, N=N, V=V, K=K, B=B))
     W, U, C = make_case(300 + seed, M, N, V, K)
     idx, What, E = vq.vptq(dev(W), dev(U), V, dev(C), B, want_E=True)
-    nv, parted = compare(W, U, C, V, B, host(idx).reshape(N, M // V), host(What), host(E))
-    say("  groups parted: %d of %d" % (parted, nv))
-    assert parted <= max(1, nv // 100)
+    compare(W, U, C, V, B, host(idx).reshape(N, M // V), host(What), host(E))
 
 
 @pytest.mark.parametrize("seed", range(12))

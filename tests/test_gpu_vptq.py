@@ -1,28 +1,23 @@
 """Parity of Algorithm 1 (second-order error propagation, column sub-vectors)
 with the oracle (GPU).
 
-The oracle keeps the working matrix in float64, the library in float32, so the
-two trajectories agree until a decision whose best and second-best distances
-are within the float32 state's error of each other; after such a decision the
-two legitimately part for that row group (V rows share every later decision).
-The bar, per group of V rows and column by column:
-  * indices equal, until the first disagreement, which must sit on an oracle
-    decision with relative margin (second - best) / second < 1e-3 (float32
-    state error is about 1e-5 relative), or where the library's pick c_g is
-    within the float32 state's reach of the oracle's c_o: with w the
-    oracle's working sub-vector, (|w - c_g|^2 - |w - c_o|^2) /
-    (2 |w| |c_g - c_o|) < 1e-4 (a shift of w by that fraction of |w| flips
-    the decision; fine codebooks, V = 1 with a thousand centroids, have
-    distance margins far below 1e-3 that are still this far apart in w); the
-    group is not compared after it;
-  * on every column compared: What equal bit for bit (codebook rows) and
-    |E - E_ref| <= 1e-4 * max(max |E_ref[:, n]|, max |W_n| / U_nn) + 1e-30,
-    W_n the working column the error is taken from (W_n = What_n + U_nn E_n).
-At most 1% of groups may part.  Cases cover V = 8 (vector path) and V = 4, 6
-(scalar path), K below, at and across 256-centroid chunks, K = 1, blocks that
-do not divide N, B > N, B = 1, U = I, an unaligned codebook (direct form for
-V = 8), working values 1e-6 and 1e4 times the codebook's scale, an all-zero
-codebook, and the 4096 x 11008 workload on eight sampled row groups.
+The library keeps the working matrix and the errors in float64 and takes
+every update in the oracle's order and rounding (VPTQ page, "The Core
+Algorithm", Algorithm 1: the in-block update column by column, the block's
+end update as one sum over the block's columns), and every nearest-row
+decision equals the exact float64 direct-form one (the matrix-core search
+certifies its winner against a rounding bound; the rest is searched again
+exactly).  So the whole trajectory equals the oracle's bit for bit:
+  * indices equal everywhere, with no parting;
+  * What equal bit for bit (codebook rows);
+  * E (float64 inside, returned as float32) equal to the oracle's float64 E
+    rounded to float32, bit for bit.
+Cases cover V = 8 (matrix-core path) and V = 4, 6 (vector path), K below, at
+and across 256- and 512-centroid chunks, K = 1, blocks that do not divide N,
+B > N, B = 1, U = I, an unaligned codebook (direct form for V = 8), working
+values 1e-6 and 1e4 times the codebook's scale, an all-zero codebook (every
+decision a tie, all of them searched again exactly), and the 4096 x 11008
+workload on 32 sampled row groups.
 """
 import sys
 
@@ -35,9 +30,6 @@ from gpu_util import dev, host
 from hessian_weighted_vector_amd import configs, synth, vq
 
 pytestmark = pytest.mark.gpu
-
-GAP_TOL = 1e-3
-REACH_TOL = 1e-4
 
 
 def say(*a):
@@ -59,48 +51,19 @@ def make_case(seed, M, N, V, K, T=64, eye=False):
     return W, U, C
 
 
-def pick_reach(What_n, E_n, unn, c_o, c_g):
-    """How far (relative to |w|) the working sub-vector w = What_n + U_nn E_n
-    must move for c_g to be as near as c_o: (|w - c_g|^2 - |w - c_o|^2) /
-    (2 |w| |c_g - c_o|)."""
-    w = What_n.astype(np.float64) + E_n * np.float64(unn)
-    c_o, c_g = c_o.astype(np.float64), c_g.astype(np.float64)
-    gap = ((w - c_g) ** 2).sum() - ((w - c_o) ** 2).sum()
-    return gap / (2.0 * np.linalg.norm(w) * np.linalg.norm(c_g - c_o) + 1e-300)
-
-
 def compare(W, U, C, V, B, idx_g, What_g, E_g, rows=None):
-    """Walks each row group against the oracle run on the same rows; returns
-    (groups compared, groups parted)."""
+    """The GPU trajectory against the oracle run on the same rows (groups of V
+    rows evolve independently given U and C): indices, What and E (rounded to
+    float32) identical.  Returns the number of row groups compared."""
     Wr = W if rows is None else W[rows]
-    idx_o, What_o, E_o, gap_o = oracle.vptq(Wr, U, V, C, B)
-    M, N = Wr.shape
-    nv = M // V
-    parted = 0
-    for v in range(nv):
-        rs = slice(v * V, v * V + V)
-        diff = np.nonzero(idx_g[:, v] != idx_o[:, v])[0]
-        upto = N
-        if diff.size:
-            n0 = int(diff[0])
-            reach = pick_reach(What_o[rs, n0], E_o[rs, n0], U[n0, n0], C[idx_o[n0, v]], C[idx_g[n0, v]])
-            assert gap_o[n0, v] < GAP_TOL or reach < REACH_TOL, (
-                "group %d parts at column %d with margin %.3g, reach %.3g" % (v, n0, gap_o[n0, v], reach))
-            parted += 1
-            upto = n0
-        if upto == 0:
-            continue
-        assert np.array_equal(What_g[rs, :upto].view(np.uint32), What_o[rs, :upto].view(np.uint32))
-        if E_g is not None:
-            # E[:, n] = (W_n - What_n) / U_nn comes from the float32 working column
-            # W_n, so its rounding error scales with max |W_n| / U_nn, which can be
-            # far above max |E[:, n]| when the codebook is fine (V = 1, large K)
-            unn = np.diag(U).astype(np.float64)[None, :upto]
-            work = np.abs(What_o[:, :upto].astype(np.float64) / unn + E_o[:, :upto]).max(axis=0)
-            scale = np.maximum(np.abs(E_o[:, :upto]).max(axis=0), work)
-            err = np.abs(E_g[rs, :upto].astype(np.float64) - E_o[rs, :upto])
-            assert np.all(err <= 1e-4 * scale[None, :] + 1e-30), float((err / (scale + 1e-30)).max())
-    return nv, parted
+    idx_o, What_o, E_o, _ = oracle.vptq(Wr, U, V, C, B)
+    bad = np.argwhere(idx_g != idx_o)
+    assert bad.size == 0, ("index differs at (column, group)", bad[:10])
+    assert np.array_equal(What_g.view(np.uint32), What_o.view(np.uint32))
+    if E_g is not None:
+        assert np.array_equal(E_g.view(np.uint32), E_o.astype(np.float32).view(np.uint32)), \
+            float(np.abs(E_g.astype(np.float64) - E_o).max())
+    return Wr.shape[0] // V
 
 
 CASES = [
@@ -120,9 +83,7 @@ def test_vptq_matches_oracle(case):
     say("vptq", case)
     W, U, C = make_case(seed, M, N, V, K)
     idx, What, E = vq.vptq(dev(W), dev(U), V, dev(C), B, want_E=True)
-    nv, parted = compare(W, U, C, V, B, host(idx).reshape(N, M // V), host(What), host(E))
-    say("  groups parted: %d of %d" % (parted, nv))
-    assert parted <= max(1, nv // 100)
+    compare(W, U, C, V, B, host(idx).reshape(N, M // V), host(What), host(E))
 
 
 def test_vptq_identity_is_plain_column_vq():
@@ -131,8 +92,7 @@ def test_vptq_identity_is_plain_column_vq():
     say("vptq U = I")
     W, U, C = make_case(7, 48, 33, 8, 50, eye=True)
     idx, What, E = vq.vptq(dev(W), dev(U), 8, dev(C), 10, want_E=True)
-    nv, parted = compare(W, U, C, 8, 10, host(idx).reshape(33, 6), host(What), host(E))
-    assert parted == 0
+    compare(W, U, C, 8, 10, host(idx).reshape(33, 6), host(What), host(E))
     assert np.array_equal(host(E), W - host(What))
 
 
@@ -155,24 +115,20 @@ def test_vptq_unaligned_codebook_takes_the_direct_form():
     Cu.copy_(torch.from_numpy(C))
     assert Cu.data_ptr() % 16 != 0
     idx, What, E = vq.vptq(dev(W), dev(U), 8, Cu, 16, want_E=True)
-    nv, parted = compare(W, U, C, 8, 16, host(idx).reshape(70, 6), host(What), host(E))
-    assert parted <= 1
+    compare(W, U, C, 8, 16, host(idx).reshape(70, 6), host(What), host(E))
 
 
 @pytest.mark.parametrize("wscale", [1e-6, 1e4])
 def test_vptq_scale_extremes(wscale):
     """Working values far below or far above the codebook's scale: the
     per-wavefront power-of-two scale is clamped (tiny columns) or the norm
-    term's factor shrinks (huge columns); the oracle is met either way."""
+    term's factor shrinks (huge columns, where the decisions sit at relative
+    distance margins near 1e-7 and most go to the exact search); the oracle
+    is met bit for bit either way."""
     say("vptq scale", wscale)
     W, U, C = make_case(10, 64, 40, 8, 200)
     idx, What, E = vq.vptq(dev(W * np.float32(wscale)), dev(U), 8, dev(C), 8, want_E=True)
-    nv, parted = compare(W * np.float32(wscale), U, C, 8, 8, host(idx).reshape(40, 8), host(What), host(E))
-    say("  groups parted: %d of %d" % (parted, nv))
-    if wscale < 1:
-        assert parted <= 1
-    # at 1e4 the distances are about |x|^2 and the decisions sit at relative
-    # margins near 1e-7 (float32 ties); compare() has checked every parting
+    compare(W * np.float32(wscale), U, C, 8, 8, host(idx).reshape(40, 8), host(What), host(E))
 
 
 def test_vptq_zero_codebook():
@@ -183,13 +139,12 @@ def test_vptq_zero_codebook():
     idx, What, E = vq.vptq(dev(W), dev(U), 8, dev(C), 8, want_E=True)
     assert not host(idx).any()
     assert not host(What).any()
-    nv, parted = compare(W, U, C, 8, 8, host(idx).reshape(24, 4), host(What), host(E))
-    assert parted == 0
+    compare(W, U, C, 8, 8, host(idx).reshape(24, 4), host(What), host(E))
 
 
 def test_vptq_fullsize_sampled_rows():
     """4096 x 11008 with K = 65536, V = 8, B = 128, H = X^T X of the workload's
-    activations, GPTQ's U; eight row groups (64 rows) against the oracle run on
+    activations, GPTQ's U; 32 row groups (256 rows) against the oracle run on
     those rows (groups of V rows evolve independently given U and C)."""
     cfg = configs.get(4)
     M, N, V, K, B = cfg.M, cfg.N, 8, cfg.K1, 128
@@ -204,12 +159,10 @@ def test_vptq_fullsize_sampled_rows():
     say("vptq full size: GPU")
     idx, What, E = vq.vptq(dev(W), dev(U), V, dev(C), B, want_E=True)
     idx, What, E = host(idx).reshape(N, M // V), host(What), host(E)
-    groups = np.sort(g.choice(M // V, 8, replace=False))
+    groups = np.sort(g.choice(M // V, 32, replace=False))
     rows = np.concatenate([np.arange(q * V, q * V + V) for q in groups])
     say("vptq full size: oracle on groups", groups)
-    nv, parted = compare(W, U, C, V, B, idx[:, groups], What[rows], E[rows], rows=rows)
-    say("  groups parted: %d of %d" % (parted, nv))
-    assert parted <= 1
+    compare(W, U, C, V, B, idx[:, groups], What[rows], E[rows], rows=rows)
 
 
 @pytest.mark.parametrize("N,T,damp", [(1, 4, 0.01), (5, 3, 0.01), (33, 40, 0.01), (64, 20, 0.1), (100, 300, 0.01),
