@@ -184,50 +184,79 @@ __global__ void k_decode(int64_t n_sub, int64_t nb, int d, const float* __restri
     }
 }
 
-// d == 8 with 16-byte aligned buffers: one thread per half sub-vector,
-// 16-byte loads and stores, same operation order as k_decode.  Workgroups are
-// laid out by row (bpr workgroups per row), so the row and its scale come
-// from the workgroup number.
-__global__ __launch_bounds__(kBlock) void k_decode8(int64_t nb, unsigned bpr, const float4* __restrict__ C1, int K1,
-                                                    const uint16_t* __restrict__ idx1, const float4* __restrict__ C2,
-                                                    int K2, const uint16_t* __restrict__ idx2,
-                                                    const float* __restrict__ rs, const float4* __restrict__ cs,
-                                                    float4* __restrict__ Wh)
-{
-    const int64_t i = blockIdx.x / bpr;
-    const int64_t hq = (int64_t)(blockIdx.x - (unsigned)i * bpr) * kBlock + threadIdx.x;
-    if (hq >= 2 * nb) return;
-    const int64_t b = hq >> 1;
-    const int half = (int)(hq & 1);
-    const int64_t s = i * nb + b;
-    const int64_t q = i * 2 * nb + hq;
-    const int k1 = idx1[s];
-    const int k2 = C2 ? idx2[s] : 0;
-    float4 v;
-    if (k1 >= K1 || (C2 && k2 >= K2)) {
-        v.x = v.y = v.z = v.w = __builtin_nanf("");
-        Wh[q] = v;
-        return;
-    }
-    v = C1[(size_t)k1 * 2 + half];
-    if (C2) {
-        const float4 c = C2[(size_t)k2 * 2 + half];
-        v.x = v.x + c.x; v.y = v.y + c.y; v.z = v.z + c.z; v.w = v.w + c.w;
-    }
-    if (cs) {
-        const float4 c = cs[b * 2 + half];
-        v.x = v.x * c.x; v.y = v.y * c.y; v.z = v.z * c.z; v.w = v.w * c.w;
-    }
-    if (rs) {
-        const float ri = rs[i];
-        v.x = v.x * ri; v.y = v.y * ri; v.z = v.z * ri; v.w = v.w * ri;
-    }
-    Wh[q] = v;
-}
-
 // The exact salient values overwrite their positions (HAS-VQ abstract:
 // exact reconstruction of the decoupled weights).  One workgroup per row;
 // its threads stride over the row's CSR entries.
+// d == 8 with 16-byte aligned buffers: 16-byte loads and stores, same
+// operation order as k_decode.  Workgroups are laid out by row (bpr
+// workgroups per row), so the row and its scale come from the workgroup
+// number.  U half sub-vectors per thread: thread t of the
+// workgroup takes halves t, t + kBlock, ..., of its slice of a row, so each
+// of the U steps is a coalesced pass.  All indices and column scales are
+// requested first, then all U first-stage centroid halves, so U gathers are
+// in flight per lane instead of one.  With C2L the residual codebook (at most
+// kC2Lds centroids) is staged in LDS once per workgroup and read from there.
+// Same arithmetic and operation order as k_decode8.
+constexpr int kC2Lds = 512;
+
+template <int U, bool C2L>
+__global__ __launch_bounds__(kBlock) void k_decode8u(int64_t nb, unsigned bpr, const float4* __restrict__ C1, int K1,
+                                                     const uint16_t* __restrict__ idx1, const float4* __restrict__ C2,
+                                                     int K2, const uint16_t* __restrict__ idx2,
+                                                     const float* __restrict__ rs, const float4* __restrict__ cs,
+                                                     float4* __restrict__ Wh)
+{
+    __shared__ float4 sC2[C2L ? 2 * kC2Lds : 1];
+    if (C2L) {
+        for (int q = threadIdx.x; q < 2 * K2; q += kBlock) sC2[q] = C2[q];
+        __syncthreads();
+    }
+    const int64_t i = blockIdx.x / bpr;
+    const int64_t base = (int64_t)(blockIdx.x - (unsigned)i * bpr) * (kBlock * U) + threadIdx.x;
+    const float ri = rs ? rs[i] : 1.0f;
+    int k1[U], k2[U];
+    float4 cv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t hq = base + (int64_t)u * kBlock;
+        const bool ok = hq < 2 * nb;
+        const int64_t s = i * nb + (hq >> 1);
+        k1[u] = ok ? (int)idx1[s] : 0;
+        k2[u] = (ok && C2) ? (int)idx2[s] : 0;
+        if (cs && ok) cv[u] = cs[hq];
+    }
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int half = (int)((base + (int64_t)u * kBlock) & 1);
+        const int kk = k1[u] < K1 ? k1[u] : 0;
+        v[u] = C1[(size_t)kk * 2 + half];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t hq = base + (int64_t)u * kBlock;
+        if (hq >= 2 * nb) continue;
+        const int half = (int)(hq & 1);
+        float4 w = v[u];
+        if (k1[u] >= K1 || (C2 && k2[u] >= K2)) {
+            w.x = w.y = w.z = w.w = __builtin_nanf("");
+        } else {
+            if (C2) {
+                const float4 c = C2L ? sC2[k2[u] * 2 + half] : C2[(size_t)k2[u] * 2 + half];
+                w.x = w.x + c.x; w.y = w.y + c.y; w.z = w.z + c.z; w.w = w.w + c.w;
+            }
+            if (cs) {
+                const float4 c = cv[u];
+                w.x = w.x * c.x; w.y = w.y * c.y; w.z = w.z * c.z; w.w = w.w * c.w;
+            }
+            if (rs) {
+                w.x = w.x * ri; w.y = w.y * ri; w.z = w.z * ri; w.w = w.w * ri;
+            }
+        }
+        Wh[i * 2 * nb + hq] = w;
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void k_sparse_overwrite(int64_t N, const int32_t* __restrict__ row_ptr,
                                                              const int32_t* __restrict__ col,
                                                              const float* __restrict__ val, float* __restrict__ Wh)
@@ -374,12 +403,21 @@ vq_status reconstruct_launch(int64_t M, int64_t N, int d, const float* C1, int K
 {
     const int64_t n_sub = M * N / d;
     TimedRegion tr("reconstruct", K1, st);
-    const int64_t bpr = (2 * (N / d) + kBlock - 1) / kBlock;   // workgroups per row in k_decode8
+    constexpr int kU = 4;                                        // halves per thread in k_decode8u
+    const int64_t bpr = (2 * (N / d) + kBlock * kU - 1) / (kBlock * kU);   // workgroups per row
     if (d == 8 && aligned16(C1) && aligned16(C2) && aligned16(cs) && aligned16(Wh) && M * bpr <= (int64_t)UINT32_MAX) {
-        hipLaunchKernelGGL(k_decode8, dim3((unsigned)(M * bpr)), dim3(kBlock), 0, st, N / d, (unsigned)bpr,
-                           reinterpret_cast<const float4*>(C1), K1, idx1, reinterpret_cast<const float4*>(C2),
-                           K2, idx2, rs, reinterpret_cast<const float4*>(cs), reinterpret_cast<float4*>(Wh));
-        VQ_LAUNCHED("k_decode8");
+        const float4* c1 = reinterpret_cast<const float4*>(C1);
+        const float4* c2 = reinterpret_cast<const float4*>(C2);
+        const float4* c4 = reinterpret_cast<const float4*>(cs);
+        float4* w4 = reinterpret_cast<float4*>(Wh);
+        if (C2 && K2 <= kC2Lds) {
+            hipLaunchKernelGGL((k_decode8u<kU, true>), dim3((unsigned)(M * bpr)), dim3(kBlock), 0, st, N / d,
+                               (unsigned)bpr, c1, K1, idx1, c2, K2, idx2, rs, c4, w4);
+        } else {
+            hipLaunchKernelGGL((k_decode8u<kU, false>), dim3((unsigned)(M * bpr)), dim3(kBlock), 0, st, N / d,
+                               (unsigned)bpr, c1, K1, idx1, c2, K2, idx2, rs, c4, w4);
+        }
+        VQ_LAUNCHED("k_decode8u");
     } else {
         hipLaunchKernelGGL(k_decode, dim3(grid_for(n_sub, kBlock)), dim3(kBlock), 0, st, n_sub, N / d, d,
                            C1, K1, idx1, C2, K2, idx2, rs, cs, Wh);
