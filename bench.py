@@ -52,10 +52,9 @@ def algorithmic_bytes_reconstruct(n_sub, M, N, d, K1, K2, nnz, binorm):
     return b
 
 
-def traffic_from_profile(kernel_src):
-    """HBM bytes per launch of the 4096 x 11008 workload's stage-1 search from the
-    committed counter summary, if it was taken on the current kernel source (else
-    None)."""
+def search_profile(kernel_src):
+    """The committed counter summary of the 4096 x 11008 workload's stage-1 search,
+    if it was taken on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", "assign_search_c4_pmc.json")
     if not os.path.exists(path):
         return None
@@ -63,9 +62,7 @@ def traffic_from_profile(kernel_src):
         prof = json.load(f)
     with open(kernel_src, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
-    if prof.get("kernel_src_sha256") != sha:
-        return None
-    return prof.get("hbm_bytes_per_launch")
+    return prof if prof.get("kernel_src_sha256") == sha else None
 
 
 def row_table(cfg, recs, nnz, oracle_ms):
@@ -668,13 +665,19 @@ def main():
     flops = 32.0 * n_sub * cfg.K1
     achieved = flops / (avg_s1 * 1e-3) / 1e12
     src = os.path.join(ROOT, "hessian_weighted_vector_amd", "csrc", "vq_assign.hip")
+    prof = search_profile(src) if cfg.cid == 4 else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP16_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_MFMA_TFLOPS, 4),
-                "traffic": traffic_from_profile(src) if cfg.cid == 4 else None}
+                "traffic": prof.get("hbm_bytes_per_launch") if prof else None}
 
     extra = {"assign_stage1_ms": round(avg_s1, 3),
              "assign_stage1_Gsub_per_s": round(n_sub / (avg_s1 * 1e-3) / 1e9, 5),
              "assign_stage1_fp32_equivalent_vs_fp32_peak": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4)}
+    if prof:
+        # executed matrix-core work from the counters (nominal = 32 flop per pair)
+        ratio = prof["executed_mfma_flops_per_launch"] / prof["algorithmic_flops_per_launch"]
+        extra["assign_stage1_executed_to_nominal_flops"] = round(ratio, 4)
+        extra["assign_stage1_executed_frac_fp16_mfma"] = round(achieved * ratio / PEAK_FP16_MFMA_TFLOPS, 4)
     if ("assign", cfg.K1) in rec:
         a = rec[("assign", cfg.K1)]
         extra["assign_stage1_with_exact_ms"] = round(a[3] / a[2], 3)
