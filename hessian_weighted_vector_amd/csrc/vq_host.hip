@@ -406,7 +406,10 @@ size_t ws_steps(int64_t M, int64_t N, int d, int K1, int K2)
     const int64_t n_sub = M * N / d;
     const int Kmax = std::max(K1, K2);
     size_t w = ws_assign(n_sub, Kmax);
-    w = std::max(w, ws_update_total(n_sub, Kmax));
+    // the update's needs are not monotone in K (a short codebook takes more
+    // pieces, a long one the bucket arrays): both stages' sizes
+    w = std::max(w, ws_update_total(n_sub, K1));
+    w = std::max(w, ws_update_total(n_sub, K2));
     w = std::max(w, ws_select(M, N));
     w = std::max(w, ws_binorm(M, N));
     w = std::max(w, ws_init(n_sub, Kmax, d));
