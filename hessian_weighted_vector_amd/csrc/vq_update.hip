@@ -13,11 +13,13 @@
 //      (exact) and tile offsets come from a scan.  With K <= 256 the whole
 //      matrix is one bucket of up to 256 centroids, read in place;
 //   2. each bucket is cut into fixed pieces; a workgroup streams its piece
-//      through LDS in sub-chunks of 1024 records, stages each record's x,
-//      its column weights (zero where masked) and its row weight, counting-
-//      sorts the sub-chunk by centroid (stable), and 8-lane groups that own
-//      fixed centroids add their members in order into float64 sums of
-//      omega*x and omega kept in registers.  A bucket that fits one piece
+//      through LDS in sub-chunks of 1024 records (the next sub-chunk's loads
+//      in flight meanwhile), stages each record's x, its column weights
+//      (zero where masked) and its row weight, counting-sorts the sub-chunk
+//      by centroid (stable), and the lanes that own a centroid (a few
+//      dimensions each) add its members in order into float64 sums of
+//      omega*x and omega kept in registers, each product and sum rounded on
+//      its own as in a plain sequential loop.  A bucket that fits one piece
 //      is finished there (members in ascending sub-vector order, the order
 //      of a plain sequential sum);
 //   3. buckets with several pieces: one pass adds the pieces' partial sums
@@ -33,8 +35,8 @@ constexpr int kTile = 2048;          // records per scatter tile
 constexpr int kTileThreads = 1024;   // two records per thread
 constexpr int kMaxBuckets = 512;     // K <= 65536, 128 centroids per bucket
 constexpr int kBucketShift = 7;
-constexpr int kSub = 1024;           // records per LDS sub-chunk (one per thread)
-constexpr int kRedThreads = 1024;
+constexpr int kSub = 1024;           // records per LDS sub-chunk
+constexpr int kRedThreads = 512;     // two records per thread
 constexpr int kPieceMax = 32768;     // records per piece in bucket mode
 constexpr int kDirectPieces = 512;   // target piece count with one bucket
 
@@ -141,10 +143,11 @@ __global__ __launch_bounds__(64) void k_piece_setup(const int* __restrict__ tota
 __device__ inline int wave_peer_rank(int key, bool valid, int bits, unsigned long long lt_mask,
                                      unsigned long long& peers)
 {
-    peers = __ballot(valid);
+    peers = __ballot(valid);   // invalid lanes drop out here; their key bits do not matter
     for (int bit = 0; bit < bits; ++bit) {
-        const unsigned long long bal = __ballot(valid && ((key >> bit) & 1));
-        peers &= ((key >> bit) & 1) ? bal : ~bal;
+        const int m = -((key >> bit) & 1);                       // 0 or all ones
+        const unsigned long long bal = __ballot(m != 0);
+        peers &= ~(bal ^ (unsigned long long)(long long)m);      // lanes whose bit equals this lane's
     }
     return __popcll(peers & lt_mask);
 }
@@ -275,30 +278,52 @@ __global__ __launch_bounds__(kTileThreads) void k_bucket_scatter(
     }
 }
 
-// One workgroup per piece.  The piece goes through LDS in sub-chunks of
-// kSub records, one per thread: the thread stages the record's x, its
-// column weights hcol (zero where the mask bit is set) and its row weight
-// rho, and ranks it by centroid within the sub-chunk (stable counting
-// sort).  Then 8-lane group g (lane t = dimension t) walks the members of
-// its centroids (g, and g + 128 when a bucket spans 256 centroids) in record
-// order, adding omega_t x_t and omega_t (omega = hcol * rho in float64, the
-// product of two floats, exact) into float64 sums kept in registers.
-// rx == nullptr: one bucket of up to 256 centroids read in place from X,
-// idx and mask.
-__global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_piece_reduce(
+// Adds one member's term of one dimension into float64 sums in the oracle's
+// operation order: omega = hcol * rho (the product of two floats, exact in
+// float64), then num + omega * x and den + omega, each rounded on its own
+// (no fused multiply-add).
+__device__ inline void add_term(double& num, double& den, float h, float x, double rd)
+{
+#pragma clang fp contract(off)
+    const double w = (double)h * rd;
+    num = num + w * (double)x;
+    den = den + w;
+}
+
+// One workgroup per piece; the piece goes through LDS in sub-chunks of kSub
+// records, kPer per thread (record r = u * kRedThreads + tid).  Each thread
+// stages its records' x, column weights hcol (zero where the mask bit is
+// set) and row weight rho, and ranks them by centroid among the records of
+// its wavefront in the same pass u (ballots: stable).  Per-key counts of the
+// kSegs (pass, wavefront) segments, taken in record order, give a stable
+// counting sort of the sub-chunk.  Then the owner lanes walk their
+// centroid's members in record order, lane = (centroid, part of the
+// dimensions): W = 256 (one bucket read in place from X, idx and mask), two
+// lanes per centroid, four dimensions each; W = 128 (scattered buckets
+// rx/rw), four lanes per centroid, two dimensions each.
+// Sums stay in registers across the piece.
+constexpr int kPer = kSub / kRedThreads;
+constexpr int kSegs = kPer * (kRedThreads / 64);
+
+template <int W>
+__global__ __launch_bounds__(kRedThreads) void k_piece_reduce(
     const float* __restrict__ rx, const uint64_t* __restrict__ rw, const float* __restrict__ X,
     const uint16_t* __restrict__ idx, const uint8_t* __restrict__ mask, const float* __restrict__ hcol,
     const float* __restrict__ rho, uint32_t nb, int d, int K, int nbk, int piece,
     const int64_t* __restrict__ bstart, const int* __restrict__ poff, float* __restrict__ C,
     int32_t* __restrict__ counts, double* __restrict__ partial)
 {
+    constexpr bool kDirect = (W == 256);
+    constexpr int KB = kDirect ? 8 : 7;            // key bits
+    constexpr int DP = 8 * W / kRedThreads;        // dimensions per owner lane
+    static_assert(DP == 4 || DP == 2, "owner layout");
     __shared__ __align__(16) float sx[kSub * 8];
-    __shared__ __align__(16) float shv[kSub * 8];
+    __shared__ __align__(16) float sh[kSub * 8];
     __shared__ float srho[kSub];
     __shared__ uint16_t perm[kSub];
-    __shared__ uint16_t wcnt[kRedThreads / 64][256];
-    __shared__ uint16_t cstart[257];
-    __shared__ int ccount[256];
+    __shared__ __align__(16) uint16_t scnt[kSegs][W];
+    __shared__ int cstart[W + 1];
+    __shared__ int wsum[kRedThreads / 64];
 
     const int j = blockIdx.x;
     if (j >= poff[nbk]) return;
@@ -311,9 +336,6 @@ __global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(8, 
         }
         bk = lo;
     }
-    const bool direct = (rx == nullptr);
-    const int width = direct ? 256 : 128;     // centroids per bucket
-    const int kbits = direct ? 8 : 7;
     const int q = j - poff[bk];
     const int npieces = poff[bk + 1] - poff[bk];
     const int64_t p0 = bstart[bk] + (int64_t)q * piece;
@@ -322,186 +344,270 @@ __global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(8, 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int t = tid & 7;
-    const int g = tid >> 3;            // 128 groups
     const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const bool vx = (d == 8) && ((reinterpret_cast<uintptr_t>(direct ? X : rx) & 15) == 0);
+    const bool vx = (d == 8) && ((reinterpret_cast<uintptr_t>(kDirect ? X : rx) & 15) == 0);
     const bool vh = (d == 8) && ((reinterpret_cast<uintptr_t>(hcol) & 15) == 0);
-    double num[2] = {0.0, 0.0}, den[2] = {0.0, 0.0};
-    int count[2] = {0, 0};
+    const int oc = tid % W;                 // owned centroid within the bucket
+    const int oq = tid / W;                 // owned dimension part (W = 128)
+    double num[DP], den[DP];
+#pragma unroll
+    for (int t = 0; t < DP; ++t) { num[t] = 0.0; den[t] = 0.0; }
+    int count = 0;
 
-    // Raw fields of record tid of a sub-chunk (the next one is loaded while
-    // the current one is reduced).
-    auto load_raw = [&](int64_t c0, bool& valid, int& key, uint32_t& sv, uint32_t& mk, float4& xa, float4& xb) {
-        const int m = (int)min((int64_t)kSub, p1 - c0);
-        valid = c0 < p1 && tid < m;
-        key = 0; sv = 0; mk = 0;
-        xa = make_float4(0.f, 0.f, 0.f, 0.f);
-        xb = xa;
-        if (!valid) return;
-        const int64_t e = c0 + tid;
-        if (direct) {
-            sv = (uint32_t)e;
-            mk = mask ? mask[e] : 0u;
-            key = idx[e] & 255;
-        } else {
-            const uint64_t wd = rw[e];
-            sv = (uint32_t)wd;
-            key = (int)((wd >> 32) & 127);
-            mk = (uint32_t)((wd >> 40) & 255);
-        }
-        const float* xs = direct ? X + e * d : rx + e * d;
-        if (vx) {
-            xa = reinterpret_cast<const float4*>(xs)[0];
-            xb = reinterpret_cast<const float4*>(xs)[1];
+    // Raw fields of record u * kRedThreads + tid of the sub-chunk at c0.  The
+    // loads of the next sub-chunk stay in flight across the sums of the
+    // current one: nothing reads their registers (no masking, shifting or
+    // selecting) until that sub-chunk is staged.
+    struct Raw {
+        float4 xa, xb, ha, hb;
+        float rv;
+        uint64_t wd;        // scattered record word (W = 128)
+        uint32_t sv, kraw, mk;
+        bool valid;
+    };
+    // Row and column block of sub-vector sv: the quotient by nb from a float64
+    // reciprocal (off by at most one for sv < 2^32), then corrected exactly.
+    const double rnb = 1.0 / (double)nb;
+    auto load_weights = [&](Raw& R) {
+        uint32_t i = (uint32_t)((double)R.sv * rnb);
+        int64_t rem = (int64_t)R.sv - (int64_t)i * nb;
+        if (rem < 0) { --i; rem += nb; }
+        else if (rem >= (int64_t)nb) { ++i; rem -= nb; }
+        const uint32_t b = (uint32_t)rem;
+        const float* hs = hcol + (size_t)b * d;
+        if (vh) {
+            R.ha = reinterpret_cast<const float4*>(hs)[0];
+            R.hb = reinterpret_cast<const float4*>(hs)[1];
         } else {
             float tmp[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) tmp[u] = u < d ? xs[u] : 0.0f;
-            xa = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
-            xb = make_float4(tmp[4], tmp[5], tmp[6], tmp[7]);
+            for (int t = 0; t < 8; ++t) tmp[t] = t < d ? hs[t] : 0.0f;
+            R.ha = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
+            R.hb = make_float4(tmp[4], tmp[5], tmp[6], tmp[7]);
         }
+        if (rho) R.rv = rho[i];
     };
-    bool valid;
-    int key;
-    uint32_t sv, mk;
-    float4 xa, xb;
-    load_raw(p0, valid, key, sv, mk, xa, xb);
+    auto load_raw = [&](int64_t c0, int u, Raw& R) {
+        const int64_t e = c0 + (int64_t)u * kRedThreads + tid;
+        R.valid = e < p1;
+        R.sv = 0; R.kraw = 0; R.mk = 0; R.wd = 0;
+        R.xa = make_float4(0.f, 0.f, 0.f, 0.f);
+        R.xb = R.xa;
+        R.ha = R.xa;
+        R.hb = R.xa;
+        R.rv = 1.0f;
+        if (!R.valid) return;
+        if (kDirect) {
+            R.sv = (uint32_t)e;
+            if (mask) R.mk = mask[e];
+            R.kraw = idx[e];
+        } else {
+            R.wd = rw[e];
+        }
+        const float* xs = (kDirect ? X : rx) + e * d;
+        if (vx) {
+            R.xa = reinterpret_cast<const float4*>(xs)[0];
+            R.xb = reinterpret_cast<const float4*>(xs)[1];
+        } else {
+            float tmp[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) tmp[t] = t < d ? xs[t] : 0.0f;
+            R.xa = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
+            R.xb = make_float4(tmp[4], tmp[5], tmp[6], tmp[7]);
+        }
+        if (kDirect) load_weights(R);   // the id is known before the record arrives
+    };
+    Raw cur[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) load_raw(p0, u, cur[u]);
 
     for (int64_t c0 = p0; c0 < p1; c0 += kSub) {
-        // ---- stage record tid: x now, weights requested (used after the ranking) ----
-        const int r = tid;
-        float4 ha = make_float4(0.f, 0.f, 0.f, 0.f), hb = ha;
-        float rhov = 1.0f;
-        if (valid) {
-            const uint32_t i = sv / nb;
-            const uint32_t b = sv - i * nb;
-            if (rho) rhov = rho[i];
-            const float* hs = hcol + (size_t)b * d;
-            if (vh) {
-                ha = reinterpret_cast<const float4*>(hs)[0];
-                hb = reinterpret_cast<const float4*>(hs)[1];
-            } else {
-                float tmp[8];
+        // ---- stage x, the masked column weights and rho; clear the segment counts ----
+        int key[kPer];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) tmp[u] = u < d ? hs[u] : 0.0f;
-                ha = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
-                hb = make_float4(tmp[4], tmp[5], tmp[6], tmp[7]);
+        for (int u = 0; u < kPer; ++u) {
+            if (!kDirect && cur[u].valid) {
+                cur[u].sv = (uint32_t)cur[u].wd;
+                cur[u].kraw = (uint32_t)(cur[u].wd >> 32);
+                cur[u].mk = (uint32_t)(cur[u].wd >> 40) & 255u;
+                load_weights(cur[u]);
             }
-            reinterpret_cast<float4*>(sx + r * 8)[0] = xa;
-            reinterpret_cast<float4*>(sx + r * 8)[1] = xb;
+            key[u] = (int)(cur[u].kraw & (uint32_t)(W - 1));
         }
-        for (int v = tid; v < (kRedThreads / 64) * 256; v += kRedThreads) (&wcnt[0][0])[v] = 0;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int r = u * kRedThreads + tid;
+            if (!cur[u].valid) continue;
+            float4 ha = cur[u].ha, hb = cur[u].hb;
+            const uint32_t mk = cur[u].mk;
+            if (mk) {   // masked element: weight +0 (bit t of mk, sign-extended, clears the float)
+                auto zap = [mk](float v, int t) {
+                    return __uint_as_float(__float_as_uint(v) & ~(uint32_t)(-(int32_t)((mk >> t) & 1u)));
+                };
+                ha.x = zap(ha.x, 0);
+                ha.y = zap(ha.y, 1);
+                ha.z = zap(ha.z, 2);
+                ha.w = zap(ha.w, 3);
+                hb.x = zap(hb.x, 4);
+                hb.y = zap(hb.y, 5);
+                hb.z = zap(hb.z, 6);
+                hb.w = zap(hb.w, 7);
+            }
+            reinterpret_cast<float4*>(sx + r * 8)[0] = cur[u].xa;
+            reinterpret_cast<float4*>(sx + r * 8)[1] = cur[u].xb;
+            reinterpret_cast<float4*>(sh + r * 8)[0] = ha;
+            reinterpret_cast<float4*>(sh + r * 8)[1] = hb;
+            srho[r] = cur[u].rv;
+        }
+        for (int v = tid; v < kSegs * W / 8; v += kRedThreads)
+            reinterpret_cast<uint4*>(&scnt[0][0])[v] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
-        // ---- stable rank of record tid by centroid ----
-        unsigned long long peers;
-        const int wr = wave_peer_rank(key, valid, kbits, lt_mask, peers);
-        int rnk = -1;
+        // ---- stable ranks within each (pass, wavefront) segment ----
+        int wr[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            unsigned long long peers;
+            wr[u] = wave_peer_rank(key[u], cur[u].valid, KB, lt_mask, peers);
+            if (cur[u].valid && wr[u] == 0) scnt[u * (kRedThreads / 64) + wave][key[u]] = (uint16_t)__popcll(peers);
+        }
+        __syncthreads();
+        // ---- per key: exclusive scan over the segments; then over the keys ----
+        int tot = 0;
+        if (tid < W) {
+#pragma unroll
+            for (int s = 0; s < kSegs; ++s) {
+                const int c = scnt[s][tid];
+                scnt[s][tid] = (uint16_t)tot;
+                tot += c;
+            }
+        }
+        int inc = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(inc, off);
+            if (lane >= off) inc += o;
+        }
+        if (lane == 63) wsum[wave] = inc;
+        __syncthreads();
         {
-            int run = 0;
-            if (valid) run = wcnt[wave][key];
-            if (valid) rnk = run + wr;
-            if (valid && wr == 0) wcnt[wave][key] = (uint16_t)(run + __popcll(peers));
+            int carry = 0;
+            for (int w2 = 0; w2 < wave; ++w2) carry += wsum[w2];
+            if (tid < W) cstart[tid] = carry + inc - tot;
+            if (tid == W - 1) cstart[W] = carry + inc;
         }
         __syncthreads();
-        if (tid < width) {
-            int acc = 0;
-            for (int w = 0; w < kRedThreads / 64; ++w) {
-                const int c = wcnt[w][tid];
-                wcnt[w][tid] = (uint16_t)acc;
-                acc += c;
-            }
-            ccount[tid] = acc;
-        }
-        __syncthreads();
-        wave_excl_scan(ccount, width, cstart);
-        __syncthreads();
-        if (valid) {
-            perm[cstart[key] + wcnt[wave][key] + rnk] = (uint16_t)r;
-            srho[r] = rhov;
-            shv[r * 8 + 0] = (mk & 1u) ? 0.0f : ha.x;
-            shv[r * 8 + 1] = (mk & 2u) ? 0.0f : ha.y;
-            shv[r * 8 + 2] = (mk & 4u) ? 0.0f : ha.z;
-            shv[r * 8 + 3] = (mk & 8u) ? 0.0f : ha.w;
-            shv[r * 8 + 4] = (mk & 16u) ? 0.0f : hb.x;
-            shv[r * 8 + 5] = (mk & 32u) ? 0.0f : hb.y;
-            shv[r * 8 + 6] = (mk & 64u) ? 0.0f : hb.z;
-            shv[r * 8 + 7] = (mk & 128u) ? 0.0f : hb.w;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            if (!cur[u].valid) continue;
+            const int k = key[u];
+            perm[cstart[k] + scnt[u * (kRedThreads / 64) + wave][k] + wr[u]] = (uint16_t)(u * kRedThreads + tid);
         }
         // next sub-chunk's raw fields, in flight during the sums below
-        load_raw(c0 + kSub, valid, key, sv, mk, xa, xb);
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) load_raw(c0 + kSub, u, cur[u]);
         __syncthreads();
-        // ---- per owned centroid, members in record order ----
-#pragma unroll
-        for (int o = 0; o < 2; ++o) {
-            const int c = g + o * 128;
-            if (c >= width) break;
-            const int b0 = cstart[c], b1 = cstart[c + 1];
-            count[o] += b1 - b0;
-            int e = b0;
-            for (; e + 2 <= b1; e += 2) {
-                double w[2], x[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int rr = perm[e + u];
-                    w[u] = (double)shv[rr * 8 + t] * (double)srho[rr];
-                    x[u] = (double)sx[rr * 8 + t];
+        // ---- owner lanes: members in record order ----
+        {
+            const int e0 = cstart[oc], e1 = cstart[oc + 1];
+            count += e1 - e0;
+            // software pipelined: the next member's fields are read from LDS
+            // while the current member's terms are added
+            auto fetch = [&](int r_, float (&xv)[DP], float (&hv)[DP], float& rv_) {
+                const int o = r_ * 8 + oq * DP;
+                if constexpr (DP == 4) {
+                    const float4 a = *reinterpret_cast<const float4*>(sx + o);
+                    const float4 b = *reinterpret_cast<const float4*>(sh + o);
+                    xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+                    hv[0] = b.x; hv[1] = b.y; hv[2] = b.z; hv[3] = b.w;
+                } else {
+                    const float2 a = *reinterpret_cast<const float2*>(sx + o);
+                    const float2 b = *reinterpret_cast<const float2*>(sh + o);
+                    xv[0] = a.x; xv[1] = a.y;
+                    hv[0] = b.x; hv[1] = b.y;
                 }
+                rv_ = srho[r_];
+            };
+            if (e0 < e1) {
+                float ax[DP], ah[DP], ar;
+                fetch(perm[e0], ax, ah, ar);
+                for (int e = e0; e < e1; ++e) {
+                    float bx[DP], bh[DP], br;
+                    fetch(perm[min(e + 1, e1 - 1)], bx, bh, br);
+                    const double rd = (double)ar;
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    num[o] = num[o] + w[u] * x[u];
-                    den[o] = den[o] + w[u];
+                    for (int t = 0; t < DP; ++t) {
+                        add_term(num[t], den[t], ah[t], ax[t], rd);
+                        ax[t] = bx[t];
+                        ah[t] = bh[t];
+                    }
+                    ar = br;
                 }
-            }
-            for (; e < b1; ++e) {
-                const int rr = perm[e];
-                const double w = (double)shv[rr * 8 + t] * (double)srho[rr];
-                num[o] = num[o] + w * (double)sx[rr * 8 + t];
-                den[o] = den[o] + w;
             }
         }
         __syncthreads();
     }
     // ---- results ----
+    const int k = bk * W + oc;
+    if (k >= K) return;
+    const int t0 = oq * DP;
+    if (npieces == 1) {
 #pragma unroll
-    for (int o = 0; o < 2; ++o) {
-        const int c = g + o * 128;
-        if (c >= width) break;
-        const int k = bk * width + c;
-        if (k >= K) continue;
-        if (npieces == 1) {
-            if (t < d && den[o] > 0.0) C[(size_t)k * d + t] = (float)(num[o] / den[o]);
-            if (t == 0 && counts) counts[k] = count[o];
-        } else {
-            double* pp = partial + ((int64_t)j * 256 + c) * 17;
-            pp[t] = t < d ? num[o] : 0.0;
-            pp[8 + t] = t < d ? den[o] : 0.0;
-            if (t == 0) pp[16] = (double)count[o];
+        for (int t = 0; t < DP; ++t)
+            if (t0 + t < d && den[t] > 0.0) C[(size_t)k * d + t0 + t] = (float)(num[t] / den[t]);
+        if (oq == 0 && counts) counts[k] = count;
+    } else {
+        double* pp = partial + ((int64_t)j * 256 + oc) * 17;
+#pragma unroll
+        for (int t = 0; t < DP; ++t) {
+            pp[t0 + t] = num[t];
+            pp[8 + t0 + t] = den[t];
         }
+        if (oq == 0) pp[16] = (double)count;
     }
 }
 
 // Buckets with several pieces (and empty buckets, whose counts are zeroed):
-// one wavefront per centroid (grid-stride);
-// lane = (group q, dimension t); group q adds pieces q, q + 8, ... in order,
-// then the 8 group sums are combined by a fixed butterfly and divided once.
-__global__ __launch_bounds__(64) void k_piece_finish(const int* __restrict__ poff, int nbk, int width, int K,
-                                                     int d, const double* __restrict__ partial,
-                                                     float* __restrict__ C, int32_t* __restrict__ counts)
+// one workgroup per centroid (grid-stride); thread = (group q of 32,
+// dimension t).  Group q adds pieces q, q + 32, ... in order, four loads in
+// flight; the 32 group sums are then combined in a fixed pattern (a
+// butterfly within each wavefront, the four wavefront sums in order) and
+// divided once.
+__global__ __launch_bounds__(256) void k_piece_finish(const int* __restrict__ poff, int nbk, int width, int K,
+                                                      int d, const double* __restrict__ partial,
+                                                      float* __restrict__ C, int32_t* __restrict__ counts)
 {
-    const int lane = threadIdx.x;
-    const int t = lane & 7, qg = lane >> 3;
+    __shared__ double wnum[4][8], wden[4][8], wcntd[4];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int t = tid & 7, qg = tid >> 3;
     for (int k = blockIdx.x; k < K; k += gridDim.x) {
         const int bk = k / width, c = k - bk * width;
         if (bk >= nbk) break;
         const int j0 = poff[bk], j1 = poff[bk + 1];
         if (j1 - j0 == 1) continue;   // finished inside its piece
         if (j1 == j0) {                // empty bucket: no members, C kept
-            if (lane == 0 && counts) counts[k] = 0;
+            if (tid == 0 && counts) counts[k] = 0;
             continue;
         }
         double num = 0.0, den = 0.0, cntd = 0.0;
-        for (int jj = j0 + qg; jj < j1; jj += 8) {
+        int jj = j0 + qg;
+        for (; jj + 96 < j1; jj += 128) {
+            double a[4], b[4], n4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const double* pp = partial + ((int64_t)(jj + 32 * u) * 256 + c) * 17;
+                a[u] = pp[t];
+                b[u] = pp[8 + t];
+                n4[u] = pp[16];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                num = num + a[u];
+                den = den + b[u];
+                cntd = cntd + n4[u];
+            }
+        }
+        for (; jj < j1; jj += 32) {
             const double* pp = partial + ((int64_t)jj * 256 + c) * 17;
             num = num + pp[t];
             den = den + pp[8 + t];
@@ -513,10 +619,24 @@ __global__ __launch_bounds__(64) void k_piece_finish(const int* __restrict__ pof
             den = den + __shfl_xor(den, off);
             cntd = cntd + __shfl_xor(cntd, off);
         }
-        if (qg == 0) {
-            if (t < d && den > 0.0) C[(size_t)k * d + t] = (float)(num / den);
-            if (t == 0 && counts) counts[k] = (int32_t)cntd;
+        if (lane < 8) {
+            wnum[wave][t] = num;
+            wden[wave][t] = den;
+            if (t == 0) wcntd[wave] = cntd;
         }
+        __syncthreads();
+        if (tid < 8) {
+            double sn = wnum[0][t], sd = wden[0][t], sc = wcntd[0];
+#pragma unroll
+            for (int w2 = 1; w2 < 4; ++w2) {
+                sn = sn + wnum[w2][t];
+                sd = sd + wden[w2][t];
+                sc = sc + wcntd[w2];
+            }
+            if (t < d && sd > 0.0) C[(size_t)k * d + t] = (float)(sn / sd);
+            if (t == 0 && counts) counts[k] = (int32_t)sc;
+        }
+        __syncthreads();
     }
 }
 
@@ -600,11 +720,16 @@ vq_status update_launch(const float* X, const float* hcol, const float* rho, con
         hipLaunchKernelGGL(k_piece_setup, dim3(1), dim3(64), 0, st, nullptr, 1, n_sub, piece, w.bstart, w.poff);
         VQ_LAUNCHED("k_piece_setup");
     }
-    hipLaunchKernelGGL(k_piece_reduce, dim3((unsigned)max_pieces(n_sub, K)), dim3(kRedThreads), 0, st,
-                       bucketed ? w.rx : nullptr, w.rw, X, idx, mask, hcol, rho, (uint32_t)(N / d), d, K, nbk, piece,
-                       w.bstart, w.poff, C, counts, w.partial);
+    if (bucketed)
+        hipLaunchKernelGGL(k_piece_reduce<128>, dim3((unsigned)max_pieces(n_sub, K)), dim3(kRedThreads), 0, st, w.rx,
+                           w.rw, X, idx, mask, hcol, rho, (uint32_t)(N / d), d, K, nbk, piece, w.bstart, w.poff, C,
+                           counts, w.partial);
+    else
+        hipLaunchKernelGGL(k_piece_reduce<256>, dim3((unsigned)max_pieces(n_sub, K)), dim3(kRedThreads), 0, st,
+                           nullptr, w.rw, X, idx, mask, hcol, rho, (uint32_t)(N / d), d, K, nbk, piece, w.bstart,
+                           w.poff, C, counts, w.partial);
     VQ_LAUNCHED("k_piece_reduce");
-    hipLaunchKernelGGL(k_piece_finish, dim3((unsigned)std::min(K, 4096)), dim3(64), 0, st, w.poff, nbk, width, K, d,
+    hipLaunchKernelGGL(k_piece_finish, dim3((unsigned)std::min(K, 4096)), dim3(256), 0, st, w.poff, nbk, width, K, d,
                        w.partial, C, counts);
     VQ_LAUNCHED("k_piece_finish");
     return VQ_OK;
