@@ -207,6 +207,31 @@ __global__ __launch_bounds__(kTileThreads) void k_bucket_scatter(
     const int wave = tid >> 6;
     const int64_t e0 = (int64_t)tile * kTile;
     const int m = (int)min((int64_t)kTile, n - e0);
+    const bool vec = (d == 8) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+    // every global load of the tile is issued first: the records' x and mask
+    // bytes arrive while the indices are ranked
+    int dg[2], rank[2], r_of[2];
+    uint16_t iv[2];
+    uint32_t mkv[2];
+    float4 xa[2], xb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = wave * 128 + h * 64 + lane;
+        r_of[h] = r;
+        iv[h] = 0;
+        mkv[h] = 0;
+        xa[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+        xb[h] = xa[h];
+        if (r < m) {
+            iv[h] = idx[e0 + r];
+            if (mask) mkv[h] = mask[e0 + r];
+            if (vec) {
+                const float4* src = reinterpret_cast<const float4*>(X + (e0 + r) * 8);
+                xa[h] = src[0];
+                xb[h] = src[1];
+            }
+        }
+    }
     for (int q = tid; q < (kTileThreads / 64) * kMaxBuckets; q += kTileThreads) (&wcnt[0][0])[q] = 0;
     for (int q = tid; q < nbk; q += kTileThreads)
         gbase[q] = bstart[q] + hist[(int64_t)q * ntile + tile];
@@ -214,13 +239,9 @@ __global__ __launch_bounds__(kTileThreads) void k_bucket_scatter(
     const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int bits = 0;
     while ((1 << bits) < nbk) ++bits;
-    int dg[2], rank[2], r_of[2];
-    uint16_t iv[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int r = wave * 128 + h * 64 + lane;
-        r_of[h] = r;
-        iv[h] = r < m ? idx[e0 + r] : (uint16_t)0;
+        const int r = r_of[h];
         const bool valid = r < m && (iv[h] >> kBucketShift) < nbk;
         dg[h] = valid ? (iv[h] >> kBucketShift) : 0;
         unsigned long long peers;
@@ -243,21 +264,19 @@ __global__ __launch_bounds__(kTileThreads) void k_bucket_scatter(
     __syncthreads();
     wave_excl_scan(tcnt, nbk, tstart);
     __syncthreads();
-    const bool vec = (d == 8) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         if (rank[h] < 0) continue;
         const int lp = tstart[dg[h]] + wcnt[wave][dg[h]] + rank[h];
         const int64_t e = e0 + r_of[h];
         if (vec) {
-            const float4* src = reinterpret_cast<const float4*>(X + e * 8);
             float4* dst = reinterpret_cast<float4*>(sxr + lp * 8);
-            dst[0] = src[0];
-            dst[1] = src[1];
+            dst[0] = xa[h];
+            dst[1] = xb[h];
         } else {
             for (int t = 0; t < d; ++t) sxr[lp * 8 + t] = X[e * d + t];
         }
-        const uint64_t mk = mask ? (uint64_t)mask[e] : 0ull;
+        const uint64_t mk = (uint64_t)mkv[h];
         sw[lp] = (uint64_t)(uint32_t)e | ((uint64_t)(iv[h] & 127) << 32) | (mk << 40);
         sdg[lp] = (uint16_t)dg[h];
     }
