@@ -586,7 +586,7 @@ __global__ __launch_bounds__(kRedThreads) void k_piece_reduce(
 }
 
 // Buckets with several pieces (and empty buckets, whose counts are zeroed):
-// one workgroup per centroid (grid-stride); thread = (group q of 32,
+// one workgroup per centroid (16 of one bucket when buckets hold 128); thread = (group q of 32,
 // dimension t).  Group q adds pieces q, q + 32, ... in order, four loads in
 // flight; the 32 group sums are then combined in a fixed pattern (a
 // butterfly within each wavefront, the four wavefront sums in order) and
@@ -599,11 +599,15 @@ __global__ __launch_bounds__(256) void k_piece_finish(const int* __restrict__ po
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int t = tid & 7, qg = tid >> 3;
-    for (int k = blockIdx.x; k < K; k += gridDim.x) {
+    // workgroup: centroids [k0, k0 + cpb) of one bucket; a bucket finished
+    // inside its piece ends the workgroup at once
+    const int cpb = width == 256 ? 1 : 16;
+    const int k0 = blockIdx.x * cpb;
+    if (k0 >= K || k0 / width >= nbk) return;
+    if (poff[k0 / width + 1] - poff[k0 / width] == 1) return;
+    for (int k = k0; k < min(k0 + cpb, K); ++k) {
         const int bk = k / width, c = k - bk * width;
-        if (bk >= nbk) break;
         const int j0 = poff[bk], j1 = poff[bk + 1];
-        if (j1 - j0 == 1) continue;   // finished inside its piece
         if (j1 == j0) {                // empty bucket: no members, C kept
             if (tid == 0 && counts) counts[k] = 0;
             continue;
@@ -748,7 +752,8 @@ vq_status update_launch(const float* X, const float* hcol, const float* rho, con
                            nullptr, w.rw, X, idx, mask, hcol, rho, (uint32_t)(N / d), d, K, nbk, piece, w.bstart,
                            w.poff, C, counts, w.partial);
     VQ_LAUNCHED("k_piece_reduce");
-    hipLaunchKernelGGL(k_piece_finish, dim3((unsigned)std::min(K, 4096)), dim3(256), 0, st, w.poff, nbk, width, K, d,
+    hipLaunchKernelGGL(k_piece_finish, dim3((unsigned)((K + (bucketed ? 15 : 0)) / (bucketed ? 16 : 1))), dim3(256), 0,
+                       st, w.poff, nbk, width, K, d,
                        w.partial, C, counts);
     VQ_LAUNCHED("k_piece_finish");
     return VQ_OK;
