@@ -698,6 +698,7 @@ def main():
         extra["reconstruct_GBs"] = round(rb / (r_[3] / r_[2] * 1e-3) / 1e9, 1)
         extra["reconstruct_frac_hbm"] = round(extra["reconstruct_GBs"] / PEAK_HBM_GBS, 4)
     extra["J_final"] = float(out["J"][-1])
+    extra["empty_centroids_per_update"] = [int(x) for x in out["empty"]]
     extra["bpw"] = out["bpw"]
 
     if args.breakdown:

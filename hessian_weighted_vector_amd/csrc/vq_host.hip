@@ -388,14 +388,37 @@ vq_status update_with_J(const float* X, const float* hcol, const float* rho, con
                          ws_bytes - wo, st);
 }
 
+// Centroids with no member: one workgroup counts the zero entries of
+// counts[0..K) (per-lane counts, a wavefront butterfly, the four wavefront
+// sums in order) and writes the total to *out.
+__global__ __launch_bounds__(256) void k_count_empty(const int32_t* __restrict__ counts, int K,
+                                                     unsigned long long* __restrict__ out)
+{
+    __shared__ unsigned long long ws4[4];
+    unsigned long long c = 0;
+    for (int k = threadIdx.x; k < K; k += 256) c += counts[k] == 0 ? 1ull : 0ull;
+    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+    if ((threadIdx.x & 63) == 0) ws4[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) *out = ws4[0] + ws4[1] + ws4[2] + ws4[3];
+}
+
 // One Lloyd stage: T x (assign, objective, update), final assign, objective.
+// With emp: the update also counts members (into counts[K]) and emp[t]
+// receives the number of centroids left with none.
 vq_status lloyd_stage(const float* X, const float* hcol, const float* rho, const uint8_t* mask, int64_t M,
                       int64_t N, int d, float* C, int K, int T, uint16_t* idx, double* Jd, void* ws,
-                      size_t ws_bytes, hipStream_t st)
+                      size_t ws_bytes, hipStream_t st, int32_t* counts = nullptr,
+                      unsigned long long* emp = nullptr)
 {
     for (int t = 0; t < T; ++t) {
         VQ_TRY(assign_launch(X, hcol, rho, mask, M, N, d, C, K, idx, nullptr, ws, ws_bytes, st));
-        VQ_TRY(update_with_J(X, hcol, rho, mask, M, N, d, idx, K, C, nullptr, Jd + t, ws, ws_bytes, st));
+        VQ_TRY(update_with_J(X, hcol, rho, mask, M, N, d, idx, K, C, emp ? counts : nullptr, Jd + t, ws, ws_bytes,
+                             st));
+        if (emp) {
+            hipLaunchKernelGGL(k_count_empty, dim3(1), dim3(256), 0, st, counts, K, emp + t);
+            VQ_LAUNCHED("k_count_empty");
+        }
     }
     VQ_TRY(assign_launch(X, hcol, rho, mask, M, N, d, C, K, idx, nullptr, ws, ws_bytes, st));
     return objective_launch(X, hcol, rho, mask, M, N, d, C, K, idx, Jd + T, ws, ws_bytes, st);
@@ -447,6 +470,8 @@ size_t vq_workspace_bytes(int64_t M, int64_t N, int d, int K1, int K2, int64_t n
     size_t w = ws_steps(M, N, d, std::max(K1, 1), std::max(K2, 1));
     if (K2 > 0) w += align_up((size_t)M * N * sizeof(float));
     w += align_up(sizeof(double) * iters_guess);
+    w += align_up(sizeof(int32_t) * (size_t)std::max(std::max(K1, K2), 1));   // member counts
+    w += align_up(sizeof(unsigned long long) * iters_guess);                  // empty-centroid history
     (void)n_sub;
     return w;
 }
@@ -774,7 +799,10 @@ vq_status vq_fit(const vq_fit_params* p, const vq_fit_inputs* in, vq_fit_outputs
     Carver cv(ws, ws_bytes);
     float* R = p->K2 > 0 ? cv.take<float>((size_t)M * N) : nullptr;
     double* Jd = cv.take<double>(256);
+    int32_t* cnt = cv.take<int32_t>((size_t)std::max(std::max(p->K1, p->K2), 1));
+    unsigned long long* emp = cv.take<unsigned long long>(256);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_fit: workspace too small");
+    unsigned long long* emp_on = out->empty_hist ? emp : nullptr;
     void* sws = cv.base + cv.used;
     const size_t sws_bytes = cv.cap - cv.used;
 
@@ -796,7 +824,8 @@ vq_status vq_fit(const vq_fit_params* p, const vq_fit_inputs* in, vq_fit_outputs
         VQ_HIP(hipMemcpyAsync(out->C1, in->C1_init, (size_t)p->K1 * d * sizeof(float), hipMemcpyDeviceToDevice, st));
     else
         VQ_TRY(init_walk(X, n_sub, d, in->perm1, p->K1, out->C1, sws, sws_bytes, st));
-    VQ_TRY(lloyd_stage(X, hc, rh, mk, M, N, d, out->C1, p->K1, p->iters1, out->idx1, Jd, sws, sws_bytes, st));
+    VQ_TRY(lloyd_stage(X, hc, rh, mk, M, N, d, out->C1, p->K1, p->iters1, out->idx1, Jd, sws, sws_bytes, st, cnt,
+                       emp_on));
     const int nJ = p->iters1 + 1 + (p->K2 > 0 ? p->iters2 + 1 : 0);
     if (p->K2 > 0) {
         VQ_TRY(residual_launch(X, M, N, d, out->C1, p->K1, out->idx1, R, st));
@@ -805,12 +834,15 @@ vq_status vq_fit(const vq_fit_params* p, const vq_fit_inputs* in, vq_fit_outputs
         else
             VQ_TRY(init_walk(R, n_sub, d, in->perm2, p->K2, out->C2, sws, sws_bytes, st));
         VQ_TRY(lloyd_stage(R, hc, rh, mk, M, N, d, out->C2, p->K2, p->iters2, out->idx2, Jd + p->iters1 + 1, sws,
-                           sws_bytes, st));
+                           sws_bytes, st, cnt, emp_on ? emp_on + p->iters1 : nullptr));
     }
     VQ_TRY(reconstruct_launch(M, N, d, out->C1, p->K1, out->idx1, p->K2 > 0 ? out->C2 : nullptr, p->K2, out->idx2,
                               p->binorm ? out->rscale : nullptr, p->binorm ? out->cscale : nullptr,
                               nnz > 0 ? out->row_ptr : nullptr, out->col, out->val, out->W_hat, st));
     VQ_HIP(hipMemcpyAsync(out->J_hist, Jd, sizeof(double) * nJ, hipMemcpyDeviceToHost, st));
+    const int nE = p->iters1 + (p->K2 > 0 ? p->iters2 : 0);
+    if (emp_on && nE > 0)
+        VQ_HIP(hipMemcpyAsync(out->empty_hist, emp, sizeof(int64_t) * nE, hipMemcpyDeviceToHost, st));
     VQ_HIP(hipStreamSynchronize(st));
     if (out->bpw) *out->bpw = vq_bits_per_weight(M, N, d, p->K1, p->K2, nnz, 32, p->binorm);
     return VQ_OK;

@@ -46,7 +46,7 @@ class FitInputs(ctypes.Structure):
 class FitOutputs(ctypes.Structure):
     _fields_ = [("idx1", _P), ("C1", _P), ("idx2", _P), ("C2", _P), ("row_ptr", _P), ("col", _P),
                 ("val", _P), ("mask", _P), ("Wp", _P), ("rscale", _P), ("cscale", _P), ("hcol", _P),
-                ("rho", _P), ("W_hat", _P), ("J_hist", _P), ("bpw", _P)]
+                ("rho", _P), ("W_hat", _P), ("J_hist", _P), ("bpw", _P), ("empty_hist", _P)]
 
 
 class GroupedParams(ctypes.Structure):
@@ -438,6 +438,7 @@ def fit(W, h, d, K1, iters1, K2=0, iters2=0, outlier_frac=0.0, binorm=False, mas
     nJ = iters1 + 1 + (iters2 + 1 if K2 > 0 else 0)
     J = np.zeros(nJ, np.float64)
     bpw = np.zeros(1, np.float64)
+    empty = np.zeros(max(iters1 + (iters2 if K2 > 0 else 0), 1), np.int64)
     p1 = None if perm1 is None else np.ascontiguousarray(perm1, dtype=np.int32)
     p2 = None if perm2 is None else np.ascontiguousarray(perm2, dtype=np.int32)
     params = FitParams(M, N, d, K1, iters1, K2, iters2, float(outlier_frac), int(bool(binorm)),
@@ -447,12 +448,13 @@ def fit(W, h, d, K1, iters1, K2=0, iters2=0, outlier_frac=0.0, binorm=False, mas
     g = lambda k: _ptr(o[k]) if k in o else None  # noqa: E731
     outputs = FitOutputs(g("idx1"), g("C1"), g("idx2"), g("C2"), g("row_ptr"), g("col"), g("val"), g("mask"),
                          g("Wp"), g("rscale"), g("cscale"), g("hcol"), g("rho"), g("W_hat"),
-                         J.ctypes.data, bpw.ctypes.data)
+                         J.ctypes.data, bpw.ctypes.data, empty.ctypes.data)
     _check(load().vq_fit(ctypes.byref(params), ctypes.byref(inputs), ctypes.byref(outputs), _ptr(ws),
                          ws.numel(), _stream()))
     o["col"] = o["col"][:nnz]
     o["val"] = o["val"][:nnz]
     o["J"] = J
+    o["empty"] = empty[:iters1 + (iters2 if K2 > 0 else 0)]
     o["bpw"] = float(bpw[0])
     o["nnz"] = nnz
     if K2 == 0:

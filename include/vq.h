@@ -326,6 +326,9 @@ typedef struct {
     float* W_hat;                  /* [M x N] */
     double* J_hist;                /* host double[iters1+1 (+ iters2+1)] */
     double* bpw;                   /* host double[1], b_cb = 32 (nullable) */
+    int64_t* empty_hist;           /* host int64[iters1 (+ iters2)] (nullable): after each
+                                      update, the number of centroids with no member (they
+                                      keep their previous value) */
 } vq_fit_outputs;
 
 vq_status vq_fit(const vq_fit_params* p, const vq_fit_inputs* in, vq_fit_outputs* out,

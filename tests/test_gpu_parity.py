@@ -377,6 +377,54 @@ def test_fit_unmasked_and_degenerate():
     assert _compare_fit(o, g, 8, 5)
 
 
+def _replay_stage(X, hc, rh, keep, d, C, T):
+    """The oracle's Lloyd stage step by step: (codebook, indices, centroids left
+    without members after each update)."""
+    empty = []
+    for _ in range(T):
+        idx, _ = oracle.assign(X, hc, rh, keep, d, C)
+        C, counts, _ = oracle.update(X, hc, rh, keep, d, idx, C)
+        empty.append(int(np.count_nonzero(counts == 0)))
+    idx, _ = oracle.assign(X, hc, rh, keep, d, C)
+    return C, idx, empty
+
+
+@pytest.mark.parametrize("case", ["ties", "binorm"])
+def test_fit_empty_centroid_history_matches_oracle(case):
+    # "ties": weights on three levels and zero column weights on the last four
+    # dimensions of every block, so distinct seeds coincide under the weighted
+    # distance; the lowest index takes every tie and the others stay empty (and
+    # keep their value) at every update.  "binorm": a plain random case (no
+    # centroid goes empty), compared the same way.
+    say("fit empty history", case)
+    inp = synth.small_case(83, 64, 128, d=8)
+    W, h = inp["W"], inp["h"]
+    binorm = case == "binorm"
+    if case == "ties":
+        g = np.random.default_rng([83, 1])
+        W = (0.01 * g.integers(0, 3, size=W.shape)).astype(np.float32)
+        h = h.copy()
+        h[(np.arange(h.size) % 8) >= 4] = 0.0
+    d, K1, T1, K2, T2, p = 8, 400, 6, 100, 4, 0.02
+    o = oracle.fit(W, h, d, K1, T1, K2, T2, p, binorm, True, inp["perm1"], inp["perm2"])
+    X, hc, rh, keep = o["Wp"], o["hcol"], (o["rho"] if binorm else None), o["keep"]
+    C1, taken = oracle.init(X, d, inp["perm1"], K1)
+    assert taken == K1
+    C1, idx1, e1 = _replay_stage(X, hc, rh, keep, d, C1, T1)
+    assert bits_equal(C1, o["C1"]) and np.array_equal(idx1, o["idx1"])      # the replay is the fit
+    R = oracle.residual(X, d, C1, idx1)
+    C2, taken = oracle.init(R, d, inp["perm2"], K2)
+    assert taken == K2
+    C2, idx2, e2 = _replay_stage(R, hc, rh, keep, d, C2, T2)
+    assert bits_equal(C2, o["C2"]) and np.array_equal(idx2, o["idx2"])
+    expect = np.array(e1 + e2, np.int64)
+    if case == "ties":
+        assert expect.min() > 0                                             # the case exercises empties
+    g = vq.fit(dev(W), dev(h), d, K1, T1, K2, T2, p, binorm, True, inp["perm1"], inp["perm2"])
+    assert np.array_equal(host(g["idx1"]), o["idx1"]) and np.array_equal(host(g["idx2"]), o["idx2"])
+    assert np.array_equal(g["empty"], expect), (g["empty"], expect)
+
+
 def test_fit_smollm2_config_matches_oracle():
     """The 2048 x 2048 workload end to end (oracle: tens of seconds)."""
     from hessian_weighted_vector_amd import configs
