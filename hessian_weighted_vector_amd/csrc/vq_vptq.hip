@@ -260,9 +260,9 @@ __global__ __launch_bounds__(256) void k_vp_prep(const float* __restrict__ C, in
 __global__ __launch_bounds__(256) void k_col_step_h16(
     double* __restrict__ Wt, int64_t M, int nv, int64_t n, int64_t s, int64_t s_end, const float* __restrict__ C,
     const float* __restrict__ U, int64_t N, unsigned long long* __restrict__ keys, const int* __restrict__ win,
-    double* __restrict__ Xc, uint16_t* __restrict__ idx, float* __restrict__ Wht, double* __restrict__ Et,
-    const vp_h16x8* __restrict__ Phi, const vp_h16x8* __restrict__ Plo, const vp_h16x8* __restrict__ Phn,
-    const float* __restrict__ cmax, int K)
+    const float* __restrict__ qrow, double* __restrict__ Xc, uint16_t* __restrict__ idx, float* __restrict__ Wht,
+    double* __restrict__ Et, const vp_h16x8* __restrict__ Phi, const vp_h16x8* __restrict__ Plo,
+    const vp_h16x8* __restrict__ Phn, const float* __restrict__ cmax, int K)
 {
     __shared__ vp_h16x8 L[3][kVpChunk];
     const int k0 = blockIdx.y * kVpChunk;
@@ -277,9 +277,13 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
     const int jl = lane & 31, half = lane >> 5;
     const int j = j0 + jl;
     const bool active = j0 < nv;                         // the wave holds sub-vectors
-    double x64[8];
+    double x64[8], e[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) x64[t] = 0.0;
+    for (int t = 0; t < 8; ++t) {
+        x64[t] = 0.0;
+        e[t] = 0.0;
+    }
+    bool later = false;                                  // the block's later columns get e (after the search)
     if (j < nv) {
         const double2* w2 = reinterpret_cast<const double2*>(Wt + n * M) + 4 * (size_t)j;
         double w[8];
@@ -296,12 +300,12 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
             // is split over the workgroups of these rows by column
             const int64_t p = n - 1;
             const int kp = win[(size_t)(p & 1) * nv + j];
-            const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)kp;
-            const float4 ca = c4[0], cb = c4[1];
+            // the winner's row, written beside its index by the column's decision
+            const float4* q4 = reinterpret_cast<const float4*>(qrow) + ((size_t)(p & 1) * nv + j) * 2;
+            const float4 ca = q4[0], cb = q4[1];
             const float qv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
             const double* xp = Xc + (size_t)(p & 1) * M + (size_t)j * 8;
             const double unn = (double)U[p * N + p], un = (double)U[p * N + n];
-            double e[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 e[t] = (xp[t] - (double)qv[t]) / unn;
@@ -315,12 +319,7 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
                 }
                 idx[p * nv + j] = (uint16_t)kp;
             }
-            for (int64_t r = n + 1 + blockIdx.y; r < s_end; r += gridDim.y) {
-                const double u = (double)U[p * N + r];
-                double* wr = Wt + r * M + (int64_t)j * 8 + half * 4;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) wr[t] = wr[t] - e[half * 4 + t] * u;
-            }
+            later = true;
         } else {
 #pragma unroll
             for (int t = 0; t < 8; ++t) x64[t] = w[t];
@@ -418,6 +417,17 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
             atomicMin(&keys[key_at(nv, slot, 1, n, j)], lost < ks_ ? lost : ks_);
         }
     }
+    // column n-1's error into the block's later columns, split over the
+    // workgroups of these rows by column (no later read in this launch)
+    if (later) {
+        const int64_t p = n - 1;
+        for (int64_t r = n + 1 + blockIdx.y; r < s_end; r += gridDim.y) {
+            const double u = (double)U[p * N + r];
+            double* wr = Wt + r * M + (int64_t)j * 8 + half * 4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) wr[t] = wr[t] - e[half * 4 + t] * u;
+        }
+    }
 }
 
 // Column n's winners (V = 8 path).  Grid: x over row blocks of kStepRows
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(256) void k_col_exact(int nv, int64_t n, int64_t M,
                                                    const float* __restrict__ cmax, const double* __restrict__ Xc,
                                                    double* __restrict__ part_d, int* __restrict__ part_i,
                                                    int* __restrict__ arrived, int* __restrict__ win,
-                                                   int* __restrict__ fl_total)
+                                                   float* __restrict__ qrow, int* __restrict__ fl_total)
 {
     __shared__ int s_nflag, s_last;
     __shared__ int s_flag[kStepRows];
@@ -473,12 +483,12 @@ __global__ __launch_bounds__(256) void k_col_exact(int nv, int64_t n, int64_t M,
         }
         const unsigned long long k2 = a2 < bmin ? a2 : bmin;
         const int kbest = (int)(a1 & 0xFFFFFFFFull);
+        const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)kbest;
+        const float4 ca = c4[0], cb = c4[1];
         bool ok = true;
         if (k2 != ~0ull) {
             const double sA = -(double)unsortable((unsigned)(a1 >> 32));
             const double sB = -(double)unsortable((unsigned)(k2 >> 32));
-            const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)kbest;
-            const float4 ca = c4[0], cb = c4[1];
             const float qv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
             double nx2 = 0.0, db = 0.0;
 #pragma unroll
@@ -496,7 +506,12 @@ __global__ __launch_bounds__(256) void k_col_exact(int nv, int64_t n, int64_t M,
             ok = gap > 2.0 * bound;                      // false also for NaN
         }
         if (ok) {
-            if (blockIdx.y == 0) win[(size_t)(n & 1) * nv + j] = kbest;
+            if (blockIdx.y == 0) {
+                win[(size_t)(n & 1) * nv + j] = kbest;
+                float4* q4 = reinterpret_cast<float4*>(qrow) + ((size_t)(n & 1) * nv + j) * 2;
+                q4[0] = ca;
+                q4[1] = cb;
+            }
         } else {
             s_flag[atomicAdd(&s_nflag, 1)] = wave * 32 + jl;
         }
@@ -575,7 +590,13 @@ __global__ __launch_bounds__(256) void k_col_exact(int nv, int64_t n, int64_t M,
             const int oi = __shfl_xor(bk, o);
             if (od < bd || (od == bd && oi < bk)) { bd = od; bk = oi; }
         }
-        if (lane == 0) win[(size_t)(n & 1) * nv + jj] = bk;
+        if (lane == 0) {
+            win[(size_t)(n & 1) * nv + jj] = bk;
+            const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)bk;
+            float4* q4 = reinterpret_cast<float4*>(qrow) + ((size_t)(n & 1) * nv + jj) * 2;
+            q4[0] = c4[0];
+            q4[1] = c4[1];
+        }
     }
     if (threadIdx.x == 0) {
         arrived[blockIdx.x] = 0;
@@ -587,6 +608,7 @@ __global__ __launch_bounds__(256) void k_col_exact(int nv, int64_t n, int64_t M,
 // the block is left to update.
 __global__ __launch_bounds__(256) void k_col_last(int64_t M, int nv, int64_t n, const float* __restrict__ C,
                                                   const float* __restrict__ U, int64_t N, const int* __restrict__ win,
+                                                  const float* __restrict__ qrow,
                                                   const double* __restrict__ Xc, uint16_t* __restrict__ idx,
                                                   float* __restrict__ Wht, double* __restrict__ Et)
 {
@@ -594,7 +616,7 @@ __global__ __launch_bounds__(256) void k_col_last(int64_t M, int nv, int64_t n, 
     if (m >= M) return;
     const int v = (int)(m >> 3), t = (int)(m & 7);
     const int k = win[(size_t)(n & 1) * nv + v];
-    const float wq = C[(size_t)k * 8 + t];
+    const float wq = qrow[((size_t)(n & 1) * nv + v) * 8 + t];
     const double e = (Xc[(size_t)(n & 1) * M + m] - (double)wq) / (double)U[n * N + n];
     Wht[n * M + m] = wq;
     Et[n * M + m] = e;
@@ -723,12 +745,14 @@ size_t ws_vptq(int64_t M, int64_t N, int V)
     const int64_t nch = (65536 + kAsgChunk - 1) / kAsgChunk;
     // the float64 working matrix and errors, the float32 quantized matrix (all
     // transposed), three key buffers (A and B keys, kKeySlots copies), two
-    // winner columns, the row-block arrival counters, two float64 working
+    // winner columns and their codebook rows, the row-block arrival counters,
+    // two float64 working
     // columns, the prepared codebook (3 x 16 bytes per centroid, at most
     // 65536), max |C|, and the per-chunk winners of the exact searches; per
     // row block an arrival counter; the count of exact searches
     return 2 * align_up((size_t)M * (size_t)N * sizeof(double)) + align_up((size_t)M * (size_t)N * sizeof(float)) +
            align_up((size_t)(3 * kKeySlots * 2 * nv) * sizeof(uint64_t)) + align_up((size_t)(2 * nv) * sizeof(int)) +
+           align_up((size_t)(16 * nv) * sizeof(float)) +
            align_up((size_t)nrb * sizeof(int)) + align_up(sizeof(int)) +
            align_up((size_t)(2 * M) * sizeof(double)) +
            3 * align_up((size_t)65536 * sizeof(vp_h16x8)) + align_up(sizeof(float)) +
@@ -747,6 +771,7 @@ vq_status vptq_launch(const float* W, const float* U, int64_t M, int64_t N, int 
     float* Wht = cv.take<float>((size_t)(M * N));
     unsigned long long* keys = cv.take<unsigned long long>((size_t)(3 * kKeySlots * 2 * nv));
     int* win = cv.take<int>((size_t)(2 * nv));
+    float* qrow = cv.take<float>((size_t)(16 * nv));
     int* arrived = cv.take<int>((size_t)nrb);
     int* fl_total = cv.take<int>(1);
     double* Xc = cv.take<double>((size_t)(2 * M));
@@ -787,14 +812,14 @@ vq_status vptq_launch(const float* W, const float* U, int64_t M, int64_t N, int 
             // and one for the block's last column
             for (int64_t n = s; n < s_end; ++n) {
                 hipLaunchKernelGGL(k_col_step_h16, gm, dim3(256), 0, st, Wt, M, (int)nv, n, s, s_end, C, U, N, keys,
-                                   win, Xc, idx, Wht, Et, Phi, Plo, Phn, cmax, K);
+                                   win, qrow, Xc, idx, Wht, Et, Phi, Plo, Phn, cmax, K);
                 VQ_LAUNCHED("k_col_step_h16");
                 hipLaunchKernelGGL(k_col_exact, gm, dim3(256), 0, st, (int)nv, n, M, C, K, keys, cmax, Xc, part_d,
-                                   part_i, arrived, win, fl_total);
+                                   part_i, arrived, win, qrow, fl_total);
                 VQ_LAUNCHED("k_col_exact");
             }
             hipLaunchKernelGGL(k_col_last, dim3(grid_for(M, 256)), dim3(256), 0, st, M, (int)nv, s_end - 1, C, U, N,
-                               win, Xc, idx, Wht, Et);
+                               win, qrow, Xc, idx, Wht, Et);
             VQ_LAUNCHED("k_col_last");
         } else {
             for (int64_t n = s; n < s_end; ++n) {
