@@ -217,6 +217,26 @@ def test_update_empty_centroid_group(case):
     assert abs(float(host(J)[0]) - Jref) <= 1e-12 * abs(Jref)
 
 
+@pytest.mark.parametrize("K", [256, 3000], ids=["one-bucket", "buckets"])
+def test_update_sorted_indices(K):
+    # indices sorted by centroid: every sub-chunk of the reduction belongs to
+    # one or two centroids, so single lanes walk a thousand members in a row
+    seed, M, N, d = 41, 512, 1024, 8
+    say("update sorted indices", K)
+    W, h, C, keep, rho = _case(seed, M, N, d, K)
+    n_sub = M * N // d
+    g = np.random.default_rng([99, seed, 3])
+    idx = np.sort(g.integers(0, K, size=n_sub)).astype(np.uint16)
+    Cref, cref, Jref = oracle.update(W, h, rho, keep, d, idx, C)
+    ws = vq.workspace(M, N, d, K)
+    Cg = dev(C)
+    counts, J = vq.update(dev(W), dev(h), dev(rho), dev(mask_from_keep(keep, d)), d, dev(idx), Cg, ws)
+    ok, bad = centroid_close(host(Cg), Cref)
+    assert ok, bad[:10]
+    assert np.array_equal(host(counts), cref)
+    assert abs(float(host(J)[0]) - Jref) <= 1e-12 * abs(Jref)
+
+
 def test_update_deterministic():
     say("update determinism")
     W, h, C, keep, rho = _case(31, 512, 1024, 8, 4096)
