@@ -56,6 +56,9 @@ constexpr int kTile = 32;                 // centroids per MFMA tile (A rows)
 constexpr int kChunkTiles = 8;            // tiles staged in LDS at once
 constexpr int kExactBlocks = 2048;
 constexpr int kSlotChunks = 8;            // codebooks of <= 8 chunks use per-slot tracking
+constexpr int kCminChunks = 8;            // chunks per workgroup of the chunk-minimum pass
+constexpr int kCminCap = 32768;           // flagged sub-vectors the chunk path takes at most
+constexpr int kCminListBlocks = 64;       // list blocks of the chunk-minimum grid (grid-stride)
 constexpr float kPadSq = 16384.0f;           // scaled c*c term of padding centroids
 
 constexpr int kMaxBlocks = 256;   // blocks of the codebook max reduction
@@ -514,6 +517,55 @@ __device__ __forceinline__ void search_epilogue(
 // with tile t-1's argmin updates between them (two accumulators alternate).
 // SLOT selects per-slot tracking (short codebooks) over per-tile tracking
 // with the best tile formed again at the end (long codebooks).
+// The general form's B operand of one sub-vector: the lanes of the lower
+// half hold the scaled omega*x parts (MFMA k-slots 0-7), those of the upper
+// half the scaled omega parts (k-slots 8-15), each split into two fp16
+// parts; S_sc = S * 2^shift_s is the sub-vector's sum omega x^2 at the same
+// scale (the rounding bound's S).
+__device__ __forceinline__ void general_operand(const float* __restrict__ X, const float* __restrict__ hcol,
+                                                const uint8_t* __restrict__ mask, int64_t s, int64_t nb, int d,
+                                                bool valid, int half, float cmax, h16x8& bh, h16x8& bl,
+                                                float& S_sc, int& shift_s)
+{
+    const bool vecX = d == 8 && ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(hcol)) & 15u) == 0;
+    float raw[8];
+    float S = 0.f;
+    float xs[8], ws_[8];
+    load_sub(X, hcol, mask, s, nb, d, valid, vecX, xs, ws_);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const float xv = xs[t], w = ws_[t];
+        S += w * xv * xv;
+        // lower half: omega*x (scale alpha*beta); upper half: omega
+        // (scale alpha*beta2*(beta/beta2))
+        raw[t] = half ? w : w * xv;
+    }
+    int e1, e2;
+    cb_exponents(cmax, e1, e2);
+    float mx = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) mx = fmaxf(mx, fabsf(raw[t]));
+    // alpha from the larger of the two halves
+    const int rel = half ? (e2 - e1) : 0;
+    int ex = -100000;
+    if (mx > 0.f) {
+        frexpf(mx, &ex);
+        ex += rel;
+    }
+    int en = max(ex, __shfl_xor(ex, 32));
+    if (en < -50000) en = 0;                                  // all weights zero
+    const int shift = (15 - en) + rel;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        _Float16 h, l;
+        split_h16(ldexpf(raw[t], shift), h, l);
+        bh[t] = h;
+        bl[t] = l;
+    }
+    shift_s = (15 - en) + (15 - e1);
+    S_sc = ldexpf(S, shift_s);
+}
+
 template <bool SLOT>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_assign_h16(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
@@ -540,48 +592,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
     const int64_t s = valid ? (list ? (int64_t)list[q] : q) : 0;
 
     // ---- the sub-vector's weights, scaled split B operand, S -----------
-    const bool vecX = d == 8 && ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(hcol)) & 15u) == 0;
     h16x8 bh, bl;
     float S_sc;
     int shift_s;   // S_sc = S * 2^shift_s: the sub-vector's scale alpha*beta
-    {
-        float raw[8];
-        float S = 0.f;
-        float xs[8], ws_[8];
-        load_sub(X, hcol, mask, s, nb, d, valid, vecX, xs, ws_);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float xv = xs[t], w = ws_[t];
-            S += w * xv * xv;
-            // lower half: omega*x (scale alpha*beta); upper half: omega
-            // (scale alpha*beta2*(beta/beta2))
-            raw[t] = half ? w : w * xv;
-        }
-        int e1, e2;
-        cb_exponents(*cmax, e1, e2);
-        float mx = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) mx = fmaxf(mx, fabsf(raw[t]));
-        // alpha from the larger of the two halves
-        const int rel = half ? (e2 - e1) : 0;
-        int ex = -100000;
-        if (mx > 0.f) {
-            frexpf(mx, &ex);
-            ex += rel;
-        }
-        int en = max(ex, __shfl_xor(ex, 32));
-        if (en < -50000) en = 0;                                  // all weights zero
-        const int shift = (15 - en) + rel;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            _Float16 h, l;
-            split_h16(ldexpf(raw[t], shift), h, l);
-            bh[t] = h;
-            bl[t] = l;
-        }
-        shift_s = (15 - en) + (15 - e1);
-        S_sc = ldexpf(S, shift_s);
-    }
+    general_operand(X, hcol, mask, s, nb, d, valid, half, *cmax, bh, bl, S_sc, shift_s);
 
     float b1 = __builtin_inff(), b2 = __builtin_inff();
     int kt1 = 0;
@@ -874,6 +888,139 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
     }
 }
 
+
+// Chunk minima of the flagged sub-vectors (long codebooks).  The general
+// three-MFMA form of the search over the flag list, entries [0, min(count,
+// cap)): workgroup = the next kSubPerBlock entries (grid-stride over x) times
+// kCminChunks consecutive chunks of the split codebook (y), staged through
+// LDS one chunk at a time with the next one loaded into registers.  Per
+// (entry, chunk): the smallest scaled score over the chunk's centroids (both
+// halves of the lane pair); per entry its S_sc, the scale of the rounding
+// bound err(e) = 48u (9 S_sc + 4 max(e, -S_sc)) + 1 that the search's
+// certification uses.
+__global__ __launch_bounds__(kWaves * 64) void k_assign_cmin(
+    const float* __restrict__ X, const float* __restrict__ hcol, const uint8_t* __restrict__ mask, int64_t nb, int d,
+    const uint4* __restrict__ P, const float* __restrict__ cmax, int nchunks, const int* __restrict__ list,
+    const int* __restrict__ list_count, int cap, float* __restrict__ cmin, float* __restrict__ ssc)
+{
+    constexpr int kChunkVec = kChunkTiles * 128;                 // uint4 per chunk
+    __shared__ uint4 lds[2][kChunkVec];
+    const int64_t count = min(*list_count, cap);
+    const int c0 = blockIdx.y * kCminChunks;
+    const int c1 = min(nchunks, c0 + kCminChunks);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int half = lane >> 5;
+    const int a_off = half * 32 + (lane & 31);
+    for (int64_t lb = blockIdx.x; lb * kSubPerBlock < count; lb += gridDim.x) {
+        const int64_t q = lb * kSubPerBlock + wave * kSubPerWave + (lane & 31);
+        const bool valid = q < count;
+        const int64_t s = valid ? (int64_t)list[q] : 0;
+        h16x8 bh, bl;
+        float S_sc;
+        int shift_s;
+        general_operand(X, hcol, mask, s, nb, d, valid, half, *cmax, bh, bl, S_sc, shift_s);
+        if (blockIdx.y == 0 && half == 0 && valid) ssc[q] = S_sc;
+        __syncthreads();                                          // the previous entries' last chunk is read
+        uint4 pre0 = P[(size_t)c0 * kChunkVec + threadIdx.x];
+        uint4 pre1 = P[(size_t)c0 * kChunkVec + threadIdx.x + kWaves * 64];
+        lds[0][threadIdx.x] = pre0;
+        lds[0][threadIdx.x + kWaves * 64] = pre1;
+        __syncthreads();
+        for (int c = c0; c < c1; ++c) {
+            if (c + 1 < c1) {
+                const uint4* src = P + (size_t)(c + 1) * kChunkVec;
+                pre0 = src[threadIdx.x];
+                pre1 = src[threadIdx.x + kWaves * 64];
+            }
+            const uint4* L = lds[(c - c0) & 1] + a_off;
+            float cm = __builtin_inff();
+#pragma unroll 2
+            for (int tt = 0; tt < kChunkTiles; ++tt) {
+                const uint4* A0 = L + tt * 128;
+                const h16x8 ah = __builtin_bit_cast(h16x8, A0[0]);
+                const h16x8 al = __builtin_bit_cast(h16x8, A0[64]);
+                f32x16 acc = {};
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc, 0, 0, 0);
+                cm = fminf(cm, tile_min(acc));
+            }
+            cm = fminf(cm, __shfl_xor(cm, 32));
+            if (half == 0 && valid) cmin[(size_t)q * nchunks + c] = cm;
+            if (c + 1 < c1) {
+                lds[(c + 1 - c0) & 1][threadIdx.x] = pre0;
+                lds[(c + 1 - c0) & 1][threadIdx.x + kWaves * 64] = pre1;
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Exact search of the flagged sub-vectors over their candidate chunks: one
+// wavefront per entry of [0, min(count, cap)) (grid-stride).  With gm the
+// smallest chunk minimum, chunk c is a candidate unless (cm_c - gm) >
+// err(cm_c) + err(gm), the search's certification applied to chunk minima:
+// every centroid of a non-candidate chunk has an exact score above the
+// sub-vector's exact minimum (a - err(a) grows with a), so no minimizer and
+// no tie is left out.  Every centroid of the candidate chunks is evaluated
+// in float64 in the direct form (terms in t order, exactly as a plain
+// float64 evaluation rounds) and the lexicographic (D, k) minimum is the
+// exact argmin with ties to the lowest index.
+__global__ __launch_bounds__(256) void k_exact_chunks(
+    const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
+    const uint8_t* __restrict__ mask, int64_t nb, int d, const float* __restrict__ C, int K, int nchunks,
+    const int* __restrict__ list, const int* __restrict__ list_count, int cap, const float* __restrict__ cmin,
+    const float* __restrict__ ssc, uint16_t* __restrict__ idx, float* __restrict__ dist)
+{
+    const int64_t count = min(*list_count, cap);
+    const int lane = threadIdx.x & 63;
+    const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const float u = 5.9604644775390625e-8f;   // 2^-24
+    for (int64_t q = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); q < count; q += waves) {
+        const int64_t s = list[q];
+        const float S = ssc[q];
+        const float* cm = cmin + (size_t)q * nchunks;
+        float gm = __builtin_inff();
+        for (int c = lane; c < nchunks; c += 64) gm = fminf(gm, cm[c]);
+        for (int off = 32; off > 0; off >>= 1) gm = fminf(gm, __shfl_xor(gm, off));
+        const float eg = 48.f * u * (9.f * S + 4.f * fmaxf(gm, -S)) + 1.f;
+        double om[8];
+        float x[8];
+        exact_weights(hcol, rho, mask, s, nb, d, om);
+        for (int t = 0; t < d; ++t) x[t] = X[s * d + t];
+        double bd = __builtin_inf();
+        int bk = K;
+        for (int cb = 0; cb < nchunks; cb += 64) {
+            bool cand = false;
+            if (cb + lane < nchunks) {
+                const float v = cm[cb + lane];
+                const float ev = 48.f * u * (9.f * S + 4.f * fmaxf(v, -S)) + 1.f;
+                cand = !((v - gm) > (ev + eg));               // NaN keeps the chunk
+            }
+            unsigned long long ball = __ballot(cand);
+            while (ball) {
+                const int c = cb + __ffsll((long long)ball) - 1;
+                ball &= ball - 1ull;
+                const int kend = min(K, (c + 1) * kChunkTiles * kTile);
+                for (int k = c * kChunkTiles * kTile + lane; k < kend; k += 64) {
+                    const double D = exact_dist(om, x, C + (size_t)k * d, d);
+                    if (D < bd || (D == bd && k < bk)) { bd = D; bk = k; }
+                }
+            }
+        }
+        for (int off = 32; off > 0; off >>= 1) {
+            const double od = __shfl_xor(bd, off);
+            const int ok = __shfl_xor(bk, off);
+            if (od < bd || (od == bd && ok < bk)) { bd = od; bk = ok; }
+        }
+        if (lane == 0) {
+            idx[s] = (uint16_t)bk;
+            if (dist) dist[s] = (float)bd;
+        }
+    }
+}
+
 // Exact re-search of the flagged sub-vectors: one wavefront per flagged
 // sub-vector (grid-stride), its lanes striding over the codebook.  For each
 // centroid the float32 expanded form e~ (a fused multiply-add chain over the
@@ -888,13 +1035,13 @@ __global__ __launch_bounds__(256) void k_assign_exact(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
     const uint8_t* __restrict__ mask, int64_t nb, int d, const float* __restrict__ C, int K,
     const int* __restrict__ flag_count, const int* __restrict__ flag_list,
-    uint16_t* __restrict__ idx, float* __restrict__ dist, int vecC)
+    uint16_t* __restrict__ idx, float* __restrict__ dist, int vecC, int start)
 {
     const int n = *flag_count;
     const int lane = threadIdx.x & 63;
     const float u = 5.9604644775390625e-8f;
     const int waves = gridDim.x * (blockDim.x >> 6);
-    for (int f = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); f < n; f += waves) {
+    for (int f = start + blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); f < n; f += waves) {
         const int64_t s = flag_list[f];
         const int64_t i = s / nb, b = s - i * nb;
         const unsigned mb = mask ? mask[s] : 0u;
@@ -1063,10 +1210,36 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
         }
         }
     }
+    // Long codebooks: the first flagged sub-vectors (as many as the workspace
+    // holds beyond its required size, at most kCminCap) take the chunk path:
+    // chunk minima on the matrix cores, then float64 over the candidate
+    // chunks only.  The rest (or all, without room) scan the whole codebook.
+    const int nch = Kpad / kChunkK;
+    int cap = 0;
+    if (nch > kSlotChunks) {
+        const size_t per = (size_t)nch * sizeof(float) + sizeof(float);
+        const size_t room = cv.cap > cv.used + 4 * kAlign ? cv.cap - cv.used - 4 * kAlign : 0;
+        cap = (int)std::min<size_t>((size_t)kCminCap, std::min<size_t>(room / per, (size_t)n_sub));
+        if (cap < kSubPerBlock) cap = 0;
+    }
+    if (cap > 0) {
+        float* cmin = cv.take<float>((size_t)cap * nch);
+        float* ssc = cv.take<float>((size_t)cap);
+        if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_assign: workspace too small");
+        const dim3 gc((unsigned)std::min<int64_t>(kCminListBlocks, (cap + kSubPerBlock - 1) / kSubPerBlock),
+                      (unsigned)((nch + kCminChunks - 1) / kCminChunks));
+        hipLaunchKernelGGL(k_assign_cmin, gc, dim3(kWaves * 64), 0, st, X, hcol, mask, nb, d, P, cmax, nch, flag_list,
+                           flag_count, cap, cmin, ssc);
+        VQ_LAUNCHED("k_assign_cmin");
+        hipLaunchKernelGGL(k_exact_chunks, dim3((unsigned)std::min<int64_t>((cap + 3) / 4, kExactBlocks)), dim3(256),
+                           0, st, X, hcol, rho, mask, nb, d, C, K, nch, flag_list, flag_count, cap, cmin, ssc, idx,
+                           dist);
+        VQ_LAUNCHED("k_exact_chunks");
+    }
     const unsigned gx = (unsigned)std::min<int64_t>((n_sub + 3) / 4, kExactBlocks);
     const int vecC = (d == 8 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0) ? 1 : 0;
     hipLaunchKernelGGL(k_assign_exact, dim3(gx), dim3(256), 0, st, X, hcol, rho, mask, nb, d, C, K,
-                       flag_count, flag_list, idx, dist, vecC);
+                       flag_count, flag_list, idx, dist, vecC, cap);
     VQ_LAUNCHED("k_assign_exact");
     return VQ_OK;
 }

@@ -129,6 +129,41 @@ def test_assign_exact_ties_go_to_lowest_index():
     assert vq.assign_exact_count(ws, M * N // d, K) > 0   # exact ties cannot be certified
 
 
+@pytest.mark.parametrize("case", ["some-ties", "all-ties"])
+def test_assign_long_codebook_ties_go_to_lowest_index(case):
+    # a codebook longer than 2048 with duplicated rows, and sub-vectors equal
+    # to codebook rows: exact ties cannot be certified, so the re-search takes
+    # them (the chunk-minimum path for up to 32768 of them, the full scan for
+    # the rest when "all-ties" floods the list with 65536)
+    say("assign long-codebook ties", case)
+    g = np.random.default_rng([7, len(case)])
+    M, N, d, K = 512, 1024, 8, 4096
+    n_sub = M * N // d
+    C = g.standard_normal((K, d)).astype(np.float32)
+    if case == "some-ties":
+        C[2900] = C[5]
+        C[1500] = C[700]
+        C[4095] = C[0]
+        rows = g.integers(0, K, size=n_sub)
+        rows[: n_sub // 4] = g.choice([5, 700, 0, 2900, 1500, 4095], size=n_sub // 4)
+    else:
+        C[1::2] = C[0::2]                       # every centroid twice
+        rows = g.integers(0, K, size=n_sub)
+    X = C[rows].reshape(M, N)
+    h = (0.5 + g.random(N)).astype(np.float32)
+    ref, ref_d = oracle.assign(X, h, None, None, d, C)
+    ws = vq.workspace(M, N, d, K)
+    idx, dist = vq.assign(dev(X), dev(h), None, None, d, dev(C), ws, want_dist=True)
+    assert bits_equal(host(idx), ref), np.flatnonzero(host(idx) != ref)[:10]
+    assert bits_equal(host(dist), ref_d.astype(np.float32))
+    got = host(idx)
+    if case == "some-ties":
+        assert not np.any(np.isin(got, [2900, 1500, 4095]))
+    else:
+        assert not np.any(got % 2 == 1)
+        assert vq.assign_exact_count(ws, n_sub, K) > 32768
+
+
 def test_assign_deterministic_and_mostly_certified():
     say("assign determinism")
     W, h, C, keep, rho = _case(21, 256, 512, 8, 512)
