@@ -977,6 +977,7 @@ __global__ __launch_bounds__(256) void k_exact_chunks(
     const int lane = threadIdx.x & 63;
     const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
     const float u = 5.9604644775390625e-8f;   // 2^-24
+    const bool vecC = d == 8 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
     for (int64_t q = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); q < count; q += waves) {
         const int64_t s = list[q];
         const float S = ssc[q];
@@ -1002,10 +1003,33 @@ __global__ __launch_bounds__(256) void k_exact_chunks(
             while (ball) {
                 const int c = cb + __ffsll((long long)ball) - 1;
                 ball &= ball - 1ull;
-                const int kend = min(K, (c + 1) * kChunkTiles * kTile);
-                for (int k = c * kChunkTiles * kTile + lane; k < kend; k += 64) {
-                    const double D = exact_dist(om, x, C + (size_t)k * d, d);
-                    if (D < bd || (D == bd && k < bk)) { bd = D; bk = k; }
+                const int kbeg = c * kChunkTiles * kTile;
+                const int kend = min(K, kbeg + kChunkTiles * kTile);
+                constexpr int kPerLane = kChunkTiles * kTile / 64;   // 4 centroids of the chunk per lane
+                if (vecC) {
+                    // the lane's rows are all requested before any is used
+                    float cr[kPerLane][8];
+#pragma unroll
+                    for (int j = 0; j < kPerLane; ++j) {
+                        const int k = kbeg + lane + 64 * j;
+                        const int kk = k < kend ? k : kbeg;
+                        const float4 ca = reinterpret_cast<const float4*>(C)[(size_t)kk * 2];
+                        const float4 cb4 = reinterpret_cast<const float4*>(C)[(size_t)kk * 2 + 1];
+                        cr[j][0] = ca.x; cr[j][1] = ca.y; cr[j][2] = ca.z; cr[j][3] = ca.w;
+                        cr[j][4] = cb4.x; cr[j][5] = cb4.y; cr[j][6] = cb4.z; cr[j][7] = cb4.w;
+                    }
+#pragma unroll
+                    for (int j = 0; j < kPerLane; ++j) {
+                        const int k = kbeg + lane + 64 * j;
+                        if (k >= kend) continue;
+                        const double D = exact_dist(om, x, cr[j], d);
+                        if (D < bd || (D == bd && k < bk)) { bd = D; bk = k; }
+                    }
+                } else {
+                    for (int k = kbeg + lane; k < kend; k += 64) {
+                        const double D = exact_dist(om, x, C + (size_t)k * d, d);
+                        if (D < bd || (D == bd && k < bk)) { bd = D; bk = k; }
+                    }
                 }
             }
         }
