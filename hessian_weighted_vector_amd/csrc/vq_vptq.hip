@@ -20,16 +20,17 @@
 // kept transposed too; they are transposed back at the end.
 //
 // V = 8 (C 16-byte aligned, M % 4 == 0): one launch per column,
-//   k_col_step_h16 finishes column n-1 (its winner, value and error, the
-//                  error's share of the block's later columns) and searches
-//                  column n on the fp16 matrix cores with split operands
-//                  (expanded form, the codebook prepared once per call by
-//                  k_vp_absmax and k_vp_prep); workgroups split K, and each
-//                  sub-vector's best and second-best scores meet in packed
-//                  64-bit atomicMin keys of (score bits, index);
-//   k_col_exact    certifies each best against a rounding bound and searches
-//                  the rest again exactly in float64, split over K;
-//   k_col_last     finishes the block's last column.
+//   k_col_step_h16 decides column n-1 (each best certified against a rounding
+//                  bound, the rest searched again exactly in float64 over the
+//                  chunks that can hold the nearest row) and finishes it (its
+//                  value and error, the error's share of the block's later
+//                  columns), then searches column n on the fp16 matrix cores
+//                  with split operands (expanded form, the codebook prepared
+//                  once per call by k_vp_absmax and k_vp_prep); workgroups
+//                  split K, and each sub-vector's best and second-best scores
+//                  meet in packed 64-bit atomicMin keys of (score bits,
+//                  index), each chunk's best score kept beside them;
+//   k_col_last     decides and finishes the block's last column.
 // Other V, or a codebook that is not 16-byte aligned, two launches per column:
 //   k_col_assign   the direct form in float64 on the vector units, one result
 //                  per 256-centroid chunk;
@@ -177,10 +178,10 @@ __device__ inline float unsortable(unsigned v)
 // best's has |c_k| <= R = |x| + sqrt(D_best), so when best - second exceeds
 // twice that bound at |c_k| = R the best is the exact nearest row, and
 // float64 rounding of the direct form (relative 2^-49) cannot reorder it.
-// k_col_exact makes this check and searches the sub-vectors that fail again
-// over the whole codebook in float64 (the direct form, terms in t order), each
-// workgroup over its 512-centroid chunk, and the last of them merges the
-// chunks in order (lowest index on ties).
+// col_certify makes this check at the start of the next launch and
+// col_resolve searches the sub-vectors that fail again in float64 (the direct
+// form, terms in t order, lowest index on ties) over the chunks that can hold
+// the nearest row.
 constexpr int kVpChunk = 512;        // centroids per workgroup (prepared codebook is padded to whole chunks)
 constexpr int kHnShift = 9;          // hn 2^(2 sc) < 2^22, its pieces below 2^13
 constexpr int kStepRows = 128;       // sub-vectors per workgroup of the column step (4 waves x 32)
@@ -257,84 +258,294 @@ __global__ __launch_bounds__(256) void k_vp_prep(const float* __restrict__ C, in
     hn[k] = p;
 }
 
+// Per-workgroup state of one column's decisions (V = 8 path): the
+// uncertified decisions of each wavefront (a slot per lane of the lower half),
+// and the exact winners found for them with their codebook rows.
+struct ColDecide {
+    int wcnt[4];                     // uncertified decisions per wavefront
+    int flag[kStepRows];             // slot wave * 32 + i: the local sub-vector
+    int sh[kStepRows];               // its score scale exponent sc + sx
+    double sa[kStepRows];            // its computed best score
+    double bnd[kStepRows];           // its rounding bound
+    int dec[kStepRows];              // exact winner, by local sub-vector
+    float4 row[kStepRows][2];        // the winner's codebook row, by local sub-vector
+};
+
+// A column's decisions for the workgroup's kStepRows sub-vectors, in two
+// parts around a workgroup barrier that the caller places between them
+// (lanes l and l + 32 of a wavefront hold the same sub-vector).
+//
+// col_certify: the lane's winner from the column's keys, certified as
+// described above; an uncertified one is listed in sd (lower half-wave).
+// x: the lane's sub-vector of column p in float64 (zero beyond nv).
+//
+// col_resolve (after the barrier): the listed sub-vectors are searched again
+// exactly in float64 (direct form, terms in t order, the lowest index among
+// equal distances), one wavefront each, over the candidate chunks only:
+// every workgroup of the column wrote its chunk's best score per sub-vector
+// (cbest), and a chunk whose best lies more than twice the bound below the
+// column's best cannot hold a centroid at least as near as the computed
+// winner (its exact scores are below the winner's exact score), so no
+// minimizer and no tie is left out.  Every workgroup of the same rows makes
+// the same decisions from the same data.  Returns the number of listed
+// sub-vectors; kw and qv then hold the lane's winner and its row.
+struct ColCert {
+    bool ok;
+    int kw;
+    float qv[8];
+};
+
+__device__ inline ColCert col_certify(ColDecide& sd, int nv, int64_t p, const float* __restrict__ C,
+                                      const unsigned long long* __restrict__ keys, float cmv, const double (&x)[8])
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int jl = lane & 31, half = lane >> 5;
+    const int local = wave * 32 + jl;
+    const int j = blockIdx.x * kStepRows + local;
+    ColCert r;
+    r.ok = true;
+    r.kw = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r.qv[t] = 0.0f;
+    // the wave's scale, as the search of column p formed it
+    float mx = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) mx = fmaxf(mx, fabsf((float)x[t]));
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const int sc = vp_scale_exp(cmv);
+    const int sx = min(vp_scale_exp(mx), sc + 15 - kHnShift);
+    const bool no_norm = kHnShift + sx - sc < -24;       // the search ran without the norm term
+    double sA = 0.0, bound = 0.0;
+    if (j < nv) {
+        unsigned long long a1 = ~0ull, a2 = ~0ull, bmin = ~0ull;
+#pragma unroll
+        for (int q = 0; q < kKeySlots; ++q) {
+            const unsigned long long ka = keys[key_at(nv, q, 0, p, j)];
+            const unsigned long long kb = keys[key_at(nv, q, 1, p, j)];
+            if (ka < a1) { a2 = a1; a1 = ka; } else if (ka < a2) { a2 = ka; }
+            bmin = kb < bmin ? kb : bmin;
+        }
+        const unsigned long long k2 = a2 < bmin ? a2 : bmin;
+        r.kw = (int)(a1 & 0xFFFFFFFFull);
+        const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)r.kw;
+        const float4 ca = c4[0], cb = c4[1];
+        r.qv[0] = ca.x; r.qv[1] = ca.y; r.qv[2] = ca.z; r.qv[3] = ca.w;
+        r.qv[4] = cb.x; r.qv[5] = cb.y; r.qv[6] = cb.z; r.qv[7] = cb.w;
+        if (k2 != ~0ull) {
+            sA = -(double)unsortable((unsigned)(a1 >> 32));
+            const double sB = -(double)unsortable((unsigned)(k2 >> 32));
+            double nx2 = 0.0, db = 0.0;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                nx2 += x[t] * x[t];
+                const double df = x[t] - (double)r.qv[t];
+                db += df * df;
+            }
+            const double nx = sqrt(nx2) * (1.0 + 0x1p-40);
+            const double R = nx + sqrt(db) * (1.0 + 0x1p-40);
+            bound = 0x1p-18 * (1.25 * R * nx + 0.3125 * R * R) + ldexp(0x1p-8, -(sc + sx)) + 0x1p-45 * (nx2 + db);
+            if (no_norm) bound += 0.5 * R * R;
+            const double gap = ldexp(sA - sB, -(sc + sx));
+            r.ok = gap > 2.0 * bound;                    // false also for NaN
+        }
+    }
+    const unsigned long long fm = __ballot(half == 0 && !r.ok);
+    if (half == 0 && !r.ok) {
+        const int slot = wave * 32 + __popcll(fm & ((1ull << lane) - 1));
+        sd.flag[slot] = local;
+        sd.sh[slot] = sc + sx;
+        sd.sa[slot] = sA;
+        sd.bnd[slot] = bound;
+    }
+    if (lane == 0) sd.wcnt[wave] = __popcll(fm);
+    return r;
+}
+
+__device__ inline int col_resolve(ColDecide& sd, int nv, int64_t p, const double* __restrict__ xcol,
+                                  const float* __restrict__ C, int K, const float* __restrict__ cbest, int nch,
+                                  ColCert& r)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int total = sd.wcnt[0] + sd.wcnt[1] + sd.wcnt[2] + sd.wcnt[3];
+    if (total == 0) return 0;
+    for (int ww = 0; ww < 4; ++ww) {
+        for (int i = wave; i < sd.wcnt[ww]; i += 4) {
+            const int slot = ww * 32 + i;
+            const int lj = sd.flag[slot];
+            const int jj = blockIdx.x * kStepRows + lj;
+            const double sa = sd.sa[slot], twob = 2.0 * sd.bnd[slot];
+            const int sh = sd.sh[slot];
+            double xv[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) xv[t] = xcol[(size_t)jj * 8 + t];
+            double bd = __builtin_inf();
+            int bk = 0x7FFFFFFF;
+            float4 ra = make_float4(0.0f, 0.0f, 0.0f, 0.0f), rb = ra;
+            for (int c0 = 0; c0 < nch; c0 += 64) {
+                bool cand = false;
+                if (c0 + lane < nch) {
+                    const float cbv = cbest[((size_t)(p & 1) * nch + c0 + lane) * nv + jj];
+                    cand = !(ldexp(sa - (double)cbv, -sh) > twob);
+                }
+                unsigned long long m = __ballot(cand);
+                while (m) {
+                    const int cc = c0 + __ffsll((long long)m) - 1;
+                    m &= m - 1;
+                    const int k0 = cc * kVpChunk;
+                    const int kn = K - k0 < kVpChunk ? K - k0 : kVpChunk;
+                    for (int q = lane; q < kn; q += 64) {
+                        const int k = k0 + q;
+                        const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)k;
+                        const float4 ca = c4[0], cb = c4[1];
+                        const float cv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+                        double dist = 0.0;
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) {
+                            const double df = xv[t] - (double)cv[t];
+                            dist += df * df;
+                        }
+                        if (dist < bd || (dist == bd && k < bk)) {
+                            bd = dist;
+                            bk = k;
+                            ra = ca;
+                            rb = cb;
+                        }
+                    }
+                }
+            }
+            // the smallest (distance, index) of the wavefront; its lane
+            // writes the winner and its row
+            double md = bd;
+            int mk = bk;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const double od = __shfl_xor(md, o);
+                const int oi = __shfl_xor(mk, o);
+                if (od < md || (od == md && oi < mk)) { md = od; mk = oi; }
+            }
+            if (bk == mk && bd == md) {                  // one lane: indices are distinct
+                sd.dec[lj] = mk;
+                sd.row[lj][0] = ra;
+                sd.row[lj][1] = rb;
+            }
+        }
+    }
+    __syncthreads();
+    if (!r.ok) {
+        const int local = wave * 32 + (lane & 31);
+        r.kw = sd.dec[local];
+        const float4 ca = sd.row[local][0], cb = sd.row[local][1];
+        r.qv[0] = ca.x; r.qv[1] = ca.y; r.qv[2] = ca.z; r.qv[3] = ca.w;
+        r.qv[4] = cb.x; r.qv[5] = cb.y; r.qv[6] = cb.z; r.qv[7] = cb.w;
+    }
+    return total;
+}
+
+// Column n (V = 8 path).  Grid: x over row blocks of kStepRows sub-vectors,
+// y over kVpChunk-centroid chunks.  For n past the block's first column it
+// first decides column n-1 (col_certify, col_resolve), then finishes it:
+// value, error, the error's share of column n (every workgroup of these rows
+// forms the same values); the first chunk's workgroups write the outputs.
+// Then it searches column n over its chunk, and pushes column n-1's error
+// into the block's later columns, split over the workgroups of these rows by
+// column (no later read in this launch).  Loads are issued early and their
+// registers used late: the chunk is written to LDS only after the keys and
+// the winners' rows are requested, and the later columns' values are loaded
+// before the key atomics.
 __global__ __launch_bounds__(256) void k_col_step_h16(
     double* __restrict__ Wt, int64_t M, int nv, int64_t n, int64_t s, int64_t s_end, const float* __restrict__ C,
-    const float* __restrict__ U, int64_t N, unsigned long long* __restrict__ keys, const int* __restrict__ win,
-    const float* __restrict__ qrow, double* __restrict__ Xc, uint16_t* __restrict__ idx, float* __restrict__ Wht,
+    const float* __restrict__ U, int64_t N, unsigned long long* __restrict__ keys, float* __restrict__ cbest,
+    int nch, double* __restrict__ Xc, uint16_t* __restrict__ idx, float* __restrict__ Wht,
     double* __restrict__ Et, const vp_h16x8* __restrict__ Phi, const vp_h16x8* __restrict__ Plo,
-    const vp_h16x8* __restrict__ Phn, const float* __restrict__ cmax, int K)
+    const vp_h16x8* __restrict__ Phn, const float* __restrict__ cmax, int K, int* __restrict__ fl_total)
 {
+    static_assert(kVpChunk == 2 * 256, "two prepared centroids per thread");
     __shared__ vp_h16x8 L[3][kVpChunk];
+    __shared__ float4 Lt[4][4][64];                      // per lane: the 16 scores of its best tile so far
+    __shared__ ColDecide sd;
     const int k0 = blockIdx.y * kVpChunk;
     const int kn = K - k0 < kVpChunk ? K - k0 : kVpChunk;
-    for (int q = threadIdx.x; q < kVpChunk; q += 256) {
-        L[0][q] = Phi[k0 + q];
-        L[1][q] = Plo[k0 + q];
-        L[2][q] = Phn[k0 + q];
-    }
+    // the chunk's prepared rows, two centroids per thread (staged in LDS
+    // later, after the decision's loads are issued)
+    const int ka = k0 + threadIdx.x, kb = ka + 256;
+    const vp_h16x8 fa0 = Phi[ka], fa1 = Plo[ka], fa2 = Phn[ka];
+    const vp_h16x8 fb0 = Phi[kb], fb1 = Plo[kb], fb2 = Phn[kb];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j0 = (blockIdx.x * 4 + wave) * 32;
     const int jl = lane & 31, half = lane >> 5;
     const int j = j0 + jl;
     const bool active = j0 < nv;                         // the wave holds sub-vectors
-    double x64[8], e[8];
+    const float cmv = *cmax;
+    double x64[8], e[8], w[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         x64[t] = 0.0;
         e[t] = 0.0;
+        w[t] = 0.0;
     }
-    bool later = false;                                  // the block's later columns get e (after the search)
     if (j < nv) {
         const double2* w2 = reinterpret_cast<const double2*>(Wt + n * M) + 4 * (size_t)j;
-        double w[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const double2 v2 = w2[q];
             w[2 * q] = v2.x;
             w[2 * q + 1] = v2.y;
         }
-        if (n > s) {
-            // column n-1 of the block: its winner, value, error; the error's
-            // share of column n is applied here (every workgroup of these rows
-            // forms the same values), its share of the block's later columns
-            // is split over the workgroups of these rows by column
-            const int64_t p = n - 1;
-            const int kp = win[(size_t)(p & 1) * nv + j];
-            // the winner's row, written beside its index by the column's decision
-            const float4* q4 = reinterpret_cast<const float4*>(qrow) + ((size_t)(p & 1) * nv + j) * 2;
-            const float4 ca = q4[0], cb = q4[1];
-            const float qv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
-            const double* xp = Xc + (size_t)(p & 1) * M + (size_t)j * 8;
-            const double unn = (double)U[p * N + p], un = (double)U[p * N + n];
+    }
+    auto stage = [&]() {
+        const int q = threadIdx.x;
+        L[0][q] = fa0;
+        L[1][q] = fa1;
+        L[2][q] = fa2;
+        L[0][q + 256] = fb0;
+        L[1][q + 256] = fb1;
+        L[2][q + 256] = fb2;
+    };
+    bool later = false;                                  // the block's later columns get e (after the search)
+    if (n > s) {
+        const int64_t p = n - 1;
+        const double* xcol = Xc + (size_t)(p & 1) * M;
+        double xp[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) xp[t] = j < nv ? xcol[(size_t)j * 8 + t] : 0.0;
+        const double unn = (double)U[p * N + p], un = (double)U[p * N + n];
+        ColCert r = col_certify(sd, nv, p, C, keys, cmv, xp);
+        stage();
+        __syncthreads();
+        const int nfl = col_resolve(sd, nv, p, xcol, C, K, cbest, nch, r);
+        if (j < nv) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                e[t] = (xp[t] - (double)qv[t]) / unn;
+                e[t] = (xp[t] - (double)r.qv[t]) / unn;
                 x64[t] = w[t] - e[t] * un;
             }
             if (blockIdx.y == 0 && half == 0) {
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
-                    Wht[p * M + (int64_t)j * 8 + t] = qv[t];
+                    Wht[p * M + (int64_t)j * 8 + t] = r.qv[t];
                     Et[p * M + (int64_t)j * 8 + t] = e[t];
                 }
-                idx[p * nv + j] = (uint16_t)kp;
+                idx[p * nv + j] = (uint16_t)r.kw;
             }
             later = true;
-        } else {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) x64[t] = w[t];
         }
-        if (blockIdx.y == 0 && half == 0) {
+        if (blockIdx.y == 0 && threadIdx.x == 0 && nfl > 0) atomicAdd(fl_total, nfl);
+    } else {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) Xc[(size_t)(n & 1) * M + (size_t)j * 8 + t] = x64[t];
+        for (int t = 0; t < 8; ++t) x64[t] = w[t];
+        stage();
+        __syncthreads();
+    }
+    if (blockIdx.y == 0 && half == 0 && j < nv) {
 #pragma unroll
-            for (int q = 0; q < kKeySlots; ++q) {
-                keys[key_at(nv, q, 0, n + 1, j)] = ~0ull;
-                keys[key_at(nv, q, 1, n + 1, j)] = ~0ull;
-            }
+        for (int t = 0; t < 8; ++t) Xc[(size_t)(n & 1) * M + (size_t)j * 8 + t] = x64[t];
+#pragma unroll
+        for (int q = 0; q < kKeySlots; ++q) {
+            keys[key_at(nv, q, 0, n + 1, j)] = ~0ull;
+            keys[key_at(nv, q, 1, n + 1, j)] = ~0ull;
         }
     }
-    __syncthreads();
     // the wave's scale (both halves hold the same 32 sub-vectors)
     float xv[8];
     float mx = 0.0f;
@@ -345,7 +556,7 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
     }
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    const int sc = vp_scale_exp(*cmax);
+    const int sc = vp_scale_exp(cmv);
     const int sx = min(vp_scale_exp(mx), sc + 15 - kHnShift);
     const int eb = kHnShift + sx - sc;                  // <= 15: b is a finite fp16
     const _Float16 b = eb >= -24 ? (_Float16)(-ldexpf(1.0f, eb)) : (_Float16)0.0f;
@@ -363,43 +574,77 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
         const vp_h16x8* A1 = L[half ? 1 : 0];
         const vp_h16x8* A2 = L[half ? 2 : 0];
         const int ntiles = (kn + 31) / 32;
-        // running best and second best of the lane's scores; the best's index
+        // per tile its largest score: the lane's best and second-best tile
+        // maxima and the best's tile, whose 16 scores the lane parks in its
+        // own LDS slots whenever a tile improves on the best
+        float m1 = -__builtin_inff(), m2 = -__builtin_inff();
+        int bt = 0;
         auto scan = [&](vp_f32x16 acc, int tb) {
             if (tb + 32 > kn) {                          // the chunk's last, partial tile
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (tb + (r >> 2) * 8 + half * 4 + (r & 3) >= kn) acc[r] = -__builtin_inff();
             }
-            float m = acc[0], m2 = -__builtin_inff();
+            float m = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
 #pragma unroll
-            for (int r = 1; r < 16; ++r) {
-                m2 = __builtin_amdgcn_fmed3f(m, m2, acc[r]);
-                m = fmaxf(m, acc[r]);
+            for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, acc[r]), acc[r + 1]);
+            m = fmaxf(m, acc[15]);
+            m2 = __builtin_amdgcn_fmed3f(m1, m2, m);
+            if (m > m1) {
+                bt = tb;
+                Lt[wave][0][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                Lt[wave][1][lane] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+                Lt[wave][2][lane] = make_float4(acc[8], acc[9], acc[10], acc[11]);
+                Lt[wave][3][lane] = make_float4(acc[12], acc[13], acc[14], acc[15]);
             }
-            sec = fmaxf(__builtin_amdgcn_fmed3f(best, sec, m), m2);
-            if (m > best) {
-                int rr = 0;
-#pragma unroll
-                for (int r = 15; r >= 0; --r)
-                    if (acc[r] == m) rr = r;
-                best = m;
-                bi = tb + (rr >> 2) * 8 + half * 4 + (rr & 3);
-            }
+            m1 = fmaxf(m1, m);
         };
         const vp_f32x16 zero = {};
+        // the operands of the next tile pair are read before the current
+        // pair's scores are scanned
+        vp_h16x8 p0 = A1[jl], p1 = A1[32 + jl], q0 = A2[jl], q1 = A2[32 + jl];
         int tb = 0;
         for (; tb + 32 < ntiles * 32; tb += 64) {
-            vp_f32x16 a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[tb + jl], bh, zero, 0, 0, 0);
-            vp_f32x16 a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[tb + 32 + jl], bh, zero, 0, 0, 0);
-            a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A2[tb + jl], b2, a0, 0, 0, 0);
-            a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A2[tb + 32 + jl], b2, a1, 0, 0, 0);
+            vp_f32x16 a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(p0, bh, zero, 0, 0, 0);
+            vp_f32x16 a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(p1, bh, zero, 0, 0, 0);
+            a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(q0, b2, a0, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(q1, b2, a1, 0, 0, 0);
+            if (tb + 64 < kVpChunk) {
+                p0 = A1[tb + 64 + jl];
+                p1 = A1[tb + 96 + jl];
+                q0 = A2[tb + 64 + jl];
+                q1 = A2[tb + 96 + jl];
+            }
             scan(a0, tb);
             scan(a1, tb + 32);
         }
         if (tb < ntiles * 32) {
-            vp_f32x16 a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[tb + jl], bh, zero, 0, 0, 0);
-            a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A2[tb + jl], b2, a0, 0, 0, 0);
+            vp_f32x16 a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(p0, bh, zero, 0, 0, 0);
+            a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(q0, b2, a0, 0, 0, 0);
             scan(a0, tb);
+        }
+        // the best tile's scores: the lane's best, its index (lowest on
+        // ties) and the tile's own second best; the other tiles' maxima give
+        // the rest of the second best
+        if (m1 > -__builtin_inff()) {
+            const float4 v0 = Lt[wave][0][lane], v1 = Lt[wave][1][lane];
+            const float4 v2 = Lt[wave][2][lane], v3 = Lt[wave][3][lane];
+            const float rf[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
+                                  v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+            int rr = 0, ties = 0;
+            float t2 = -__builtin_inff();                // largest score below the best
+#pragma unroll
+            for (int r = 15; r >= 0; --r) {
+                if (rf[r] == m1) {
+                    rr = r;
+                    ++ties;
+                } else {
+                    t2 = fmaxf(t2, rf[r]);
+                }
+            }
+            best = m1;
+            sec = fmaxf(m2, ties > 1 ? m1 : t2);
+            bi = bt + (rr >> 2) * 8 + half * 4 + (rr & 3);
         }
         // the two halves of the sub-vector's centroid rows: best with the
         // lower index among equal scores, second best of the four values
@@ -408,219 +653,74 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
         const float lo = fminf(best, ob);
         sec = fmaxf(fmaxf(sec, os), lo);
         if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
-        if (half == 0 && j < nv) {
-            const int slot = blockIdx.y % kKeySlots;
-            const unsigned long long kb_ = ((unsigned long long)sortable(-best + 0.0f) << 32) | (unsigned)(k0 + bi);
-            const unsigned long long ks_ = ((unsigned long long)sortable(-sec + 0.0f) << 32) | 0xFFFFFFFFull;
-            const unsigned long long old = atomicMin(&keys[key_at(nv, slot, 0, n, j)], kb_);
-            const unsigned long long lost = old > kb_ ? old : kb_;
-            atomicMin(&keys[key_at(nv, slot, 1, n, j)], lost < ks_ ? lost : ks_);
-        }
     }
     // column n-1's error into the block's later columns, split over the
-    // workgroups of these rows by column (no later read in this launch)
-    if (later) {
-        const int64_t p = n - 1;
-        for (int64_t r = n + 1 + blockIdx.y; r < s_end; r += gridDim.y) {
-            const double u = (double)U[p * N + r];
-            double* wr = Wt + r * M + (int64_t)j * 8 + half * 4;
+    // workgroups of these rows by column (no later read in this launch); the
+    // first row's values are requested before the key atomics
+    const int64_t p = n - 1;
+    int64_t r = n + 1 + blockIdx.y;
+    const bool upd = later && r < s_end;
+    double u = 0.0, wv[4] = {0.0, 0.0, 0.0, 0.0};
+    if (upd) {
+        u = (double)U[p * N + r];
+        const double* wr = Wt + r * M + (int64_t)j * 8 + half * 4;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) wr[t] = wr[t] - e[half * 4 + t] * u;
+        for (int t = 0; t < 4; ++t) wv[t] = wr[t];
+    }
+    if (active && half == 0 && j < nv) {
+        cbest[((size_t)(n & 1) * nch + blockIdx.y) * nv + j] = fmaxf(best, sec);
+        const int slot = blockIdx.y % kKeySlots;
+        const unsigned long long kb_ = ((unsigned long long)sortable(-best + 0.0f) << 32) | (unsigned)(k0 + bi);
+        const unsigned long long ks_ = ((unsigned long long)sortable(-sec + 0.0f) << 32) | 0xFFFFFFFFull;
+        const unsigned long long old = atomicMin(&keys[key_at(nv, slot, 0, n, j)], kb_);
+        const unsigned long long lost = old > kb_ ? old : kb_;
+        atomicMin(&keys[key_at(nv, slot, 1, n, j)], lost < ks_ ? lost : ks_);
+    }
+    if (upd) {
+        double* wr = Wt + r * M + (int64_t)j * 8 + half * 4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) wr[t] = wv[t] - e[half * 4 + t] * u;
+        for (r += gridDim.y; r < s_end; r += gridDim.y) {
+            const double ur = (double)U[p * N + r];
+            double* wq = Wt + r * M + (int64_t)j * 8 + half * 4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) wq[t] = wq[t] - e[half * 4 + t] * ur;
         }
     }
 }
 
-// Column n's winners (V = 8 path).  Grid: x over row blocks of kStepRows
-// sub-vectors, y over 512-centroid chunks.  Every workgroup of a row block
-// reads the best and second-best keys of its sub-vectors and makes the same
-// certification (the working values from Xc give the same per-wave scale as
-// the search); the first chunk's workgroup writes the certified winners.  The
-// others are searched again in float64 (direct form, terms in t order,
-// strictly smaller wins, so the lowest index keeps a tie), each workgroup over
-// its chunk, and the last workgroup of the row block (an arrival counter)
-// merges the chunks in chunk order.
-__global__ __launch_bounds__(256) void k_col_exact(int nv, int64_t n, int64_t M, const float* __restrict__ C, int K,
-                                                   const unsigned long long* __restrict__ keys,
-                                                   const float* __restrict__ cmax, const double* __restrict__ Xc,
-                                                   double* __restrict__ part_d, int* __restrict__ part_i,
-                                                   int* __restrict__ arrived, int* __restrict__ win,
-                                                   float* __restrict__ qrow, int* __restrict__ fl_total)
+// The block's last column n (V = 8 path): its decisions (col_certify,
+// col_resolve), value and error; nothing of the block is left to update.
+// Grid: row blocks of kStepRows sub-vectors.
+__global__ __launch_bounds__(256) void k_col_last(int64_t M, int nv, int64_t n, const float* __restrict__ C, int K,
+                                                  const float* __restrict__ U, int64_t N,
+                                                  const unsigned long long* __restrict__ keys,
+                                                  const float* __restrict__ cbest, int nch,
+                                                  const float* __restrict__ cmax, const double* __restrict__ Xc,
+                                                  uint16_t* __restrict__ idx, float* __restrict__ Wht,
+                                                  double* __restrict__ Et, int* __restrict__ fl_total)
 {
-    __shared__ int s_nflag, s_last;
-    __shared__ int s_flag[kStepRows];
-    __shared__ double s_rd[256];
-    __shared__ int s_ri[256];
+    __shared__ ColDecide sd;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int jl = lane & 31, half = lane >> 5;
-    const int j = (blockIdx.x * 4 + wave) * 32 + jl;
-    if (threadIdx.x == 0) s_nflag = 0;
-    double x64[8];
+    const int half = lane >> 5;
+    const int j = blockIdx.x * kStepRows + wave * 32 + (lane & 31);
+    const double* xcol = Xc + (size_t)(n & 1) * M;
+    double x[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) x64[t] = 0.0;
-    float mx = 0.0f;
-    if (j < nv) {
-        const double* x = Xc + (size_t)(n & 1) * M + (size_t)j * 8;
+    for (int t = 0; t < 8; ++t) x[t] = j < nv ? xcol[(size_t)j * 8 + t] : 0.0;
+    const double unn = (double)U[n * N + n];
+    ColCert r = col_certify(sd, nv, n, C, keys, *cmax, x);
+    __syncthreads();
+    const int nfl = col_resolve(sd, nv, n, xcol, C, K, cbest, nch, r);
+    if (j < nv && half == 0) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            x64[t] = x[t];
-            mx = fmaxf(mx, fabsf((float)x64[t]));
+            Wht[n * M + (int64_t)j * 8 + t] = r.qv[t];
+            Et[n * M + (int64_t)j * 8 + t] = (x[t] - (double)r.qv[t]) / unn;
         }
+        idx[n * nv + j] = (uint16_t)r.kw;
     }
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    const int sc = vp_scale_exp(*cmax);
-    const int sx = min(vp_scale_exp(mx), sc + 15 - kHnShift);
-    const bool no_norm = kHnShift + sx - sc < -24;      // the search ran without the norm term
-    __syncthreads();
-    if (half == 0 && j < nv) {
-        unsigned long long a1 = ~0ull, a2 = ~0ull, bmin = ~0ull;
-#pragma unroll
-        for (int q = 0; q < kKeySlots; ++q) {
-            const unsigned long long ka = keys[key_at(nv, q, 0, n, j)];
-            const unsigned long long kb = keys[key_at(nv, q, 1, n, j)];
-            if (ka < a1) { a2 = a1; a1 = ka; } else if (ka < a2) { a2 = ka; }
-            bmin = kb < bmin ? kb : bmin;
-        }
-        const unsigned long long k2 = a2 < bmin ? a2 : bmin;
-        const int kbest = (int)(a1 & 0xFFFFFFFFull);
-        const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)kbest;
-        const float4 ca = c4[0], cb = c4[1];
-        bool ok = true;
-        if (k2 != ~0ull) {
-            const double sA = -(double)unsortable((unsigned)(a1 >> 32));
-            const double sB = -(double)unsortable((unsigned)(k2 >> 32));
-            const float qv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
-            double nx2 = 0.0, db = 0.0;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                nx2 += x64[t] * x64[t];
-                const double df = x64[t] - (double)qv[t];
-                db += df * df;
-            }
-            const double nx = sqrt(nx2) * (1.0 + 0x1p-40);
-            const double R = nx + sqrt(db) * (1.0 + 0x1p-40);
-            double bound = 0x1p-18 * (1.25 * R * nx + 0.3125 * R * R) + ldexp(0x1p-8, -(sc + sx)) +
-                           0x1p-45 * (nx2 + db);
-            if (no_norm) bound += 0.5 * R * R;
-            const double gap = ldexp(sA - sB, -(sc + sx));
-            ok = gap > 2.0 * bound;                      // false also for NaN
-        }
-        if (ok) {
-            if (blockIdx.y == 0) {
-                win[(size_t)(n & 1) * nv + j] = kbest;
-                float4* q4 = reinterpret_cast<float4*>(qrow) + ((size_t)(n & 1) * nv + j) * 2;
-                q4[0] = ca;
-                q4[1] = cb;
-            }
-        } else {
-            s_flag[atomicAdd(&s_nflag, 1)] = wave * 32 + jl;
-        }
-    }
-    __syncthreads();
-    const int cnt = s_nflag;
-    if (cnt == 0) return;
-    const int k0 = blockIdx.y * kVpChunk;
-    const int kn = K - k0 < kVpChunk ? K - k0 : kVpChunk;
-    for (int f = 0; f < cnt; ++f) {
-        const int jj = blockIdx.x * kStepRows + s_flag[f];
-        const double* x = Xc + (size_t)(n & 1) * M + (size_t)jj * 8;
-        double xv[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) xv[t] = x[t];
-        double bd = __builtin_inf();
-        int bk = 0;
-        for (int q = threadIdx.x; q < kn; q += 256) {
-            const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)(k0 + q);
-            const float4 ca = c4[0], cb = c4[1];
-            const float cv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
-            double dist = 0.0;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const double df = xv[t] - (double)cv[t];
-                dist += df * df;
-            }
-            if (dist < bd) { bd = dist; bk = k0 + q; }
-        }
-        s_rd[threadIdx.x] = bd;
-        s_ri[threadIdx.x] = bk;
-        __syncthreads();
-        for (int w = 128; w > 0; w >>= 1) {
-            if ((int)threadIdx.x < w) {
-                const double od = s_rd[threadIdx.x + w];
-                const int oi = s_ri[threadIdx.x + w];
-                if (od < s_rd[threadIdx.x] || (od == s_rd[threadIdx.x] && oi < s_ri[threadIdx.x])) {
-                    s_rd[threadIdx.x] = od;
-                    s_ri[threadIdx.x] = oi;
-                }
-            }
-            __syncthreads();
-        }
-        if (threadIdx.x == 0) {
-            // device-scope stores: visible to the merging workgroup without a
-            // cache write-back
-            __hip_atomic_store(&part_d[(size_t)blockIdx.y * nv + jj], s_rd[0], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&part_i[(size_t)blockIdx.y * nv + jj], s_ri[0], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = atomicAdd(&arrived[blockIdx.x], 1) == (int)gridDim.y - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // one wavefront per listed sub-vector: its lanes load the chunks' results
-    // at once, then the smallest (distance, index) wins, which is the
-    // chunk-order merge with strict comparison
-    for (int f = wave; f < cnt; f += 4) {
-        const int jj = blockIdx.x * kStepRows + s_flag[f];
-        double bd = __builtin_inf();
-        int bk = 0x7FFFFFFF;
-        for (int c = lane; c < (int)gridDim.y; c += 64) {
-            const double d = __hip_atomic_load(&part_d[(size_t)c * nv + jj], __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-            const int i = __hip_atomic_load(&part_i[(size_t)c * nv + jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (d < bd || (d == bd && i < bk)) { bd = d; bk = i; }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const double od = __shfl_xor(bd, o);
-            const int oi = __shfl_xor(bk, o);
-            if (od < bd || (od == bd && oi < bk)) { bd = od; bk = oi; }
-        }
-        if (lane == 0) {
-            win[(size_t)(n & 1) * nv + jj] = bk;
-            const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)bk;
-            float4* q4 = reinterpret_cast<float4*>(qrow) + ((size_t)(n & 1) * nv + jj) * 2;
-            q4[0] = c4[0];
-            q4[1] = c4[1];
-        }
-    }
-    if (threadIdx.x == 0) {
-        arrived[blockIdx.x] = 0;
-        atomicAdd(fl_total, cnt);
-    }
-}
-
-// The block's last column n (V = 8 path): winner, value and error; nothing of
-// the block is left to update.
-__global__ __launch_bounds__(256) void k_col_last(int64_t M, int nv, int64_t n, const float* __restrict__ C,
-                                                  const float* __restrict__ U, int64_t N, const int* __restrict__ win,
-                                                  const float* __restrict__ qrow,
-                                                  const double* __restrict__ Xc, uint16_t* __restrict__ idx,
-                                                  float* __restrict__ Wht, double* __restrict__ Et)
-{
-    const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (m >= M) return;
-    const int v = (int)(m >> 3), t = (int)(m & 7);
-    const int k = win[(size_t)(n & 1) * nv + v];
-    const float wq = qrow[((size_t)(n & 1) * nv + v) * 8 + t];
-    const double e = (Xc[(size_t)(n & 1) * M + m] - (double)wq) / (double)U[n * N + n];
-    Wht[n * M + m] = wq;
-    Et[n * M + m] = e;
-    if (t == 0) idx[n * nv + v] = (uint16_t)k;
+    if (threadIdx.x == 0 && nfl > 0) atomicAdd(fl_total, nfl);
 }
 
 // Column n (other V): the chunks' winners merged in chunk order (strictly
@@ -741,19 +841,17 @@ __global__ __launch_bounds__(256) void k_block_gemm(double* __restrict__ Wt, con
 size_t ws_vptq(int64_t M, int64_t N, int V)
 {
     const int64_t nv = M / V;
-    const int64_t nrb = (nv + kStepRows - 1) / kStepRows;
     const int64_t nch = (65536 + kAsgChunk - 1) / kAsgChunk;
+    const int64_t nvp = 65536 / kVpChunk;
     // the float64 working matrix and errors, the float32 quantized matrix (all
-    // transposed), three key buffers (A and B keys, kKeySlots copies), two
-    // winner columns and their codebook rows, the row-block arrival counters,
-    // two float64 working
-    // columns, the prepared codebook (3 x 16 bytes per centroid, at most
-    // 65536), max |C|, and the per-chunk winners of the exact searches; per
-    // row block an arrival counter; the count of exact searches
+    // transposed), three key buffers (A and B keys, kKeySlots copies), the
+    // chunk best scores of two columns, the count of exact searches, two
+    // float64 working columns, the prepared codebook (3 x 16 bytes per
+    // centroid, at most 65536), max |C|, and the per-chunk winners of the
+    // direct-form search (other V)
     return 2 * align_up((size_t)M * (size_t)N * sizeof(double)) + align_up((size_t)M * (size_t)N * sizeof(float)) +
-           align_up((size_t)(3 * kKeySlots * 2 * nv) * sizeof(uint64_t)) + align_up((size_t)(2 * nv) * sizeof(int)) +
-           align_up((size_t)(16 * nv) * sizeof(float)) +
-           align_up((size_t)nrb * sizeof(int)) + align_up(sizeof(int)) +
+           align_up((size_t)(3 * kKeySlots * 2 * nv) * sizeof(uint64_t)) +
+           align_up((size_t)(2 * nvp * nv) * sizeof(float)) + align_up(sizeof(int)) +
            align_up((size_t)(2 * M) * sizeof(double)) +
            3 * align_up((size_t)65536 * sizeof(vp_h16x8)) + align_up(sizeof(float)) +
            align_up((size_t)(nch * nv) * sizeof(double)) + align_up((size_t)(nch * nv) * sizeof(int));
@@ -765,14 +863,13 @@ vq_status vptq_launch(const float* W, const float* U, int64_t M, int64_t N, int 
     const int64_t nv = M / V;
     const int64_t nrb = (nv + kStepRows - 1) / kStepRows;
     const int64_t nch_all = (65536 + kAsgChunk - 1) / kAsgChunk;
+    const int64_t nvp = 65536 / kVpChunk;
     Carver cv(ws, ws_bytes);
     double* Wt = cv.take<double>((size_t)(M * N));
     double* Et = cv.take<double>((size_t)(M * N));
     float* Wht = cv.take<float>((size_t)(M * N));
     unsigned long long* keys = cv.take<unsigned long long>((size_t)(3 * kKeySlots * 2 * nv));
-    int* win = cv.take<int>((size_t)(2 * nv));
-    float* qrow = cv.take<float>((size_t)(16 * nv));
-    int* arrived = cv.take<int>((size_t)nrb);
+    float* cbest = cv.take<float>((size_t)(2 * nvp * nv));
     int* fl_total = cv.take<int>(1);
     double* Xc = cv.take<double>((size_t)(2 * M));
     const int Kp = (K + kVpChunk - 1) / kVpChunk * kVpChunk;
@@ -792,8 +889,6 @@ vq_status vptq_launch(const float* W, const float* U, int64_t M, int64_t N, int 
         hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(3 * kKeySlots * 2 * nv, 256)), dim3(256), 0, st, keys,
                            3 * kKeySlots * 2 * nv, ~0ull);
         VQ_LAUNCHED("k_fill_u64");
-        hipLaunchKernelGGL(k_fill_i32, dim3(grid_for(nrb, 256)), dim3(256), 0, st, arrived, nrb, 0);
-        VQ_LAUNCHED("k_fill_i32");
         hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, st, fl_total, (int64_t)1, 0);
         VQ_LAUNCHED("k_fill_i32");
         hipLaunchKernelGGL(k_vp_absmax, dim3(1), dim3(1024), 0, st, reinterpret_cast<const float4*>(C),
@@ -804,22 +899,20 @@ vq_status vptq_launch(const float* W, const float* U, int64_t M, int64_t N, int 
     }
     const int nch = (K + kAsgChunk - 1) / kAsgChunk;
     const dim3 ga(grid_for(nv, kAsgThreads), (unsigned)nch);
-    const dim3 gm((unsigned)nrb, (unsigned)(Kp / kVpChunk));
+    const int nchv = Kp / kVpChunk;
+    const dim3 gm((unsigned)nrb, (unsigned)nchv);
     for (int64_t s = 0; s < N; s += B) {
         const int64_t s_end = s + B < N ? s + B : N;
         if (v8) {
-            // one launch per column (it also finishes the column before it),
-            // and one for the block's last column
+            // one launch per column (it also decides and finishes the column
+            // before it), and one for the block's last column
             for (int64_t n = s; n < s_end; ++n) {
                 hipLaunchKernelGGL(k_col_step_h16, gm, dim3(256), 0, st, Wt, M, (int)nv, n, s, s_end, C, U, N, keys,
-                                   win, qrow, Xc, idx, Wht, Et, Phi, Plo, Phn, cmax, K);
+                                   cbest, nchv, Xc, idx, Wht, Et, Phi, Plo, Phn, cmax, K, fl_total);
                 VQ_LAUNCHED("k_col_step_h16");
-                hipLaunchKernelGGL(k_col_exact, gm, dim3(256), 0, st, (int)nv, n, M, C, K, keys, cmax, Xc, part_d,
-                                   part_i, arrived, win, qrow, fl_total);
-                VQ_LAUNCHED("k_col_exact");
             }
-            hipLaunchKernelGGL(k_col_last, dim3(grid_for(M, 256)), dim3(256), 0, st, M, (int)nv, s_end - 1, C, U, N,
-                               win, qrow, Xc, idx, Wht, Et);
+            hipLaunchKernelGGL(k_col_last, dim3((unsigned)nrb), dim3(256), 0, st, M, (int)nv, s_end - 1, C, K, U, N,
+                               keys, cbest, nchv, cmax, Xc, idx, Wht, Et, fl_total);
             VQ_LAUNCHED("k_col_last");
         } else {
             for (int64_t n = s; n < s_end; ++n) {
