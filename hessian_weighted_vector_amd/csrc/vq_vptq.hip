@@ -269,6 +269,9 @@ struct ColDecide {
     double bnd[kStepRows];           // its rounding bound
     int dec[kStepRows];              // exact winner, by local sub-vector
     float4 row[kStepRows][2];        // the winner's codebook row, by local sub-vector
+    double wd[4];                    // one exact search: each wavefront's nearest row,
+    int wk[4];                       // its index
+    float4 wr[4][2];                 // and the row
 };
 
 // A column's decisions for the workgroup's kStepRows sub-vectors, in two
@@ -295,8 +298,33 @@ struct ColCert {
     float qv[8];
 };
 
-__device__ inline ColCert col_certify(ColDecide& sd, int nv, int64_t p, const float* __restrict__ C,
-                                      const unsigned long long* __restrict__ keys, float cmv, const double (&x)[8])
+// The best and second-best keys of the lane's sub-vector in column p (the
+// smallest over A's copies; the smallest over the rest and B's copies).
+__device__ inline void col_keys(int nv, int64_t p, const unsigned long long* __restrict__ keys,
+                                unsigned long long& a1, unsigned long long& k2)
+{
+    const int j = blockIdx.x * kStepRows + (threadIdx.x >> 6) * 32 + (threadIdx.x & 31);
+    a1 = ~0ull;
+    k2 = ~0ull;
+    if (j < nv) {
+        unsigned long long ka[kKeySlots], kb[kKeySlots];
+#pragma unroll
+        for (int q = 0; q < kKeySlots; ++q) {
+            ka[q] = keys[key_at(nv, q, 0, p, j)];
+            kb[q] = keys[key_at(nv, q, 1, p, j)];
+        }
+        unsigned long long a2 = ~0ull, bmin = ~0ull;
+#pragma unroll
+        for (int q = 0; q < kKeySlots; ++q) {
+            if (ka[q] < a1) { a2 = a1; a1 = ka[q]; } else if (ka[q] < a2) { a2 = ka[q]; }
+            bmin = kb[q] < bmin ? kb[q] : bmin;
+        }
+        k2 = a2 < bmin ? a2 : bmin;
+    }
+}
+
+__device__ inline ColCert col_certify(ColDecide& sd, int nv, const float* __restrict__ C, unsigned long long a1,
+                                      unsigned long long k2, float cmv, const double (&x)[8])
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int jl = lane & 31, half = lane >> 5;
@@ -318,15 +346,6 @@ __device__ inline ColCert col_certify(ColDecide& sd, int nv, int64_t p, const fl
     const bool no_norm = kHnShift + sx - sc < -24;       // the search ran without the norm term
     double sA = 0.0, bound = 0.0;
     if (j < nv) {
-        unsigned long long a1 = ~0ull, a2 = ~0ull, bmin = ~0ull;
-#pragma unroll
-        for (int q = 0; q < kKeySlots; ++q) {
-            const unsigned long long ka = keys[key_at(nv, q, 0, p, j)];
-            const unsigned long long kb = keys[key_at(nv, q, 1, p, j)];
-            if (ka < a1) { a2 = a1; a1 = ka; } else if (ka < a2) { a2 = ka; }
-            bmin = kb < bmin ? kb : bmin;
-        }
-        const unsigned long long k2 = a2 < bmin ? a2 : bmin;
         r.kw = (int)(a1 & 0xFFFFFFFFull);
         const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)r.kw;
         const float4 ca = c4[0], cb = c4[1];
@@ -369,8 +388,12 @@ __device__ inline int col_resolve(ColDecide& sd, int nv, int64_t p, const double
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int total = sd.wcnt[0] + sd.wcnt[1] + sd.wcnt[2] + sd.wcnt[3];
     if (total == 0) return 0;
+    // one listed sub-vector at a time, its candidate chunks dealt to the four
+    // wavefronts in turn (each wavefront finds the same candidates), all rows
+    // of a chunk requested at once; the wavefronts' results meet in LDS
     for (int ww = 0; ww < 4; ++ww) {
-        for (int i = wave; i < sd.wcnt[ww]; i += 4) {
+        const int cnt = sd.wcnt[ww];
+        for (int i = 0; i < cnt; ++i) {
             const int slot = ww * 32 + i;
             const int lj = sd.flag[slot];
             const int jj = blockIdx.x * kStepRows + lj;
@@ -382,6 +405,7 @@ __device__ inline int col_resolve(ColDecide& sd, int nv, int64_t p, const double
             double bd = __builtin_inf();
             int bk = 0x7FFFFFFF;
             float4 ra = make_float4(0.0f, 0.0f, 0.0f, 0.0f), rb = ra;
+            int seen = 0;                                // candidates met so far (the same in every wavefront)
             for (int c0 = 0; c0 < nch; c0 += 64) {
                 bool cand = false;
                 if (c0 + lane < nch) {
@@ -392,30 +416,39 @@ __device__ inline int col_resolve(ColDecide& sd, int nv, int64_t p, const double
                 while (m) {
                     const int cc = c0 + __ffsll((long long)m) - 1;
                     m &= m - 1;
+                    if ((seen++ & 3) != wave) continue;
                     const int k0 = cc * kVpChunk;
                     const int kn = K - k0 < kVpChunk ? K - k0 : kVpChunk;
-                    for (int q = lane; q < kn; q += 64) {
-                        const int k = k0 + q;
-                        const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)k;
-                        const float4 ca = c4[0], cb = c4[1];
-                        const float cv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+                    float4 ca[kVpChunk / 64], cb[kVpChunk / 64];
+#pragma unroll
+                    for (int u = 0; u < kVpChunk / 64; ++u) {
+                        const int q = lane + 64 * u;
+                        const float4* c4 = reinterpret_cast<const float4*>(C) + 2 * (size_t)(k0 + (q < kn ? q : 0));
+                        ca[u] = c4[0];
+                        cb[u] = c4[1];
+                    }
+#pragma unroll
+                    for (int u = 0; u < kVpChunk / 64; ++u) {
+                        const int q = lane + 64 * u;
+                        const float cv[8] = {ca[u].x, ca[u].y, ca[u].z, ca[u].w, cb[u].x, cb[u].y, cb[u].z, cb[u].w};
                         double dist = 0.0;
 #pragma unroll
                         for (int t = 0; t < 8; ++t) {
                             const double df = xv[t] - (double)cv[t];
                             dist += df * df;
                         }
-                        if (dist < bd || (dist == bd && k < bk)) {
+                        const int k = k0 + q;
+                        if (q < kn && (dist < bd || (dist == bd && k < bk))) {
                             bd = dist;
                             bk = k;
-                            ra = ca;
-                            rb = cb;
+                            ra = ca[u];
+                            rb = cb[u];
                         }
                     }
                 }
             }
-            // the smallest (distance, index) of the wavefront; its lane
-            // writes the winner and its row
+            // the wavefront's smallest (distance, index); its lane (indices
+            // are distinct) leaves it, with the row, for the merge
             double md = bd;
             int mk = bk;
 #pragma unroll
@@ -424,14 +457,25 @@ __device__ inline int col_resolve(ColDecide& sd, int nv, int64_t p, const double
                 const int oi = __shfl_xor(mk, o);
                 if (od < md || (od == md && oi < mk)) { md = od; mk = oi; }
             }
-            if (bk == mk && bd == md) {                  // one lane: indices are distinct
-                sd.dec[lj] = mk;
-                sd.row[lj][0] = ra;
-                sd.row[lj][1] = rb;
+            if (mk == 0x7FFFFFFF ? lane == 0 : (bk == mk && bd == md)) {
+                sd.wd[wave] = md;
+                sd.wk[wave] = mk;
+                sd.wr[wave][0] = ra;
+                sd.wr[wave][1] = rb;
             }
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                int w = 0;
+#pragma unroll
+                for (int v = 1; v < 4; ++v)
+                    if (sd.wd[v] < sd.wd[w] || (sd.wd[v] == sd.wd[w] && sd.wk[v] < sd.wk[w])) w = v;
+                sd.dec[lj] = sd.wk[w];
+                sd.row[lj][0] = sd.wr[w][0];
+                sd.row[lj][1] = sd.wr[w][1];
+            }
+            __syncthreads();
         }
     }
-    __syncthreads();
     if (!r.ok) {
         const int local = wave * 32 + (lane & 31);
         r.kw = sd.dec[local];
@@ -466,6 +510,9 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
     __shared__ ColDecide sd;
     const int k0 = blockIdx.y * kVpChunk;
     const int kn = K - k0 < kVpChunk ? K - k0 : kVpChunk;
+    // the previous column's keys first: the certification waits on them
+    unsigned long long ka1 = ~0ull, kk2 = ~0ull;
+    if (n > s) col_keys(nv, n - 1, keys, ka1, kk2);
     // the chunk's prepared rows, two centroids per thread (staged in LDS
     // later, after the decision's loads are issued)
     const int ka = k0 + threadIdx.x, kb = ka + 256;
@@ -510,7 +557,7 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
 #pragma unroll
         for (int t = 0; t < 8; ++t) xp[t] = j < nv ? xcol[(size_t)j * 8 + t] : 0.0;
         const double unn = (double)U[p * N + p], un = (double)U[p * N + n];
-        ColCert r = col_certify(sd, nv, p, C, keys, cmv, xp);
+        ColCert r = col_certify(sd, nv, C, ka1, kk2, cmv, xp);
         stage();
         __syncthreads();
         const int nfl = col_resolve(sd, nv, p, xcol, C, K, cbest, nch, r);
@@ -709,7 +756,9 @@ __global__ __launch_bounds__(256) void k_col_last(int64_t M, int nv, int64_t n, 
 #pragma unroll
     for (int t = 0; t < 8; ++t) x[t] = j < nv ? xcol[(size_t)j * 8 + t] : 0.0;
     const double unn = (double)U[n * N + n];
-    ColCert r = col_certify(sd, nv, n, C, keys, *cmax, x);
+    unsigned long long a1, k2;
+    col_keys(nv, n, keys, a1, k2);
+    ColCert r = col_certify(sd, nv, C, a1, k2, *cmax, x);
     __syncthreads();
     const int nfl = col_resolve(sd, nv, n, xcol, C, K, cbest, nch, r);
     if (j < nv && half == 0) {
