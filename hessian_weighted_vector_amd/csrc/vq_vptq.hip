@@ -490,13 +490,12 @@ __device__ inline int col_resolve(ColDecide& sd, int nv, int64_t p, const double
 // y over kVpChunk-centroid chunks.  For n past the block's first column it
 // first decides column n-1 (col_certify, col_resolve), then finishes it:
 // value, error, the error's share of column n (every workgroup of these rows
-// forms the same values); the first chunk's workgroups write the outputs.
-// Then it searches column n over its chunk, and pushes column n-1's error
-// into the block's later columns, split over the workgroups of these rows by
-// column (no later read in this launch).  Loads are issued early and their
-// registers used late: the chunk is written to LDS only after the keys and
-// the winners' rows are requested, and the later columns' values are loaded
-// before the key atomics.
+// forms the same values); the first chunk's workgroups write the outputs,
+// and column n-1's error goes into the block's later columns.  Then it
+// searches column n over its chunk.  Loads are issued early and their
+// registers used late: the previous column's keys first, the chunk written to
+// LDS only after the keys and the winners' rows are requested, the later
+// column's values at the start.
 __global__ __launch_bounds__(256) void k_col_step_h16(
     double* __restrict__ Wt, int64_t M, int nv, int64_t n, int64_t s, int64_t s_end, const float* __restrict__ C,
     const float* __restrict__ U, int64_t N, unsigned long long* __restrict__ keys, float* __restrict__ cbest,
@@ -540,6 +539,18 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
             w[2 * q + 1] = v2.y;
         }
     }
+    // the first of the block's later columns that this workgroup updates
+    // with column n-1's error (its values requested now, written before the
+    // search, so the stores complete while the matrix cores run)
+    int64_t rl = n + 1 + blockIdx.y;
+    const bool upd = n > s && rl < s_end && j < nv;
+    double ul = 0.0, wl[4] = {0.0, 0.0, 0.0, 0.0};
+    if (upd) {
+        ul = (double)U[(n - 1) * N + rl];
+        const double* wr = Wt + rl * M + (int64_t)j * 8 + half * 4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) wl[t] = wr[t];
+    }
     auto stage = [&]() {
         const int q = threadIdx.x;
         L[0][q] = fa0;
@@ -549,7 +560,6 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
         L[1][q + 256] = fb1;
         L[2][q + 256] = fb2;
     };
-    bool later = false;                                  // the block's later columns get e (after the search)
     if (n > s) {
         const int64_t p = n - 1;
         const double* xcol = Xc + (size_t)(p & 1) * M;
@@ -575,7 +585,20 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
                 }
                 idx[p * nv + j] = (uint16_t)r.kw;
             }
-            later = true;
+            // column n-1's error into the block's later columns, split over
+            // the workgroups of these rows by column (no later read in this
+            // launch)
+            if (upd) {
+                double* wr = Wt + rl * M + (int64_t)j * 8 + half * 4;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) wr[t] = wl[t] - e[half * 4 + t] * ul;
+                for (rl += gridDim.y; rl < s_end; rl += gridDim.y) {
+                    const double ur = (double)U[p * N + rl];
+                    double* wq = Wt + rl * M + (int64_t)j * 8 + half * 4;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) wq[t] = wq[t] - e[half * 4 + t] * ur;
+                }
+            }
         }
         if (blockIdx.y == 0 && threadIdx.x == 0 && nfl > 0) atomicAdd(fl_total, nfl);
     } else {
@@ -701,19 +724,6 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
         sec = fmaxf(fmaxf(sec, os), lo);
         if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
     }
-    // column n-1's error into the block's later columns, split over the
-    // workgroups of these rows by column (no later read in this launch); the
-    // first row's values are requested before the key atomics
-    const int64_t p = n - 1;
-    int64_t r = n + 1 + blockIdx.y;
-    const bool upd = later && r < s_end;
-    double u = 0.0, wv[4] = {0.0, 0.0, 0.0, 0.0};
-    if (upd) {
-        u = (double)U[p * N + r];
-        const double* wr = Wt + r * M + (int64_t)j * 8 + half * 4;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) wv[t] = wr[t];
-    }
     if (active && half == 0 && j < nv) {
         cbest[((size_t)(n & 1) * nch + blockIdx.y) * nv + j] = fmaxf(best, sec);
         const int slot = blockIdx.y % kKeySlots;
@@ -722,17 +732,6 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
         const unsigned long long old = atomicMin(&keys[key_at(nv, slot, 0, n, j)], kb_);
         const unsigned long long lost = old > kb_ ? old : kb_;
         atomicMin(&keys[key_at(nv, slot, 1, n, j)], lost < ks_ ? lost : ks_);
-    }
-    if (upd) {
-        double* wr = Wt + r * M + (int64_t)j * 8 + half * 4;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) wr[t] = wv[t] - e[half * 4 + t] * u;
-        for (r += gridDim.y; r < s_end; r += gridDim.y) {
-            const double ur = (double)U[p * N + r];
-            double* wq = Wt + r * M + (int64_t)j * 8 + half * 4;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) wq[t] = wq[t] - e[half * 4 + t] * ur;
-        }
     }
 }
 
