@@ -505,7 +505,6 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
 {
     static_assert(kVpChunk == 2 * 256, "two prepared centroids per thread");
     __shared__ vp_h16x8 L[3][kVpChunk];
-    __shared__ float4 Lt[4][4][64];                      // per lane: the 16 scores of its best tile so far
     __shared__ ColDecide sd;
     const int k0 = blockIdx.y * kVpChunk;
     const int kn = K - k0 < kVpChunk ? K - k0 : kVpChunk;
@@ -645,10 +644,13 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
         const vp_h16x8* A2 = L[half ? 2 : 0];
         const int ntiles = (kn + 31) / 32;
         // per tile its largest score: the lane's best and second-best tile
-        // maxima and the best's tile, whose 16 scores the lane parks in its
-        // own LDS slots whenever a tile improves on the best
+        // maxima and the best's tile, whose 16 scores the lane keeps (a
+        // select per score, no branch)
         float m1 = -__builtin_inff(), m2 = -__builtin_inff();
         int bt = 0;
+        float pk[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pk[r] = -__builtin_inff();
         auto scan = [&](vp_f32x16 acc, int tb) {
             if (tb + 32 > kn) {                          // the chunk's last, partial tile
 #pragma unroll
@@ -660,13 +662,10 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
             for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, acc[r]), acc[r + 1]);
             m = fmaxf(m, acc[15]);
             m2 = __builtin_amdgcn_fmed3f(m1, m2, m);
-            if (m > m1) {
-                bt = tb;
-                Lt[wave][0][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-                Lt[wave][1][lane] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-                Lt[wave][2][lane] = make_float4(acc[8], acc[9], acc[10], acc[11]);
-                Lt[wave][3][lane] = make_float4(acc[12], acc[13], acc[14], acc[15]);
-            }
+            const bool imp = m > m1;
+            bt = imp ? tb : bt;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pk[r] = imp ? acc[r] : pk[r];
             m1 = fmaxf(m1, m);
         };
         const vp_f32x16 zero = {};
@@ -697,10 +696,7 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
         // ties) and the tile's own second best; the other tiles' maxima give
         // the rest of the second best
         if (m1 > -__builtin_inff()) {
-            const float4 v0 = Lt[wave][0][lane], v1 = Lt[wave][1][lane];
-            const float4 v2 = Lt[wave][2][lane], v3 = Lt[wave][3][lane];
-            const float rf[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
-                                  v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+            const float* rf = pk;
             int rr = 0, ties = 0;
             float t2 = -__builtin_inff();                // largest score below the best
 #pragma unroll
