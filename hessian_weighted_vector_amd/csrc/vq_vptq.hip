@@ -195,6 +195,26 @@ __device__ inline size_t key_at(int nv, int slot, int kind, int64_t n, int j)
     return (((size_t)(n % 3) * kKeySlots + (size_t)slot) * 2 + (size_t)kind) * (size_t)nv + (size_t)j;
 }
 
+// v of another lane by a DPP pattern (every row and bank enabled).
+template <int kCtrl>
+__device__ inline float dpp_f(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true));
+}
+
+// Largest of v over the lane's half-wavefront (lanes 0-31 or 32-63): DPP
+// exchanges inside each row of 16 lanes (quad swaps, then the half-row and
+// row mirrors) and one swizzle between the two rows of the half.
+__device__ inline float half_max(float v)
+{
+    v = fmaxf(v, dpp_f<0xB1>(v));                        // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_f<0x4E>(v));                        // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_f<0x141>(v));                       // row_half_mirror
+    v = fmaxf(v, dpp_f<0x140>(v));                       // row_mirror
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F)));
+    return v;
+}
+
 typedef float vp_f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 vp_h16x8 __attribute__((ext_vector_type(8)));
 
@@ -339,8 +359,7 @@ __device__ inline ColCert col_certify(ColDecide& sd, int nv, const float* __rest
     float mx = 0.0f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) mx = fmaxf(mx, fabsf((float)x[t]));
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    mx = half_max(mx);
     const int sc = vp_scale_exp(cmv);
     const int sx = min(vp_scale_exp(mx), sc + 15 - kHnShift);
     const bool no_norm = kHnShift + sx - sc < -24;       // the search ran without the norm term
@@ -623,8 +642,7 @@ __global__ __launch_bounds__(256) void k_col_step_h16(
         xv[t] = (float)x64[t];
         mx = fmaxf(mx, fabsf(xv[t]));
     }
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    mx = half_max(mx);
     const int sc = vp_scale_exp(cmv);
     const int sx = min(vp_scale_exp(mx), sc + 15 - kHnShift);
     const int eb = kHnShift + sx - sc;                  // <= 15: b is a finite fp16
