@@ -250,30 +250,45 @@ __device__ __forceinline__ void load_sub(const float* __restrict__ X, const floa
         if ((mb >> t) & 1u) w[t] = 0.f;
 }
 
-// Per-slot tracking (short codebooks, where a few branchy updates cost less
-// than forming a tile again at the end): exact (best, second best, position
-// = kt*16 + slot) over the 16 values of tile kt, in slot order (slot order is
-// centroid order within the lane, so equal values keep the lower index).
-// Only tiles whose minimum beats the second best are walked.
-__device__ __forceinline__ void slot_track(const f32x16& a, int kt, float& b1, float& b2, int& kbp)
+// Short codebooks: the tile tracking above, plus the 16 values of the lane's
+// best tile kept in registers (a select per value, no branch).  At the end
+// park_resolve finds the best's slot in that tile (the first of equal
+// values: slot order is centroid order within the lane, so the lower index)
+// and folds the tile's own second best into b2; pos becomes kt*16 + slot.
+__device__ __forceinline__ void park_track(const f32x16& a, int kt, float& b1, float& b2, int& kt1,
+                                           float (&pk)[16])
 {
-    if (tile_min(a) < b2) {
+    const float tm = tile_min(a);
+    b2 = __builtin_amdgcn_fmed3f(b1, tm, b2);
+    const bool lt = tm < b1;
+    b1 = lt ? tm : b1;
+    kt1 = lt ? kt : kt1;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float v = a[j];
-            const bool lt = v < b1;
-            b2 = __builtin_amdgcn_fmed3f(b1, b2, v);
-            b1 = lt ? v : b1;
-            kbp = lt ? kt * 16 + j : kbp;
+    for (int j = 0; j < 16; ++j) pk[j] = lt ? a[j] : pk[j];
+}
+
+__device__ __forceinline__ void park_resolve(const float (&pk)[16], float b1, float& b2, int& pos)
+{
+    int jj = 0, ties = 0;
+    float t2 = __builtin_inff();                          // smallest value above the best
+#pragma unroll
+    for (int j = 15; j >= 0; --j) {
+        if (pk[j] == b1) {
+            jj = j;
+            ++ties;
+        } else {
+            t2 = fminf(t2, pk[j]);
         }
     }
+    b2 = fminf(b2, ties > 1 ? b1 : t2);
+    pos = pos * 16 + jj;
 }
 
 template <bool SLOT>
-__device__ __forceinline__ void track(const f32x16& a, int kt, float& b1, float& b2, int& pos)
+__device__ __forceinline__ void track(const f32x16& a, int kt, float& b1, float& b2, int& pos, float (&pk)[16])
 {
     if (SLOT)
-        slot_track(a, kt, b1, b2, pos);
+        park_track(a, kt, b1, b2, pos, pk);
     else
         tile_track(a, kt, b1, b2, pos);
 }
@@ -282,13 +297,14 @@ __device__ __forceinline__ void track(const f32x16& a, int kt, float& b1, float&
 // previous tile's tracking update between them.
 template <bool SLOT>
 __device__ __forceinline__ f32x16 tile_h16(const h16x8 ah, const h16x8 al, const h16x8 bh, const h16x8 bl,
-                                           const f32x16& prev, int ktp, float& b1, float& b2, int& pos)
+                                           const f32x16& prev, int ktp, float& b1, float& b2, int& pos,
+                                           float (&pk)[16])
 {
     f32x16 acc = {};
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc, 0, 0, 0);
-    track<SLOT>(prev, ktp, b1, b2, pos);
+    track<SLOT>(prev, ktp, b1, b2, pos, pk);
 #pragma unroll
     for (int g = 0; g < 3; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
@@ -378,7 +394,8 @@ __device__ __forceinline__ f32x16 tile2_h16(const h16x8 a0, const h16x8 a1, cons
     f32x16 acc = {};
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1v, acc, 0, 0, 0);
-    track<SLOT>(prev, ktp, b1, b2, pos);
+    static_assert(!SLOT, "the shared-weight form tracks tiles");
+    tile_track(prev, ktp, b1, b2, pos);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
@@ -515,8 +532,9 @@ __device__ __forceinline__ void search_epilogue(
 // while the current one is searched, so there is one barrier per chunk.
 // Within a wave the tiles are software pipelined: tile t's MFMAs are issued
 // with tile t-1's argmin updates between them (two accumulators alternate).
-// SLOT selects per-slot tracking (short codebooks) over per-tile tracking
-// with the best tile formed again at the end (long codebooks).
+// SLOT (short codebooks) keeps the best tile's values in registers and finds
+// the best's slot at the end; otherwise (long codebooks) the best tile is
+// formed again at the end.
 // The general form's B operand of one sub-vector: the lanes of the lower
 // half hold the scaled omega*x parts (MFMA k-slots 0-7), those of the upper
 // half the scaled omega parts (k-slots 8-15), each split into two fp16
@@ -567,7 +585,7 @@ __device__ __forceinline__ void general_operand(const float* __restrict__ X, con
 }
 
 template <bool SLOT>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_assign_h16(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(SLOT ? 4 : 5, 8))) void k_assign_h16(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
     const uint8_t* __restrict__ mask, int64_t n_sub, int64_t nb, int d, const uint4* __restrict__ P,
     const float* __restrict__ cmax, const float* __restrict__ C, int K, int nchunks,
@@ -599,6 +617,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
 
     float b1 = __builtin_inff(), b2 = __builtin_inff();
     int kt1 = 0;
+    float pk[16];                                                // short codebooks: the best tile's values
+#pragma unroll
+    for (int j = 0; j < 16; ++j) pk[j] = __builtin_inff();
 
     uint4 pre0 = P[threadIdx.x];
     uint4 pre1 = P[threadIdx.x + kWaves * 64];
@@ -626,10 +647,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
                 const uint4* A1 = A0 + 128;
                 const h16x8 ah0 = __builtin_bit_cast(h16x8, A0[0]);
                 const h16x8 al0 = __builtin_bit_cast(h16x8, A0[64]);
-                accA = tile_h16<SLOT>(ah0, al0, bh, bl, accB, ktB, b1, b2, kt1);
+                accA = tile_h16<SLOT>(ah0, al0, bh, bl, accB, ktB, b1, b2, kt1, pk);
                 const h16x8 ah1 = __builtin_bit_cast(h16x8, A1[0]);
                 const h16x8 al1 = __builtin_bit_cast(h16x8, A1[64]);
-                accB = tile_h16<SLOT>(ah1, al1, bh, bl, accA, kt0 + tt, b1, b2, kt1);
+                accB = tile_h16<SLOT>(ah1, al1, bh, bl, accA, kt0 + tt, b1, b2, kt1, pk);
                 ktB = kt0 + tt + 1;
             }
         }
@@ -640,7 +661,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(5, 
         __syncthreads();
     }
     if (!active) return;
-    track<SLOT>(accB, ktB, b1, b2, kt1);
+    track<SLOT>(accB, ktB, b1, b2, kt1, pk);
+    if (SLOT) park_resolve(pk, b1, b2, kt1);
 
     search_epilogue<SLOT>(X, hcol, rho, mask, nb, d, C, K, s, valid, valid, false, false, lane, half, b1, b2,
                           kt1, S_sc, shift_s, idx, dist, flag_count, flag_list);
@@ -871,7 +893,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
     }
     if (!active) return;
 #pragma unroll
-    for (int u = 0; u < NS; ++u) track<SLOT>(accB[u], ktB, b1[u], b2[u], kt1[u]);
+    for (int u = 0; u < NS; ++u) tile_track(accB[u], ktB, b1[u], b2[u], kt1[u]);
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
         int r = lane & 31;
