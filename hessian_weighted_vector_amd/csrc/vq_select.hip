@@ -35,12 +35,22 @@ struct SelState {
     int64_t remaining;  // elements still to take among those matching prefix
 };
 
-__device__ inline uint32_t score_bits(const float* W, const float* h, int64_t e, int64_t N)
+__device__ inline uint32_t score_of(float w, float hj)
 {
-    const float w = W[e];
     const float sq = w * w;
-    const float s = h[e % N] * sq;
-    return __float_as_uint(s);
+    return __float_as_uint(hj * sq);
+}
+
+// Scores of row i, columns j .. j+3 (vec: N % 4 == 0 and W, h 16-byte aligned).
+__device__ inline void score4(const float* __restrict__ W, const float* __restrict__ h, int64_t i, int64_t N,
+                              int64_t j, uint32_t (&b)[4])
+{
+    const float4 w = *reinterpret_cast<const float4*>(W + i * N + j);
+    const float4 hh = *reinterpret_cast<const float4*>(h + j);
+    b[0] = score_of(w.x, hh.x);
+    b[1] = score_of(w.y, hh.y);
+    b[2] = score_of(w.z, hh.z);
+    b[3] = score_of(w.w, hh.w);
 }
 
 __global__ void k_sel_init(SelState* st, int64_t nnz, int* hist)
@@ -50,24 +60,42 @@ __global__ void k_sel_init(SelState* st, int64_t nnz, int* hist)
     if (t < kBins) hist[t] = 0;
 }
 
+// Workgroups take whole rows (row, then columns: no index division), four
+// columns per thread per step with 16-byte loads where vec; each wavefront
+// counts into its own LDS copy of the histogram (less contention on the
+// few crowded bins of the first digit), summed at the end.
 __global__ __launch_bounds__(256) void k_sel_hist(const float* __restrict__ W,
-                                                  const float* __restrict__ h, int64_t total,
-                                                  int64_t N, const SelState* __restrict__ st,
+                                                  const float* __restrict__ h, int64_t M,
+                                                  int64_t N, bool vec, const SelState* __restrict__ st,
                                                   uint32_t pmask, int shift, uint32_t dmask,
                                                   int* __restrict__ hist)
 {
-    __shared__ int cnt[kBins];
-    for (int q = threadIdx.x; q < kBins; q += blockDim.x) cnt[q] = 0;
+    __shared__ int cnt[4][kBins];
+    for (int q = threadIdx.x; q < 4 * kBins; q += blockDim.x) (&cnt[0][0])[q] = 0;
     __syncthreads();
     const uint32_t prefix = st->prefix;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
-        const uint32_t b = score_bits(W, h, e, N);
-        if ((b & pmask) == prefix) atomicAdd(&cnt[(b >> shift) & dmask], 1);
+    int* my = cnt[threadIdx.x >> 6];
+    for (int64_t i = blockIdx.x; i < M; i += gridDim.x) {
+        if (vec) {
+            for (int64_t j = (int64_t)threadIdx.x * 4; j < N; j += 4 * (int64_t)blockDim.x) {
+                uint32_t b[4];
+                score4(W, h, i, N, j, b);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if ((b[u] & pmask) == prefix) atomicAdd(&my[(b[u] >> shift) & dmask], 1);
+            }
+        } else {
+            for (int64_t j = threadIdx.x; j < N; j += blockDim.x) {
+                const uint32_t b = score_of(W[i * N + j], h[j]);
+                if ((b & pmask) == prefix) atomicAdd(&my[(b >> shift) & dmask], 1);
+            }
+        }
     }
     __syncthreads();
-    for (int q = threadIdx.x; q < kBins; q += blockDim.x)
-        if (cnt[q]) atomicAdd(&hist[q], cnt[q]);
+    for (int q = threadIdx.x; q < kBins; q += blockDim.x) {
+        const int c = cnt[0][q] + cnt[1][q] + cnt[2][q] + cnt[3][q];
+        if (c) atomicAdd(&hist[q], c);
+    }
 }
 
 // Picks the digit holding the remaining-th largest element; clears hist.
@@ -116,17 +144,29 @@ __global__ __launch_bounds__(256) void k_sel_pick(SelState* st, int* hist, int s
 
 // Per row: number of scores > tau and == tau.
 __global__ __launch_bounds__(kRowThreads) void k_sel_row_count(
-    const float* __restrict__ W, const float* __restrict__ h, int64_t N,
+    const float* __restrict__ W, const float* __restrict__ h, int64_t N, bool vec,
     const SelState* __restrict__ st, int* __restrict__ cgt, int* __restrict__ ceq)
 {
     __shared__ int sg[kRowThreads], se[kRowThreads];
     const int64_t i = blockIdx.x;
     const uint32_t tau = st->prefix;
     int g = 0, q = 0;
-    for (int64_t j = threadIdx.x; j < N; j += kRowThreads) {
-        const uint32_t b = score_bits(W, h, i * N + j, N);
-        g += b > tau;
-        q += b == tau;
+    if (vec) {
+        for (int64_t j = (int64_t)threadIdx.x * 4; j < N; j += 4 * kRowThreads) {
+            uint32_t b[4];
+            score4(W, h, i, N, j, b);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                g += b[u] > tau;
+                q += b[u] == tau;
+            }
+        }
+    } else {
+        for (int64_t j = threadIdx.x; j < N; j += kRowThreads) {
+            const uint32_t b = score_of(W[i * N + j], h[j]);
+            g += b > tau;
+            q += b == tau;
+        }
     }
     sg[threadIdx.x] = g;
     se[threadIdx.x] = q;
@@ -212,7 +252,7 @@ __device__ inline int scan256(int v, int* sh)
 
 // Per row: walk sub-vectors in column order, write CSR entries and masks.
 __global__ __launch_bounds__(kRowThreads) void k_sel_compact(
-    const float* __restrict__ W, const float* __restrict__ h, int64_t N, int d,
+    const float* __restrict__ W, const float* __restrict__ h, int64_t N, int d, bool vec8,
     const SelState* __restrict__ st, const int* __restrict__ take,
     const int32_t* __restrict__ row_ptr, int64_t nnz, int32_t* __restrict__ col,
     float* __restrict__ val, uint8_t* __restrict__ mask)
@@ -230,10 +270,13 @@ __global__ __launch_bounds__(kRowThreads) void k_sel_compact(
         uint32_t bits[8];
         int n_eq = 0;
         if (b < nb) {
-            for (int t = 0; t < d; ++t) {
-                bits[t] = score_bits(W, h, i * N + b * d + t, N);
-                n_eq += bits[t] == tau;
+            if (vec8) {
+                score4(W, h, i, N, b * 8, *reinterpret_cast<uint32_t(*)[4]>(&bits[0]));
+                score4(W, h, i, N, b * 8 + 4, *reinterpret_cast<uint32_t(*)[4]>(&bits[4]));
+            } else {
+                for (int t = 0; t < d; ++t) bits[t] = score_of(W[i * N + b * d + t], h[b * d + t]);
             }
+            for (int t = 0; t < d; ++t) n_eq += bits[t] == tau;
         }
         const int eq_incl = scan256(n_eq, sh);
         int eq_rank = eq_run + eq_incl - n_eq;
@@ -590,6 +633,9 @@ vq_status select_launch(const float* W, const float* h, int64_t M, int64_t N, in
     int* take = cv.take<int>((size_t)M);
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_sparse_select: workspace too small");
     const int64_t total = M * N;
+    (void)total;
+    // 16-byte loads of W's rows and of h: rows of whole float4 groups
+    const bool vec = N % 4 == 0 && ((reinterpret_cast<uintptr_t>(W) | reinterpret_cast<uintptr_t>(h)) & 15u) == 0;
     TimedRegion tr("select", 0, st);
 
     // nnz == 0 skips the threshold search: the initial threshold pattern
@@ -600,22 +646,22 @@ vq_status select_launch(const float* W, const float* h, int64_t M, int64_t N, in
         const int shifts[3] = {21, 10, 0};
         const int nbins[3] = {2048, 2048, 1024};
         const uint32_t pmasks[3] = {0u, 0xFFE00000u, 0xFFFFFC00u};
-        const unsigned hb = (unsigned)std::min<int64_t>(kHistBlocks, grid_for(total, 256 * 16));
+        const unsigned hb = (unsigned)std::min<int64_t>(kHistBlocks, M);
         for (int p = 0; p < 3; ++p) {
-            hipLaunchKernelGGL(k_sel_hist, dim3(hb), dim3(256), 0, st, W, h, total, N, state, pmasks[p],
+            hipLaunchKernelGGL(k_sel_hist, dim3(hb), dim3(256), 0, st, W, h, M, N, vec, state, pmasks[p],
                                shifts[p], (uint32_t)(nbins[p] - 1), hist);
             VQ_LAUNCHED("k_sel_hist");
             hipLaunchKernelGGL(k_sel_pick, dim3(1), dim3(256), 0, st, state, hist, shifts[p], nbins[p]);
             VQ_LAUNCHED("k_sel_pick");
         }
     }
-    hipLaunchKernelGGL(k_sel_row_count, dim3((unsigned)M), dim3(kRowThreads), 0, st, W, h, N, state, cgt,
+    hipLaunchKernelGGL(k_sel_row_count, dim3((unsigned)M), dim3(kRowThreads), 0, st, W, h, N, vec, state, cgt,
                        ceq);
     VQ_LAUNCHED("k_sel_row_count");
     hipLaunchKernelGGL(k_sel_rows, dim3(1), dim3(kScanThreads), 0, st, state, M, cgt, ceq, take, row_ptr);
     VQ_LAUNCHED("k_sel_rows");
-    hipLaunchKernelGGL(k_sel_compact, dim3((unsigned)M), dim3(kRowThreads), 0, st, W, h, N, d, state,
-                       take, row_ptr, nnz, col, val, mask);
+    hipLaunchKernelGGL(k_sel_compact, dim3((unsigned)M), dim3(kRowThreads), 0, st, W, h, N, d, vec && d == 8,
+                       state, take, row_ptr, nnz, col, val, mask);
     VQ_LAUNCHED("k_sel_compact");
     return VQ_OK;
 }
