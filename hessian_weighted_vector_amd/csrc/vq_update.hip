@@ -4,9 +4,9 @@
 // exact minimizer of the objective is the per-dimension weighted mean).
 //
 // Design (no floating-point atomics; bitwise deterministic):
-//   1. buckets (K > 256 only): one stable scatter by idx >> 7 moves whole
+//   1. buckets (K > 256 only): one stable scatter by idx >> 8 moves whole
 //      records (the sub-vector's d values and a word holding its id, mask
-//      byte and idx & 127) into 128-centroid buckets, so no sub-vector is
+//      byte and idx & 255) into 256-centroid buckets, so no sub-vector is
 //      gathered at random later.  Each 2048-record tile is ordered by bucket
 //      in LDS first (ranks from wavefront ballots: stable), then written out
 //      as contiguous runs.  Tile digit counts use LDS integer atomics
@@ -33,8 +33,9 @@ namespace {
 
 constexpr int kTile = 2048;          // records per scatter tile
 constexpr int kTileThreads = 1024;   // two records per thread
-constexpr int kMaxBuckets = 512;     // K <= 65536, 128 centroids per bucket
-constexpr int kBucketShift = 7;
+constexpr int kMaxBuckets = 256;     // K <= 65536, 256 centroids per bucket
+constexpr int kBucketShift = 8;
+constexpr int kWidth = 1 << kBucketShift;
 constexpr int kSub = 1024;           // records per LDS sub-chunk
 constexpr int kRedThreads = 512;     // two records per thread
 constexpr int kPieceMax = 32768;     // records per piece in bucket mode
@@ -182,7 +183,7 @@ __device__ inline void wave_excl_scan(const int* cnt, int n, T* out)
 // ranked by bucket (wavefront ballots + a prefix over the wavefronts), laid
 // out in bucket order in LDS, and written to its place in each bucket as
 // contiguous runs: rx gets the d values, rw the word
-//   id | (idx & 127) << 32 | mask << 40.
+//   id | (idx & 255) << 32 | mask << 40.
 __global__ __launch_bounds__(kTileThreads) void k_bucket_scatter(
     const uint16_t* __restrict__ idx, const uint8_t* __restrict__ mask, const float* __restrict__ X, int d,
     int64_t n, int nbk, const int* __restrict__ hist, int ntile, const int64_t* __restrict__ bstart,
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(kTileThreads) void k_bucket_scatter(
             for (int t = 0; t < d; ++t) sxr[lp * 8 + t] = X[e * d + t];
         }
         const uint64_t mk = (uint64_t)mkv[h];
-        sw[lp] = (uint64_t)(uint32_t)e | ((uint64_t)(iv[h] & 127) << 32) | (mk << 40);
+        sw[lp] = (uint64_t)(uint32_t)e | ((uint64_t)(iv[h] & (kWidth - 1)) << 32) | (mk << 40);
         sdg[lp] = (uint16_t)dg[h];
     }
     __syncthreads();
@@ -317,14 +318,15 @@ __device__ inline void add_term(double& num, double& den, float h, float x, doub
 // kSegs (pass, wavefront) segments, taken in record order, give a stable
 // counting sort of the sub-chunk.  Then the owner lanes walk their
 // centroid's members in record order, lane = (centroid, part of the
-// dimensions): W = 256 (one bucket read in place from X, idx and mask), two
-// lanes per centroid, four dimensions each; W = 128 (scattered buckets
-// rx/rw), four lanes per centroid, two dimensions each.
+// dimensions): two lanes per centroid, four dimensions each (W = 256), or
+// four lanes per centroid, two dimensions each (W = 128).  DIRECT: one
+// bucket read in place from X, idx and mask; otherwise the scattered
+// buckets rx/rw.
 // Sums stay in registers across the piece.
 constexpr int kPer = kSub / kRedThreads;
 constexpr int kSegs = kPer * (kRedThreads / 64);
 
-template <int W>
+template <int W, bool DIRECT>
 __global__ __launch_bounds__(kRedThreads) void k_piece_reduce(
     const float* __restrict__ rx, const uint64_t* __restrict__ rw, const float* __restrict__ X,
     const uint16_t* __restrict__ idx, const uint8_t* __restrict__ mask, const float* __restrict__ hcol,
@@ -332,8 +334,8 @@ __global__ __launch_bounds__(kRedThreads) void k_piece_reduce(
     const int64_t* __restrict__ bstart, const int* __restrict__ poff, float* __restrict__ C,
     int32_t* __restrict__ counts, double* __restrict__ partial)
 {
-    constexpr bool kDirect = (W == 256);
-    constexpr int KB = kDirect ? 8 : 7;            // key bits
+    constexpr bool kDirect = DIRECT;
+    constexpr int KB = W == 256 ? 8 : 7;           // key bits
     constexpr int DP = 8 * W / kRedThreads;        // dimensions per owner lane
     static_assert(DP == 4 || DP == 2, "owner layout");
     __shared__ __align__(16) float sx[kSub * 8];
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(kRedThreads) void k_piece_reduce(
     const bool vx = (d == 8) && ((reinterpret_cast<uintptr_t>(kDirect ? X : rx) & 15) == 0);
     const bool vh = (d == 8) && ((reinterpret_cast<uintptr_t>(hcol) & 15) == 0);
     const int oc = tid % W;                 // owned centroid within the bucket
-    const int oq = tid / W;                 // owned dimension part (W = 128)
+    const int oq = tid / W;                 // owned dimension part
     double num[DP], den[DP];
 #pragma unroll
     for (int t = 0; t < DP; ++t) { num[t] = 0.0; den[t] = 0.0; }
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(kRedThreads) void k_piece_reduce(
     struct Raw {
         float4 xa, xb, ha, hb;
         float rv;
-        uint64_t wd;        // scattered record word (W = 128)
+        uint64_t wd;        // scattered record word (not DIRECT)
         uint32_t sv, kraw, mk;
         bool valid;
     };
@@ -586,13 +588,13 @@ __global__ __launch_bounds__(kRedThreads) void k_piece_reduce(
 }
 
 // Buckets with several pieces (and empty buckets, whose counts are zeroed):
-// one workgroup per centroid (16 of one bucket when buckets hold 128); thread = (group q of 32,
+// one workgroup per cpb centroids of one bucket; thread = (group q of 32,
 // dimension t).  Group q adds pieces q, q + 32, ... in order, four loads in
 // flight; the 32 group sums are then combined in a fixed pattern (a
 // butterfly within each wavefront, the four wavefront sums in order) and
 // divided once.
-__global__ __launch_bounds__(256) void k_piece_finish(const int* __restrict__ poff, int nbk, int width, int K,
-                                                      int d, const double* __restrict__ partial,
+__global__ __launch_bounds__(256) void k_piece_finish(const int* __restrict__ poff, int nbk, int width, int cpb,
+                                                      int K, int d, const double* __restrict__ partial,
                                                       float* __restrict__ C, int32_t* __restrict__ counts)
 {
     __shared__ double wnum[4][8], wden[4][8], wcntd[4];
@@ -601,7 +603,6 @@ __global__ __launch_bounds__(256) void k_piece_finish(const int* __restrict__ po
     const int t = tid & 7, qg = tid >> 3;
     // workgroup: centroids [k0, k0 + cpb) of one bucket; a bucket finished
     // inside its piece ends the workgroup at once
-    const int cpb = width == 256 ? 1 : 16;
     const int k0 = blockIdx.x * cpb;
     if (k0 >= K || k0 / width >= nbk) return;
     if (poff[k0 / width + 1] - poff[k0 / width] == 1) return;
@@ -683,7 +684,7 @@ int piece_size(int64_t n_sub, int K)
 
 int64_t max_pieces(int64_t n_sub, int K)
 {
-    const int nbk = K > 256 ? (K + 127) / 128 : 1;
+    const int nbk = K > 256 ? (K + kWidth - 1) / kWidth : 1;
     return (n_sub + piece_size(n_sub, K) - 1) / piece_size(n_sub, K) + nbk;
 }
 
@@ -725,8 +726,11 @@ vq_status update_launch(const float* X, const float* hcol, const float* rho, con
     if (n_sub > (int64_t)UINT32_MAX) return fail(VQ_ERR_UNSUPPORTED, "vq_update: more than 2^32 sub-vectors");
     TimedRegion tr("update", K, st);
     const bool bucketed = K > 256;
-    const int nbk = bucketed ? (K + 127) / 128 : 1;
-    const int width = bucketed ? 128 : 256;
+    const int nbk = bucketed ? (K + kWidth - 1) / kWidth : 1;
+    const int width = bucketed ? kWidth : 256;
+    // the merge: per workgroup 16 centroids of one bucket when there are
+    // many buckets (a workgroup per centroid would mostly exit at once)
+    const int cpb = bucketed ? 16 : 1;
     const int piece = piece_size(n_sub, K);
     if (bucketed) {
         const int ntile = (int)((n_sub + kTile - 1) / kTile);
@@ -744,17 +748,16 @@ vq_status update_launch(const float* X, const float* hcol, const float* rho, con
         VQ_LAUNCHED("k_piece_setup");
     }
     if (bucketed)
-        hipLaunchKernelGGL(k_piece_reduce<128>, dim3((unsigned)max_pieces(n_sub, K)), dim3(kRedThreads), 0, st, w.rx,
+        hipLaunchKernelGGL((k_piece_reduce<kWidth, false>), dim3((unsigned)max_pieces(n_sub, K)), dim3(kRedThreads), 0, st, w.rx,
                            w.rw, X, idx, mask, hcol, rho, (uint32_t)(N / d), d, K, nbk, piece, w.bstart, w.poff, C,
                            counts, w.partial);
     else
-        hipLaunchKernelGGL(k_piece_reduce<256>, dim3((unsigned)max_pieces(n_sub, K)), dim3(kRedThreads), 0, st,
+        hipLaunchKernelGGL((k_piece_reduce<256, true>), dim3((unsigned)max_pieces(n_sub, K)), dim3(kRedThreads), 0, st,
                            nullptr, w.rw, X, idx, mask, hcol, rho, (uint32_t)(N / d), d, K, nbk, piece, w.bstart,
                            w.poff, C, counts, w.partial);
     VQ_LAUNCHED("k_piece_reduce");
-    hipLaunchKernelGGL(k_piece_finish, dim3((unsigned)((K + (bucketed ? 15 : 0)) / (bucketed ? 16 : 1))), dim3(256), 0,
-                       st, w.poff, nbk, width, K, d,
-                       w.partial, C, counts);
+    hipLaunchKernelGGL(k_piece_finish, dim3((unsigned)((K + cpb - 1) / cpb)), dim3(256), 0, st, w.poff, nbk, width,
+                       cpb, K, d, w.partial, C, counts);
     VQ_LAUNCHED("k_piece_finish");
     return VQ_OK;
 }
