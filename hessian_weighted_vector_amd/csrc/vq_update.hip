@@ -40,6 +40,7 @@ constexpr int kSub = 1024;           // records per LDS sub-chunk
 constexpr int kRedThreads = 512;     // two records per thread
 constexpr int kPieceMax = 32768;     // records per piece in bucket mode
 constexpr int kDirectPieces = 512;   // target piece count with one bucket
+constexpr int kMinPieces = 256;      // target piece count with few buckets
 
 // Per-tile bucket histogram: hist[bucket * ntile + tile].
 __global__ __launch_bounds__(256) void k_bucket_hist(const uint16_t* __restrict__ idx, int64_t n, int nbk,
@@ -672,11 +673,19 @@ struct UpdateWs {
     double* partial;
 };
 
-// Records per piece: bucket mode kPieceMax; one bucket: about kDirectPieces
-// pieces, a multiple of kSub.
+// Records per piece, a multiple of kSub: bucket mode kPieceMax when there
+// are enough buckets to fill the device (a bucket then usually stays one
+// piece, with no merge), else about kMinPieces pieces in all; one bucket:
+// about kDirectPieces pieces.
 int piece_size(int64_t n_sub, int K)
 {
-    if (K > 256) return kPieceMax;
+    if (K > 256) {
+        const int nbk = (K + kWidth - 1) / kWidth;
+        if (nbk >= kMinPieces) return kPieceMax;
+        int64_t p = (n_sub + kMinPieces - 1) / kMinPieces;
+        p = (p + kSub - 1) / kSub * kSub;
+        return (int)std::max<int64_t>(kSub, std::min<int64_t>(kPieceMax, p));
+    }
     int64_t p = (n_sub + kDirectPieces - 1) / kDirectPieces;
     p = (p + kSub - 1) / kSub * kSub;
     return (int)std::max<int64_t>(kSub, std::min<int64_t>(kPieceMax, p));
