@@ -59,6 +59,7 @@ constexpr int kSlotChunks = 8;            // codebooks of <= 8 chunks use per-sl
 constexpr int kCminChunks = 8;            // chunks per workgroup of the chunk-minimum pass
 constexpr int kCminCap = 32768;           // flagged sub-vectors the chunk path takes at most
 constexpr int kCminListBlocks = 64;       // list blocks of the chunk-minimum grid (grid-stride)
+constexpr int kBlockPatterns = 4;         // shared weight patterns per column block (bias pairs in k-slots 8-15)
 constexpr float kPadSq = 16384.0f;           // scaled c*c term of padding centroids
 
 constexpr int kMaxBlocks = 256;   // blocks of the codebook max reduction
@@ -313,10 +314,13 @@ __device__ __forceinline__ f32x16 tile_h16(const h16x8 ah, const h16x8 al, const
     return acc;
 }
 
-// The majority mask byte of each column block (lowest byte on ties): the
-// weight pattern shared by most of its sub-vectors.
+// The (up to) four most frequent mask bytes of each column block, most
+// frequent first and the lower byte first among equal counts, packed one
+// byte each into a 32-bit word; a block with fewer distinct bytes repeats its
+// first in the remaining slots.  Sub-vectors with one of these bytes share
+// that byte's weights with the rest of its class.
 __global__ __launch_bounds__(256) void k_block_pattern(const uint8_t* __restrict__ mask, int64_t M, int64_t nb,
-                                                       uint8_t* __restrict__ pattern)
+                                                       uint32_t* __restrict__ pattern)
 {
     __shared__ int cnt[256];
     __shared__ int best_c[256], best_p[256];
@@ -325,27 +329,46 @@ __global__ __launch_bounds__(256) void k_block_pattern(const uint8_t* __restrict
     const int64_t b = blockIdx.x;
     for (int64_t i = threadIdx.x; i < M; i += 256) atomicAdd(&cnt[mask[i * nb + b]], 1);
     __syncthreads();
-    best_c[threadIdx.x] = cnt[threadIdx.x];
-    best_p[threadIdx.x] = threadIdx.x;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) {
-            const int oc = best_c[threadIdx.x + w], op = best_p[threadIdx.x + w];
-            if (oc > best_c[threadIdx.x] || (oc == best_c[threadIdx.x] && op < best_p[threadIdx.x])) {
-                best_c[threadIdx.x] = oc;
-                best_p[threadIdx.x] = op;
+    uint32_t word = 0;
+    for (int q = 0; q < kBlockPatterns; ++q) {
+        best_c[threadIdx.x] = cnt[threadIdx.x];
+        best_p[threadIdx.x] = threadIdx.x;
+        __syncthreads();
+        for (int w = 128; w > 0; w >>= 1) {
+            if ((int)threadIdx.x < w) {
+                const int oc = best_c[threadIdx.x + w], op = best_p[threadIdx.x + w];
+                if (oc > best_c[threadIdx.x] || (oc == best_c[threadIdx.x] && op < best_p[threadIdx.x])) {
+                    best_c[threadIdx.x] = oc;
+                    best_p[threadIdx.x] = op;
+                }
             }
+            __syncthreads();
         }
+        const int c = best_c[0], p = best_p[0];
+        // slot 0 always has a count >= 1 (M >= 1); an empty slot repeats it
+        word |= (uint32_t)(c > 0 ? p : (int)(word & 0xFFu)) << (8 * q);
+        __syncthreads();
+        if (threadIdx.x == 0) cnt[p] = -1;
         __syncthreads();
     }
-    if (threadIdx.x == 0) pattern[b] = (uint8_t)best_p[0];
+    if (threadIdx.x == 0) pattern[b] = word;
 }
 
-// Sub-vectors whose mask byte differs from their block's pattern are listed
+// Slot (0-3) of mask byte mb among a block's pattern word, or -1.
+__device__ __forceinline__ int pattern_slot(uint32_t word, unsigned mb)
+{
+    int q = -1;
+#pragma unroll
+    for (int t = kBlockPatterns - 1; t >= 0; --t)
+        if (((word >> (8 * t)) & 0xFFu) == mb) q = t;
+    return q;
+}
+
+// Sub-vectors whose mask byte is none of their block's patterns are listed
 // for the general kernel: wavefront ballots, a workgroup prefix in LDS and
 // one integer atomic per workgroup (the order of the list does not affect
 // any result).
-__global__ __launch_bounds__(1024) void k_dirty(const uint8_t* __restrict__ mask, const uint8_t* __restrict__ pattern,
+__global__ __launch_bounds__(1024) void k_dirty(const uint8_t* __restrict__ mask, const uint32_t* __restrict__ pattern,
                                                 int64_t n_sub, uint32_t nb, int* __restrict__ count,
                                                 int* __restrict__ list)
 {
@@ -359,7 +382,7 @@ __global__ __launch_bounds__(1024) void k_dirty(const uint8_t* __restrict__ mask
     for (int r = 0; r < kItems; ++r) {
         const int64_t s = ((int64_t)blockIdx.x * kItems + r) * 1024 + threadIdx.x;
         take[r] = false;
-        if (s < n_sub) take[r] = mask[s] != pattern[(uint32_t)(s % nb)];
+        if (s < n_sub) take[r] = pattern_slot(pattern[(uint32_t)(s % nb)], mask[s]) < 0;
         ball[r] = __ballot(take[r]);
         if (lane == 0) wsum[r][wave] = __popcll(ball[r]);
     }
@@ -668,30 +691,38 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(SLO
                           kt1, S_sc, shift_s, idx, dist, flag_count, flag_list);
 }
 
-// Sub-vectors that share one weight vector: workgroup = column block b x
-// 256*NS consecutive rows (wavefront w: NS sets of 32 rows, set u holding rows
-// (rb*8 + w)*32*NS + u*32 + (l & 31)), taken with the block's majority mask
-// byte.  Every A operand read from LDS feeds the MFMAs of all NS sets, so the
-// LDS traffic per MFMA falls as 1/NS.  Their common weights make
-// sum_t omega_t c_t^2 a per-centroid bias.  The workgroup forms it once per
-// chunk in float64 (rounded once to fp32), scales it by 2^sb and splits it
-// into two fp16 parts that enter the second MFMA through two k-slots against
-// a power-of-two gamma on the B side.  A tile then takes two MFMAs:
+// Sub-vectors whose weights are one of a few per block: workgroup = column
+// block b x 256*NS consecutive rows (wavefront w: NS sets of 32 rows, set u
+// holding rows (rb*8 + w)*32*NS + u*32 + (l & 31)).  Every A operand read from
+// LDS feeds the MFMAs of all NS sets, so the LDS traffic per MFMA falls as
+// 1/NS.  The block's pattern word names up to four mask bytes; the sub-vectors
+// with pattern q share the weights omega_q, which make sum_t omega_qt c_t^2 a
+// per-centroid bias of that class.  The workgroup forms the four biases once
+// per chunk in float64 (fused multiply-adds, each sum rounded once to fp32;
+// the threads that stage the chunk's centroid rows do it: spreading it over
+// every wavefront or into the tile loop measured slower), scales them by 2^sb and
+// splits each into two fp16 parts; they fill k-slots 8-15 of the second
+// MFMA's A operand, and the B operand of a sub-vector of class q holds a
+// power-of-two gamma in slots 8+2q and 9+2q and zeros elsewhere.  A tile then
+// takes two MFMAs:
 //   1: lower half al(-2 beta c) . bh(alpha omega x), upper half ah(-2 beta c) . bl(alpha omega x)
-//   2: lower half ah(-2 beta c) . bh(alpha omega x), upper half [bias_hi, bias_lo] . [gamma, gamma]
+//   2: lower half ah(-2 beta c) . bh(alpha omega x),
+//      upper half [b0_hi, b0_lo, .., b3_hi, b3_lo] . [0, .., gamma, gamma, .., 0]
 // with gamma = alpha * beta * 2^-sb.  alpha is capped so that gamma <= 2^15.
 // A lane whose gamma would fall below 2^-24 is sent to the exact re-search.
 // The general form's error bound holds: the bias is within 1.25u of
-// sum omega c*c, and the last MFMA adds 10 products to a small accumulator.
-// Lanes whose own mask byte differs from the block's are computed but not
-// written: they are in the list of the general kernel.
+// sum omega c*c, and the last MFMA adds 10 nonzero products (the others are
+// exact zeros) to a small accumulator.  Lanes whose mask byte is none of the
+// block's patterns are computed (with pattern 0) but not written: they are in
+// the list of the general kernel.
 template <bool SLOT, int NS>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS == 1 ? 4 : (NS == 2 ? 3 : 2), 8))) void k_assign_h16s(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
-    const uint8_t* __restrict__ mask, const uint8_t* __restrict__ pattern, int64_t M, int64_t nb, int d,
+    const uint8_t* __restrict__ mask, const uint32_t* __restrict__ pattern, int64_t M, int64_t nb, int d,
     const uint4* __restrict__ P, const float* __restrict__ cmax, const float* __restrict__ C, int K, int nchunks,
     uint16_t* __restrict__ idx, float* __restrict__ dist, int* __restrict__ flag_count, int* __restrict__ flag_list)
 {
+    static_assert(kBlockPatterns * 2 == 8, "the four bias pairs fill k-slots 8-15");
     constexpr int kRowVec = kChunkTiles * 96;    // uint4 per chunk: rows (lo, hi, bias) of 32 per tile
     static_assert(kChunkTiles * 64 == kWaves * 64, "one cross-term uint4 per thread per chunk");
     static_assert(kChunkTiles % 2 == 0, "tiles are processed in pairs");
@@ -705,32 +736,38 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
     // NS sets of 32 rows per wave: set u holds rows w0 + u*32 + (l & 31)
     const int64_t w0 = (rb * kWaves + wave) * (int64_t)(kSubPerWave * NS);
     const bool active = w0 < M;                                   // wave-uniform
-    const unsigned pat = pattern ? pattern[b] : 0u;
-    // Row i of set u, its sub-vector id s and whether its weights are the
-    // block's; formed before the main loop and again after it (r is passed
+    const uint32_t pw = (uint32_t)__builtin_amdgcn_readfirstlane((int)(pattern ? pattern[b] : 0u));
+    // Row i of set u, its sub-vector id s, whether its weights are one of the
+    // block's patterns (owner), its pattern slot q and the mask byte mq its
+    // operands are formed with (pattern 0's for a lane that is not an
+    // owner); formed before the main loop and again after it (r is passed
     // through an empty asm so the second forming is not merged with the
     // first: keeping these per-set values alive across the loop would spill).
-    auto row_of = [&](int u, int r, int64_t& s, bool& valid, bool& owner) {
+    auto row_of = [&](int u, int r, int64_t& s, bool& valid, bool& owner, int& q, unsigned& mq) {
         const int64_t i = w0 + u * kSubPerWave + r;
         valid = i < M;
         s = valid ? i * nb + b : 0;
         const unsigned mb = (valid && mask) ? mask[s] : 0u;
-        owner = valid && mb == pat;
+        const int qs = pattern_slot(pw, mb);
+        owner = valid && qs >= 0;
+        q = qs >= 0 ? qs : 0;
+        mq = (pw >> (8 * q)) & 0xFFu;
     };
 
-    // the block's weights (its majority pattern), the same in every lane:
-    // kept in scalar registers
-    float om[8];
+    // the block's column weights (no mask), the same in every lane: kept in
+    // scalar registers
+    float hb[8];
     float wsum = 0.f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const float w = (t < d && !((pat >> t) & 1u)) ? hcol[b * d + t] : 0.f;
-        om[t] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, w)));
-        wsum += om[t];
+        const float w = t < d ? hcol[b * d + t] : 0.f;
+        hb[t] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, w)));
+        wsum += hb[t];
     }
     int e1, e2;
     cb_exponents(*cmax, e1, e2);
-    // bias scale: every bias_k <= sum_t omega_t * max c^2 (margin for roundings)
+    // bias scale: every pattern's bias_k <= sum_t h_t * max c^2 (margin for
+    // roundings)
     const float cm = *cmax;
     const float bmax = wsum * (cm * cm) * 1.0001f;
     int eb = 0;
@@ -739,7 +776,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
 
     // The sub-vector's scaled split B operands, its scaled energy S_sc, its
     // scale exponent and whether gamma underflows.
-    auto prep = [&](int64_t s, bool valid, h16x8& bA, h16x8& bB, float& S_sc, int& shift_s, bool& bad) {
+    auto prep = [&](int64_t s, bool valid, int q, unsigned mq, h16x8& bA, h16x8& bB, float& S_sc, int& shift_s,
+                    bool& bad) {
+        float om[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) om[t] = ((mq >> t) & 1u) ? 0.f : hb[t];
         float raw[8];
         float S = 0.f, mx = 0.f;
         float xs[8];
@@ -773,10 +814,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
             bh[t] = h;
             bl[t] = l;
         }
-        h16x8 gv = {};
+        h16x8 gv;
         const _Float16 g = (_Float16)ldexpf(1.f, max(gexp, -24));
-        gv[0] = g;
-        gv[1] = g;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gv[j] = (j >> 1) == q ? g : (_Float16)0.f;
         bA = half ? bl : bh;
         bB = half ? gv : bh;
         shift_s = sh + (15 - e1);
@@ -788,14 +829,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
         int64_t s;
         bool valid, owner, bad;
         float S_sc;
-        int shift_s;
-        row_of(u, lane & 31, s, valid, owner);
-        prep(s, valid, bA[u], bB[u], S_sc, shift_s, bad);
+        int shift_s, q;
+        unsigned mq;
+        row_of(u, lane & 31, s, valid, owner, q, mq);
+        prep(s, valid, q, mq, bA[u], bB[u], S_sc, shift_s, bad);
     }
 
     // chunk staging: thread q copies one cross-term uint4 (tile q/64, row
-    // (q/32)&1: 0 = lo, 1 = hi, position q&31); threads q < 256 form the bias
-    // part of centroid q of the chunk
+    // (q/32)&1: 0 = lo, 1 = hi, position q&31); threads q < 256 form the four
+    // biases of centroid q of the chunk
     const int ct = threadIdx.x >> 6, crow = (threadIdx.x >> 5) & 1, cpos = threadIdx.x & 31;
     const bool vecC = d == 8 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
     auto load_cross = [&](int c) -> uint4 {
@@ -821,21 +863,29 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
         lds[buf][ct * 96 + crow * 32 + cpos] = cross;
         if (threadIdx.x < kChunkTiles * kTile) {
             const int k = c * kChunkTiles * kTile + (int)threadIdx.x;
-            float a;
-            if (k < K) {
-                const double cv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-                double acc = 0.0;
+            const double cv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+            double c2[8];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) acc = acc + (double)om[t] * (cv[t] * cv[t]);
-                a = ldexpf((float)acc, sb);
-            } else {
-                a = kPadSq;
+            for (int t = 0; t < 8; ++t) c2[t] = cv[t] * cv[t];   // exact
+            // one float64 fused multiply-add per term (a masked term adds
+            // an exact zero); the sum is rounded once to fp32
+            h16x8 v;
+#pragma unroll
+            for (int q = 0; q < kBlockPatterns; ++q) {
+                const unsigned mq = (pw >> (8 * q)) & 0xFFu;
+                float a = kPadSq;
+                if (k < K) {
+                    double acc = 0.0;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        acc = __builtin_fma((double)(((mq >> t) & 1u) ? 0.f : hb[t]), c2[t], acc);
+                    a = ldexpf((float)acc, sb);
+                }
+                _Float16 h, l;
+                split_h16(a, h, l);
+                v[2 * q] = h;
+                v[2 * q + 1] = l;
             }
-            _Float16 h, l;
-            split_h16(a, h, l);
-            h16x8 v = {};
-            v[0] = h;
-            v[1] = l;
             const int tt = threadIdx.x >> 5, m = threadIdx.x & 31;
             lds[buf][tt * 96 + 64 + m] = __builtin_bit_cast(uint4, v);
         }
@@ -901,10 +951,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
         int64_t s;
         bool valid, owner, bad;
         float S_sc;
-        int shift_s;
+        int shift_s, q;
+        unsigned mq;
         h16x8 ua, ub;
-        row_of(u, r, s, valid, owner);
-        prep(s, valid, ua, ub, S_sc, shift_s, bad);
+        row_of(u, r, s, valid, owner, q, mq);
+        prep(s, valid, q, mq, ua, ub, S_sc, shift_s, bad);
         search_epilogue<SLOT>(X, hcol, rho, mask, nb, d, C, K, s, valid, owner, bad, wsum == 0.f, lane, half, b1[u],
                               b2[u], kt1[u], S_sc, shift_s, idx, dist, flag_count, flag_list);
     }
@@ -1186,8 +1237,9 @@ inline int padded_K(int K) { return (K + kChunkK - 1) / kChunkK * kChunkK; }
 size_t ws_assign(int64_t n_sub, int K)
 {
     // split codebook (64 bytes per centroid), flag counter, flag list, max |c|,
-    // partial maxima, dirty counter, dirty list, block patterns (at most n_sub
-    // column blocks)
+    // partial maxima, dirty counter, dirty list, block pattern words (4 bytes
+    // per column block: at most n_sub bytes when there are 4 rows or more;
+    // fewer rows do not classify blocks)
     return align_up((size_t)padded_K(K) * 64) + align_up(sizeof(int)) + align_up((size_t)n_sub * sizeof(int)) +
            align_up(sizeof(float)) + align_up(sizeof(float) * kMaxBlocks) + align_up(sizeof(int)) +
            align_up((size_t)n_sub * sizeof(int)) + align_up((size_t)n_sub);
@@ -1209,7 +1261,10 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
     float* part = cv.take<float>(kMaxBlocks);
     int* dirty_count = cv.take<int>(1);
     int* dirty_list = cv.take<int>((size_t)n_sub);
-    uint8_t* pattern = cv.take<uint8_t>((size_t)nb);
+    // blocks are classified when there are at least 4 rows (their pattern
+    // words then fit in the n_sub bytes the workspace holds for them)
+    const bool classify = mask != nullptr && M >= 4;
+    uint32_t* pattern = classify ? cv.take<uint32_t>((size_t)nb) : nullptr;
     if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_assign: workspace too small");
     if (n_sub > (int64_t)INT32_MAX) return fail(VQ_ERR_UNSUPPORTED, "vq_assign: more than 2^31 sub-vectors");
     const int64_t shared_groups = (M + kSharedRows - 1) / kSharedRows * nb;
@@ -1227,7 +1282,13 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
         TimedRegion tr("assign_search", K, st);
         const int nch = Kpad / kChunkK;
         const bool slot = nch <= kSlotChunks;
-        if (slot) {
+        if (!slot && mask && !classify) {
+            // long codebook, masked, fewer than 4 rows: the general form for all
+            hipLaunchKernelGGL(k_assign_h16<false>, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st, X,
+                               hcol, rho, mask, n_sub, nb, d, P, cmax, C, K, nch, nullptr, nullptr, idx, dist,
+                               flag_count, flag_list);
+            VQ_LAUNCHED("k_assign_h16");
+        } else if (slot) {
             // short codebooks: one pass of the general form (the block
             // classification would cost more than the shared form saves)
             hipLaunchKernelGGL(k_assign_h16<true>, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st, X,

@@ -60,6 +60,7 @@ ASSIGN_CASES = [
     (10, 96, 96, 6, 200, True, True),
     (11, 256, 512, 8, 3000, True, True),   # long codebook: per-tile tracking, last tile re-formed
     (12, 300, 96, 3, 2500, True, False),   # long codebook, d = 3, ragged last chunk
+    (13, 3, 6400, 8, 2200, True, True),    # long codebook, masked, fewer than 4 rows (no block classes)
 ]
 
 
@@ -78,15 +79,36 @@ def test_assign_matches_oracle_bitwise(case):
     assert bits_equal(host(dist), ref_dist.astype(np.float32))
 
 
-@pytest.mark.parametrize("mode", ["no-mask", "zero-mask", "salient"])
+def _many_pattern_keep(M, N, d, seed):
+    """Per column block, mask bytes drawn from six candidates (0xFF, fully
+    masked, among them) with uneven frequencies, so most blocks have more than
+    four classes; block 0 has five bytes with equal counts (the four lowest
+    bytes are its classes) and block 1 a single byte."""
+    g = np.random.default_rng([77, seed])
+    nb = N // d
+    mb = np.zeros((M, nb), np.uint8)
+    for b in range(nb):
+        cand = g.choice(256, 6, replace=False).astype(np.uint8)
+        cand[g.integers(6)] = 0xFF
+        mb[:, b] = cand[g.choice(6, M, p=g.dirichlet(np.ones(6)))]
+    assert M % 5 == 0
+    mb[:, 0] = np.repeat(np.array([9, 200, 3, 0xFF, 17], np.uint8), M // 5)[g.permutation(M)]
+    mb[:, 1] = 0x24
+    return keep_from_mask(mb.ravel(), M, N, d)
+
+
+@pytest.mark.parametrize("mode", ["no-mask", "zero-mask", "salient", "many-patterns"])
 def test_assign_long_codebook_block_shared_weights(mode):
-    # K > 2048: sub-vectors of a column block that share its weights take the
-    # two-MFMA form, the others (their own mask byte) the three-MFMA form
+    # K > 2048: sub-vectors whose mask byte is one of their column block's
+    # four most frequent take the two-MFMA form, the others (their own mask
+    # byte) the three-MFMA form
     say("assign long codebook", mode)
     M, N, d, K = 640, 256, 8, 2600          # 2.5 row groups of 256, ragged codebook chunk
     W, h, C, keep, rho = _case(41, M, N, d, K, masked=(mode != "no-mask"), with_rho=True)
     if mode == "zero-mask":
         keep = np.ones_like(keep)
+    if mode == "many-patterns":
+        keep = _many_pattern_keep(M, N, d, 41)
     ref_idx, ref_dist = oracle.assign(W, h, rho, keep, d, C)
     ws = vq.workspace(M, N, d, K)
     mask = None if keep is None else dev(mask_from_keep(keep, d))
