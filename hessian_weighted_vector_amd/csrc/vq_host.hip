@@ -388,19 +388,33 @@ vq_status update_with_J(const float* X, const float* hcol, const float* rho, con
                          ws_bytes - wo, st);
 }
 
-// Centroids with no member: one workgroup counts the zero entries of
-// counts[0..K) (per-lane counts, a wavefront butterfly, the four wavefront
-// sums in order) and writes the total to *out.
-__global__ __launch_bounds__(256) void k_count_empty(const int32_t* __restrict__ counts, int K,
-                                                     unsigned long long* __restrict__ out)
+// Centroids with no member: one workgroup of 1024 counts the zero entries
+// of counts[0..K) (16-byte loads when K % 4 == 0 and the array allows, a
+// wavefront butterfly, the 16 wavefront sums in order: an exact integer
+// count) and writes the total to *out.
+__global__ __launch_bounds__(1024) void k_count_empty(const int32_t* __restrict__ counts, int K,
+                                                      unsigned long long* __restrict__ out)
 {
-    __shared__ unsigned long long ws4[4];
-    unsigned long long c = 0;
-    for (int k = threadIdx.x; k < K; k += 256) c += counts[k] == 0 ? 1ull : 0ull;
+    __shared__ unsigned ws16[16];
+    unsigned c = 0;
+    if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(counts) & 15u) == 0) {
+        const int4* c4 = reinterpret_cast<const int4*>(counts);
+#pragma unroll 4
+        for (int i = threadIdx.x; i < K / 4; i += 1024) {
+            const int4 v = c4[i];
+            c += (v.x == 0) + (v.y == 0) + (v.z == 0) + (v.w == 0);
+        }
+    } else {
+        for (int k = threadIdx.x; k < K; k += 1024) c += counts[k] == 0 ? 1u : 0u;
+    }
     for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-    if ((threadIdx.x & 63) == 0) ws4[threadIdx.x >> 6] = c;
+    if ((threadIdx.x & 63) == 0) ws16[threadIdx.x >> 6] = c;
     __syncthreads();
-    if (threadIdx.x == 0) *out = ws4[0] + ws4[1] + ws4[2] + ws4[3];
+    if (threadIdx.x == 0) {
+        unsigned long long t = 0;
+        for (int w = 0; w < 16; ++w) t += ws16[w];
+        *out = t;
+    }
 }
 
 // One Lloyd stage: T x (assign, objective, update), final assign, objective.
@@ -416,7 +430,7 @@ vq_status lloyd_stage(const float* X, const float* hcol, const float* rho, const
         VQ_TRY(update_with_J(X, hcol, rho, mask, M, N, d, idx, K, C, emp ? counts : nullptr, Jd + t, ws, ws_bytes,
                              st));
         if (emp) {
-            hipLaunchKernelGGL(k_count_empty, dim3(1), dim3(256), 0, st, counts, K, emp + t);
+            hipLaunchKernelGGL(k_count_empty, dim3(1), dim3(1024), 0, st, counts, K, emp + t);
             VQ_LAUNCHED("k_count_empty");
         }
     }
