@@ -691,6 +691,68 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(SLO
                           kt1, S_sc, shift_s, idx, dist, flag_count, flag_list);
 }
 
+// Codebooks of one chunk (K <= 256), per-slot tracking: the workgroup stages
+// the split codebook in LDS once and then takes groups of kSubPerBlock
+// consecutive sub-vectors in turn (grid-stride; wavefront w takes the
+// group's w-th 32), each searched as in k_assign_h16.  No barrier follows
+// the staging, so the waves of a workgroup drift apart freely and the
+// codebook crosses from L2 once per workgroup rather than once per group.
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_assign_h16_one(
+    const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
+    const uint8_t* __restrict__ mask, int64_t n_sub, int64_t nb, int d, const uint4* __restrict__ P,
+    const float* __restrict__ cmax, const float* __restrict__ C, int K, uint16_t* __restrict__ idx,
+    float* __restrict__ dist, int* __restrict__ flag_count, int* __restrict__ flag_list)
+{
+    constexpr int kChunkVec = kChunkTiles * 128;                 // uint4 per chunk
+    static_assert(kChunkVec == 2 * kWaves * 64, "two uint4 per thread per chunk");
+    __shared__ uint4 lds[kChunkVec];
+    lds[threadIdx.x] = P[threadIdx.x];
+    lds[threadIdx.x + kWaves * 64] = P[threadIdx.x + kWaves * 64];
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int half = lane >> 5;
+    const int a_off = half * 32 + (lane & 31);
+    const float cm = *cmax;
+    for (int64_t g = blockIdx.x; g * kSubPerBlock < n_sub; g += gridDim.x) {
+        const int64_t w0 = (g * kWaves + wave) * kSubPerWave;
+        if (w0 >= n_sub) break;                                  // wave-uniform; later groups start further on
+        const int64_t q = w0 + (lane & 31);
+        const bool valid = q < n_sub;
+        const int64_t s = valid ? q : 0;
+        h16x8 bh, bl;
+        float S_sc;
+        int shift_s;
+        general_operand(X, hcol, mask, s, nb, d, valid, half, cm, bh, bl, S_sc, shift_s);
+        float b1 = __builtin_inff(), b2 = __builtin_inff();
+        int kt1 = 0;
+        float pk[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) pk[j] = __builtin_inff();
+        f32x16 accA, accB;
+        for (int j = 0; j < 16; ++j) accB[j] = __builtin_inff();
+        int ktB = 0;
+        const uint4* L = lds + a_off;
+#pragma unroll 1
+        for (int tt = 0; tt < kChunkTiles; tt += 2) {
+            const uint4* A0 = L + tt * 128;
+            const uint4* A1 = A0 + 128;
+            const h16x8 ah0 = __builtin_bit_cast(h16x8, A0[0]);
+            const h16x8 al0 = __builtin_bit_cast(h16x8, A0[64]);
+            accA = tile_h16<true>(ah0, al0, bh, bl, accB, ktB, b1, b2, kt1, pk);
+            const h16x8 ah1 = __builtin_bit_cast(h16x8, A1[0]);
+            const h16x8 al1 = __builtin_bit_cast(h16x8, A1[64]);
+            accB = tile_h16<true>(ah1, al1, bh, bl, accA, tt, b1, b2, kt1, pk);
+            ktB = tt + 1;
+        }
+        track<true>(accB, ktB, b1, b2, kt1, pk);
+        park_resolve(pk, b1, b2, kt1);
+        search_epilogue<true>(X, hcol, rho, mask, nb, d, C, K, s, valid, valid, false, false, lane, half, b1, b2,
+                              kt1, S_sc, shift_s, idx, dist, flag_count, flag_list);
+    }
+}
+
 // Sub-vectors whose weights are one of a few per block: workgroup = column
 // block b x 256*NS consecutive rows (wavefront w: NS sets of 32 rows, set u
 // holding rows (rb*8 + w)*32*NS + u*32 + (l & 31)).  Every A operand read from
@@ -1228,6 +1290,8 @@ __global__ __launch_bounds__(256) void k_assign_exact(
 
 // Centroids per LDS chunk; the split codebook is padded to whole chunks.
 constexpr int kChunkK = kChunkTiles * kTile;
+// Workgroups of the one-chunk search (16 per CU on 256 CUs; 2048-8192 measured alike).
+constexpr unsigned kOneBlocks = 4096;
 // Row sets of 32 per wave in the shared-weight search, and rows per workgroup.
 constexpr int kSharedSets = 4;
 constexpr int kSharedRows = kSubPerBlock * kSharedSets;
@@ -1291,10 +1355,18 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
         } else if (slot) {
             // short codebooks: one pass of the general form (the block
             // classification would cost more than the shared form saves)
-            hipLaunchKernelGGL(k_assign_h16<true>, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st, X,
-                               hcol, rho, mask, n_sub, nb, d, P, cmax, C, K, nch, nullptr, nullptr, idx, dist,
-                               flag_count, flag_list);
-            VQ_LAUNCHED("k_assign_h16");
+            if (nch == 1) {
+                // one chunk: staged once per workgroup, groups taken in turn
+                const unsigned groups = grid_for(n_sub, kSubPerBlock);
+                hipLaunchKernelGGL(k_assign_h16_one, dim3(std::min(groups, kOneBlocks)), dim3(kWaves * 64), 0, st, X,
+                                   hcol, rho, mask, n_sub, nb, d, P, cmax, C, K, idx, dist, flag_count, flag_list);
+                VQ_LAUNCHED("k_assign_h16_one");
+            } else {
+                hipLaunchKernelGGL(k_assign_h16<true>, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st,
+                                   X, hcol, rho, mask, n_sub, nb, d, P, cmax, C, K, nch, nullptr, nullptr, idx, dist,
+                                   flag_count, flag_list);
+                VQ_LAUNCHED("k_assign_h16");
+            }
         } else {
         if (mask) {
             hipLaunchKernelGGL(k_block_pattern, dim3((unsigned)nb), dim3(256), 0, st, mask, M, nb, pattern);

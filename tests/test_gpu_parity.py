@@ -61,6 +61,7 @@ ASSIGN_CASES = [
     (11, 256, 512, 8, 3000, True, True),   # long codebook: per-tile tracking, last tile re-formed
     (12, 300, 96, 3, 2500, True, False),   # long codebook, d = 3, ragged last chunk
     (13, 3, 6400, 8, 2200, True, True),    # long codebook, masked, fewer than 4 rows (no block classes)
+    (14, 1040, 8096, 8, 3, True, True),    # one-chunk search: > 4096 groups of 256, workgroups take two
 ]
 
 
