@@ -2,7 +2,7 @@
 //
 // Method: HAS-VQ abstract ("Hessian-Masked Decoupling" isolates the weights
 // with the largest second-order sensitivity; they are held exactly) and the
-// SCVQ summary (one sparse correction matrix).  Score of element (i,j):
+// SCVQ summary (every exactly held weight lives in one CSR).  Score of element (i,j):
 // s_ij = h_j * (w_ij * w_ij) in float32 (two roundings, no fused
 // multiply-add).  The nnz largest scores are selected, ties broken by the
 // smaller linear index i*N + j.

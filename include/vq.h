@@ -13,7 +13,7 @@
  *   - VPTQ page, "Residual Vector Quantization": a second codebook quantizes
  *     the first stage's error; decode adds the two centroids.
  *   - SCVQ summary: weights bi-normalized across rows and columns, salience-
- *     weighted K-means, one sparse correction matrix.
+ *     weighted K-means, every exactly held weight in one CSR.
  *
  * Conventions (all entry points):
  *   - W is [M x N] row-major float32, M outputs by N inputs.  h (the diagonal
@@ -81,7 +81,7 @@ size_t vq_workspace_bytes(int64_t M, int64_t N, int d, int K1, int K2, int64_t n
 
 /* Salience selection into the exact sparse correction.
  * HAS-VQ abstract (Hessian-Masked Decoupling; exact reconstruction of the
- * salient weights); SCVQ summary (one sparse correction matrix).
+ * salient weights); SCVQ summary (every exactly held weight in one CSR).
  * Score s_ij = h_j * (w_ij * w_ij) in float32 (no fused multiply-add).  The
  * nnz largest scores are selected, ties broken by the smaller linear index
  * i*N+j.  Outputs: row_ptr int32[M+1], col int32[nnz] (ascending within each

@@ -45,8 +45,8 @@ long long orc_nnz(long long M, long long N, double p)
 
 /* ------------------------------------------------------------------ */
 /* Salience selection (HAS-VQ abstract: Hessian-Masked Decoupling isolates the
- * second-order-sensitive weights and holds them exactly; SCVQ summary: one
- * sparse correction matrix).  Score of element (i,j): s = h_j * (w_ij * w_ij)
+ * second-order-sensitive weights and holds them exactly; SCVQ summary: every
+ * exactly held weight in one CSR).  Score of element (i,j): s = h_j * (w_ij * w_ij)
  * in fp32, taken on the original W and h.  The nnz largest scores are selected,
  * ties broken by the smaller linear index i*N+j.  Output: CSR (row_ptr[M+1],
  * col[nnz] ascending within a row, val[nnz] = the exact W value) and keep[M*N]
