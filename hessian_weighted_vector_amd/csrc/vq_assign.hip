@@ -753,6 +753,89 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
     }
 }
 
+// ---- coarse pass of the two-pass search (long codebooks, shared weights) ----
+// The coarse score is the shared form's second MFMA alone: hi*hi of the
+// cross terms plus the class bias.  With x_t = alpha omega_t x_t and
+// c_t = -2 beta c_t (scaled), each fp16 part is within 2^-11 of its value in
+// the normal range, so the dropped products (those with a lo part) miss at
+// most 2^-10 (1 + 2^-10) sum_t |x_t| |c_t|.  Cauchy-Schwarz in the
+// omega-weighted inner product gives sum_t |x_t| |c_t| <= 2 sqrt(S B_k), with
+// S = sum_t omega_t x_t^2 and B_k = sum_t omega_t c_kt^2 (the bias), and
+// sqrt(B_k) <= sqrt(S) + sqrt(D_k) where D_k = e_k + S is the weighted
+// distance itself.  So |e~_k - e_k| <= a (sqrt(S) + sqrt(D_k)) + E0 with
+// a = 2^-9 (1 + 2^-10) sqrt(S) and E0 = 48u (9 S + 4 |e~|) + 2 (the fp32
+// accumulation, the bias split and fp16's subnormal range, all in scaled
+// units).  Solving for sqrt(D_k) with the coarse value D~ = e~ + S gives
+// sqrt(D_k) <= (a + sqrt(a^2 + 4 (D~ + a sqrt(S) + E0))) / 2, hence a bound
+// Ehat(e~) on |e~ - e| from the coarse value alone.  Its slope is below
+// 2^-5, so L(v) = v - Ehat(v) grows with v.
+constexpr int kGroupChunks = 2;           // chunks per candidate group of the two-pass search
+constexpr int kMaxGroups = 128;           // groups of a 65536-centroid codebook
+constexpr int kBucketItems = 4;           // sub-vectors per thread of the candidate bucketing
+constexpr int kRefineBlocks = 2048;       // workgroups of the candidate search (grid-stride)
+
+__device__ __forceinline__ float coarse_err(float v, float S, float sqS, float a)
+{
+    const float u = 5.9604644775390625e-8f;   // 2^-24
+    const float E0 = 48.f * u * (9.f * S + 4.f * fabsf(v)) + 2.f;
+    const float Dt = fmaxf(v + S, 0.f);
+    const float y = 0.5f * (a + sqrtf(a * a + 4.f * (Dt + a * sqS + E0)));
+    return 1.001f * (a * (sqS + y) + E0);     // margin for this evaluation's roundings
+}
+
+// Running minimum of a tile's 16 values (eight three-way minima).
+__device__ __forceinline__ float fold16(const f32x16& a, float m)
+{
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) m = fminf(fminf(m, a[j]), a[j + 1]);
+    return m;
+}
+
+// One coarse tile: the hi*hi-plus-bias MFMA, with the previous tile folded
+// into the running group minimum between issue and use.
+__device__ __forceinline__ f32x16 tile1_h16(const h16x8 a1, const h16x8 b1v, const f32x16& prev, float& gm)
+{
+    f32x16 acc = {};
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1v, acc, 0, 0, 0);
+    gm = fold16(prev, gm);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // eight VALU
+    return acc;
+}
+
+// Closes group g of one lane pair: the two halves' minima are merged and
+// inserted into the three smallest group minima (t1 <= t2 <= t3, groups g1..g3;
+// the earlier group first among equal minima) and the fourth smallest t4.
+__device__ __forceinline__ void close_group(float& gm, int g, float& t1, float& t2, float& t3, float& t4, int& g1,
+                                            int& g2, int& g3)
+{
+    const float m = fminf(gm, __shfl_xor(gm, 32));
+    const bool l1 = m < t1, l2 = m < t2, l3 = m < t3;
+    g3 = l2 ? g2 : (l3 ? g : g3);
+    g2 = l1 ? g1 : (l2 ? g : g2);
+    g1 = l1 ? g : g1;
+    t4 = __builtin_amdgcn_fmed3f(t3, m, t4);
+    t3 = __builtin_amdgcn_fmed3f(t2, m, t3);
+    t2 = __builtin_amdgcn_fmed3f(t1, m, t2);
+    t1 = fminf(t1, m);
+    gm = __builtin_inff();
+}
+
+// Appends the lanes with take set to a list (one atomic per wavefront; the
+// order of the list affects no result).  Every lane of the wavefront calls it.
+__device__ __forceinline__ void list_append(bool take, int lane, int64_t s, int* __restrict__ count,
+                                            int* __restrict__ list)
+{
+    const unsigned long long ball = __ballot(take);
+    if (ball) {
+        int base = 0;
+        const int leader = __ffsll((long long)ball) - 1;
+        if (lane == leader) base = atomicAdd(count, __popcll(ball));
+        base = __shfl(base, leader);
+        if (take) list[base + __popcll(ball & ((1ull << lane) - 1ull))] = (int)s;
+    }
+}
+
 // Sub-vectors whose weights are one of a few per block: workgroup = column
 // block b x 256*NS consecutive rows (wavefront w: NS sets of 32 rows, set u
 // holding rows (rb*8 + w)*32*NS + u*32 + (l & 31)).  Every A operand read from
@@ -777,12 +860,26 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
 // exact zeros) to a small accumulator.  Lanes whose mask byte is none of the
 // block's patterns are computed (with pattern 0) but not written: they are in
 // the list of the general kernel.
-template <bool SLOT, int NS>
+//
+// COARSE: the coarse pass of the two-pass search.  One MFMA per tile (the
+// second above); per lane the running minimum of the current group of
+// kGroupChunks chunks, and at each group's end the lane pair's minimum goes
+// into the three smallest group minima with their groups and the fourth
+// smallest value.  Group g is a candidate when L(m_g) <= U = m_1 + Ehat(m_1)
+// (coarse_err); since L grows with m, the candidates are the groups of the
+// smallest minima.  Per owned sub-vector: cand[s] = n | g1 << 8 | g2 << 16 |
+// g3 << 24 with n the number of candidates (1..3); a sub-vector with a fourth
+// candidate goes to the dirty list (the general form over the whole codebook),
+// one with all weights zero takes index 0, one whose gamma underflows goes to
+// the exact re-search; these and every sub-vector the kernel does not own get
+// cand[s] = 0.
+template <bool SLOT, int NS, bool COARSE>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS == 1 ? 4 : (NS == 2 ? 3 : 2), 8))) void k_assign_h16s(
     const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
     const uint8_t* __restrict__ mask, const uint32_t* __restrict__ pattern, int64_t M, int64_t nb, int d,
     const uint4* __restrict__ P, const float* __restrict__ cmax, const float* __restrict__ C, int K, int nchunks,
-    uint16_t* __restrict__ idx, float* __restrict__ dist, int* __restrict__ flag_count, int* __restrict__ flag_list)
+    uint16_t* __restrict__ idx, float* __restrict__ dist, int* __restrict__ flag_count, int* __restrict__ flag_list,
+    int* __restrict__ dirty_count, int* __restrict__ dirty_list, uint32_t* __restrict__ cand)
 {
     static_assert(kBlockPatterns * 2 == 8, "the four bias pairs fill k-slots 8-15");
     constexpr int kRowVec = kChunkTiles * 96;    // uint4 per chunk: rows (lo, hi, bias) of 32 per tile
@@ -953,6 +1050,109 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
         }
     };
 
+    uint4 pre = load_cross(0);
+    float4 r0, r1;
+    load_row(0, r0, r1);
+    store_chunk(0, 0, pre, r0, r1);
+    __syncthreads();
+    const int a_off = half * 32 + (lane & 31);
+
+    if constexpr (COARSE) {
+        float gmn[NS], t1[NS], t2[NS], t3[NS], t4[NS];
+        int g1[NS], g2[NS], g3[NS];
+        f32x16 cA[NS], cB[NS];
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            gmn[u] = t1[u] = t2[u] = t3[u] = t4[u] = __builtin_inff();
+            g1[u] = g2[u] = g3[u] = 0;
+            for (int j = 0; j < 16; ++j) cB[u][j] = __builtin_inff();
+        }
+        for (int c = 0; c < nchunks; ++c) {
+            if (c + 1 < nchunks) {
+                pre = load_cross(c + 1);
+                load_row(c + 1, r0, r1);
+            }
+            if (active) {
+                const uint4* L = lds[c & 1] + a_off;
+#pragma unroll 1
+                for (int tt = 0; tt < kChunkTiles; tt += 2) {
+                    const h16x8 q0 = __builtin_bit_cast(h16x8, L[tt * 96 + 32]);
+#pragma unroll
+                    for (int u = 0; u < NS; ++u) cA[u] = tile1_h16(q0, bB[u], cB[u], gmn[u]);
+                    // the pending tile just folded was the last of the previous group
+                    if (tt == 0 && c > 0 && c % kGroupChunks == 0) {
+#pragma unroll
+                        for (int u = 0; u < NS; ++u)
+                            close_group(gmn[u], c / kGroupChunks - 1, t1[u], t2[u], t3[u], t4[u], g1[u], g2[u], g3[u]);
+                    }
+                    const h16x8 q1 = __builtin_bit_cast(h16x8, L[(tt + 1) * 96 + 32]);
+#pragma unroll
+                    for (int u = 0; u < NS; ++u) cB[u] = tile1_h16(q1, bB[u], cA[u], gmn[u]);
+                }
+            }
+            if (c + 1 < nchunks) store_chunk((c + 1) & 1, c + 1, pre, r0, r1);
+            __syncthreads();
+        }
+        if (!active) return;
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            gmn[u] = fold16(cB[u], gmn[u]);
+            close_group(gmn[u], (nchunks - 1) / kGroupChunks, t1[u], t2[u], t3[u], t4[u], g1[u], g2[u], g3[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            int r = lane & 31;
+            asm volatile("" : "+v"(r));
+            int64_t s;
+            bool valid, owner, bad;
+            float S_sc;
+            int shift_s, q;
+            unsigned mq;
+            h16x8 ua, ub;
+            row_of(u, r, s, valid, owner, q, mq);
+            prep(s, valid, q, mq, ua, ub, S_sc, shift_s, bad);
+            bool allz = true;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) allz = allz && (((mq >> t) & 1u) || hb[t] == 0.f);
+            const bool writer = half == 0 && valid;
+            bool to_exact = false, to_dirty = false;
+            uint32_t cw = 0;
+            if (writer && owner) {
+                if (allz) {
+                    // every weighted distance is exactly 0: the lowest index
+                    idx[s] = 0;
+                    if (dist) {
+                        double omd[8];
+                        float xs[8];
+                        exact_weights(hcol, rho, mask, s, nb, d, omd);
+                        for (int t = 0; t < d; ++t) xs[t] = X[s * d + t];
+                        dist[s] = (float)exact_dist(omd, xs, C, d);
+                    }
+                } else if (bad) {
+                    to_exact = true;
+                } else {
+                    const float sqS = sqrtf(S_sc);
+                    const float a = 0x1.004p-9f * sqS;                   // 2^-9 (1 + 2^-10) sqrt(S)
+                    const float U = t1[u] + coarse_err(t1[u], S_sc, sqS, a);
+                    auto low = [&](float m) {
+                        const float mm = fminf(m, 1.0e30f);              // unfilled slots stay far above U
+                        return mm - coarse_err(mm, S_sc, sqS, a);
+                    };
+                    if (low(t4[u]) <= U) {
+                        to_dirty = true;
+                    } else {
+                        const uint32_t n = 1u + (low(t2[u]) <= U ? 1u : 0u) + (low(t3[u]) <= U ? 1u : 0u);
+                        cw = n | ((uint32_t)g1[u] << 8) | ((uint32_t)g2[u] << 16) | ((uint32_t)g3[u] << 24);
+                    }
+                }
+            }
+            if (writer) cand[s] = cw;
+            list_append(to_exact, lane, s, flag_count, flag_list);
+            list_append(to_dirty, lane, s, dirty_count, dirty_list);
+        }
+        return;
+    }
+
     float b1[NS], b2[NS];
     int kt1[NS];
 #pragma unroll
@@ -961,11 +1161,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
         b2[u] = __builtin_inff();
         kt1[u] = 0;
     }
-    uint4 pre = load_cross(0);
-    float4 r0, r1;
-    load_row(0, r0, r1);
-    store_chunk(0, 0, pre, r0, r1);
-    __syncthreads();
 
     // each set's A operands are read from LDS once per tile and used by the
     // MFMAs of every set
@@ -974,7 +1169,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
     for (int u = 0; u < NS; ++u)
         for (int j = 0; j < 16; ++j) accB[u][j] = __builtin_inff();
     int ktB = 0;
-    const int a_off = half * 32 + (lane & 31);
     for (int c = 0; c < nchunks; ++c) {
         if (c + 1 < nchunks) {
             pre = load_cross(c + 1);
@@ -1023,6 +1217,227 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
     }
 }
 
+
+// ---- candidate groups of the two-pass search ----------------------------
+// Entry s * 4 + j of group g's list names candidate j of sub-vector s.
+
+// Fills n ints with v.
+__global__ void k_fill_int(int* __restrict__ p, int n, int v)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// Candidates per group: a histogram per workgroup in LDS, then one atomic per
+// (workgroup, group).
+__global__ __launch_bounds__(1024) void k_cand_count(const uint32_t* __restrict__ cand, int64_t n_sub, int ng,
+                                                     int* __restrict__ gcount)
+{
+    __shared__ int h[kMaxGroups];
+    if (threadIdx.x < kMaxGroups) h[threadIdx.x] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kBucketItems; ++r) {
+        const int64_t s = ((int64_t)blockIdx.x * kBucketItems + r) * 1024 + threadIdx.x;
+        if (s < n_sub) {
+            const uint32_t w = cand[s];
+            const int n = (int)(w & 3u);
+            for (int j = 0; j < n; ++j) atomicAdd(&h[(w >> (8 * (j + 1))) & 0xFFu], 1);
+        }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < ng && h[threadIdx.x]) atomicAdd(&gcount[threadIdx.x], h[threadIdx.x]);
+}
+
+// One thread: goff[g] = first list slot of group g, cursor[g] = goff[g],
+// gblk[g] = first work item of group g (kSubPerBlock entries per item),
+// gblk[ng] = the number of work items.
+__global__ void k_cand_scan(const int* __restrict__ gcount, int ng, int* __restrict__ goff, int* __restrict__ cursor,
+                            int* __restrict__ gblk)
+{
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    int off = 0, blk = 0;
+    for (int g = 0; g < ng; ++g) {
+        goff[g] = off;
+        cursor[g] = off;
+        gblk[g] = blk;
+        off += gcount[g];
+        blk += (gcount[g] + kSubPerBlock - 1) / kSubPerBlock;
+    }
+    gblk[ng] = blk;
+}
+
+// Scatter into the group lists: ranks within the workgroup from LDS atomics,
+// one global atomic per (workgroup, group) for the base.
+__global__ __launch_bounds__(1024) void k_cand_scatter(const uint32_t* __restrict__ cand, int64_t n_sub, int ng,
+                                                       int* __restrict__ cursor, int* __restrict__ pairs)
+{
+    __shared__ int h[kMaxGroups];
+    __shared__ int base[kMaxGroups];
+    if (threadIdx.x < kMaxGroups) h[threadIdx.x] = 0;
+    __syncthreads();
+    uint32_t w[kBucketItems];
+    int rk[kBucketItems][3];
+#pragma unroll
+    for (int r = 0; r < kBucketItems; ++r) {
+        const int64_t s = ((int64_t)blockIdx.x * kBucketItems + r) * 1024 + threadIdx.x;
+        w[r] = s < n_sub ? cand[s] : 0u;
+        const int n = (int)(w[r] & 3u);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) rk[r][j] = j < n ? atomicAdd(&h[(w[r] >> (8 * (j + 1))) & 0xFFu], 1) : 0;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < ng) base[threadIdx.x] = h[threadIdx.x] ? atomicAdd(&cursor[threadIdx.x], h[threadIdx.x]) : 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kBucketItems; ++r) {
+        const int64_t s = ((int64_t)blockIdx.x * kBucketItems + r) * 1024 + threadIdx.x;
+        const int n = (int)(w[r] & 3u);
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (j < n) pairs[base[(w[r] >> (8 * (j + 1))) & 0xFFu] + rk[r][j]] = (int)(s * 4 + j);
+    }
+}
+
+// Search of the candidate groups in the general three-MFMA form: work item w
+// (grid-stride over workgroups) is up to kSubPerBlock consecutive entries of
+// one group's list; the workgroup stages the group's chunks of the split
+// codebook in LDS and each wavefront searches 32 entries with per-slot
+// tracking, as the short-codebook search does.  Per entry (s, j): the lane
+// pair's best score, second best, best index and S_sc go to
+// part[j * n_sub + s].
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_refine_h16(
+    const float* __restrict__ X, const float* __restrict__ hcol, const uint8_t* __restrict__ mask, int64_t n_sub,
+    int64_t nb, int d, const uint4* __restrict__ P, const float* __restrict__ cmax, int nchunks, int ng,
+    const int* __restrict__ gcount, const int* __restrict__ goff, const int* __restrict__ gblk,
+    const int* __restrict__ pairs, float4* __restrict__ part)
+{
+    constexpr int kChunkVec = kChunkTiles * 128;                 // uint4 per chunk
+    __shared__ uint4 lds[kGroupChunks * kChunkVec];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int half = lane >> 5;
+    const int a_off = half * 32 + (lane & 31);
+    const float cm = *cmax;
+    const int T = gblk[ng];
+    for (int w = blockIdx.x; w < T; w += gridDim.x) {
+        int lo = 0, hi = ng;                                      // gblk[lo] <= w < gblk[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (gblk[mid] <= w) lo = mid; else hi = mid;
+        }
+        const int g = lo;
+        const int first = (w - gblk[g]) * kSubPerBlock;
+        const int cnt = min(kSubPerBlock, gcount[g] - first);
+        const int c0 = g * kGroupChunks;
+        const int ncg = min(kGroupChunks, nchunks - c0);
+        __syncthreads();                                          // the previous item's tiles are read
+        for (int i = threadIdx.x; i < ncg * kChunkVec; i += kWaves * 64) lds[i] = P[(size_t)c0 * kChunkVec + i];
+        __syncthreads();
+        if (wave * kSubPerWave >= cnt) continue;                  // wave-uniform
+        const int qi = wave * kSubPerWave + (lane & 31);
+        const bool valid = qi < cnt;
+        const int e = valid ? pairs[goff[g] + first + qi] : 0;
+        const int64_t s = e >> 2;
+        const int j = e & 3;
+        h16x8 bh, bl;
+        float S_sc;
+        int shift_s;
+        general_operand(X, hcol, mask, s, nb, d, valid, half, cm, bh, bl, S_sc, shift_s);
+        float b1 = __builtin_inff(), b2 = __builtin_inff();
+        int kt1 = 0;
+        float pk[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) pk[t] = __builtin_inff();
+        f32x16 accA, accB;
+        for (int t = 0; t < 16; ++t) accB[t] = __builtin_inff();
+        const int kt0 = c0 * kChunkTiles;
+        int ktB = kt0;
+        const uint4* L = lds + a_off;
+#pragma unroll 1
+        for (int tt = 0; tt < ncg * kChunkTiles; tt += 2) {
+            const uint4* A0 = L + tt * 128;
+            const uint4* A1 = A0 + 128;
+            const h16x8 ah0 = __builtin_bit_cast(h16x8, A0[0]);
+            const h16x8 al0 = __builtin_bit_cast(h16x8, A0[64]);
+            accA = tile_h16<true>(ah0, al0, bh, bl, accB, ktB, b1, b2, kt1, pk);
+            const h16x8 ah1 = __builtin_bit_cast(h16x8, A1[0]);
+            const h16x8 al1 = __builtin_bit_cast(h16x8, A1[64]);
+            accB = tile_h16<true>(ah1, al1, bh, bl, accA, kt0 + tt, b1, b2, kt1, pk);
+            ktB = kt0 + tt + 1;
+        }
+        track<true>(accB, ktB, b1, b2, kt1, pk);
+        park_resolve(pk, b1, b2, kt1);
+        // merge of the lane pair (the two halves hold the tile's two row sets)
+        const int jb = kt1 & 15;
+        const int kb = (kt1 >> 4) * kTile + (jb >> 2) * 8 + half * 4 + (jb & 3);
+        const float ob1 = __shfl_xor(b1, 32);
+        const float ob2 = __shfl_xor(b2, 32);
+        const int okb = __shfl_xor(kb, 32);
+        float gb, gs;
+        int gk;
+        if (b1 < ob1 || (b1 == ob1 && kb < okb)) {
+            gb = b1; gk = kb; gs = fminf(b2, ob1);
+        } else {
+            gb = ob1; gk = okb; gs = fminf(ob2, b1);
+        }
+        if (half == 0 && valid) part[(size_t)j * n_sub + s] = make_float4(gb, gs, __int_as_float(gk), S_sc);
+    }
+}
+
+// Per sub-vector with candidates: the lexicographic (score, index) minimum
+// over its candidates' results and the second best over the rest, certified
+// with the search's bound; certified winners are written, the rest go to the
+// exact re-search.  Outside the candidate groups every exact score lies
+// above the exact minimum, so a winner certified among the candidates is the
+// exact argmin over the whole codebook.
+__global__ __launch_bounds__(256) void k_cand_merge(
+    const float* __restrict__ X, const float* __restrict__ hcol, const float* __restrict__ rho,
+    const uint8_t* __restrict__ mask, int64_t nb, int d, const float* __restrict__ C, int K, int64_t n_sub,
+    const uint32_t* __restrict__ cand, const float4* __restrict__ part, uint16_t* __restrict__ idx,
+    float* __restrict__ dist, int* __restrict__ flag_count, int* __restrict__ flag_list)
+{
+    const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    bool flag = false;
+    if (s < n_sub) {
+        const uint32_t w = cand[s];
+        const int n = (int)(w & 3u);
+        if (n) {
+            const float4 p0 = part[s];
+            float gb = p0.x, gs = p0.y;
+            int gk = __float_as_int(p0.z);
+            const float S_sc = p0.w;
+            for (int j = 1; j < n; ++j) {
+                const float4 q = part[(size_t)j * n_sub + s];
+                const int qk = __float_as_int(q.z);
+                if (q.x < gb || (q.x == gb && qk < gk)) {
+                    gs = fminf(q.y, gb);
+                    gb = q.x;
+                    gk = qk;
+                } else {
+                    gs = fminf(gs, q.x);
+                }
+            }
+            const float u = 5.9604644775390625e-8f;   // 2^-24
+            const float eb = 48.f * u * (9.f * S_sc + 4.f * fmaxf(gb, -S_sc)) + 1.f;
+            const float es = 48.f * u * (9.f * S_sc + 4.f * fmaxf(gs, -S_sc)) + 1.f;
+            if ((gs - gb) > (eb + es) && gk < K) {
+                idx[s] = (uint16_t)gk;
+                if (dist) {
+                    double omd[8];
+                    float xs[8];
+                    exact_weights(hcol, rho, mask, s, nb, d, omd);
+                    for (int t = 0; t < d; ++t) xs[t] = X[s * d + t];
+                    dist[s] = (float)exact_dist(omd, xs, C + (size_t)gk * d, d);
+                }
+            } else {
+                flag = true;
+            }
+        }
+    }
+    list_append(flag, lane, s, flag_count, flag_list);
+}
 
 // Chunk minima of the flagged sub-vectors (long codebooks).  The general
 // three-MFMA form of the search over the flag list, entries [0, min(count,
@@ -1298,6 +1713,25 @@ constexpr int kSharedRows = kSubPerBlock * kSharedSets;
 
 inline int padded_K(int K) { return (K + kChunkK - 1) / kChunkK * kChunkK; }
 
+// Arrays of the two-pass search, taken from the workspace beyond
+// ws_assign's size when there is room: cand (4 bytes per sub-vector), the
+// group lists (up to three entries per sub-vector), the candidates' results
+// (three float4 per sub-vector) and the per-group counters.
+size_t ws_coarse(int64_t n_sub)
+{
+    return align_up((size_t)n_sub * 4) + align_up((size_t)n_sub * 3 * 4) + align_up((size_t)n_sub * 3 * 16) +
+           4 * align_up(sizeof(int) * (kMaxGroups + 1));
+}
+
+// Workspace an assignment uses at most: ws_assign plus the two-pass search's
+// arrays and the chunk path's room for flagged sub-vectors.
+size_t ws_assign_full(int64_t n_sub, int K)
+{
+    const int nch = padded_K(K) / kChunkK;
+    return ws_assign(n_sub, K) + ws_coarse(n_sub) +
+           align_up((size_t)kCminCap * ((size_t)nch + 1) * sizeof(float)) + 4 * kAlign;
+}
+
 size_t ws_assign(int64_t n_sub, int K)
 {
     // split codebook (64 bytes per centroid), flag counter, flag list, max |c|,
@@ -1375,13 +1809,51 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
                                (uint32_t)nb, dirty_count, dirty_list);
             VQ_LAUNCHED("k_dirty");
         }
-        // sub-vectors with their block's weights: two MFMAs per tile
-        hipLaunchKernelGGL((k_assign_h16s<false, kSharedSets>), dim3((unsigned)shared_groups), dim3(kWaves * 64), 0, st, X, hcol,
-                           rho, mask, mask ? pattern : nullptr, M, nb, d, P, cmax, C, K, nch, idx, dist, flag_count,
-                           flag_list);
-        VQ_LAUNCHED("k_assign_h16s");
-        // the rest, each with its own weights: three MFMAs per tile
-        if (mask) {
+        // Two passes when the workspace has room for them: the coarse pass
+        // (one MFMA per tile) names each sub-vector's candidate groups, the
+        // groups are searched in the general form over their lists only,
+        // and the merge certifies the winners.
+        const int ng = (nch + kGroupChunks - 1) / kGroupChunks;
+        const size_t room = cv.cap > cv.used + 8 * kAlign ? cv.cap - cv.used - 8 * kAlign : 0;
+        const bool two_pass = ng <= kMaxGroups && n_sub < ((int64_t)1 << 29) && room >= ws_coarse(n_sub);
+        if (two_pass) {
+            uint32_t* cand = cv.take<uint32_t>((size_t)n_sub);
+            int* pairs = cv.take<int>((size_t)n_sub * 3);
+            float4* partv = cv.take<float4>((size_t)n_sub * 3);
+            int* gcount = cv.take<int>(kMaxGroups + 1);
+            int* goff = cv.take<int>(kMaxGroups + 1);
+            int* cursor = cv.take<int>(kMaxGroups + 1);
+            int* gblk = cv.take<int>(kMaxGroups + 1);
+            if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_assign: workspace too small");
+            hipLaunchKernelGGL(k_fill_int, dim3(1), dim3(kMaxGroups + 1), 0, st, gcount, kMaxGroups + 1, 0);
+            VQ_LAUNCHED("k_fill_int");
+            hipLaunchKernelGGL((k_assign_h16s<false, kSharedSets, true>), dim3((unsigned)shared_groups),
+                               dim3(kWaves * 64), 0, st, X, hcol, rho, mask, mask ? pattern : nullptr, M, nb, d, P,
+                               cmax, C, K, nch, idx, dist, flag_count, flag_list, dirty_count, dirty_list, cand);
+            VQ_LAUNCHED("k_assign_h16s");
+            const unsigned gb = grid_for(n_sub, 1024 * kBucketItems);
+            hipLaunchKernelGGL(k_cand_count, dim3(gb), dim3(1024), 0, st, cand, n_sub, ng, gcount);
+            VQ_LAUNCHED("k_cand_count");
+            hipLaunchKernelGGL(k_cand_scan, dim3(1), dim3(64), 0, st, gcount, ng, goff, cursor, gblk);
+            VQ_LAUNCHED("k_cand_scan");
+            hipLaunchKernelGGL(k_cand_scatter, dim3(gb), dim3(1024), 0, st, cand, n_sub, ng, cursor, pairs);
+            VQ_LAUNCHED("k_cand_scatter");
+            hipLaunchKernelGGL(k_refine_h16, dim3(kRefineBlocks), dim3(kWaves * 64), 0, st, X, hcol, mask, n_sub, nb,
+                               d, P, cmax, nch, ng, gcount, goff, gblk, pairs, partv);
+            VQ_LAUNCHED("k_refine_h16");
+            hipLaunchKernelGGL(k_cand_merge, dim3(grid_for(n_sub, 256)), dim3(256), 0, st, X, hcol, rho, mask, nb, d,
+                               C, K, n_sub, cand, partv, idx, dist, flag_count, flag_list);
+            VQ_LAUNCHED("k_cand_merge");
+        } else {
+            // sub-vectors with their block's weights: two MFMAs per tile
+            hipLaunchKernelGGL((k_assign_h16s<false, kSharedSets, false>), dim3((unsigned)shared_groups),
+                               dim3(kWaves * 64), 0, st, X, hcol, rho, mask, mask ? pattern : nullptr, M, nb, d, P,
+                               cmax, C, K, nch, idx, dist, flag_count, flag_list, nullptr, nullptr, nullptr);
+            VQ_LAUNCHED("k_assign_h16s");
+        }
+        // the rest, each with its own weights (and, after the coarse pass, the
+        // sub-vectors with more than three candidate groups): three MFMAs per tile
+        if (mask || two_pass) {
             hipLaunchKernelGGL(k_assign_h16<false>, dim3(grid_for(n_sub, kSubPerBlock)), dim3(kWaves * 64), 0, st, X,
                                hcol, rho, mask, n_sub, nb, d, P, cmax, C, K, nch, dirty_list, dirty_count, idx, dist,
                                flag_count, flag_list);

@@ -442,7 +442,8 @@ size_t ws_steps(int64_t M, int64_t N, int d, int K1, int K2)
 {
     const int64_t n_sub = M * N / d;
     const int Kmax = std::max(K1, K2);
-    size_t w = ws_assign(n_sub, Kmax);
+    // the assignment with its optional arrays (two-pass search, chunk path)
+    size_t w = ws_assign_full(n_sub, Kmax);
     // the update's needs are not monotone in K (a short codebook takes more
     // pieces, a long one the bucket arrays): both stages' sizes
     w = std::max(w, ws_update_total(n_sub, K1));

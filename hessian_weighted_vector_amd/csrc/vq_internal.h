@@ -57,6 +57,7 @@ struct Carver {
 
 // Workspace needs of each step (bytes); must match the carving in each file.
 size_t ws_assign(int64_t n_sub, int K);
+size_t ws_assign_full(int64_t n_sub, int K);
 size_t ws_update(int64_t n_sub, int K);
 size_t ws_objective(int64_t n_sub);
 size_t ws_select(int64_t M, int64_t N);
