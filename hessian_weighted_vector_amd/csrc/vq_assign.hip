@@ -769,8 +769,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
 // sqrt(D_k) <= (a + sqrt(a^2 + 4 (D~ + a sqrt(S) + E0))) / 2, hence a bound
 // Ehat(e~) on |e~ - e| from the coarse value alone.  Its slope is below
 // 2^-5, so L(v) = v - Ehat(v) grows with v.
-constexpr int kGroupChunks = 2;           // chunks per candidate group of the two-pass search
-constexpr int kMaxGroups = 128;           // groups of a 65536-centroid codebook
+constexpr int kGroupChunks = 4;           // chunks per candidate group of the two-pass search
+constexpr int kMaxGroups = 64;            // groups of a 65536-centroid codebook
 constexpr int kBucketItems = 4;           // sub-vectors per thread of the candidate bucketing
 constexpr int kRefineBlocks = 2048;       // workgroups of the candidate search (grid-stride)
 
@@ -1065,7 +1065,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
         for (int u = 0; u < NS; ++u) {
             gmn[u] = t1[u] = t2[u] = t3[u] = t4[u] = __builtin_inff();
             g1[u] = g2[u] = g3[u] = 0;
-            for (int j = 0; j < 16; ++j) cB[u][j] = __builtin_inff();
         }
         for (int c = 0; c < nchunks; ++c) {
             if (c + 1 < nchunks) {
@@ -1073,32 +1072,40 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
                 load_row(c + 1, r0, r1);
             }
             if (active) {
+                // the chunk's tiles, software pipelined within the chunk: tile
+                // t's MFMAs are issued before tile t-1 is folded (two
+                // accumulator sets alternate) and the last tile is folded
+                // after the loop, so a group ends with its last chunk
                 const uint4* L = lds[c & 1] + a_off;
+                static_assert(kChunkTiles % 2 == 0, "tiles 1..kChunkTiles-2 go in pairs");
+                const h16x8 qf = __builtin_bit_cast(h16x8, L[32]);
+#pragma unroll
+                for (int u = 0; u < NS; ++u)
+                    cA[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf, bB[u], f32x16{}, 0, 0, 0);
 #pragma unroll 1
-                for (int tt = 0; tt < kChunkTiles; tt += 2) {
+                for (int tt = 1; tt < kChunkTiles - 1; tt += 2) {
                     const h16x8 q0 = __builtin_bit_cast(h16x8, L[tt * 96 + 32]);
-#pragma unroll
-                    for (int u = 0; u < NS; ++u) cA[u] = tile1_h16(q0, bB[u], cB[u], gmn[u]);
-                    // the pending tile just folded was the last of the previous group
-                    if (tt == 0 && c > 0 && c % kGroupChunks == 0) {
-#pragma unroll
-                        for (int u = 0; u < NS; ++u)
-                            close_group(gmn[u], c / kGroupChunks - 1, t1[u], t2[u], t3[u], t4[u], g1[u], g2[u], g3[u]);
-                    }
                     const h16x8 q1 = __builtin_bit_cast(h16x8, L[(tt + 1) * 96 + 32]);
 #pragma unroll
-                    for (int u = 0; u < NS; ++u) cB[u] = tile1_h16(q1, bB[u], cA[u], gmn[u]);
+                    for (int u = 0; u < NS; ++u) cB[u] = tile1_h16(q0, bB[u], cA[u], gmn[u]);
+#pragma unroll
+                    for (int u = 0; u < NS; ++u) cA[u] = tile1_h16(q1, bB[u], cB[u], gmn[u]);
+                }
+                const h16x8 ql = __builtin_bit_cast(h16x8, L[(kChunkTiles - 1) * 96 + 32]);
+#pragma unroll
+                for (int u = 0; u < NS; ++u) cB[u] = tile1_h16(ql, bB[u], cA[u], gmn[u]);
+#pragma unroll
+                for (int u = 0; u < NS; ++u) gmn[u] = fold16(cB[u], gmn[u]);
+                if ((c + 1) % kGroupChunks == 0 || c + 1 == nchunks) {
+#pragma unroll
+                    for (int u = 0; u < NS; ++u)
+                        close_group(gmn[u], c / kGroupChunks, t1[u], t2[u], t3[u], t4[u], g1[u], g2[u], g3[u]);
                 }
             }
             if (c + 1 < nchunks) store_chunk((c + 1) & 1, c + 1, pre, r0, r1);
             __syncthreads();
         }
         if (!active) return;
-#pragma unroll
-        for (int u = 0; u < NS; ++u) {
-            gmn[u] = fold16(cB[u], gmn[u]);
-            close_group(gmn[u], (nchunks - 1) / kGroupChunks, t1[u], t2[u], t3[u], t4[u], g1[u], g2[u], g3[u]);
-        }
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
             int r = lane & 31;
