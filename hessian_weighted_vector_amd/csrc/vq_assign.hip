@@ -763,9 +763,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 
 // S = sum_t omega_t x_t^2 and B_k = sum_t omega_t c_kt^2 (the bias), and
 // sqrt(B_k) <= sqrt(S) + sqrt(D_k) where D_k = e_k + S is the weighted
 // distance itself.  So |e~_k - e_k| <= a (sqrt(S) + sqrt(D_k)) + E0 with
-// a = 2^-9 (1 + 2^-10) sqrt(S) and E0 = 48u (9 S + 4 |e~|) + 2 (the fp32
-// accumulation, the bias split and fp16's subnormal range, all in scaled
-// units).  Solving for sqrt(D_k) with the coarse value D~ = e~ + S gives
+// a = 2^-9 (1 + 2^-10) sqrt(S) and E0 = 48u (11 S + 5 |e~|) + 2: the fp32
+// accumulation, fp16's subnormal range (all in scaled units) and the bias,
+// which the coarse pass forms in fp32 (within 13u of B_k, and B_k <= 4 S +
+// 2 |e~| up to terms of second order).  Solving for sqrt(D_k) with the coarse value D~ = e~ + S gives
 // sqrt(D_k) <= (a + sqrt(a^2 + 4 (D~ + a sqrt(S) + E0))) / 2, hence a bound
 // Ehat(e~) on |e~ - e| from the coarse value alone.  Its slope is below
 // 2^-5, so L(v) = v - Ehat(v) grows with v.
@@ -777,7 +778,7 @@ constexpr int kRefineBlocks = 2048;       // workgroups of the candidate search 
 __device__ __forceinline__ float coarse_err(float v, float S, float sqS, float a)
 {
     const float u = 5.9604644775390625e-8f;   // 2^-24
-    const float E0 = 48.f * u * (9.f * S + 4.f * fabsf(v)) + 2.f;
+    const float E0 = 48.f * u * (11.f * S + 5.f * fabsf(v)) + 2.f;
     const float Dt = fmaxf(v + S, 0.f);
     const float y = 0.5f * (a + sqrtf(a * a + 4.f * (Dt + a * sqS + E0)));
     return 1.001f * (a * (sqS + y) + E0);     // margin for this evaluation's roundings
@@ -1022,23 +1023,39 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
         lds[buf][ct * 96 + crow * 32 + cpos] = cross;
         if (threadIdx.x < kChunkTiles * kTile) {
             const int k = c * kChunkTiles * kTile + (int)threadIdx.x;
-            const double cv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+            const float cf[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
             double c2[8];
+            float c2f[8];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) c2[t] = cv[t] * cv[t];   // exact
-            // one float64 fused multiply-add per term (a masked term adds
-            // an exact zero); the sum is rounded once to fp32
+            for (int t = 0; t < 8; ++t) {
+                if constexpr (COARSE)
+                    c2f[t] = cf[t] * cf[t];                       // one rounding
+                else
+                    c2[t] = (double)cf[t] * (double)cf[t];        // exact
+            }
+            // one fused multiply-add per term (a masked term adds an exact
+            // zero): in float64 with one rounding to fp32 at the end for the
+            // certified search; in fp32 for the coarse pass, whose bound
+            // carries the sum's rounding (at most 13u of the bias with the
+            // squares and the split)
             h16x8 v;
 #pragma unroll
             for (int q = 0; q < kBlockPatterns; ++q) {
                 const unsigned mq = (pw >> (8 * q)) & 0xFFu;
                 float a = kPadSq;
                 if (k < K) {
-                    double acc = 0.0;
+                    if constexpr (COARSE) {
+                        float acc = 0.f;
 #pragma unroll
-                    for (int t = 0; t < 8; ++t)
-                        acc = __builtin_fma((double)(((mq >> t) & 1u) ? 0.f : hb[t]), c2[t], acc);
-                    a = ldexpf((float)acc, sb);
+                        for (int t = 0; t < 8; ++t) acc = fmaf(((mq >> t) & 1u) ? 0.f : hb[t], c2f[t], acc);
+                        a = ldexpf(acc, sb);
+                    } else {
+                        double acc = 0.0;
+#pragma unroll
+                        for (int t = 0; t < 8; ++t)
+                            acc = __builtin_fma((double)(((mq >> t) & 1u) ? 0.f : hb[t]), c2[t], acc);
+                        a = ldexpf((float)acc, sb);
+                    }
                 }
                 _Float16 h, l;
                 split_h16(a, h, l);
