@@ -792,29 +792,19 @@ __device__ __forceinline__ float fold16(const f32x16& a, float m)
     return m;
 }
 
-// One coarse tile: the hi*hi-plus-bias MFMA, with the previous tile folded
-// into the running group minimum between issue and use.
-__device__ __forceinline__ f32x16 tile1_h16(const h16x8 a1, const h16x8 b1v, const f32x16& prev, float& gm)
-{
-    f32x16 acc = {};
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1v, acc, 0, 0, 0);
-    gm = fold16(prev, gm);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // eight VALU
-    return acc;
-}
-
 // Closes group g of one lane pair: the two halves' minima are merged and
-// inserted into the three smallest group minima (t1 <= t2 <= t3, groups g1..g3;
-// the earlier group first among equal minima) and the fourth smallest t4.
-__device__ __forceinline__ void close_group(float& gm, int g, float& t1, float& t2, float& t3, float& t4, int& g1,
-                                            int& g2, int& g3)
+// inserted into the three smallest group minima (t1 <= t2 <= t3; their groups
+// packed in one word, g1 | g2 << 8 | g3 << 16; the earlier group first among
+// equal minima) and the fourth smallest t4.
+__device__ __forceinline__ void close_group_packed(float& gm, uint32_t g, float& t1, float& t2, float& t3, float& t4,
+                                                   uint32_t& gp)
 {
     const float m = fminf(gm, __shfl_xor(gm, 32));
     const bool l1 = m < t1, l2 = m < t2, l3 = m < t3;
-    g3 = l2 ? g2 : (l3 ? g : g3);
-    g2 = l1 ? g1 : (l2 ? g : g2);
-    g1 = l1 ? g : g1;
+    const uint32_t a1 = ((gp << 8) | g) & 0xFFFFFFu;
+    const uint32_t a2 = (gp & 0xFFu) | (g << 8) | ((gp << 8) & 0xFF0000u);
+    const uint32_t a3 = (gp & 0xFFFFu) | (g << 16);
+    gp = l1 ? a1 : (l2 ? a2 : (l3 ? a3 : gp));
     t4 = __builtin_amdgcn_fmed3f(t3, m, t4);
     t3 = __builtin_amdgcn_fmed3f(t2, m, t3);
     t2 = __builtin_amdgcn_fmed3f(t1, m, t2);
@@ -863,10 +853,13 @@ __device__ __forceinline__ void list_append(bool take, int lane, int64_t s, int*
 // the list of the general kernel.
 //
 // COARSE: the coarse pass of the two-pass search.  One MFMA per tile (the
-// second above); per lane the running minimum of the current group of
-// kGroupChunks chunks, and at each group's end the lane pair's minimum goes
-// into the three smallest group minima with their groups and the fourth
-// smallest value.  Group g is a candidate when L(m_g) <= U = m_1 + Ehat(m_1)
+// second above) for each of the NS sets, then the sets' folds into the running
+// minimum of the current group of kGroupChunks chunks (no accumulator
+// ping-pong: the sets' independent MFMAs cover each other's latency, and the
+// registers it would take hold twice the sets, so each staged chunk serves
+// twice the rows); at each group's end the lane pair's minimum goes into the
+// three smallest group minima with their groups and the fourth smallest
+// value.  Group g is a candidate when L(m_g) <= U = m_1 + Ehat(m_1)
 // (coarse_err); since L grows with m, the candidates are the groups of the
 // smallest minima.  Per owned sub-vector: cand[s] = n | g1 << 8 | g2 << 16 |
 // g3 << 24 with n the number of candidates (1..3); a sub-vector with a fourth
@@ -1076,12 +1069,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
 
     if constexpr (COARSE) {
         float gmn[NS], t1[NS], t2[NS], t3[NS], t4[NS];
-        int g1[NS], g2[NS], g3[NS];
-        f32x16 cA[NS], cB[NS];
+        uint32_t gp[NS];
+        f32x16 acc[NS];
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
             gmn[u] = t1[u] = t2[u] = t3[u] = t4[u] = __builtin_inff();
-            g1[u] = g2[u] = g3[u] = 0;
+            gp[u] = 0;
         }
         for (int c = 0; c < nchunks; ++c) {
             if (c + 1 < nchunks) {
@@ -1089,34 +1082,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
                 load_row(c + 1, r0, r1);
             }
             if (active) {
-                // the chunk's tiles, software pipelined within the chunk: tile
-                // t's MFMAs are issued before tile t-1 is folded (two
-                // accumulator sets alternate) and the last tile is folded
-                // after the loop, so a group ends with its last chunk
+                // per tile: the MFMAs of every set, then their folds (the
+                // sets' independent MFMAs cover each other's latency)
                 const uint4* L = lds[c & 1] + a_off;
-                static_assert(kChunkTiles % 2 == 0, "tiles 1..kChunkTiles-2 go in pairs");
-                const h16x8 qf = __builtin_bit_cast(h16x8, L[32]);
-#pragma unroll
-                for (int u = 0; u < NS; ++u)
-                    cA[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf, bB[u], f32x16{}, 0, 0, 0);
 #pragma unroll 1
-                for (int tt = 1; tt < kChunkTiles - 1; tt += 2) {
-                    const h16x8 q0 = __builtin_bit_cast(h16x8, L[tt * 96 + 32]);
-                    const h16x8 q1 = __builtin_bit_cast(h16x8, L[(tt + 1) * 96 + 32]);
+                for (int t = 0; t < kChunkTiles; ++t) {
+                    const h16x8 q = __builtin_bit_cast(h16x8, L[t * 96 + 32]);
 #pragma unroll
-                    for (int u = 0; u < NS; ++u) cB[u] = tile1_h16(q0, bB[u], cA[u], gmn[u]);
+                    for (int u = 0; u < NS; ++u)
+                        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(q, bB[u], f32x16{}, 0, 0, 0);
 #pragma unroll
-                    for (int u = 0; u < NS; ++u) cA[u] = tile1_h16(q1, bB[u], cB[u], gmn[u]);
+                    for (int u = 0; u < NS; ++u) gmn[u] = fold16(acc[u], gmn[u]);
                 }
-                const h16x8 ql = __builtin_bit_cast(h16x8, L[(kChunkTiles - 1) * 96 + 32]);
-#pragma unroll
-                for (int u = 0; u < NS; ++u) cB[u] = tile1_h16(ql, bB[u], cA[u], gmn[u]);
-#pragma unroll
-                for (int u = 0; u < NS; ++u) gmn[u] = fold16(cB[u], gmn[u]);
                 if ((c + 1) % kGroupChunks == 0 || c + 1 == nchunks) {
 #pragma unroll
                     for (int u = 0; u < NS; ++u)
-                        close_group(gmn[u], c / kGroupChunks, t1[u], t2[u], t3[u], t4[u], g1[u], g2[u], g3[u]);
+                        close_group_packed(gmn[u], (uint32_t)(c / kGroupChunks), t1[u], t2[u], t3[u], t4[u], gp[u]);
                 }
             }
             if (c + 1 < nchunks) store_chunk((c + 1) & 1, c + 1, pre, r0, r1);
@@ -1166,7 +1147,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NS 
                         to_dirty = true;
                     } else {
                         const uint32_t n = 1u + (low(t2[u]) <= U ? 1u : 0u) + (low(t3[u]) <= U ? 1u : 0u);
-                        cw = n | ((uint32_t)g1[u] << 8) | ((uint32_t)g2[u] << 16) | ((uint32_t)g3[u] << 24);
+                        cw = n | (gp[u] << 8);
                     }
                 }
             }
@@ -1734,6 +1715,10 @@ constexpr unsigned kOneBlocks = 4096;
 // Row sets of 32 per wave in the shared-weight search, and rows per workgroup.
 constexpr int kSharedSets = 4;
 constexpr int kSharedRows = kSubPerBlock * kSharedSets;
+// Row sets of 32 per wave in the coarse pass (no accumulator ping-pong, so
+// twice the sets fit, and the chunk staging serves twice the rows).
+constexpr int kCoarseSets = 8;
+constexpr int kCoarseRows = kSubPerBlock * kCoarseSets;
 
 inline int padded_K(int K) { return (K + kChunkK - 1) / kChunkK * kChunkK; }
 
@@ -1851,7 +1836,8 @@ vq_status assign_launch(const float* X, const float* hcol, const float* rho, con
             if (!cv.ok) return fail(VQ_ERR_WORKSPACE, "vq_assign: workspace too small");
             hipLaunchKernelGGL(k_fill_int, dim3(1), dim3(kMaxGroups + 1), 0, st, gcount, kMaxGroups + 1, 0);
             VQ_LAUNCHED("k_fill_int");
-            hipLaunchKernelGGL((k_assign_h16s<false, kSharedSets, true>), dim3((unsigned)shared_groups),
+            const int64_t coarse_groups = (M + kCoarseRows - 1) / kCoarseRows * nb;
+            hipLaunchKernelGGL((k_assign_h16s<false, kCoarseSets, true>), dim3((unsigned)coarse_groups),
                                dim3(kWaves * 64), 0, st, X, hcol, rho, mask, mask ? pattern : nullptr, M, nb, d, P,
                                cmax, C, K, nch, idx, dist, flag_count, flag_list, dirty_count, dirty_list, cand);
             VQ_LAUNCHED("k_assign_h16s");
