@@ -74,15 +74,18 @@ def test_one_pass_and_two_pass_match_oracle(masked):
     assert bits_equal(host(d1), ref_dist.astype(np.float32))
 
 
+@pytest.mark.parametrize("masked", [False, True], ids=["shared", "own-weights"])
 @pytest.mark.parametrize("copies,jitter", [(2, 1e-3), (3, 1e-3), (4, 1e-3), (6, 1e-3), (5, 0.0), (4, 1e-6)],
                          ids=["2-groups", "3-groups", "4-groups", "6-groups", "5-exact-ties", "4-near-ties"])
-def test_near_copies_across_groups(copies, jitter):
+def test_near_copies_across_groups(copies, jitter, masked):
     # Every sub-vector sits next to a centroid that has near copies in other
     # groups of 1024, so the coarse pass names several candidate groups: up to
     # three are searched as candidates, more send the sub-vector to the
     # whole-codebook search; exact copies are ties that only the exact
-    # re-search can settle (lowest index).
-    say("near copies", copies, jitter)
+    # re-search can settle (lowest index).  "own-weights" masks about a third
+    # of the elements at random, so most column blocks have far more than four
+    # mask bytes and most sub-vectors take the general form's coarse pass.
+    say("near copies", copies, jitter, masked)
     g = np.random.default_rng([31, copies, int(jitter * 1e6)])
     M, N, d, K = 256, 512, 8, 8192
     n_sub = M * N // d
@@ -93,8 +96,13 @@ def test_near_copies_across_groups(copies, jitter):
     rows = g.choice(base, n_sub)
     X = (C[rows] + 0.05 * g.standard_normal((n_sub, d))).astype(np.float32).reshape(M, N)
     h = (0.5 + g.random(N)).astype(np.float32)
-    ref, ref_d = oracle.assign(X, h, None, None, d, C)
+    keep = (g.random((M, N)) > 0.3).astype(np.uint8) if masked else None
+    if masked:
+        keep[:, :d] = 0                          # a fully masked block: index 0 (shared form)
+        keep.reshape(-1, d)[g.choice(n_sub, 50, replace=False)] = 0   # and single ones (general form)
+    ref, ref_d = oracle.assign(X, h, None, keep, d, C)
     ws = vq.workspace(M, N, d, K)
-    idx, dist = vq.assign(dev(X), dev(h), None, None, d, dev(C), ws, want_dist=True)
+    mask = dev(mask_from_keep(keep, d)) if masked else None
+    idx, dist = vq.assign(dev(X), dev(h), None, mask, d, dev(C), ws, want_dist=True)
     assert bits_equal(host(idx), ref), np.flatnonzero(host(idx) != ref)[:10]
     assert bits_equal(host(dist), ref_d.astype(np.float32))
