@@ -146,7 +146,12 @@ vq_status vq_init(const float* X, int64_t M, int64_t N, int d, const int32_t* pe
  * form runs on the fp16 matrix cores with every fp32 operand split into two
  * fp16 parts (fp32 accumulation), each winner is certified against a
  * rigorous rounding bound, and uncertified sub-vectors are re-searched
- * exactly in float64.  X = the matrix being quantized ([M x N] f32),
+ * exactly in float64.  With more than 2048 centroids and a workspace of
+ * vq_workspace_bytes (64 bytes per sub-vector beyond the minimum), the search
+ * runs in two passes: a coarse pass (one fp16 product per term) with a
+ * derived bound names each sub-vector's candidate groups of 1024 centroids,
+ * and only those are searched as above; with a smaller workspace it runs in
+ * one pass.  The results are the same.  X = the matrix being quantized ([M x N] f32),
  * hcol [N], rho [M] (nullable), mask (nullable), C [K x d].  Outputs
  * idx uint16[n_sub] and, if dist != NULL, dist float32[n_sub] = D(s, idx[s])
  * computed in float64 and rounded. */
@@ -161,7 +166,8 @@ vq_status vq_assign(const float* X, const float* hcol, const float* rho, const u
  * library-held device array of 64 MiB per GPU, allocated when the library is
  * loaded and held until the process ends.  Needs 64*ceil(K/256)*256 +
  * 9*n_sub bytes plus about 2 KiB: K = 65536 allows n_sub up to about 6.99
- * million.  Larger sizes return VQ_ERR_INVALID before any launch.  The call
+ * million (the two-pass search of long codebooks runs where the array also
+ * holds its 64 bytes per sub-vector, else the one-pass search).  Larger sizes return VQ_ERR_INVALID before any launch.  The call
  * allocates nothing.  Every call on one GPU shares that GPU's array (each call
  * clears what it needs), so calls that overlap in time on one GPU race; the
  * vq_assign_exact_* diagnostics do not see this array. */
