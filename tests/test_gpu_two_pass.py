@@ -84,7 +84,8 @@ def test_near_copies_across_groups(copies, jitter, masked):
     # whole-codebook search; exact copies are ties that only the exact
     # re-search can settle (lowest index).  "own-weights" masks about a third
     # of the elements at random, so most column blocks have far more than four
-    # mask bytes and most sub-vectors take the general form's coarse pass.
+    # mask bytes and most sub-vectors are searched with their own weights over
+    # the whole codebook (the general form) beside the two-pass search.
     say("near copies", copies, jitter, masked)
     g = np.random.default_rng([31, copies, int(jitter * 1e6)])
     M, N, d, K = 256, 512, 8, 8192
